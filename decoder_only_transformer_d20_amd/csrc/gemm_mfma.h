@@ -1,0 +1,377 @@
+// bf16 matrix-core GEMM for gfx950 (CDNA4), shared by the per-tile-size
+// translation units.
+//
+//   C[m][n] = sum_k P[m][k] * Q[n][k]
+//
+// Block: 512 threads (8 waves, 2 along m x 4 along n), tile BM x BN x 64,
+// fp32 accumulation in v_mfma_f32_32x32x16_bf16.  Q (the n side) is the
+// instruction's A operand and P (the m side) its B operand, so a lane's
+// sixteen accumulators hold one row m and runs of four consecutive columns
+// n: every epilogue works on contiguous 8-byte (bf16) / 16-byte (fp32)
+// pieces of a row, and row-wise reductions (log-sum-exp) stay in a lane.
+//
+// Both operand tiles live in LDS as [row][64 k] bf16 (128 B per row), the
+// 16-byte chunk c of row r stored at chunk c ^ (r & 7): a fragment read
+// (32 rows x one chunk) and a row write both hit 8 distinct chunk slots per
+// 8 lanes.  Operands stored k-major ([rows][K]) are copied in 16-byte
+// pieces; operands stored row-major in k ([K][rows], the backward pass's
+// transposed products) are read as 8 x 8 blocks and transposed in
+// registers before the LDS write, so every layout reaches the same LDS
+// image.  Two LDS stages: the global loads of tile k+1 are in flight while
+// tile k is multiplied; one barrier per tile.
+#pragma once
+
+#include "nc_internal.h"
+
+namespace nc {
+namespace mfma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 64;
+constexpr int kThreads = 512;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline uint32_t lds_off(int row, int chunk) { return (uint32_t)row * 128u + ((uint32_t)(chunk ^ (row & 7)) << 4); }
+
+__device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ inline uint32_t pack2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+__device__ inline float relu2f(float x) {
+  x = fmaxf(x, 0.f);
+  return x * x;
+}
+__device__ inline uint32_t relu2_pair(uint32_t w) { return pack2(relu2f(bf_lo(w)), relu2f(bf_hi(w))); }
+__device__ inline uint4 relu2_chunk(uint4 v) {
+  return make_uint4(relu2_pair(v.x), relu2_pair(v.y), relu2_pair(v.z), relu2_pair(v.w));
+}
+
+__device__ inline uint32_t word(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
+
+// 8 x 8 bf16 transpose: in[kk] holds 8 consecutive rows' elements at one k;
+// out[e] holds row e's 8 consecutive k values.
+__device__ inline void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a = word(in[2 * p], e >> 1), b = word(in[2 * p + 1], e >> 1);
+      w[p] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    out[e] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// One operand tile (R rows x 64 k) -> registers -> LDS, by 256 threads.
+template <int R, bool TRANS, bool XF>
+struct TileLoader {
+  static constexpr int kLoads = 8;
+  uint4 reg[8];
+  const bf16* base;   // operand origin
+  int64_t ld;
+  int tl;             // thread index within the 256 loaders
+
+  __device__ inline bool active() const { return TRANS ? (tl < R) : true; }
+
+  __device__ inline void load(int64_t row0, int64_t k0) {
+    if (!TRANS) {
+      // R*8 chunks of 16 B; 8 lanes cover one 128-byte row segment
+#pragma unroll
+      for (int i = 0; i < R / 32; ++i) {
+        const int q = tl + 256 * i;
+        const int r = q >> 3, c = q & 7;
+        reg[i] = *reinterpret_cast<const uint4*>(base + (row0 + r) * ld + k0 + c * 8);
+      }
+    } else if (tl < R) {
+      // micro-block: k rows kc*8 .. +7, columns (rows of the tile) mg*8 .. +7
+      const int kc = tl & 7, mg = tl >> 3;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        reg[kk] = *reinterpret_cast<const uint4*>(base + (k0 + kc * 8 + kk) * ld + row0 + mg * 8);
+    }
+  }
+
+  __device__ inline void store(char* lds) {
+    if (!TRANS) {
+#pragma unroll
+      for (int i = 0; i < R / 32; ++i) {
+        const int q = tl + 256 * i;
+        const int r = q >> 3, c = q & 7;
+        uint4 v = reg[i];
+        if (XF) v = relu2_chunk(v);
+        *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = v;
+      }
+    } else if (tl < R) {
+      const int kc = tl & 7, mg = tl >> 3;
+      uint4 t[8];
+      transpose8(reg, t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint4 v = t[e];
+        if (XF) v = relu2_chunk(v);
+        *reinterpret_cast<uint4*>(lds + lds_off(mg * 8 + e, kc)) = v;
+      }
+    }
+  }
+};
+
+template <int BM, int BN, bool PT, bool QT, bool XP, bool XQ, int EPI>
+__global__ void __launch_bounds__(kThreads, 1) k_gemm_mfma(GemmDesc g) {
+  static_assert(BM % 64 == 0 && BN % 128 == 0, "tile");
+  constexpr int WTM = BM / 2, WTN = BN / 4;      // wave tile
+  constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 fragments per wave
+  constexpr int STAGE = (BM + BN) * 128;         // bytes per LDS stage
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // XCD-aware tile order: consecutive logical tiles run on one XCD (blocks
+  // are dealt to the 8 XCDs round-robin), n fastest so a P row-panel is
+  // reused from that XCD's L2.
+  const int ntn = g.N / BN, ntm = g.M / BM;
+  const int nb = ntn * ntm;
+  int b = blockIdx.x;
+  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+  const int tm = b / ntn, tn = b % ntn;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int kper = g.K / g.splits;
+  const int64_t kbeg = (int64_t)blockIdx.y * kper;
+  const int nk = kper / BK;
+
+  // waves 0-3 load P tiles, waves 4-7 load Q tiles
+  const bool loadsP = tid < 256;
+  TileLoader<BM, PT, XP> lp;
+  TileLoader<BN, QT, XQ> lq;
+  lp.base = (const bf16*)g.P; lp.ld = g.ldp; lp.tl = tid & 255;
+  lq.base = (const bf16*)g.Q; lq.ld = g.ldq; lq.tl = tid & 255;
+
+  auto gload = [&](int64_t k0) {
+    if (loadsP) lp.load(m0, k0); else lq.load(n0, k0);
+  };
+  auto lstore = [&](int stage) {
+    char* s = smem + stage * STAGE;
+    if (loadsP) lp.store(s); else lq.store(s + BM * 128);
+  };
+
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  gload(kbeg);
+  lstore(0);
+  __syncthreads();
+
+  const int frow = lane & 31, fchunk = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) gload(kbeg + (int64_t)(kt + 1) * BK);
+    const char* sP = smem + (kt & 1) * STAGE;
+    const char* sQ = sP + BM * 128;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      bf16x8 a[FN], bb[FM];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        a[j] = *reinterpret_cast<const bf16x8*>(sQ + lds_off(wn * WTN + j * 32 + frow, 2 * s + fchunk));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        bb[i] = *reinterpret_cast<const bf16x8*>(sP + lds_off(wm * WTM + i * 32 + frow, 2 * s + fchunk));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], bb[i], acc[i][j], 0, 0, 0);
+    }
+    if (more) lstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------------ epilogue
+  // lane holds row m = m0 + wm*WTM + i*32 + (lane&31) and, for register
+  // group q (4 regs), columns n = n0 + wn*WTN + j*32 + 8q + 4*(lane>>5) + 0..3
+  const int64_t nw = n0 + wn * WTN + 4 * (lane >> 5);
+
+  if constexpr (EPI == EPI_LSE) {
+    float2* red = reinterpret_cast<float2*>(smem);      // [4 wn][BM]
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int ml = wm * WTM + i * 32 + (lane & 31);
+      const int64_t m = m0 + ml;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float s = 0.f;
+      const float mxs = mx * kLog2e;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(acc[i][j][r] * kLog2e - mxs);
+      s += __shfl_xor(s, 32, 64);
+      if (lane < 32) red[wn * BM + ml] = make_float2(mx, s);
+      // the target's logit, from whichever lane holds it
+      const int t = g.tgt[m];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (t == nw + j * 32 + 8 * (r >> 2) + (r & 3)) g.ztgt[m] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (tid < BM) {
+      float2 p[4];
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        p[w] = red[w * BM + tid];
+        M = fmaxf(M, p[w].x);
+      }
+      float S = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) S += p[w].y * __builtin_amdgcn_exp2f((p[w].x - M) * kLog2e);
+      g.lse_part[(m0 + tid) * g.lse_stride + tn] = make_float2(M, S);
+    }
+    return;
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
+      float dz_l = 0.f, dz_s = 0.f;
+      int dz_t = -1;
+      int rope_t = 0;
+      if constexpr (EPI == EPI_DZ) {
+        dz_t = g.tgt[m];
+        dz_l = g.lse[m] * kLog2e;
+        dz_s = dz_t >= 0 ? *g.inv_nvalid : 0.f;
+      }
+      if constexpr (EPI == EPI_ROPE) rope_t = (int)(m % g.rope_T);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = nw + j * 32 + 8 * q;
+          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if constexpr (EPI == EPI_F32) {
+            if (g.splits > 1) {
+              float* dst = g.part + (int64_t)blockIdx.y * g.M * g.N + m * g.N + n;
+              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              float* dst = (float*)g.C + m * g.ldc + n;
+              float4 o = make_float4(v[0], v[1], v[2], v[3]);
+              if (g.beta) {
+                const float4 c = *reinterpret_cast<const float4*>(dst);
+                o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+              }
+              *reinterpret_cast<float4*>(dst) = o;
+            }
+            continue;
+          }
+          if constexpr (EPI == EPI_ROPE) {
+            if (n < g.rope_cols) {
+              const int pi = (int)(n % g.head_dim) >> 1;
+              const float4 cs = *reinterpret_cast<const float4*>(g.rope + (int64_t)rope_t * (g.head_dim >> 1) + pi);
+              const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+              v[0] = x0 * cs.x - x1 * cs.y;
+              v[1] = x0 * cs.y + x1 * cs.x;
+              v[2] = x2 * cs.z - x3 * cs.w;
+              v[3] = x2 * cs.w + x3 * cs.z;
+            }
+          }
+          if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2) {
+            const uint2 a = *reinterpret_cast<const uint2*>((const bf16*)g.aux + m * g.ldaux + n);
+            const float a0 = bf_lo(a.x), a1 = bf_hi(a.x), a2 = bf_lo(a.y), a3 = bf_hi(a.y);
+            if constexpr (EPI == EPI_RESID) {
+              v[0] += a0; v[1] += a1; v[2] += a2; v[3] += a3;
+            } else {
+              v[0] *= 2.f * fmaxf(a0, 0.f);
+              v[1] *= 2.f * fmaxf(a1, 0.f);
+              v[2] *= 2.f * fmaxf(a2, 0.f);
+              v[3] *= 2.f * fmaxf(a3, 0.f);
+            }
+          }
+          if constexpr (EPI == EPI_DZ) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = (__builtin_amdgcn_exp2f(v[e] * kLog2e - dz_l) - ((n + e) == dz_t ? 1.f : 0.f)) * dz_s;
+          }
+          *reinterpret_cast<uint2*>((bf16*)g.C + m * g.ldc + n) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+        }
+    }
+  }
+}
+
+template <int BM, int BN, bool PT, bool QT, bool XP, bool XQ, int EPI>
+hipError_t launch(const GemmDesc& g, hipStream_t s) {
+  dim3 grid((g.M / BM) * (g.N / BN), g.splits);
+  k_gemm_mfma<BM, BN, PT, QT, XP, XQ, EPI><<<grid, kThreads, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+}  // namespace mfma
+}  // namespace nc
+
+// Operand-layout / transform / epilogue combinations the library uses.
+//   forward:  qkv (ROPE), o Wo^T + x (RESID), m W1^T (STORE),
+//             relu(h)^2 W2^T + x (P transform, RESID), head (LSE), head
+//             recompute (DZ)
+//   backward: weight gradients (both operands transposed, fp32 partials,
+//             relu^2 on Q for dW2), data gradients (Q transposed: STORE,
+//             DRELU2)
+//   tests:    every layout with fp32 and bf16 stores
+#define NC_MFMA_COMBOS(X)             \
+  X(0, 0, 0, 0, EPI_STORE)            \
+  X(0, 0, 0, 0, EPI_ROPE)             \
+  X(0, 0, 0, 0, EPI_RESID)            \
+  X(0, 0, 1, 0, EPI_RESID)            \
+  X(0, 0, 0, 0, EPI_LSE)              \
+  X(0, 0, 0, 0, EPI_DZ)               \
+  X(0, 0, 0, 0, EPI_F32)              \
+  X(0, 1, 0, 0, EPI_STORE)            \
+  X(0, 1, 0, 0, EPI_DRELU2)           \
+  X(0, 1, 0, 0, EPI_F32)              \
+  X(1, 0, 0, 0, EPI_STORE)            \
+  X(1, 0, 0, 0, EPI_F32)              \
+  X(1, 1, 0, 0, EPI_STORE)            \
+  X(1, 1, 0, 0, EPI_F32)              \
+  X(1, 1, 0, 1, EPI_F32)
+
+namespace nc {
+namespace mfma {
+inline bool combo_supported(const GemmDesc& g) {
+#define NC_X(PT, QT, XP, XQ, EPI) \
+  if (g.p_trans == PT && g.q_trans == QT && g.p_relu2 == XP && g.q_relu2 == XQ && g.epi == EPI) return true;
+  NC_MFMA_COMBOS(NC_X)
+#undef NC_X
+  return false;
+}
+
+template <int BM, int BN>
+hipError_t dispatch(const GemmDesc& g, hipStream_t s) {
+#define NC_X(PT, QT, XP, XQ, EPI) \
+  if (g.p_trans == PT && g.q_trans == QT && g.p_relu2 == XP && g.q_relu2 == XQ && g.epi == EPI) \
+    return launch<BM, BN, PT, QT, XP, XQ, EPI>(g, s);
+  NC_MFMA_COMBOS(NC_X)
+#undef NC_X
+  return hipErrorInvalidValue;
+}
+
+hipError_t gemm_256x256(const GemmDesc& g, hipStream_t s);
+hipError_t gemm_256x128(const GemmDesc& g, hipStream_t s);
+hipError_t gemm_128x128(const GemmDesc& g, hipStream_t s);
+}  // namespace mfma
+}  // namespace nc

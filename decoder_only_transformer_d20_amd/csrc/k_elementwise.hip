@@ -1,0 +1,376 @@
+// HBM-bound kernels of the training step: embedding gather / scatter-add,
+// parameter-free RMSNorm forward / backward, the rotary cos/sin table, the
+// cross-entropy combine of per-tile log-sum-exp partials, the loss and
+// bits-per-byte reduction, the split-K reduction and small fills.
+//
+// One 64-lane wavefront owns one row wherever a row is reduced; rows are
+// read with 16-byte vector loads, so a wave touches whole 128-byte lines.
+#include "nc_internal.h"
+
+namespace nc {
+
+namespace {
+
+constexpr int kWave = 64;
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// 16-byte vector of T
+template <typename T> struct Vec;
+template <> struct Vec<float> {
+  static constexpr int n = 4;
+  float v[4];
+};
+template <> struct Vec<bf16> {
+  static constexpr int n = 8;
+  bf16 v[8];
+};
+
+template <typename T> __device__ inline Vec<T> ld16(const T* p) {
+  Vec<T> r;
+  *reinterpret_cast<uint4*>(&r) = *reinterpret_cast<const uint4*>(p);
+  return r;
+}
+template <typename T> __device__ inline void st16(T* p, const Vec<T>& r) {
+  *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(&r);
+}
+
+// ---------------------------------------------------------------------------
+// embedding
+// ---------------------------------------------------------------------------
+// x[n, :] = E[idx[n], :]  (a bitwise copy of the row)
+template <typename T>
+__global__ void __launch_bounds__(256) k_embed_fwd(const T* __restrict__ E, const int32_t* __restrict__ idx,
+                                                   T* __restrict__ x, int64_t n, int d) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const int64_t src = (int64_t)idx[row] * d;
+  const int chunks = d * (int)sizeof(T) / 16;
+  const uint4* s = reinterpret_cast<const uint4*>(E + src);
+  uint4* t = reinterpret_cast<uint4*>(x + row * d);
+  for (int c = lane; c < chunks; c += kWave) t[c] = s[c];
+}
+
+// dE[idx[n], :] += g[n, :]  (fp32 hardware atomics; the order of the adds
+// into one row is not fixed, so low bits may vary between runs)
+template <typename T>
+__global__ void __launch_bounds__(256) k_embed_bwd(const T* __restrict__ g, const int32_t* __restrict__ idx,
+                                                   float* __restrict__ dE, int64_t n, int d) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  float* dst = dE + (int64_t)idx[row] * d;
+  const T* src = g + row * d;
+  constexpr int VN = Vec<T>::n;
+  for (int c = lane; c < d / VN; c += kWave) {
+    Vec<T> v = ld16(src + c * VN);
+#pragma unroll
+    for (int i = 0; i < VN; ++i) unsafeAtomicAdd(dst + c * VN + i, to_f32(v.v[i]));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm: y = x * r, r = 1/sqrt(mean(x^2) + eps).  One wave per row; a lane
+// keeps its chunks of the row in registers between the two passes.
+// ---------------------------------------------------------------------------
+constexpr int kMaxChunks = 8;   // d <= 64 lanes * 8 chunks * (16 B / sizeof(T))
+
+template <typename T>
+__global__ void __launch_bounds__(256) k_rmsnorm_fwd(const T* __restrict__ x, T* __restrict__ y,
+                                                     float* __restrict__ r, int64_t rows, int d, float eps) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  constexpr int VN = Vec<T>::n;
+  const int chunks = d / VN;
+  const T* xr = x + row * d;
+  Vec<T> buf[kMaxChunks];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = lane + i * kWave;
+    if (c < chunks) {
+      buf[i] = ld16(xr + c * VN);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        const float f = to_f32(buf[i].v[e]);
+        ss += f * f;
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  const float rr = 1.0f / sqrtf(ss / (float)d + eps);
+  T* yr = y + row * d;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = lane + i * kWave;
+    if (c < chunks) {
+      Vec<T> o;
+#pragma unroll
+      for (int e = 0; e < VN; ++e) o.v[e] = from_f32<T>(to_f32(buf[i].v[e]) * rr);
+      st16(yr + c * VN, o);
+    }
+  }
+  if (lane == 0) r[row] = rr;
+}
+
+// dx = r * (dy - y * mean(dy * y));  dx_io = dx (accumulate = 0) or dx_io + dx.
+template <typename T>
+__global__ void __launch_bounds__(256) k_rmsnorm_bwd(const T* __restrict__ y, const float* __restrict__ r,
+                                                     const T* __restrict__ dy, T* __restrict__ dx_io,
+                                                     int64_t rows, int d, int accumulate) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  constexpr int VN = Vec<T>::n;
+  const int chunks = d / VN;
+  const T* yr = y + row * d;
+  const T* gr = dy + row * d;
+  Vec<T> yb[kMaxChunks], gb[kMaxChunks];
+  float dot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = lane + i * kWave;
+    if (c < chunks) {
+      yb[i] = ld16(yr + c * VN);
+      gb[i] = ld16(gr + c * VN);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) dot += to_f32(yb[i].v[e]) * to_f32(gb[i].v[e]);
+    }
+  }
+  dot = wave_sum(dot) / (float)d;
+  const float rr = r[row];
+  T* xr = dx_io + row * d;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = lane + i * kWave;
+    if (c < chunks) {
+      Vec<T> o;
+      if (accumulate) o = ld16(xr + c * VN);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        float v = rr * (to_f32(gb[i].v[e]) - to_f32(yb[i].v[e]) * dot);
+        if (accumulate) v += to_f32(o.v[e]);
+        o.v[e] = from_f32<T>(v);
+      }
+      st16(xr + c * VN, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rotary table: tab[t][i] = (cos, sin)(t * base^(-2i/Q)), computed in fp64
+// and rounded once (angles reach T radians, far beyond fp32's safe range)
+// ---------------------------------------------------------------------------
+__global__ void k_rope_table(float2* tab, int T, int Q, double base) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = Q / 2;
+  if (k >= (int64_t)T * half) return;
+  const int t = (int)(k / half), i = (int)(k % half);
+  const double theta = pow(base, -2.0 * (double)i / (double)Q);
+  const double phi = (double)t * theta;
+  tab[k] = make_float2((float)cos(phi), (float)sin(phi));
+}
+
+// ---------------------------------------------------------------------------
+// cross-entropy: combine per-tile (max, sum exp) partials of one row into
+// lse, then ce = lse - z[target] (0 for an ignored target)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_ce_combine(const float2* __restrict__ part, int nblk,
+                                                    const float* __restrict__ ztgt, const int32_t* __restrict__ tgt,
+                                                    float* __restrict__ lse, float* __restrict__ ce, int64_t rows) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float2* p = part + row * nblk;
+  float mx = -INFINITY;
+  for (int b = lane; b < nblk; b += kWave) mx = fmaxf(mx, p[b].x);
+  mx = wave_max(mx);
+  float s = 0.f;
+  for (int b = lane; b < nblk; b += kWave) s += p[b].y * expf(p[b].x - mx);
+  s = wave_sum(s);
+  if (lane == 0) {
+    const float l = mx + logf(s);
+    lse[row] = l;
+    ce[row] = tgt[row] >= 0 ? l - ztgt[row] : 0.f;
+  }
+}
+
+// one block: number of valid targets -> 1/n (0 when none)
+__global__ void __launch_bounds__(1024) k_count_valid(const int32_t* __restrict__ tgt, int64_t n, float* inv) {
+  __shared__ int64_t red[1024];
+  int64_t c = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) c += tgt[i] >= 0;
+  red[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *inv = red[0] > 0 ? (float)(1.0 / (double)red[0]) : 0.f;
+}
+
+// one block, fixed order: out = {sum ce / n, sum ce / (ln2 * sum bytes), sum ce, sum bytes, n}
+__global__ void __launch_bounds__(1024) k_loss_bpb(const float* __restrict__ ce, const int32_t* __restrict__ tgt,
+                                                   const int32_t* __restrict__ bytes, int64_t n, double* out) {
+  __shared__ double sce[1024];
+  __shared__ int64_t sb[1024], sn[1024];
+  double a = 0.0;
+  int64_t b = 0, c = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) {
+    const int t = tgt[i];
+    if (t >= 0) {
+      a += (double)ce[i];
+      b += bytes[t];
+      c += 1;
+    }
+  }
+  sce[threadIdx.x] = a;
+  sb[threadIdx.x] = b;
+  sn[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      sce[threadIdx.x] += sce[threadIdx.x + w];
+      sb[threadIdx.x] += sb[threadIdx.x + w];
+      sn[threadIdx.x] += sn[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double s = sce[0];
+    const double nb = (double)sb[0], nv = (double)sn[0];
+    out[0] = nv > 0 ? s / nv : 0.0;
+    out[1] = nb > 0 ? s / (0.69314718055994530942 * nb) : 0.0;
+    out[2] = s;
+    out[3] = nb;
+    out[4] = nv;
+  }
+}
+
+// out[i] = (beta ? out[i] : 0) + sum_s part[s][i], in split order
+__global__ void __launch_bounds__(256) k_splitk_reduce(const float4* __restrict__ part, int splits, int64_t n4,
+                                                       float4* __restrict__ out, int beta) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 a = beta ? out[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < splits; ++s) {
+    const float4 p = part[s * n4 + i];
+    a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
+  }
+  out[i] = a;
+}
+
+__global__ void k_fill_f32(float* p, int64_t n, float v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// delta[b][h][t] = sum_e dO[b,t,h,e] * O[b,t,h,e]; one wave per (token, head)
+template <typename T>
+__global__ void __launch_bounds__(256) k_attn_delta(const T* __restrict__ o, const T* __restrict__ dout,
+                                                    float* __restrict__ delta, int B, int Tn, int H, int Q) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= (int64_t)B * Tn * H) return;
+  const int64_t tok = w / H;
+  const int h = (int)(w % H);
+  const int64_t base = tok * (int64_t)H * Q + (int64_t)h * Q;
+  float s = 0.f;
+  for (int e = lane; e < Q; e += kWave) s += to_f32(o[base + e]) * to_f32(dout[base + e]);
+  s = wave_sum(s);
+  if (lane == 0) {
+    const int64_t b = tok / Tn, t = tok % Tn;
+    delta[(b * H + h) * Tn + t] = s;
+  }
+}
+
+inline unsigned nblocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+template <typename T>
+hipError_t embed_fwd(const T* E, const int32_t* idx, T* x, int64_t n, int d, hipStream_t s) {
+  k_embed_fwd<T><<<nblocks(n, 4), 256, 0, s>>>(E, idx, x, n, d);
+  return hipGetLastError();
+}
+template <typename T>
+hipError_t embed_bwd(const T* g, const int32_t* idx, float* dE, int64_t n, int d, hipStream_t s) {
+  k_embed_bwd<T><<<nblocks(n, 4), 256, 0, s>>>(g, idx, dE, n, d);
+  return hipGetLastError();
+}
+template <typename T>
+hipError_t rmsnorm_fwd(const T* x, T* y, float* r, int64_t rows, int d, float eps, hipStream_t s) {
+  if (d % Vec<T>::n != 0 || d > kWave * kMaxChunks * Vec<T>::n) return hipErrorInvalidValue;
+  k_rmsnorm_fwd<T><<<nblocks(rows, 4), 256, 0, s>>>(x, y, r, rows, d, eps);
+  return hipGetLastError();
+}
+template <typename T>
+hipError_t rmsnorm_bwd(const T* y, const float* r, const T* dy, T* dx_io, int64_t rows, int d, int accumulate,
+                       hipStream_t s) {
+  if (d % Vec<T>::n != 0 || d > kWave * kMaxChunks * Vec<T>::n) return hipErrorInvalidValue;
+  k_rmsnorm_bwd<T><<<nblocks(rows, 4), 256, 0, s>>>(y, r, dy, dx_io, rows, d, accumulate);
+  return hipGetLastError();
+}
+template <typename T>
+hipError_t attn_delta(const AttnDesc& a, hipStream_t s) {
+  const int64_t w = (int64_t)a.B * a.T * a.H;
+  k_attn_delta<T><<<nblocks(w, 4), 256, 0, s>>>((const T*)a.o, (const T*)a.dout, a.delta, a.B, a.T, a.H, a.Q);
+  return hipGetLastError();
+}
+
+template hipError_t embed_fwd<float>(const float*, const int32_t*, float*, int64_t, int, hipStream_t);
+template hipError_t embed_fwd<bf16>(const bf16*, const int32_t*, bf16*, int64_t, int, hipStream_t);
+template hipError_t embed_bwd<float>(const float*, const int32_t*, float*, int64_t, int, hipStream_t);
+template hipError_t embed_bwd<bf16>(const bf16*, const int32_t*, float*, int64_t, int, hipStream_t);
+template hipError_t rmsnorm_fwd<float>(const float*, float*, float*, int64_t, int, float, hipStream_t);
+template hipError_t rmsnorm_fwd<bf16>(const bf16*, bf16*, float*, int64_t, int, float, hipStream_t);
+template hipError_t rmsnorm_bwd<float>(const float*, const float*, const float*, float*, int64_t, int, int, hipStream_t);
+template hipError_t rmsnorm_bwd<bf16>(const bf16*, const float*, const bf16*, bf16*, int64_t, int, int, hipStream_t);
+template hipError_t attn_delta<float>(const AttnDesc&, hipStream_t);
+template hipError_t attn_delta<bf16>(const AttnDesc&, hipStream_t);
+
+hipError_t rope_table(float2* tab, int T, int Q, float base, hipStream_t s) {
+  const int64_t n = (int64_t)T * (Q / 2);
+  k_rope_table<<<nblocks(n, 256), 256, 0, s>>>(tab, T, Q, (double)base);
+  return hipGetLastError();
+}
+hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int32_t* tgt, float* lse, float* ce,
+                      int64_t rows, hipStream_t s) {
+  k_ce_combine<<<nblocks(rows, 4), 256, 0, s>>>(part, nblk, ztgt, tgt, lse, ce, rows);
+  return hipGetLastError();
+}
+hipError_t count_valid(const int32_t* tgt, int64_t n, float* inv, hipStream_t s) {
+  k_count_valid<<<1, 1024, 0, s>>>(tgt, n, inv);
+  return hipGetLastError();
+}
+hipError_t loss_bpb(const float* ce, const int32_t* tgt, const int32_t* bytes, int64_t n, double* out,
+                    hipStream_t s) {
+  k_loss_bpb<<<1, 1024, 0, s>>>(ce, tgt, bytes, n, out);
+  return hipGetLastError();
+}
+hipError_t splitk_reduce(const float* part, int splits, int64_t n, float* out, int beta, hipStream_t s) {
+  if (n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  k_splitk_reduce<<<nblocks(n4, 256), 256, 0, s>>>((const float4*)part, splits, n4, (float4*)out, beta);
+  return hipGetLastError();
+}
+hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  k_fill_f32<<<nblocks(n, 256), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+hipError_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s) {
+  return hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, s);
+}
+
+}  // namespace nc

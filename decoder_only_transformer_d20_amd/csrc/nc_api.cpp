@@ -1,0 +1,528 @@
+// Host side of the C ABI declared in include/nc.h and include/nc_ops.h:
+// configuration checks, the flat parameter layout, the workspace plan and
+// the order of kernel launches for the forward and backward passes.
+//
+// The step follows the nanochat speedrun walkthrough (lyylswood.com,
+// sections Pretraining): pre-norm blocks of causal self-attention with
+// rotary positions and a squared-ReLU MLP, parameter-free RMSNorm, untied
+// embedding / unembedding, next-token cross-entropy and bits per byte.
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "nc.h"
+#include "nc_ops.h"
+#include "nc_internal.h"
+
+using namespace nc;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_block(const nc_config& c) { return (c.flags & NC_FLAG_BLOCK_ONLY) != 0; }
+bool is_bf16(const nc_config& c) { return c.dtype == NC_DTYPE_BF16; }
+size_t esize(const nc_config& c) { return is_bf16(c) ? 2 : 4; }
+bool portable(const nc_config& c) { return !is_bf16(c) || (c.flags & NC_FLAG_PORTABLE_KERNELS); }
+
+int validate(const nc_config* c) {
+  if (!c) return NC_ERR_INVALID_ARG;
+  if (c->dtype != NC_DTYPE_F32 && c->dtype != NC_DTYPE_BF16) return NC_ERR_INVALID_ARG;
+  if (c->flags & ~(NC_FLAG_BLOCK_ONLY | NC_FLAG_PORTABLE_KERNELS)) return NC_ERR_INVALID_ARG;
+  if (c->n_layer <= 0 || c->d_model <= 0 || c->n_head <= 0 || c->head_dim <= 0 || c->d_ff <= 0 ||
+      c->batch <= 0 || c->seq_len <= 0)
+    return NC_ERR_SHAPE;
+  if (c->n_head * c->head_dim != c->d_model) return NC_ERR_SHAPE;
+  if (c->d_model % 64 || c->d_ff % 64 || c->seq_len % 64 || c->head_dim % 64) return NC_ERR_SHAPE;
+  if (c->head_dim > 256) return NC_ERR_UNSUPPORTED;
+  if (is_block(*c)) {
+    if (c->n_layer != 1 || c->vocab != 0) return NC_ERR_SHAPE;
+  } else {
+    if (c->vocab <= 0 || c->vocab % 64) return NC_ERR_SHAPE;
+  }
+  if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return NC_ERR_INVALID_ARG;
+  // one row of the residual stream must fit the RMSNorm kernel's registers
+  if ((int64_t)c->d_model * (int64_t)esize(*c) > 64 * 8 * 16) return NC_ERR_UNSUPPORTED;
+  return NC_OK;
+}
+
+int64_t layer_elems(const nc_config& c) {
+  const int64_t d = c.d_model, F = c.d_ff;
+  return 4 * d * d + 2 * F * d;
+}
+
+// The N-tile the GEMM dispatcher uses for an [M x N] output (the head's
+// log-sum-exp partials have one entry per N-tile).
+int tile_n(const nc_config& c, int M, int N) {
+  if (portable(c)) return 64;
+  GemmDesc g{};
+  g.M = M; g.N = N; g.K = c.d_model; g.splits = 1; g.epi = EPI_LSE;
+  return gemm_mfma_supported(g) ? gemm_mfma_tile_n(M, N) : 64;
+}
+
+// Split-K factor for the weight-gradient products (K = tokens): enough
+// workgroups to fill the chip, every split a multiple of 256 tokens.
+int choose_splits(const nc_config& c, int M, int N, int64_t K) {
+  const int64_t tiles = portable(c) ? (int64_t)(M / 64) * (N / 64)
+                                    : (int64_t)(M / gemm_mfma_tile_m(M, N)) * (N / gemm_mfma_tile_n(M, N));
+  int s = 1;
+  while (tiles * s < 1024 && K % (2LL * s * 256) == 0 && K / (2 * s) >= 2048 && s < 64) s *= 2;
+  return s;
+}
+
+struct Plan {
+  size_t total = 0;
+  size_t rope = 0, idx = 0, tgt = 0, x = 0, xf = 0, rf = 0, ce = 0, lse_head = 0, ztgt = 0, lse_part = 0;
+  size_t scalars = 0, dz = 0, g = 0, gtmp = 0, big = 0, part = 0, delta = 0;
+  size_t layer0 = 0, layer_stride = 0;
+  size_t l_a = 0, l_r1 = 0, l_qkv = 0, l_o = 0, l_lse = 0, l_m = 0, l_r2 = 0, l_h = 0;
+  int head_nblk = 0;
+  int64_t head_chunk = 0;
+};
+
+Plan make_plan(const nc_config& c) {
+  Plan p;
+  const size_t es = esize(c);
+  const int64_t N = (int64_t)c.batch * c.seq_len, d = c.d_model, F = c.d_ff, V = c.vocab;
+  const int64_t BHT = (int64_t)c.batch * c.n_head * c.seq_len;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  p.rope = take((size_t)c.seq_len * (c.head_dim / 2) * 8);
+  p.scalars = take(256);
+  p.delta = take(BHT * 4);
+  p.g = take(N * d * es);
+  p.gtmp = take(N * d * es);
+  p.big = take(N * std::max(F, 3 * d) * es);
+  // split-K partials: the largest of the weight-gradient products
+  size_t part = 0;
+  auto need = [&](int M_, int N_, int64_t K_) {
+    const int s = choose_splits(c, M_, N_, K_);
+    if (s > 1) part = std::max(part, (size_t)s * M_ * N_ * 4);
+  };
+  need((int)(3 * d), (int)d, N);
+  need((int)d, (int)d, N);
+  need((int)F, (int)d, N);
+  need((int)d, (int)F, N);
+  if (!is_block(c)) {
+    p.idx = take(N * 4);
+    p.tgt = take(N * 4);
+    p.x = take(N * d * es);
+    p.xf = take(N * d * es);
+    p.rf = take(N * 4);
+    p.ce = take(N * 4);
+    p.lse_head = take(N * 4);
+    p.ztgt = take(N * 4);
+    p.head_nblk = (int)(V / tile_n(c, (int)std::min<int64_t>(N, 1 << 30), (int)V));
+    p.lse_part = take((size_t)N * p.head_nblk * 8);
+    // token chunks for the head's backward: whole rows, about 16k tokens
+    const int64_t rows = std::max<int64_t>(1, std::min<int64_t>(c.batch, 16384 / c.seq_len));
+    p.head_chunk = rows * c.seq_len;
+    p.dz = take((size_t)p.head_chunk * V * es);
+    need((int)V, (int)d, p.head_chunk);
+  }
+  p.part = take(part);
+  // saved activations, one block of regions per layer
+  size_t lo = 0;
+  auto ltake = [&](size_t bytes) { size_t o = lo; lo += align_up(bytes); return o; };
+  p.l_a = ltake(N * d * es);
+  p.l_r1 = ltake(N * 4);
+  p.l_qkv = ltake(N * 3 * d * es);
+  p.l_o = ltake(N * d * es);
+  p.l_lse = ltake(BHT * 4);
+  p.l_m = ltake(N * d * es);
+  p.l_r2 = ltake(N * 4);
+  p.l_h = ltake(N * F * es);
+  p.layer_stride = lo;
+  p.layer0 = off;
+  off += lo * c.n_layer;
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+struct nc_ctx {
+  nc_config cfg;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipStream_t stream = nullptr;
+  Plan plan;
+  bool have_forward = false;
+  bool have_block_forward = false;
+  std::string err;
+
+  template <typename T> T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
+  char* layer(int l) { return ws + plan.layer0 + plan.layer_stride * (size_t)l; }
+};
+
+namespace {
+
+int fail(nc_ctx* ctx, hipError_t e, const char* what) {
+  ctx->err = std::string(what) + ": " + hipGetErrorString(e);
+  return NC_ERR_HIP;
+}
+#define NC_TRY(expr, what)                      \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return fail(ctx, e_, what); \
+  } while (0)
+
+hipError_t run_gemm(nc_ctx* ctx, const GemmDesc& g) {
+  if (!is_bf16(ctx->cfg)) return gemm_portable<float>(g, ctx->stream);
+  if (portable(ctx->cfg) || !gemm_mfma_supported(g)) return gemm_portable<bf16>(g, ctx->stream);
+  return gemm_mfma_bf16(g, ctx->stream);
+}
+
+GemmDesc gemm(int M, int N, int K, const void* P, int64_t ldp, int pt, const void* Q, int64_t ldq, int qt, int epi,
+              void* C, int64_t ldc) {
+  GemmDesc g{};
+  g.M = M; g.N = N; g.K = K;
+  g.P = P; g.ldp = ldp; g.p_trans = pt;
+  g.Q = Q; g.ldq = ldq; g.q_trans = qt;
+  g.epi = epi; g.C = C; g.ldc = ldc; g.splits = 1;
+  return g;
+}
+
+// weight gradient dW[M'][N'] (+)= sum over tokens P[tok][m'] Q[tok][n']
+hipError_t weight_grad(nc_ctx* ctx, int Mw, int Nw, const void* P, int64_t ldp, const void* Q, int64_t ldq, int q_relu2,
+                       float* dW, int accumulate) {
+  const int64_t N = (int64_t)ctx->cfg.batch * ctx->cfg.seq_len;
+  GemmDesc g = gemm(Mw, Nw, (int)N, P, ldp, 1, Q, ldq, 1, EPI_F32, dW, Nw);
+  g.q_relu2 = q_relu2;
+  g.beta = accumulate;
+  g.splits = choose_splits(ctx->cfg, Mw, Nw, N);
+  g.part = ctx->at<float>(ctx->plan.part);
+  return run_gemm(ctx, g);
+}
+
+template <typename T> hipError_t attn_fwd(nc_ctx* ctx, const AttnDesc& a) {
+  if (!portable(ctx->cfg)) return attn_fwd_mfma(a, ctx->stream);
+  return attn_fwd_portable<T>(a, ctx->stream);
+}
+template <typename T> hipError_t attn_bwd(nc_ctx* ctx, const AttnDesc& a) {
+  if (!portable(ctx->cfg)) return attn_bwd_mfma(a, ctx->stream);
+  return attn_bwd_portable<T>(a, ctx->stream);
+}
+
+// one pre-norm block; x is the residual stream, updated in place
+template <typename T>
+int layer_forward(nc_ctx* ctx, int l, const T* w, T* x) {
+  const nc_config& c = ctx->cfg;
+  const Plan& p = ctx->plan;
+  const int N = c.batch * c.seq_len, d = c.d_model, F = c.d_ff;
+  const T* Wqkv = w;
+  const T* Wo = w + 3LL * d * d;
+  const T* W1 = w + 4LL * d * d;
+  const T* W2 = W1 + (int64_t)F * d;
+  char* L = ctx->layer(l);
+  T* a = (T*)(L + p.l_a);
+  float* r1 = (float*)(L + p.l_r1);
+  T* qkv = (T*)(L + p.l_qkv);
+  T* o = (T*)(L + p.l_o);
+  float* lse = (float*)(L + p.l_lse);
+  T* m = (T*)(L + p.l_m);
+  float* r2 = (float*)(L + p.l_r2);
+  T* h = (T*)(L + p.l_h);
+  hipStream_t s = ctx->stream;
+
+  NC_TRY(rmsnorm_fwd<T>(x, a, r1, N, d, c.rms_eps, s), "rmsnorm (attention input)");
+  GemmDesc g = gemm(N, 3 * d, d, a, d, 0, Wqkv, d, 0, EPI_ROPE, qkv, 3 * d);
+  g.rope = ctx->at<float2>(p.rope); g.rope_T = c.seq_len; g.rope_cols = 2 * d; g.head_dim = c.head_dim;
+  NC_TRY(run_gemm(ctx, g), "qkv projection + rotary");
+  AttnDesc ad{};
+  ad.B = c.batch; ad.T = c.seq_len; ad.H = c.n_head; ad.Q = c.head_dim;
+  ad.qkv = qkv; ad.o_out = o; ad.lse = lse;
+  NC_TRY(attn_fwd<T>(ctx, ad), "attention forward");
+  g = gemm(N, d, d, o, d, 0, Wo, d, 0, EPI_RESID, x, d);
+  g.aux = x; g.ldaux = d;
+  NC_TRY(run_gemm(ctx, g), "output projection + residual");
+  NC_TRY(rmsnorm_fwd<T>(x, m, r2, N, d, c.rms_eps, s), "rmsnorm (MLP input)");
+  NC_TRY(run_gemm(ctx, gemm(N, F, d, m, d, 0, W1, d, 0, EPI_STORE, h, F)), "MLP up projection");
+  g = gemm(N, d, F, h, F, 0, W2, F, 0, EPI_RESID, x, d);
+  g.p_relu2 = 1; g.aux = x; g.ldaux = d;
+  NC_TRY(run_gemm(ctx, g), "MLP down projection + residual");
+  return NC_OK;
+}
+
+// reverse of layer_forward: g = dL/d(layer output) in, dL/d(layer input) out
+template <typename T>
+int layer_backward(nc_ctx* ctx, int l, const T* w, T* gr, float* dw, int accumulate) {
+  const nc_config& c = ctx->cfg;
+  const Plan& p = ctx->plan;
+  const int N = c.batch * c.seq_len, d = c.d_model, F = c.d_ff;
+  const T* Wqkv = w;
+  const T* Wo = w + 3LL * d * d;
+  const T* W1 = w + 4LL * d * d;
+  const T* W2 = W1 + (int64_t)F * d;
+  float* dWqkv = dw;
+  float* dWo = dw + 3LL * d * d;
+  float* dW1 = dw + 4LL * d * d;
+  float* dW2 = dW1 + (int64_t)F * d;
+  char* L = ctx->layer(l);
+  T* a = (T*)(L + p.l_a);
+  float* r1 = (float*)(L + p.l_r1);
+  T* qkv = (T*)(L + p.l_qkv);
+  T* o = (T*)(L + p.l_o);
+  float* lse = (float*)(L + p.l_lse);
+  T* m = (T*)(L + p.l_m);
+  float* r2 = (float*)(L + p.l_r2);
+  T* h = (T*)(L + p.l_h);
+  T* tmp = ctx->at<T>(p.gtmp);
+  T* big = ctx->at<T>(p.big);
+  hipStream_t s = ctx->stream;
+
+  // MLP: x2 = x1 + relu(h)^2 W2^T, h = m W1^T
+  NC_TRY(weight_grad(ctx, d, F, gr, d, h, F, 1, dW2, accumulate), "dW2");
+  GemmDesc g = gemm(N, F, d, gr, d, 0, W2, F, 1, EPI_DRELU2, big, F);
+  g.aux = h; g.ldaux = F;
+  NC_TRY(run_gemm(ctx, g), "dh = (g W2) * 2 relu(h)");
+  NC_TRY(weight_grad(ctx, F, d, big, F, m, d, 0, dW1, accumulate), "dW1");
+  NC_TRY(run_gemm(ctx, gemm(N, d, F, big, F, 0, W1, d, 1, EPI_STORE, tmp, d)), "dm = dh W1");
+  NC_TRY(rmsnorm_bwd<T>(m, r2, tmp, gr, N, d, 1, s), "rmsnorm backward (MLP input)");
+  // attention: x1 = x0 + o Wo^T
+  NC_TRY(weight_grad(ctx, d, d, gr, d, o, d, 0, dWo, accumulate), "dWo");
+  NC_TRY(run_gemm(ctx, gemm(N, d, d, gr, d, 0, Wo, d, 1, EPI_STORE, tmp, d)), "do = g Wo");
+  AttnDesc ad{};
+  ad.B = c.batch; ad.T = c.seq_len; ad.H = c.n_head; ad.Q = c.head_dim;
+  ad.qkv = qkv; ad.o = o; ad.lse = lse; ad.dout = tmp; ad.delta = ctx->at<float>(p.delta);
+  ad.dqkv = big; ad.rope = ctx->at<float2>(p.rope);
+  NC_TRY(attn_bwd<T>(ctx, ad), "attention backward");
+  NC_TRY(weight_grad(ctx, 3 * d, d, big, 3 * d, a, d, 0, dWqkv, accumulate), "dWqkv");
+  NC_TRY(run_gemm(ctx, gemm(N, d, 3 * d, big, 3 * d, 0, Wqkv, d, 1, EPI_STORE, tmp, d)), "da = dqkv Wqkv");
+  NC_TRY(rmsnorm_bwd<T>(a, r1, tmp, gr, N, d, 1, s), "rmsnorm backward (attention input)");
+  return NC_OK;
+}
+
+template <typename T>
+int model_forward(nc_ctx* ctx, const T* params, const int32_t* idx, const int32_t* tgt, float* ce_out) {
+  const nc_config& c = ctx->cfg;
+  const Plan& p = ctx->plan;
+  const int N = c.batch * c.seq_len, d = c.d_model, V = c.vocab;
+  hipStream_t s = ctx->stream;
+  int32_t* widx = ctx->at<int32_t>(p.idx);
+  int32_t* wtgt = ctx->at<int32_t>(p.tgt);
+  NC_TRY(copy_bytes(widx, idx, (size_t)N * 4, s), "copy token ids");
+  NC_TRY(copy_bytes(wtgt, tgt, (size_t)N * 4, s), "copy targets");
+  NC_TRY(count_valid(wtgt, N, ctx->at<float>(p.scalars), s), "count valid targets");
+  T* x = ctx->at<T>(p.x);
+  NC_TRY(embed_fwd<T>(params, widx, x, N, d, s), "embedding gather");
+  const T* w = params + (int64_t)V * d;
+  for (int l = 0; l < c.n_layer; ++l) {
+    int st = layer_forward<T>(ctx, l, w + (int64_t)l * layer_elems(c), x);
+    if (st != NC_OK) return st;
+  }
+  T* xf = ctx->at<T>(p.xf);
+  float* rf = ctx->at<float>(p.rf);
+  NC_TRY(rmsnorm_fwd<T>(x, xf, rf, N, d, c.rms_eps, s), "final rmsnorm");
+  const T* U = w + (int64_t)c.n_layer * layer_elems(c);
+  GemmDesc g = gemm(N, V, d, xf, d, 0, U, d, 0, EPI_LSE, nullptr, 0);
+  g.tgt = wtgt; g.lse_part = ctx->at<float2>(p.lse_part); g.lse_stride = p.head_nblk;
+  g.ztgt = ctx->at<float>(p.ztgt);
+  NC_TRY(run_gemm(ctx, g), "unembedding + log-sum-exp partials");
+  float* ce = ctx->at<float>(p.ce);
+  NC_TRY(ce_combine(g.lse_part, p.head_nblk, g.ztgt, wtgt, ctx->at<float>(p.lse_head), ce, N, s), "cross-entropy");
+  if (ce_out) NC_TRY(copy_bytes(ce_out, ce, (size_t)N * 4, s), "copy ce");
+  return NC_OK;
+}
+
+template <typename T>
+int model_backward(nc_ctx* ctx, const T* params, float* grads, int accumulate) {
+  const nc_config& c = ctx->cfg;
+  const Plan& p = ctx->plan;
+  const int N = c.batch * c.seq_len, d = c.d_model, V = c.vocab;
+  hipStream_t s = ctx->stream;
+  const T* w = params + (int64_t)V * d;
+  const T* U = w + (int64_t)c.n_layer * layer_elems(c);
+  float* dE = grads;
+  float* dw = grads + (int64_t)V * d;
+  float* dU = dw + (int64_t)c.n_layer * layer_elems(c);
+  T* xf = ctx->at<T>(p.xf);
+  T* gr = ctx->at<T>(p.g);
+  T* tmp = ctx->at<T>(p.gtmp);
+  T* dz = ctx->at<T>(p.dz);
+  const int32_t* wtgt = ctx->at<int32_t>(p.tgt);
+  // head, one token chunk at a time: dz = (softmax(z) - onehot) / n_valid,
+  // dxf = dz U, dU (+)= dz^T xf
+  for (int64_t r0 = 0; r0 < N; r0 += p.head_chunk) {
+    const int Mc = (int)std::min<int64_t>(p.head_chunk, N - r0);
+    GemmDesc g = gemm(Mc, V, d, xf + r0 * d, d, 0, U, d, 0, EPI_DZ, dz, V);
+    g.tgt = wtgt + r0; g.lse = ctx->at<float>(p.lse_head) + r0; g.inv_nvalid = ctx->at<float>(p.scalars);
+    NC_TRY(run_gemm(ctx, g), "recompute logits -> dz");
+    NC_TRY(run_gemm(ctx, gemm(Mc, d, V, dz, V, 0, U, d, 1, EPI_STORE, tmp + r0 * d, d)), "dxf = dz U");
+    g = gemm(V, d, Mc, dz, V, 1, xf + r0 * d, d, 1, EPI_F32, dU, d);
+    g.beta = (accumulate || r0 > 0) ? 1 : 0;
+    g.splits = choose_splits(c, V, d, Mc);
+    g.part = ctx->at<float>(p.part);
+    NC_TRY(run_gemm(ctx, g), "dU = dz^T xf");
+  }
+  NC_TRY(rmsnorm_bwd<T>(xf, ctx->at<float>(p.rf), tmp, gr, N, d, 0, s), "final rmsnorm backward");
+  for (int l = c.n_layer - 1; l >= 0; --l) {
+    int st = layer_backward<T>(ctx, l, w + (int64_t)l * layer_elems(c), gr, dw + (int64_t)l * layer_elems(c),
+                               accumulate);
+    if (st != NC_OK) return st;
+  }
+  if (!accumulate) NC_TRY(fill_f32(dE, (int64_t)V * d, 0.f, s), "zero dE");
+  NC_TRY(embed_bwd<T>(gr, ctx->at<int32_t>(p.idx), dE, N, d, s), "embedding scatter-add");
+  return NC_OK;
+}
+
+template <typename T>
+int block_forward(nc_ctx* ctx, const T* w, const T* x, T* y) {
+  const nc_config& c = ctx->cfg;
+  const size_t bytes = (size_t)c.batch * c.seq_len * c.d_model * sizeof(T);
+  NC_TRY(copy_bytes(y, x, bytes, ctx->stream), "copy block input");
+  return layer_forward<T>(ctx, 0, w, y);
+}
+
+template <typename T>
+int block_backward(nc_ctx* ctx, const T* w, const T* dy, T* dx, float* dparams, int accumulate) {
+  const nc_config& c = ctx->cfg;
+  const size_t bytes = (size_t)c.batch * c.seq_len * c.d_model * sizeof(T);
+  NC_TRY(copy_bytes(dx, dy, bytes, ctx->stream), "copy upstream gradient");
+  return layer_backward<T>(ctx, 0, w, dx, dparams, accumulate);
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+int64_t nc_param_count(const nc_config* cfg) {
+  int st = validate(cfg);
+  if (st != NC_OK) return st;
+  const int64_t per = layer_elems(*cfg) * cfg->n_layer;
+  return is_block(*cfg) ? per : per + 2LL * cfg->vocab * cfg->d_model;
+}
+
+int nc_param_offset(const nc_config* cfg, int32_t tensor, int32_t layer, int64_t* offset, int64_t* rows,
+                    int64_t* cols) {
+  int st = validate(cfg);
+  if (st != NC_OK) return st;
+  if (!offset || !rows || !cols) return NC_ERR_INVALID_ARG;
+  const int64_t d = cfg->d_model, F = cfg->d_ff, V = cfg->vocab;
+  const int64_t base = is_block(*cfg) ? 0 : V * d;
+  if (tensor == NC_T_E || tensor == NC_T_U) {
+    if (is_block(*cfg)) return NC_ERR_INVALID_ARG;
+    *rows = V; *cols = d;
+    *offset = tensor == NC_T_E ? 0 : base + layer_elems(*cfg) * cfg->n_layer;
+    return NC_OK;
+  }
+  if (tensor < NC_T_WQ || tensor > NC_T_W2 || layer < 0 || layer >= cfg->n_layer) return NC_ERR_INVALID_ARG;
+  int64_t off = base + layer_elems(*cfg) * layer;
+  const int64_t sizes[6][2] = {{d, d}, {d, d}, {d, d}, {d, d}, {F, d}, {d, F}};
+  for (int t = NC_T_WQ; t < tensor; ++t) off += sizes[t - NC_T_WQ][0] * sizes[t - NC_T_WQ][1];
+  *offset = off;
+  *rows = sizes[tensor - NC_T_WQ][0];
+  *cols = sizes[tensor - NC_T_WQ][1];
+  return NC_OK;
+}
+
+int64_t nc_workspace_bytes(const nc_config* cfg) {
+  int st = validate(cfg);
+  if (st != NC_OK) return st;
+  return (int64_t)make_plan(*cfg).total;
+}
+
+const char* nc_status_string(int status) {
+  switch (status) {
+    case NC_OK: return "ok";
+    case NC_ERR_INVALID_ARG: return "invalid argument";
+    case NC_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case NC_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case NC_ERR_STATE: return "call out of order";
+    case NC_ERR_HIP: return "HIP error";
+    case NC_ERR_UNSUPPORTED: return "not supported";
+    default: return "unknown status";
+  }
+}
+
+int nc_init(const nc_config* cfg, void* workspace, size_t ws_bytes, void* hip_stream, nc_ctx** out) {
+  if (!out) return NC_ERR_INVALID_ARG;
+  *out = nullptr;
+  int st = validate(cfg);
+  if (st != NC_OK) return st;
+  if (!workspace) return NC_ERR_INVALID_ARG;
+  Plan plan = make_plan(*cfg);
+  if (ws_bytes < plan.total || ((uintptr_t)workspace % kAlign) != 0) return NC_ERR_WORKSPACE;
+  nc_ctx* ctx = new (std::nothrow) nc_ctx();
+  if (!ctx) return NC_ERR_INVALID_ARG;
+  ctx->cfg = *cfg;
+  ctx->ws = (char*)workspace;
+  ctx->ws_bytes = ws_bytes;
+  ctx->stream = (hipStream_t)hip_stream;
+  ctx->plan = plan;
+  hipError_t e = rope_table(ctx->at<float2>(plan.rope), cfg->seq_len, cfg->head_dim, cfg->rope_base, ctx->stream);
+  if (e != hipSuccess) {
+    delete ctx;
+    return NC_ERR_HIP;
+  }
+  *out = ctx;
+  return NC_OK;
+}
+
+int nc_set_stream(nc_ctx* ctx, void* hip_stream) {
+  if (!ctx) return NC_ERR_INVALID_ARG;
+  ctx->stream = (hipStream_t)hip_stream;
+  return NC_OK;
+}
+
+void nc_destroy(nc_ctx* ctx) { delete ctx; }
+
+const char* nc_last_error(const nc_ctx* ctx) { return ctx ? ctx->err.c_str() : "null context"; }
+
+int nc_forward(nc_ctx* ctx, const void* params, const int32_t* idx, const int32_t* targets, float* ce_out) {
+  if (!ctx || !params || !idx || !targets) return NC_ERR_INVALID_ARG;
+  if (is_block(ctx->cfg)) return NC_ERR_STATE;
+  ctx->have_forward = false;
+  int st = is_bf16(ctx->cfg) ? model_forward<bf16>(ctx, (const bf16*)params, idx, targets, ce_out)
+                             : model_forward<float>(ctx, (const float*)params, idx, targets, ce_out);
+  ctx->have_forward = st == NC_OK;
+  return st;
+}
+
+int nc_loss_bpb(nc_ctx* ctx, const int32_t* token_bytes, double* out) {
+  if (!ctx || !token_bytes || !out) return NC_ERR_INVALID_ARG;
+  if (!ctx->have_forward) return NC_ERR_STATE;
+  const Plan& p = ctx->plan;
+  const int64_t N = (int64_t)ctx->cfg.batch * ctx->cfg.seq_len;
+  NC_TRY(loss_bpb(ctx->at<float>(p.ce), ctx->at<int32_t>(p.tgt), token_bytes, N, out, ctx->stream), "loss / bpb");
+  return NC_OK;
+}
+
+int nc_backward(nc_ctx* ctx, const void* params, float* grads, int32_t accumulate) {
+  if (!ctx || !params || !grads) return NC_ERR_INVALID_ARG;
+  if (accumulate != 0 && accumulate != 1) return NC_ERR_INVALID_ARG;
+  if (!ctx->have_forward) return NC_ERR_STATE;
+  return is_bf16(ctx->cfg) ? model_backward<bf16>(ctx, (const bf16*)params, grads, accumulate)
+                           : model_backward<float>(ctx, (const float*)params, grads, accumulate);
+}
+
+int nc_block_forward(nc_ctx* ctx, const void* block_params, const void* x, void* y) {
+  if (!ctx || !block_params || !x || !y) return NC_ERR_INVALID_ARG;
+  if (!is_block(ctx->cfg)) return NC_ERR_STATE;
+  if (x == y) return NC_ERR_INVALID_ARG;
+  ctx->have_block_forward = false;
+  int st = is_bf16(ctx->cfg) ? block_forward<bf16>(ctx, (const bf16*)block_params, (const bf16*)x, (bf16*)y)
+                             : block_forward<float>(ctx, (const float*)block_params, (const float*)x, (float*)y);
+  ctx->have_block_forward = st == NC_OK;
+  return st;
+}
+
+int nc_block_backward(nc_ctx* ctx, const void* block_params, const void* dy, void* dx, float* dparams,
+                      int32_t accumulate) {
+  if (!ctx || !block_params || !dy || !dx || !dparams) return NC_ERR_INVALID_ARG;
+  if (accumulate != 0 && accumulate != 1) return NC_ERR_INVALID_ARG;
+  if (!is_block(ctx->cfg) || !ctx->have_block_forward) return NC_ERR_STATE;
+  if (dy == dx) return NC_ERR_INVALID_ARG;
+  return is_bf16(ctx->cfg)
+             ? block_backward<bf16>(ctx, (const bf16*)block_params, (const bf16*)dy, (bf16*)dx, dparams, accumulate)
+             : block_backward<float>(ctx, (const float*)block_params, (const float*)dy, (float*)dx, dparams,
+                                     accumulate);
+}
+
+}  // extern "C"

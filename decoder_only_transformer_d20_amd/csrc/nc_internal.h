@@ -1,0 +1,118 @@
+// Internal declarations shared by the host library and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace nc {
+
+// ---------------------------------------------------------------------------
+// storage types
+// ---------------------------------------------------------------------------
+struct bf16 {
+  uint16_t x;
+};
+
+__host__ __device__ inline float to_f32(float v) { return v; }
+__host__ __device__ inline float to_f32(bf16 v) {
+  uint32_t u = (uint32_t)v.x << 16;
+  float f;
+  __builtin_memcpy(&f, &u, 4);
+  return f;
+}
+
+template <typename T> __host__ __device__ inline T from_f32(float f);
+template <> __host__ __device__ inline float from_f32<float>(float f) { return f; }
+// round to nearest, ties to even; NaN stays a quiet NaN
+template <> __host__ __device__ inline bf16 from_f32<bf16>(float f) {
+  uint32_t u;
+  __builtin_memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16{(uint16_t)0x7fc0};
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16{(uint16_t)(u >> 16)};
+}
+
+// ---------------------------------------------------------------------------
+// GEMM:  C[m][n] = sum_k P[m][k] * Q[n][k]       (m < M, n < N, k < K)
+// P is stored [M][K] (p_trans = 0) or [K][M] (p_trans = 1); likewise Q is
+// [N][K] or [K][N].  p_relu2 / q_relu2 replace the operand by relu(.)^2 as it
+// is loaded.  The epilogue decides what is written.
+// ---------------------------------------------------------------------------
+enum Epi {
+  EPI_STORE = 0,     // C(T) = acc
+  EPI_ROPE = 1,      // C(T) = acc, columns < rope_cols rotated in adjacent pairs
+  EPI_RESID = 2,     // C(T) = aux(T) + acc            (aux may alias C)
+  EPI_DRELU2 = 3,    // C(T) = acc * 2 relu(aux(T))
+  EPI_F32 = 4,       // C(f32) = (beta ? C : 0) + acc; with splits > 1, partials
+  EPI_LSE = 5,       // per-row (max, sum exp) of the N-tile -> lse_part; z[tgt] -> ztgt
+  EPI_DZ = 6,        // C(T) = (exp(acc - lse[m]) - [n == tgt[m]]) * inv_nvalid
+};
+
+struct GemmDesc {
+  int M, N, K;
+  const void* P; int64_t ldp; int p_trans; int p_relu2;
+  const void* Q; int64_t ldq; int q_trans; int q_relu2;
+  int epi;
+  void* C; int64_t ldc;
+  const void* aux; int64_t ldaux;
+  int beta;                 // EPI_F32: add to C
+  int splits;               // EPI_F32: split-K count (partials + reduce when > 1)
+  float* part;              // EPI_F32 split-K partials [splits][M][N]
+  // EPI_ROPE
+  const float2* rope;       // [T][head_dim/2] (cos, sin)
+  int rope_T, rope_cols, head_dim;
+  // EPI_LSE / EPI_DZ
+  const int32_t* tgt;       // [M]
+  float2* lse_part;         // [M][lse_stride]
+  int lse_stride;           // number of N-tiles
+  float* ztgt;              // [M]
+  const float* lse;         // [M]
+  const float* inv_nvalid;  // device scalar
+};
+
+// ---------------------------------------------------------------------------
+// attention on token-major qkv: row (b*T + t) holds [q | k | v], each H*Q
+// ---------------------------------------------------------------------------
+struct AttnDesc {
+  int B, T, H, Q;
+  const void* qkv;          // [B*T][3*H*Q], q and k already rotated
+  const void* o;            // [B*T][H*Q]
+  void* o_out;
+  float* lse;               // [B][H][T]
+  const void* dout;         // [B*T][H*Q]
+  float* delta;             // [B][H][T] rowsum(dO * O)
+  void* dqkv;               // [B*T][3*H*Q]
+  const float2* rope;       // inverse rotation of dq, dk on store; NULL = none
+};
+
+// ---------------------------------------------------------------------------
+// launchers (all enqueue on `s`; return hipError_t of the launch)
+// ---------------------------------------------------------------------------
+template <typename T> hipError_t gemm_portable(const GemmDesc& g, hipStream_t s);
+hipError_t gemm_mfma_bf16(const GemmDesc& g, hipStream_t s);
+bool gemm_mfma_supported(const GemmDesc& g);
+int gemm_mfma_tile_m(int M, int N);   // tile sizes the MFMA GEMM picks for an M x N output
+int gemm_mfma_tile_n(int M, int N);
+hipError_t splitk_reduce(const float* part, int splits, int64_t n, float* out, int beta, hipStream_t s);
+
+template <typename T> hipError_t attn_fwd_portable(const AttnDesc& a, hipStream_t s);
+template <typename T> hipError_t attn_bwd_portable(const AttnDesc& a, hipStream_t s);
+hipError_t attn_fwd_mfma(const AttnDesc& a, hipStream_t s);
+hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s);
+template <typename T> hipError_t attn_delta(const AttnDesc& a, hipStream_t s);
+
+template <typename T> hipError_t embed_fwd(const T* E, const int32_t* idx, T* x, int64_t n, int d, hipStream_t s);
+template <typename T> hipError_t embed_bwd(const T* g, const int32_t* idx, float* dE, int64_t n, int d, hipStream_t s);
+template <typename T> hipError_t rmsnorm_fwd(const T* x, T* y, float* r, int64_t rows, int d, float eps, hipStream_t s);
+template <typename T> hipError_t rmsnorm_bwd(const T* y, const float* r, const T* dy, T* dx_io, int64_t rows, int d,
+                                            int accumulate, hipStream_t s);
+hipError_t rope_table(float2* tab, int T, int Q, float base, hipStream_t s);
+hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int32_t* tgt,
+                      float* lse, float* ce, int64_t rows, hipStream_t s);
+hipError_t count_valid(const int32_t* tgt, int64_t n, float* inv_nvalid, hipStream_t s);
+hipError_t loss_bpb(const float* ce, const int32_t* tgt, const int32_t* bytes, int64_t n, double* out, hipStream_t s);
+hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
+hipError_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s);
+
+}  // namespace nc

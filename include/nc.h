@@ -1,0 +1,178 @@
+/*
+ * nc.h -- C ABI of the MI355X (gfx950) forward/backward library for the
+ * nanochat-style decoder-only Transformer (the "d20" model).
+ *
+ * What the library computes is one training step's forward pass, loss and
+ * backward pass of the model the nanochat speedrun walkthrough pretrains
+ * (lyylswood.com page "100 dollars, 8000 lines of code: a hand-built ChatGPT
+ * clone"): a Llama-like pre-norm decoder-only Transformer (introduction:
+ * the author's note on the architecture), trained on next-token prediction
+ * over packed rows (section Pretraining), 20 layers of 1280 channels and
+ * 10 heads of dimension 128 at d20 (Pretraining, the printed model summary),
+ * with no biases and no RMSNorm parameters and separate embedding and
+ * unembedding tensors (Pretraining, optimiser paragraph), reporting the loss
+ * also as bits per byte (Pretraining, bits-per-byte paragraph).
+ *
+ * Model, per row of T tokens (d = n_head * head_dim, F = d_ff, V = vocab):
+ *   x = E[idx]
+ *   per layer:  a = rms(x);  q,k,v = a Wq^T, a Wk^T, a Wv^T
+ *               q,k = rotary(q,k)   (pairs (2i,2i+1), angle t*base^(-2i/Q))
+ *               o = causal_softmax(q k^T / sqrt(Q)) v
+ *               x = x + o Wo^T
+ *               m = rms(x);  h = m W1^T;  x = x + relu(h)^2 W2^T
+ *   xf = rms(x);  z = xf U^T;  ce[t] = logsumexp(z[t]) - z[t, target[t]]
+ *   rms(x) = x / sqrt(mean(x^2) + eps)
+ *   loss = sum(ce) / n_valid;  bpb = sum(ce) / (ln 2 * sum(bytes[target]))
+ * A target of -1 is ignored (no loss, no bytes, no gradient).
+ *
+ * Conventions
+ *  - Every pointer argument named as device memory must point to memory of
+ *    the GPU that is current when nc_init is called.  The caller owns every
+ *    buffer, the workspace and the stream; the library allocates no device
+ *    memory and frees nothing it did not create (nc_ctx is a host object).
+ *  - Parameters (and their gradients) are one flat buffer each, in this
+ *    order: E [V,d]; for each layer Wq, Wk, Wv, Wo [d,d], W1 [F,d], W2 [d,F];
+ *    U [V,d].  Each matrix is row-major [out, in] and used as y = x W^T.
+ *    Wq, Wk, Wv are adjacent, forming one [3d, d] matrix.  In block-only mode
+ *    the buffer holds one layer's six tensors.
+ *  - Parameters and activations are stored in the configuration's dtype
+ *    (fp32 or bf16); every accumulation inside a kernel is fp32; row
+ *    statistics are fp32; gradients of parameters are always fp32.
+ *  - Activations are row-major [batch, seq_len, features] (token-major).
+ *  - Every call enqueues its work on the context's stream and returns
+ *    before the GPU finishes.  Outputs are valid once the stream is
+ *    synchronised.  Host-only queries make no HIP call.
+ *  - Host-side validation happens first; on failure nothing is enqueued.
+ *  - A context is not thread-safe: use one context per stream.
+ */
+#ifndef NC_H
+#define NC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NC_OK = 0,
+  NC_ERR_INVALID_ARG = -1,   /* null pointer, bad enum value, bad flag */
+  NC_ERR_SHAPE = -2,         /* dims not positive / not multiples of 64 / d != H*Q */
+  NC_ERR_WORKSPACE = -3,     /* workspace too small or misaligned */
+  NC_ERR_STATE = -4,         /* call out of order (e.g. backward before forward) */
+  NC_ERR_HIP = -5,           /* a HIP call or kernel launch failed; see nc_last_error */
+  NC_ERR_UNSUPPORTED = -6    /* valid but not supported by this build */
+} nc_status;
+
+typedef enum { NC_DTYPE_F32 = 0, NC_DTYPE_BF16 = 1 } nc_dtype;
+
+enum {
+  NC_FLAG_BLOCK_ONLY = 1,     /* one layer: no embedding, no head, no loss */
+  NC_FLAG_PORTABLE_KERNELS = 2 /* bf16 only: use the plain (non-MFMA) GEMM and
+                                 attention kernels, for cross-checking */
+};
+
+typedef struct {
+  int32_t n_layer;    /* L */
+  int32_t d_model;    /* d = n_head * head_dim */
+  int32_t n_head;     /* H */
+  int32_t head_dim;   /* Q, even */
+  int32_t d_ff;       /* F (4d in the reference model) */
+  int32_t vocab;      /* V (0 in block-only mode) */
+  int32_t batch;      /* B rows per step */
+  int32_t seq_len;    /* T tokens per row */
+  float rope_base;    /* 10000 */
+  float rms_eps;      /* 1e-6 */
+  int32_t dtype;      /* nc_dtype */
+  int32_t flags;      /* NC_FLAG_* */
+} nc_config;
+
+typedef struct nc_ctx nc_ctx;
+
+/* Tensor ids for nc_param_offset. */
+enum { NC_T_E = 0, NC_T_WQ, NC_T_WK, NC_T_WV, NC_T_WO, NC_T_W1, NC_T_W2, NC_T_U };
+
+/* ---- host-only queries (no HIP calls) --------------------------------- */
+
+/* Number of parameters: 12*L*d^2 + 2*V*d (560,988,160 at d20), or the six
+ * layer tensors in block-only mode.  Negative nc_status on a bad config. */
+int64_t nc_param_count(const nc_config* cfg);
+
+/* Offset (in elements) and shape of one tensor in the flat parameter /
+ * gradient buffer.  layer is ignored for E and U.  Returns nc_status. */
+int nc_param_offset(const nc_config* cfg, int32_t tensor, int32_t layer,
+                    int64_t* offset, int64_t* rows, int64_t* cols);
+
+/* Bytes of device workspace nc_init needs for this config (saved
+ * activations, the rotary table, loss partials, backward scratch).  The
+ * workspace must be 256-byte aligned.  Negative nc_status on a bad config. */
+int64_t nc_workspace_bytes(const nc_config* cfg);
+
+/* Static text for a status code. */
+const char* nc_status_string(int status);
+
+/* ---- context ------------------------------------------------------------ */
+
+/* Validate cfg, bind the workspace (device, >= nc_workspace_bytes(cfg)) and
+ * the HIP stream (hipStream_t; NULL = the default stream), and enqueue the
+ * fill of the rotary table.  *out receives a host object owned by the
+ * caller (release with nc_destroy).  Returns nc_status. */
+int nc_init(const nc_config* cfg, void* workspace, size_t ws_bytes,
+            void* hip_stream, nc_ctx** out);
+
+/* Switch the stream later calls enqueue on. */
+int nc_set_stream(nc_ctx* ctx, void* hip_stream);
+
+void nc_destroy(nc_ctx* ctx);
+
+/* Text of the last error on this context ("" if none). */
+const char* nc_last_error(const nc_ctx* ctx);
+
+/* ---- full model ------------------------------------------------------------ */
+
+/* Forward pass over B x T tokens.
+ *   params  device, dtype, [nc_param_count]
+ *   idx     device int32 [B*T], token ids in [0, V)
+ *   targets device int32 [B*T], next-token ids in [0, V) or -1 (ignored)
+ *   ce_out  device fp32 [B*T] per-token cross-entropy in nats (0 where the
+ *           target is ignored), or NULL
+ * idx and targets are copied into the workspace, and every activation the
+ * backward pass needs is saved there.  Ids outside [0, V) are undefined
+ * behaviour.  Not available in block-only mode (NC_ERR_STATE). */
+int nc_forward(nc_ctx* ctx, const void* params, const int32_t* idx,
+               const int32_t* targets, float* ce_out);
+
+/* Loss and bits per byte of the last nc_forward.
+ *   token_bytes device int32 [V], UTF-8 bytes of each vocabulary id
+ *   out         device double [5]: mean ce in nats, bits per byte,
+ *               sum of ce, sum of target bytes, number of valid targets.
+ * Sums run in fp64 over the per-token fp32 ce (deterministic order).
+ * NC_ERR_STATE without a prior nc_forward. */
+int nc_loss_bpb(nc_ctx* ctx, const int32_t* token_bytes, double* out);
+
+/* Gradient of the mean cross-entropy of the last nc_forward with respect to
+ * every parameter, fp32, written to grads (device fp32 [nc_param_count]),
+ * overwriting it (accumulate = 0) or adding to it (accumulate = 1).
+ * params must be the buffer passed to nc_forward, unchanged.  NC_ERR_STATE
+ * without a prior nc_forward.  Embedding rows are accumulated with fp32
+ * atomics, so their low bits may differ from run to run; everything else is
+ * deterministic. */
+int nc_backward(nc_ctx* ctx, const void* params, float* grads, int32_t accumulate);
+
+/* ---- single block (NC_FLAG_BLOCK_ONLY) ------------------------------------ */
+
+/* y = block(x) for x, y device dtype [B*T, d] (may not alias).  Saves what
+ * nc_block_backward needs.  NC_ERR_STATE unless the config is block-only. */
+int nc_block_forward(nc_ctx* ctx, const void* block_params, const void* x, void* y);
+
+/* Vector-Jacobian product of the last nc_block_forward with dy (device dtype
+ * [B*T, d]): dx (device dtype [B*T, d]) and the six weight gradients
+ * (device fp32, flat, block layout), overwritten or accumulated. */
+int nc_block_backward(nc_ctx* ctx, const void* block_params, const void* dy,
+                      void* dx, float* dparams, int32_t accumulate);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NC_H */

@@ -1,0 +1,87 @@
+/*
+ * nc_ops.h -- component entry points of the d20 forward/backward library.
+ *
+ * Each call runs one kernel family of the training step on caller-owned
+ * device buffers, so that a component can be checked against its plain
+ * definition and timed on its own.  The model-level calls in nc.h are built
+ * from exactly these kernels.  Conventions as in nc.h: device pointers, the
+ * caller owns every buffer, the work is enqueued on `hip_stream` (NULL = the
+ * default stream), nothing is allocated, host checks run first and enqueue
+ * nothing on failure.  dtype is an nc_dtype; "T" below means fp32 or bf16
+ * storage accordingly.  `portable` = 1 selects the plain (non-MFMA) kernels.
+ */
+#ifndef NC_OPS_H
+#define NC_OPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "nc.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Matrix product C[m][n] = sum_k P[m][k] * Q[n][k]   (the linear layers,
+ * y = x W^T, of the speedrun walkthrough's Transformer, section Pretraining).
+ *   P    T [M][K] row-major, or [K][M] when p_trans = 1
+ *   Q    T [N][K] row-major, or [K][N] when q_trans = 1
+ *   C    fp32 [M][N] (out_f32 = 1, written with plain stores) or T [M][N]
+ *        (out_f32 = 0, rounded to T)
+ *   splits  split-K factor (out_f32 = 1 only); splits > 1 needs `part`,
+ *        fp32 scratch of splits*M*N elements, reduced in a fixed order.
+ * M, N multiples of 64; K a multiple of 64*splits. */
+int nc_op_matmul(int32_t dtype, int32_t p_trans, int32_t q_trans, int64_t M, int64_t N, int64_t K,
+                 const void* P, const void* Q, void* C, int32_t out_f32, int32_t splits, float* part,
+                 int32_t portable, void* hip_stream);
+
+/* Parameter-free RMSNorm (section Pretraining: no RMSNorm parameters):
+ * y = x / sqrt(mean(x^2) + eps) per row; r = the per-row factor (fp32).
+ *   x, y T [rows][d];  r fp32 [rows]. */
+int nc_op_rmsnorm_fwd(int32_t dtype, int64_t rows, int32_t d, float eps, const void* x, void* y, float* r,
+                      void* hip_stream);
+
+/* Its reverse mode from the saved output: dx = r * (dy - y * mean(dy * y));
+ * dx_io receives dx (accumulate = 0) or dx_io + dx (accumulate = 1). */
+int nc_op_rmsnorm_bwd(int32_t dtype, int64_t rows, int32_t d, const void* y, const float* r, const void* dy,
+                      void* dx_io, int32_t accumulate, void* hip_stream);
+
+/* Rotary table tab[t][i] = (cos, sin)(t * base^(-2i/Q)), fp32 [T][Q/2][2],
+ * computed in fp64 and rounded once. */
+int nc_op_rope_table(int32_t T, int32_t Q, float base, float* tab, void* hip_stream);
+
+/* Causal attention forward over token-major qkv.
+ *   qkv  T [B*T][3*H*Q]: per token q | k | v (q, k already rotated)
+ *   o    T [B*T][H*Q];  lse fp32 [B][H][T] (log-sum-exp of the scaled scores) */
+int nc_op_attention_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t Q, const void* qkv, void* o,
+                        float* lse, int32_t portable, void* hip_stream);
+
+/* Causal attention backward.
+ *   dout T [B*T][H*Q];  delta fp32 [B][H][T] scratch (rowsum(dO * O));
+ *   dqkv T [B*T][3*H*Q] receives dq | dk | dv; when rope_tab (fp32
+ *   [T][Q/2][2]) is non-NULL, dq and dk are rotated back by -angle. */
+int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t Q, const void* qkv, const void* o,
+                        const void* dout, const float* lse, float* delta, void* dqkv, const float* rope_tab,
+                        int32_t portable, void* hip_stream);
+
+/* Embedding gather x[n] = E[idx[n]] (T [V][d] -> T [n][d]) and scatter-add
+ * dE[idx[n]] += g[n] (fp32 dE, accumulated with atomics). */
+int nc_op_embed_fwd(int32_t dtype, int64_t n, int32_t d, const void* E, const int32_t* idx, void* x,
+                    void* hip_stream);
+int nc_op_embed_bwd(int32_t dtype, int64_t n, int32_t d, const void* g, const int32_t* idx, float* dE,
+                    void* hip_stream);
+
+/* Fused unembedding + log-softmax + cross-entropy, forward only:
+ * ce[n] = logsumexp_v(xf[n] . U[v]) - xf[n] . U[tgt[n]] (0 where tgt < 0),
+ * lse[n] the log-sum-exp, without storing the logits.
+ *   xf T [n][d], U T [V][d], tgt int32 [n], ce, lse fp32 [n]
+ *   scratch: fp32 device scratch of nc_op_head_scratch_bytes(...) bytes */
+int64_t nc_op_head_scratch_bytes(int32_t dtype, int64_t n, int32_t d, int32_t V, int32_t portable);
+int nc_op_head_ce_fwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void* xf, const void* U,
+                      const int32_t* tgt, float* ce, float* lse, void* scratch, int32_t portable,
+                      void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NC_OPS_H */

@@ -1,0 +1,198 @@
+"""End-to-end parity of the training step on the GPU (nc_forward, nc_loss_bpb,
+nc_backward, nc_block_*) against the fp64 oracle on the same seeded inputs.
+
+Tolerances: fp32 configuration -- max relative error <= 1e-4 on loss, bpb
+and every gradient tensor (max_i |g - g*| / max_i |g*|); bf16
+configurations -- loss and bpb within 1e-2 relative, cosine similarity
+>= 0.999 for every parameter-gradient tensor (and dx / y in block mode)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synthdata
+from _util import dev, host, empty, max_rel_err, cosine, flat_tensors
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import decoder_only_transformer_d20_amd as nc  # noqa: E402
+
+
+def _inputs(cfg, rows=None, ignore=()):
+    params = synthdata.make_params(cfg)
+    idx, tgt = synthdata.make_tokens(cfg, rows=rows)
+    tgt = tgt.copy()
+    for (b, t) in ignore:
+        tgt[b, t] = -1
+    tb = synthdata.make_token_bytes(cfg)
+    c = cfg.with_(batch=idx.shape[0])
+    return c, params, idx, tgt, tb
+
+
+def _gpu_step(cfg, params, idx, tgt, tb, portable=False, grads=True):
+    sess = nc.Session(cfg, portable=portable)
+    P = dev(params, cfg.dtype)
+    ce = empty((idx.size,), "f32")
+    out = empty((5,), "f64")
+    sess.forward(P, dev(idx.ravel()), dev(tgt.ravel()), ce)
+    sess.loss_bpb(dev(tb), out)
+    g = None
+    if grads:
+        g = empty((params.size,), "f32")
+        sess.backward(P, g)
+    torch.cuda.synchronize()
+    res = dict(ce=host(ce).reshape(idx.shape), out=host(out))
+    if grads:
+        res["grads"] = host(g)
+    return res
+
+
+def _oracle_step(cfg, params, idx, tgt, tb, **kw):
+    return oracle.train_step(cfg, synthdata.split_params(cfg, params.astype(np.float64)), idx, tgt, tb, **kw)
+
+
+def test_tiny_fp32_matches_oracle():
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("tiny"), ignore=[(1, 5), (0, 63)])
+    got = _gpu_step(cfg, params, idx, tgt, tb)
+    want = _oracle_step(cfg, params, idx, tgt, tb)
+    assert max_rel_err(got["ce"], want["ce"]) <= 1e-4
+    assert abs(got["out"][0] - want["loss"]) / want["loss"] <= 1e-4
+    assert abs(got["out"][1] - want["bpb"]) / want["bpb"] <= 1e-4
+    assert got["out"][4] == np.sum(tgt >= 0)
+    for (name, layer, g), (_, _, w) in zip(flat_tensors(cfg, got["grads"]), flat_tensors(cfg, want["grads"])):
+        assert max_rel_err(g, w) <= 1e-4, (name, layer, max_rel_err(g, w))
+
+
+def test_tiny_fp32_accumulate_doubles():
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("tiny"))
+    sess = nc.Session(cfg)
+    P = dev(params, "f32")
+    sess.forward(P, dev(idx.ravel()), dev(tgt.ravel()))
+    g = empty((params.size,), "f32")
+    sess.backward(P, g)
+    g1 = host(g)
+    sess.backward(P, g, accumulate=True)
+    torch.cuda.synchronize()
+    # embedding rows are summed with atomics in no fixed order: compare
+    # against the tensor's scale rather than element by element
+    assert max_rel_err(host(g), 2 * g1) <= 1e-6
+    nE = cfg.vocab * cfg.d_model
+    np.testing.assert_array_equal(host(g)[nE:], 2 * g1[nE:])
+
+
+def test_state_errors_on_device():
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("tiny"))
+    sess = nc.Session(cfg)
+    P = dev(params, "f32")
+    g = empty((params.size,), "f32")
+    with pytest.raises(nc.NcError) as e:
+        sess.backward(P, g)
+    assert e.value.status == -4
+    with pytest.raises(nc.NcError) as e:
+        sess.loss_bpb(dev(tb), empty((5,), "f64"))
+    assert e.value.status == -4
+    with pytest.raises(nc.NcError) as e:
+        sess.block_forward(P, P, g)
+    assert e.value.status == -4
+
+
+@pytest.mark.parametrize("portable", [False, True])
+def test_small_bf16_matches_oracle(portable):
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("small"), ignore=[(3, 100)])
+    got = _gpu_step(cfg, params, idx, tgt, tb, portable=portable)
+    want = _oracle_step(cfg, params, idx, tgt, tb)
+    assert abs(got["out"][0] - want["loss"]) / want["loss"] <= 1e-2
+    assert abs(got["out"][1] - want["bpb"]) / want["bpb"] <= 1e-2
+    assert np.max(np.abs(got["ce"] - want["ce"])) <= 0.05
+    for (name, layer, g), (_, _, w) in zip(flat_tensors(cfg, got["grads"]), flat_tensors(cfg, want["grads"])):
+        assert cosine(g, w) >= 0.999, (name, layer, cosine(g, w))
+
+
+def test_small_bf16_deterministic():
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("small"))
+    a = _gpu_step(cfg, params, idx, tgt, tb)
+    b = _gpu_step(cfg, params, idx, tgt, tb)
+    np.testing.assert_array_equal(a["ce"], b["ce"])
+    np.testing.assert_array_equal(a["out"], b["out"])
+    nE = cfg.vocab * cfg.d_model     # embedding rows use atomics: compare the rest bitwise
+    np.testing.assert_array_equal(a["grads"][nE:], b["grads"][nE:])
+    np.testing.assert_allclose(a["grads"][:nE], b["grads"][:nE], rtol=1e-5, atol=1e-9)
+
+
+def _block_inputs(rows):
+    cfg = synthdata.get_config("block")
+    params = synthdata.make_params(cfg)
+    x, dy = synthdata.make_block_io(cfg, rows=rows)
+    return cfg.with_(batch=x.shape[0]), params, x, dy
+
+
+def _gpu_block(cfg, params, x, dy):
+    sess = nc.Session(cfg)
+    P = dev(params, "bf16")
+    y = empty(x.shape, "bf16")
+    dx = empty(x.shape, "bf16")
+    g = empty((params.size,), "f32")
+    sess.block_forward(P, dev(x, "bf16"), y)
+    sess.block_backward(P, dev(dy, "bf16"), dx, g)
+    torch.cuda.synchronize()
+    return host(y, "bf16"), host(dx, "bf16"), host(g)
+
+
+def test_block_real_shape_two_rows():
+    """One d20 layer at its real width and row length (2 rows of 2048)."""
+    cfg, params, x, dy = _block_inputs(rows=2)
+    y, dx, g = _gpu_block(cfg, params, x, dy)
+    lp = synthdata.split_params(cfg, params)["layers"][0]
+    want = oracle.block_step(cfg, lp, x, dy)
+    assert cosine(y - x, want["y"] - x) >= 0.999       # the block's own contribution
+    assert max_rel_err(y, want["y"]) <= 2e-2
+    assert cosine(dx, want["dx"]) >= 0.999
+    for name, layer, gt in flat_tensors(cfg, g):
+        assert cosine(gt, want["grads"][name]) >= 0.999, name
+
+
+@pytest.mark.slow
+def test_block_full_batch_sampled_rows():
+    """The block at the full 32 x 2048 launch; rows 0 and 31 against the
+    oracle (rows are independent in y and dx)."""
+    cfg, params, x, dy = _block_inputs(rows=None)
+    y, dx, g = _gpu_block(cfg, params, x, dy)
+    lp = synthdata.split_params(cfg, params)["layers"][0]
+    want = oracle.block_step(cfg, lp, x[[0, 31]], dy[[0, 31]])
+    for i, b in enumerate((0, 31)):
+        assert cosine(y[b] - x[b], want["y"][i] - x[b]) >= 0.999
+        assert cosine(dx[b], want["dx"][i]) >= 0.999
+    assert np.all(np.isfinite(g))
+
+
+@pytest.mark.slow
+def test_d20_one_row_matches_oracle():
+    """The full d20 model (20 layers, vocab 65,536) on one 2048-token row."""
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("d20"), rows=1)
+    got = _gpu_step(cfg, params, idx, tgt, tb)
+    want = _oracle_step(cfg, params, idx, tgt, tb)
+    assert abs(got["out"][0] - want["loss"]) / want["loss"] <= 1e-2
+    assert abs(got["out"][1] - want["bpb"]) / want["bpb"] <= 1e-2
+    for (name, layer, g), (_, _, w) in zip(flat_tensors(cfg, got["grads"]), flat_tensors(cfg, want["grads"])):
+        assert cosine(g, w) >= 0.999, (name, layer, cosine(g, w))
+
+
+@pytest.mark.slow
+def test_d20_full_batch_consistency():
+    """The benchmarked launch (32 x 2048): row 0's losses equal those of the
+    one-row run (rows never interact and every reduction order is fixed per
+    output element), loss and bpb follow from the per-token ce, and every
+    gradient is finite."""
+    cfg1, params, idx1, tgt1, tb = _inputs(synthdata.get_config("d20"), rows=1)
+    one = _gpu_step(cfg1, params, idx1, tgt1, tb, grads=False)
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("d20"))
+    full = _gpu_step(cfg, params, idx, tgt, tb)
+    np.testing.assert_array_equal(full["ce"][0], one["ce"][0])
+    s = full["ce"].astype(np.float64).sum()
+    assert full["out"][0] == pytest.approx(s / idx.size, rel=1e-9)
+    assert full["out"][1] == pytest.approx(s / (math.log(2) * tb[tgt].sum()), rel=1e-9)
+    assert np.all(np.isfinite(full["grads"]))
+    # near-uniform predictions at init: loss close to ln V
+    assert abs(full["out"][0] - math.log(cfg.vocab)) < 2.0

@@ -1,0 +1,268 @@
+"""Per-kernel parity on the GPU, through the C ABI (include/nc_ops.h), against
+the fp64 oracle's component functions on the same seeded inputs.
+
+Matrix products are checked bit-exactly on small-integer inputs (every
+product and every fp32 partial sum is then exact, so any layout, tiling or
+reduction-order bug shows up as a wrong integer).  bf16 outputs are compared
+with the round-to-nearest-even of the exact result.  Floating-point
+components use the fp32-mode bar (max relative error <= 1e-5 for fp32
+storage) or a bound derived from bf16 output rounding (2^-8 relative per
+element -> max relative error <= 1e-2, cosine >= 0.9999)."""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp
+
+import oracle
+import synthdata
+from _util import dev, host, empty, zeros, max_rel_err, cosine
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import decoder_only_transformer_d20_amd as nc  # noqa: E402
+
+DT = {"f32": 0, "bf16": 1}
+
+
+def _ints(rng, shape, lo=-3, hi=3):
+    return rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# matrix products
+# ---------------------------------------------------------------------------
+MM_CASES = [
+    # dtype, portable, M, N, K  (several tiles of every kernel + ragged tails)
+    ("f32", 1, 320, 192, 384),
+    ("bf16", 1, 320, 192, 384),
+    ("bf16", 0, 384, 640, 320),      # 128 x 128 tiles
+    ("bf16", 0, 768, 1280, 640),     # 256 x 256 tiles
+    ("bf16", 0, 512, 384, 2048),     # 256 x 128 tiles
+]
+
+
+@pytest.mark.parametrize("dtype,portable,M,N,K", MM_CASES)
+@pytest.mark.parametrize("pt,qt", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_matmul_exact_integers(dtype, portable, M, N, K, pt, qt):
+    rng = np.random.default_rng(100 + M + 7 * pt + 3 * qt)
+    P = _ints(rng, (M, K))
+    Q = _ints(rng, (N, K))
+    want = P.astype(np.int64) @ Q.astype(np.int64).T
+    Pd = dev(P.T.copy() if pt else P, dtype)
+    Qd = dev(Q.T.copy() if qt else Q, dtype)
+    C = empty((M, N), "f32")
+    nc.ops.matmul(DT[dtype], pt, qt, M, N, K, Pd, Qd, C, 1, 1, None, portable, None)
+    _sync()
+    np.testing.assert_array_equal(host(C), want)
+    # stored in the operand dtype: the RNE rounding of the exact result
+    Cs = empty((M, N), dtype)
+    nc.ops.matmul(DT[dtype], pt, qt, M, N, K, Pd, Qd, Cs, 0, 1, None, portable, None)
+    _sync()
+    wantr = want.astype(np.float32)
+    if dtype == "bf16":
+        wantr = synthdata.round_to_bf16(wantr)
+    np.testing.assert_array_equal(host(Cs, dtype), wantr)
+
+
+@pytest.mark.parametrize("dtype,portable", [("f32", 1), ("bf16", 1), ("bf16", 0)])
+def test_matmul_split_k_exact(dtype, portable):
+    rng = np.random.default_rng(7)
+    M, N, K, S = 256, 384, 4096, 4
+    P = _ints(rng, (K, M))     # stored [K][M]: the weight-gradient layout
+    Q = _ints(rng, (K, N))
+    want = P.astype(np.int64).T @ Q.astype(np.int64)
+    C = empty((M, N), "f32")
+    part = empty((S * M * N,), "f32")
+    nc.ops.matmul(DT[dtype], 1, 1, M, N, K, dev(P, dtype), dev(Q, dtype), C, 1, S, part, portable, None)
+    _sync()
+    np.testing.assert_array_equal(host(C), want)
+
+
+def test_matmul_full_size_sampled_rows():
+    """The d20 QKV product at its real shape (65,536 x 3,840 x 1,280), checked
+    exactly on sampled rows."""
+    rng = np.random.default_rng(8)
+    M, N, K = 65536, 3840, 1280
+    P = _ints(rng, (M, K), -2, 2)
+    Q = _ints(rng, (N, K), -2, 2)
+    C = empty((M, N), "f32")
+    nc.ops.matmul(1, 0, 0, M, N, K, dev(P, "bf16"), dev(Q, "bf16"), C, 1, 1, None, 0, None)
+    _sync()
+    rows = np.concatenate([[0, M - 1], rng.choice(M, 30, replace=False)])
+    got = host(C[torch.from_numpy(rows).cuda()])
+    np.testing.assert_array_equal(got, P[rows].astype(np.int64) @ Q.astype(np.int64).T)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,rows,d", [("f32", 130, 128), ("bf16", 300, 1280), ("bf16", 68, 1920)])
+def test_rmsnorm_fwd_bwd(dtype, rows, d):
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((rows, d)).astype(np.float32) * 2.5
+    dy = rng.standard_normal((rows, d)).astype(np.float32)
+    res = rng.standard_normal((rows, d)).astype(np.float32)
+    if dtype == "bf16":
+        x, dy, res = (synthdata.round_to_bf16(a) for a in (x, dy, res))
+    eps = 1e-6
+    y_want, r_want = oracle.rmsnorm(x.astype(np.float64), eps)
+    xd, yd, rd = dev(x, dtype), empty((rows, d), dtype), empty((rows,), "f32")
+    nc.ops.rmsnorm_fwd(DT[dtype], rows, d, eps, xd, yd, rd, None)
+    _sync()
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    assert max_rel_err(host(rd), r_want) <= 1e-6
+    assert max_rel_err(host(yd, dtype), y_want) <= tol
+    # backward from the kernel's own stored y and r, with and without residual
+    y_used = host(yd, dtype)
+    dx_want = oracle.rmsnorm_bwd(y_used, host(rd), dy.astype(np.float64))
+    for acc in (0, 1):
+        io = dev(res, dtype)
+        nc.ops.rmsnorm_bwd(DT[dtype], rows, d, yd, rd, dev(dy, dtype), io, acc, None)
+        _sync()
+        want = dx_want + (res if acc else 0)
+        assert max_rel_err(host(io, dtype), want) <= tol
+        assert cosine(host(io, dtype), want) >= 0.9999
+
+
+# ---------------------------------------------------------------------------
+# rotary table
+# ---------------------------------------------------------------------------
+def test_rope_table_matches_fp64_angles():
+    T, Q = 2048, 128
+    tab = empty((T, Q // 2, 2), "f32")
+    nc.ops.rope_table(T, Q, 10000.0, tab, None)
+    _sync()
+    phi = oracle.rope_angles(T, Q, 10000.0)
+    got = host(tab)
+    assert np.max(np.abs(got[..., 0] - np.cos(phi))) <= 1e-7
+    assert np.max(np.abs(got[..., 1] - np.sin(phi))) <= 1e-7
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+ATT_CASES = [
+    # dtype, portable, B, T, H, Q
+    ("f32", 1, 2, 128, 2, 64),
+    ("bf16", 1, 2, 192, 2, 128),
+    ("bf16", 0, 2, 192, 2, 128),
+    ("bf16", 0, 1, 640, 3, 128),
+]
+
+
+def _qkv(rng, B, T, H, Q, dtype):
+    a = rng.standard_normal((B, T, 3, H, Q)).astype(np.float32)
+    return synthdata.round_to_bf16(a) if dtype == "bf16" else a
+
+
+@pytest.mark.parametrize("dtype,portable,B,T,H,Q", ATT_CASES)
+def test_attention_fwd(dtype, portable, B, T, H, Q):
+    rng = np.random.default_rng(10 + T)
+    qkv = _qkv(rng, B, T, H, Q, dtype)
+    o = empty((B, T, H, Q), dtype)
+    lse = empty((B, H, T), "f32")
+    nc.ops.attention_fwd(DT[dtype], B, T, H, Q, dev(qkv, dtype), o, lse, portable, None)
+    _sync()
+    og, lg = host(o, dtype), host(lse)
+    tol = 1e-5 if dtype == "f32" else 1e-2
+    for b in range(B):
+        q, k, v = (qkv[b, :, i].astype(np.float64) for i in range(3))
+        want = oracle.causal_attention(q, k, v)
+        assert max_rel_err(og[b], want) <= tol
+        assert cosine(og[b], want) >= 0.99995
+        for h in range(H):
+            S = q[:, h] @ k[:, h].T / math.sqrt(Q)
+            S[np.triu(np.ones((T, T), bool), 1)] = -np.inf
+            np.testing.assert_allclose(lg[b, h], logsumexp(S, axis=1), rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype,portable,B,T,H,Q", ATT_CASES)
+@pytest.mark.parametrize("with_rope", [0, 1])
+def test_attention_bwd(dtype, portable, B, T, H, Q, with_rope):
+    rng = np.random.default_rng(20 + T)
+    qkv = _qkv(rng, B, T, H, Q, dtype)
+    dout = rng.standard_normal((B, T, H, Q)).astype(np.float32)
+    if dtype == "bf16":
+        dout = synthdata.round_to_bf16(dout)
+    qkvd = dev(qkv, dtype)
+    o = empty((B, T, H, Q), dtype)
+    lse = empty((B, H, T), "f32")
+    nc.ops.attention_fwd(DT[dtype], B, T, H, Q, qkvd, o, lse, portable, None)
+    tab = empty((T, Q // 2, 2), "f32")
+    nc.ops.rope_table(T, Q, 10000.0, tab, None)
+    delta = empty((B, H, T), "f32")
+    dqkv = zeros((B, T, 3, H, Q), dtype)
+    nc.ops.attention_bwd(DT[dtype], B, T, H, Q, qkvd, o, dev(dout, dtype), lse, delta, dqkv,
+                         tab if with_rope else None, portable, None)
+    _sync()
+    got = host(dqkv, dtype)
+    phi = oracle.rope_angles(T, Q, 10000.0)
+    tol = 1e-4 if dtype == "f32" else 2e-2
+    for b in range(B):
+        q, k, v = (qkv[b, :, i].astype(np.float64) for i in range(3))
+        dq, dk, dv = oracle.causal_attention_bwd(q, k, v, dout[b].astype(np.float64))
+        if with_rope:
+            dq, dk = oracle.rope(dq, phi, inverse=True), oracle.rope(dk, phi, inverse=True)
+        for i, want in enumerate((dq, dk, dv)):
+            assert max_rel_err(got[b, :, i], want) <= tol, ("dq", "dk", "dv")[i]
+            assert cosine(got[b, :, i], want) >= 0.9999, ("dq", "dk", "dv")[i]
+
+
+# ---------------------------------------------------------------------------
+# embedding
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 1280)])
+def test_embedding_gather_bitwise_and_scatter_add(dtype, d):
+    rng = np.random.default_rng(30)
+    V, n = 512, 1000
+    E = rng.standard_normal((V, d)).astype(np.float32)
+    if dtype == "bf16":
+        E = synthdata.round_to_bf16(E)
+    cfg = synthdata.get_config("small")
+    idx = synthdata.make_tokens(cfg)[0].ravel()[:n] % V     # Zipf: hot rows repeat
+    x = empty((n, d), dtype)
+    nc.ops.embed_fwd(DT[dtype], n, d, dev(E, dtype), dev(idx), x, None)
+    _sync()
+    np.testing.assert_array_equal(host(x, dtype), E[idx])
+    g = rng.standard_normal((n, d)).astype(np.float32)
+    if dtype == "bf16":
+        g = synthdata.round_to_bf16(g)
+    dE = zeros((V, d), "f32")
+    nc.ops.embed_bwd(DT[dtype], n, d, dev(g, dtype), dev(idx), dE, None)
+    _sync()
+    want = np.zeros((V, d))
+    np.add.at(want, idx, g.astype(np.float64))
+    assert max_rel_err(host(dE), want) <= 1e-6
+    assert np.all(host(dE)[np.setdiff1d(np.arange(V), idx)] == 0)
+
+
+# ---------------------------------------------------------------------------
+# fused unembedding + cross-entropy
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,portable,n,d,V", [("f32", 1, 128, 128, 512), ("bf16", 1, 256, 256, 640),
+                                                  ("bf16", 0, 256, 256, 640), ("bf16", 0, 512, 1280, 4096)])
+def test_head_ce_forward(dtype, portable, n, d, V):
+    rng = np.random.default_rng(40)
+    xf = rng.standard_normal((n, d)).astype(np.float32)
+    U = (rng.standard_normal((V, d)) / math.sqrt(d)).astype(np.float32) * 3
+    if dtype == "bf16":
+        xf, U = synthdata.round_to_bf16(xf), synthdata.round_to_bf16(U)
+    tgt = rng.integers(0, V, size=n).astype(np.int32)
+    tgt[5] = -1
+    tgt[7] = V - 1
+    tgt[9] = 0
+    ce, lse = empty((n,), "f32"), empty((n,), "f32")
+    scratch = empty((nc.ops.head_scratch_bytes(DT[dtype], n, d, V, portable) // 4 + 1,), "f32")
+    nc.ops.head_ce_fwd(DT[dtype], n, d, V, dev(xf, dtype), dev(U, dtype), dev(tgt), ce, lse, scratch, portable, None)
+    _sync()
+    z = xf.astype(np.float64) @ U.astype(np.float64).T
+    want = oracle.cross_entropy(z, tgt)
+    np.testing.assert_allclose(host(ce), want, rtol=1e-5, atol=2e-5)
+    np.testing.assert_allclose(host(lse), logsumexp(z, axis=1), rtol=1e-5, atol=2e-5)
+    assert host(ce)[5] == 0.0

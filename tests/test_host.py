@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, every
+function include/*.h declares is exported, the flat parameter layout agrees
+with the seeded generators' layout, and invalid arguments are rejected before
+any HIP call."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import synthdata
+import decoder_only_transformer_d20_amd as nc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        txt = open(h).read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        names |= set(re.findall(r"\b(nc_[a-z0-9_]+)\s*\(", txt))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    L = ctypes.CDLL(nc.LIB_PATH)
+    declared = _declared_functions()
+    assert len(declared) >= 20
+    missing = [n for n in sorted(declared) if not hasattr(L, n)]
+    assert not missing, missing
+    # and the binding wraps every one of them
+    assert declared <= set(nc._SIGS), sorted(declared - set(nc._SIGS))
+
+
+@pytest.mark.parametrize("name", list(synthdata.CONFIGS))
+def test_param_layout_matches_generators(name):
+    cfg = synthdata.get_config(name)
+    assert nc.param_count(cfg) == synthdata.param_count(cfg)
+    for tname, layer, r, c, off in synthdata.param_layout(cfg):
+        assert nc.param_offset(cfg, tname, max(layer, 0)) == (off, r, c), (tname, layer)
+
+
+def test_d20_param_count_exact():
+    assert nc.param_count(synthdata.get_config("d20")) == 560_988_160
+
+
+@pytest.mark.parametrize("name", list(synthdata.CONFIGS))
+def test_workspace_is_positive_and_fits_hbm(name):
+    cfg = synthdata.get_config(name)
+    ws = nc.workspace_bytes(cfg)
+    assert 0 < ws < 200 * 2 ** 30
+    if name == "d20":
+        # the saved activations dominate: ~1.7 GB per layer in bf16
+        assert ws > 20 * 1.6e9
+
+
+def _cfg(**kw):
+    c = nc.make_config(synthdata.get_config("small"))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d_model", 250, -2), ("head_dim", 100, -2), ("n_head", 3, -2), ("seq_len", 100, -2),
+    ("n_layer", 0, -2), ("vocab", 0, -2), ("dtype", 7, -1), ("flags", 64, -1), ("rms_eps", -1.0, -1),
+])
+def test_invalid_configs_rejected(field, value, status):
+    c = _cfg(**{field: value})
+    assert nc.lib().nc_param_count(ctypes.byref(c)) == status
+    assert nc.lib().nc_workspace_bytes(ctypes.byref(c)) == status
+
+
+def test_block_only_rules():
+    c = nc.make_config(synthdata.get_config("block"))
+    assert c.flags & nc.FLAG_BLOCK_ONLY
+    assert nc.param_count(c) == 12 * 1280 * 1280
+    c.n_layer = 2
+    assert nc.lib().nc_param_count(ctypes.byref(c)) == -2
+    with pytest.raises(nc.NcError):
+        nc.param_offset(synthdata.get_config("block"), "E")
+
+
+def test_init_checks_before_any_hip_call():
+    L = nc.lib()
+    c = _cfg()
+    h = ctypes.c_void_p()
+    need = nc.workspace_bytes(c)
+    assert L.nc_init(ctypes.byref(c), None, need, None, ctypes.byref(h)) == -1       # null workspace
+    assert L.nc_init(ctypes.byref(c), 256, need - 1, None, ctypes.byref(h)) == -3    # too small
+    assert L.nc_init(ctypes.byref(c), 256 + 8, need, None, ctypes.byref(h)) == -3    # misaligned
+    assert L.nc_init(ctypes.byref(c), 256, need, None, None) == -1                   # no out pointer
+    assert h.value is None
+
+
+def test_calls_on_null_context_rejected():
+    L = nc.lib()
+    assert L.nc_forward(None, 1, 1, 1, None) == -1
+    assert L.nc_backward(None, 1, 1, 0) == -1
+    assert L.nc_loss_bpb(None, 1, 1) == -1
+    assert L.nc_block_forward(None, 1, 1, 2) == -1
+    assert L.nc_last_error(None) == b"null context"
+
+
+def test_ops_reject_bad_shapes_before_launch():
+    L = nc.lib()
+    # M not a multiple of 64
+    assert L.nc_op_matmul(1, 0, 0, 100, 64, 64, 1, 1, 1, 1, 1, None, 0, None) == -2
+    # split-K without partial buffer / with a stored (non-fp32) output
+    assert L.nc_op_matmul(1, 0, 0, 64, 64, 128, 1, 1, 1, 1, 2, None, 0, None) == -1
+    assert L.nc_op_matmul(1, 0, 0, 64, 64, 128, 1, 1, 1, 0, 2, 1, 0, None) == -1
+    assert L.nc_op_rmsnorm_fwd(1, 4, 100, 1e-6, 1, 1, 1, None) == -2
+    assert L.nc_op_attention_fwd(1, 1, 100, 1, 128, 1, 1, 1, 0, None) == -2
+    assert L.nc_op_attention_fwd(5, 1, 64, 1, 128, 1, 1, 1, 0, None) == -1
+    assert L.nc_op_head_scratch_bytes(1, 128, 64, 100, 0) == -2
+
+
+def test_status_strings():
+    assert nc.status_string(0) == "ok"
+    assert "workspace" in nc.status_string(-3)
+    assert nc.status_string(-99) == "unknown status"
+
+
+def test_flop_formula_d20():
+    from decoder_only_transformer_d20_amd.flops import flops_per_token, flops_per_step
+    cfg = synthdata.get_config("d20")
+    assert flops_per_token(cfg) == pytest.approx(3.492e9, rel=1e-3)
+    assert flops_per_step(cfg) == pytest.approx(2.288e14, rel=1e-3)
