@@ -28,6 +28,7 @@ namespace mfma {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 64;
 constexpr int kThreads = 512;
@@ -48,78 +49,90 @@ __device__ inline float relu2f(float x) {
   return x * x;
 }
 __device__ inline uint32_t relu2_pair(uint32_t w) { return pack2(relu2f(bf_lo(w)), relu2f(bf_hi(w))); }
-__device__ inline uint4 relu2_chunk(uint4 v) {
-  return make_uint4(relu2_pair(v.x), relu2_pair(v.y), relu2_pair(v.z), relu2_pair(v.w));
+__device__ inline u32x4 relu2_chunk(u32x4 v) {
+  u32x4 r;
+  r[0] = relu2_pair(v[0]); r[1] = relu2_pair(v[1]); r[2] = relu2_pair(v[2]); r[3] = relu2_pair(v[3]);
+  return r;
 }
-
-__device__ inline uint32_t word(const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; }
 
 // 8 x 8 bf16 transpose: in[kk] holds 8 consecutive rows' elements at one k;
 // out[e] holds row e's 8 consecutive k values.
-__device__ inline void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
+__device__ inline void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    uint32_t w[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t a = word(in[2 * p], e >> 1), b = word(in[2 * p + 1], e >> 1);
-      w[p] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      const uint32_t a = in[2 * p][e >> 1], b = in[2 * p + 1][e >> 1];
+      out[e][p] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
     }
-    out[e] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
-// One operand tile (R rows x 64 k) -> registers -> LDS, by 256 threads.
-template <int R, bool TRANS, bool XF>
-struct TileLoader {
-  static constexpr int kLoads = 8;
-  uint4 reg[8];
-  const bf16* base;   // operand origin
-  int64_t ld;
-  int tl;             // thread index within the 256 loaders
+typedef const u32x4 __attribute__((address_space(1)))* gptr;
 
-  __device__ inline bool active() const { return TRANS ? (tl < R) : true; }
+// Per-thread plan for one operand tile (R rows x 64 k), loaded by 256
+// threads into `reg` (8 x 16 B) and written to LDS.
+//  k-major operand ([rows][K]): thread tl takes chunk tl & 7 of rows
+//    (tl >> 3) + 32 i, i < R/32 -- 8 lanes read one 128-byte row segment.
+//  transposed operand ([K][rows]): thread tl < R takes the 8 x 8 block at
+//    k rows (tl & 7)*8 .. +7 and tile rows (tl >> 3)*8 .. +7.
+template <int R, bool TRANS>
+struct Plan {
+  gptr ptr;          // this thread's first 16-byte piece of the current tile
+  int64_t step;      // elements between the thread's successive pieces
+  int64_t kstep;     // elements to advance by one 64-k tile
+  uint32_t lds[8];   // byte offsets in the operand's LDS image
+  bool active;
 
-  __device__ inline void load(int64_t row0, int64_t k0) {
+  __device__ inline void init(const bf16* base, int64_t ld, int64_t row0, int64_t k0, int tl) {
     if (!TRANS) {
-      // R*8 chunks of 16 B; 8 lanes cover one 128-byte row segment
+      const int r = tl >> 3, c = tl & 7;
+      ptr = (gptr)(base + (row0 + r) * ld + k0 + c * 8);
+      step = 32 * ld;
+      kstep = BK;
 #pragma unroll
-      for (int i = 0; i < R / 32; ++i) {
-        const int q = tl + 256 * i;
-        const int r = q >> 3, c = q & 7;
-        reg[i] = *reinterpret_cast<const uint4*>(base + (row0 + r) * ld + k0 + c * 8);
-      }
-    } else if (tl < R) {
-      // micro-block: k rows kc*8 .. +7, columns (rows of the tile) mg*8 .. +7
+      for (int i = 0; i < 8; ++i) lds[i] = i < R / 32 ? lds_off(r + 32 * i, c) : 0;
+      active = true;
+    } else {
       const int kc = tl & 7, mg = tl >> 3;
+      ptr = (gptr)(base + (k0 + kc * 8) * ld + row0 + mg * 8);
+      step = ld;
+      kstep = (int64_t)BK * ld;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk)
-        reg[kk] = *reinterpret_cast<const uint4*>(base + (k0 + kc * 8 + kk) * ld + row0 + mg * 8);
+      for (int e = 0; e < 8; ++e) lds[e] = lds_off(mg * 8 + e, kc);
+      active = tl < R;
     }
   }
-
-  __device__ inline void store(char* lds) {
+  __device__ inline void load(u32x4 (&reg)[8]) const {
+    if (!TRANS) {
+#pragma unroll
+      for (int i = 0; i < R / 32; ++i) reg[i] = ptr[(i * step) >> 3];
+    } else if (active) {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) reg[kk] = ptr[(kk * step) >> 3];
+    }
+  }
+  template <bool XF>
+  __device__ inline void store(const u32x4 (&reg)[8], char* lds_base) const {
     if (!TRANS) {
 #pragma unroll
       for (int i = 0; i < R / 32; ++i) {
-        const int q = tl + 256 * i;
-        const int r = q >> 3, c = q & 7;
-        uint4 v = reg[i];
+        u32x4 v = reg[i];
         if (XF) v = relu2_chunk(v);
-        *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = v;
+        *reinterpret_cast<u32x4*>(lds_base + lds[i]) = v;
       }
-    } else if (tl < R) {
-      const int kc = tl & 7, mg = tl >> 3;
-      uint4 t[8];
+    } else if (active) {
+      u32x4 t[8];
       transpose8(reg, t);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint4 v = t[e];
+        u32x4 v = t[e];
         if (XF) v = relu2_chunk(v);
-        *reinterpret_cast<uint4*>(lds + lds_off(mg * 8 + e, kc)) = v;
+        *reinterpret_cast<u32x4*>(lds_base + lds[e]) = v;
       }
     }
   }
+  __device__ inline void advance() { ptr += kstep >> 3; }
 };
 
 template <int BM, int BN, bool PT, bool QT, bool XP, bool XQ, int EPI>
@@ -148,20 +161,13 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_mfma(GemmDesc g) {
   const int64_t kbeg = (int64_t)blockIdx.y * kper;
   const int nk = kper / BK;
 
-  // waves 0-3 load P tiles, waves 4-7 load Q tiles
+  // waves 0-3 stage P tiles, waves 4-7 stage Q tiles (a wave-uniform split)
   const bool loadsP = tid < 256;
-  TileLoader<BM, PT, XP> lp;
-  TileLoader<BN, QT, XQ> lq;
-  lp.base = (const bf16*)g.P; lp.ld = g.ldp; lp.tl = tid & 255;
-  lq.base = (const bf16*)g.Q; lq.ld = g.ldq; lq.tl = tid & 255;
-
-  auto gload = [&](int64_t k0) {
-    if (loadsP) lp.load(m0, k0); else lq.load(n0, k0);
-  };
-  auto lstore = [&](int stage) {
-    char* s = smem + stage * STAGE;
-    if (loadsP) lp.store(s); else lq.store(s + BM * 128);
-  };
+  Plan<BM, PT> pp;
+  Plan<BN, QT> pq;
+  if (loadsP) pp.init((const bf16*)g.P, g.ldp, m0, kbeg, tid & 255);
+  else pq.init((const bf16*)g.Q, g.ldq, n0, kbeg, tid & 255);
+  u32x4 reg[8];
 
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -171,31 +177,62 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_mfma(GemmDesc g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  gload(kbeg);
-  lstore(0);
+  if (loadsP) {
+    pp.load(reg);
+    pp.template store<XP>(reg, smem);
+    pp.advance();
+  } else {
+    pq.load(reg);
+    pq.template store<XQ>(reg, smem + BM * 128);
+    pq.advance();
+  }
   __syncthreads();
 
   const int frow = lane & 31, fchunk = lane >> 5;
+  uint32_t offQ[FN], offP[FM];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) offQ[j] = BM * 128 + lds_off(wn * WTN + j * 32 + frow, fchunk);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) offP[i] = lds_off(wm * WTM + i * 32 + frow, fchunk);
+  // chunk 2s + fchunk of a row sits at ((2s + fchunk) ^ (row & 7)) = (fchunk ^ (row & 7)) ^ 2s
+  // since 2s only touches bits 1-2: the k16 step s moves the byte offset by an xor of 32*s
+
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
-    if (more) gload(kbeg + (int64_t)(kt + 1) * BK);
-    const char* sP = smem + (kt & 1) * STAGE;
-    const char* sQ = sP + BM * 128;
+    if (more) {
+      if (loadsP) pp.load(reg); else pq.load(reg);
+    }
+    const char* st = smem + (kt & 1) * STAGE;
+    bf16x8 a[2][FN], bb[2][FM];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) a[0][j] = *reinterpret_cast<const bf16x8*>(st + offQ[j]);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) bb[0][i] = *reinterpret_cast<const bf16x8*>(st + offP[i]);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 a[FN], bb[FM];
+      const int cur = s & 1, nxt = cur ^ 1;
+      if (s + 1 < BK / 16) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        a[j] = *reinterpret_cast<const bf16x8*>(sQ + lds_off(wn * WTN + j * 32 + frow, 2 * s + fchunk));
+        for (int j = 0; j < FN; ++j) a[nxt][j] = *reinterpret_cast<const bf16x8*>(st + (offQ[j] ^ (32u * (s + 1))));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) bb[nxt][i] = *reinterpret_cast<const bf16x8*>(st + (offP[i] ^ (32u * (s + 1))));
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        bb[i] = *reinterpret_cast<const bf16x8*>(sP + lds_off(wm * WTM + i * 32 + frow, 2 * s + fchunk));
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], bb[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][j], bb[cur][i], acc[i][j], 0, 0, 0);
     }
-    if (more) lstore((kt + 1) & 1);
+    if (more) {
+      char* nx = smem + ((kt + 1) & 1) * STAGE;
+      if (loadsP) {
+        pp.template store<XP>(reg, nx);
+        pp.advance();
+      } else {
+        pq.template store<XQ>(reg, nx + BM * 128);
+        pq.advance();
+      }
+    }
     __syncthreads();
   }
 
