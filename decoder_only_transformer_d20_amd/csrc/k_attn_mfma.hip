@@ -1,7 +1,384 @@
-// bf16 MFMA flash attention for gfx950 (placeholder: routes to the portable kernels).
-#include "nc_internal.h"
+// Causal flash attention, forward and backward, on gfx950 matrix cores
+// (bf16 operands, fp32 accumulation and softmax statistics), head dim 128.
+//
+// Forward: a workgroup (4 waves) owns 128 query rows of one (row, head), a
+// wave 32 of them; it walks the 64-key tiles up to its diagonal with an
+// online softmax.  Backward: delta = rowsum(dO * O) (attn_delta), then one
+// kernel accumulates dQ over key tiles and one accumulates dK, dV over query
+// tiles, both recomputing P from the saved log-sum-exp -- no atomics, so the
+// result does not depend on scheduling.  dQ and dK leave through the
+// inverse rotary rotation, so the caller receives gradients with respect to
+// the pre-rotation q and k.
+#include "attn_mfma.h"
 
 namespace nc {
-hipError_t attn_fwd_mfma(const AttnDesc& a, hipStream_t s) { return attn_fwd_portable<bf16>(a, s); }
-hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s) { return attn_bwd_portable<bf16>(a, s); }
+using namespace attn;
+
+namespace {
+
+constexpr float kScaleLog2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
+
+// ===========================================================================
+// forward
+// ===========================================================================
+__global__ void __launch_bounds__(256) k_attn_fwd(AttnDesc a) {
+  __shared__ __attribute__((aligned(16))) char smem[2][32768];   // per stage: K image | V^T image
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int T = a.T, H = a.H, d = H * HD;
+  const int qt = T / 128 - 1 - (int)blockIdx.x;                  // heaviest tiles first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t ld = 3LL * d;
+  const bf16* rows = (const bf16*)a.qkv + (int64_t)b * T * ld;
+  const bf16* qb = rows + h * HD;
+  const bf16* kb = rows + d + h * HD;
+  const bf16* vb = rows + 2 * d + h * HD;
+  const int q0 = qt * 128, i0 = q0 + wave * 32, my_i = i0 + (lane & 31);
+
+  bf16x8 qf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(gload(qb + (int64_t)my_i * ld + 16 * s + 8 * hh));
+
+  floatx16 o[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) zero(o[t]);
+  float m = -INFINITY, l = 0.f;
+
+  const int ntiles = (q0 + 128) / 64;
+  u32x4 reg[8];
+  // threads 0-127 stage V^T, threads 128-255 stage K
+  auto gl = [&](int jt) {
+    const int64_t j0 = (int64_t)jt * 64;
+    if (tid < 128) load_tr64(vb + j0 * ld, ld, tid, reg);
+    else load_nat64<128>(kb + j0 * ld, ld, tid - 128, reg);
+  };
+  auto st = [&](int stage) {
+    if (tid < 128) store_tr64(smem[stage] + 16384, tid, reg);
+    else store_nat64<128>(smem[stage], tid - 128, reg);
+  };
+  gl(0);
+  st(0);
+  __syncthreads();
+
+  for (int jt = 0; jt < ntiles; ++jt) {
+    const bool more = jt + 1 < ntiles;
+    if (more) gl(jt + 1);
+    const int j0 = jt * 64;
+    const char* sK = smem[jt & 1];
+    const char* sV = sK + 16384;
+    if (j0 <= i0 + 31) {
+      floatx16 s[2];
+      zero(s[0]);
+      zero(s[1]);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + off256(js * 32 + (lane & 31), 2 * ks + hh));
+          s[js] = mfma(kf, qf[ks], s[js]);
+        }
+      const bool diag = j0 + 63 > i0;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = s[js][r] * kScaleLog2;
+          if (diag && j0 + js * 32 + 8 * (r >> 2) + 4 * hh + (r & 3) > my_i) v = -INFINITY;
+          s[js][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      float ls = 0.f;
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[js][r] - mn);
+          s[js][r] = p;
+          ls += p;
+        }
+      l = l * alpha + ls;
+      m = mn;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+#pragma unroll
+      for (int sp = 0; sp < 4; ++sp) {
+        const bf16x8 pf = pack8(s[sp >> 1], 8 * (sp & 1));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + off128(t * 32 + (lane & 31), 2 * sp + hh));
+          o[t] = mfma(vf, pf, o[t]);
+        }
+      }
+    }
+    if (more) st((jt + 1) & 1);
+    __syncthreads();
+  }
+
+  l += __shfl_xor(l, 32, 64);
+  const float inv = 1.f / l;
+  bf16* out = (bf16*)a.o_out + ((int64_t)b * T + my_i) * d + h * HD + 4 * hh;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint2 w = make_uint2(pack2(o[t][4 * g] * inv, o[t][4 * g + 1] * inv),
+                                 pack2(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv));
+      *reinterpret_cast<uint2*>(out + t * 32 + 8 * g) = w;
+    }
+  if (hh == 0) a.lse[((int64_t)b * H + h) * T + my_i] = (m + __log2f(l)) * kLn2;
+}
+
+// inverse rotation of 4 consecutive features (2 adjacent pairs) at pair index pi
+__device__ inline void rope_inv4(float* v, const float2* tab_t, int pi) {
+  const float4 cs = *reinterpret_cast<const float4*>(tab_t + pi);
+  const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+  v[0] = x0 * cs.x + x1 * cs.y;
+  v[1] = -x0 * cs.y + x1 * cs.x;
+  v[2] = x2 * cs.z + x3 * cs.w;
+  v[3] = -x2 * cs.w + x3 * cs.z;
+}
+
+// store a wave's 32 rows x 128 features accumulator (lane = row, regs = features)
+__device__ inline void store_rows(floatx16 (&acc)[4], float scale, bf16* dst_row, const float2* rope_t, int hh) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float v[4] = {acc[t][4 * g] * scale, acc[t][4 * g + 1] * scale, acc[t][4 * g + 2] * scale,
+                    acc[t][4 * g + 3] * scale};
+      const int f = t * 32 + 8 * g + 4 * hh;
+      if (rope_t) rope_inv4(v, rope_t, f >> 1);
+      *reinterpret_cast<uint2*>(dst_row + f) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+    }
+}
+
+// ===========================================================================
+// backward: dQ (one wave = 32 query rows, walking key tiles up to the diagonal)
+// ===========================================================================
+__global__ void __launch_bounds__(256) k_attn_dq(AttnDesc a) {
+  __shared__ __attribute__((aligned(16))) char smem[3 * 16384];  // K image | V image | K^T image
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int T = a.T, H = a.H, d = H * HD;
+  const int qt = T / 128 - 1 - (int)blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t ld = 3LL * d;
+  const bf16* rows = (const bf16*)a.qkv + (int64_t)b * T * ld;
+  const bf16* qb = rows + h * HD;
+  const bf16* kb = rows + d + h * HD;
+  const bf16* vb = rows + 2 * d + h * HD;
+  const int q0 = qt * 128, i0 = q0 + wave * 32, my_i = i0 + (lane & 31);
+  const bf16* dob = (const bf16*)a.dout + ((int64_t)b * T + my_i) * d + h * HD;
+
+  bf16x8 qf[8], dof[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    qf[s] = as_bf16x8(gload(qb + (int64_t)my_i * ld + 16 * s + 8 * hh));
+    dof[s] = as_bf16x8(gload(dob + 16 * s + 8 * hh));
+  }
+  const int64_t sidx = ((int64_t)b * H + h) * T + my_i;
+  const float lse2 = a.lse[sidx] * kLog2e;
+  const float Dl = a.delta[sidx];
+
+  floatx16 dq[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) zero(dq[t]);
+
+  const int ntiles = (q0 + 128) / 64;
+  char* sK = smem;
+  char* sV = smem + 16384;
+  char* sKT = smem + 32768;
+  for (int jt = 0; jt < ntiles; ++jt) {
+    const int64_t j0 = (int64_t)jt * 64;
+    {
+      u32x4 r1[8], r2[8];
+      if (tid < 128) {
+        load_tr64(kb + j0 * ld, ld, tid, r1);
+        store_tr64(sKT, tid, r1);
+      } else {
+        load_nat64<128>(kb + j0 * ld, ld, tid - 128, r1);
+        load_nat64<128>(vb + j0 * ld, ld, tid - 128, r2);
+        store_nat64<128>(sK, tid - 128, r1);
+        store_nat64<128>(sV, tid - 128, r2);
+      }
+    }
+    __syncthreads();
+    if (j0 <= i0 + 31) {
+      floatx16 s[2], dp[2];
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        zero(s[js]);
+        zero(dp[js]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+          const int row = js * 32 + (lane & 31);
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + off256(row, 2 * ks + hh));
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + off256(row, 2 * ks + hh));
+          s[js] = mfma(kf, qf[ks], s[js]);
+          dp[js] = mfma(vf, dof[ks], dp[js]);
+        }
+      const bool diag = j0 + 63 > i0;
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = __builtin_amdgcn_exp2f(s[js][r] * kScaleLog2 - lse2);
+          if (diag && j0 + js * 32 + 8 * (r >> 2) + 4 * hh + (r & 3) > my_i) p = 0.f;
+          s[js][r] = p * (dp[js][r] - Dl);          // dS
+        }
+#pragma unroll
+      for (int sp = 0; sp < 4; ++sp) {
+        const bf16x8 df = pack8(s[sp >> 1], 8 * (sp & 1));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sKT + off128(t * 32 + (lane & 31), 2 * sp + hh));
+          dq[t] = mfma(kf, df, dq[t]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  bf16* dst = (bf16*)a.dqkv + ((int64_t)b * T + my_i) * ld + h * HD;
+  store_rows(dq, 0.08838834764831845f, dst, a.rope ? a.rope + (int64_t)my_i * (HD / 2) : nullptr, hh);
+}
+
+// ===========================================================================
+// backward: dK, dV (one wave = 32 keys, walking query tiles from the diagonal)
+// ===========================================================================
+__global__ void __launch_bounds__(256) k_attn_dkdv(AttnDesc a) {
+  // Q image | dO image | Q^T image | dO^T image | lse2[64] | delta[64]
+  __shared__ __attribute__((aligned(16))) char smem[4 * 16384 + 512];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  const int T = a.T, H = a.H, d = H * HD;
+  const int kt = blockIdx.x;                                     // low key tiles do the most work
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t ld = 3LL * d;
+  const bf16* rows = (const bf16*)a.qkv + (int64_t)b * T * ld;
+  const bf16* qb = rows + h * HD;
+  const bf16* kb = rows + d + h * HD;
+  const bf16* vb = rows + 2 * d + h * HD;
+  const bf16* dob = (const bf16*)a.dout + (int64_t)b * T * d + h * HD;
+  const int jb = kt * 128, jw = jb + wave * 32, my_j = jw + (lane & 31);
+
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    kf[s] = as_bf16x8(gload(kb + (int64_t)my_j * ld + 16 * s + 8 * hh));
+    vf[s] = as_bf16x8(gload(vb + (int64_t)my_j * ld + 16 * s + 8 * hh));
+  }
+  floatx16 dk[4], dv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    zero(dk[t]);
+    zero(dv[t]);
+  }
+  char* sQ = smem;
+  char* sO = smem + 16384;
+  char* sQT = smem + 32768;
+  char* sOT = smem + 49152;
+  float* sL = reinterpret_cast<float*>(smem + 65536);
+  float* sD = sL + 64;
+  const float* lse_bh = a.lse + ((int64_t)b * H + h) * T;
+  const float* del_bh = a.delta + ((int64_t)b * H + h) * T;
+
+  for (int qt = jb / 64; qt < T / 64; ++qt) {
+    const int64_t i0 = (int64_t)qt * 64;
+    {
+      u32x4 r1[8], r2[8];
+      if (tid < 128) {
+        load_tr64(qb + i0 * ld, ld, tid, r1);
+        load_tr64(dob + i0 * d, d, tid, r2);
+        store_tr64(sQT, tid, r1);
+        store_tr64(sOT, tid, r2);
+        if (tid < 64) sL[tid] = lse_bh[i0 + tid] * kLog2e;
+        else sD[tid - 64] = del_bh[i0 + tid - 64];
+      } else {
+        load_nat64<128>(qb + i0 * ld, ld, tid - 128, r1);
+        load_nat64<128>(dob + i0 * d, d, tid - 128, r2);
+        store_nat64<128>(sQ, tid - 128, r1);
+        store_nat64<128>(sO, tid - 128, r2);
+      }
+    }
+    __syncthreads();
+    if (i0 + 63 >= jw) {
+      const bool diag = i0 < jw + 31;
+#pragma unroll
+      for (int is = 0; is < 2; ++is) {
+        floatx16 s, dp;
+        zero(s);
+        zero(dp);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int row = is * 32 + (lane & 31);
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sQ + off256(row, 2 * ks + hh));
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(sO + off256(row, 2 * ks + hh));
+          s = mfma(qa, kf[ks], s);
+          dp = mfma(oa, vf[ks], dp);
+        }
+        // lane = key j, register r = query is*32 + 8(r/4) + 4hh + r%4
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int il = is * 32 + 8 * g + 4 * hh;
+          const float4 L = *reinterpret_cast<const float4*>(sL + il);
+          const float4 Dv = *reinterpret_cast<const float4*>(sD + il);
+          const float Ls[4] = {L.x, L.y, L.z, L.w}, Ds[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float p = __builtin_amdgcn_exp2f(s[r] * kScaleLog2 - Ls[e]);
+            if (diag && i0 + il + e < my_j) p = 0.f;
+            s[r] = p;
+            dp[r] = p * (dp[r] - Ds[e]);        // dS
+          }
+        }
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const int sp = is * 2 + gp;
+          const bf16x8 pf = pack8(s, 8 * gp);
+          const bf16x8 df = pack8(dp, 8 * gp);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int row = t * 32 + (lane & 31);
+            const bf16x8 oT = *reinterpret_cast<const bf16x8*>(sOT + off128(row, 2 * sp + hh));
+            const bf16x8 qT = *reinterpret_cast<const bf16x8*>(sQT + off128(row, 2 * sp + hh));
+            dv[t] = mfma(oT, pf, dv[t]);
+            dk[t] = mfma(qT, df, dk[t]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  bf16* dst = (bf16*)a.dqkv + ((int64_t)b * T + my_j) * ld + h * HD;
+  store_rows(dk, 0.08838834764831845f, dst + d, a.rope ? a.rope + (int64_t)my_j * (HD / 2) : nullptr, hh);
+  store_rows(dv, 1.f, dst + 2 * d, nullptr, hh);
+}
+
+}  // namespace
+
+bool attn_mfma_supported(const AttnDesc& a) { return a.Q == HD && a.T % 128 == 0 && a.T > 0; }
+
+hipError_t attn_fwd_mfma(const AttnDesc& a, hipStream_t s) {
+  if (!attn_mfma_supported(a)) return hipErrorNotSupported;
+  k_attn_fwd<<<dim3(a.T / 128, a.H, a.B), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s) {
+  if (!attn_mfma_supported(a)) return hipErrorNotSupported;
+  hipError_t e = attn_delta<bf16>(a, s);
+  if (e != hipSuccess) return e;
+  k_attn_dq<<<dim3(a.T / 128, a.H, a.B), 256, 0, s>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  k_attn_dkdv<<<dim3(a.T / 128, a.H, a.B), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace nc

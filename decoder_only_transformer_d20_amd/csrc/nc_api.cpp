@@ -199,11 +199,11 @@ hipError_t weight_grad(nc_ctx* ctx, int Mw, int Nw, const void* P, int64_t ldp, 
 }
 
 template <typename T> hipError_t attn_fwd(nc_ctx* ctx, const AttnDesc& a) {
-  if (!portable(ctx->cfg)) return attn_fwd_mfma(a, ctx->stream);
+  if (!portable(ctx->cfg) && attn_mfma_supported(a)) return attn_fwd_mfma(a, ctx->stream);
   return attn_fwd_portable<T>(a, ctx->stream);
 }
 template <typename T> hipError_t attn_bwd(nc_ctx* ctx, const AttnDesc& a) {
-  if (!portable(ctx->cfg)) return attn_bwd_mfma(a, ctx->stream);
+  if (!portable(ctx->cfg) && attn_mfma_supported(a)) return attn_bwd_mfma(a, ctx->stream);
   return attn_bwd_portable<T>(a, ctx->stream);
 }
 

@@ -98,6 +98,7 @@ hipError_t splitk_reduce(const float* part, int splits, int64_t n, float* out, i
 
 template <typename T> hipError_t attn_fwd_portable(const AttnDesc& a, hipStream_t s);
 template <typename T> hipError_t attn_bwd_portable(const AttnDesc& a, hipStream_t s);
+bool attn_mfma_supported(const AttnDesc& a);   // head dim 128, T % 128 == 0
 hipError_t attn_fwd_mfma(const AttnDesc& a, hipStream_t s);
 hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s);
 template <typename T> hipError_t attn_delta(const AttnDesc& a, hipStream_t s);

@@ -151,7 +151,7 @@ ATT_CASES = [
     # dtype, portable, B, T, H, Q
     ("f32", 1, 2, 128, 2, 64),
     ("bf16", 1, 2, 192, 2, 128),
-    ("bf16", 0, 2, 192, 2, 128),
+    ("bf16", 0, 2, 256, 2, 128),
     ("bf16", 0, 1, 640, 3, 128),
 ]
 
