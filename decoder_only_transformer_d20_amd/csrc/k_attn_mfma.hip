@@ -18,15 +18,29 @@ namespace {
 
 constexpr float kScaleLog2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
 
+// Block -> (tile, head, row).  Workgroups are dealt to the 8 XCDs
+// round-robin; renumbering so each XCD takes a contiguous run of the
+// (row, head) groups keeps the 16 tiles that share one head's K/V (or Q/dO)
+// rows in one XCD's L2.
+__device__ inline void tile_order(int ntile, int H, int B, int& tile, int& h, int& b) {
+  const int total = ntile * H * B;
+  int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  tile = L % ntile;
+  h = (L / ntile) % H;
+  b = L / (ntile * H);
+}
+
 // ===========================================================================
 // forward
 // ===========================================================================
-__global__ void __launch_bounds__(256) k_attn_fwd(AttnDesc a) {
+__global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
   __shared__ __attribute__((aligned(16))) char smem[2][32768];   // per stage: K image | V^T image
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int T = a.T, H = a.H, d = H * HD;
-  const int qt = T / 128 - 1 - (int)blockIdx.x;                  // heaviest tiles first
-  const int h = blockIdx.y, b = blockIdx.z;
+  int qt, h, b;
+  tile_order(T / 128, H, a.B, qt, h, b);
+  qt = T / 128 - 1 - qt;                                         // heaviest tiles first
   const int64_t ld = 3LL * d;
   const bf16* rows = (const bf16*)a.qkv + (int64_t)b * T * ld;
   const bf16* qb = rows + h * HD;
@@ -158,31 +172,41 @@ __device__ inline void store_rows(floatx16 (&acc)[4], float scale, bf16* dst_row
 }
 
 // ===========================================================================
-// backward: dQ (one wave = 32 query rows, walking key tiles up to the diagonal)
+// backward: dQ (one wave = 32 query rows, walking key tiles up to the
+// diagonal).  It also forms delta_i = sum_d dO[i,d] O[i,d] from the rows it
+// holds and stores it for the dK kernel.
 // ===========================================================================
-__global__ void __launch_bounds__(256) k_attn_dq(AttnDesc a) {
+__global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
   __shared__ __attribute__((aligned(16))) char smem[3 * 16384];  // K image | V image | K^T image
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int T = a.T, H = a.H, d = H * HD;
-  const int qt = T / 128 - 1 - (int)blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  int qt, h, b;
+  tile_order(T / 128, H, a.B, qt, h, b);
+  qt = T / 128 - 1 - qt;
   const int64_t ld = 3LL * d;
   const bf16* rows = (const bf16*)a.qkv + (int64_t)b * T * ld;
   const bf16* qb = rows + h * HD;
   const bf16* kb = rows + d + h * HD;
   const bf16* vb = rows + 2 * d + h * HD;
   const int q0 = qt * 128, i0 = q0 + wave * 32, my_i = i0 + (lane & 31);
-  const bf16* dob = (const bf16*)a.dout + ((int64_t)b * T + my_i) * d + h * HD;
+  const int64_t tok = (int64_t)b * T + my_i;
+  const bf16* dob = (const bf16*)a.dout + tok * d + h * HD;
+  const bf16* ob = (const bf16*)a.o + tok * d + h * HD;
 
   bf16x8 qf[8], dof[8];
+  float Dl = 0.f;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     qf[s] = as_bf16x8(gload(qb + (int64_t)my_i * ld + 16 * s + 8 * hh));
-    dof[s] = as_bf16x8(gload(dob + 16 * s + 8 * hh));
+    const u32x4 dw = gload(dob + 16 * s + 8 * hh), ow = gload(ob + 16 * s + 8 * hh);
+    dof[s] = as_bf16x8(dw);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Dl += bf_lo(dw[e]) * bf_lo(ow[e]) + bf_hi(dw[e]) * bf_hi(ow[e]);
   }
+  Dl += __shfl_xor(Dl, 32, 64);
   const int64_t sidx = ((int64_t)b * H + h) * T + my_i;
+  if (hh == 0) a.delta[sidx] = Dl;
   const float lse2 = a.lse[sidx] * kLog2e;
-  const float Dl = a.delta[sidx];
 
   floatx16 dq[4];
 #pragma unroll
@@ -195,47 +219,44 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnDesc a) {
   for (int jt = 0; jt < ntiles; ++jt) {
     const int64_t j0 = (int64_t)jt * 64;
     {
-      u32x4 r1[8], r2[8];
+      u32x4 r[8];
       if (tid < 128) {
-        load_tr64(kb + j0 * ld, ld, tid, r1);
-        store_tr64(sKT, tid, r1);
+        load_tr64(kb + j0 * ld, ld, tid, r);
+        store_tr64(sKT, tid, r);
       } else {
-        load_nat64<128>(kb + j0 * ld, ld, tid - 128, r1);
-        load_nat64<128>(vb + j0 * ld, ld, tid - 128, r2);
-        store_nat64<128>(sK, tid - 128, r1);
-        store_nat64<128>(sV, tid - 128, r2);
+        load_nat64<128>(kb + j0 * ld, ld, tid - 128, r);
+        store_nat64<128>(sK, tid - 128, r);
+        load_nat64<128>(vb + j0 * ld, ld, tid - 128, r);
+        store_nat64<128>(sV, tid - 128, r);
       }
     }
     __syncthreads();
-    if (j0 <= i0 + 31) {
-      floatx16 s[2], dp[2];
 #pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        zero(s[js]);
-        zero(dp[js]);
+    for (int js = 0; js < 2; ++js) {
+      const int jh = (int)j0 + js * 32;
+      if (jh > i0 + 31) continue;                 // all 32 keys above the diagonal
+      floatx16 s, dp;
+      zero(s);
+      zero(dp);
+      const int row = js * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + off256(row, 2 * ks + hh));
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + off256(row, 2 * ks + hh));
+        s = mfma(kf, qf[ks], s);
+        dp = mfma(vf, dof[ks], dp);
+      }
+      const bool diag = jh + 31 > i0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(s[r] * kScaleLog2 - lse2);
+        if (diag && jh + 8 * (r >> 2) + 4 * hh + (r & 3) > my_i) p = 0.f;
+        s[r] = p * (dp[r] - Dl);                   // dS
       }
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int js = 0; js < 2; ++js) {
-          const int row = js * 32 + (lane & 31);
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + off256(row, 2 * ks + hh));
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + off256(row, 2 * ks + hh));
-          s[js] = mfma(kf, qf[ks], s[js]);
-          dp[js] = mfma(vf, dof[ks], dp[js]);
-        }
-      const bool diag = j0 + 63 > i0;
-#pragma unroll
-      for (int js = 0; js < 2; ++js)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = __builtin_amdgcn_exp2f(s[js][r] * kScaleLog2 - lse2);
-          if (diag && j0 + js * 32 + 8 * (r >> 2) + 4 * hh + (r & 3) > my_i) p = 0.f;
-          s[js][r] = p * (dp[js][r] - Dl);          // dS
-        }
-#pragma unroll
-      for (int sp = 0; sp < 4; ++sp) {
-        const bf16x8 df = pack8(s[sp >> 1], 8 * (sp & 1));
+      for (int gp = 0; gp < 2; ++gp) {
+        const bf16x8 df = pack8(s, 8 * gp);
+        const int sp = js * 2 + gp;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sKT + off128(t * 32 + (lane & 31), 2 * sp + hh));
@@ -245,20 +266,24 @@ __global__ void __launch_bounds__(256) k_attn_dq(AttnDesc a) {
     }
     __syncthreads();
   }
-  bf16* dst = (bf16*)a.dqkv + ((int64_t)b * T + my_i) * ld + h * HD;
+  bf16* dst = (bf16*)a.dqkv + tok * ld + h * HD;
   store_rows(dq, 0.08838834764831845f, dst, a.rope ? a.rope + (int64_t)my_i * (HD / 2) : nullptr, hh);
 }
 
 // ===========================================================================
-// backward: dK, dV (one wave = 32 keys, walking query tiles from the diagonal)
+// backward: dK and dV, one wave = 32 keys walking the query tiles from the
+// diagonal.  Two kernels (dV needs P only; dK needs dS): each keeps its
+// accumulators and key-side operands in registers at two waves per SIMD.
 // ===========================================================================
-__global__ void __launch_bounds__(256) k_attn_dkdv(AttnDesc a) {
-  // Q image | dO image | Q^T image | dO^T image | lse2[64] | delta[64]
-  __shared__ __attribute__((aligned(16))) char smem[4 * 16384 + 512];
+template <bool DK>
+__global__ void __launch_bounds__(256, 2) k_attn_dkv(AttnDesc a) {
+  // Q image | (dO image) | Q^T or dO^T image | lse2[64] | delta[64]
+  constexpr int NIMG = DK ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) char smem[NIMG * 16384 + 512];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int T = a.T, H = a.H, d = H * HD;
-  const int kt = blockIdx.x;                                     // low key tiles do the most work
-  const int h = blockIdx.y, b = blockIdx.z;
+  int kt, h, b;
+  tile_order(T / 128, H, a.B, kt, h, b);                         // low key tiles do the most work
   const int64_t ld = 3LL * d;
   const bf16* rows = (const bf16*)a.qkv + (int64_t)b * T * ld;
   const bf16* qb = rows + h * HD;
@@ -271,19 +296,15 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnDesc a) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     kf[s] = as_bf16x8(gload(kb + (int64_t)my_j * ld + 16 * s + 8 * hh));
-    vf[s] = as_bf16x8(gload(vb + (int64_t)my_j * ld + 16 * s + 8 * hh));
+    if (DK) vf[s] = as_bf16x8(gload(vb + (int64_t)my_j * ld + 16 * s + 8 * hh));
   }
-  floatx16 dk[4], dv[4];
+  floatx16 acc[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    zero(dk[t]);
-    zero(dv[t]);
-  }
+  for (int t = 0; t < 4; ++t) zero(acc[t]);
   char* sQ = smem;
-  char* sO = smem + 16384;
-  char* sQT = smem + 32768;
-  char* sOT = smem + 49152;
-  float* sL = reinterpret_cast<float*>(smem + 65536);
+  char* sO = smem + 16384;                       // dK only
+  char* sT = smem + (NIMG - 1) * 16384;          // Q^T (dK) or dO^T (dV)
+  float* sL = reinterpret_cast<float*>(smem + NIMG * 16384);
   float* sD = sL + 64;
   const float* lse_bh = a.lse + ((int64_t)b * H + h) * T;
   const float* del_bh = a.delta + ((int64_t)b * H + h) * T;
@@ -291,74 +312,76 @@ __global__ void __launch_bounds__(256) k_attn_dkdv(AttnDesc a) {
   for (int qt = jb / 64; qt < T / 64; ++qt) {
     const int64_t i0 = (int64_t)qt * 64;
     {
-      u32x4 r1[8], r2[8];
+      u32x4 r[8];
       if (tid < 128) {
-        load_tr64(qb + i0 * ld, ld, tid, r1);
-        load_tr64(dob + i0 * d, d, tid, r2);
-        store_tr64(sQT, tid, r1);
-        store_tr64(sOT, tid, r2);
+        if (DK) load_tr64(qb + i0 * ld, ld, tid, r);
+        else load_tr64(dob + i0 * d, d, tid, r);
+        store_tr64(sT, tid, r);
         if (tid < 64) sL[tid] = lse_bh[i0 + tid] * kLog2e;
-        else sD[tid - 64] = del_bh[i0 + tid - 64];
+        else if (DK) sD[tid - 64] = del_bh[i0 + tid - 64];
       } else {
-        load_nat64<128>(qb + i0 * ld, ld, tid - 128, r1);
-        load_nat64<128>(dob + i0 * d, d, tid - 128, r2);
-        store_nat64<128>(sQ, tid - 128, r1);
-        store_nat64<128>(sO, tid - 128, r2);
+        load_nat64<128>(qb + i0 * ld, ld, tid - 128, r);
+        store_nat64<128>(sQ, tid - 128, r);
+        if (DK) {
+          load_nat64<128>(dob + i0 * d, d, tid - 128, r);
+          store_nat64<128>(sO, tid - 128, r);
+        }
       }
     }
     __syncthreads();
-    if (i0 + 63 >= jw) {
-      const bool diag = i0 < jw + 31;
 #pragma unroll
-      for (int is = 0; is < 2; ++is) {
-        floatx16 s, dp;
-        zero(s);
-        zero(dp);
+    for (int is = 0; is < 2; ++is) {
+      const int ih = (int)i0 + is * 32;
+      if (ih + 31 < jw) continue;                 // all 32 queries before the wave's keys
+      const bool diag = ih < jw + 31;
+      floatx16 s, dp;
+      zero(s);
+      if (DK) zero(dp);
+      const int row = is * 32 + (lane & 31);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const int row = is * 32 + (lane & 31);
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sQ + off256(row, 2 * ks + hh));
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sQ + off256(row, 2 * ks + hh));
+        s = mfma(qa, kf[ks], s);
+        if (DK) {
           const bf16x8 oa = *reinterpret_cast<const bf16x8*>(sO + off256(row, 2 * ks + hh));
-          s = mfma(qa, kf[ks], s);
           dp = mfma(oa, vf[ks], dp);
         }
-        // lane = key j, register r = query is*32 + 8(r/4) + 4hh + r%4
+      }
+      // lane = key j, register r = query ih + 8(r/4) + 4hh + r%4
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int il = is * 32 + 8 * g + 4 * hh;
-          const float4 L = *reinterpret_cast<const float4*>(sL + il);
+      for (int g = 0; g < 4; ++g) {
+        const int il = is * 32 + 8 * g + 4 * hh;
+        const float4 L = *reinterpret_cast<const float4*>(sL + il);
+        const float Ls[4] = {L.x, L.y, L.z, L.w};
+        float Ds[4] = {0.f, 0.f, 0.f, 0.f};
+        if (DK) {
           const float4 Dv = *reinterpret_cast<const float4*>(sD + il);
-          const float Ls[4] = {L.x, L.y, L.z, L.w}, Ds[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float p = __builtin_amdgcn_exp2f(s[r] * kScaleLog2 - Ls[e]);
-            if (diag && i0 + il + e < my_j) p = 0.f;
-            s[r] = p;
-            dp[r] = p * (dp[r] - Ds[e]);        // dS
-          }
+          Ds[0] = Dv.x; Ds[1] = Dv.y; Ds[2] = Dv.z; Ds[3] = Dv.w;
         }
 #pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          const int sp = is * 2 + gp;
-          const bf16x8 pf = pack8(s, 8 * gp);
-          const bf16x8 df = pack8(dp, 8 * gp);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = __builtin_amdgcn_exp2f(s[r] * kScaleLog2 - Ls[e]);
+          if (diag && (int)i0 + il + e < my_j) p = 0.f;
+          s[r] = DK ? p * (dp[r] - Ds[e]) : p;     // dS or P
+        }
+      }
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int row = t * 32 + (lane & 31);
-            const bf16x8 oT = *reinterpret_cast<const bf16x8*>(sOT + off128(row, 2 * sp + hh));
-            const bf16x8 qT = *reinterpret_cast<const bf16x8*>(sQT + off128(row, 2 * sp + hh));
-            dv[t] = mfma(oT, pf, dv[t]);
-            dk[t] = mfma(qT, df, dk[t]);
-          }
+      for (int gp = 0; gp < 2; ++gp) {
+        const int sp = is * 2 + gp;
+        const bf16x8 bfr = pack8(s, 8 * gp);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 at = *reinterpret_cast<const bf16x8*>(sT + off128(t * 32 + (lane & 31), 2 * sp + hh));
+          acc[t] = mfma(at, bfr, acc[t]);
         }
       }
     }
     __syncthreads();
   }
   bf16* dst = (bf16*)a.dqkv + ((int64_t)b * T + my_j) * ld + h * HD;
-  store_rows(dk, 0.08838834764831845f, dst + d, a.rope ? a.rope + (int64_t)my_j * (HD / 2) : nullptr, hh);
-  store_rows(dv, 1.f, dst + 2 * d, nullptr, hh);
+  if (DK) store_rows(acc, 0.08838834764831845f, dst + d, a.rope ? a.rope + (int64_t)my_j * (HD / 2) : nullptr, hh);
+  else store_rows(acc, 1.f, dst + 2 * d, nullptr, hh);
 }
 
 }  // namespace
@@ -373,11 +396,13 @@ hipError_t attn_fwd_mfma(const AttnDesc& a, hipStream_t s) {
 
 hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s) {
   if (!attn_mfma_supported(a)) return hipErrorNotSupported;
-  hipError_t e = attn_delta<bf16>(a, s);
+  const dim3 grid(a.T / 128, a.H, a.B);
+  k_attn_dq<<<grid, 256, 0, s>>>(a);             // also writes delta
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_attn_dq<<<dim3(a.T / 128, a.H, a.B), 256, 0, s>>>(a);
+  k_attn_dkv<true><<<grid, 256, 0, s>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_attn_dkdv<<<dim3(a.T / 128, a.H, a.B), 256, 0, s>>>(a);
+  k_attn_dkv<false><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

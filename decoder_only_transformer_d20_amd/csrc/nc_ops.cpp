@@ -149,4 +149,20 @@ int nc_op_head_ce_fwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void
   return status_of(e);
 }
 
+int nc_op_head_gemm_lse(int32_t dtype, int64_t n, int32_t d, int32_t V, const void* xf, const void* U,
+                        const int32_t* tgt, void* scratch, void* hip_stream) {
+  if (dtype != NC_DTYPE_BF16 || !xf || !U || !tgt || !scratch) return NC_ERR_INVALID_ARG;
+  if (n <= 0 || d <= 0 || V <= 0 || n % 64 || V % 64 || d % 64 || n > (1 << 30)) return NC_ERR_SHAPE;
+  const int nblk = V / head_tile(dtype, n, d, V, 0);
+  GemmDesc g{};
+  g.M = (int)n; g.N = V; g.K = d;
+  g.P = xf; g.ldp = d; g.Q = U; g.ldq = d;
+  g.epi = EPI_LSE; g.splits = 1;
+  g.tgt = tgt;
+  g.lse_part = (float2*)scratch;
+  g.lse_stride = nblk;
+  g.ztgt = (float*)((char*)scratch + n * nblk * 8);
+  return status_of(dispatch_gemm(dtype, 0, g, (hipStream_t)hip_stream));
+}
+
 }  // extern "C"

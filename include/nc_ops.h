@@ -81,6 +81,13 @@ int nc_op_head_ce_fwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void
                       const int32_t* tgt, float* ce, float* lse, void* scratch, int32_t portable,
                       void* hip_stream);
 
+/* The first kernel of nc_op_head_ce_fwd alone: the unembedding product with
+ * its log-sum-exp epilogue, writing per-tile (max, sum of exp) partials and
+ * the target logits into `scratch` (same size and layout), without the
+ * combine.  One kernel launch, for timing the dominant kernel of the step. */
+int nc_op_head_gemm_lse(int32_t dtype, int64_t n, int32_t d, int32_t V, const void* xf, const void* U,
+                        const int32_t* tgt, void* scratch, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif
