@@ -31,10 +31,15 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 64;
-constexpr int kThreads = 512;
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ inline uint32_t lds_off(int row, int chunk) { return (uint32_t)row * 128u + ((uint32_t)(chunk ^ (row & 7)) << 4); }
+// LDS swizzle: chunk c of row r at chunk slot c ^ ((r >> 1) & 7).  gfx950's
+// LDS serves 16 lanes x 16 B (64 banks) per cycle; a fragment read takes 16
+// consecutive rows at one chunk, rows r and r+1 differ in bank half (128 B
+// rows) and the 8 even (odd) rows in slot, so the 16 reads are distinct.
+__device__ inline uint32_t lds_off(int row, int chunk) {
+  return (uint32_t)row * 128u + ((uint32_t)(chunk ^ ((row >> 1) & 7)) << 4);
+}
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -69,6 +74,12 @@ __device__ inline void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
 }
 
 typedef const u32x4 __attribute__((address_space(1)))* gptr;
+
+template <bool B, typename T>
+__device__ inline T& pick(T& a, T& b) {
+  if constexpr (B) return a;
+  else return b;
+}
 
 // Per-thread plan for one operand tile (R rows x 64 k), loaded by 256
 // threads into `reg` (8 x 16 B) and written to LDS.
@@ -135,10 +146,16 @@ struct Plan {
   __device__ inline void advance() { ptr += kstep >> 3; }
 };
 
-template <int BM, int BN, bool PT, bool QT, bool XP, bool XQ, int EPI>
-__global__ void __launch_bounds__(kThreads, 1) k_gemm_mfma(GemmDesc g) {
-  static_assert(BM % 64 == 0 && BN % 128 == 0, "tile");
-  constexpr int WTM = BM / 2, WTN = BN / 4;      // wave tile
+// NW = 8: waves in a 2 x 4 grid, wave tile (BM/2) x (BN/4), waves 0-3 stage
+//         P and waves 4-7 stage Q (two waves per SIMD).
+// NW = 4: waves in a 2 x 2 grid, wave tile (BM/2) x (BN/2) -- half the LDS
+//         fragment reads per FLOP; every thread stages both operands; the
+//         accumulators live in AGPRs (one wave per SIMD).
+template <int NW, int BM, int BN, bool PT, bool QT, bool XP, bool XQ, int EPI>
+__global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
+  static_assert(BM % 64 == 0 && BN % 128 == 0 && (NW == 4 || NW == 8), "tile");
+  constexpr int WGN = NW / 2;                    // waves along n
+  constexpr int WTM = BM / 2, WTN = BN / WGN;    // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 fragments per wave
   constexpr int STAGE = (BM + BN) * 128;         // bytes per LDS stage
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
@@ -161,13 +178,16 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_mfma(GemmDesc g) {
   const int64_t kbeg = (int64_t)blockIdx.y * kper;
   const int nk = kper / BK;
 
-  // waves 0-3 stage P tiles, waves 4-7 stage Q tiles (a wave-uniform split)
-  const bool loadsP = tid < 256;
+  // NW = 8: waves 0-3 stage P tiles, waves 4-7 stage Q tiles (a wave-uniform
+  // split).  NW = 4: every thread stages its share of both.
+  const bool loadsP = NW == 4 || tid < 256;
+  const bool loadsQ = NW == 4 || tid >= 256;
   Plan<BM, PT> pp;
   Plan<BN, QT> pq;
   if (loadsP) pp.init((const bf16*)g.P, g.ldp, m0, kbeg, tid & 255);
-  else pq.init((const bf16*)g.Q, g.ldq, n0, kbeg, tid & 255);
-  u32x4 reg[8];
+  if (loadsQ) pq.init((const bf16*)g.Q, g.ldq, n0, kbeg, tid & 255);
+  u32x4 reg[8], regq[8];
+  u32x4(&rq)[8] = pick<NW == 4>(regq, reg);   // NW = 8: a thread stages one operand only
 
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -177,14 +197,28 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_mfma(GemmDesc g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Pipeline (stage s of LDS holds tile t with s = t & 1):
+  //   iteration t:  write tile t+1 (staged in registers) to stage (t+1)&1,
+  //                 issue the global loads of tile t+2,
+  //                 k16 steps 0-2 of tile t (fragments read one step ahead),
+  //                 barrier,
+  //                 read tile t+1's step-0 fragments, then step 3 of tile t --
+  //   so the MFMAs of step 3 cover the first LDS reads after the barrier.
+  // The write of tile t+1 reuses the stage tile t-1 occupied; its last reads
+  // were issued before the previous barrier, which waits for them.
+  if (loadsP) pp.load(reg);
+  if (loadsQ) pq.load(rq);
   if (loadsP) {
-    pp.load(reg);
     pp.template store<XP>(reg, smem);
     pp.advance();
-  } else {
-    pq.load(reg);
-    pq.template store<XQ>(reg, smem + BM * 128);
+  }
+  if (loadsQ) {
+    pq.template store<XQ>(rq, smem + BM * 128);
     pq.advance();
+  }
+  if (nk > 1) {
+    if (loadsP) pp.load(reg);
+    if (loadsQ) pq.load(rq);
   }
   __syncthreads();
 
@@ -194,47 +228,52 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_mfma(GemmDesc g) {
   for (int j = 0; j < FN; ++j) offQ[j] = BM * 128 + lds_off(wn * WTN + j * 32 + frow, fchunk);
 #pragma unroll
   for (int i = 0; i < FM; ++i) offP[i] = lds_off(wm * WTM + i * 32 + frow, fchunk);
-  // chunk 2s + fchunk of a row sits at ((2s + fchunk) ^ (row & 7)) = (fchunk ^ (row & 7)) ^ 2s
-  // since 2s only touches bits 1-2: the k16 step s moves the byte offset by an xor of 32*s
+  // chunk 2s + fchunk sits at slot (2s + fchunk) ^ f(row) = (fchunk ^ f(row)) ^ 2s:
+  // the k16 step s moves the byte offset by an xor of 32*s
+
+  bf16x8 a[2][FN], bb[2][FM];
+  auto read_frags = [&](const char* st, int s, int buf) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) a[buf][j] = *reinterpret_cast<const bf16x8*>(st + (offQ[j] ^ (32u * s)));
+#pragma unroll
+    for (int i = 0; i < FM; ++i) bb[buf][i] = *reinterpret_cast<const bf16x8*>(st + (offP[i] ^ (32u * s)));
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[buf][j], bb[buf][i], acc[i][j], 0, 0, 0);
+  };
+  read_frags(smem, 0, 0);
 
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      if (loadsP) pp.load(reg); else pq.load(reg);
-    }
     const char* st = smem + (kt & 1) * STAGE;
-    bf16x8 a[2][FN], bb[2][FM];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) a[0][j] = *reinterpret_cast<const bf16x8*>(st + offQ[j]);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) bb[0][i] = *reinterpret_cast<const bf16x8*>(st + offP[i]);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int cur = s & 1, nxt = cur ^ 1;
-      if (s + 1 < BK / 16) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) a[nxt][j] = *reinterpret_cast<const bf16x8*>(st + (offQ[j] ^ (32u * (s + 1))));
-#pragma unroll
-        for (int i = 0; i < FM; ++i) bb[nxt][i] = *reinterpret_cast<const bf16x8*>(st + (offP[i] ^ (32u * (s + 1))));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][j], bb[cur][i], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      char* nx = smem + ((kt + 1) & 1) * STAGE;
+    char* nx = smem + ((kt + 1) & 1) * STAGE;
+    if (kt + 1 < nk) {
       if (loadsP) {
         pp.template store<XP>(reg, nx);
         pp.advance();
-      } else {
-        pq.template store<XQ>(reg, nx + BM * 128);
+      }
+      if (loadsQ) {
+        pq.template store<XQ>(rq, nx + BM * 128);
         pq.advance();
       }
+      if (kt + 2 < nk) {
+        if (loadsP) pp.load(reg);
+        if (loadsQ) pq.load(rq);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < BK / 16 - 1; ++s) {
+      read_frags(st, s + 1, (s + 1) & 1);
+      mfmas(s & 1);
     }
     __syncthreads();
+    if (kt + 1 < nk) read_frags(nx, 0, 0);
+    mfmas((BK / 16 - 1) & 1);
   }
+  __syncthreads();
 
   // ------------------------------------------------------------------ epilogue
   // lane holds row m = m0 + wm*WTM + i*32 + (lane&31) and, for register
@@ -271,16 +310,16 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_mfma(GemmDesc g) {
     }
     __syncthreads();
     if (tid < BM) {
-      float2 p[4];
+      float2 p[WGN];
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < WGN; ++w) {
         p[w] = red[w * BM + tid];
         M = fmaxf(M, p[w].x);
       }
       float S = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) S += p[w].y * __builtin_amdgcn_exp2f((p[w].x - M) * kLog2e);
+      for (int w = 0; w < WGN; ++w) S += p[w].y * __builtin_amdgcn_exp2f((p[w].x - M) * kLog2e);
       g.lse_part[(m0 + tid) * g.lse_stride + tn] = make_float2(M, S);
     }
     return;
@@ -352,10 +391,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_gemm_mfma(GemmDesc g) {
   }
 }
 
-template <int BM, int BN, bool PT, bool QT, bool XP, bool XQ, int EPI>
+template <int NW, int BM, int BN, bool PT, bool QT, bool XP, bool XQ, int EPI>
 hipError_t launch(const GemmDesc& g, hipStream_t s) {
   dim3 grid((g.M / BM) * (g.N / BN), g.splits);
-  k_gemm_mfma<BM, BN, PT, QT, XP, XQ, EPI><<<grid, kThreads, 0, s>>>(g);
+  k_gemm_mfma<NW, BM, BN, PT, QT, XP, XQ, EPI><<<grid, NW * 64, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -397,17 +436,18 @@ inline bool combo_supported(const GemmDesc& g) {
   return false;
 }
 
-template <int BM, int BN>
+template <int NW, int BM, int BN>
 hipError_t dispatch(const GemmDesc& g, hipStream_t s) {
 #define NC_X(PT, QT, XP, XQ, EPI) \
   if (g.p_trans == PT && g.q_trans == QT && g.p_relu2 == XP && g.q_relu2 == XQ && g.epi == EPI) \
-    return launch<BM, BN, PT, QT, XP, XQ, EPI>(g, s);
+    return launch<NW, BM, BN, PT, QT, XP, XQ, EPI>(g, s);
   NC_MFMA_COMBOS(NC_X)
 #undef NC_X
   return hipErrorInvalidValue;
 }
 
 hipError_t gemm_256x256(const GemmDesc& g, hipStream_t s);
+hipError_t gemm_256x256_w4(const GemmDesc& g, hipStream_t s);
 hipError_t gemm_256x128(const GemmDesc& g, hipStream_t s);
 hipError_t gemm_128x128(const GemmDesc& g, hipStream_t s);
 }  // namespace mfma

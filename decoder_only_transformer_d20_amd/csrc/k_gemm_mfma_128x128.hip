@@ -3,6 +3,6 @@
 
 namespace nc {
 namespace mfma {
-hipError_t gemm_128x128(const GemmDesc& g, hipStream_t s) { return dispatch<128, 128>(g, s); }
+hipError_t gemm_128x128(const GemmDesc& g, hipStream_t s) { return dispatch<8, 128, 128>(g, s); }
 }  // namespace mfma
 }  // namespace nc

@@ -3,6 +3,6 @@
 
 namespace nc {
 namespace mfma {
-hipError_t gemm_256x128(const GemmDesc& g, hipStream_t s) { return dispatch<256, 128>(g, s); }
+hipError_t gemm_256x128(const GemmDesc& g, hipStream_t s) { return dispatch<8, 256, 128>(g, s); }
 }  // namespace mfma
 }  // namespace nc
