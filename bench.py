@@ -2,18 +2,31 @@
 one MI355X, through the C ABI (include/nc.h).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d20]
-                    [--no-cpu-baseline] [--no-roofline]
+                    [--no-cpu-baseline] [--no-roofline] [--copy-calibration]
 
 Prints one JSON line.  `value` is training tokens/s of the whole job with
-inputs already resident in HBM; MFU uses the FLOP convention of
-decoder_only_transformer_d20_amd.flops against the bf16 dense MFMA peak.
-`roofline` reports the dominant kernel (the unembedding + log-sum-exp GEMM)
-timed live with HIP events on its own stream; `cpu_baseline` times the fp64
-oracle on a bounded prefix of one row on this host's cores.
+inputs already resident in HBM (host-to-device copies happen before timing);
+MFU uses the FLOP convention of decoder_only_transformer_d20_amd.flops
+against the bf16 dense MFMA peak of 2.5 PFLOP/s.
+
+`roofline`: one untimed traced step per kernel family ranks the families by
+time; during the timed steps the largest family's launches are bracketed by
+HIP events on the library's stream (nc_trace_*), and `achieved` is its
+algorithmic FLOPs per launch divided by its average launch time.
+`traffic` is the HBM traffic per launch measured with rocprofv3 FETCH_SIZE /
+WRITE_SIZE counters (calibrated against a plain device copy), reported only
+while the measured kernel's source is unchanged.
+
+`cpu_baseline`: the fp64 oracle (untuned) on a 512-token prefix of row 0 --
+forward, loss and backward -- on this host's cores.
+
+`--copy-calibration` only runs a 1 GiB device-to-device copy (the reference
+kernel for scaling the FETCH_SIZE / WRITE_SIZE counters) and exits.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +38,12 @@ sys.path.insert(0, ROOT)
 METRIC = "train tokens/s + MFU (fwd+bwd) on 1 MI355X, d20 at 32x2048 tok/step"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# on `python bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-roofline`,
+# scaled by the counters' reading for --copy-calibration (see profiles/).
+# Keyed by family; valid only for the recorded hash of the kernel source.
+TRAFFIC = {}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -34,8 +53,19 @@ def parse():
     ap.add_argument("--config", default="d20")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     return ap.parse_args()
+
+
+def kernel_source_hash(family: str) -> str:
+    src = "attn_mfma.h" if family.startswith("attn") else "gemm_mfma.h"
+    csrc = os.path.join(ROOT, "decoder_only_transformer_d20_amd", "csrc")
+    names = [src, "k_attn_mfma.hip"] if family.startswith("attn") else [src]
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(csrc, n), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def to_dev(a, bf16):
@@ -47,12 +77,28 @@ def to_dev(a, bf16):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import numpy as np
     import torch
     import synthdata
@@ -60,6 +106,8 @@ def main():
     from decoder_only_transformer_d20_amd.flops import flops_per_step, flops_per_token, flops_per_token_causal
 
     cfg = synthdata.get_config(args.config)
+    if cfg.block_only:
+        sys.exit("bench.py times the full model; use a model configuration")
     bf16 = cfg.dtype == "bf16"
     N = cfg.batch * cfg.seq_len
     t0 = time.time()
@@ -75,7 +123,6 @@ def main():
     ce = torch.empty(N, dtype=torch.float32, device="cuda")
     out = torch.empty(5, dtype=torch.float64, device="cuda")
     G = torch.empty(params.size, dtype=torch.float32, device="cuda")
-    del params
 
     def step():
         sess.forward(P, I, Tg, ce)
@@ -86,6 +133,22 @@ def main():
         step()
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    # per-family breakdown (untimed): one traced step per family
+    families = {}
+    dominant = None
+    if not args.no_roofline:
+        for f in nc.TRACE_FAMILIES:
+            sess.trace_enable(f)
+            step()
+            n, ms, fl, by = sess.trace_read()
+            if n:
+                families[f] = {"launches": n, "ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+        sess.trace_enable(None)
+        dominant = max(families, key=lambda f: families[f]["ms"]) if families else None
+        if dominant:
+            sess.trace_enable(dominant)
+
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -132,71 +195,52 @@ def main():
         "grads_finite": grads_finite,
     }
 
-    if not args.no_roofline and not cfg.block_only:
-        result["roofline"] = roofline_head(cfg, sess, P, Tg, nc, torch)
+    if dominant:
+        n, tms, fl, by = sess.trace_read()
+        sess.trace_enable(None)
+        avg = tms / n * 1e-3
+        achieved = fl / n / avg / 1e12
+        tr = TRAFFIC.get(dominant)
+        traffic = tr["bytes_per_launch"] if tr and tr["source_hash"] == kernel_source_hash(dominant) else None
+        result["roofline"] = {
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_family": dominant,
+            "launches_timed": n,
+            "avg_launch_ms": round(tms / n, 4),
+            "flops_per_launch": fl / n,
+            "algorithmic_bytes_per_launch": by / n,
+            "kernel_source_hash": kernel_source_hash(dominant),
+        }
+        result["kernel_families"] = families
+    del P, G
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
+        result["cpu_baseline"] = cpu_baseline(cfg, params, idx, tgt, tb, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)
 
 
-def roofline_head(cfg, sess, P, Tg, nc, torch):
-    """Dominant kernel: the unembedding GEMM with the fused log-sum-exp
-    epilogue (k_gemm_mfma<256,256,...,EPI_LSE>), launched alone at the
-    step's shape through nc_op_head_gemm_lse and timed with HIP events on the
-    stream it runs on.  Algorithmic work per launch = 2 * (B*T) * V * d."""
-    N, d, V = cfg.batch * cfg.seq_len, cfg.d_model, cfg.vocab
-    xf = torch.randn(N * d, device="cuda").to(torch.bfloat16).view(torch.int16)
-    U_off, _, _ = nc.param_offset(cfg, "U")
-    U = P[U_off:U_off + V * d]
-    scratch = torch.empty(nc.ops.head_scratch_bytes(1, N, d, V, 0) // 4 + 64, dtype=torch.float32, device="cuda")
-    s = torch.cuda.current_stream()
-    for _ in range(2):
-        nc.ops.head_gemm_lse(1, N, d, V, xf, U, Tg, scratch, s.cuda_stream)
-    iters = 5
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(s)
-    for _ in range(iters):
-        nc.ops.head_gemm_lse(1, N, d, V, xf, U, Tg, scratch, s.cuda_stream)
-    e1.record(s)
-    torch.cuda.synchronize()
-    dur = e0.elapsed_time(e1) / iters * 1e-3
-    flops = 2.0 * N * V * d
-    achieved = flops / dur / 1e12
-    return {
-        "kernel": "k_gemm_mfma<256,256,...,EPI_LSE> (unembedding GEMM + log-sum-exp partials)",
-        "bound": "mfma",
-        "achieved": round(achieved, 1),
-        "peak": PEAK_BF16_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
-        "launch_ms": round(dur * 1e3, 4),
-        "flops_per_launch": flops,
-    }
-
-
-def cpu_baseline(cfg, sample_tokens):
-    """The fp64 oracle (untuned) on the first `sample_tokens` tokens of row 0:
-    forward + loss + backward of that causal prefix.  Rows are independent and
-    the prefix's losses equal the full row's at those positions, so this is a
-    bounded slice of the same workload; per-token attention work grows with
-    the prefix length, so it slightly flatters the oracle against full rows."""
-    import numpy as np
+def cpu_baseline(cfg, params, idx, tgt, tb, sample_tokens):
+    """The fp64 oracle (as written, untuned) on the first `sample_tokens`
+    tokens of row 0: forward + loss + backward of that causal prefix.  Rows
+    are independent and a prefix's losses equal the full row's at those
+    positions, so this is a bounded slice of the same workload; per-token
+    attention work grows with position, so a prefix slightly flatters the
+    oracle against full 2048-token rows."""
     import synthdata
     import oracle
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    params = synthdata.make_params(cfg)
-    idx, tgt = synthdata.make_tokens(cfg, rows=1)
-    tb = synthdata.make_token_bytes(cfg)
     T = min(sample_tokens, cfg.seq_len)
     c = cfg.with_(batch=1, seq_len=T)
     p = synthdata.split_params(cfg, params)
     t0 = time.time()
-    oracle.train_step(c, p, idx[:, :T], tgt[:, :T], tb)
+    oracle.train_step(c, p, idx[:1, :T], tgt[:1, :T], tb)
     dt = time.time() - t0
     return {
         "value": round(T / dt, 3),
@@ -204,7 +248,7 @@ def cpu_baseline(cfg, sample_tokens):
         "cores": cores,
         "kind": "oracle",
         "sample": f"fp64 numpy oracle fwd+loss+bwd on the first {T} tokens of row 0 of the {cfg.name} "
-                  f"workload ({dt:.1f} s)",
+                  f"workload ({dt:.1f} s wall)",
     }
 
 

@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnc.so")
 DTYPE_F32, DTYPE_BF16 = 0, 1
 FLAG_BLOCK_ONLY, FLAG_PORTABLE_KERNELS = 1, 2
 TENSOR_IDS = {"E": 0, "Wq": 1, "Wk": 2, "Wv": 3, "Wo": 4, "W1": 5, "W2": 6, "U": 7}
+TRACE_FAMILIES = ["qkv", "attn_out", "mlp_up", "mlp_down", "head_lse", "head_dz", "dgrad", "dh", "wgrad",
+                  "wgrad_relu2", "attn_fwd", "attn_bwd"]
 
 
 class NcConfig(ctypes.Structure):
@@ -60,6 +62,9 @@ _SIGS = {
     "nc_backward": (ctypes.c_int, [_P, _P, _P, _I32]),
     "nc_block_forward": (ctypes.c_int, [_P, _P, _P, _P]),
     "nc_block_backward": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32]),
+    "nc_trace_enable": (ctypes.c_int, [_P, _I32]),
+    "nc_trace_read": (ctypes.c_int, [_P, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "nc_op_matmul": (ctypes.c_int, [_I32, _I32, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I32, _P, _I32, _P]),
     "nc_op_rmsnorm_fwd": (ctypes.c_int, [_I32, _I64, _I32, _F32, _P, _P, _P, _P]),
     "nc_op_rmsnorm_bwd": (ctypes.c_int, [_I32, _I64, _I32, _P, _P, _P, _P, _I32, _P]),
@@ -174,6 +179,19 @@ class Context:
 
     def backward(self, params, grads, accumulate: bool = False):
         _check(lib().nc_backward(self.h, _ptr(params), _ptr(grads), int(bool(accumulate))), "nc_backward", self.h)
+
+    def trace_enable(self, family):
+        """Time launches of one kernel family (a name from TRACE_FAMILIES or
+        its index; None disables)."""
+        f = -1 if family is None else (TRACE_FAMILIES.index(family) if isinstance(family, str) else int(family))
+        _check(lib().nc_trace_enable(self.h, f), "nc_trace_enable", self.h)
+
+    def trace_read(self):
+        """(launches, total ms, total algorithmic FLOPs, total algorithmic bytes)."""
+        n, ms, fl, by = _I64(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        _check(lib().nc_trace_read(self.h, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(by)),
+               "nc_trace_read", self.h)
+        return n.value, ms.value, fl.value, by.value
 
     def block_forward(self, params, x, y):
         _check(lib().nc_block_forward(self.h, _ptr(params), _ptr(x), _ptr(y)), "nc_block_forward", self.h)

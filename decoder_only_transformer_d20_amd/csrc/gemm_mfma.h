@@ -11,14 +11,14 @@
 // pieces of a row, and row-wise reductions (log-sum-exp) stay in a lane.
 //
 // Both operand tiles live in LDS as [row][64 k] bf16 (128 B per row), the
-// 16-byte chunk c of row r stored at chunk c ^ (r & 7): a fragment read
-// (32 rows x one chunk) and a row write both hit 8 distinct chunk slots per
-// 8 lanes.  Operands stored k-major ([rows][K]) are copied in 16-byte
-// pieces; operands stored row-major in k ([K][rows], the backward pass's
-// transposed products) are read as 8 x 8 blocks and transposed in
-// registers before the LDS write, so every layout reaches the same LDS
-// image.  Two LDS stages: the global loads of tile k+1 are in flight while
-// tile k is multiplied; one barrier per tile.
+// 16-byte chunk c of row r stored at chunk slot c ^ ((r >> 1) & 7) (see
+// lds_off): fragment reads and row writes are free of bank conflicts.
+// Operands stored k-major ([rows][K]) are copied in 16-byte pieces;
+// operands stored row-major in k ([K][rows], the backward pass's transposed
+// products) are read as 8 x 8 blocks and transposed in registers before the
+// LDS write, so every layout reaches the same LDS image.  Two LDS stages
+// and one register stage: the global loads of tile k+2 are in flight while
+// tile k is multiplied and tile k+1 is written; one barrier per tile.
 #pragma once
 
 #include "nc_internal.h"
@@ -147,10 +147,11 @@ struct Plan {
 };
 
 // NW = 8: waves in a 2 x 4 grid, wave tile (BM/2) x (BN/4), waves 0-3 stage
-//         P and waves 4-7 stage Q (two waves per SIMD).
+//         P and waves 4-7 stage Q (two waves per SIMD).  The library uses this.
 // NW = 4: waves in a 2 x 2 grid, wave tile (BM/2) x (BN/2) -- half the LDS
 //         fragment reads per FLOP; every thread stages both operands; the
-//         accumulators live in AGPRs (one wave per SIMD).
+//         accumulators live in AGPRs (one wave per SIMD).  Measured 10-15%
+//         slower on the d20 shapes, so it is not instantiated.
 template <int NW, int BM, int BN, bool PT, bool QT, bool XP, bool XQ, int EPI>
 __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   static_assert(BM % 64 == 0 && BN % 128 == 0 && (NW == 4 || NW == 8), "tile");
@@ -447,7 +448,6 @@ hipError_t dispatch(const GemmDesc& g, hipStream_t s) {
 }
 
 hipError_t gemm_256x256(const GemmDesc& g, hipStream_t s);
-hipError_t gemm_256x256_w4(const GemmDesc& g, hipStream_t s);
 hipError_t gemm_256x128(const GemmDesc& g, hipStream_t s);
 hipError_t gemm_128x128(const GemmDesc& g, hipStream_t s);
 }  // namespace mfma

@@ -1,6 +1,4 @@
 // bf16 MFMA GEMM: shape checks and tile selection (kernels in gemm_mfma.h).
-#include <cstdlib>
-
 #include "gemm_mfma.h"
 
 namespace nc {
@@ -20,14 +18,16 @@ bool gemm_mfma_supported(const GemmDesc& g) {
   return mfma::combo_supported(g);
 }
 
-hipError_t gemm_mfma_bf16(const GemmDesc& g, hipStream_t s) {
+hipError_t gemm_mfma_bf16_product(const GemmDesc& g, hipStream_t s) {
   if (!gemm_mfma_supported(g)) return hipErrorInvalidValue;
   const int bm = gemm_mfma_tile_m(g.M, g.N), bn = gemm_mfma_tile_n(g.M, g.N);
-  hipError_t e;
-  static const int waves = getenv("NC_GEMM_WAVES") ? atoi(getenv("NC_GEMM_WAVES")) : 8;
-  if (bm == 256 && bn == 256) e = waves == 4 ? mfma::gemm_256x256_w4(g, s) : mfma::gemm_256x256(g, s);
-  else if (bm == 256) e = mfma::gemm_256x128(g, s);
-  else e = mfma::gemm_128x128(g, s);
+  if (bm == 256 && bn == 256) return mfma::gemm_256x256(g, s);
+  if (bm == 256) return mfma::gemm_256x128(g, s);
+  return mfma::gemm_128x128(g, s);
+}
+
+hipError_t gemm_mfma_bf16(const GemmDesc& g, hipStream_t s) {
+  hipError_t e = gemm_mfma_bf16_product(g, s);
   if (e == hipSuccess && g.epi == EPI_F32 && g.splits > 1) {
     if (g.ldc != g.N) return hipErrorInvalidValue;
     e = splitk_reduce(g.part, g.splits, (int64_t)g.M * g.N, (float*)g.C, g.beta, s);

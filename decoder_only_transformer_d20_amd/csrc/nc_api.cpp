@@ -11,6 +11,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "nc.h"
 #include "nc_ops.h"
@@ -153,9 +154,17 @@ struct nc_ctx {
   bool have_forward = false;
   bool have_block_forward = false;
   std::string err;
+  // kernel timing (nc_trace_*)
+  int trace_family = -1;
+  std::vector<hipEvent_t> ev;      // start/end pairs, created on demand
+  size_t n_rec = 0;
+  double trace_flops = 0.0, trace_bytes = 0.0;
 
   template <typename T> T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
   char* layer(int l) { return ws + plan.layer0 + plan.layer_stride * (size_t)l; }
+  ~nc_ctx() {
+    for (hipEvent_t e : ev) hipEventDestroy(e);
+  }
 };
 
 namespace {
@@ -170,10 +179,70 @@ int fail(nc_ctx* ctx, hipError_t e, const char* what) {
     if (e_ != hipSuccess) return fail(ctx, e_, what); \
   } while (0)
 
+// ---- kernel timing -----------------------------------------------------------
+constexpr size_t kMaxTrace = 65536;
+
+int gemm_family(const GemmDesc& g) {
+  const int key = g.p_trans * 16 + g.q_trans * 8 + g.p_relu2 * 4 + g.q_relu2 * 2;
+  switch (g.epi) {
+    case EPI_ROPE: return key == 0 ? NC_TRACE_QKV : -1;
+    case EPI_RESID: return key == 0 ? NC_TRACE_ATTN_OUT : key == 4 ? NC_TRACE_MLP_DOWN : -1;
+    case EPI_STORE: return key == 0 ? NC_TRACE_MLP_UP : key == 8 ? NC_TRACE_DGRAD : -1;
+    case EPI_LSE: return key == 0 ? NC_TRACE_HEAD_LSE : -1;
+    case EPI_DZ: return key == 0 ? NC_TRACE_HEAD_DZ : -1;
+    case EPI_DRELU2: return key == 8 ? NC_TRACE_DH : -1;
+    case EPI_F32: return key == 24 ? NC_TRACE_WGRAD : key == 26 ? NC_TRACE_WGRAD_RELU2 : -1;
+    default: return -1;
+  }
+}
+
+// algorithmic HBM bytes of one product: operands read once, result written once
+double gemm_bytes(const GemmDesc& g, size_t es) {
+  const double M = g.M, N = g.N, K = g.K;
+  double b = (M * K + N * K) * es;
+  switch (g.epi) {
+    case EPI_F32: b += M * N * 4.0 * (g.beta ? 2 : 1); break;
+    case EPI_LSE: b += M * 4.0 * 2; break;                       // targets in, z[target] out
+    case EPI_DZ: b += M * N * es + M * 8.0; break;
+    case EPI_RESID:
+    case EPI_DRELU2: b += 2.0 * M * N * es; break;
+    default: b += M * N * es; break;
+  }
+  return b;
+}
+
+// run `launch` bracketed by events when `family` is being traced
+template <typename F>
+hipError_t traced(nc_ctx* ctx, int family, double flops, double bytes, F&& launch) {
+  if (family < 0 || family != ctx->trace_family || ctx->n_rec >= kMaxTrace) return launch();
+  if (ctx->ev.size() < 2 * (ctx->n_rec + 1)) {
+    for (int i = 0; i < 2; ++i) {
+      hipEvent_t e;
+      hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) return r;
+      ctx->ev.push_back(e);
+    }
+  }
+  hipError_t r = hipEventRecord(ctx->ev[2 * ctx->n_rec], ctx->stream);
+  if (r != hipSuccess) return r;
+  r = launch();
+  if (r != hipSuccess) return r;
+  r = hipEventRecord(ctx->ev[2 * ctx->n_rec + 1], ctx->stream);
+  if (r != hipSuccess) return r;
+  ctx->n_rec++;
+  ctx->trace_flops += flops;
+  ctx->trace_bytes += bytes;
+  return hipSuccess;
+}
+
 hipError_t run_gemm(nc_ctx* ctx, const GemmDesc& g) {
   if (!is_bf16(ctx->cfg)) return gemm_portable<float>(g, ctx->stream);
   if (portable(ctx->cfg) || !gemm_mfma_supported(g)) return gemm_portable<bf16>(g, ctx->stream);
-  return gemm_mfma_bf16(g, ctx->stream);
+  hipError_t e = traced(ctx, gemm_family(g), 2.0 * g.M * g.N * g.K, gemm_bytes(g, 2),
+                        [&] { return gemm_mfma_bf16_product(g, ctx->stream); });
+  if (e == hipSuccess && g.epi == EPI_F32 && g.splits > 1)
+    e = splitk_reduce(g.part, g.splits, (int64_t)g.M * g.N, (float*)g.C, g.beta, ctx->stream);
+  return e;
 }
 
 GemmDesc gemm(int M, int N, int K, const void* P, int64_t ldp, int pt, const void* Q, int64_t ldq, int qt, int epi,
@@ -198,12 +267,26 @@ hipError_t weight_grad(nc_ctx* ctx, int Mw, int Nw, const void* P, int64_t ldp, 
   return run_gemm(ctx, g);
 }
 
+// causal score pairs of one step: B * H * T (T + 1) / 2
+double attn_pairs(const AttnDesc& a) { return (double)a.B * a.H * (double)a.T * (a.T + 1) / 2.0; }
+
 template <typename T> hipError_t attn_fwd(nc_ctx* ctx, const AttnDesc& a) {
-  if (!portable(ctx->cfg) && attn_mfma_supported(a)) return attn_fwd_mfma(a, ctx->stream);
+  if (!portable(ctx->cfg) && attn_mfma_supported(a)) {
+    // S = Q K^T and O = P V over the causal pairs; q,k,v read, o and lse written
+    const double tok = (double)a.B * a.T, d = (double)a.H * a.Q;
+    return traced(ctx, NC_TRACE_ATTN_FWD, 2 * 2.0 * attn_pairs(a) * a.Q, tok * (3 * d + d) * 2 + tok * a.H * 4,
+                  [&] { return attn_fwd_mfma(a, ctx->stream); });
+  }
   return attn_fwd_portable<T>(a, ctx->stream);
 }
 template <typename T> hipError_t attn_bwd(nc_ctx* ctx, const AttnDesc& a) {
-  if (!portable(ctx->cfg) && attn_mfma_supported(a)) return attn_bwd_mfma(a, ctx->stream);
+  if (!portable(ctx->cfg) && attn_mfma_supported(a)) {
+    // flash backward: recompute S, then dV, dP, dQ, dK (5 causal products);
+    // q,k,v,o,dO read, dq,dk,dv written
+    const double tok = (double)a.B * a.T, d = (double)a.H * a.Q;
+    return traced(ctx, NC_TRACE_ATTN_BWD, 5 * 2.0 * attn_pairs(a) * a.Q, tok * (5 * d + 3 * d) * 2 + tok * a.H * 8,
+                  [&] { return attn_bwd_mfma(a, ctx->stream); });
+  }
   return attn_bwd_portable<T>(a, ctx->stream);
 }
 
@@ -472,6 +555,32 @@ int nc_set_stream(nc_ctx* ctx, void* hip_stream) {
 }
 
 void nc_destroy(nc_ctx* ctx) { delete ctx; }
+
+int nc_trace_enable(nc_ctx* ctx, int32_t family) {
+  if (!ctx) return NC_ERR_INVALID_ARG;
+  if (family < -1 || family >= NC_TRACE_COUNT) return NC_ERR_INVALID_ARG;
+  ctx->trace_family = family;
+  ctx->n_rec = 0;
+  ctx->trace_flops = ctx->trace_bytes = 0.0;
+  return NC_OK;
+}
+
+int nc_trace_read(nc_ctx* ctx, int64_t* launches, double* ms, double* flops, double* bytes) {
+  if (!ctx) return NC_ERR_INVALID_ARG;
+  double total = 0.0;
+  for (size_t i = 0; i < ctx->n_rec; ++i) {
+    float t = 0.f;
+    hipError_t e = hipEventSynchronize(ctx->ev[2 * i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, ctx->ev[2 * i], ctx->ev[2 * i + 1]);
+    if (e != hipSuccess) return fail(ctx, e, "trace read");
+    total += t;
+  }
+  if (launches) *launches = (int64_t)ctx->n_rec;
+  if (ms) *ms = total;
+  if (flops) *flops = ctx->trace_flops;
+  if (bytes) *bytes = ctx->trace_bytes;
+  return NC_OK;
+}
 
 const char* nc_last_error(const nc_ctx* ctx) { return ctx ? ctx->err.c_str() : "null context"; }
 

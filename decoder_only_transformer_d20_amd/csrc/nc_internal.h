@@ -90,7 +90,8 @@ struct AttnDesc {
 // launchers (all enqueue on `s`; return hipError_t of the launch)
 // ---------------------------------------------------------------------------
 template <typename T> hipError_t gemm_portable(const GemmDesc& g, hipStream_t s);
-hipError_t gemm_mfma_bf16(const GemmDesc& g, hipStream_t s);
+hipError_t gemm_mfma_bf16(const GemmDesc& g, hipStream_t s);          // product + split-K reduce
+hipError_t gemm_mfma_bf16_product(const GemmDesc& g, hipStream_t s);  // the product kernel alone
 bool gemm_mfma_supported(const GemmDesc& g);
 int gemm_mfma_tile_m(int M, int N);   // tile sizes the MFMA GEMM picks for an M x N output
 int gemm_mfma_tile_n(int M, int N);

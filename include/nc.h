@@ -172,6 +172,40 @@ int nc_block_forward(nc_ctx* ctx, const void* block_params, const void* x, void*
 int nc_block_backward(nc_ctx* ctx, const void* block_params, const void* dy,
                       void* dx, float* dparams, int32_t accumulate);
 
+/* ---- kernel timing (for roofline reports) --------------------------------- */
+
+/* Kernel families of the step.  Each GEMM family is one matrix-core kernel
+ * (one operand layout + epilogue); the attention families are the forward
+ * kernel and the three backward kernels together. */
+enum {
+  NC_TRACE_QKV = 0,        /* a Wqkv^T with the rotary epilogue            */
+  NC_TRACE_ATTN_OUT,       /* x + o Wo^T                                    */
+  NC_TRACE_MLP_UP,         /* m W1^T                                        */
+  NC_TRACE_MLP_DOWN,       /* x + relu(h)^2 W2^T                            */
+  NC_TRACE_HEAD_LSE,       /* xf U^T with the log-sum-exp epilogue          */
+  NC_TRACE_HEAD_DZ,        /* xf U^T recomputed, softmax - onehot           */
+  NC_TRACE_DGRAD,          /* activation gradients g W (dm, do, da, dxf)    */
+  NC_TRACE_DH,             /* (g W2) * 2 relu(h)                            */
+  NC_TRACE_WGRAD,          /* weight gradients dWo, dW1, dWqkv, dU          */
+  NC_TRACE_WGRAD_RELU2,    /* dW2 = g^T relu(h)^2                           */
+  NC_TRACE_ATTN_FWD,
+  NC_TRACE_ATTN_BWD,
+  NC_TRACE_COUNT
+};
+
+/* While enabled, every launch of `family` inside the model-level calls is
+ * bracketed by HIP events recorded on the context's stream (host-side event
+ * objects; no device memory).  family = -1 disables.  Enabling resets the
+ * counters.  At most 65536 launches are recorded. */
+int nc_trace_enable(nc_ctx* ctx, int32_t family);
+
+/* Wait for the recorded events and report the family's launches: count,
+ * summed duration (ms), summed algorithmic FLOPs (2*M*N*K per product; the
+ * attention families count the causal products they compute) and summed
+ * algorithmic HBM bytes (operands read once + result written once).  Any
+ * pointer may be NULL. */
+int nc_trace_read(nc_ctx* ctx, int64_t* launches, double* ms, double* flops, double* bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,8 +20,19 @@ torch = pytest.importorskip("torch")
 import decoder_only_transformer_d20_amd as nc  # noqa: E402
 
 
+_PARAMS = {}
+
+
+def _params(cfg):
+    # drawing the d20 weights takes ~15 s: share one draw per configuration
+    if cfg.name not in _PARAMS:
+        _PARAMS.clear()
+        _PARAMS[cfg.name] = synthdata.make_params(cfg)
+    return _PARAMS[cfg.name]
+
+
 def _inputs(cfg, rows=None, ignore=()):
-    params = synthdata.make_params(cfg)
+    params = _params(cfg)
     idx, tgt = synthdata.make_tokens(cfg, rows=rows)
     tgt = tgt.copy()
     for (b, t) in ignore:
@@ -154,6 +165,7 @@ def test_block_real_shape_two_rows():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(600)
 def test_block_full_batch_sampled_rows():
     """The block at the full 32 x 2048 launch; rows 0 and 31 against the
     oracle (rows are independent in y and dx)."""
@@ -168,6 +180,7 @@ def test_block_full_batch_sampled_rows():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_d20_one_row_matches_oracle():
     """The full d20 model (20 layers, vocab 65,536) on one 2048-token row."""
     cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("d20"), rows=1)
@@ -180,6 +193,7 @@ def test_d20_one_row_matches_oracle():
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(600)
 def test_d20_full_batch_consistency():
     """The benchmarked launch (32 x 2048): row 0's losses equal those of the
     one-row run (rows never interact and every reduction order is fixed per
