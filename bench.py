@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     return ap.parse_args()
 
 
@@ -145,7 +145,8 @@ def main():
             if n:
                 families[f] = {"launches": n, "ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
         sess.trace_enable(None)
-        dominant = max(families, key=lambda f: families[f]["ms"]) if families else None
+        single = [f for f in families if f in nc.SINGLE_KERNEL_FAMILIES]
+        dominant = max(single, key=lambda f: families[f]["ms"]) if single else None
         if dominant:
             sess.trace_enable(dominant)
 

@@ -22,8 +22,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnc.so")
 DTYPE_F32, DTYPE_BF16 = 0, 1
 FLAG_BLOCK_ONLY, FLAG_PORTABLE_KERNELS = 1, 2
 TENSOR_IDS = {"E": 0, "Wq": 1, "Wk": 2, "Wv": 3, "Wo": 4, "W1": 5, "W2": 6, "U": 7}
-TRACE_FAMILIES = ["qkv", "attn_out", "mlp_up", "mlp_down", "head_lse", "head_dz", "dgrad", "dh", "wgrad",
-                  "wgrad_relu2", "attn_fwd", "attn_bwd"]
+# nc.h NC_TRACE_* in order; every family but attn_bwd is a single kernel
+TRACE_FAMILIES = ["gemm_qkv_rope", "gemm_residual", "gemm_relu2", "gemm_head_lse", "gemm_head_dz", "gemm_dgrad",
+                  "gemm_dgrad_relu2", "gemm_wgrad", "attn_fwd", "attn_bwd"]
+SINGLE_KERNEL_FAMILIES = TRACE_FAMILIES[:-1]
 
 
 class NcConfig(ctypes.Structure):

@@ -49,16 +49,6 @@ __device__ inline uint32_t f2bf(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 __device__ inline uint32_t pack2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
-__device__ inline float relu2f(float x) {
-  x = fmaxf(x, 0.f);
-  return x * x;
-}
-__device__ inline uint32_t relu2_pair(uint32_t w) { return pack2(relu2f(bf_lo(w)), relu2f(bf_hi(w))); }
-__device__ inline u32x4 relu2_chunk(u32x4 v) {
-  u32x4 r;
-  r[0] = relu2_pair(v[0]); r[1] = relu2_pair(v[1]); r[2] = relu2_pair(v[2]); r[3] = relu2_pair(v[3]);
-  return r;
-}
 
 // 8 x 8 bf16 transpose: in[kk] holds 8 consecutive rows' elements at one k;
 // out[e] holds row e's 8 consecutive k values.
@@ -123,24 +113,15 @@ struct Plan {
       for (int kk = 0; kk < 8; ++kk) reg[kk] = ptr[(kk * step) >> 3];
     }
   }
-  template <bool XF>
   __device__ inline void store(const u32x4 (&reg)[8], char* lds_base) const {
     if (!TRANS) {
 #pragma unroll
-      for (int i = 0; i < R / 32; ++i) {
-        u32x4 v = reg[i];
-        if (XF) v = relu2_chunk(v);
-        *reinterpret_cast<u32x4*>(lds_base + lds[i]) = v;
-      }
+      for (int i = 0; i < R / 32; ++i) *reinterpret_cast<u32x4*>(lds_base + lds[i]) = reg[i];
     } else if (active) {
       u32x4 t[8];
       transpose8(reg, t);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u32x4 v = t[e];
-        if (XF) v = relu2_chunk(v);
-        *reinterpret_cast<u32x4*>(lds_base + lds[e]) = v;
-      }
+      for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(lds_base + lds[e]) = t[e];
     }
   }
   __device__ inline void advance() { ptr += kstep >> 3; }
@@ -152,7 +133,7 @@ struct Plan {
 //         fragment reads per FLOP; every thread stages both operands; the
 //         accumulators live in AGPRs (one wave per SIMD).  Measured 10-15%
 //         slower on the d20 shapes, so it is not instantiated.
-template <int NW, int BM, int BN, bool PT, bool QT, bool XP, bool XQ, int EPI>
+template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
 __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   static_assert(BM % 64 == 0 && BN % 128 == 0 && (NW == 4 || NW == 8), "tile");
   constexpr int WGN = NW / 2;                    // waves along n
@@ -210,11 +191,11 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   if (loadsP) pp.load(reg);
   if (loadsQ) pq.load(rq);
   if (loadsP) {
-    pp.template store<XP>(reg, smem);
+    pp.store(reg, smem);
     pp.advance();
   }
   if (loadsQ) {
-    pq.template store<XQ>(rq, smem + BM * 128);
+    pq.store(rq, smem + BM * 128);
     pq.advance();
   }
   if (nk > 1) {
@@ -253,11 +234,11 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
     char* nx = smem + ((kt + 1) & 1) * STAGE;
     if (kt + 1 < nk) {
       if (loadsP) {
-        pp.template store<XP>(reg, nx);
+        pp.store(reg, nx);
         pp.advance();
       }
       if (loadsQ) {
-        pq.template store<XQ>(rq, nx + BM * 128);
+        pq.store(rq, nx + BM * 128);
         pq.advance();
       }
       if (kt + 2 < nk) {
@@ -375,11 +356,16 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
             if constexpr (EPI == EPI_RESID) {
               v[0] += a0; v[1] += a1; v[2] += a2; v[3] += a3;
             } else {
-              v[0] *= 2.f * fmaxf(a0, 0.f);
-              v[1] *= 2.f * fmaxf(a1, 0.f);
-              v[2] *= 2.f * fmaxf(a2, 0.f);
-              v[3] *= 2.f * fmaxf(a3, 0.f);
+              // aux = relu(h)^2, so 2 relu(h) = 2 sqrt(aux)
+              v[0] *= 2.f * __builtin_sqrtf(fmaxf(a0, 0.f));
+              v[1] *= 2.f * __builtin_sqrtf(fmaxf(a1, 0.f));
+              v[2] *= 2.f * __builtin_sqrtf(fmaxf(a2, 0.f));
+              v[3] *= 2.f * __builtin_sqrtf(fmaxf(a3, 0.f));
             }
+          }
+          if constexpr (EPI == EPI_RELU2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f) * fmaxf(v[e], 0.f);
           }
           if constexpr (EPI == EPI_DZ) {
 #pragma unroll
@@ -392,46 +378,43 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   }
 }
 
-template <int NW, int BM, int BN, bool PT, bool QT, bool XP, bool XQ, int EPI>
+template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
 hipError_t launch(const GemmDesc& g, hipStream_t s) {
   dim3 grid((g.M / BM) * (g.N / BN), g.splits);
-  k_gemm_mfma<NW, BM, BN, PT, QT, XP, XQ, EPI><<<grid, NW * 64, 0, s>>>(g);
+  k_gemm_mfma<NW, BM, BN, PT, QT, EPI><<<grid, NW * 64, 0, s>>>(g);
   return hipGetLastError();
 }
 
 }  // namespace mfma
 }  // namespace nc
 
-// Operand-layout / transform / epilogue combinations the library uses.
-//   forward:  qkv (ROPE), o Wo^T + x (RESID), m W1^T (STORE),
-//             relu(h)^2 W2^T + x (P transform, RESID), head (LSE), head
-//             recompute (DZ)
-//   backward: weight gradients (both operands transposed, fp32 partials,
-//             relu^2 on Q for dW2), data gradients (Q transposed: STORE,
-//             DRELU2)
+// Operand-layout / epilogue combinations the library uses.
+//   forward:  qkv (ROPE), o Wo^T + x and u W2^T + x (RESID),
+//             u = relu(m W1^T)^2 (RELU2), head (LSE), head recompute (DZ)
+//   backward: weight gradients (both operands transposed, fp32 partials),
+//             activation gradients (Q transposed: STORE, DRELU2)
 //   tests:    every layout with fp32 and bf16 stores
-#define NC_MFMA_COMBOS(X)             \
-  X(0, 0, 0, 0, EPI_STORE)            \
-  X(0, 0, 0, 0, EPI_ROPE)             \
-  X(0, 0, 0, 0, EPI_RESID)            \
-  X(0, 0, 1, 0, EPI_RESID)            \
-  X(0, 0, 0, 0, EPI_LSE)              \
-  X(0, 0, 0, 0, EPI_DZ)               \
-  X(0, 0, 0, 0, EPI_F32)              \
-  X(0, 1, 0, 0, EPI_STORE)            \
-  X(0, 1, 0, 0, EPI_DRELU2)           \
-  X(0, 1, 0, 0, EPI_F32)              \
-  X(1, 0, 0, 0, EPI_STORE)            \
-  X(1, 0, 0, 0, EPI_F32)              \
-  X(1, 1, 0, 0, EPI_STORE)            \
-  X(1, 1, 0, 0, EPI_F32)              \
-  X(1, 1, 0, 1, EPI_F32)
+#define NC_MFMA_COMBOS(X)     \
+  X(0, 0, EPI_STORE)          \
+  X(0, 0, EPI_ROPE)           \
+  X(0, 0, EPI_RESID)          \
+  X(0, 0, EPI_RELU2)          \
+  X(0, 0, EPI_LSE)            \
+  X(0, 0, EPI_DZ)             \
+  X(0, 0, EPI_F32)            \
+  X(0, 1, EPI_STORE)          \
+  X(0, 1, EPI_DRELU2)         \
+  X(0, 1, EPI_F32)            \
+  X(1, 0, EPI_STORE)          \
+  X(1, 0, EPI_F32)            \
+  X(1, 1, EPI_STORE)          \
+  X(1, 1, EPI_F32)
 
 namespace nc {
 namespace mfma {
 inline bool combo_supported(const GemmDesc& g) {
-#define NC_X(PT, QT, XP, XQ, EPI) \
-  if (g.p_trans == PT && g.q_trans == QT && g.p_relu2 == XP && g.q_relu2 == XQ && g.epi == EPI) return true;
+#define NC_X(PT, QT, EPI) \
+  if (g.p_trans == PT && g.q_trans == QT && g.epi == EPI) return true;
   NC_MFMA_COMBOS(NC_X)
 #undef NC_X
   return false;
@@ -439,9 +422,8 @@ inline bool combo_supported(const GemmDesc& g) {
 
 template <int NW, int BM, int BN>
 hipError_t dispatch(const GemmDesc& g, hipStream_t s) {
-#define NC_X(PT, QT, XP, XQ, EPI) \
-  if (g.p_trans == PT && g.q_trans == QT && g.p_relu2 == XP && g.q_relu2 == XQ && g.epi == EPI) \
-    return launch<NW, BM, BN, PT, QT, XP, XQ, EPI>(g, s);
+#define NC_X(PT, QT, EPI) \
+  if (g.p_trans == PT && g.q_trans == QT && g.epi == EPI) return launch<NW, BM, BN, PT, QT, EPI>(g, s);
   NC_MFMA_COMBOS(NC_X)
 #undef NC_X
   return hipErrorInvalidValue;

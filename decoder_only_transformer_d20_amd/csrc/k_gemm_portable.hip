@@ -12,13 +12,8 @@ namespace {
 constexpr int BM = 64, BN = 64, BK = 16;
 
 template <typename T>
-__device__ inline float load_op(const T* p, int64_t ld, int trans, int relu2, int64_t row, int64_t k) {
-  float v = to_f32(trans ? p[k * ld + row] : p[row * ld + k]);
-  if (relu2) {
-    v = fmaxf(v, 0.f);
-    v = v * v;
-  }
-  return v;
+__device__ inline float load_op(const T* p, int64_t ld, int trans, int64_t row, int64_t k) {
+  return to_f32(trans ? p[k * ld + row] : p[row * ld + k]);
 }
 
 template <typename T>
@@ -41,9 +36,9 @@ __global__ void __launch_bounds__(256) k_gemm_portable(GemmDesc g) {
       const int e = tid + 256 * i;
       int r, k;
       if (g.p_trans) { r = e % BM; k = e / BM; } else { r = e / BK; k = e % BK; }
-      Ps[k][r] = load_op(P, g.ldp, g.p_trans, g.p_relu2, m0 + r, k0 + k);
+      Ps[k][r] = load_op(P, g.ldp, g.p_trans, m0 + r, k0 + k);
       if (g.q_trans) { r = e % BN; k = e / BN; } else { r = e / BK; k = e % BK; }
-      Qs[k][r] = load_op(Q, g.ldq, g.q_trans, g.q_relu2, n0 + r, k0 + k);
+      Qs[k][r] = load_op(Q, g.ldq, g.q_trans, n0 + r, k0 + k);
     }
     __syncthreads();
 #pragma unroll
@@ -112,9 +107,13 @@ __global__ void __launch_bounds__(256) k_gemm_portable(GemmDesc g) {
       case EPI_DRELU2: {
         const T* a = (const T*)g.aux + m * g.ldaux + n;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] *= 2.f * fmaxf(to_f32(a[j]), 0.f);
+        for (int j = 0; j < 4; ++j) v[j] *= 2.f * sqrtf(fmaxf(to_f32(a[j]), 0.f));
         break;
       }
+      case EPI_RELU2:
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = fmaxf(v[j], 0.f) * fmaxf(v[j], 0.f);
+        break;
       case EPI_DZ: {
         const int t = g.tgt[m];
         const float l = g.lse[m];

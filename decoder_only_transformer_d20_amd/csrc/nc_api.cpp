@@ -79,7 +79,7 @@ struct Plan {
   size_t rope = 0, idx = 0, tgt = 0, x = 0, xf = 0, rf = 0, ce = 0, lse_head = 0, ztgt = 0, lse_part = 0;
   size_t scalars = 0, dz = 0, g = 0, gtmp = 0, big = 0, part = 0, delta = 0;
   size_t layer0 = 0, layer_stride = 0;
-  size_t l_a = 0, l_r1 = 0, l_qkv = 0, l_o = 0, l_lse = 0, l_m = 0, l_r2 = 0, l_h = 0;
+  size_t l_a = 0, l_r1 = 0, l_qkv = 0, l_o = 0, l_lse = 0, l_m = 0, l_r2 = 0, l_u = 0;
   int head_nblk = 0;
   int64_t head_chunk = 0;
 };
@@ -135,7 +135,7 @@ Plan make_plan(const nc_config& c) {
   p.l_lse = ltake(BHT * 4);
   p.l_m = ltake(N * d * es);
   p.l_r2 = ltake(N * 4);
-  p.l_h = ltake(N * F * es);
+  p.l_u = ltake(N * F * es);
   p.layer_stride = lo;
   p.layer0 = off;
   off += lo * c.n_layer;
@@ -183,15 +183,16 @@ int fail(nc_ctx* ctx, hipError_t e, const char* what) {
 constexpr size_t kMaxTrace = 65536;
 
 int gemm_family(const GemmDesc& g) {
-  const int key = g.p_trans * 16 + g.q_trans * 8 + g.p_relu2 * 4 + g.q_relu2 * 2;
+  const int key = g.p_trans * 2 + g.q_trans;
   switch (g.epi) {
-    case EPI_ROPE: return key == 0 ? NC_TRACE_QKV : -1;
-    case EPI_RESID: return key == 0 ? NC_TRACE_ATTN_OUT : key == 4 ? NC_TRACE_MLP_DOWN : -1;
-    case EPI_STORE: return key == 0 ? NC_TRACE_MLP_UP : key == 8 ? NC_TRACE_DGRAD : -1;
-    case EPI_LSE: return key == 0 ? NC_TRACE_HEAD_LSE : -1;
-    case EPI_DZ: return key == 0 ? NC_TRACE_HEAD_DZ : -1;
-    case EPI_DRELU2: return key == 8 ? NC_TRACE_DH : -1;
-    case EPI_F32: return key == 24 ? NC_TRACE_WGRAD : key == 26 ? NC_TRACE_WGRAD_RELU2 : -1;
+    case EPI_ROPE: return key == 0 ? NC_TRACE_GEMM_QKV_ROPE : -1;
+    case EPI_RESID: return key == 0 ? NC_TRACE_GEMM_RESIDUAL : -1;
+    case EPI_RELU2: return key == 0 ? NC_TRACE_GEMM_RELU2 : -1;
+    case EPI_STORE: return key == 1 ? NC_TRACE_GEMM_DGRAD : -1;
+    case EPI_LSE: return key == 0 ? NC_TRACE_GEMM_HEAD_LSE : -1;
+    case EPI_DZ: return key == 0 ? NC_TRACE_GEMM_HEAD_DZ : -1;
+    case EPI_DRELU2: return key == 1 ? NC_TRACE_GEMM_DGRAD_RELU2 : -1;
+    case EPI_F32: return key == 3 ? NC_TRACE_GEMM_WGRAD : -1;
     default: return -1;
   }
 }
@@ -256,11 +257,10 @@ GemmDesc gemm(int M, int N, int K, const void* P, int64_t ldp, int pt, const voi
 }
 
 // weight gradient dW[M'][N'] (+)= sum over tokens P[tok][m'] Q[tok][n']
-hipError_t weight_grad(nc_ctx* ctx, int Mw, int Nw, const void* P, int64_t ldp, const void* Q, int64_t ldq, int q_relu2,
+hipError_t weight_grad(nc_ctx* ctx, int Mw, int Nw, const void* P, int64_t ldp, const void* Q, int64_t ldq,
                        float* dW, int accumulate) {
   const int64_t N = (int64_t)ctx->cfg.batch * ctx->cfg.seq_len;
   GemmDesc g = gemm(Mw, Nw, (int)N, P, ldp, 1, Q, ldq, 1, EPI_F32, dW, Nw);
-  g.q_relu2 = q_relu2;
   g.beta = accumulate;
   g.splits = choose_splits(ctx->cfg, Mw, Nw, N);
   g.part = ctx->at<float>(ctx->plan.part);
@@ -308,7 +308,7 @@ int layer_forward(nc_ctx* ctx, int l, const T* w, T* x) {
   float* lse = (float*)(L + p.l_lse);
   T* m = (T*)(L + p.l_m);
   float* r2 = (float*)(L + p.l_r2);
-  T* h = (T*)(L + p.l_h);
+  T* u = (T*)(L + p.l_u);
   hipStream_t s = ctx->stream;
 
   NC_TRY(rmsnorm_fwd<T>(x, a, r1, N, d, c.rms_eps, s), "rmsnorm (attention input)");
@@ -323,9 +323,11 @@ int layer_forward(nc_ctx* ctx, int l, const T* w, T* x) {
   g.aux = x; g.ldaux = d;
   NC_TRY(run_gemm(ctx, g), "output projection + residual");
   NC_TRY(rmsnorm_fwd<T>(x, m, r2, N, d, c.rms_eps, s), "rmsnorm (MLP input)");
-  NC_TRY(run_gemm(ctx, gemm(N, F, d, m, d, 0, W1, d, 0, EPI_STORE, h, F)), "MLP up projection");
-  g = gemm(N, d, F, h, F, 0, W2, F, 0, EPI_RESID, x, d);
-  g.p_relu2 = 1; g.aux = x; g.ldaux = d;
+  // the saved MLP activation is u = relu(h)^2, h = m W1^T: the down
+  // projection and dW2 consume u as is, and dh needs only 2 relu(h) = 2 sqrt(u)
+  NC_TRY(run_gemm(ctx, gemm(N, F, d, m, d, 0, W1, d, 0, EPI_RELU2, u, F)), "MLP up projection + relu^2");
+  g = gemm(N, d, F, u, F, 0, W2, F, 0, EPI_RESID, x, d);
+  g.aux = x; g.ldaux = d;
   NC_TRY(run_gemm(ctx, g), "MLP down projection + residual");
   return NC_OK;
 }
@@ -352,28 +354,28 @@ int layer_backward(nc_ctx* ctx, int l, const T* w, T* gr, float* dw, int accumul
   float* lse = (float*)(L + p.l_lse);
   T* m = (T*)(L + p.l_m);
   float* r2 = (float*)(L + p.l_r2);
-  T* h = (T*)(L + p.l_h);
+  T* u = (T*)(L + p.l_u);
   T* tmp = ctx->at<T>(p.gtmp);
   T* big = ctx->at<T>(p.big);
   hipStream_t s = ctx->stream;
 
-  // MLP: x2 = x1 + relu(h)^2 W2^T, h = m W1^T
-  NC_TRY(weight_grad(ctx, d, F, gr, d, h, F, 1, dW2, accumulate), "dW2");
+  // MLP: x2 = x1 + u W2^T, u = relu(h)^2, h = m W1^T
+  NC_TRY(weight_grad(ctx, d, F, gr, d, u, F, dW2, accumulate), "dW2");
   GemmDesc g = gemm(N, F, d, gr, d, 0, W2, F, 1, EPI_DRELU2, big, F);
-  g.aux = h; g.ldaux = F;
+  g.aux = u; g.ldaux = F;
   NC_TRY(run_gemm(ctx, g), "dh = (g W2) * 2 relu(h)");
-  NC_TRY(weight_grad(ctx, F, d, big, F, m, d, 0, dW1, accumulate), "dW1");
+  NC_TRY(weight_grad(ctx, F, d, big, F, m, d, dW1, accumulate), "dW1");
   NC_TRY(run_gemm(ctx, gemm(N, d, F, big, F, 0, W1, d, 1, EPI_STORE, tmp, d)), "dm = dh W1");
   NC_TRY(rmsnorm_bwd<T>(m, r2, tmp, gr, N, d, 1, s), "rmsnorm backward (MLP input)");
   // attention: x1 = x0 + o Wo^T
-  NC_TRY(weight_grad(ctx, d, d, gr, d, o, d, 0, dWo, accumulate), "dWo");
+  NC_TRY(weight_grad(ctx, d, d, gr, d, o, d, dWo, accumulate), "dWo");
   NC_TRY(run_gemm(ctx, gemm(N, d, d, gr, d, 0, Wo, d, 1, EPI_STORE, tmp, d)), "do = g Wo");
   AttnDesc ad{};
   ad.B = c.batch; ad.T = c.seq_len; ad.H = c.n_head; ad.Q = c.head_dim;
   ad.qkv = qkv; ad.o = o; ad.lse = lse; ad.dout = tmp; ad.delta = ctx->at<float>(p.delta);
   ad.dqkv = big; ad.rope = ctx->at<float2>(p.rope);
   NC_TRY(attn_bwd<T>(ctx, ad), "attention backward");
-  NC_TRY(weight_grad(ctx, 3 * d, d, big, 3 * d, a, d, 0, dWqkv, accumulate), "dWqkv");
+  NC_TRY(weight_grad(ctx, 3 * d, d, big, 3 * d, a, d, dWqkv, accumulate), "dWqkv");
   NC_TRY(run_gemm(ctx, gemm(N, d, 3 * d, big, 3 * d, 0, Wqkv, d, 1, EPI_STORE, tmp, d)), "da = dqkv Wqkv");
   NC_TRY(rmsnorm_bwd<T>(a, r1, tmp, gr, N, d, 1, s), "rmsnorm backward (attention input)");
   return NC_OK;

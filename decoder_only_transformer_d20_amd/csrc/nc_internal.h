@@ -36,23 +36,23 @@ template <> __host__ __device__ inline bf16 from_f32<bf16>(float f) {
 // ---------------------------------------------------------------------------
 // GEMM:  C[m][n] = sum_k P[m][k] * Q[n][k]       (m < M, n < N, k < K)
 // P is stored [M][K] (p_trans = 0) or [K][M] (p_trans = 1); likewise Q is
-// [N][K] or [K][N].  p_relu2 / q_relu2 replace the operand by relu(.)^2 as it
-// is loaded.  The epilogue decides what is written.
+// [N][K] or [K][N].  The epilogue decides what is written.
 // ---------------------------------------------------------------------------
 enum Epi {
   EPI_STORE = 0,     // C(T) = acc
   EPI_ROPE = 1,      // C(T) = acc, columns < rope_cols rotated in adjacent pairs
   EPI_RESID = 2,     // C(T) = aux(T) + acc            (aux may alias C)
-  EPI_DRELU2 = 3,    // C(T) = acc * 2 relu(aux(T))
+  EPI_DRELU2 = 3,    // C(T) = acc * 2 sqrt(aux(T)), aux = relu(h)^2 (so the factor is 2 relu(h))
   EPI_F32 = 4,       // C(f32) = (beta ? C : 0) + acc; with splits > 1, partials
   EPI_LSE = 5,       // per-row (max, sum exp) of the N-tile -> lse_part; z[tgt] -> ztgt
   EPI_DZ = 6,        // C(T) = (exp(acc - lse[m]) - [n == tgt[m]]) * inv_nvalid
+  EPI_RELU2 = 7,     // C(T) = relu(acc)^2
 };
 
 struct GemmDesc {
   int M, N, K;
-  const void* P; int64_t ldp; int p_trans; int p_relu2;
-  const void* Q; int64_t ldq; int q_trans; int q_relu2;
+  const void* P; int64_t ldp; int p_trans;
+  const void* Q; int64_t ldq; int q_trans;
   int epi;
   void* C; int64_t ldc;
   const void* aux; int64_t ldaux;

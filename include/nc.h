@@ -175,19 +175,17 @@ int nc_block_backward(nc_ctx* ctx, const void* block_params, const void* dy,
 /* ---- kernel timing (for roofline reports) --------------------------------- */
 
 /* Kernel families of the step.  Each GEMM family is one matrix-core kernel
- * (one operand layout + epilogue); the attention families are the forward
- * kernel and the three backward kernels together. */
+ * (one operand layout + epilogue); NC_TRACE_ATTN_FWD is one kernel and
+ * NC_TRACE_ATTN_BWD the three backward kernels together. */
 enum {
-  NC_TRACE_QKV = 0,        /* a Wqkv^T with the rotary epilogue            */
-  NC_TRACE_ATTN_OUT,       /* x + o Wo^T                                    */
-  NC_TRACE_MLP_UP,         /* m W1^T                                        */
-  NC_TRACE_MLP_DOWN,       /* x + relu(h)^2 W2^T                            */
-  NC_TRACE_HEAD_LSE,       /* xf U^T with the log-sum-exp epilogue          */
-  NC_TRACE_HEAD_DZ,        /* xf U^T recomputed, softmax - onehot           */
-  NC_TRACE_DGRAD,          /* activation gradients g W (dm, do, da, dxf)    */
-  NC_TRACE_DH,             /* (g W2) * 2 relu(h)                            */
-  NC_TRACE_WGRAD,          /* weight gradients dWo, dW1, dWqkv, dU          */
-  NC_TRACE_WGRAD_RELU2,    /* dW2 = g^T relu(h)^2                           */
+  NC_TRACE_GEMM_QKV_ROPE = 0, /* a Wqkv^T with the rotary epilogue           */
+  NC_TRACE_GEMM_RESIDUAL,     /* x + o Wo^T and x + u W2^T                    */
+  NC_TRACE_GEMM_RELU2,        /* u = relu(m W1^T)^2                           */
+  NC_TRACE_GEMM_HEAD_LSE,     /* xf U^T with the log-sum-exp epilogue         */
+  NC_TRACE_GEMM_HEAD_DZ,      /* xf U^T recomputed, softmax - onehot          */
+  NC_TRACE_GEMM_DGRAD,        /* activation gradients g W (dm, do, da, dxf)   */
+  NC_TRACE_GEMM_DGRAD_RELU2,  /* dh = (g W2) * 2 relu(h)                      */
+  NC_TRACE_GEMM_WGRAD,        /* weight gradients dWqkv, dWo, dW1, dW2, dU    */
   NC_TRACE_ATTN_FWD,
   NC_TRACE_ATTN_BWD,
   NC_TRACE_COUNT
