@@ -44,10 +44,16 @@ __device__ inline uint32_t pack2(float lo, float hi) { return f2bf(lo) | (f2bf(h
 
 __device__ inline u32x4 gload(const bf16* p) { return *(gptr)p; }
 
-// LDS image of a [rows][128] tile (256 B rows, 16 chunks): chunk c of row r at c ^ (r & 7)
-__device__ inline uint32_t off256(int row, int chunk) { return (uint32_t)row * 256u + ((uint32_t)(chunk ^ (row & 7)) << 4); }
-// LDS image of a [128][64 slots] transposed tile (128 B rows, 8 chunks)
-__device__ inline uint32_t off128(int row, int chunk) { return (uint32_t)row * 128u + ((uint32_t)(chunk ^ (row & 7)) << 4); }
+// gfx950's LDS serves 16 lanes x 16 B (64 banks, 256 B) per cycle, and a
+// fragment read takes 16 consecutive rows at one chunk, so the swizzles
+// give those 16 rows 16 distinct 16-byte slots modulo 256 B.
+// LDS image of a [rows][128] tile (256 B rows, 16 chunks): chunk c of row r at c ^ (r & 15)
+__device__ inline uint32_t off256(int row, int chunk) { return (uint32_t)row * 256u + ((uint32_t)(chunk ^ (row & 15)) << 4); }
+// LDS image of a [128][64 slots] transposed tile (128 B rows, 8 chunks):
+// chunk c of row r at c ^ ((r >> 1) & 7) (rows r, r+1 sit in opposite halves)
+__device__ inline uint32_t off128(int row, int chunk) {
+  return (uint32_t)row * 128u + ((uint32_t)(chunk ^ ((row >> 1) & 7)) << 4);
+}
 
 // key (or query) index, within a 64-row tile, of slot e of chunk cj
 __device__ inline int slot_row(int cj, int e) {

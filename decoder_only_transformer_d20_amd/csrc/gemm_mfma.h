@@ -104,11 +104,12 @@ struct Plan {
       active = tl < R;
     }
   }
+  static constexpr bool kAllActive = !TRANS || R >= 256;   // 256 loaders cover the tile
   __device__ inline void load(u32x4 (&reg)[8]) const {
     if (!TRANS) {
 #pragma unroll
       for (int i = 0; i < R / 32; ++i) reg[i] = ptr[(i * step) >> 3];
-    } else if (active) {
+    } else if (kAllActive || active) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) reg[kk] = ptr[(kk * step) >> 3];
     }
@@ -117,14 +118,14 @@ struct Plan {
     if (!TRANS) {
 #pragma unroll
       for (int i = 0; i < R / 32; ++i) *reinterpret_cast<u32x4*>(lds_base + lds[i]) = reg[i];
-    } else if (active) {
+    } else if (kAllActive || active) {
       u32x4 t[8];
       transpose8(reg, t);
 #pragma unroll
       for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(lds_base + lds[e]) = t[e];
     }
   }
-  __device__ inline void advance() { ptr += kstep >> 3; }
+  __device__ inline void advance_if(bool more) { ptr += more ? (kstep >> 3) : 0; }
 };
 
 // NW = 8: waves in a 2 x 4 grid, wave tile (BM/2) x (BN/4), waves 0-3 stage
@@ -146,30 +147,74 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // XCD-aware tile order: consecutive logical tiles run on one XCD (blocks
-  // are dealt to the 8 XCDs round-robin), n fastest so a P row-panel is
-  // reused from that XCD's L2.
+  // Block -> (split, m-tile, n-tile).  Workgroups are dealt to the 8 XCDs
+  // round-robin, so the flat index is renumbered to give each XCD a
+  // contiguous run of logical tiles (splits outermost: with 8 splits an XCD
+  // owns one K range).  Within a split, tiles are rastered in groups of
+  // kGroupM m-tiles, m fastest: the ~32 blocks an XCD runs at once cover
+  // about 8 m-tiles x 4 n-tiles, so each P panel and each Q panel (weights)
+  // is reused from that XCD's L2 instead of refetched per tile.
+  constexpr int kGroupM = 8;
   const int ntn = g.N / BN, ntm = g.M / BM;
-  const int nb = ntn * ntm;
-  int b = blockIdx.x;
-  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
-  const int tm = b / ntn, tn = b % ntn;
+  const int ntiles = ntn * ntm, total = ntiles * g.splits;
+  int L = blockIdx.x;
+  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  const int split = L / ntiles;
+  const int t = L - split * ntiles;
+  const int first_m = (t / (kGroupM * ntn)) * kGroupM;
+  const int gm = min(kGroupM, ntm - first_m);
+  const int tg = t - first_m * ntn;
+  const int tm = first_m + tg % gm, tn = tg / gm;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
   const int kper = g.K / g.splits;
-  const int64_t kbeg = (int64_t)blockIdx.y * kper;
+  const int64_t kbeg = (int64_t)split * kper;
   const int nk = kper / BK;
 
   // NW = 8: waves 0-3 stage P tiles, waves 4-7 stage Q tiles (a wave-uniform
-  // split).  NW = 4: every thread stages its share of both.
+  // split).  NW = 4: every thread stages its share of both.  When both
+  // operands have the same layout and tile height, a thread's single plan is
+  // set up for whichever operand it stages, so the main loop has no branch.
+  constexpr bool kUnified = NW == 8 && PT == QT && BM == BN;
   const bool loadsP = NW == 4 || tid < 256;
   const bool loadsQ = NW == 4 || tid >= 256;
   Plan<BM, PT> pp;
   Plan<BN, QT> pq;
-  if (loadsP) pp.init((const bf16*)g.P, g.ldp, m0, kbeg, tid & 255);
-  if (loadsQ) pq.init((const bf16*)g.Q, g.ldq, n0, kbeg, tid & 255);
+  uint32_t my_lds = 0;
+  if constexpr (kUnified) {
+    if (loadsP) pp.init((const bf16*)g.P, g.ldp, m0, kbeg, tid & 255);
+    else pp.init((const bf16*)g.Q, g.ldq, n0, kbeg, tid & 255);
+    my_lds = loadsP ? 0u : (uint32_t)BM * 128u;
+  } else {
+    if (loadsP) pp.init((const bf16*)g.P, g.ldp, m0, kbeg, tid & 255);
+    if (loadsQ) pq.init((const bf16*)g.Q, g.ldq, n0, kbeg, tid & 255);
+  }
   u32x4 reg[8], regq[8];
   u32x4(&rq)[8] = pick<NW == 4>(regq, reg);   // NW = 8: a thread stages one operand only
+  auto stage_load = [&]() {
+    if constexpr (kUnified) {
+      pp.load(reg);
+    } else {
+      if (loadsP) pp.load(reg);
+      if (loadsQ) pq.load(rq);
+    }
+  };
+  auto stage_store = [&](char* base) {
+    if constexpr (kUnified) {
+      pp.store(reg, base + my_lds);
+    } else {
+      if (loadsP) pp.store(reg, base);
+      if (loadsQ) pq.store(rq, base + BM * 128);
+    }
+  };
+  auto stage_advance = [&](bool more) {
+    if constexpr (kUnified) {
+      pp.advance_if(more);
+    } else {
+      if (loadsP) pp.advance_if(more);
+      if (loadsQ) pq.advance_if(more);
+    }
+  };
 
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -188,20 +233,13 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   //   so the MFMAs of step 3 cover the first LDS reads after the barrier.
   // The write of tile t+1 reuses the stage tile t-1 occupied; its last reads
   // were issued before the previous barrier, which waits for them.
-  if (loadsP) pp.load(reg);
-  if (loadsQ) pq.load(rq);
-  if (loadsP) {
-    pp.store(reg, smem);
-    pp.advance();
-  }
-  if (loadsQ) {
-    pq.store(rq, smem + BM * 128);
-    pq.advance();
-  }
-  if (nk > 1) {
-    if (loadsP) pp.load(reg);
-    if (loadsQ) pq.load(rq);
-  }
+  // Tiles past the last are never fetched: the staged tile index is clamped
+  // to nk-1 (the pointer stops advancing), so the final iterations restage
+  // the last tile into the idle stage instead of branching around the copy.
+  stage_load();                 // tile 0
+  stage_store(smem);
+  stage_advance(nk > 1);
+  stage_load();                 // tile min(1, nk-1)
   __syncthreads();
 
   const int frow = lane & 31, fchunk = lane >> 5;
@@ -232,28 +270,41 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   for (int kt = 0; kt < nk; ++kt) {
     const char* st = smem + (kt & 1) * STAGE;
     char* nx = smem + ((kt + 1) & 1) * STAGE;
-    if (kt + 1 < nk) {
-      if (loadsP) {
-        pp.store(reg, nx);
-        pp.advance();
-      }
-      if (loadsQ) {
-        pq.store(rq, nx + BM * 128);
-        pq.advance();
-      }
-      if (kt + 2 < nk) {
-        if (loadsP) pp.load(reg);
-        if (loadsQ) pq.load(rq);
-      }
-    }
+    stage_store(nx);              // tile min(kt+1, nk-1)
+    stage_advance(kt + 2 < nk);
+    stage_load();                 // tile min(kt+2, nk-1)
 #pragma unroll
     for (int s = 0; s < BK / 16 - 1; ++s) {
       read_frags(st, s + 1, (s + 1) & 1);
       mfmas(s & 1);
+      // Interleave so every memory instruction issues between MFMAs: in
+      // step 0 the staged tile's LDS writes and the next global loads, in
+      // every step the fragment reads of the following step.
+      constexpr int nm = FM * FN, nr = FM + FN, ns = kUnified ? BM / 32 : 0;
+      if (s == 0 && kUnified) {
+#pragma unroll
+        for (int q = 0; q < nm; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+          if (q < ns) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // DS write
+          if (q < ns) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // global load
+          if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < nm; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
     }
     __syncthreads();
-    if (kt + 1 < nk) read_frags(nx, 0, 0);
+    read_frags(nx, 0, 0);         // next tile's step 0 (a harmless reread after the last)
     mfmas((BK / 16 - 1) & 1);
+#pragma unroll
+    for (int q = 0; q < FM * FN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   }
   __syncthreads();
 
@@ -326,7 +377,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
           float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
           if constexpr (EPI == EPI_F32) {
             if (g.splits > 1) {
-              float* dst = g.part + (int64_t)blockIdx.y * g.M * g.N + m * g.N + n;
+              float* dst = g.part + (int64_t)split * g.M * g.N + m * g.N + n;
               *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
             } else {
               float* dst = (float*)g.C + m * g.ldc + n;
@@ -380,7 +431,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
 
 template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
 hipError_t launch(const GemmDesc& g, hipStream_t s) {
-  dim3 grid((g.M / BM) * (g.N / BN), g.splits);
+  dim3 grid((g.M / BM) * (g.N / BN) * g.splits);
   k_gemm_mfma<NW, BM, BN, PT, QT, EPI><<<grid, NW * 64, 0, s>>>(g);
   return hipGetLastError();
 }
