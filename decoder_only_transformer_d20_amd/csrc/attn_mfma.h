@@ -35,12 +35,13 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ inline uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two fp32 -> packed bf16, round to nearest even: one v_cvt_pk_bf16_f32
+__device__ inline uint32_t pack2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
-__device__ inline uint32_t pack2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
 
 __device__ inline u32x4 gload(const bf16* p) { return *(gptr)p; }
 

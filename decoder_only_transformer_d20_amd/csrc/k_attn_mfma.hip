@@ -90,35 +90,42 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + off256(js * 32 + (lane & 31), 2 * ks + hh));
           s[js] = mfma(kf, qf[ks], s[js]);
         }
-      const bool diag = j0 + 63 > i0;
+      // running max over raw scores (the positive scale preserves order);
+      // masked keys only on the diagonal tiles
+      if (j0 + 63 > i0) {
+#pragma unroll
+        for (int js = 0; js < 2; ++js)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (j0 + js * 32 + 8 * (r >> 2) + 4 * hh + (r & 3) > my_i) s[js][r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int js = 0; js < 2; ++js)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s[js][r] * kScaleLog2;
-          if (diag && j0 + js * 32 + 8 * (r >> 2) + 4 * hh + (r & 3) > my_i) v = -INFINITY;
-          s[js][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[js][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * kScaleLog2;
       const float mn = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
       float ls = 0.f;
 #pragma unroll
       for (int js = 0; js < 2; ++js)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[js][r] - mn);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[js][r], kScaleLog2, -mn));
           s[js][r] = p;
           ls += p;
         }
-      l = l * alpha + ls;
+      // rescale the running sums only when some row's maximum moved
+      if (__any(mn > m)) {
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      }
+      l += ls;
       m = mn;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
         const bf16x8 pf = pack8(s[sp >> 1], 8 * (sp & 1));
