@@ -7,8 +7,9 @@
 // fp32 accumulation in v_mfma_f32_32x32x16_bf16.  Q (the n side) is the
 // instruction's A operand and P (the m side) its B operand, so a lane's
 // sixteen accumulators hold one row m and runs of four consecutive columns
-// n: every epilogue works on contiguous 8-byte (bf16) / 16-byte (fp32)
-// pieces of a row, and row-wise reductions (log-sum-exp) stay in a lane.
+// n, so row-wise reductions (log-sum-exp) stay in a lane.  Other epilogues
+// pass the accumulators through LDS and finish them in row order, so aux
+// reads and output writes are contiguous runs of a row.
 //
 // Both operand tiles live in LDS as [row][64 k] bf16 (128 B per row), the
 // 16-byte chunk c of row r stored at chunk slot c ^ ((r >> 1) & 7) (see
@@ -17,9 +18,13 @@
 // operands stored row-major in k ([K][rows], the backward pass's transposed
 // products) are read as 8 x 8 blocks and transposed in registers before the
 // LDS write, so every layout reaches the same LDS image.  Two LDS stages
-// and one register stage: the global loads of tile k+2 are in flight while
-// tile k is multiplied and tile k+1 is written; one barrier per tile.
+// and one register stage: the global loads of k-tile t+2 are in flight
+// while k-tile t is multiplied and k-tile t+1 is written; one barrier per
+// k-tile.  The grid is persistent (one block per CU, each looping over
+// output tiles).
 #pragma once
+
+#include <algorithm>
 
 #include "nc_internal.h"
 
@@ -66,78 +71,78 @@ __device__ inline void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
 
 typedef const u32x4 __attribute__((address_space(1)))* gptr;
 
-template <bool B, typename T>
-__device__ inline T& pick(T& a, T& b) {
-  if constexpr (B) return a;
-  else return b;
-}
-
 // Per-thread plan for one operand tile (R rows x 64 k), loaded by 256
 // threads into `reg` (8 x 16 B) and written to LDS.
 //  k-major operand ([rows][K]): thread tl takes chunk tl & 7 of rows
 //    (tl >> 3) + 32 i, i < R/32 -- 8 lanes read one 128-byte row segment.
+//    Row r + 32 i has the swizzle of row r, so its LDS offset is that of
+//    row r plus 4096 i.
 //  transposed operand ([K][rows]): thread tl < R takes the 8 x 8 block at
-//    k rows (tl & 7)*8 .. +7 and tile rows (tl >> 3)*8 .. +7.
-template <int R, bool TRANS>
+//    k rows (tl & 7)*8 .. +7 and tile rows (tl >> 3)*8 .. +7.  Row
+//    8 mg + e of chunk kc sits at (8 mg)*128 + 128 e with chunk slot
+//    kc ^ 4 (mg & 1) ^ (e >> 1): one base offset and an xor per row.
+// The state is layout-independent, so the two wave roles of a block share
+// one set of registers; the layout is a template argument of each call.
 struct Plan {
   gptr ptr;          // this thread's first 16-byte piece of the current tile
   int64_t step;      // elements between the thread's successive pieces
   int64_t kstep;     // elements to advance by one 64-k tile
-  uint32_t lds[8];   // byte offsets in the operand's LDS image
-  bool active;
+  uint32_t lds0;     // byte offset of the first piece in the operand's LDS image
 
+  template <int R, bool TRANS>
   __device__ inline void init(const bf16* base, int64_t ld, int64_t row0, int64_t k0, int tl) {
     if (!TRANS) {
       const int r = tl >> 3, c = tl & 7;
       ptr = (gptr)(base + (row0 + r) * ld + k0 + c * 8);
       step = 32 * ld;
       kstep = BK;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) lds[i] = i < R / 32 ? lds_off(r + 32 * i, c) : 0;
-      active = true;
+      lds0 = lds_off(r, c);
     } else {
       const int kc = tl & 7, mg = tl >> 3;
       ptr = (gptr)(base + (k0 + kc * 8) * ld + row0 + mg * 8);
       step = ld;
       kstep = (int64_t)BK * ld;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lds[e] = lds_off(mg * 8 + e, kc);
-      active = tl < R;
+      lds0 = (uint32_t)mg * 1024u + ((uint32_t)(kc ^ ((mg & 1) << 2)) << 4);
     }
   }
-  static constexpr bool kAllActive = !TRANS || R >= 256;   // 256 loaders cover the tile
-  __device__ inline void load(u32x4 (&reg)[8]) const {
+  // transposed: 256 threads cover a 256-row tile; with R = 128 threads tl >= R idle
+  template <int R, bool TRANS>
+  __device__ inline void load(u32x4 (&reg)[8], int tl) const {
     if (!TRANS) {
 #pragma unroll
       for (int i = 0; i < R / 32; ++i) reg[i] = ptr[(i * step) >> 3];
-    } else if (kAllActive || active) {
+    } else if (R >= 256 || tl < R) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) reg[kk] = ptr[(kk * step) >> 3];
     }
   }
-  __device__ inline void store(const u32x4 (&reg)[8], char* lds_base) const {
+  template <int R, bool TRANS>
+  __device__ inline void store(const u32x4 (&reg)[8], char* lds_base, int tl) const {
     if (!TRANS) {
 #pragma unroll
-      for (int i = 0; i < R / 32; ++i) *reinterpret_cast<u32x4*>(lds_base + lds[i]) = reg[i];
-    } else if (kAllActive || active) {
+      for (int i = 0; i < R / 32; ++i) *reinterpret_cast<u32x4*>(lds_base + lds0 + 4096u * i) = reg[i];
+    } else if (R >= 256 || tl < R) {
       u32x4 t[8];
       transpose8(reg, t);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(lds_base + lds[e]) = t[e];
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<u32x4*>(lds_base + ((lds0 ^ (16u * (e >> 1))) + 128u * e)) = t[e];
     }
   }
   __device__ inline void advance_if(bool more) { ptr += more ? (kstep >> 3) : 0; }
 };
 
-// NW = 8: waves in a 2 x 4 grid, wave tile (BM/2) x (BN/4), waves 0-3 stage
-//         P and waves 4-7 stage Q (two waves per SIMD).  The library uses this.
-// NW = 4: waves in a 2 x 2 grid, wave tile (BM/2) x (BN/2) -- half the LDS
-//         fragment reads per FLOP; every thread stages both operands; the
-//         accumulators live in AGPRs (one wave per SIMD).  Measured 10-15%
-//         slower on the d20 shapes, so it is not instantiated.
+// Waves in a 2 x 4 grid, wave tile (BM/2) x (BN/4); waves 0-3 stage P and
+// waves 4-7 stage Q (two waves per SIMD).
+//
+// Persistent: the grid holds as many blocks as fit on the device at once and
+// block b takes the logical tiles b, b + G, b + 2G, ... (G = grid size).
+// While a tile's epilogue runs, the first k-tile of the block's next tile is
+// already on its way into registers, so tile boundaries cost neither a
+// block launch nor an exposed load latency.
 template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
 __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
-  static_assert(BM % 64 == 0 && BN % 128 == 0 && (NW == 4 || NW == 8), "tile");
+  static_assert(BM % 64 == 0 && BN % 128 == 0 && NW == 8, "tile");
   constexpr int WGN = NW / 2;                    // waves along n
   constexpr int WTM = BM / 2, WTN = BN / WGN;    // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 fragments per wave
@@ -145,103 +150,74 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // the wave index as a scalar: wave-role branches are uniform
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
 
-  // Block -> (split, m-tile, n-tile).  Workgroups are dealt to the 8 XCDs
-  // round-robin, so the flat index is renumbered to give each XCD a
-  // contiguous run of logical tiles (splits outermost: with 8 splits an XCD
-  // owns one K range).  Within a split, tiles are rastered in groups of
-  // kGroupM m-tiles, m fastest: the ~32 blocks an XCD runs at once cover
-  // about 8 m-tiles x 4 n-tiles, so each P panel and each Q panel (weights)
-  // is reused from that XCD's L2 instead of refetched per tile.
+  // Logical tile -> (split, m-tile, n-tile).  Workgroups are dealt to the 8
+  // XCDs round-robin (and G is a multiple of 8, so a block stays on one
+  // XCD), so the flat index is renumbered to give each XCD a contiguous run
+  // of logical tiles (splits outermost: with 8 splits an XCD owns one K
+  // range).  Within a split, tiles are rastered in groups of kGroupM
+  // m-tiles, m fastest: the ~32 blocks an XCD runs at once cover about 8
+  // m-tiles x 4 n-tiles, so each P panel and each Q panel (weights) is
+  // reused from that XCD's L2 instead of refetched per tile.
   constexpr int kGroupM = 8;
   const int ntn = g.N / BN, ntm = g.M / BM;
   const int ntiles = ntn * ntm, total = ntiles * g.splits;
-  int L = blockIdx.x;
-  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-  const int split = L / ntiles;
-  const int t = L - split * ntiles;
-  const int first_m = (t / (kGroupM * ntn)) * kGroupM;
-  const int gm = min(kGroupM, ntm - first_m);
-  const int tg = t - first_m * ntn;
-  const int tm = first_m + tg % gm, tn = tg / gm;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-
   const int kper = g.K / g.splits;
-  const int64_t kbeg = (int64_t)split * kper;
   const int nk = kper / BK;
+  struct Tile {
+    int split, tn;
+    int64_t m0, n0, kbeg;
+  };
+  auto coords = [&](int v) {
+    int L = v;
+    if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+    Tile c;
+    c.split = L / ntiles;
+    const int t = L - c.split * ntiles;
+    const int first_m = (t / (kGroupM * ntn)) * kGroupM;
+    const int gm = min(kGroupM, ntm - first_m);
+    const int tg = t - first_m * ntn;
+    c.tn = tg / gm;
+    c.m0 = (int64_t)(first_m + tg % gm) * BM;
+    c.n0 = (int64_t)c.tn * BN;
+    c.kbeg = (int64_t)c.split * kper;
+    return c;
+  };
 
-  // NW = 8: waves 0-3 stage P tiles, waves 4-7 stage Q tiles (a wave-uniform
-  // split).  NW = 4: every thread stages its share of both.  When both
-  // operands have the same layout and tile height, a thread's single plan is
-  // set up for whichever operand it stages, so the main loop has no branch.
-  constexpr bool kUnified = NW == 8 && PT == QT && BM == BN;
-  const bool loadsP = NW == 4 || tid < 256;
-  const bool loadsQ = NW == 4 || tid >= 256;
-  Plan<BM, PT> pp;
-  Plan<BN, QT> pq;
-  uint32_t my_lds = 0;
-  if constexpr (kUnified) {
-    if (loadsP) pp.init((const bf16*)g.P, g.ldp, m0, kbeg, tid & 255);
-    else pp.init((const bf16*)g.Q, g.ldq, n0, kbeg, tid & 255);
-    my_lds = loadsP ? 0u : (uint32_t)BM * 128u;
-  } else {
-    if (loadsP) pp.init((const bf16*)g.P, g.ldp, m0, kbeg, tid & 255);
-    if (loadsQ) pq.init((const bf16*)g.Q, g.ldq, n0, kbeg, tid & 255);
-  }
-  u32x4 reg[8], regq[8];
-  u32x4(&rq)[8] = pick<NW == 4>(regq, reg);   // NW = 8: a thread stages one operand only
+  // Waves 0-3 stage P tiles, waves 4-7 Q tiles (a wave-uniform split), with
+  // one plan per thread.  When both operands have the same layout and tile
+  // height the staging code is the same for both roles and the main loop
+  // has no branch.
+  constexpr bool kUnified = PT == QT && BM == BN;
+  const bool loadsP = wave < 4;
+  const int tl = tid & 255;
+  Plan pl;
+  const uint32_t my_lds = loadsP ? 0u : (uint32_t)BM * 128u;
+  auto plan_init = [&](const Tile& c) {
+    if (loadsP) pl.init<BM, PT>((const bf16*)g.P, g.ldp, c.m0, c.kbeg, tl);
+    else pl.init<BN, QT>((const bf16*)g.Q, g.ldq, c.n0, c.kbeg, tl);
+  };
+  u32x4 reg[8];
   auto stage_load = [&]() {
     if constexpr (kUnified) {
-      pp.load(reg);
+      pl.load<BM, PT>(reg, tl);
     } else {
-      if (loadsP) pp.load(reg);
-      if (loadsQ) pq.load(rq);
+      if (loadsP) pl.load<BM, PT>(reg, tl);
+      else pl.load<BN, QT>(reg, tl);
     }
   };
   auto stage_store = [&](char* base) {
     if constexpr (kUnified) {
-      pp.store(reg, base + my_lds);
+      pl.store<BM, PT>(reg, base + my_lds, tl);
     } else {
-      if (loadsP) pp.store(reg, base);
-      if (loadsQ) pq.store(rq, base + BM * 128);
+      if (loadsP) pl.store<BM, PT>(reg, base, tl);
+      else pl.store<BN, QT>(reg, base + BM * 128, tl);
     }
   };
-  auto stage_advance = [&](bool more) {
-    if constexpr (kUnified) {
-      pp.advance_if(more);
-    } else {
-      if (loadsP) pp.advance_if(more);
-      if (loadsQ) pq.advance_if(more);
-    }
-  };
-
-  floatx16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // Pipeline (stage s of LDS holds tile t with s = t & 1):
-  //   iteration t:  write tile t+1 (staged in registers) to stage (t+1)&1,
-  //                 issue the global loads of tile t+2,
-  //                 k16 steps 0-2 of tile t (fragments read one step ahead),
-  //                 barrier,
-  //                 read tile t+1's step-0 fragments, then step 3 of tile t --
-  //   so the MFMAs of step 3 cover the first LDS reads after the barrier.
-  // The write of tile t+1 reuses the stage tile t-1 occupied; its last reads
-  // were issued before the previous barrier, which waits for them.
-  // Tiles past the last are never fetched: the staged tile index is clamped
-  // to nk-1 (the pointer stops advancing), so the final iterations restage
-  // the last tile into the idle stage instead of branching around the copy.
-  stage_load();                 // tile 0
-  stage_store(smem);
-  stage_advance(nk > 1);
-  stage_load();                 // tile min(1, nk-1)
-  __syncthreads();
+  auto stage_advance = [&](bool more) { pl.advance_if(more); };
 
   const int frow = lane & 31, fchunk = lane >> 5;
   uint32_t offQ[FN], offP[FM];
@@ -252,6 +228,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   // chunk 2s + fchunk sits at slot (2s + fchunk) ^ f(row) = (fchunk ^ f(row)) ^ 2s:
   // the k16 step s moves the byte offset by an xor of 32*s
 
+  floatx16 acc[FM][FN];
   bf16x8 a[2][FN], bb[2][FM];
   auto read_frags = [&](const char* st, int s, int buf) {
 #pragma unroll
@@ -266,173 +243,310 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[buf][j], bb[buf][i], acc[i][j], 0, 0, 0);
   };
-  read_frags(smem, 0, 0);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* st = smem + (kt & 1) * STAGE;
-    char* nx = smem + ((kt + 1) & 1) * STAGE;
-    stage_store(nx);              // tile min(kt+1, nk-1)
-    stage_advance(kt + 2 < nk);
-    stage_load();                 // tile min(kt+2, nk-1)
+  int v = blockIdx.x;
+  Tile cur = coords(v);
+  plan_init(cur);
+  stage_load();                 // k-tile 0 of the first tile
+
+  for (;;) {
 #pragma unroll
-    for (int s = 0; s < BK / 16 - 1; ++s) {
-      read_frags(st, s + 1, (s + 1) & 1);
-      mfmas(s & 1);
-      // Interleave so every memory instruction issues between MFMAs: in
-      // step 0 the staged tile's LDS writes and the next global loads, in
-      // every step the fragment reads of the following step.
-      constexpr int nm = FM * FN, nr = FM + FN, ns = kUnified ? BM / 32 : 0;
-      if (s == 0 && kUnified) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int q = 0; q < nm; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
-          if (q < ns) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // DS write
-          if (q < ns) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // global load
-          if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Pipeline (stage s of LDS holds k-tile t with s = t & 1):
+    //   iteration t:  k16 steps 0-2 of k-tile t (fragments read one step
+    //                 ahead), with, during step 2, k-tile t+1 (staged in
+    //                 registers) written to stage (t+1)&1 and the global
+    //                 loads of k-tile t+2 issued;
+    //                 barrier;
+    //                 read k-tile t+1's step-0 fragments, then step 3 of
+    //                 k-tile t -- its MFMAs cover the first LDS reads after
+    //                 the barrier.
+    // The write of k-tile t+1 reuses the stage k-tile t-1 occupied; its
+    // last reads were issued before the previous barrier, which waits for
+    // them.  A k-tile's loads have a whole iteration to arrive, and the
+    // first one's latency hides behind the previous tile's epilogue.
+    // K-tiles past the last are never fetched: the staged index is clamped
+    // to nk-1 (the pointer stops advancing), so the final iterations restage
+    // the last k-tile into the idle stage instead of branching around it.
+    stage_store(smem);          // k-tile 0
+    stage_advance(nk > 1);
+    stage_load();               // k-tile min(1, nk-1)
+    __syncthreads();
+    read_frags(smem, 0, 0);
+
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* st = smem + (kt & 1) * STAGE;
+      char* nx = smem + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+      for (int s = 0; s < BK / 16 - 1; ++s) {
+        if (s == BK / 16 - 2) {
+          // before the next fragment reads, so the staging registers (and a
+          // transpose's temporaries) are dead by the time those land
+          stage_store(nx);      // k-tile min(kt+1, nk-1)
+          stage_advance(kt + 2 < nk);
+          stage_load();         // k-tile min(kt+2, nk-1)
         }
-      } else {
+        read_frags(st, s + 1, (s + 1) & 1);
+        mfmas(s & 1);
+        // Interleave so every memory instruction issues between MFMAs: in
+        // the last step before the barrier the staged k-tile's LDS writes
+        // and the next global loads, then the fragment reads of the
+        // following step; in the other steps the fragment reads.
+        constexpr int nm = FM * FN, nr = FM + FN, ns = kUnified ? BM / 32 : 0;
+        if (s == BK / 16 - 2 && kUnified) {
 #pragma unroll
-        for (int q = 0; q < nm; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int q = 0; q < nm; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+            if (q < ns) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // DS write
+            if (q < ns) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // global load
+            if (q >= nm - nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < nm; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
         }
+      }
+      __syncthreads();
+      read_frags(nx, 0, 0);       // next k-tile's step 0 (a harmless reread after the last)
+      mfmas((BK / 16 - 1) & 1);
+#pragma unroll
+      for (int q = 0; q < FM * FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
     __syncthreads();
-    read_frags(nx, 0, 0);         // next tile's step 0 (a harmless reread after the last)
-    mfmas((BK / 16 - 1) & 1);
-#pragma unroll
-    for (int q = 0; q < FM * FN; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  }
-  __syncthreads();
 
-  // ------------------------------------------------------------------ epilogue
-  // lane holds row m = m0 + wm*WTM + i*32 + (lane&31) and, for register
-  // group q (4 regs), columns n = n0 + wn*WTN + j*32 + 8q + 4*(lane>>5) + 0..3
-  const int64_t nw = n0 + wn * WTN + 4 * (lane >> 5);
+    // The block's next tile: its first k-tile's loads are issued once the
+    // accumulators have gone to LDS, and overlap the rest of the epilogue.
+    const int vn = v + (int)gridDim.x;
+    const bool more = vn < total;
+    const Tile c = cur;
+    auto prefetch_next = [&]() {
+      if (more) {
+        cur = coords(vn);
+        plan_init(cur);
+        stage_load();
+      }
+    };
+    v = vn;
+    // The thread index, opaque to the compiler once per tile: without this
+    // the epilogue's per-thread addresses are hoisted out of the tile loop
+    // and held (or spilled) through the main loop.
+    int etid = tid;
+    asm volatile("" : "+v"(etid));
+    const int elane = etid & 63;
 
-  if constexpr (EPI == EPI_LSE) {
-    float2* red = reinterpret_cast<float2*>(smem);      // [4 wn][BM]
+    // ---------------------------------------------------------------- epilogue
+    // lane holds row m = m0 + wm*WTM + i*32 + (lane&31) and, for register
+    // group q (4 regs), columns n = n0 + wn*WTN + j*32 + 8q + 4*(lane>>5) + 0..3
+    if constexpr (EPI == EPI_LSE) {
+      const int64_t nw = c.n0 + wn * WTN + 4 * (elane >> 5);
+      float2* red = reinterpret_cast<float2*>(smem);      // [4 wn][BM]
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int ml = wm * WTM + i * 32 + (lane & 31);
-      const int64_t m = m0 + ml;
-      float mx = -INFINITY;
+      for (int i = 0; i < FM; ++i) {
+        const int ml = wm * WTM + i * 32 + (elane & 31);
+        const int64_t m = c.m0 + ml;
+        float mx = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float s = 0.f;
-      const float mxs = mx * kLog2e;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        float s = 0.f;
+        const float mxs = mx * kLog2e;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(acc[i][j][r] * kLog2e - mxs);
-      s += __shfl_xor(s, 32, 64);
-      if (lane < 32) red[wn * BM + ml] = make_float2(mx, s);
-      // the target's logit, from whichever lane holds it
-      const int t = g.tgt[m];
+          for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(acc[i][j][r] * kLog2e - mxs);
+        s += __shfl_xor(s, 32, 64);
+        if (elane < 32) red[wn * BM + ml] = make_float2(mx, s);
+        // the target's logit, from whichever lane holds it
+        const int t = g.tgt[m];
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (t == nw + j * 32 + 8 * (r >> 2) + (r & 3)) g.ztgt[m] = acc[i][j][r];
-    }
-    __syncthreads();
-    if (tid < BM) {
-      float2 p[WGN];
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < WGN; ++w) {
-        p[w] = red[w * BM + tid];
-        M = fmaxf(M, p[w].x);
+          for (int r = 0; r < 16; ++r)
+            if (t == nw + j * 32 + 8 * (r >> 2) + (r & 3)) g.ztgt[m] = acc[i][j][r];
       }
-      float S = 0.f;
+      __syncthreads();
+      prefetch_next();
+      if (etid < BM) {
+        float2 p[WGN];
+        float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < WGN; ++w) S += p[w].y * __builtin_amdgcn_exp2f((p[w].x - M) * kLog2e);
-      g.lse_part[(m0 + tid) * g.lse_stride + tn] = make_float2(M, S);
-    }
-    return;
-  } else {
+        for (int w = 0; w < WGN; ++w) {
+          p[w] = red[w * BM + etid];
+          M = fmaxf(M, p[w].x);
+        }
+        float S = 0.f;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
-      float dz_l = 0.f, dz_s = 0.f;
-      int dz_t = -1;
-      int rope_t = 0;
-      if constexpr (EPI == EPI_DZ) {
-        dz_t = g.tgt[m];
-        dz_l = g.lse[m] * kLog2e;
-        dz_s = dz_t >= 0 ? *g.inv_nvalid : 0.f;
+        for (int w = 0; w < WGN; ++w) S += p[w].y * __builtin_amdgcn_exp2f((p[w].x - M) * kLog2e);
+        g.lse_part[(c.m0 + etid) * g.lse_stride + c.tn] = make_float2(M, S);
       }
-      if constexpr (EPI == EPI_ROPE) rope_t = (int)(m % g.rope_T);
+    } else {
+      // Two passes, one per half of the tile's rows (the waves with wm = h
+      // own rows h*WTM ..): those waves write their fp32 accumulators to
+      // LDS as [WTM][BN] (16-byte chunk cc of row r at slot cc ^ (r & 15), so
+      // the 16 rows of a write and the 16 chunks of a read are
+      // conflict-free), then all threads read the half back a row segment
+      // at a time and finish it -- aux reads and stores cover contiguous
+      // runs of a row instead of 8 bytes in each of 32 rows.
+      constexpr int CPR = BN / 4;                      // 16-byte fp32 chunks per row
+      constexpr int RPS = NW * 64 / CPR;               // rows per sweep of the block
+      static_assert(WTM * BN * 4 <= 2 * STAGE && CPR >= 16 && (NW * 64) % CPR == 0, "epilogue staging");
+      float* ep = reinterpret_cast<float*>(smem);
+      const int cc = etid % CPR, r0 = etid / CPR;
+      const int64_t n = c.n0 + 4 * cc;
+      constexpr int NR = WTM / RPS;                    // rows per thread and pass
+      const float inv_nv = EPI == EPI_DZ ? *g.inv_nvalid : 0.f;
+      int pi = 0;
+      if constexpr (EPI == EPI_ROPE) pi = (int)(n % g.head_dim) >> 1;
+      const bool rot = EPI == EPI_ROPE && n < g.rope_cols;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int h = 0; h < 2; ++h) {
+        // The pass's global inputs (aux rows, rotary factors, per-row loss
+        // terms) are requested W rows ahead of their use, the first W
+        // before the LDS round trip, which hides their latency.
+        constexpr int W = EPI == EPI_ROPE ? (NR >= 16 ? NR / 4 : NR) : (NR >= 8 ? NR / 2 : NR);
+        uint2 pa[W];
+        float4 pc[W];
+        int pt[W];
+        float pl[W];
+        // rotary: position of the pass's first row in its sequence (rows
+        // index tokens; the table is read for every column, in bounds, and
+        // used where rot holds)
+        uint32_t tpos = 0;
+        if constexpr (EPI == EPI_ROPE) tpos = (uint32_t)((c.m0 + h * WTM + r0) % g.rope_T);
+        auto fetch = [&](int k) {
+          const int64_t m = c.m0 + h * WTM + r0 + k * RPS;
+          if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2)
+            pa[k % W] = *reinterpret_cast<const uint2*>((const bf16*)g.aux + m * g.ldaux + n);
+          if constexpr (EPI == EPI_ROPE) {
+            const uint32_t t = (tpos + (uint32_t)(k * RPS)) % (uint32_t)g.rope_T;
+            pc[k % W] = *reinterpret_cast<const float4*>(g.rope + t * (uint32_t)(g.head_dim >> 1) + pi);
+          }
+          if constexpr (EPI == EPI_DZ) {
+            pt[k % W] = g.tgt[m];
+            pl[k % W] = g.lse[m];
+          }
+        };
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = nw + j * 32 + 8 * q;
-          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        for (int k = 0; k < W; ++k) fetch(k);
+        if (wm == h) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int r = i * 32 + (elane & 31);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int ch = (wn * WTN + j * 32 + 8 * q) / 4 + (elane >> 5);
+                *reinterpret_cast<float4*>(ep + r * BN + ((ch ^ (r & 15)) << 2)) =
+                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+              }
+          }
+        }
+        __syncthreads();
+        if (h == 1) prefetch_next();
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+          const int r = r0 + k * RPS;
+          const int64_t m = c.m0 + h * WTM + r;
+          const float4 f = *reinterpret_cast<const float4*>(ep + r * BN + ((cc ^ (r & 15)) << 2));
+          float x[4] = {f.x, f.y, f.z, f.w};
+          const uint2 y = pa[k % W];
+          const float4 cs = pc[k % W];
+          const int dz_t = pt[k % W];
+          const float dz_l = pl[k % W] * kLog2e;
+          if (k + W < NR) fetch(k + W);
           if constexpr (EPI == EPI_F32) {
             if (g.splits > 1) {
-              float* dst = g.part + (int64_t)split * g.M * g.N + m * g.N + n;
-              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+              float* dst = g.part + (int64_t)c.split * g.M * g.N + m * g.N + n;
+              *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
             } else {
               float* dst = (float*)g.C + m * g.ldc + n;
-              float4 o = make_float4(v[0], v[1], v[2], v[3]);
+              float4 o = make_float4(x[0], x[1], x[2], x[3]);
               if (g.beta) {
-                const float4 c = *reinterpret_cast<const float4*>(dst);
-                o.x += c.x; o.y += c.y; o.z += c.z; o.w += c.w;
+                const float4 y = *reinterpret_cast<const float4*>(dst);
+                o.x += y.x; o.y += y.y; o.z += y.z; o.w += y.w;
               }
               *reinterpret_cast<float4*>(dst) = o;
             }
             continue;
           }
           if constexpr (EPI == EPI_ROPE) {
-            if (n < g.rope_cols) {
-              const int pi = (int)(n % g.head_dim) >> 1;
-              const float4 cs = *reinterpret_cast<const float4*>(g.rope + (int64_t)rope_t * (g.head_dim >> 1) + pi);
-              const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
-              v[0] = x0 * cs.x - x1 * cs.y;
-              v[1] = x0 * cs.y + x1 * cs.x;
-              v[2] = x2 * cs.z - x3 * cs.w;
-              v[3] = x2 * cs.w + x3 * cs.z;
-            }
+            // (rot ? rotated : as is), without a branch
+            const float c0 = rot ? cs.x : 1.f, s0 = rot ? cs.y : 0.f;
+            const float c1 = rot ? cs.z : 1.f, s1 = rot ? cs.w : 0.f;
+            const float x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
+            x[0] = x0 * c0 - x1 * s0;
+            x[1] = x0 * s0 + x1 * c0;
+            x[2] = x2 * c1 - x3 * s1;
+            x[3] = x2 * s1 + x3 * c1;
           }
           if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2) {
-            const uint2 a = *reinterpret_cast<const uint2*>((const bf16*)g.aux + m * g.ldaux + n);
-            const float a0 = bf_lo(a.x), a1 = bf_hi(a.x), a2 = bf_lo(a.y), a3 = bf_hi(a.y);
+            const float a0 = bf_lo(y.x), a1 = bf_hi(y.x), a2 = bf_lo(y.y), a3 = bf_hi(y.y);
             if constexpr (EPI == EPI_RESID) {
-              v[0] += a0; v[1] += a1; v[2] += a2; v[3] += a3;
+              x[0] += a0; x[1] += a1; x[2] += a2; x[3] += a3;
             } else {
               // aux = relu(h)^2, so 2 relu(h) = 2 sqrt(aux)
-              v[0] *= 2.f * __builtin_sqrtf(fmaxf(a0, 0.f));
-              v[1] *= 2.f * __builtin_sqrtf(fmaxf(a1, 0.f));
-              v[2] *= 2.f * __builtin_sqrtf(fmaxf(a2, 0.f));
-              v[3] *= 2.f * __builtin_sqrtf(fmaxf(a3, 0.f));
+              x[0] *= 2.f * __builtin_sqrtf(fmaxf(a0, 0.f));
+              x[1] *= 2.f * __builtin_sqrtf(fmaxf(a1, 0.f));
+              x[2] *= 2.f * __builtin_sqrtf(fmaxf(a2, 0.f));
+              x[3] *= 2.f * __builtin_sqrtf(fmaxf(a3, 0.f));
             }
           }
           if constexpr (EPI == EPI_RELU2) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f) * fmaxf(v[e], 0.f);
+            for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], 0.f) * fmaxf(x[e], 0.f);
           }
           if constexpr (EPI == EPI_DZ) {
+            const float dz_s = dz_t >= 0 ? inv_nv : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              v[e] = (__builtin_amdgcn_exp2f(v[e] * kLog2e - dz_l) - ((n + e) == dz_t ? 1.f : 0.f)) * dz_s;
+              x[e] = (__builtin_amdgcn_exp2f(x[e] * kLog2e - dz_l) - ((n + e) == dz_t ? 1.f : 0.f)) * dz_s;
           }
-          *reinterpret_cast<uint2*>((bf16*)g.C + m * g.ldc + n) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+          *reinterpret_cast<uint2*>((bf16*)g.C + m * g.ldc + n) = make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
         }
+        if (h == 0) __syncthreads();
+      }
     }
+    if (!more) break;
+    __syncthreads();            // epilogue LDS traffic done before k-tile 0 is written
   }
+}
+
+// Blocks of one instantiation that fit on the device at once, times the
+// device's CU count; cached per instantiation and device.
+template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
+int resident_blocks() {
+  static int cached[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (!cached[dev]) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemm_mfma<NW, BM, BN, PT, QT, EPI>, NW * 64, 0) !=
+            hipSuccess || per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    cached[dev] = ((per_cu * cus) + 7) / 8 * 8;
+  }
+  return cached[dev];
 }
 
 template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
 hipError_t launch(const GemmDesc& g, hipStream_t s) {
-  dim3 grid((g.M / BM) * (g.N / BN) * g.splits);
+  const int total = (g.M / BM) * (g.N / BN) * g.splits;
+  dim3 grid(std::min(total, resident_blocks<NW, BM, BN, PT, QT, EPI>()));
   k_gemm_mfma<NW, BM, BN, PT, QT, EPI><<<grid, NW * 64, 0, s>>>(g);
   return hipGetLastError();
 }
@@ -444,18 +558,19 @@ hipError_t launch(const GemmDesc& g, hipStream_t s) {
 //   forward:  qkv (ROPE), o Wo^T + x and u W2^T + x (RESID),
 //             u = relu(m W1^T)^2 (RELU2), head (LSE), head recompute (DZ)
 //   backward: weight gradients (both operands transposed, fp32 partials),
-//             activation gradients (Q transposed: STORE, DRELU2)
+//             activation gradients against transposed weight images
+//             (both k-major: STORE, DRELU2)
 //   tests:    every layout with fp32 and bf16 stores
 #define NC_MFMA_COMBOS(X)     \
   X(0, 0, EPI_STORE)          \
   X(0, 0, EPI_ROPE)           \
   X(0, 0, EPI_RESID)          \
   X(0, 0, EPI_RELU2)          \
+  X(0, 0, EPI_DRELU2)         \
   X(0, 0, EPI_LSE)            \
   X(0, 0, EPI_DZ)             \
   X(0, 0, EPI_F32)            \
   X(0, 1, EPI_STORE)          \
-  X(0, 1, EPI_DRELU2)         \
   X(0, 1, EPI_F32)            \
   X(1, 0, EPI_STORE)          \
   X(1, 0, EPI_F32)            \

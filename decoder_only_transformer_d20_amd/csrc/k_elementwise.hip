@@ -271,6 +271,42 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float4* __restrict_
   out[i] = a;
 }
 
+// out[c][r] = in[r][c] for a [rows][cols] 16-bit matrix (rows, cols
+// multiples of 8): 64 x 64 tiles through LDS, 16-byte reads and writes.
+__global__ void __launch_bounds__(256) k_transpose16(const uint16_t* __restrict__ in, int64_t rows, int64_t cols,
+                                                     uint16_t* __restrict__ out) {
+  __shared__ uint16_t t[64][64 + 2];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + 256 * k, rr = q >> 3, ch = q & 7;      // tile row, 8-element chunk
+    const int64_t r = r0 + rr, c = c0 + ch * 8;
+    if (r < rows && c < cols) {
+      const uint4 v = *reinterpret_cast<const uint4*>(in + r * cols + c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t[rr][ch * 8 + 2 * e] = (uint16_t)(w[e] & 0xffffu);
+        t[rr][ch * 8 + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int q = tid + 256 * k, cc = q >> 3, ch = q & 7;      // output row (input column), chunk
+    const int64_t c = c0 + cc, r = r0 + ch * 8;
+    if (c < cols && r < rows) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)t[ch * 8 + 2 * e][cc] | ((uint32_t)t[ch * 8 + 2 * e + 1][cc] << 16);
+      *reinterpret_cast<uint4*>(out + c * rows + r) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 __global__ void k_fill_f32(float* p, int64_t n, float v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -363,6 +399,12 @@ hipError_t splitk_reduce(const float* part, int splits, int64_t n, float* out, i
   if (n % 4) return hipErrorInvalidValue;
   const int64_t n4 = n / 4;
   k_splitk_reduce<<<nblocks(n4, 256), 256, 0, s>>>((const float4*)part, splits, n4, (float4*)out, beta);
+  return hipGetLastError();
+}
+hipError_t transpose_bf16(const bf16* in, int64_t rows, int64_t cols, bf16* out, hipStream_t s) {
+  if (rows <= 0 || cols <= 0 || rows % 8 || cols % 8 || (rows + 63) / 64 > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  k_transpose16<<<grid, 256, 0, s>>>((const uint16_t*)in, rows, cols, (uint16_t*)out);
   return hipGetLastError();
 }
 hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {

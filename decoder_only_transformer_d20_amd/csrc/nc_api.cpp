@@ -77,7 +77,7 @@ int choose_splits(const nc_config& c, int M, int N, int64_t K) {
 struct Plan {
   size_t total = 0;
   size_t rope = 0, idx = 0, tgt = 0, x = 0, xf = 0, rf = 0, ce = 0, lse_head = 0, ztgt = 0, lse_part = 0;
-  size_t scalars = 0, dz = 0, g = 0, gtmp = 0, big = 0, part = 0, delta = 0;
+  size_t scalars = 0, dz = 0, g = 0, gtmp = 0, big = 0, part = 0, delta = 0, wt = 0;
   size_t layer0 = 0, layer_stride = 0;
   size_t l_a = 0, l_r1 = 0, l_qkv = 0, l_o = 0, l_lse = 0, l_m = 0, l_r2 = 0, l_u = 0;
   int head_nblk = 0;
@@ -97,6 +97,8 @@ Plan make_plan(const nc_config& c) {
   p.g = take(N * d * es);
   p.gtmp = take(N * d * es);
   p.big = take(N * std::max(F, 3 * d) * es);
+  // bf16: transposed image of the weight an activation gradient multiplies by
+  if (is_bf16(c)) p.wt = take(std::max({F * d, 3 * d * d, is_block(c) ? 0 : V * d}) * es);
   // split-K partials: the largest of the weight-gradient products
   size_t part = 0;
   auto need = [&](int M_, int N_, int64_t K_) {
@@ -188,10 +190,10 @@ int gemm_family(const GemmDesc& g) {
     case EPI_ROPE: return key == 0 ? NC_TRACE_GEMM_QKV_ROPE : -1;
     case EPI_RESID: return key == 0 ? NC_TRACE_GEMM_RESIDUAL : -1;
     case EPI_RELU2: return key == 0 ? NC_TRACE_GEMM_RELU2 : -1;
-    case EPI_STORE: return key == 1 ? NC_TRACE_GEMM_DGRAD : -1;
+    case EPI_STORE: return key <= 1 ? NC_TRACE_GEMM_DGRAD : -1;
     case EPI_LSE: return key == 0 ? NC_TRACE_GEMM_HEAD_LSE : -1;
     case EPI_DZ: return key == 0 ? NC_TRACE_GEMM_HEAD_DZ : -1;
-    case EPI_DRELU2: return key == 1 ? NC_TRACE_GEMM_DGRAD_RELU2 : -1;
+    case EPI_DRELU2: return key <= 1 ? NC_TRACE_GEMM_DGRAD_RELU2 : -1;
     case EPI_F32: return key == 3 ? NC_TRACE_GEMM_WGRAD : -1;
     default: return -1;
   }
@@ -254,6 +256,24 @@ GemmDesc gemm(int M, int N, int K, const void* P, int64_t ldp, int pt, const voi
   g.Q = Q; g.ldq = ldq; g.q_trans = qt;
   g.epi = epi; g.C = C; g.ldc = ldc; g.splits = 1;
   return g;
+}
+
+// Activation gradient dX[M][cols] = dY[M][rows] W (W [rows][cols], the
+// weight of a forward product y = x W^T).  In bf16 the weight is first
+// transposed into the workspace, so the product reads both operands k-major;
+// in fp32 the product reads W as a transposed operand.
+template <typename T>
+hipError_t dgrad_desc(nc_ctx* ctx, int M, const T* dY, int64_t ldy, const T* W, int rows, int cols, int epi, T* out,
+                      int64_t ldo, GemmDesc* g) {
+  if constexpr (sizeof(T) == 2) {
+    T* wt = ctx->at<T>(ctx->plan.wt);
+    hipError_t e = transpose_bf16((const bf16*)W, rows, cols, (bf16*)wt, ctx->stream);
+    if (e != hipSuccess) return e;
+    *g = gemm(M, cols, rows, dY, ldy, 0, wt, rows, 0, epi, out, ldo);
+  } else {
+    *g = gemm(M, cols, rows, dY, ldy, 0, W, cols, 1, epi, out, ldo);
+  }
+  return hipSuccess;
 }
 
 // weight gradient dW[M'][N'] (+)= sum over tokens P[tok][m'] Q[tok][n']
@@ -361,22 +381,26 @@ int layer_backward(nc_ctx* ctx, int l, const T* w, T* gr, float* dw, int accumul
 
   // MLP: x2 = x1 + u W2^T, u = relu(h)^2, h = m W1^T
   NC_TRY(weight_grad(ctx, d, F, gr, d, u, F, dW2, accumulate), "dW2");
-  GemmDesc g = gemm(N, F, d, gr, d, 0, W2, F, 1, EPI_DRELU2, big, F);
+  GemmDesc g;
+  NC_TRY(dgrad_desc<T>(ctx, N, gr, d, W2, d, F, EPI_DRELU2, big, F, &g), "transpose W2");
   g.aux = u; g.ldaux = F;
   NC_TRY(run_gemm(ctx, g), "dh = (g W2) * 2 relu(h)");
   NC_TRY(weight_grad(ctx, F, d, big, F, m, d, dW1, accumulate), "dW1");
-  NC_TRY(run_gemm(ctx, gemm(N, d, F, big, F, 0, W1, d, 1, EPI_STORE, tmp, d)), "dm = dh W1");
+  NC_TRY(dgrad_desc<T>(ctx, N, big, F, W1, F, d, EPI_STORE, tmp, d, &g), "transpose W1");
+  NC_TRY(run_gemm(ctx, g), "dm = dh W1");
   NC_TRY(rmsnorm_bwd<T>(m, r2, tmp, gr, N, d, 1, s), "rmsnorm backward (MLP input)");
   // attention: x1 = x0 + o Wo^T
   NC_TRY(weight_grad(ctx, d, d, gr, d, o, d, dWo, accumulate), "dWo");
-  NC_TRY(run_gemm(ctx, gemm(N, d, d, gr, d, 0, Wo, d, 1, EPI_STORE, tmp, d)), "do = g Wo");
+  NC_TRY(dgrad_desc<T>(ctx, N, gr, d, Wo, d, d, EPI_STORE, tmp, d, &g), "transpose Wo");
+  NC_TRY(run_gemm(ctx, g), "do = g Wo");
   AttnDesc ad{};
   ad.B = c.batch; ad.T = c.seq_len; ad.H = c.n_head; ad.Q = c.head_dim;
   ad.qkv = qkv; ad.o = o; ad.lse = lse; ad.dout = tmp; ad.delta = ctx->at<float>(p.delta);
   ad.dqkv = big; ad.rope = ctx->at<float2>(p.rope);
   NC_TRY(attn_bwd<T>(ctx, ad), "attention backward");
   NC_TRY(weight_grad(ctx, 3 * d, d, big, 3 * d, a, d, dWqkv, accumulate), "dWqkv");
-  NC_TRY(run_gemm(ctx, gemm(N, d, 3 * d, big, 3 * d, 0, Wqkv, d, 1, EPI_STORE, tmp, d)), "da = dqkv Wqkv");
+  NC_TRY(dgrad_desc<T>(ctx, N, big, 3 * d, Wqkv, 3 * d, d, EPI_STORE, tmp, d, &g), "transpose Wqkv");
+  NC_TRY(run_gemm(ctx, g), "da = dqkv Wqkv");
   NC_TRY(rmsnorm_bwd<T>(a, r1, tmp, gr, N, d, 1, s), "rmsnorm backward (attention input)");
   return NC_OK;
 }
@@ -430,13 +454,17 @@ int model_backward(nc_ctx* ctx, const T* params, float* grads, int accumulate) {
   T* dz = ctx->at<T>(p.dz);
   const int32_t* wtgt = ctx->at<int32_t>(p.tgt);
   // head, one token chunk at a time: dz = (softmax(z) - onehot) / n_valid,
-  // dxf = dz U, dU (+)= dz^T xf
+  // dxf = dz U, dU (+)= dz^T xf.  (U is transposed once, for every chunk.)
+  GemmDesc gx;
+  NC_TRY(dgrad_desc<T>(ctx, 0, dz, V, U, V, d, EPI_STORE, tmp, d, &gx), "transpose U");
   for (int64_t r0 = 0; r0 < N; r0 += p.head_chunk) {
     const int Mc = (int)std::min<int64_t>(p.head_chunk, N - r0);
     GemmDesc g = gemm(Mc, V, d, xf + r0 * d, d, 0, U, d, 0, EPI_DZ, dz, V);
     g.tgt = wtgt + r0; g.lse = ctx->at<float>(p.lse_head) + r0; g.inv_nvalid = ctx->at<float>(p.scalars);
     NC_TRY(run_gemm(ctx, g), "recompute logits -> dz");
-    NC_TRY(run_gemm(ctx, gemm(Mc, d, V, dz, V, 0, U, d, 1, EPI_STORE, tmp + r0 * d, d)), "dxf = dz U");
+    gx.M = Mc;
+    gx.C = tmp + r0 * d;
+    NC_TRY(run_gemm(ctx, gx), "dxf = dz U");
     g = gemm(V, d, Mc, dz, V, 1, xf + r0 * d, d, 1, EPI_F32, dU, d);
     g.beta = (accumulate || r0 > 0) ? 1 : 0;
     g.splits = choose_splits(c, V, d, Mc);

@@ -115,6 +115,8 @@ hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int
 hipError_t count_valid(const int32_t* tgt, int64_t n, float* inv_nvalid, hipStream_t s);
 hipError_t loss_bpb(const float* ce, const int32_t* tgt, const int32_t* bytes, int64_t n, double* out, hipStream_t s);
 hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// out [cols][rows] = transpose of in [rows][cols]; rows, cols multiples of 8
+hipError_t transpose_bf16(const bf16* in, int64_t rows, int64_t cols, bf16* out, hipStream_t s);
 hipError_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s);
 
 }  // namespace nc

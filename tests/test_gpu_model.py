@@ -132,6 +132,27 @@ def test_small_bf16_deterministic():
     np.testing.assert_allclose(a["grads"][:nE], b["grads"][:nE], rtol=1e-5, atol=1e-9)
 
 
+def test_small_bf16_every_product_on_matrix_cores():
+    """Every GEMM family of the bf16 step (all shapes of the small
+    configuration are tile multiples) launches the matrix-core kernel: a
+    family with no traced launch has fallen back to the portable kernel."""
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("small"))
+    sess = nc.Session(cfg)
+    P = dev(params, cfg.dtype)
+    I, Tg = dev(idx.ravel()), dev(tgt.ravel())
+    ce = empty((idx.size,), "f32")
+    out = empty((5,), "f64")
+    g = empty((params.size,), "f32")
+    for fam in nc.TRACE_FAMILIES:
+        sess.trace_enable(fam)
+        sess.forward(P, I, Tg, ce)
+        sess.loss_bpb(dev(tb), out)
+        sess.backward(P, g)
+        n, ms, fl, by = sess.trace_read()
+        assert n > 0 and ms > 0 and fl > 0, fam
+    sess.trace_enable(None)
+
+
 def _block_inputs(rows):
     cfg = synthdata.get_config("block")
     params = synthdata.make_params(cfg)
