@@ -11,20 +11,27 @@
 // pass the accumulators through LDS and finish them in row order, so aux
 // reads and output writes are contiguous runs of a row.
 //
-// Both operand tiles live in LDS as [row][64 k] bf16 (128 B per row), the
-// 16-byte chunk c of row r stored at chunk slot c ^ ((r >> 1) & 7) (see
-// lds_off): fragment reads and row writes are free of bank conflicts.
-// Operands stored k-major ([rows][K]) are copied in 16-byte pieces;
-// operands stored row-major in k ([K][rows], the backward pass's transposed
-// products) are read as 8 x 8 blocks and transposed in registers before the
-// LDS write, so every layout reaches the same LDS image.  Two LDS stages
-// and one register stage: the global loads of k-tile t+2 are in flight
-// while k-tile t is multiplied and k-tile t+1 is written; one barrier per
-// k-tile.  The grid is persistent (one block per CU, each looping over
-// output tiles).
+// An operand stored k-major ([rows][K]) lives in LDS as [row][64 k] bf16
+// (128 B per row), the 16-byte chunk c of row r at chunk slot
+// c ^ ((r >> 1) & 7) (see lds_off); a fragment is one ds_read_b128 per lane.
+// An operand stored the other way ([K][rows], the weight gradients' token
+// contractions) is copied unchanged, as [64 k][R rows] (2R bytes per k row,
+// chunk c of k row k at slot c ^ 4 (k & 3)), and its fragments are read with
+// gfx950's transposing LDS read (ds_read_b64_tr_b16): within each group of
+// 16 lanes, lane i receives element i & 3 of the 8-byte pieces that lanes
+// 4e + (i >> 2), e < 4, address -- so when those 16 lanes address four k
+// rows x four 4-element column pieces, every lane gets four consecutive k
+// of one row, which is the operand layout of the MFMA.  No layout needs
+// VALU transposes.  Global loads and LDS writes are row segments of 16-byte
+// chunks in either layout, and every fragment read and row write is free of
+// bank conflicts.  Two LDS stages and one register stage: the global loads
+// of k-tile t+2 are in flight while k-tile t is multiplied and k-tile t+1 is
+// written; one barrier per k-tile.  The grid is persistent (one block per
+// CU, each looping over output tiles).
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
 
 #include "nc_internal.h"
 
@@ -56,33 +63,21 @@ __device__ inline uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// 8 x 8 bf16 transpose: in[kk] holds 8 consecutive rows' elements at one k;
-// out[e] holds row e's 8 consecutive k values.
-__device__ inline void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = in[2 * p][e >> 1], b = in[2 * p + 1][e >> 1];
-      out[e][p] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
-}
-
 typedef const u32x4 __attribute__((address_space(1)))* gptr;
 
 // Per-thread plan for one operand tile (R rows x 64 k), loaded by 256
-// threads into `reg` (8 x 16 B) and written to LDS.
+// threads into `reg` (R/32 x 16 B) and written to LDS.
 //  k-major operand ([rows][K]): thread tl takes chunk tl & 7 of rows
 //    (tl >> 3) + 32 i, i < R/32 -- 8 lanes read one 128-byte row segment.
 //    Row r + 32 i has the swizzle of row r, so its LDS offset is that of
 //    row r plus 4096 i.
-//  transposed operand ([K][rows]): thread tl < R takes the 8 x 8 block at
-//    k rows (tl & 7)*8 .. +7 and tile rows (tl >> 3)*8 .. +7.  Row
-//    8 mg + e of chunk kc sits at (8 mg)*128 + 128 e with chunk slot
-//    kc ^ 4 (mg & 1) ^ (e >> 1): one base offset and an xor per row.
-// The state is layout-independent, so the two wave roles of a block share
-// one set of registers; the layout is a template argument of each call.
+//  [K][rows] operand: thread tl takes chunk tl % (R/8) of k rows
+//    tl / (R/8) + (2048/R) i, i < R/32 -- R/8 lanes read one 2R-byte row;
+//    the k rows of a thread agree mod 4, so their LDS offsets also step by
+//    (2048/R) * 2R = 4096 bytes.
+// Both layouts therefore load and store the same way; only the mapping
+// set up here differs.  The state is layout-independent, so the two wave
+// roles of a block share one set of registers.
 struct Plan {
   gptr ptr;          // this thread's first 16-byte piece of the current tile
   int64_t step;      // elements between the thread's successive pieces
@@ -98,39 +93,50 @@ struct Plan {
       kstep = BK;
       lds0 = lds_off(r, c);
     } else {
-      const int kc = tl & 7, mg = tl >> 3;
-      ptr = (gptr)(base + (k0 + kc * 8) * ld + row0 + mg * 8);
-      step = ld;
+      constexpr int CPR = R / 8;                 // 16-byte chunks per k row
+      const int c = tl % CPR, kr = tl / CPR;
+      ptr = (gptr)(base + (k0 + kr) * ld + row0 + c * 8);
+      step = (int64_t)(256 / CPR) * ld;
       kstep = (int64_t)BK * ld;
-      lds0 = (uint32_t)mg * 1024u + ((uint32_t)(kc ^ ((mg & 1) << 2)) << 4);
+      lds0 = (uint32_t)kr * (2u * R) + ((uint32_t)(c ^ (4 * (kr & 3))) << 4);
     }
   }
-  // transposed: 256 threads cover a 256-row tile; with R = 128 threads tl >= R idle
-  template <int R, bool TRANS>
-  __device__ inline void load(u32x4 (&reg)[8], int tl) const {
-    if (!TRANS) {
+  template <int R>
+  __device__ inline void load(u32x4 (&reg)[8]) const {
 #pragma unroll
-      for (int i = 0; i < R / 32; ++i) reg[i] = ptr[(i * step) >> 3];
-    } else if (R >= 256 || tl < R) {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) reg[kk] = ptr[(kk * step) >> 3];
-    }
+    for (int i = 0; i < R / 32; ++i) reg[i] = ptr[(i * step) >> 3];
   }
-  template <int R, bool TRANS>
-  __device__ inline void store(const u32x4 (&reg)[8], char* lds_base, int tl) const {
-    if (!TRANS) {
+  template <int R>
+  __device__ inline void store(const u32x4 (&reg)[8], char* lds_base) const {
 #pragma unroll
-      for (int i = 0; i < R / 32; ++i) *reinterpret_cast<u32x4*>(lds_base + lds0 + 4096u * i) = reg[i];
-    } else if (R >= 256 || tl < R) {
-      u32x4 t[8];
-      transpose8(reg, t);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<u32x4*>(lds_base + ((lds0 ^ (16u * (e >> 1))) + 128u * e)) = t[e];
-    }
+    for (int i = 0; i < R / 32; ++i) *reinterpret_cast<u32x4*>(lds_base + lds0 + 4096u * i) = reg[i];
   }
   __device__ inline void advance_if(bool more) { ptr += more ? (kstep >> 3) : 0; }
 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+// One MFMA operand fragment from a [64 k][R rows] image: the lane's byte
+// offset `off` (k rows 16 s + 8 (l >> 5) + ((l & 15) >> 2), see frag_tr_off)
+// gives k 0-3 of its row, the same offset plus 4 k rows gives k 4-7.
+template <int R>
+__device__ inline bf16x8 frag_tr(const char* p) {
+  typedef __attribute__((address_space(3))) v4i16* lptr;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(p + 8 * R));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// Lane l's offset for the fragment of rows row0 .. row0+31 at k16 step 0 in a
+// [64 k][R rows] image.  Lane groups of 16 (g = l >> 4) cover rows
+// row0 + 16 (g & 1) .. +15 at k half g >> 1; in a group, lane j addresses
+// k row (j >> 2) of the four and the 4-element piece j & 3 of the rows --
+// k rows that agree mod 4 share the swizzle 4 (j >> 2).
+template <int R>
+__device__ inline uint32_t frag_tr_off(int row0, int l) {
+  const int j = l & 15, g = l >> 4;
+  const int k = 8 * (g >> 1) + (j >> 2);
+  const int m = row0 + 16 * (g & 1) + 4 * (j & 3);
+  return (uint32_t)k * (2u * R) + ((uint32_t)((m >> 3) ^ (4 * (j >> 2))) << 4) + 8u * ((m >> 2) & 1);
+}
 
 // Waves in a 2 x 4 grid, wave tile (BM/2) x (BN/4); waves 0-3 stage P and
 // waves 4-7 stage Q (two waves per SIMD).
@@ -188,10 +194,10 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   };
 
   // Waves 0-3 stage P tiles, waves 4-7 Q tiles (a wave-uniform split), with
-  // one plan per thread.  When both operands have the same layout and tile
-  // height the staging code is the same for both roles and the main loop
-  // has no branch.
-  constexpr bool kUnified = PT == QT && BM == BN;
+  // one plan per thread.  Staging code depends only on the tile height, so
+  // with BM = BN it is the same for both roles and the main loop has no
+  // branch.
+  constexpr bool kUnified = BM == BN;
   const bool loadsP = wave < 4;
   const int tl = tid & 255;
   Plan pl;
@@ -202,19 +208,19 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   };
   u32x4 reg[8];
   auto stage_load = [&]() {
-    if constexpr (kUnified) {
-      pl.load<BM, PT>(reg, tl);
+    if constexpr (BM == BN) {
+      pl.load<BM>(reg);
     } else {
-      if (loadsP) pl.load<BM, PT>(reg, tl);
-      else pl.load<BN, QT>(reg, tl);
+      if (loadsP) pl.load<BM>(reg);
+      else pl.load<BN>(reg);
     }
   };
   auto stage_store = [&](char* base) {
-    if constexpr (kUnified) {
-      pl.store<BM, PT>(reg, base + my_lds, tl);
+    if constexpr (BM == BN) {
+      pl.store<BM>(reg, base + my_lds);
     } else {
-      if (loadsP) pl.store<BM, PT>(reg, base, tl);
-      else pl.store<BN, QT>(reg, base + BM * 128, tl);
+      if (loadsP) pl.store<BM>(reg, base);
+      else pl.store<BN>(reg, base + BM * 128);
     }
   };
   auto stage_advance = [&](bool more) { pl.advance_if(more); };
@@ -222,19 +228,28 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   const int frow = lane & 31, fchunk = lane >> 5;
   uint32_t offQ[FN], offP[FM];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) offQ[j] = BM * 128 + lds_off(wn * WTN + j * 32 + frow, fchunk);
+  for (int j = 0; j < FN; ++j)
+    offQ[j] = BM * 128 + (QT ? frag_tr_off<BN>(wn * WTN + j * 32, lane) : lds_off(wn * WTN + j * 32 + frow, fchunk));
 #pragma unroll
-  for (int i = 0; i < FM; ++i) offP[i] = lds_off(wm * WTM + i * 32 + frow, fchunk);
-  // chunk 2s + fchunk sits at slot (2s + fchunk) ^ f(row) = (fchunk ^ f(row)) ^ 2s:
-  // the k16 step s moves the byte offset by an xor of 32*s
+  for (int i = 0; i < FM; ++i)
+    offP[i] = PT ? frag_tr_off<BM>(wm * WTM + i * 32, lane) : lds_off(wm * WTM + i * 32 + frow, fchunk);
+  // k-major image: chunk 2s + fchunk sits at slot (2s + fchunk) ^ f(row) =
+  // (fchunk ^ f(row)) ^ 2s, so the k16 step s moves the byte offset by an
+  // xor of 32*s; [64 k][R] image: step s is 16 k rows further, 32R bytes
+  auto frag = [&](const char* st, uint32_t off, int s, auto trans, auto rows) -> bf16x8 {
+    if constexpr (decltype(trans)::value) return frag_tr<decltype(rows)::value>(st + off + 32u * decltype(rows)::value * s);
+    else return *reinterpret_cast<const bf16x8*>(st + (off ^ (32u * s)));
+  };
 
   floatx16 acc[FM][FN];
   bf16x8 a[2][FN], bb[2][FM];
   auto read_frags = [&](const char* st, int s, int buf) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) a[buf][j] = *reinterpret_cast<const bf16x8*>(st + (offQ[j] ^ (32u * s)));
+    for (int j = 0; j < FN; ++j)
+      a[buf][j] = frag(st, offQ[j], s, std::integral_constant<bool, QT>{}, std::integral_constant<int, BN>{});
 #pragma unroll
-    for (int i = 0; i < FM; ++i) bb[buf][i] = *reinterpret_cast<const bf16x8*>(st + (offP[i] ^ (32u * s)));
+    for (int i = 0; i < FM; ++i)
+      bb[buf][i] = frag(st, offP[i], s, std::integral_constant<bool, PT>{}, std::integral_constant<int, BM>{});
   };
   auto mfmas = [&](int buf) {
 #pragma unroll
@@ -242,6 +257,31 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[buf][j], bb[buf][i], acc[i][j], 0, 0, 0);
+  };
+
+  // Interleave so every memory instruction issues between MFMAs: in the
+  // last step before the barrier the staged k-tile's LDS writes and the next
+  // global loads, then the fragment reads of the following step; in the
+  // other steps the fragment reads, spread evenly.
+  constexpr int kMfma = FM * FN;
+  constexpr int kReads = FM * (PT ? 2 : 1) + FN * (QT ? 2 : 1);   // LDS read instructions per step
+  constexpr int kStage = BM / 32;                                 // LDS writes / global loads per k-tile
+  static_assert(kReads <= 3 * kMfma, "interleave");
+  // reads placed after the q-th MFMA, kPer at a time: as early as possible
+  // (the next step's operands have the longest to land), or, in a staging
+  // step, after the LDS writes, as late as possible
+  constexpr int kPer = (kReads + kMfma - 1) / kMfma;
+  auto reads_early = [&](int q) { return std::min(kPer, std::max(0, kReads - kPer * q)); };
+  auto reads_late = [&](int q) { return reads_early(kMfma - 1 - q); };
+  auto interleave_reads = [&]() {
+#pragma unroll
+    for (int q = 0; q < kMfma; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      const int r = reads_early(q);
+      if (r >= 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (r >= 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (r >= 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   };
 
   int v = blockIdx.x;
@@ -285,8 +325,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
 #pragma unroll
       for (int s = 0; s < BK / 16 - 1; ++s) {
         if (s == BK / 16 - 2) {
-          // before the next fragment reads, so the staging registers (and a
-          // transpose's temporaries) are dead by the time those land
+          // before the next fragment reads, so the staging registers are
+          // free again by the time those land
           stage_store(nx);      // k-tile min(kt+1, nk-1)
           stage_advance(kt + 2 < nk);
           stage_load();         // k-tile min(kt+2, nk-1)
@@ -297,31 +337,25 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
         // the last step before the barrier the staged k-tile's LDS writes
         // and the next global loads, then the fragment reads of the
         // following step; in the other steps the fragment reads.
-        constexpr int nm = FM * FN, nr = FM + FN, ns = kUnified ? BM / 32 : 0;
         if (s == BK / 16 - 2 && kUnified) {
 #pragma unroll
-          for (int q = 0; q < nm; ++q) {
+          for (int q = 0; q < kMfma; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
-            if (q < ns) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);       // DS write
-            if (q < ns) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);       // global load
-            if (q >= nm - nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+            if (q < kStage) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
+            if (q < kStage) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+            const int r = reads_late(q);
+            if (r >= 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+            if (r >= 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (r >= 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
         } else {
-#pragma unroll
-          for (int q = 0; q < nm; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
+          interleave_reads();
         }
       }
       __syncthreads();
       read_frags(nx, 0, 0);       // next k-tile's step 0 (a harmless reread after the last)
       mfmas((BK / 16 - 1) & 1);
-#pragma unroll
-      for (int q = 0; q < FM * FN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (q < FM + FN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+      interleave_reads();
     }
     __syncthreads();
 
