@@ -12,11 +12,13 @@
 // are computed transposed (S^T = K Q^T), which puts one query row in one
 // lane: the softmax statistics are per-lane scalars and the 8 consecutive
 // accumulators of a 16-key group are exactly the B operand of the next
-// product (P^T as B), provided the A operand (V^T, K^T, Q^T, dO^T in LDS)
-// lists its 16 keys in the matching order: keys 0-3, 8-11, 4-7, 12-15 of
-// each group ("slot order").  Tiles that need a transposed LDS image are
-// read as 8 x 8 blocks whose 8 rows are picked in slot order and
-// transposed in registers.
+// product (P^T as B), provided the A operand (V^T, K^T, Q^T, dO^T) lists its
+// 16 keys in the matching order: keys 0-3, 8-11, 4-7, 12-15 of each group
+// ("slot order").  Every tile sits in LDS once, in its natural
+// [rows][128 features] layout; the transposed operands are read from that
+// image with gfx950's transposing LDS read (ds_read_b64_tr_b16), which
+// hands each lane four consecutive rows of one feature column -- two reads
+// give the eight slot-ordered keys.
 #pragma once
 
 #include "nc_internal.h"
@@ -45,32 +47,16 @@ __device__ inline uint32_t pack2(float lo, float hi) {
 
 __device__ inline u32x4 gload(const bf16* p) { return *(gptr)p; }
 
-// gfx950's LDS serves 16 lanes x 16 B (64 banks, 256 B) per cycle, and a
-// fragment read takes 16 consecutive rows at one chunk, so the swizzles
-// give those 16 rows 16 distinct 16-byte slots modulo 256 B.
-// LDS image of a [rows][128] tile (256 B rows, 16 chunks): chunk c of row r at c ^ (r & 15)
-__device__ inline uint32_t off256(int row, int chunk) { return (uint32_t)row * 256u + ((uint32_t)(chunk ^ (row & 15)) << 4); }
-// LDS image of a [128][64 slots] transposed tile (128 B rows, 8 chunks):
-// chunk c of row r at c ^ ((r >> 1) & 7) (rows r, r+1 sit in opposite halves)
-__device__ inline uint32_t off128(int row, int chunk) {
-  return (uint32_t)row * 128u + ((uint32_t)(chunk ^ ((row >> 1) & 7)) << 4);
-}
-
-// key (or query) index, within a 64-row tile, of slot e of chunk cj
-__device__ inline int slot_row(int cj, int e) {
-  const int s = cj >> 1, h = cj & 1;
-  return 16 * s + 4 * h + (e < 4 ? e : e + 4);
-}
-
-__device__ inline void transpose8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = in[2 * p][e >> 1], b = in[2 * p + 1][e >> 1];
-      out[e][p] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-}
+// LDS image of a [64 rows][128 features] tile (256 B rows, 16 chunks of 16 B):
+// chunk c of row r at slot c ^ swz(r), swz(r) = 4 (r & 3) + ((r >> 2) & 3).
+// gfx950's LDS serves 256 B (64 banks) per cycle.  A natural fragment read
+// takes 16 consecutive rows at one chunk: swz is a permutation over them.
+// A transposing read takes, per 32 lanes, four rows r0 .. r0+3 (r0 a
+// multiple of 4) at four consecutive chunks 4t .. 4t+3: swz moves row
+// r0 + b to chunk group t ^ b, so the 16 slots are distinct.  A row write
+// (16 lanes, one row's 16 chunks) is a permutation too.
+__device__ inline uint32_t swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+__device__ inline uint32_t offN(int row, int chunk) { return (uint32_t)row * 256u + ((chunk ^ swz(row)) << 4); }
 
 // Natural image of 64 rows x 128 of one head (row stride ld elements in
 // global memory) by `nthr` threads starting at thread `t`: 1024 chunks.
@@ -87,23 +73,37 @@ __device__ inline void store_nat64(char* lds, int t, const u32x4 (&reg)[1024 / N
 #pragma unroll
   for (int i = 0; i < 1024 / NTHR; ++i) {
     const int q = t + NTHR * i;
-    *reinterpret_cast<u32x4*>(lds + off256(q >> 4, q & 15)) = reg[i];
+    *reinterpret_cast<u32x4*>(lds + offN(q >> 4, q & 15)) = reg[i];
   }
 }
 
-// Transposed image ([128 features][64 rows in slot order]) of 64 rows x 128:
-// 128 blocks of 8 x 8; thread t < 128 takes slot chunk t & 7, features (t >> 3)*8.
-__device__ inline void load_tr64(const bf16* src, int64_t ld, int t, u32x4 (&reg)[8]) {
-  const int cj = t & 7, fg = t >> 3;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) reg[e] = gload(src + (int64_t)slot_row(cj, e) * ld + fg * 8);
-}
-__device__ inline void store_tr64(char* lds, int t, const u32x4 (&reg)[8]) {
-  const int cj = t & 7, fg = t >> 3;
-  u32x4 tr[8];
-  transpose8(reg, tr);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(lds + off128(fg * 8 + e, cj)) = tr[e];
+// Transposed fragments of a natural image: for feature block t (features
+// 32t .. 32t+31) lane l receives feature 32t + (l & 31) at the 8
+// slot-ordered rows 16 sp + 4 hh + {0-3, 8-11} (hh = l >> 5).  In each group
+// of 16 lanes (g = l >> 4), lane j addresses row 4 hh + (j >> 2) (+8 for the
+// second read) and the 4-feature piece 16 (g & 1) + 4 (j & 3) of the block;
+// the read returns to lane j the four rows at feature 16 (g & 1) + j.
+// Moving to sp adds 16 rows = 4096 bytes (swz is unchanged); moving to t
+// adds 4 to the chunk index, which under swz (rows agree in their low 2 bits
+// of the chunk term) is an xor of 64 on the byte offset.
+struct TrOff {
+  uint32_t lo, hi;          // byte offsets of the two reads for t = 0, sp = 0
+  __device__ inline void init(int lane) {
+    const int j = lane & 15, g = lane >> 4, hh = g >> 1;
+    const int rlo = 4 * hh + (j >> 2), rhi = rlo + 8;
+    const int c = 2 * (g & 1) + ((j & 3) >> 1);
+    lo = (uint32_t)rlo * 256u + ((c ^ swz(rlo)) << 4) + 8u * (j & 1);
+    hi = (uint32_t)rhi * 256u + ((c ^ swz(rhi)) << 4) + 8u * (j & 1);
+  }
+  __device__ inline uint32_t l(int t, int sp) const { return (lo ^ (64u * t)) + 4096u * sp; }
+  __device__ inline uint32_t h(int t, int sp) const { return (hi ^ (64u * t)) + 4096u * sp; }
+};
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+__device__ inline bf16x8 frag_tr(const char* img, uint32_t lo, uint32_t hi) {
+  typedef __attribute__((address_space(3))) v4i16* lptr;
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(img + lo));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(img + hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

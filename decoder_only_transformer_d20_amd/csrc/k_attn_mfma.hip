@@ -35,7 +35,7 @@ __device__ inline void tile_order(int ntile, int H, int B, int& tile, int& h, in
 // forward
 // ===========================================================================
 __global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
-  __shared__ __attribute__((aligned(16))) char smem[2][32768];   // per stage: K image | V^T image
+  __shared__ __attribute__((aligned(16))) char smem[2][32768];   // per stage: K image | V image
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int T = a.T, H = a.H, d = H * HD;
   int qt, h, b;
@@ -56,18 +56,23 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) zero(o[t]);
   float m = -INFINITY, l = 0.f;
+  TrOff tv;
+  tv.init(lane);
+  uint32_t offK[2];
+#pragma unroll
+  for (int js = 0; js < 2; ++js) offK[js] = offN(js * 32 + (lane & 31), hh);   // chunk 2 ks + hh: ^ 32 ks
 
   const int ntiles = (q0 + 128) / 64;
-  u32x4 reg[8];
-  // threads 0-127 stage V^T, threads 128-255 stage K
+  u32x4 rk[4], rv[4];
+  // next key tile into registers while this one is used; stored after
   auto gl = [&](int jt) {
     const int64_t j0 = (int64_t)jt * 64;
-    if (tid < 128) load_tr64(vb + j0 * ld, ld, tid, reg);
-    else load_nat64<128>(kb + j0 * ld, ld, tid - 128, reg);
+    load_nat64<256>(kb + j0 * ld, ld, tid, rk);
+    load_nat64<256>(vb + j0 * ld, ld, tid, rv);
   };
   auto st = [&](int stage) {
-    if (tid < 128) store_tr64(smem[stage] + 16384, tid, reg);
-    else store_nat64<128>(smem[stage], tid - 128, reg);
+    store_nat64<256>(smem[stage], tid, rk);
+    store_nat64<256>(smem[stage] + 16384, tid, rv);
   };
   gl(0);
   st(0);
@@ -87,7 +92,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
       for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
         for (int js = 0; js < 2; ++js) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + off256(js * 32 + (lane & 31), 2 * ks + hh));
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (offK[js] ^ (32u * ks)));
           s[js] = mfma(kf, qf[ks], s[js]);
         }
       // running max over raw scores (the positive scale preserves order);
@@ -131,7 +136,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
         const bf16x8 pf = pack8(s[sp >> 1], 8 * (sp & 1));
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + off128(t * 32 + (lane & 31), 2 * sp + hh));
+          const bf16x8 vf = frag_tr(sV, tv.l(t, sp), tv.h(t, sp));
           o[t] = mfma(vf, pf, o[t]);
         }
       }
@@ -181,10 +186,11 @@ __device__ inline void store_rows(floatx16 (&acc)[4], float scale, bf16* dst_row
 // ===========================================================================
 // backward: dQ (one wave = 32 query rows, walking key tiles up to the
 // diagonal).  It also forms delta_i = sum_d dO[i,d] O[i,d] from the rows it
-// holds and stores it for the dK kernel.
+// holds and stores it for the dK kernel.  K and V tiles are double-buffered:
+// the next tile's loads are in flight while this one is used.
 // ===========================================================================
 __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
-  __shared__ __attribute__((aligned(16))) char smem[3 * 16384];  // K image | V image | K^T image
+  __shared__ __attribute__((aligned(16))) char smem[2][32768];   // per stage: K image | V image
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int T = a.T, H = a.H, d = H * HD;
   int qt, h, b;
@@ -199,6 +205,13 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
   const int64_t tok = (int64_t)b * T + my_i;
   const bf16* dob = (const bf16*)a.dout + tok * d + h * HD;
   const bf16* ob = (const bf16*)a.o + tok * d + h * HD;
+
+  const int ntiles = (q0 + 128) / 64;
+  // one staging register set, used for the K then the V image of a tile
+  u32x4 rg[4];
+  auto gl = [&](const bf16* src, int jt) { load_nat64<256>(src + (int64_t)jt * 64 * ld, ld, tid, rg); };
+  auto st = [&](char* img) { store_nat64<256>(img, tid, rg); };
+  gl(kb, 0);
 
   bf16x8 qf[8], dof[8];
   float Dl = 0.f;
@@ -218,38 +231,41 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
   floatx16 dq[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) zero(dq[t]);
+  TrOff tk;
+  tk.init(lane);
+  uint32_t offR[2];
+#pragma unroll
+  for (int js = 0; js < 2; ++js) offR[js] = offN(js * 32 + (lane & 31), hh);   // chunk 2 ks + hh: ^ 32 ks
 
-  const int ntiles = (q0 + 128) / 64;
-  char* sK = smem;
-  char* sV = smem + 16384;
-  char* sKT = smem + 32768;
+  st(smem[0]);
+  gl(vb, 0);
+  st(smem[0] + 16384);
+  __syncthreads();
+  // The next tile is staged in two halves, each loaded before and written
+  // after half of this tile's work: K(jt+1) around keys 0-31, V(jt+1)
+  // around keys 32-63.
   for (int jt = 0; jt < ntiles; ++jt) {
-    const int64_t j0 = (int64_t)jt * 64;
-    {
-      u32x4 r[8];
-      if (tid < 128) {
-        load_tr64(kb + j0 * ld, ld, tid, r);
-        store_tr64(sKT, tid, r);
-      } else {
-        load_nat64<128>(kb + j0 * ld, ld, tid - 128, r);
-        store_nat64<128>(sK, tid - 128, r);
-        load_nat64<128>(vb + j0 * ld, ld, tid - 128, r);
-        store_nat64<128>(sV, tid - 128, r);
-      }
-    }
-    __syncthreads();
+    const bool more = jt + 1 < ntiles;
+    char* nx = smem[(jt + 1) & 1];
+    if (more) gl(kb, jt + 1);
+    const int j0 = jt * 64;
+    const char* sK = smem[jt & 1];
+    const char* sV = sK + 16384;
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
-      const int jh = (int)j0 + js * 32;
+      if (js == 1 && more) {
+        st(nx);
+        gl(vb, jt + 1);
+      }
+      const int jh = j0 + js * 32;
       if (jh > i0 + 31) continue;                 // all 32 keys above the diagonal
       floatx16 s, dp;
       zero(s);
       zero(dp);
-      const int row = js * 32 + (lane & 31);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + off256(row, 2 * ks + hh));
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + off256(row, 2 * ks + hh));
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (offR[js] ^ (32u * ks)));
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + (offR[js] ^ (32u * ks)));
         s = mfma(kf, qf[ks], s);
         dp = mfma(vf, dof[ks], dp);
       }
@@ -263,14 +279,15 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
         const bf16x8 df = pack8(s, 8 * gp);
-        const int sp = js * 2 + gp;
+        const uint32_t sp = js * 2 + gp;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sKT + off128(t * 32 + (lane & 31), 2 * sp + hh));
+          const bf16x8 kf = frag_tr(sK, tk.l(t, sp), tk.h(t, sp));
           dq[t] = mfma(kf, df, dq[t]);
         }
       }
     }
+    if (more) st(nx + 16384);
     __syncthreads();
   }
   bf16* dst = (bf16*)a.dqkv + tok * ld + h * HD;
@@ -281,12 +298,13 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
 // backward: dK and dV, one wave = 32 keys walking the query tiles from the
 // diagonal.  Two kernels (dV needs P only; dK needs dS): each keeps its
 // accumulators and key-side operands in registers at two waves per SIMD.
+// Q and dO tiles (with their log-sum-exp and delta values) are
+// double-buffered like the key tiles of the dQ kernel.
 // ===========================================================================
 template <bool DK>
 __global__ void __launch_bounds__(256, 2) k_attn_dkv(AttnDesc a) {
-  // Q image | (dO image) | Q^T or dO^T image | lse2[64] | delta[64]
-  constexpr int NIMG = DK ? 3 : 2;
-  __shared__ __attribute__((aligned(16))) char smem[NIMG * 16384 + 512];
+  constexpr int SST = 32768 + 512;               // per stage: Q image | dO image | lse2[64] | delta[64]
+  __shared__ __attribute__((aligned(16))) char smem[2 * SST];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
   const int T = a.T, H = a.H, d = H * HD;
   int kt, h, b;
@@ -298,6 +316,26 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkv(AttnDesc a) {
   const bf16* vb = rows + 2 * d + h * HD;
   const bf16* dob = (const bf16*)a.dout + (int64_t)b * T * d + h * HD;
   const int jb = kt * 128, jw = jb + wave * 32, my_j = jw + (lane & 31);
+  const float* lse_bh = a.lse + ((int64_t)b * H + h) * T;
+  const float* del_bh = a.delta + ((int64_t)b * H + h) * T;
+
+  // one staging register set, used for the Q then the dO image of a tile
+  u32x4 rg[4];
+  float rs = 0.f;                                // lse2 (threads 0-63) or delta (64-127) of one query
+  auto glq = [&](int qt) {
+    const int64_t i0 = (int64_t)qt * 64;
+    load_nat64<256>(qb + i0 * ld, ld, tid, rg);
+    if (tid < 64) rs = lse_bh[i0 + tid] * kLog2e;
+    else if (DK && tid < 128) rs = del_bh[i0 + tid - 64];
+  };
+  auto stq = [&](char* base) {
+    store_nat64<256>(base, tid, rg);
+    if (tid < (DK ? 128 : 64)) reinterpret_cast<float*>(base + 32768)[tid] = rs;
+  };
+  auto glo = [&](int qt) { load_nat64<256>(dob + (int64_t)qt * 64 * d, d, tid, rg); };
+  auto sto = [&](char* base) { store_nat64<256>(base + 16384, tid, rg); };
+  const int qt0 = jb / 64, nq = T / 64;
+  glq(qt0);
 
   bf16x8 kf[8], vf[8];
 #pragma unroll
@@ -308,49 +346,46 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkv(AttnDesc a) {
   floatx16 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) zero(acc[t]);
-  char* sQ = smem;
-  char* sO = smem + 16384;                       // dK only
-  char* sT = smem + (NIMG - 1) * 16384;          // Q^T (dK) or dO^T (dV)
-  float* sL = reinterpret_cast<float*>(smem + NIMG * 16384);
-  float* sD = sL + 64;
-  const float* lse_bh = a.lse + ((int64_t)b * H + h) * T;
-  const float* del_bh = a.delta + ((int64_t)b * H + h) * T;
+  TrOff tt;
+  tt.init(lane);
+  uint32_t offR[2];
+#pragma unroll
+  for (int is = 0; is < 2; ++is) offR[is] = offN(is * 32 + (lane & 31), hh);   // chunk 2 ks + hh: ^ 32 ks
 
-  for (int qt = jb / 64; qt < T / 64; ++qt) {
-    const int64_t i0 = (int64_t)qt * 64;
-    {
-      u32x4 r[8];
-      if (tid < 128) {
-        if (DK) load_tr64(qb + i0 * ld, ld, tid, r);
-        else load_tr64(dob + i0 * d, d, tid, r);
-        store_tr64(sT, tid, r);
-        if (tid < 64) sL[tid] = lse_bh[i0 + tid] * kLog2e;
-        else if (DK) sD[tid - 64] = del_bh[i0 + tid - 64];
-      } else {
-        load_nat64<128>(qb + i0 * ld, ld, tid - 128, r);
-        store_nat64<128>(sQ, tid - 128, r);
-        if (DK) {
-          load_nat64<128>(dob + i0 * d, d, tid - 128, r);
-          store_nat64<128>(sO, tid - 128, r);
-        }
-      }
-    }
-    __syncthreads();
+  stq(smem);
+  glo(qt0);
+  sto(smem);
+  __syncthreads();
+  // The next tile is staged in two halves around the two 32-query halves of
+  // this one: Q (with lse / delta), then dO.
+  for (int qt = qt0; qt < nq; ++qt) {
+    const bool more = qt + 1 < nq;
+    char* nx = smem + ((qt + 1 - qt0) & 1) * SST;
+    if (more) glq(qt + 1);
+    const int i0 = qt * 64;
+    const char* sQ = smem + ((qt - qt0) & 1) * SST;
+    const char* sO = sQ + 16384;
+    const float* sL = reinterpret_cast<const float*>(sQ + 32768);
+    const float* sD = sL + 64;
+    const char* sT = DK ? sQ : sO;               // Q^T (dK) or dO^T (dV), read transposed
 #pragma unroll
     for (int is = 0; is < 2; ++is) {
-      const int ih = (int)i0 + is * 32;
+      if (is == 1 && more) {
+        stq(nx);
+        glo(qt + 1);
+      }
+      const int ih = i0 + is * 32;
       if (ih + 31 < jw) continue;                 // all 32 queries before the wave's keys
       const bool diag = ih < jw + 31;
       floatx16 s, dp;
       zero(s);
       if (DK) zero(dp);
-      const int row = is * 32 + (lane & 31);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sQ + off256(row, 2 * ks + hh));
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sQ + (offR[is] ^ (32u * ks)));
         s = mfma(qa, kf[ks], s);
         if (DK) {
-          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(sO + off256(row, 2 * ks + hh));
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(sO + (offR[is] ^ (32u * ks)));
           dp = mfma(oa, vf[ks], dp);
         }
       }
@@ -369,21 +404,22 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkv(AttnDesc a) {
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           float p = __builtin_amdgcn_exp2f(s[r] * kScaleLog2 - Ls[e]);
-          if (diag && (int)i0 + il + e < my_j) p = 0.f;
+          if (diag && i0 + il + e < my_j) p = 0.f;
           s[r] = DK ? p * (dp[r] - Ds[e]) : p;     // dS or P
         }
       }
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
-        const int sp = is * 2 + gp;
+        const uint32_t sp = is * 2 + gp;
         const bf16x8 bfr = pack8(s, 8 * gp);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const bf16x8 at = *reinterpret_cast<const bf16x8*>(sT + off128(t * 32 + (lane & 31), 2 * sp + hh));
+          const bf16x8 at = frag_tr(sT, tt.l(t, sp), tt.h(t, sp));
           acc[t] = mfma(at, bfr, acc[t]);
         }
       }
     }
+    if (more) sto(nx);
     __syncthreads();
   }
   bf16* dst = (bf16*)a.dqkv + ((int64_t)b * T + my_j) * ld + h * HD;
