@@ -120,8 +120,10 @@ Plan make_plan(const nc_config& c) {
     p.ztgt = take(N * 4);
     p.head_nblk = (int)(V / tile_n(c, (int)std::min<int64_t>(N, 1 << 30), (int)V));
     p.lse_part = take((size_t)N * p.head_nblk * 8);
-    // token chunks for the head's backward: whole rows, about 16k tokens
-    const int64_t rows = std::max<int64_t>(1, std::min<int64_t>(c.batch, 16384 / c.seq_len));
+    // token chunks for the head's backward: whole rows, up to 64k tokens
+    // (the d20 batch in one piece: the products over the chunk then fill
+    // whole waves of tiles; dz takes 2 bytes per token and vocabulary entry)
+    const int64_t rows = std::max<int64_t>(1, std::min<int64_t>(c.batch, 65536 / c.seq_len));
     p.head_chunk = rows * c.seq_len;
     p.dz = take((size_t)p.head_chunk * V * es);
     need((int)V, (int)d, p.head_chunk);
