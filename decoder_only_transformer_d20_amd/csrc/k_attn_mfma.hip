@@ -295,17 +295,25 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
 }
 
 // ===========================================================================
-// backward: dK and dV, one wave = 32 keys walking the query tiles from the
-// diagonal.  Two kernels (dV needs P only; dK needs dS): each keeps its
-// accumulators and key-side operands in registers at two waves per SIMD.
+// backward: dK and dV.  A block owns 128 keys and has 8 waves in 4 pairs;
+// the two waves of pair w (w and w + 4, on the same SIMD) own keys
+// jb + 32w .. +31 and walk the query tiles from the diagonal, splitting the
+// work of each 32-query half:
+//   wave w     (P role): S = Q K^T, P = exp(S - lse) -> LDS, dV += P^T dO
+//   wave w + 4 (D role): dP = dO V^T, then (after the barrier) reads P,
+//                        dS = P (dP - delta), dK += dS^T Q
+// Each wave issues 32 MFMAs per half and P's exponentials are formed once.
 // Q and dO tiles (with their log-sum-exp and delta values) are
-// double-buffered like the key tiles of the dQ kernel.
+// double-buffered: the next tile's loads are in flight during this one.
 // ===========================================================================
-template <bool DK>
-__global__ void __launch_bounds__(256, 2) k_attn_dkv(AttnDesc a) {
+__global__ void __launch_bounds__(512, 1) k_attn_dkdv(AttnDesc a) {
   constexpr int SST = 32768 + 512;               // per stage: Q image | dO image | lse2[64] | delta[64]
-  __shared__ __attribute__((aligned(16))) char smem[2 * SST];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  constexpr int PX = 4096;                       // one pair's P for one half: [4][64 lanes][4 floats]
+  __shared__ __attribute__((aligned(16))) char smem[2 * SST + 8 * PX];
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave & 3;
+  const bool roleP = wave < 4;
   const int T = a.T, H = a.H, d = H * HD;
   int kt, h, b;
   tile_order(T / 128, H, a.B, kt, h, b);                         // low key tiles do the most work
@@ -315,35 +323,35 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkv(AttnDesc a) {
   const bf16* kb = rows + d + h * HD;
   const bf16* vb = rows + 2 * d + h * HD;
   const bf16* dob = (const bf16*)a.dout + (int64_t)b * T * d + h * HD;
-  const int jb = kt * 128, jw = jb + wave * 32, my_j = jw + (lane & 31);
+  const int jb = kt * 128, jw = jb + pair * 32, my_j = jw + (lane & 31);
   const float* lse_bh = a.lse + ((int64_t)b * H + h) * T;
   const float* del_bh = a.delta + ((int64_t)b * H + h) * T;
 
-  // one staging register set, used for the Q then the dO image of a tile
-  u32x4 rg[4];
+  u32x4 rq[2], ro[2];
   float rs = 0.f;                                // lse2 (threads 0-63) or delta (64-127) of one query
-  auto glq = [&](int qt) {
+  auto gl = [&](int qt) {
     const int64_t i0 = (int64_t)qt * 64;
-    load_nat64<256>(qb + i0 * ld, ld, tid, rg);
+    load_nat64<512>(qb + i0 * ld, ld, tid, rq);
+    load_nat64<512>(dob + i0 * d, d, tid, ro);
     if (tid < 64) rs = lse_bh[i0 + tid] * kLog2e;
-    else if (DK && tid < 128) rs = del_bh[i0 + tid - 64];
+    else if (tid < 128) rs = del_bh[i0 + tid - 64];
   };
-  auto stq = [&](char* base) {
-    store_nat64<256>(base, tid, rg);
-    if (tid < (DK ? 128 : 64)) reinterpret_cast<float*>(base + 32768)[tid] = rs;
+  auto st = [&](char* base) {
+    store_nat64<512>(base, tid, rq);
+    store_nat64<512>(base + 16384, tid, ro);
+    if (tid < 128) reinterpret_cast<float*>(base + 32768)[tid] = rs;
   };
-  auto glo = [&](int qt) { load_nat64<256>(dob + (int64_t)qt * 64 * d, d, tid, rg); };
-  auto sto = [&](char* base) { store_nat64<256>(base + 16384, tid, rg); };
   const int qt0 = jb / 64, nq = T / 64;
-  glq(qt0);
+  gl(qt0);
 
-  bf16x8 kf[8], vf[8];
+  // key-side operand: K rows (P role) or V rows (D role) of the pair's keys
+  bf16x8 kv[8];
+  {
+    const bf16* src = (roleP ? kb : vb) + (int64_t)my_j * ld + 8 * hh;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    kf[s] = as_bf16x8(gload(kb + (int64_t)my_j * ld + 16 * s + 8 * hh));
-    if (DK) vf[s] = as_bf16x8(gload(vb + (int64_t)my_j * ld + 16 * s + 8 * hh));
+    for (int s = 0; s < 8; ++s) kv[s] = as_bf16x8(gload(src + 16 * s));
   }
-  floatx16 acc[4];
+  floatx16 acc[4];                               // dV (P role) or dK (D role)
 #pragma unroll
   for (int t = 0; t < 4; ++t) zero(acc[t]);
   TrOff tt;
@@ -351,80 +359,86 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkv(AttnDesc a) {
   uint32_t offR[2];
 #pragma unroll
   for (int is = 0; is < 2; ++is) offR[is] = offN(is * 32 + (lane & 31), hh);   // chunk 2 ks + hh: ^ 32 ks
+  float* pxb = reinterpret_cast<float*>(smem + 2 * SST) + pair * 2 * (PX / 4);
 
-  stq(smem);
-  glo(qt0);
-  sto(smem);
+  st(smem);
   __syncthreads();
-  // The next tile is staged in two halves around the two 32-query halves of
-  // this one: Q (with lse / delta), then dO.
   for (int qt = qt0; qt < nq; ++qt) {
     const bool more = qt + 1 < nq;
-    char* nx = smem + ((qt + 1 - qt0) & 1) * SST;
-    if (more) glq(qt + 1);
+    if (more) gl(qt + 1);
     const int i0 = qt * 64;
     const char* sQ = smem + ((qt - qt0) & 1) * SST;
     const char* sO = sQ + 16384;
     const float* sL = reinterpret_cast<const float*>(sQ + 32768);
     const float* sD = sL + 64;
-    const char* sT = DK ? sQ : sO;               // Q^T (dK) or dO^T (dV), read transposed
 #pragma unroll
     for (int is = 0; is < 2; ++is) {
-      if (is == 1 && more) {
-        stq(nx);
-        glo(qt + 1);
-      }
       const int ih = i0 + is * 32;
-      if (ih + 31 < jw) continue;                 // all 32 queries before the wave's keys
+      const bool live = ih + 31 >= jw;            // some query of the half sees the pair's keys
       const bool diag = ih < jw + 31;
-      floatx16 s, dp;
-      zero(s);
-      if (DK) zero(dp);
+      float* px = pxb + is * (PX / 4);
+      // phase 1: S and P (P role) / dP (D role); lane = key j, register r =
+      // query ih + 8(r/4) + 4hh + r%4
+      floatx16 x;
+      zero(x);
+      if (live) {
+        const char* img = roleP ? sQ : sO;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(sQ + (offR[is] ^ (32u * ks)));
-        s = mfma(qa, kf[ks], s);
-        if (DK) {
-          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(sO + (offR[is] ^ (32u * ks)));
-          dp = mfma(oa, vf[ks], dp);
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 fa = *reinterpret_cast<const bf16x8*>(img + (offR[is] ^ (32u * ks)));
+          x = mfma(fa, kv[ks], x);
+        }
+        if (roleP) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int il = is * 32 + 8 * g + 4 * hh;
+            const float4 L = *reinterpret_cast<const float4*>(sL + il);
+            const float Ls[4] = {L.x, L.y, L.z, L.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * g + e;
+              float p = __builtin_amdgcn_exp2f(x[r] * kScaleLog2 - Ls[e]);
+              if (diag && i0 + il + e < my_j) p = 0.f;
+              x[r] = p;
+            }
+            *reinterpret_cast<float4*>(px + (g * 64 + lane) * 4) = make_float4(x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]);
+          }
         }
       }
-      // lane = key j, register r = query ih + 8(r/4) + 4hh + r%4
+      __syncthreads();                            // P of this half visible to the D role
+      if (live) {
+        if (!roleP) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int il = is * 32 + 8 * g + 4 * hh;
-        const float4 L = *reinterpret_cast<const float4*>(sL + il);
-        const float Ls[4] = {L.x, L.y, L.z, L.w};
-        float Ds[4] = {0.f, 0.f, 0.f, 0.f};
-        if (DK) {
-          const float4 Dv = *reinterpret_cast<const float4*>(sD + il);
-          Ds[0] = Dv.x; Ds[1] = Dv.y; Ds[2] = Dv.z; Ds[3] = Dv.w;
+          for (int g = 0; g < 4; ++g) {
+            const int il = is * 32 + 8 * g + 4 * hh;
+            const float4 Dv = *reinterpret_cast<const float4*>(sD + il);
+            const float4 P = *reinterpret_cast<const float4*>(px + (g * 64 + lane) * 4);
+            x[4 * g + 0] = P.x * (x[4 * g + 0] - Dv.x);
+            x[4 * g + 1] = P.y * (x[4 * g + 1] - Dv.y);
+            x[4 * g + 2] = P.z * (x[4 * g + 2] - Dv.z);
+            x[4 * g + 3] = P.w * (x[4 * g + 3] - Dv.w);
+          }
         }
+        // phase 2: dV += P^T dO (P role) / dK += dS^T Q (D role)
+        const char* sT = roleP ? sO : sQ;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float p = __builtin_amdgcn_exp2f(s[r] * kScaleLog2 - Ls[e]);
-          if (diag && i0 + il + e < my_j) p = 0.f;
-          s[r] = DK ? p * (dp[r] - Ds[e]) : p;     // dS or P
-        }
-      }
+        for (int gp = 0; gp < 2; ++gp) {
+          const uint32_t sp = is * 2 + gp;
+          const bf16x8 bfr = pack8(x, 8 * gp);
 #pragma unroll
-      for (int gp = 0; gp < 2; ++gp) {
-        const uint32_t sp = is * 2 + gp;
-        const bf16x8 bfr = pack8(s, 8 * gp);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x8 at = frag_tr(sT, tt.l(t, sp), tt.h(t, sp));
-          acc[t] = mfma(at, bfr, acc[t]);
+          for (int t = 0; t < 4; ++t) {
+            const bf16x8 at = frag_tr(sT, tt.l(t, sp), tt.h(t, sp));
+            acc[t] = mfma(at, bfr, acc[t]);
+          }
         }
       }
     }
-    if (more) sto(nx);
+    if (more) st(smem + ((qt + 1 - qt0) & 1) * SST);
     __syncthreads();
   }
   bf16* dst = (bf16*)a.dqkv + ((int64_t)b * T + my_j) * ld + h * HD;
-  if (DK) store_rows(acc, 0.08838834764831845f, dst + d, a.rope ? a.rope + (int64_t)my_j * (HD / 2) : nullptr, hh);
-  else store_rows(acc, 1.f, dst + 2 * d, nullptr, hh);
+  if (roleP) store_rows(acc, 1.f, dst + 2 * d, nullptr, hh);
+  else store_rows(acc, 0.08838834764831845f, dst + d, a.rope ? a.rope + (int64_t)my_j * (HD / 2) : nullptr, hh);
 }
 
 }  // namespace
@@ -443,9 +457,7 @@ hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s) {
   k_attn_dq<<<grid, 256, 0, s>>>(a);             // also writes delta
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_attn_dkv<true><<<grid, 256, 0, s>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_attn_dkv<false><<<grid, 256, 0, s>>>(a);
+  k_attn_dkdv<<<grid, 512, 0, s>>>(a);
   return hipGetLastError();
 }
 
