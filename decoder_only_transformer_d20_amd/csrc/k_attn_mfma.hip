@@ -9,6 +9,8 @@
 // result does not depend on scheduling.  dQ and dK leave through the
 // inverse rotary rotation, so the caller receives gradients with respect to
 // the pre-rotation q and k.
+#include <type_traits>
+
 #include "attn_mfma.h"
 
 namespace nc {
@@ -297,14 +299,17 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
 // ===========================================================================
 // backward: dK and dV.  A block owns 128 keys and has 8 waves in 4 pairs;
 // the two waves of pair w (w and w + 4, on the same SIMD) own keys
-// jb + 32w .. +31 and walk the query tiles from the diagonal, splitting the
-// work of each 32-query half:
+// jb + 32w .. +31 and walk the 32-query halves of the query tiles from the
+// diagonal, splitting the work:
 //   wave w     (P role): S = Q K^T, P = exp(S - lse) -> LDS, dV += P^T dO
-//   wave w + 4 (D role): dP = dO V^T, then (after the barrier) reads P,
-//                        dS = P (dP - delta), dK += dS^T Q
-// Each wave issues 32 MFMAs per half and P's exponentials are formed once.
-// Q and dO tiles (with their log-sum-exp and delta values) are
-// double-buffered: the next tile's loads are in flight during this one.
+//   wave w + 4 (D role): dP = dO V^T; one half later, with that half's P
+//                        from LDS, dS = P (dP - delta), dK += dS^T Q
+// The D role lags one half so that, between two barriers, the two waves'
+// work is independent and interleaves on their SIMD; each issues 32 MFMAs
+// per half and P's exponentials are formed once.  Q and dO tiles (with
+// their log-sum-exp and delta values) are double-buffered: the next tile's
+// loads are in flight during this one, and a stage is rewritten only after
+// the lagging role's last use of it.
 // ===========================================================================
 __global__ void __launch_bounds__(512, 1) k_attn_dkdv(AttnDesc a) {
   constexpr int SST = 32768 + 512;               // per stage: Q image | dO image | lse2[64] | delta[64]
@@ -361,81 +366,110 @@ __global__ void __launch_bounds__(512, 1) k_attn_dkdv(AttnDesc a) {
   for (int is = 0; is < 2; ++is) offR[is] = offN(is * 32 + (lane & 31), hh);   // chunk 2 ks + hh: ^ 32 ks
   float* pxb = reinterpret_cast<float*>(smem + 2 * SST) + pair * 2 * (PX / 4);
 
+  // phase 2 of a half: acc += X^T x with X^T read transposed from img (Q^T
+  // for dK, dO^T for dV) at the half's slot pairs
+  auto accumulate = [&](floatx16& x, const char* img, int is) {
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      const uint32_t sp = is * 2 + gp;
+      const bf16x8 bfr = pack8(x, 8 * gp);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = mfma(frag_tr(img, tt.l(t, sp), tt.h(t, sp)), bfr, acc[t]);
+    }
+  };
+  // D role, lagging half: dS = P (dP - delta), dK += dS^T Q
+  floatx16 dpp;                                  // dP of the pending half
+  zero(dpp);
+  bool pend = false;                             // a half waits for its dS / dK
+  const char* pQ = smem;                         // that half's stage
+  int pis = 0, pk = 0;
+  auto finish_d = [&]() {
+    const float* px = pxb + (pk & 1) * (PX / 4);
+    const float* sD = reinterpret_cast<const float*>(pQ + 32768) + 64;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int il = pis * 32 + 8 * g + 4 * hh;
+      const float4 Dv = *reinterpret_cast<const float4*>(sD + il);
+      const float4 P = *reinterpret_cast<const float4*>(px + (g * 64 + lane) * 4);
+      dpp[4 * g + 0] = P.x * (dpp[4 * g + 0] - Dv.x);
+      dpp[4 * g + 1] = P.y * (dpp[4 * g + 1] - Dv.y);
+      dpp[4 * g + 2] = P.z * (dpp[4 * g + 2] - Dv.z);
+      dpp[4 * g + 3] = P.w * (dpp[4 * g + 3] - Dv.w);
+    }
+    accumulate(dpp, pQ, pis);
+  };
+
   st(smem);
   __syncthreads();
-  for (int qt = qt0; qt < nq; ++qt) {
-    const bool more = qt + 1 < nq;
-    if (more) gl(qt + 1);
-    const int i0 = qt * 64;
-    const char* sQ = smem + ((qt - qt0) & 1) * SST;
-    const char* sO = sQ + 16384;
-    const float* sL = reinterpret_cast<const float*>(sQ + 32768);
-    const float* sD = sL + 64;
+  // One loop per role (the roles branch on a wave-uniform value; both
+  // loops pass the same barriers).
+  auto run = [&](auto role) {
+    constexpr bool kP = decltype(role)::value;
+    int k = 0;                                   // half counter: P of half k goes to buffer k & 1
+    for (int qt = qt0; qt < nq; ++qt) {
+      const bool more = qt + 1 < nq;
+      if (more) gl(qt + 1);
+      const int i0 = qt * 64;
+      const char* sQ = smem + ((qt - qt0) & 1) * SST;
+      const char* sO = sQ + 16384;
+      const float* sL = reinterpret_cast<const float*>(sQ + 32768);
 #pragma unroll
-    for (int is = 0; is < 2; ++is) {
-      const int ih = i0 + is * 32;
-      const bool live = ih + 31 >= jw;            // some query of the half sees the pair's keys
-      const bool diag = ih < jw + 31;
-      float* px = pxb + is * (PX / 4);
-      // phase 1: S and P (P role) / dP (D role); lane = key j, register r =
-      // query ih + 8(r/4) + 4hh + r%4
-      floatx16 x;
-      zero(x);
-      if (live) {
-        const char* img = roleP ? sQ : sO;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 fa = *reinterpret_cast<const bf16x8*>(img + (offR[is] ^ (32u * ks)));
-          x = mfma(fa, kv[ks], x);
+      for (int is = 0; is < 2; ++is, ++k) {
+        const int ih = i0 + is * 32;
+        const bool live = ih + 31 >= jw;          // some query of the half sees the pair's keys
+        const bool diag = ih < jw + 31;
+        if constexpr (!kP) {
+          if (pend) finish_d();
         }
-        if (roleP) {
+        // lane = key j, register r = query ih + 8(r/4) + 4hh + r%4
+        floatx16 x;
+        zero(x);
+        if (live) {
+          const char* img = kP ? sQ : sO;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int il = is * 32 + 8 * g + 4 * hh;
-            const float4 L = *reinterpret_cast<const float4*>(sL + il);
-            const float Ls[4] = {L.x, L.y, L.z, L.w};
+          for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 fa = *reinterpret_cast<const bf16x8*>(img + (offR[is] ^ (32u * ks)));
+            x = mfma(fa, kv[ks], x);
+          }
+        }
+        if constexpr (kP) {
+          if (live) {
+            float* px = pxb + (k & 1) * (PX / 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * g + e;
-              float p = __builtin_amdgcn_exp2f(x[r] * kScaleLog2 - Ls[e]);
-              if (diag && i0 + il + e < my_j) p = 0.f;
-              x[r] = p;
+            for (int g = 0; g < 4; ++g) {
+              const int il = is * 32 + 8 * g + 4 * hh;
+              const float4 L = *reinterpret_cast<const float4*>(sL + il);
+              const float Ls[4] = {L.x, L.y, L.z, L.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * g + e;
+                float p = __builtin_amdgcn_exp2f(x[r] * kScaleLog2 - Ls[e]);
+                if (diag && i0 + il + e < my_j) p = 0.f;
+                x[r] = p;
+              }
+              *reinterpret_cast<float4*>(px + (g * 64 + lane) * 4) =
+                  make_float4(x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]);
             }
-            *reinterpret_cast<float4*>(px + (g * 64 + lane) * 4) = make_float4(x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]);
+            accumulate(x, sO, is);                // dV += P^T dO
           }
+        } else {
+          dpp = x;
+          pend = live;
+          pQ = sQ;
+          pis = is;
+          pk = k;
         }
-      }
-      __syncthreads();                            // P of this half visible to the D role
-      if (live) {
-        if (!roleP) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int il = is * 32 + 8 * g + 4 * hh;
-            const float4 Dv = *reinterpret_cast<const float4*>(sD + il);
-            const float4 P = *reinterpret_cast<const float4*>(px + (g * 64 + lane) * 4);
-            x[4 * g + 0] = P.x * (x[4 * g + 0] - Dv.x);
-            x[4 * g + 1] = P.y * (x[4 * g + 1] - Dv.y);
-            x[4 * g + 2] = P.z * (x[4 * g + 2] - Dv.z);
-            x[4 * g + 3] = P.w * (x[4 * g + 3] - Dv.w);
-          }
-        }
-        // phase 2: dV += P^T dO (P role) / dK += dS^T Q (D role)
-        const char* sT = roleP ? sO : sQ;
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          const uint32_t sp = is * 2 + gp;
-          const bf16x8 bfr = pack8(x, 8 * gp);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const bf16x8 at = frag_tr(sT, tt.l(t, sp), tt.h(t, sp));
-            acc[t] = mfma(at, bfr, acc[t]);
-          }
-        }
+        // P of this half visible to the D role from here on; with is = 1,
+        // the staged next tile is written first (its stage last served the
+        // previous tile, whose pending half the D role finished above)
+        if (is == 1 && more) st(smem + ((qt + 1 - qt0) & 1) * SST);
+        __syncthreads();
       }
     }
-    if (more) st(smem + ((qt + 1 - qt0) & 1) * SST);
-    __syncthreads();
-  }
+  };
+  if (roleP) run(std::true_type{});
+  else run(std::false_type{});
+  if (!roleP && pend) finish_d();
   bf16* dst = (bf16*)a.dqkv + ((int64_t)b * T + my_j) * ld + h * HD;
   if (roleP) store_rows(acc, 1.f, dst + 2 * d, nullptr, hh);
   else store_rows(acc, 0.08838834764831845f, dst + d, a.rope ? a.rope + (int64_t)my_j * (HD / 2) : nullptr, hh);
