@@ -112,27 +112,32 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[js][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * kScaleLog2;
-      const float mn = fmaxf(m, mx);
-      float ls = 0.f;
-#pragma unroll
-      for (int js = 0; js < 2; ++js)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[js][r], kScaleLog2, -mn));
-          s[js][r] = p;
-          ls += p;
-        }
-      // rescale the running sums only when some row's maximum moved
-      if (__any(mn > m)) {
+      // m is the reference (log2-scaled) the exponentials are taken
+      // against.  It follows the running maximum lazily: only when some
+      // row's maximum passes it by more than kLazy is it raised (and the
+      // running sums rescaled), so p <= 2^kLazy -- harmless in fp32 sums
+      // and bf16 operands -- and most tiles skip the rescale.
+      constexpr float kLazy = 8.f;
+      if (__any(mx > m + kLazy)) {
+        const float mn = fmaxf(m, mx);
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
         l *= alpha;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        m = mn;
       }
+      float ls = 0.f;
+#pragma unroll
+      for (int js = 0; js < 2; ++js)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[js][r], kScaleLog2, -m));
+          s[js][r] = p;
+          ls += p;
+        }
       l += ls;
-      m = mn;
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
         const bf16x8 pf = pack8(s[sp >> 1], 8 * (sp & 1));
