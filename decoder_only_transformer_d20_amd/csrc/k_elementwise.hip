@@ -61,22 +61,224 @@ __global__ void __launch_bounds__(256) k_embed_fwd(const T* __restrict__ E, cons
   for (int c = lane; c < chunks; c += kWave) t[c] = s[c];
 }
 
-// dE[idx[n], :] += g[n, :]  (fp32 hardware atomics; the order of the adds
-// into one row is not fixed, so low bits may vary between runs)
-template <typename T>
-__global__ void __launch_bounds__(256) k_embed_bwd(const T* __restrict__ g, const int32_t* __restrict__ idx,
-                                                   float* __restrict__ dE, int64_t n, int d) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= n) return;
-  float* dst = dE + (int64_t)idx[row] * d;
-  const T* src = g + row * d;
-  constexpr int VN = Vec<T>::n;
-  for (int c = lane; c < d / VN; c += kWave) {
-    Vec<T> v = ld16(src + c * VN);
-#pragma unroll
-    for (int i = 0; i < VN; ++i) unsafeAtomicAdd(dst + c * VN + i, to_f32(v.v[i]));
+// ---------------------------------------------------------------------------
+// Embedding backward, deterministic: dE[v] (+)= sum of g[p] over the
+// positions p with idx[p] = v, summed in increasing p.
+//  1. stable LSD radix sort of (id, position) by id, 8-bit digits: per
+//     pass a block histogram, one exclusive scan over (digit, block), and a
+//     stable scatter (ranks within a wave from ballots over the digit bits,
+//     across waves from per-wave digit counts).  Ids outside [0, V) sort as
+//     V and are dropped.
+//  2. the sorted rows in tiles of 32, one wave each, summed segment by
+//     segment in order; a segment wholly inside a tile is written to dE,
+//     one that crosses a tile boundary leaves its piece in the tile's
+//     "first" (continued from the previous tile) or "last" (continuing)
+//     partial row.
+//  3. one wave per segment that starts in a tile and continues: its pieces,
+//     added in tile order, go to dE.
+// No float atomics, so the result is bitwise reproducible.
+// ---------------------------------------------------------------------------
+constexpr int kSortBlock = 1024;
+constexpr int kEmbTile = 32;
+
+__device__ inline int sort_key(const int32_t* kin, int64_t p, int V, bool first) {
+  const int k = kin[p];
+  return first ? ((k >= 0 && k < V) ? k : V) : k;
+}
+
+__global__ void __launch_bounds__(kSortBlock) k_sort_hist(const int32_t* __restrict__ kin, int64_t n, int V,
+                                                          int first, int shift, int32_t* __restrict__ H, int nblk) {
+  __shared__ int h[256];
+  const int tid = threadIdx.x;
+  if (tid < 256) h[tid] = 0;
+  __syncthreads();
+  const int64_t p = (int64_t)blockIdx.x * kSortBlock + tid;
+  if (p < n) atomicAdd(&h[(sort_key(kin, p, V, first) >> shift) & 255], 1);
+  __syncthreads();
+  if (tid < 256) H[(int64_t)tid * nblk + blockIdx.x] = h[tid];
+}
+
+// in-place exclusive scan of H[0..total) by one block
+__global__ void __launch_bounds__(kSortBlock) k_sort_scan(int32_t* __restrict__ H, int total) {
+  __shared__ int part[kSortBlock];
+  const int tid = threadIdx.x;
+  const int seg = (total + kSortBlock - 1) / kSortBlock;
+  const int b0 = tid * seg, b1 = min(total, b0 + seg);
+  int sum = 0;
+  for (int i = b0; i < b1; ++i) sum += H[i];
+  part[tid] = sum;
+  __syncthreads();
+  for (int o = 1; o < kSortBlock; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
   }
+  int run = part[tid] - sum;
+  for (int i = b0; i < b1; ++i) {
+    const int c = H[i];
+    H[i] = run;
+    run += c;
+  }
+}
+
+__global__ void __launch_bounds__(kSortBlock) k_sort_scatter(const int32_t* __restrict__ kin,
+                                                             const int32_t* __restrict__ vin, int64_t n, int V,
+                                                             int first, int shift, const int32_t* __restrict__ off,
+                                                             int nblk, int32_t* __restrict__ kout,
+                                                             int32_t* __restrict__ vout) {
+  constexpr int NW = kSortBlock / kWave;
+  __shared__ int wcnt[NW][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < NW * 256; i += kSortBlock) (&wcnt[0][0])[i] = 0;
+  const int64_t p = (int64_t)blockIdx.x * kSortBlock + tid;
+  const bool valid = p < n;
+  int key = 0, val = 0;
+  if (valid) {
+    key = sort_key(kin, p, V, first);
+    val = first ? (int)p : vin[p];
+  }
+  const int dig = valid ? (key >> shift) & 255 : 256;
+  // lanes of this wave with the same digit
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (dig >> b) & 1;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  const int rank = __popcll(m & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (valid && rank == 0) wcnt[w][dig] = __popcll(m);
+  __syncthreads();
+  if (tid < 256) {
+    int run = 0;
+    for (int ww = 0; ww < NW; ++ww) {
+      const int c = wcnt[ww][tid];
+      wcnt[ww][tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  if (valid) {
+    const int dst = off[(int64_t)dig * nblk + blockIdx.x] + wcnt[w][dig] + rank;
+    kout[dst] = key;
+    vout[dst] = val;
+  }
+}
+
+template <typename T, int NCH>
+struct RowAcc {
+  static constexpr int VN = Vec<T>::n;
+  float a[NCH][VN];
+  __device__ inline void zero() {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+      for (int e = 0; e < VN; ++e) a[i][e] = 0.f;
+  }
+  __device__ inline void add(const T* row, int lane, int chunks) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + i * kWave;
+      if (c < chunks) {
+        const Vec<T> v = ld16(row + c * VN);
+#pragma unroll
+        for (int e = 0; e < VN; ++e) a[i][e] += to_f32(v.v[e]);
+      }
+    }
+  }
+  __device__ inline void add_f32(const float* row, int lane, int chunks) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + i * kWave;
+      if (c < chunks) {
+#pragma unroll
+        for (int e = 0; e < VN; e += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(row + c * VN + e);
+          a[i][e] += v.x; a[i][e + 1] += v.y; a[i][e + 2] += v.z; a[i][e + 3] += v.w;
+        }
+      }
+    }
+  }
+  // dst = a, or dst += a
+  __device__ inline void store(float* dst, int lane, int chunks, bool add) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + i * kWave;
+      if (c < chunks) {
+#pragma unroll
+        for (int e = 0; e < VN; e += 4) {
+          float4* q = reinterpret_cast<float4*>(dst + c * VN + e);
+          float4 v = make_float4(a[i][e], a[i][e + 1], a[i][e + 2], a[i][e + 3]);
+          if (add) {
+            const float4 o = *q;
+            v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+          }
+          *q = v;
+        }
+      }
+    }
+  }
+};
+
+template <typename T, int NCH>
+__global__ void __launch_bounds__(256) k_embed_tiles(const T* __restrict__ g, const int32_t* __restrict__ sid,
+                                                     const int32_t* __restrict__ spos, int64_t n, int d, int V,
+                                                     float* __restrict__ dE, int accumulate,
+                                                     float* __restrict__ Pf, float* __restrict__ Pl) {
+  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t r0 = tile * kEmbTile;
+  if (r0 >= n) return;
+  const int64_t r1 = r0 + kEmbTile < n ? r0 + kEmbTile : n;
+  const int chunks = d / Vec<T>::n;
+  RowAcc<T, NCH> acc;
+  acc.zero();
+  int cur = sid[r0];
+  const bool from_prev = r0 > 0 && sid[r0 - 1] == cur;
+  bool first = true;
+  auto flush = [&](bool to_next) {
+    if (cur >= V) return;                         // dropped ids
+    if (first && from_prev) acc.store(Pf + tile * d, lane, chunks, false);
+    else if (to_next) acc.store(Pl + tile * d, lane, chunks, false);
+    else acc.store(dE + (int64_t)cur * d, lane, chunks, accumulate != 0);
+  };
+  for (int64_t r = r0; r < r1; ++r) {
+    const int id = sid[r];
+    if (id != cur) {
+      flush(false);
+      acc.zero();
+      cur = id;
+      first = false;
+    }
+    acc.add(g + (int64_t)spos[r] * d, lane, chunks);
+  }
+  flush(r1 < n && sid[r1] == cur);
+}
+
+template <typename T, int NCH>
+__global__ void __launch_bounds__(256) k_embed_fix(const int32_t* __restrict__ sid, int64_t n, int d, int V,
+                                                   float* __restrict__ dE, int accumulate,
+                                                   const float* __restrict__ Pf, const float* __restrict__ Pl) {
+  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t r0 = tile * kEmbTile;
+  if (r0 >= n) return;
+  const int64_t r1 = r0 + kEmbTile < n ? r0 + kEmbTile : n;
+  const int id = sid[r1 - 1];
+  if (r1 >= n || sid[r1] != id || id >= V) return;               // the tile's last segment ends here
+  if (sid[r0] == id && r0 > 0 && sid[r0 - 1] == id) return;      // it started in an earlier tile
+  const int chunks = d / Vec<T>::n;
+  RowAcc<T, NCH> acc;
+  acc.zero();
+  acc.add_f32(Pl + tile * d, lane, chunks);
+  for (int64_t u = tile + 1;; ++u) {
+    acc.add_f32(Pf + u * d, lane, chunks);
+    const int64_t e = (u + 1) * kEmbTile < n ? (u + 1) * kEmbTile : n;
+    if (e >= n || sid[e] != id || sid[e - 1] != id) break;
+  }
+  acc.store(dE + (int64_t)id * d, lane, chunks, accumulate != 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -84,8 +286,10 @@ __global__ void __launch_bounds__(256) k_embed_bwd(const T* __restrict__ g, cons
 // keeps its chunks of the row in registers between the two passes.
 // ---------------------------------------------------------------------------
 constexpr int kMaxChunks = 8;   // d <= 64 lanes * 8 chunks * (16 B / sizeof(T))
+// NCH = chunks a lane holds (a template argument, so the row stays in as
+// few registers as the width needs)
 
-template <typename T>
+template <typename T, int NCH>
 __global__ void __launch_bounds__(256) k_rmsnorm_fwd(const T* __restrict__ x, T* __restrict__ y,
                                                      float* __restrict__ r, int64_t rows, int d, float eps) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -94,10 +298,10 @@ __global__ void __launch_bounds__(256) k_rmsnorm_fwd(const T* __restrict__ x, T*
   constexpr int VN = Vec<T>::n;
   const int chunks = d / VN;
   const T* xr = x + row * d;
-  Vec<T> buf[kMaxChunks];
+  Vec<T> buf[NCH];
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = lane + i * kWave;
     if (c < chunks) {
       buf[i] = ld16(xr + c * VN);
@@ -112,7 +316,7 @@ __global__ void __launch_bounds__(256) k_rmsnorm_fwd(const T* __restrict__ x, T*
   const float rr = 1.0f / sqrtf(ss / (float)d + eps);
   T* yr = y + row * d;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = lane + i * kWave;
     if (c < chunks) {
       Vec<T> o;
@@ -125,7 +329,7 @@ __global__ void __launch_bounds__(256) k_rmsnorm_fwd(const T* __restrict__ x, T*
 }
 
 // dx = r * (dy - y * mean(dy * y));  dx_io = dx (accumulate = 0) or dx_io + dx.
-template <typename T>
+template <typename T, int NCH>
 __global__ void __launch_bounds__(256) k_rmsnorm_bwd(const T* __restrict__ y, const float* __restrict__ r,
                                                      const T* __restrict__ dy, T* __restrict__ dx_io,
                                                      int64_t rows, int d, int accumulate) {
@@ -136,27 +340,35 @@ __global__ void __launch_bounds__(256) k_rmsnorm_bwd(const T* __restrict__ y, co
   const int chunks = d / VN;
   const T* yr = y + row * d;
   const T* gr = dy + row * d;
-  Vec<T> yb[kMaxChunks], gb[kMaxChunks];
+  T* xr = dx_io + row * d;
+  // every load of the row (y, dy and, when accumulating, dx) is issued
+  // before the reduction
+  Vec<T> yb[NCH], gb[NCH], xb[NCH];
   float dot = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = lane + i * kWave;
     if (c < chunks) {
       yb[i] = ld16(yr + c * VN);
       gb[i] = ld16(gr + c * VN);
+      if (accumulate) xb[i] = ld16(xr + c * VN);
+    }
+  }
+  const float rr = r[row];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane + i * kWave;
+    if (c < chunks) {
 #pragma unroll
       for (int e = 0; e < VN; ++e) dot += to_f32(yb[i].v[e]) * to_f32(gb[i].v[e]);
     }
   }
   dot = wave_sum(dot) / (float)d;
-  const float rr = r[row];
-  T* xr = dx_io + row * d;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = lane + i * kWave;
     if (c < chunks) {
-      Vec<T> o;
-      if (accumulate) o = ld16(xr + c * VN);
+      Vec<T> o = xb[i];
 #pragma unroll
       for (int e = 0; e < VN; ++e) {
         float v = rr * (to_f32(gb[i].v[e]) - to_f32(yb[i].v[e]) * dot);
@@ -340,22 +552,86 @@ hipError_t embed_fwd(const T* E, const int32_t* idx, T* x, int64_t n, int d, hip
   k_embed_fwd<T><<<nblocks(n, 4), 256, 0, s>>>(E, idx, x, n, d);
   return hipGetLastError();
 }
+int64_t embed_bwd_scratch_bytes(int64_t n, int d) {
+  const int64_t nblk = (n + kSortBlock - 1) / kSortBlock, ntile = (n + kEmbTile - 1) / kEmbTile;
+  return 4 * n * 4 + 256 * nblk * 4 + 2 * ntile * (int64_t)d * 4 + 256;
+}
 template <typename T>
-hipError_t embed_bwd(const T* g, const int32_t* idx, float* dE, int64_t n, int d, hipStream_t s) {
-  k_embed_bwd<T><<<nblocks(n, 4), 256, 0, s>>>(g, idx, dE, n, d);
+hipError_t embed_bwd(const T* g, const int32_t* idx, float* dE, int64_t n, int d, int V, int accumulate,
+                     void* scratch, hipStream_t s) {
+  constexpr int VN = Vec<T>::n;
+  if (n <= 0 || d <= 0 || d % VN || d > kWave * kMaxChunks * VN || V <= 0 || n > (1LL << 31) - 1)
+    return hipErrorInvalidValue;
+  const int64_t nblk64 = (n + kSortBlock - 1) / kSortBlock, ntile = (n + kEmbTile - 1) / kEmbTile;
+  if (256 * nblk64 > (1LL << 31) - 1) return hipErrorInvalidValue;
+  const int nblk = (int)nblk64;
+  int32_t* ka = (int32_t*)scratch;
+  int32_t* va = ka + n;
+  int32_t* kb = va + n;
+  int32_t* vb = kb + n;
+  int32_t* H = vb + n;
+  float* Pf = (float*)(H + 256 * nblk64);
+  float* Pl = Pf + ntile * d;
+  // digits: enough 8-bit passes for keys 0..V (V marks dropped ids)
+  int bits = 0;
+  while (bits < 31 && (V >> bits) != 0) ++bits;
+  const int passes = (bits + 7) / 8;
+  const int32_t* kin = idx;
+  const int32_t* vin = nullptr;
+  for (int ps = 0; ps < passes; ++ps) {
+    int32_t* ko = (ps & 1) ? kb : ka;
+    int32_t* vo = (ps & 1) ? vb : va;
+    k_sort_hist<<<nblk, kSortBlock, 0, s>>>(kin, n, V, ps == 0, 8 * ps, H, nblk);
+    k_sort_scan<<<1, kSortBlock, 0, s>>>(H, 256 * nblk);
+    k_sort_scatter<<<nblk, kSortBlock, 0, s>>>(kin, vin, n, V, ps == 0, 8 * ps, H, nblk, ko, vo);
+    kin = ko;
+    vin = vo;
+  }
+  if (!accumulate) k_fill_f32<<<nblocks((int64_t)V * d, 256), 256, 0, s>>>(dE, (int64_t)V * d, 0.f);
+  const int nch = (d / VN + kWave - 1) / kWave;
+  const unsigned nb = nblocks(ntile, 4);
+#define NC_EMB(NCH)                                                                                        \
+  do {                                                                                                     \
+    k_embed_tiles<T, NCH><<<nb, 256, 0, s>>>(g, kin, vin, n, d, V, dE, accumulate, Pf, Pl);               \
+    k_embed_fix<T, NCH><<<nb, 256, 0, s>>>(kin, n, d, V, dE, accumulate, Pf, Pl);                         \
+  } while (0)
+  switch (nch) {
+    case 1: NC_EMB(1); break;
+    case 2: NC_EMB(2); break;
+    case 3: NC_EMB(3); break;
+    case 4: NC_EMB(4); break;
+    default: NC_EMB(kMaxChunks); break;
+  }
+#undef NC_EMB
   return hipGetLastError();
 }
 template <typename T>
 hipError_t rmsnorm_fwd(const T* x, T* y, float* r, int64_t rows, int d, float eps, hipStream_t s) {
   if (d % Vec<T>::n != 0 || d > kWave * kMaxChunks * Vec<T>::n) return hipErrorInvalidValue;
-  k_rmsnorm_fwd<T><<<nblocks(rows, 4), 256, 0, s>>>(x, y, r, rows, d, eps);
+  const int nch = (d / Vec<T>::n + kWave - 1) / kWave;
+  const unsigned nb = nblocks(rows, 4);
+  switch (nch) {
+    case 1: k_rmsnorm_fwd<T, 1><<<nb, 256, 0, s>>>(x, y, r, rows, d, eps); break;
+    case 2: k_rmsnorm_fwd<T, 2><<<nb, 256, 0, s>>>(x, y, r, rows, d, eps); break;
+    case 3: k_rmsnorm_fwd<T, 3><<<nb, 256, 0, s>>>(x, y, r, rows, d, eps); break;
+    case 4: k_rmsnorm_fwd<T, 4><<<nb, 256, 0, s>>>(x, y, r, rows, d, eps); break;
+    default: k_rmsnorm_fwd<T, kMaxChunks><<<nb, 256, 0, s>>>(x, y, r, rows, d, eps); break;
+  }
   return hipGetLastError();
 }
 template <typename T>
 hipError_t rmsnorm_bwd(const T* y, const float* r, const T* dy, T* dx_io, int64_t rows, int d, int accumulate,
                        hipStream_t s) {
   if (d % Vec<T>::n != 0 || d > kWave * kMaxChunks * Vec<T>::n) return hipErrorInvalidValue;
-  k_rmsnorm_bwd<T><<<nblocks(rows, 4), 256, 0, s>>>(y, r, dy, dx_io, rows, d, accumulate);
+  const int nch = (d / Vec<T>::n + kWave - 1) / kWave;
+  const unsigned nb = nblocks(rows, 4);
+  switch (nch) {
+    case 1: k_rmsnorm_bwd<T, 1><<<nb, 256, 0, s>>>(y, r, dy, dx_io, rows, d, accumulate); break;
+    case 2: k_rmsnorm_bwd<T, 2><<<nb, 256, 0, s>>>(y, r, dy, dx_io, rows, d, accumulate); break;
+    case 3: k_rmsnorm_bwd<T, 3><<<nb, 256, 0, s>>>(y, r, dy, dx_io, rows, d, accumulate); break;
+    case 4: k_rmsnorm_bwd<T, 4><<<nb, 256, 0, s>>>(y, r, dy, dx_io, rows, d, accumulate); break;
+    default: k_rmsnorm_bwd<T, kMaxChunks><<<nb, 256, 0, s>>>(y, r, dy, dx_io, rows, d, accumulate); break;
+  }
   return hipGetLastError();
 }
 template <typename T>
@@ -367,8 +643,8 @@ hipError_t attn_delta(const AttnDesc& a, hipStream_t s) {
 
 template hipError_t embed_fwd<float>(const float*, const int32_t*, float*, int64_t, int, hipStream_t);
 template hipError_t embed_fwd<bf16>(const bf16*, const int32_t*, bf16*, int64_t, int, hipStream_t);
-template hipError_t embed_bwd<float>(const float*, const int32_t*, float*, int64_t, int, hipStream_t);
-template hipError_t embed_bwd<bf16>(const bf16*, const int32_t*, float*, int64_t, int, hipStream_t);
+template hipError_t embed_bwd<float>(const float*, const int32_t*, float*, int64_t, int, int, int, void*, hipStream_t);
+template hipError_t embed_bwd<bf16>(const bf16*, const int32_t*, float*, int64_t, int, int, int, void*, hipStream_t);
 template hipError_t rmsnorm_fwd<float>(const float*, float*, float*, int64_t, int, float, hipStream_t);
 template hipError_t rmsnorm_fwd<bf16>(const bf16*, bf16*, float*, int64_t, int, float, hipStream_t);
 template hipError_t rmsnorm_bwd<float>(const float*, const float*, const float*, float*, int64_t, int, int, hipStream_t);

@@ -77,7 +77,7 @@ int choose_splits(const nc_config& c, int M, int N, int64_t K) {
 struct Plan {
   size_t total = 0;
   size_t rope = 0, idx = 0, tgt = 0, x = 0, xf = 0, rf = 0, ce = 0, lse_head = 0, ztgt = 0, lse_part = 0;
-  size_t scalars = 0, dz = 0, g = 0, gtmp = 0, big = 0, part = 0, delta = 0, wt = 0;
+  size_t scalars = 0, dz = 0, g = 0, gtmp = 0, big = 0, part = 0, delta = 0, wt = 0, embs = 0;
   size_t layer0 = 0, layer_stride = 0;
   size_t l_a = 0, l_r1 = 0, l_qkv = 0, l_o = 0, l_lse = 0, l_m = 0, l_r2 = 0, l_u = 0;
   int head_nblk = 0;
@@ -126,6 +126,7 @@ Plan make_plan(const nc_config& c) {
     const int64_t rows = std::max<int64_t>(1, std::min<int64_t>(c.batch, 65536 / c.seq_len));
     p.head_chunk = rows * c.seq_len;
     p.dz = take((size_t)p.head_chunk * V * es);
+    p.embs = take((size_t)embed_bwd_scratch_bytes(N, (int)d));
     need((int)V, (int)d, p.head_chunk);
   }
   p.part = take(part);
@@ -479,8 +480,8 @@ int model_backward(nc_ctx* ctx, const T* params, float* grads, int accumulate) {
                                accumulate);
     if (st != NC_OK) return st;
   }
-  if (!accumulate) NC_TRY(fill_f32(dE, (int64_t)V * d, 0.f, s), "zero dE");
-  NC_TRY(embed_bwd<T>(gr, ctx->at<int32_t>(p.idx), dE, N, d, s), "embedding scatter-add");
+  NC_TRY(embed_bwd<T>(gr, ctx->at<int32_t>(p.idx), dE, N, d, V, accumulate, ctx->at<char>(p.embs), s),
+         "embedding gradient");
   return NC_OK;
 }
 

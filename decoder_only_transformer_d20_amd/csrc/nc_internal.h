@@ -105,7 +105,11 @@ hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s);
 template <typename T> hipError_t attn_delta(const AttnDesc& a, hipStream_t s);
 
 template <typename T> hipError_t embed_fwd(const T* E, const int32_t* idx, T* x, int64_t n, int d, hipStream_t s);
-template <typename T> hipError_t embed_bwd(const T* g, const int32_t* idx, float* dE, int64_t n, int d, hipStream_t s);
+// dE [V][d] (accumulate ? += : =) per-id sums of g rows, deterministic (sort
+// by id, ordered sums); scratch of embed_bwd_scratch_bytes(n, d) bytes
+int64_t embed_bwd_scratch_bytes(int64_t n, int d);
+template <typename T> hipError_t embed_bwd(const T* g, const int32_t* idx, float* dE, int64_t n, int d, int V,
+                                           int accumulate, void* scratch, hipStream_t s);
 template <typename T> hipError_t rmsnorm_fwd(const T* x, T* y, float* r, int64_t rows, int d, float eps, hipStream_t s);
 template <typename T> hipError_t rmsnorm_bwd(const T* y, const float* r, const T* dy, T* dx_io, int64_t rows, int d,
                                             int accumulate, hipStream_t s);

@@ -113,13 +113,19 @@ int nc_op_embed_fwd(int32_t dtype, int64_t n, int32_t d, const void* E, const in
                                          : embed_fwd<bf16>((const bf16*)E, idx, (bf16*)x, n, d, s));
 }
 
-int nc_op_embed_bwd(int32_t dtype, int64_t n, int32_t d, const void* g, const int32_t* idx, float* dE,
-                    void* hip_stream) {
-  if (!dtype_ok(dtype) || !g || !idx || !dE) return NC_ERR_INVALID_ARG;
-  if (n <= 0 || d <= 0 || d % 64) return NC_ERR_SHAPE;
+int64_t nc_op_embed_bwd_scratch_bytes(int64_t n, int32_t d) {
+  if (n <= 0 || d <= 0 || d % 64 || n >= (1LL << 31)) return NC_ERR_SHAPE;
+  return embed_bwd_scratch_bytes(n, d);
+}
+
+int nc_op_embed_bwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void* g, const int32_t* idx, float* dE,
+                    int32_t accumulate, void* scratch, void* hip_stream) {
+  if (!dtype_ok(dtype) || !g || !idx || !dE || !scratch) return NC_ERR_INVALID_ARG;
+  if (n <= 0 || d <= 0 || d % 64 || V <= 0 || n >= (1LL << 31)) return NC_ERR_SHAPE;
   hipStream_t s = (hipStream_t)hip_stream;
-  return status_of(dtype == NC_DTYPE_F32 ? embed_bwd<float>((const float*)g, idx, dE, n, d, s)
-                                         : embed_bwd<bf16>((const bf16*)g, idx, dE, n, d, s));
+  return status_of(dtype == NC_DTYPE_F32
+                       ? embed_bwd<float>((const float*)g, idx, dE, n, d, V, accumulate, scratch, s)
+                       : embed_bwd<bf16>((const bf16*)g, idx, dE, n, d, V, accumulate, scratch, s));
 }
 
 int64_t nc_op_head_scratch_bytes(int32_t dtype, int64_t n, int32_t d, int32_t V, int32_t portable) {

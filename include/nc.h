@@ -155,9 +155,9 @@ int nc_loss_bpb(nc_ctx* ctx, const int32_t* token_bytes, double* out);
  * every parameter, fp32, written to grads (device fp32 [nc_param_count]),
  * overwriting it (accumulate = 0) or adding to it (accumulate = 1).
  * params must be the buffer passed to nc_forward, unchanged.  NC_ERR_STATE
- * without a prior nc_forward.  Embedding rows are accumulated with fp32
- * atomics, so their low bits may differ from run to run; everything else is
- * deterministic. */
+ * without a prior nc_forward.  Deterministic: every sum (embedding rows
+ * included: the positions of each token id are summed in increasing order)
+ * runs in a fixed order, so repeated calls give identical bits. */
 int nc_backward(nc_ctx* ctx, const void* params, float* grads, int32_t accumulate);
 
 /* ---- single block (NC_FLAG_BLOCK_ONLY) ------------------------------------ */

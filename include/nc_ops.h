@@ -64,12 +64,24 @@ int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t 
                         const void* dout, const float* lse, float* delta, void* dqkv, const float* rope_tab,
                         int32_t portable, void* hip_stream);
 
-/* Embedding gather x[n] = E[idx[n]] (T [V][d] -> T [n][d]) and scatter-add
- * dE[idx[n]] += g[n] (fp32 dE, accumulated with atomics). */
+/* Embedding gather x[n] = E[idx[n]] (T [V][d] -> T [n][d]), a bitwise row
+ * copy; idx must lie in [0, V). */
 int nc_op_embed_fwd(int32_t dtype, int64_t n, int32_t d, const void* E, const int32_t* idx, void* x,
                     void* hip_stream);
-int nc_op_embed_bwd(int32_t dtype, int64_t n, int32_t d, const void* g, const int32_t* idx, float* dE,
-                    void* hip_stream);
+
+/* Embedding gradient, the transpose of the gather: for every v in [0, V),
+ * dE[v] = (accumulate ? dE[v] : 0) + sum of g[p] over the positions p with
+ * idx[p] = v (fp32 dE [V][d]; g T [n][d]; positions with idx outside
+ * [0, V) contribute nothing).  Deterministic: the (id, position) pairs are
+ * sorted by id (stable radix sort) and each id's rows are summed in
+ * increasing position, so repeated calls give identical bits.  scratch is
+ * device memory of nc_op_embed_bwd_scratch_bytes(n, d) bytes owned by the
+ * caller; d a multiple of 64, 0 < n < 2^31.  Returns NC_ERR_INVALID_ARG on
+ * NULL pointers, NC_ERR_SHAPE on sizes outside these limits (the scratch
+ * size query returns NC_ERR_SHAPE for them too). */
+int64_t nc_op_embed_bwd_scratch_bytes(int64_t n, int32_t d);
+int nc_op_embed_bwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void* g, const int32_t* idx, float* dE,
+                    int32_t accumulate, void* scratch, void* hip_stream);
 
 /* Fused unembedding + log-softmax + cross-entropy, forward only:
  * ce[n] = logsumexp_v(xf[n] . U[v]) - xf[n] . U[tgt[n]] (0 where tgt < 0),

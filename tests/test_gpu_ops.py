@@ -217,15 +217,18 @@ def test_attention_bwd(dtype, portable, B, T, H, Q, with_rope):
 # ---------------------------------------------------------------------------
 # embedding
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 1280)])
-def test_embedding_gather_bitwise_and_scatter_add(dtype, d):
+@pytest.mark.parametrize("dtype,d,V,n", [("f32", 128, 512, 1000), ("bf16", 1280, 512, 1000),
+                                         ("bf16", 192, 65536, 5000), ("f32", 64, 300, 1)])
+def test_embedding_gather_bitwise_and_gradient(dtype, d, V, n):
+    """Gather is a bitwise row copy; the gradient (a per-id sum of rows) is
+    checked against an fp64 np.add.at, with and without accumulation, with
+    ids outside [0, V) dropped, and is bitwise identical across calls."""
     rng = np.random.default_rng(30)
-    V, n = 512, 1000
     E = rng.standard_normal((V, d)).astype(np.float32)
     if dtype == "bf16":
         E = synthdata.round_to_bf16(E)
-    cfg = synthdata.get_config("small")
-    idx = synthdata.make_tokens(cfg)[0].ravel()[:n] % V     # Zipf: hot rows repeat
+    cfg = synthdata.get_config("d20")
+    idx = (synthdata.make_tokens(cfg.with_(batch=1, seq_len=max(n, 2)), rows=1)[0].ravel()[:n] % V).astype(np.int32)
     x = empty((n, d), dtype)
     nc.ops.embed_fwd(DT[dtype], n, d, dev(E, dtype), dev(idx), x, None)
     _sync()
@@ -233,13 +236,27 @@ def test_embedding_gather_bitwise_and_scatter_add(dtype, d):
     g = rng.standard_normal((n, d)).astype(np.float32)
     if dtype == "bf16":
         g = synthdata.round_to_bf16(g)
+    bad = idx.copy()
+    if n > 4:
+        bad[1], bad[3] = -5, V + 7                 # dropped
+    scratch = empty((nc.ops.embed_bwd_scratch_bytes(n, d) // 4 + 1,), "f32")
+    G, I = dev(g, dtype), dev(bad)
     dE = zeros((V, d), "f32")
-    nc.ops.embed_bwd(DT[dtype], n, d, dev(g, dtype), dev(idx), dE, None)
+    nc.ops.embed_bwd(DT[dtype], n, d, V, G, I, dE, 0, scratch, None)
     _sync()
+    keep = (bad >= 0) & (bad < V)
     want = np.zeros((V, d))
-    np.add.at(want, idx, g.astype(np.float64))
-    assert max_rel_err(host(dE), want) <= 1e-6
-    assert np.all(host(dE)[np.setdiff1d(np.arange(V), idx)] == 0)
+    np.add.at(want, bad[keep], g[keep].astype(np.float64))
+    got = host(dE)
+    assert max_rel_err(got, want) <= 1e-6
+    assert np.all(got[np.setdiff1d(np.arange(V), bad[keep])] == 0)
+    # bitwise repeatable; accumulate adds onto what is there
+    dE2 = dev(np.full((V, d), 7.0, np.float32))
+    nc.ops.embed_bwd(DT[dtype], n, d, V, G, I, dE2, 0, scratch, None)
+    nc.ops.embed_bwd(DT[dtype], n, d, V, G, I, dE, 1, scratch, None)
+    _sync()
+    np.testing.assert_array_equal(host(dE2), got)
+    assert max_rel_err(host(dE), 2 * want) <= 1e-6
 
 
 # ---------------------------------------------------------------------------

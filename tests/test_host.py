@@ -115,6 +115,12 @@ def test_ops_reject_bad_shapes_before_launch():
     assert L.nc_op_attention_fwd(1, 1, 100, 1, 128, 1, 1, 1, 0, None) == -2
     assert L.nc_op_attention_fwd(5, 1, 64, 1, 128, 1, 1, 1, 0, None) == -1
     assert L.nc_op_head_scratch_bytes(1, 128, 64, 100, 0) == -2
+    # embedding gradient: sizes, then a missing scratch buffer
+    assert L.nc_op_embed_bwd_scratch_bytes(0, 64) == -2
+    assert L.nc_op_embed_bwd_scratch_bytes(10, 100) == -2
+    assert L.nc_op_embed_bwd_scratch_bytes(10, 64) > 0
+    assert L.nc_op_embed_bwd(1, 10, 100, 50, 1, 1, 1, 0, 1, None) == -2
+    assert L.nc_op_embed_bwd(1, 10, 64, 50, 1, 1, 1, 0, None, None) == -1
 
 
 def test_status_strings():
