@@ -171,10 +171,9 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   constexpr int kGroupM = 8;
   const int ntn = g.N / BN, ntm = g.M / BM;
   const int ntiles = ntn * ntm, total = ntiles * g.splits;
-  const int kper = g.K / g.splits;
-  const int nk = kper / BK;
+  const int nkt = g.K / BK;                      // split i: k-tiles [i nkt/splits, (i+1) nkt/splits)
   struct Tile {
-    int split, tn;
+    int split, tn, nk;
     int64_t m0, n0, kbeg;
   };
   auto coords = [&](int v) {
@@ -189,7 +188,9 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
     c.tn = tg / gm;
     c.m0 = (int64_t)(first_m + tg % gm) * BM;
     c.n0 = (int64_t)c.tn * BN;
-    c.kbeg = (int64_t)c.split * kper;
+    const int kt0 = (int)((int64_t)c.split * nkt / g.splits);
+    c.nk = (int)((int64_t)(c.split + 1) * nkt / g.splits) - kt0;
+    c.kbeg = (int64_t)kt0 * BK;
     return c;
   };
 
@@ -290,6 +291,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   stage_load();                 // k-tile 0 of the first tile
 
   for (;;) {
+    const int nk = cur.nk;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll

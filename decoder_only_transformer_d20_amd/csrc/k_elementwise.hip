@@ -475,10 +475,16 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(const float4* __restrict_
                                                        float4* __restrict__ out, int beta) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
-  float4 a = beta ? out[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < splits; ++s) {
+  // the product is summed first and then added to out, so accumulating
+  // adds exactly the value a fresh call would write
+  float4 a = part[i];
+  for (int s = 1; s < splits; ++s) {
     const float4 p = part[s * n4 + i];
     a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
+  }
+  if (beta) {
+    const float4 o = out[i];
+    a.x = o.x + a.x; a.y = o.y + a.y; a.z = o.z + a.z; a.w = o.w + a.w;
   }
   out[i] = a;
 }

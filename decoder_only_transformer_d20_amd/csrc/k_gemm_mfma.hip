@@ -12,7 +12,7 @@ int gemm_mfma_tile_n(int M, int N) {
 
 bool gemm_mfma_supported(const GemmDesc& g) {
   if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.M % 128 || g.N % 128 || g.splits < 1) return false;
-  if (g.K % (mfma::BK * g.splits)) return false;
+  if (g.K % mfma::BK || g.splits > g.K / mfma::BK) return false;
   if (g.splits > 1 && g.epi != EPI_F32) return false;
   if (g.epi == EPI_ROPE && (g.head_dim % 4 || g.rope_cols % 4)) return false;
   return mfma::combo_supported(g);

@@ -26,8 +26,8 @@ __global__ void __launch_bounds__(256) k_gemm_portable(GemmDesc g) {
   const int tid = threadIdx.x;
   const int tx = tid % 16, ty = tid / 16;
   const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int kper = g.K / g.splits;
-  const int64_t kbeg = (int64_t)blockIdx.z * kper, kend = kbeg + kper;
+  const int64_t nb = g.K / 64;                   // split z: 64-wide k blocks [z nb/s, (z+1) nb/s)
+  const int64_t kbeg = (int64_t)blockIdx.z * nb / g.splits * 64, kend = ((int64_t)blockIdx.z + 1) * nb / g.splits * 64;
 
   float acc[4][4] = {};
   for (int64_t k0 = kbeg; k0 < kend; k0 += BK) {
@@ -147,7 +147,7 @@ __global__ void __launch_bounds__(256) k_gemm_portable(GemmDesc g) {
 
 template <typename T>
 hipError_t gemm_portable(const GemmDesc& g, hipStream_t s) {
-  if (g.M % BM || g.N % BN || g.splits < 1 || g.K % (BK * g.splits)) return hipErrorInvalidValue;
+  if (g.M % BM || g.N % BN || g.splits < 1 || g.K % 64 || g.splits > g.K / 64) return hipErrorInvalidValue;
   if (g.splits > 1 && g.epi != EPI_F32) return hipErrorInvalidValue;
   dim3 grid(g.N / BN, g.M / BM, g.splits);
   k_gemm_portable<T><<<grid, 256, 0, s>>>(g);

@@ -7,6 +7,7 @@
 // rotary positions and a squared-ReLU MLP, parameter-free RMSNorm, untied
 // embedding / unembedding, next-token cross-entropy and bits per byte.
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -64,14 +65,28 @@ int tile_n(const nc_config& c, int M, int N) {
   return gemm_mfma_supported(g) ? gemm_mfma_tile_n(M, N) : 64;
 }
 
-// Split-K factor for the weight-gradient products (K = tokens): enough
-// workgroups to fill the chip, every split a multiple of 256 tokens.
+// Split-K factor for the weight-gradient products (K = tokens).  Each split
+// is a (tile, k-range) unit of the persistent grid; more splits fill the
+// chip's 256 CUs in fuller waves but write and re-read more fp32 partials.
+// The count minimises a simple model: compute time at 1 PFLOP/s scaled by
+// the wave quantisation, plus the partials' round trip at 5 TB/s.
 int choose_splits(const nc_config& c, int M, int N, int64_t K) {
+  constexpr int kCUs = 256;
   const int64_t tiles = portable(c) ? (int64_t)(M / 64) * (N / 64)
                                     : (int64_t)(M / gemm_mfma_tile_m(M, N)) * (N / gemm_mfma_tile_n(M, N));
-  int s = 1;
-  while (tiles * s < 1024 && K % (2LL * s * 256) == 0 && K / (2 * s) >= 2048 && s < 64) s *= 2;
-  return s;
+  const int64_t nb = K / 64;
+  int best_s = 1;
+  double best = 0.0;
+  for (int s = 1; s <= 32 && s <= nb; ++s) {
+    const double units = (double)tiles * s;
+    const double waves = std::ceil(units / kCUs);
+    const double t = 2.0 * M * N * (double)K / 1e15 * (waves * kCUs / units) + (s > 1 ? s * 8.0 * M * N / 5e12 : 0.0);
+    if (s == 1 || t < best * (1.0 - 1e-9)) {
+      best = t;
+      best_s = s;
+    }
+  }
+  return best_s;
 }
 
 struct Plan {

@@ -57,7 +57,8 @@ struct GemmDesc {
   void* C; int64_t ldc;
   const void* aux; int64_t ldaux;
   int beta;                 // EPI_F32: add to C
-  int splits;               // EPI_F32: split-K count (partials + reduce when > 1)
+  int splits;               // EPI_F32: split-K count (partials + reduce when > 1); split i
+                            // covers the 64-wide k blocks [i*nb/splits, (i+1)*nb/splits), nb = K/64
   float* part;              // EPI_F32 split-K partials [splits][M][N]
   // EPI_ROPE
   const float2* rope;       // [T][head_dim/2] (cos, sin)

@@ -42,7 +42,7 @@ int nc_op_matmul(int32_t dtype, int32_t p_trans, int32_t q_trans, int64_t M, int
   if (M <= 0 || N <= 0 || K <= 0 || M % 64 || N % 64 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
     return NC_ERR_SHAPE;
   if (splits < 1 || (splits > 1 && (!out_f32 || !part))) return NC_ERR_INVALID_ARG;
-  if (K % (64LL * splits)) return NC_ERR_SHAPE;
+  if (K % 64 || splits > K / 64) return NC_ERR_SHAPE;
   GemmDesc g{};
   g.M = (int)M; g.N = (int)N; g.K = (int)K;
   g.P = P; g.ldp = p_trans ? M : K; g.p_trans = p_trans ? 1 : 0;

@@ -28,9 +28,11 @@ extern "C" {
  *   Q    T [N][K] row-major, or [K][N] when q_trans = 1
  *   C    fp32 [M][N] (out_f32 = 1, written with plain stores) or T [M][N]
  *        (out_f32 = 0, rounded to T)
- *   splits  split-K factor (out_f32 = 1 only); splits > 1 needs `part`,
- *        fp32 scratch of splits*M*N elements, reduced in a fixed order.
- * M, N multiples of 64; K a multiple of 64*splits. */
+ *   splits  split-K factor (out_f32 = 1 only): split i sums the 64-wide k
+ *        blocks [i*nb/splits, (i+1)*nb/splits), nb = K/64; splits > 1 needs
+ *        `part`, fp32 scratch of splits*M*N elements, reduced in a fixed
+ *        order.
+ * M, N multiples of 64; K a multiple of 64, splits <= K/64. */
 int nc_op_matmul(int32_t dtype, int32_t p_trans, int32_t q_trans, int64_t M, int64_t N, int64_t K,
                  const void* P, const void* Q, void* C, int32_t out_f32, int32_t splits, float* part,
                  int32_t portable, void* hip_stream);

@@ -70,10 +70,13 @@ def test_matmul_exact_integers(dtype, portable, M, N, K, pt, qt):
     np.testing.assert_array_equal(host(Cs, dtype), wantr)
 
 
+@pytest.mark.parametrize("K,S", [(4096, 4), (4096, 5), (832, 7)])
 @pytest.mark.parametrize("dtype,portable", [("f32", 1), ("bf16", 1), ("bf16", 0)])
-def test_matmul_split_k_exact(dtype, portable):
+def test_matmul_split_k_exact(dtype, portable, K, S):
+    """Split-K with even and uneven splits (split i takes the 64-wide k
+    blocks [i nb/S, (i+1) nb/S)), exact on integer data."""
     rng = np.random.default_rng(7)
-    M, N, K, S = 256, 384, 4096, 4
+    M, N = 256, 384
     P = _ints(rng, (K, M))     # stored [K][M]: the weight-gradient layout
     Q = _ints(rng, (K, N))
     want = P.astype(np.int64).T @ Q.astype(np.int64)
