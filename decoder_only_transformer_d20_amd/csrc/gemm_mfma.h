@@ -161,10 +161,10 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   const int wm = wave & 1, wn = wave >> 1;
 
   // Logical tile -> (split, m-tile, n-tile).  Workgroups are dealt to the 8
-  // XCDs round-robin (and G is a multiple of 8, so a block stays on one
-  // XCD), so the flat index is renumbered to give each XCD a contiguous run
-  // of logical tiles (splits outermost: with 8 splits an XCD owns one K
-  // range).  Within a split, tiles are rastered in groups of kGroupM
+  // XCDs round-robin (and a full grid's G is a multiple of 8, so a block
+  // stays on one XCD), so block slots are renumbered to give each XCD a
+  // contiguous run of logical tiles (splits outermost, so an XCD works
+  // through few K ranges).  Within a split, tiles are rastered in groups of kGroupM
   // m-tiles, m fastest: the ~32 blocks an XCD runs at once cover about 8
   // m-tiles x 4 n-tiles, so each P panel and each Q panel (weights) is
   // reused from that XCD's L2 instead of refetched per tile.
@@ -176,9 +176,19 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
     int split, tn, nk;
     int64_t m0, n0, kbeg;
   };
-  auto coords = [&](int v) {
-    int L = v;
-    if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
+  // Block slot v (block b takes v = b, b + G, ...) -> logical tile L.  With
+  // G a multiple of 8, slot v runs on XCD v & 7, which owns the contiguous
+  // logical range [x*chunk, (x+1)*chunk), chunk = ceil(total/8); -1 when the
+  // XCD's range is exhausted.
+  const int G = (int)gridDim.x;
+  const int chunk = (total + 7) >> 3;
+  auto logical = [&](int v) -> int {
+    if (G & 7) return v < total ? v : -1;
+    const int x = v & 7, j = v >> 3;
+    const int L = x * chunk + j;
+    return (j < chunk && L < total) ? L : -1;
+  };
+  auto coords = [&](int L) {
     Tile c;
     c.split = L / ntiles;
     const int t = L - c.split * ntiles;
@@ -286,7 +296,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   };
 
   int v = blockIdx.x;
-  Tile cur = coords(v);
+  if (logical(v) < 0) return;                    // no tile for this block (uniform)
+  Tile cur = coords(logical(v));
   plan_init(cur);
   stage_load();                 // k-tile 0 of the first tile
 
@@ -363,12 +374,13 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
 
     // The block's next tile: its first k-tile's loads are issued once the
     // accumulators have gone to LDS, and overlap the rest of the epilogue.
-    const int vn = v + (int)gridDim.x;
-    const bool more = vn < total;
+    const int vn = v + G;
+    const int Ln = logical(vn);
+    const bool more = Ln >= 0;
     const Tile c = cur;
     auto prefetch_next = [&]() {
       if (more) {
-        cur = coords(vn);
+        cur = coords(Ln);
         plan_init(cur);
         stage_load();
       }
