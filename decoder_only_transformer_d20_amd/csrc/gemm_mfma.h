@@ -138,6 +138,135 @@ __device__ inline uint32_t frag_tr_off(int row0, int l) {
   return (uint32_t)k * (2u * R) + ((uint32_t)((m >> 3) ^ (4 * (j >> 2))) << 4) + 8u * ((m >> 2) & 1);
 }
 
+// One output tile of the persistent grid: split, n-tile, k-tiles, origin.
+struct GemmTile {
+  int split, tn, nk;
+  int64_t m0, n0, kbeg;
+};
+
+// Logical tile -> (split, m-tile, n-tile).  Workgroups are dealt to the 8
+// XCDs round-robin (and a full grid's G is a multiple of 8, so a block stays
+// on one XCD), so block slots are renumbered to give each XCD a contiguous
+// run of logical tiles (splits outermost, so an XCD works through few K
+// ranges).  Within a split, tiles are rastered in groups of kGroupM m-tiles,
+// m fastest: the ~32 blocks an XCD runs at once cover about 8 m-tiles x 4
+// n-tiles, so each P panel and each Q panel (weights) is reused from that
+// XCD's L2 instead of refetched per tile.  Split i covers the k-tiles
+// [i nkt/splits, (i+1) nkt/splits).
+template <int BM, int BN>
+struct TileMap {
+  static constexpr int kGroupM = 8;
+  int ntn, ntm, ntiles, total, nkt, G, chunk, splits;
+  __device__ inline TileMap(const GemmDesc& g) {
+    ntn = g.N / BN;
+    ntm = g.M / BM;
+    ntiles = ntn * ntm;
+    splits = g.splits;
+    total = ntiles * splits;
+    nkt = g.K / BK;
+    G = (int)gridDim.x;
+    chunk = (total + 7) >> 3;
+  }
+  // block slot v (block b takes v = b, b + G, ...) -> logical tile, or -1
+  // once the slot's XCD range [x*chunk, (x+1)*chunk) is exhausted
+  __device__ inline int logical(int v) const {
+    if (G & 7) return v < total ? v : -1;
+    const int x = v & 7, j = v >> 3;
+    const int L = x * chunk + j;
+    return (j < chunk && L < total) ? L : -1;
+  }
+  __device__ inline GemmTile coords(int L) const {
+    GemmTile c;
+    c.split = L / ntiles;
+    const int t = L - c.split * ntiles;
+    const int first_m = (t / (kGroupM * ntn)) * kGroupM;
+    const int gm = min(kGroupM, ntm - first_m);
+    const int tg = t - first_m * ntn;
+    c.tn = tg / gm;
+    c.m0 = (int64_t)(first_m + tg % gm) * BM;
+    c.n0 = (int64_t)c.tn * BN;
+    const int kt0 = (int)((int64_t)c.split * nkt / splits);
+    c.nk = (int)((int64_t)(c.split + 1) * nkt / splits) - kt0;
+    c.kbeg = (int64_t)kt0 * BK;
+    return c;
+  }
+};
+
+// Finish and store four consecutive outputs (row m, columns n .. n+3) of a
+// row-order epilogue: x holds the fp32 products; y, cs, dz_t, dz_l are the
+// row's prefetched inputs (aux pair, rotary factors, target and lse).
+template <int EPI>
+__device__ inline void epi_store4(const GemmDesc& g, const GemmTile& c, int64_t m, int64_t n, float (&x)[4],
+                                  uint2 y, float4 cs, bool rot, int dz_t, float dz_l, float inv_nv) {
+  if constexpr (EPI == EPI_F32) {
+    if (g.splits > 1) {
+      float* dst = g.part + (int64_t)c.split * g.M * g.N + m * g.N + n;
+      *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+    } else {
+      float* dst = (float*)g.C + m * g.ldc + n;
+      float4 o = make_float4(x[0], x[1], x[2], x[3]);
+      if (g.beta) {
+        const float4 q = *reinterpret_cast<const float4*>(dst);
+        o.x += q.x; o.y += q.y; o.z += q.z; o.w += q.w;
+      }
+      *reinterpret_cast<float4*>(dst) = o;
+    }
+    return;
+  }
+  if constexpr (EPI == EPI_ROPE) {
+    // (rot ? rotated : as is), without a branch
+    const float c0 = rot ? cs.x : 1.f, s0 = rot ? cs.y : 0.f;
+    const float c1 = rot ? cs.z : 1.f, s1 = rot ? cs.w : 0.f;
+    const float x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
+    x[0] = x0 * c0 - x1 * s0;
+    x[1] = x0 * s0 + x1 * c0;
+    x[2] = x2 * c1 - x3 * s1;
+    x[3] = x2 * s1 + x3 * c1;
+  }
+  if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2) {
+    const float a0 = bf_lo(y.x), a1 = bf_hi(y.x), a2 = bf_lo(y.y), a3 = bf_hi(y.y);
+    if constexpr (EPI == EPI_RESID) {
+      x[0] += a0; x[1] += a1; x[2] += a2; x[3] += a3;
+    } else {
+      // aux = relu(h)^2, so 2 relu(h) = 2 sqrt(aux)
+      x[0] *= 2.f * __builtin_sqrtf(fmaxf(a0, 0.f));
+      x[1] *= 2.f * __builtin_sqrtf(fmaxf(a1, 0.f));
+      x[2] *= 2.f * __builtin_sqrtf(fmaxf(a2, 0.f));
+      x[3] *= 2.f * __builtin_sqrtf(fmaxf(a3, 0.f));
+    }
+  }
+  if constexpr (EPI == EPI_RELU2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], 0.f) * fmaxf(x[e], 0.f);
+  }
+  if constexpr (EPI == EPI_DZ) {
+    const float dz_s = dz_t >= 0 ? inv_nv : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      x[e] = (__builtin_amdgcn_exp2f(x[e] * kLog2e - dz_l) - ((n + e) == dz_t ? 1.f : 0.f)) * dz_s;
+  }
+  *reinterpret_cast<uint2*>((bf16*)g.C + m * g.ldc + n) = make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
+}
+
+// Per-row (max, sum exp) of a tile's logits from the WGN column groups
+// (red [WGN][BM], written by the waves), combined by the first BM threads.
+template <int WGN, int BM>
+__device__ inline void lse_combine(const GemmDesc& g, const GemmTile& c, const float2* red, int etid) {
+  if (etid < BM) {
+    float2 p[WGN];
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WGN; ++w) {
+      p[w] = red[w * BM + etid];
+      M = fmaxf(M, p[w].x);
+    }
+    float S = 0.f;
+#pragma unroll
+    for (int w = 0; w < WGN; ++w) S += p[w].y * __builtin_amdgcn_exp2f((p[w].x - M) * kLog2e);
+    g.lse_part[(c.m0 + etid) * g.lse_stride + c.tn] = make_float2(M, S);
+  }
+}
+
 // Waves in a 2 x 4 grid, wave tile (BM/2) x (BN/4); waves 0-3 stage P and
 // waves 4-7 stage Q (two waves per SIMD).
 //
@@ -160,49 +289,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
 
-  // Logical tile -> (split, m-tile, n-tile).  Workgroups are dealt to the 8
-  // XCDs round-robin (and a full grid's G is a multiple of 8, so a block
-  // stays on one XCD), so block slots are renumbered to give each XCD a
-  // contiguous run of logical tiles (splits outermost, so an XCD works
-  // through few K ranges).  Within a split, tiles are rastered in groups of kGroupM
-  // m-tiles, m fastest: the ~32 blocks an XCD runs at once cover about 8
-  // m-tiles x 4 n-tiles, so each P panel and each Q panel (weights) is
-  // reused from that XCD's L2 instead of refetched per tile.
-  constexpr int kGroupM = 8;
-  const int ntn = g.N / BN, ntm = g.M / BM;
-  const int ntiles = ntn * ntm, total = ntiles * g.splits;
-  const int nkt = g.K / BK;                      // split i: k-tiles [i nkt/splits, (i+1) nkt/splits)
-  struct Tile {
-    int split, tn, nk;
-    int64_t m0, n0, kbeg;
-  };
-  // Block slot v (block b takes v = b, b + G, ...) -> logical tile L.  With
-  // G a multiple of 8, slot v runs on XCD v & 7, which owns the contiguous
-  // logical range [x*chunk, (x+1)*chunk), chunk = ceil(total/8); -1 when the
-  // XCD's range is exhausted.
-  const int G = (int)gridDim.x;
-  const int chunk = (total + 7) >> 3;
-  auto logical = [&](int v) -> int {
-    if (G & 7) return v < total ? v : -1;
-    const int x = v & 7, j = v >> 3;
-    const int L = x * chunk + j;
-    return (j < chunk && L < total) ? L : -1;
-  };
-  auto coords = [&](int L) {
-    Tile c;
-    c.split = L / ntiles;
-    const int t = L - c.split * ntiles;
-    const int first_m = (t / (kGroupM * ntn)) * kGroupM;
-    const int gm = min(kGroupM, ntm - first_m);
-    const int tg = t - first_m * ntn;
-    c.tn = tg / gm;
-    c.m0 = (int64_t)(first_m + tg % gm) * BM;
-    c.n0 = (int64_t)c.tn * BN;
-    const int kt0 = (int)((int64_t)c.split * nkt / g.splits);
-    c.nk = (int)((int64_t)(c.split + 1) * nkt / g.splits) - kt0;
-    c.kbeg = (int64_t)kt0 * BK;
-    return c;
-  };
+  const TileMap<BM, BN> tm(g);
+  typedef GemmTile Tile;
 
   // Waves 0-3 stage P tiles, waves 4-7 Q tiles (a wave-uniform split), with
   // one plan per thread.  Staging code depends only on the tile height, so
@@ -296,8 +384,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   };
 
   int v = blockIdx.x;
-  if (logical(v) < 0) return;                    // no tile for this block (uniform)
-  Tile cur = coords(logical(v));
+  if (tm.logical(v) < 0) return;                 // no tile for this block (uniform)
+  Tile cur = tm.coords(tm.logical(v));
   plan_init(cur);
   stage_load();                 // k-tile 0 of the first tile
 
@@ -374,13 +462,13 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
 
     // The block's next tile: its first k-tile's loads are issued once the
     // accumulators have gone to LDS, and overlap the rest of the epilogue.
-    const int vn = v + G;
-    const int Ln = logical(vn);
+    const int vn = v + tm.G;
+    const int Ln = tm.logical(vn);
     const bool more = Ln >= 0;
     const Tile c = cur;
     auto prefetch_next = [&]() {
       if (more) {
-        cur = coords(Ln);
+        cur = tm.coords(Ln);
         plan_init(cur);
         stage_load();
       }
@@ -427,19 +515,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
       }
       __syncthreads();
       prefetch_next();
-      if (etid < BM) {
-        float2 p[WGN];
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < WGN; ++w) {
-          p[w] = red[w * BM + etid];
-          M = fmaxf(M, p[w].x);
-        }
-        float S = 0.f;
-#pragma unroll
-        for (int w = 0; w < WGN; ++w) S += p[w].y * __builtin_amdgcn_exp2f((p[w].x - M) * kLog2e);
-        g.lse_part[(c.m0 + etid) * g.lse_stride + c.tn] = make_float2(M, S);
-      }
+      lse_combine<WGN, BM>(g, c, red, etid);
     } else {
       // Two passes, one per half of the tile's rows (the waves with wm = h
       // own rows h*WTM ..): those waves write their fp32 accumulators to
@@ -516,54 +592,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
           const int dz_t = pt[k % W];
           const float dz_l = pl[k % W] * kLog2e;
           if (k + W < NR) fetch(k + W);
-          if constexpr (EPI == EPI_F32) {
-            if (g.splits > 1) {
-              float* dst = g.part + (int64_t)c.split * g.M * g.N + m * g.N + n;
-              *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
-            } else {
-              float* dst = (float*)g.C + m * g.ldc + n;
-              float4 o = make_float4(x[0], x[1], x[2], x[3]);
-              if (g.beta) {
-                const float4 y = *reinterpret_cast<const float4*>(dst);
-                o.x += y.x; o.y += y.y; o.z += y.z; o.w += y.w;
-              }
-              *reinterpret_cast<float4*>(dst) = o;
-            }
-            continue;
-          }
-          if constexpr (EPI == EPI_ROPE) {
-            // (rot ? rotated : as is), without a branch
-            const float c0 = rot ? cs.x : 1.f, s0 = rot ? cs.y : 0.f;
-            const float c1 = rot ? cs.z : 1.f, s1 = rot ? cs.w : 0.f;
-            const float x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
-            x[0] = x0 * c0 - x1 * s0;
-            x[1] = x0 * s0 + x1 * c0;
-            x[2] = x2 * c1 - x3 * s1;
-            x[3] = x2 * s1 + x3 * c1;
-          }
-          if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2) {
-            const float a0 = bf_lo(y.x), a1 = bf_hi(y.x), a2 = bf_lo(y.y), a3 = bf_hi(y.y);
-            if constexpr (EPI == EPI_RESID) {
-              x[0] += a0; x[1] += a1; x[2] += a2; x[3] += a3;
-            } else {
-              // aux = relu(h)^2, so 2 relu(h) = 2 sqrt(aux)
-              x[0] *= 2.f * __builtin_sqrtf(fmaxf(a0, 0.f));
-              x[1] *= 2.f * __builtin_sqrtf(fmaxf(a1, 0.f));
-              x[2] *= 2.f * __builtin_sqrtf(fmaxf(a2, 0.f));
-              x[3] *= 2.f * __builtin_sqrtf(fmaxf(a3, 0.f));
-            }
-          }
-          if constexpr (EPI == EPI_RELU2) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], 0.f) * fmaxf(x[e], 0.f);
-          }
-          if constexpr (EPI == EPI_DZ) {
-            const float dz_s = dz_t >= 0 ? inv_nv : 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              x[e] = (__builtin_amdgcn_exp2f(x[e] * kLog2e - dz_l) - ((n + e) == dz_t ? 1.f : 0.f)) * dz_s;
-          }
-          *reinterpret_cast<uint2*>((bf16*)g.C + m * g.ldc + n) = make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
+          epi_store4<EPI>(g, c, m, n, x, y, cs, rot, dz_t, dz_l, inv_nv);
         }
         if (h == 0) __syncthreads();
       }
@@ -573,17 +602,16 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   }
 }
 
-// Blocks of one instantiation that fit on the device at once, times the
-// device's CU count; cached per instantiation and device.
-template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
-int resident_blocks() {
-  static int cached[16] = {0};
+// Blocks of a kernel that fit on the device at once, times the device's CU
+// count, rounded up to a multiple of 8 (one share per XCD); cached per
+// instantiation (`cached`) and device.
+template <typename Kernel>
+int resident_blocks(Kernel kern, int threads, int (&cached)[16]) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   if (!cached[dev]) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemm_mfma<NW, BM, BN, PT, QT, EPI>, NW * 64, 0) !=
-            hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess || per_cu < 1)
       per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
     cached[dev] = ((per_cu * cus) + 7) / 8 * 8;
@@ -593,11 +621,13 @@ int resident_blocks() {
 
 template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
 hipError_t launch(const GemmDesc& g, hipStream_t s) {
+  static int cached[16] = {0};
   const int total = (g.M / BM) * (g.N / BN) * g.splits;
-  dim3 grid(std::min(total, resident_blocks<NW, BM, BN, PT, QT, EPI>()));
+  dim3 grid(std::min(total, resident_blocks(k_gemm_mfma<NW, BM, BN, PT, QT, EPI>, NW * 64, cached)));
   k_gemm_mfma<NW, BM, BN, PT, QT, EPI><<<grid, NW * 64, 0, s>>>(g);
   return hipGetLastError();
 }
+
 
 }  // namespace mfma
 }  // namespace nc
