@@ -338,18 +338,20 @@ __global__ void __launch_bounds__(512, 1) k_attn_dkdv(AttnDesc a) {
   const float* del_bh = a.delta + ((int64_t)b * H + h) * T;
 
   u32x4 rq[2], ro[2];
-  float rs = 0.f;                                // lse2 (threads 0-63) or delta (64-127) of one query
+  float rs = 0.f;                                // lse (threads 0-63) or delta (64-127) of one query
+  // (lse is scaled to base 2 when stored, not when loaded: a use right
+  // after the load would wait for every load in flight)
   auto gl = [&](int qt) {
     const int64_t i0 = (int64_t)qt * 64;
     load_nat64<512>(qb + i0 * ld, ld, tid, rq);
     load_nat64<512>(dob + i0 * d, d, tid, ro);
-    if (tid < 64) rs = lse_bh[i0 + tid] * kLog2e;
+    if (tid < 64) rs = lse_bh[i0 + tid];
     else if (tid < 128) rs = del_bh[i0 + tid - 64];
   };
   auto st = [&](char* base) {
     store_nat64<512>(base, tid, rq);
     store_nat64<512>(base + 16384, tid, ro);
-    if (tid < 128) reinterpret_cast<float*>(base + 32768)[tid] = rs;
+    if (tid < 128) reinterpret_cast<float*>(base + 32768)[tid] = tid < 64 ? rs * kLog2e : rs;
   };
   const int qt0 = jb / 64, nq = T / 64;
   gl(qt0);
@@ -360,6 +362,11 @@ __global__ void __launch_bounds__(512, 1) k_attn_dkdv(AttnDesc a) {
     const bf16* src = (roleP ? kb : vb) + (int64_t)my_j * ld + 8 * hh;
 #pragma unroll
     for (int s = 0; s < 8; ++s) kv[s] = as_bf16x8(gload(src + 16 * s));
+    // Wait for these rows here, once: otherwise the loop's first products
+    // wait on the load counter, which by then also counts the next tile's
+    // loads, and every tile would sit out their latency.
+#pragma unroll
+    for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(kv[s]));
   }
   floatx16 acc[4];                               // dV (P role) or dK (D role)
 #pragma unroll
