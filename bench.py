@@ -43,8 +43,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 # scaled by the counters' reading for --copy-calibration (see profiles/).
 # Keyed by family; valid only for the recorded hash of the kernel source.
 TRAFFIC = {
-    # profiles/d20_step_hbm_traffic.md: 1.504 GB fetched + 0.347 GB written per dispatch
-    "gemm_wgrad": {"bytes_per_launch": 1850848069, "source_hash": "32bef025e87c486a"},
+    # profiles/d20_step_hbm_traffic.md: 1.846 GB fetched + 0.134 GB written per dispatch
+    "gemm_wgrad": {"bytes_per_launch": 1979186304, "source_hash": "704f596975cfa06d"},
 }
 
 
