@@ -227,3 +227,37 @@ def test_d20_full_batch_consistency():
     assert np.all(np.isfinite(full["grads"]))
     # near-uniform predictions at init: loss close to ln V
     assert abs(full["out"][0] - math.log(cfg.vocab)) < 2.0
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_d30_one_row_matches_oracle():
+    """The scaled d30 model (30 layers, d_model 1920, 15 heads x 128, MLP
+    7680, vocab 65,536) on one 2048-token row.  Its widths 1920 and 5760 are
+    not multiples of 256, so the projections run on 256 x 128 tiles."""
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("d30"), rows=1)
+    got = _gpu_step(cfg, params, idx, tgt, tb)
+    want = _oracle_step(cfg, params, idx, tgt, tb)
+    assert abs(got["out"][0] - want["loss"]) / want["loss"] <= 1e-2
+    assert abs(got["out"][1] - want["bpb"]) / want["bpb"] <= 1e-2
+    for (name, layer, g), (_, _, w) in zip(flat_tensors(cfg, got["grads"]), flat_tensors(cfg, want["grads"])):
+        assert cosine(g, w) >= 0.999, (name, layer, cosine(g, w))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_d30_full_batch_consistency():
+    """The d30 step at its full launch (16 x 2048): row 0's losses equal the
+    one-row run's, loss and bpb follow from the per-token ce, every gradient
+    is finite."""
+    cfg1, params, idx1, tgt1, tb = _inputs(synthdata.get_config("d30"), rows=1)
+    one = _gpu_step(cfg1, params, idx1, tgt1, tb, grads=False)
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("d30"))
+    assert idx.shape == (16, 2048)
+    full = _gpu_step(cfg, params, idx, tgt, tb)
+    np.testing.assert_array_equal(full["ce"][0], one["ce"][0])
+    s = full["ce"].astype(np.float64).sum()
+    assert full["out"][0] == pytest.approx(s / idx.size, rel=1e-9)
+    assert full["out"][1] == pytest.approx(s / (math.log(2) * tb[tgt].sum()), rel=1e-9)
+    assert np.all(np.isfinite(full["grads"]))
+    assert abs(full["out"][0] - math.log(cfg.vocab)) < 2.0
