@@ -93,6 +93,41 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
 
 
+def measured_peaks(torch, nc, stream):
+    """What the chip sustains on this machine, next to the spec peaks: the bf16
+    matrix-core rate of a register-only MFMA loop (nc_op_mfma_loop: 8
+    independent 32x32x16 products per round, no memory traffic), and HBM
+    read+write bandwidth of a 2 GiB device-to-device copy."""
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sink = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    iters = 4000
+    nc.ops.mfma_loop(iters, cus, sink, stream.cuda_stream)               # warm-up
+    ev0.record(stream)
+    nc.ops.mfma_loop(iters, cus, sink, stream.cuda_stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    mfma_tflops = cus * 4 * iters * 8 * 32768 / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    with torch.cuda.stream(stream):
+        b.copy_(a)                                                        # warm-up
+        ev0.record(stream)
+        for _ in range(3):
+            b.copy_(a)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 3 * 2 * n / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del a, b
+    return {"device": props.name, "compute_units": cus, "mfma_loop_tflops": round(mfma_tflops, 1),
+            "hbm_copy_gbps": round(copy_gbps, 1),
+            "note": "mfma_loop: register-only bf16 MFMA loop on every CU; hbm_copy: read+write bytes of a "
+                    "2 GiB device copy"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -153,15 +188,18 @@ def main():
         if dominant:
             sess.trace_enable(dominant)
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps (on the library's stream): the
+    # mean over the K steps is ms_per_step; median and min come from the
+    # per-step intervals
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     loss, bpb = out.cpu().numpy()[:2]
     grads_finite = bool(torch.isfinite(G).all().item())
     tok_s = N / (ms * 1e-3)
@@ -178,6 +216,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "ms_per_step_median": round(per_step[len(per_step) // 2] if len(per_step) % 2
+                                    else 0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2]), 3),
+        "ms_per_step_min": round(per_step[0], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -222,6 +263,11 @@ def main():
         }
         result["kernel_families"] = families
     del P, G
+    if not args.no_roofline:
+        result["measured_peaks"] = measured_peaks(torch, nc, stream)
+        if "roofline" in result:
+            result["roofline"]["frac_of_measured_mfma"] = round(
+                result["roofline"]["achieved"] / result["measured_peaks"]["mfma_loop_tflops"], 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, params, idx, tgt, tb, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)

@@ -35,4 +35,41 @@ hipError_t gemm_mfma_bf16(const GemmDesc& g, hipStream_t s) {
   return e;
 }
 
+namespace {
+// Matrix-core throughput probe: every wave issues `iters` rounds of eight
+// independent v_mfma_f32_32x32x16_bf16 on register operands -- no memory
+// traffic, no dependence between the rounds' products beyond each
+// accumulator's own chain -- so the rate it reaches is what the matrix
+// cores sustain at the clock the chip holds under that load.  Each thread
+// writes the sum of its accumulators to sink, which keeps the work live.
+__global__ void __launch_bounds__(256) k_mfma_loop(int64_t iters, float* sink) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float floatx16 __attribute__((ext_vector_type(16)));
+  const int tid = threadIdx.x;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)((float)((tid + e) & 31) * 0.001f);
+    b[e] = (__bf16)((float)((tid ^ e) & 31) * 0.001f);
+  }
+  floatx16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = floatx16{};
+  for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  sink[(int64_t)blockIdx.x * 256 + tid] = s;
+}
+}  // namespace
+
+hipError_t mfma_loop(int64_t iters, int blocks, float* sink, hipStream_t s) {
+  k_mfma_loop<<<blocks, 256, 0, s>>>(iters, sink);
+  return hipGetLastError();
+}
+
 }  // namespace nc

@@ -97,6 +97,8 @@ bool gemm_mfma_supported(const GemmDesc& g);
 int gemm_mfma_tile_m(int M, int N);   // tile sizes the MFMA GEMM picks for an M x N output
 int gemm_mfma_tile_n(int M, int N);
 hipError_t splitk_reduce(const float* part, int splits, int64_t n, float* out, int beta, hipStream_t s);
+// blocks x 4 waves x iters x 8 products of 32x32x16 (bf16) on registers only
+hipError_t mfma_loop(int64_t iters, int blocks, float* sink, hipStream_t s);
 
 template <typename T> hipError_t attn_fwd_portable(const AttnDesc& a, hipStream_t s);
 template <typename T> hipError_t attn_bwd_portable(const AttnDesc& a, hipStream_t s);

@@ -73,6 +73,12 @@ int nc_op_rmsnorm_bwd(int32_t dtype, int64_t rows, int32_t d, const void* y, con
                                            accumulate ? 1 : 0, s));
 }
 
+int nc_op_mfma_loop(int64_t iters, int32_t blocks, float* sink, void* hip_stream) {
+  if (!sink) return NC_ERR_INVALID_ARG;
+  if (iters < 1 || blocks < 1 || blocks > (1 << 20)) return NC_ERR_SHAPE;
+  return status_of(mfma_loop(iters, blocks, sink, (hipStream_t)hip_stream));
+}
+
 int nc_op_rope_table(int32_t T, int32_t Q, float base, float* tab, void* hip_stream) {
   if (!tab) return NC_ERR_INVALID_ARG;
   if (T <= 0 || Q <= 0 || Q % 2) return NC_ERR_SHAPE;

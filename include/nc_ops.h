@@ -48,6 +48,16 @@ int nc_op_rmsnorm_fwd(int32_t dtype, int64_t rows, int32_t d, float eps, const v
 int nc_op_rmsnorm_bwd(int32_t dtype, int64_t rows, int32_t d, const void* y, const float* r, const void* dy,
                       void* dx_io, int32_t accumulate, void* hip_stream);
 
+/* Matrix-core throughput probe (not part of the training step): `blocks`
+ * workgroups of 4 waves each issue `iters` rounds of 8 independent
+ * v_mfma_f32_32x32x16_bf16 on register operands, i.e.
+ * blocks * 4 * iters * 8 * 32768 FLOP with no memory traffic, so its rate
+ * is the bf16 matrix throughput the chip sustains under that load (the
+ * clock it holds), a measured counterpart of the 2.5 PFLOP/s dense peak.
+ *   sink  fp32 [blocks * 256], one value per thread (keeps the work live).
+ * iters >= 1, 1 <= blocks <= 2^20. */
+int nc_op_mfma_loop(int64_t iters, int32_t blocks, float* sink, void* hip_stream);
+
 /* Rotary table tab[t][i] = (cos, sin)(t * base^(-2i/Q)), fp32 [T][Q/2][2],
  * computed in fp64 and rounded once. */
 int nc_op_rope_table(int32_t T, int32_t Q, float base, float* tab, void* hip_stream);

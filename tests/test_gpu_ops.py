@@ -286,3 +286,18 @@ def test_head_ce_forward(dtype, portable, n, d, V):
     np.testing.assert_allclose(host(ce), want, rtol=1e-5, atol=2e-5)
     np.testing.assert_allclose(host(lse), logsumexp(z, axis=1), rtol=1e-5, atol=2e-5)
     assert host(ce)[5] == 0.0
+
+
+def test_mfma_loop_probe_runs_every_round():
+    """The throughput probe behind bench.py's measured MFMA peak: each
+    thread's sink value is a sum of `iters` identical rounds of products,
+    so doubling iters doubles it (to fp32 rounding), and it is finite and
+    non-zero."""
+    blocks = 8
+    s1, s2 = empty((blocks * 256,), "f32"), empty((blocks * 256,), "f32")
+    nc.ops.mfma_loop(100, blocks, s1, None)
+    nc.ops.mfma_loop(200, blocks, s2, None)
+    torch.cuda.synchronize()
+    a, b = host(s1), host(s2)
+    assert np.all(np.isfinite(a)) and np.all(a > 0)
+    np.testing.assert_allclose(b, 2 * a, rtol=1e-5)
