@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roofline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--mfma-calibration", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     return ap.parse_args()
 
@@ -93,6 +94,19 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
 
 
+def mfma_loop_tflops(torch, nc, stream, iters=4000):
+    """bf16 TFLOP/s of nc_op_mfma_loop with one block (4 waves) per CU."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sink = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    nc.ops.mfma_loop(iters, cus, sink, stream.cuda_stream)               # warm-up
+    ev0.record(stream)
+    nc.ops.mfma_loop(iters, cus, sink, stream.cuda_stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return round(cus * 4 * iters * 8 * 32768 / (ev0.elapsed_time(ev1) * 1e-3) / 1e12, 1)
+
+
 def measured_peaks(torch, nc, stream):
     """What the chip sustains on this machine, next to the spec peaks: the bf16
     matrix-core rate of a register-only MFMA loop (nc_op_mfma_loop: 8
@@ -100,15 +114,8 @@ def measured_peaks(torch, nc, stream):
     read+write bandwidth of a 2 GiB device-to-device copy."""
     props = torch.cuda.get_device_properties(0)
     cus = props.multi_processor_count
+    mfma_tflops = mfma_loop_tflops(torch, nc, stream)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    sink = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
-    iters = 4000
-    nc.ops.mfma_loop(iters, cus, sink, stream.cuda_stream)               # warm-up
-    ev0.record(stream)
-    nc.ops.mfma_loop(iters, cus, sink, stream.cuda_stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    mfma_tflops = cus * 4 * iters * 8 * 32768 / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
     n = 2 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     a.fill_(1)
@@ -122,7 +129,7 @@ def measured_peaks(torch, nc, stream):
     torch.cuda.synchronize()
     copy_gbps = 3 * 2 * n / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
     del a, b
-    return {"device": props.name, "compute_units": cus, "mfma_loop_tflops": round(mfma_tflops, 1),
+    return {"device": props.name, "compute_units": cus, "mfma_loop_tflops": mfma_tflops,
             "hbm_copy_gbps": round(copy_gbps, 1),
             "note": "mfma_loop: register-only bf16 MFMA loop on every CU; hbm_copy: read+write bytes of a "
                     "2 GiB device copy"}
@@ -136,6 +143,11 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.mfma_calibration:
+        import torch
+        import decoder_only_transformer_d20_amd as nc
+        print(json.dumps({"mfma_loop_tflops": mfma_loop_tflops(torch, nc, torch.cuda.current_stream())}))
         return
     import numpy as np
     import torch

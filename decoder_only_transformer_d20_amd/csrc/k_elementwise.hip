@@ -201,6 +201,29 @@ struct RowAcc {
       }
     }
   }
+  // add_f32 split in two, so that several rows' loads can be in flight
+  // before the (ordered) additions
+  __device__ inline void load_f32(const float* row, int lane, int chunks, float (&v)[NCH][VN]) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + i * kWave;
+      if (c < chunks) {
+#pragma unroll
+        for (int e = 0; e < VN; e += 4) {
+          const float4 q = *reinterpret_cast<const float4*>(row + c * VN + e);
+          v[i][e] = q.x; v[i][e + 1] = q.y; v[i][e + 2] = q.z; v[i][e + 3] = q.w;
+        }
+      }
+    }
+  }
+  __device__ inline void add_vals(const float (&v)[NCH][VN], int lane, int chunks) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (lane + i * kWave < chunks) {
+#pragma unroll
+        for (int e = 0; e < VN; ++e) a[i][e] += v[i][e];
+      }
+  }
   // dst = a, or dst += a
   __device__ inline void store(float* dst, int lane, int chunks, bool add) const {
 #pragma unroll
@@ -270,13 +293,32 @@ __global__ void __launch_bounds__(256) k_embed_fix(const int32_t* __restrict__ s
   if (r1 >= n || sid[r1] != id || id >= V) return;               // the tile's last segment ends here
   if (sid[r0] == id && r0 > 0 && sid[r0 - 1] == id) return;      // it started in an earlier tile
   const int chunks = d / Vec<T>::n;
+  // The id's rows are contiguous in sid (sorted), so it continues into tile
+  // u exactly when tile u starts with it.  Tile + 1 does (checked above);
+  // the wave probes 64 further tile starts per round, one per lane -- the
+  // continuing tiles form a prefix -- instead of one dependent load per tile.
+  const int64_t ntile = (n + kEmbTile - 1) / kEmbTile;
+  int64_t ulast = tile + 1;                      // last tile holding the id
+  for (int64_t base = tile + 2;; base += kWave) {
+    const int64_t u = base + lane;
+    const bool cont = u < ntile && sid[u * kEmbTile] == id;
+    const int k = __popcll(__ballot(cont));
+    ulast = base - 1 + k;
+    if (k < kWave) break;
+  }
+  // Pl[tile] + Pf[tile+1] + ... + Pf[ulast], added in that order; the loads
+  // of four partial rows are issued before their additions.
   RowAcc<T, NCH> acc;
   acc.zero();
   acc.add_f32(Pl + tile * d, lane, chunks);
-  for (int64_t u = tile + 1;; ++u) {
-    acc.add_f32(Pf + u * d, lane, chunks);
-    const int64_t e = (u + 1) * kEmbTile < n ? (u + 1) * kEmbTile : n;
-    if (e >= n || sid[e] != id || sid[e - 1] != id) break;
+  constexpr int kAhead = 4;
+  for (int64_t u = tile + 1; u <= ulast; u += kAhead) {
+    float v[kAhead][NCH][RowAcc<T, NCH>::VN];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) acc.load_f32(Pf + (u + j <= ulast ? u + j : ulast) * d, lane, chunks, v[j]);
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j)
+      if (u + j <= ulast) acc.add_vals(v[j], lane, chunks);
   }
   acc.store(dE + (int64_t)id * d, lane, chunks, accumulate != 0);
 }
