@@ -23,7 +23,8 @@
  *   xf = rms(x);  z = xf U^T;  ce[t] = logsumexp(z[t]) - z[t, target[t]]
  *   rms(x) = x / sqrt(mean(x^2) + eps)
  *   loss = sum(ce) / n_valid;  bpb = sum(ce) / (ln 2 * sum(bytes[target]))
- * A target of -1 is ignored (no loss, no bytes, no gradient).
+ * A target of -1 is ignored (no loss, no bytes, no gradient).  With no
+ * valid target at all, loss and bpb are 0 and every gradient is 0.
  *
  * Conventions
  *  - Every pointer argument named as device memory must point to memory of

@@ -177,7 +177,8 @@ def loss_bpb(ce, tgt, token_bytes):
     s = float(np.sum(ce[valid]))
     nbytes = int(np.sum(np.asarray(token_bytes, dtype=np.int64)[tgt[valid]]))
     n = int(np.sum(valid))
-    return s / n, s / (LN2 * nbytes)
+    # no valid target: the mean over an empty set is taken as 0 (so is bpb)
+    return (s / n if n else 0.0), (s / (LN2 * nbytes) if nbytes else 0.0)
 
 
 # ---------------------------------------------------------------------------
@@ -288,7 +289,7 @@ def train_step(cfg, params, idx, tgt, token_bytes, want_grads=True, rows=None):
     tgt = np.asarray(tgt)
     B, T = idx.shape
     n_valid = int(np.sum(tgt >= 0))
-    scale = 1.0 / n_valid
+    scale = 1.0 / n_valid if n_valid else 0.0     # no valid target: zero loss, zero gradient
     phi = rope_angles(T, cfg.head_dim, cfg.rope_base)
     ce = np.zeros((B, T), dtype=np.float64)
     grads = zero_grads(p) if want_grads else None

@@ -76,6 +76,18 @@ def test_tiny_fp32_matches_oracle():
         assert max_rel_err(g, w) <= 1e-4, (name, layer, max_rel_err(g, w))
 
 
+def test_tiny_no_valid_target():
+    """Every target ignored: loss, bpb and every gradient are exactly 0 on
+    the GPU, as in the oracle (the mean over an empty set taken as 0)."""
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("tiny"))
+    tgt = np.full_like(tgt, -1)
+    got = _gpu_step(cfg, params, idx, tgt, tb)
+    want = _oracle_step(cfg, params, idx, tgt, tb)
+    assert want["loss"] == 0.0 and want["bpb"] == 0.0
+    np.testing.assert_array_equal(got["out"], np.zeros(5))
+    assert not np.any(got["grads"])
+
+
 def test_tiny_fp32_accumulate_doubles():
     cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("tiny"))
     sess = nc.Session(cfg)

@@ -313,6 +313,28 @@ def test_model_row_independence():
         np.testing.assert_allclose(a, b + c, rtol=1e-12, atol=1e-16)
 
 
+def test_ignored_targets_contribute_nothing():
+    """A row whose targets are all ignored adds no loss and no gradient: the
+    batch gradient equals the other row's part (same n_valid), exactly.  With
+    no valid target anywhere the mean over the empty set is 0 and so is every
+    gradient."""
+    cfg = MICRO
+    _, p = _micro_params()
+    idx, tgt = synthdata.make_tokens(cfg)
+    tb = synthdata.make_token_bytes(cfg)
+    tgt = tgt.copy()
+    tgt[1, :] = -1
+    full = oracle.train_step(cfg, p, idx, tgt, tb)
+    r0 = oracle.train_step(cfg, p, idx, tgt, tb, rows=[0])
+    for a, b in zip(_flat(full["grads"], cfg), _flat(r0["grads"], cfg)):
+        np.testing.assert_array_equal(a, b)
+    assert full["loss"] == pytest.approx(full["ce"][0].sum() / tgt.shape[1], rel=1e-15)
+    tgt[:] = -1
+    none = oracle.train_step(cfg, p, idx, tgt, tb)
+    assert none["loss"] == 0.0 and none["bpb"] == 0.0
+    assert all(not np.any(g) for g in _flat(none["grads"], cfg))
+
+
 def _flat(grads, cfg):
     out = []
     for name, layer, r, c, off in synthdata.param_layout(cfg):
