@@ -535,6 +535,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
       int pi = 0;
       if constexpr (EPI == EPI_ROPE) pi = (int)(n % g.head_dim) >> 1;
       const bool rot = EPI == EPI_ROPE && n < g.rope_cols;
+      const bool tile_rot = EPI == EPI_ROPE && c.n0 < g.rope_cols;   // uniform over the block
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // The pass's global inputs (aux rows, rotary factors, per-row loss
@@ -555,8 +556,13 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
           if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2)
             pa[k % W] = *reinterpret_cast<const uint2*>((const bf16*)g.aux + m * g.ldaux + n);
           if constexpr (EPI == EPI_ROPE) {
-            const uint32_t t = (tpos + (uint32_t)(k * RPS)) % (uint32_t)g.rope_T;
-            pc[k % W] = *reinterpret_cast<const float4*>(g.rope + t * (uint32_t)(g.head_dim >> 1) + pi);
+            // a tile with no rotated column (v) reads no rotary factors
+            if (tile_rot) {
+              const uint32_t t = (tpos + (uint32_t)(k * RPS)) % (uint32_t)g.rope_T;
+              pc[k % W] = *reinterpret_cast<const float4*>(g.rope + t * (uint32_t)(g.head_dim >> 1) + pi);
+            } else {
+              pc[k % W] = make_float4(1.f, 0.f, 1.f, 0.f);
+            }
           }
           if constexpr (EPI == EPI_DZ) {
             pt[k % W] = g.tgt[m];
