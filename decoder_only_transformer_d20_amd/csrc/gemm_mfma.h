@@ -155,7 +155,7 @@ struct GemmTile {
 // [i nkt/splits, (i+1) nkt/splits).
 template <int BM, int BN>
 struct TileMap {
-  static constexpr int kGroupM = 8;
+  static constexpr int kGroupM = 8, kNarrow = 8;
   int ntn, ntm, ntiles, total, nkt, G, chunk, splits;
   __device__ inline TileMap(const GemmDesc& g) {
     ntn = g.N / BN;
@@ -182,8 +182,12 @@ struct TileMap {
     const int first_m = (t / (kGroupM * ntn)) * kGroupM;
     const int gm = min(kGroupM, ntm - first_m);
     const int tg = t - first_m * ntn;
-    c.tn = tg / gm;
-    c.m0 = (int64_t)(first_m + tg % gm) * BM;
+    // narrow products (few n-tiles): n fastest, so the blocks an XCD runs
+    // at once cover whole rows of tiles and each P panel is fetched once;
+    // wide ones: m fastest, so each Q panel serves gm blocks
+    const bool nfast = ntn <= kNarrow;
+    c.tn = nfast ? tg % ntn : tg / gm;
+    c.m0 = (int64_t)(first_m + (nfast ? tg / ntn : tg % gm)) * BM;
     c.n0 = (int64_t)c.tn * BN;
     const int kt0 = (int)((int64_t)c.split * nkt / splits);
     c.nk = (int)((int64_t)(c.split + 1) * nkt / splits) - kt0;
