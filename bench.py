@@ -43,8 +43,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 # scaled by the counters' reading for --copy-calibration (see profiles/).
 # Keyed by family; valid only for the recorded hash of the kernel source.
 TRAFFIC = {
-    # profiles/d20_step_hbm_traffic.md: 1.848 GB fetched + 0.134 GB written per dispatch
-    "gemm_wgrad": {"bytes_per_launch": 1981193942, "source_hash": "8562eb58d19405d4"},
+    # profiles/d20_step_hbm_traffic.md: 1.592 GB fetched + 0.134 GB written per dispatch
+    "gemm_wgrad": {"bytes_per_launch": 1725481629, "source_hash": "155091d0d9e78f12"},
 }
 
 
