@@ -112,8 +112,11 @@ def measured_peaks(torch, nc, stream):
     matrix-core rate of a register-only MFMA loop (nc_op_mfma_loop: 8
     independent 32x32x16 products per round, no memory traffic), and HBM
     read+write bandwidth of a 2 GiB device-to-device copy."""
+    import ctypes
     props = torch.cuda.get_device_properties(0)
-    cus = props.multi_processor_count
+    info = [ctypes.c_int32() for _ in range(4)]
+    nc.ops.device_info(torch.cuda.current_device(), *[ctypes.byref(x) for x in info])
+    hip_cus, clock_khz, mem_clock_khz, bus_bits = (x.value for x in info)
     mfma_tflops = mfma_loop_tflops(torch, nc, stream)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = 2 << 30
@@ -129,7 +132,12 @@ def measured_peaks(torch, nc, stream):
     torch.cuda.synchronize()
     copy_gbps = 3 * 2 * n / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
     del a, b
-    return {"device": props.name, "compute_units": cus, "mfma_loop_tflops": mfma_tflops,
+    # dense bf16 on CDNA4: 4096 FLOP per clock per CU, which gives the
+    # 2.5 PFLOP/s figure at 256 CUs and 2.4 GHz
+    return {"device": props.name, "compute_units": hip_cus, "peak_clock_mhz": clock_khz / 1000,
+            "bf16_dense_peak_at_peak_clock_tflops": round(hip_cus * 4096 * clock_khz * 1e3 / 1e12, 1),
+            "memory_clock_mhz": mem_clock_khz / 1000, "memory_bus_bits": bus_bits,
+            "mfma_loop_tflops": mfma_tflops,
             "hbm_copy_gbps": round(copy_gbps, 1),
             "note": "mfma_loop: register-only bf16 MFMA loop on every CU; hbm_copy: read+write bytes of a "
                     "2 GiB device copy"}

@@ -72,6 +72,7 @@ _SIGS = {
     "nc_op_rmsnorm_bwd": (ctypes.c_int, [_I32, _I64, _I32, _P, _P, _P, _P, _I32, _P]),
     "nc_op_rope_table": (ctypes.c_int, [_I32, _I32, _F32, _P, _P]),
     "nc_op_mfma_loop": (ctypes.c_int, [_I64, _I32, _P, _P]),
+    "nc_op_device_info": (ctypes.c_int, [_I32] + [ctypes.POINTER(_I32)] * 4),
     "nc_op_attention_fwd": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P]),
     "nc_op_attention_bwd": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
     "nc_op_embed_fwd": (ctypes.c_int, [_I32, _I64, _I32, _P, _P, _P, _P]),

@@ -73,6 +73,18 @@ int nc_op_rmsnorm_bwd(int32_t dtype, int64_t rows, int32_t d, const void* y, con
                                            accumulate ? 1 : 0, s));
 }
 
+int nc_op_device_info(int32_t device, int32_t* compute_units, int32_t* clock_khz, int32_t* mem_clock_khz,
+                      int32_t* mem_bus_bits) {
+  if (!compute_units || !clock_khz || !mem_clock_khz || !mem_bus_bits || device < 0) return NC_ERR_INVALID_ARG;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, device) != hipSuccess) return NC_ERR_HIP;
+  *compute_units = p.multiProcessorCount;
+  *clock_khz = p.clockRate;
+  *mem_clock_khz = p.memoryClockRate;
+  *mem_bus_bits = p.memoryBusWidth;
+  return NC_OK;
+}
+
 int nc_op_mfma_loop(int64_t iters, int32_t blocks, float* sink, void* hip_stream) {
   if (!sink) return NC_ERR_INVALID_ARG;
   if (iters < 1 || blocks < 1 || blocks > (1 << 20)) return NC_ERR_SHAPE;

@@ -58,6 +58,13 @@ int nc_op_rmsnorm_bwd(int32_t dtype, int64_t rows, int32_t d, const void* y, con
  * iters >= 1, 1 <= blocks <= 2^20. */
 int nc_op_mfma_loop(int64_t iters, int32_t blocks, float* sink, void* hip_stream);
 
+/* Properties of HIP device `device` (hipGetDeviceProperties): compute
+ * units, peak shader clock and memory clock (kHz), memory bus width (bits)
+ * -- the figures the spec peaks are derived from.  Host call: launches
+ * nothing, enqueues nothing. */
+int nc_op_device_info(int32_t device, int32_t* compute_units, int32_t* clock_khz, int32_t* mem_clock_khz,
+                      int32_t* mem_bus_bits);
+
 /* Rotary table tab[t][i] = (cos, sin)(t * base^(-2i/Q)), fp32 [T][Q/2][2],
  * computed in fp64 and rounded once. */
 int nc_op_rope_table(int32_t T, int32_t Q, float base, float* tab, void* hip_stream);

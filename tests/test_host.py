@@ -121,6 +121,7 @@ def test_ops_reject_bad_shapes_before_launch():
     assert L.nc_op_mfma_loop(0, 4, 1, None) == -2
     assert L.nc_op_mfma_loop(10, 0, 1, None) == -2
     assert L.nc_op_mfma_loop(10, 4, None, None) == -1
+    assert L.nc_op_device_info(0, None, None, None, None) == -1
     assert L.nc_op_embed_bwd_scratch_bytes(10, 64) > 0
     assert L.nc_op_embed_bwd(1, 10, 100, 50, 1, 1, 1, 0, 1, None) == -2
     assert L.nc_op_embed_bwd(1, 10, 64, 50, 1, 1, 1, 0, None, None) == -1
