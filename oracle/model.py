@@ -26,7 +26,8 @@ adjacent pairs (2i, 2i+1), angle t * base^(-2i/Q), base 10000, positions
 restarting at 0 in every row; attention scale 1/sqrt(Q) with a plain causal
 mask over the packed row; full multi-head attention; MLP relu(h)^2 of width
 4d; untied unembedding; mean cross-entropy over valid targets (target -1 is
-ignored); bits per byte = sum(ce) / (ln 2 * sum(bytes[target])).
+ignored), taken as 0 when no target is valid; bits per byte =
+sum(ce) / (ln 2 * sum(bytes[target])).
 
 Rows are independent (attention never crosses a row), so everything runs
 one row at a time and weight gradients are summed over rows in fp64.
