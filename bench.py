@@ -44,7 +44,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 # Keyed by family; valid only for the recorded hash of the kernel source.
 TRAFFIC = {
     # profiles/d20_step_hbm_traffic.md: 1.592 GB fetched + 0.134 GB written per dispatch
-    "gemm_wgrad": {"bytes_per_launch": 1725481629, "source_hash": "155091d0d9e78f12"},
+    "gemm_wgrad": {"bytes_per_launch": 1725484652, "source_hash": "49a479fc9c0bbf01"},
 }
 
 
@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-roofline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--mfma-calibration", action="store_true")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="time the vendor BLAS (torch.matmul) next to nc_op_matmul on the d20 product shapes")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     return ap.parse_args()
 
@@ -107,10 +109,82 @@ def mfma_loop_tflops(torch, nc, stream, iters=4000):
     return round(cus * 4 * iters * 8 * 32768 / (ev0.elapsed_time(ev1) * 1e-3) / 1e12, 1)
 
 
+def wgrad_splits(M, N, K, cus=256):
+    """The split-K count the library picks for a weight-gradient product:
+    the count minimising (compute at 1 PFLOP/s x wave quantisation) + the
+    fp32 partials' round trip at 5 TB/s, over 256 x 256 tiles."""
+    tiles = (M // 256) * (N // 256)
+    best_s, best = 1, None
+    for s in range(1, min(32, K // 64) + 1):
+        units = tiles * s
+        waves = -(-units // cus)
+        t = 2.0 * M * N * K / 1e15 * (waves * cus / units) + (s * 8.0 * M * N / 5e12 if s > 1 else 0.0)
+        if best is None or t < best * (1.0 - 1e-9):
+            best, best_s = t, s
+    return best_s
+
+
+def library_gemm(reps=10):
+    """TFLOP/s of the vendor BLAS (torch.matmul, bf16 in and out) and of
+    nc_op_matmul on the products of one d20 step (32 x 2048 tokens), same
+    operands and transposition.  nc's weight-gradient products write fp32
+    (split-K as in the step); the BLAS writes bf16, which only favours it.
+    The step's own kernels also fuse epilogues (rotary, relu^2, residual,
+    log-sum-exp) that these plain products leave out."""
+    import torch
+    import decoder_only_transformer_d20_amd as nc
+    stream = torch.cuda.current_stream()
+    T, d, F, V = 32 * 2048, 1280, 5120, 65536
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rnd = lambda *shape: (torch.randn(*shape, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+    # (name, M, N, K, p_trans, q_trans, out_f32) in C[m][n] = sum_k P[m][k] Q[n][k]
+    shapes = [("fwd qkv", T, 3 * d, d, 0, 0, 0), ("fwd attn-out", T, d, d, 0, 0, 0),
+              ("fwd mlp-up", T, F, d, 0, 0, 0), ("fwd mlp-down", T, d, F, 0, 0, 0),
+              ("fwd head", T, V, d, 0, 0, 0),
+              ("dgrad qkv", T, d, 3 * d, 0, 1, 0), ("dgrad mlp-up", T, d, F, 0, 1, 0),
+              ("dgrad mlp-down", T, F, d, 0, 1, 0), ("dgrad head", T, d, V, 0, 1, 0),
+              ("wgrad qkv", 3 * d, d, T, 1, 1, 1), ("wgrad attn-out", d, d, T, 1, 1, 1),
+              ("wgrad mlp-up", F, d, T, 1, 1, 1), ("wgrad mlp-down", d, F, T, 1, 1, 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        fn()
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    rows = []
+    for name, M, N, K, pt, qt, f32 in shapes:
+        P = rnd(K, M) if pt else rnd(M, K)
+        Q = rnd(K, N) if qt else rnd(N, K)
+        s = wgrad_splits(M, N, K) if f32 else 1
+        C = torch.empty(M, N, dtype=torch.float32 if f32 else torch.bfloat16, device="cuda")
+        part = torch.empty(s * M * N if s > 1 else 1, dtype=torch.float32, device="cuda")
+        Pm = P.t() if pt else P                   # [M][K] view
+        Qm = Q if qt else Q.t()                   # [K][N] view
+        ms_nc = timed(lambda: nc.ops.matmul(nc.DTYPE_BF16, pt, qt, M, N, K, P, Q, C, f32, s, part, 0,
+                                            stream.cuda_stream))
+        ms_lib = timed(lambda: torch.matmul(Pm, Qm))
+        ref = torch.matmul(Pm, Qm).float()
+        err = ((C.float() - ref).abs().max() / ref.abs().max()).item()
+        fl = 2.0 * M * N * K
+        rows.append({"product": name, "M": M, "N": N, "K": K, "splits": s,
+                     "nc_tflops": round(fl / (ms_nc * 1e-3) / 1e12, 1),
+                     "blas_tflops": round(fl / (ms_lib * 1e-3) / 1e12, 1),
+                     "nc_over_blas": round(ms_lib / ms_nc, 3), "max_rel_diff": float(f"{err:.2e}")})
+        print(f"[library-gemm] {rows[-1]}", file=sys.stderr, flush=True)
+        del P, Q, C, part, ref
+    blas = getattr(torch.backends.cuda, "preferred_blas_library", lambda: None)()
+    print(json.dumps({"library_gemm": rows, "blas": str(blas), "reps": reps}), flush=True)
+
+
 def measured_peaks(torch, nc, stream):
     """What the chip sustains on this machine, next to the spec peaks: the bf16
     matrix-core rate of a register-only MFMA loop (nc_op_mfma_loop: 8
-    independent 32x32x16 products per round, no memory traffic), and HBM
+    independent 32x32x16 products per iteration, no memory traffic), and HBM
     read+write bandwidth of a 2 GiB device-to-device copy."""
     import ctypes
     props = torch.cuda.get_device_properties(0)
@@ -151,6 +225,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.library_gemm:
+        library_gemm()
         return
     if args.mfma_calibration:
         import torch

@@ -295,7 +295,7 @@ __global__ void __launch_bounds__(256) k_embed_fix(const int32_t* __restrict__ s
   const int chunks = d / Vec<T>::n;
   // The id's rows are contiguous in sid (sorted), so it continues into tile
   // u exactly when tile u starts with it.  Tile + 1 does (checked above);
-  // the wave probes 64 further tile starts per round, one per lane -- the
+  // the wave probes 64 further tile starts per step, one per lane -- the
   // continuing tiles form a prefix -- instead of one dependent load per tile.
   const int64_t ntile = (n + kEmbTile - 1) / kEmbTile;
   int64_t ulast = tile + 1;                      // last tile holding the id

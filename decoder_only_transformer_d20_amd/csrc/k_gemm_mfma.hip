@@ -36,9 +36,9 @@ hipError_t gemm_mfma_bf16(const GemmDesc& g, hipStream_t s) {
 }
 
 namespace {
-// Matrix-core throughput probe: every wave issues `iters` rounds of eight
+// Matrix-core throughput probe: every wave issues `iters` iterations of eight
 // independent v_mfma_f32_32x32x16_bf16 on register operands -- no memory
-// traffic, no dependence between the rounds' products beyond each
+// traffic, no dependence between the iterations' products beyond each
 // accumulator's own chain -- so the rate it reaches is what the matrix
 // cores sustain at the clock the chip holds under that load.  Each thread
 // writes the sum of its accumulators to sink, which keeps the work live.

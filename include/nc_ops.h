@@ -49,7 +49,7 @@ int nc_op_rmsnorm_bwd(int32_t dtype, int64_t rows, int32_t d, const void* y, con
                       void* dx_io, int32_t accumulate, void* hip_stream);
 
 /* Matrix-core throughput probe (not part of the training step): `blocks`
- * workgroups of 4 waves each issue `iters` rounds of 8 independent
+ * workgroups of 4 waves each issue `iters` iterations of 8 independent
  * v_mfma_f32_32x32x16_bf16 on register operands, i.e.
  * blocks * 4 * iters * 8 * 32768 FLOP with no memory traffic, so its rate
  * is the bf16 matrix throughput the chip sustains under that load (the

@@ -288,9 +288,9 @@ def test_head_ce_forward(dtype, portable, n, d, V):
     assert host(ce)[5] == 0.0
 
 
-def test_mfma_loop_probe_runs_every_round():
+def test_mfma_loop_probe_runs_every_iteration():
     """The throughput probe behind bench.py's measured MFMA peak: each
-    thread's sink value is a sum of `iters` identical rounds of products,
+    thread's sink value is a sum of `iters` identical iterations of products,
     so doubling iters doubles it (to fp32 rounding), and it is finite and
     non-zero."""
     blocks = 8
