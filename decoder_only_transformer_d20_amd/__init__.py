@@ -15,6 +15,7 @@ __all__ = [
     "lib", "NcConfig", "NcError", "Context", "Session", "make_config", "param_count",
     "param_offset", "workspace_bytes", "status_string", "ops", "LIB_PATH",
     "DTYPE_F32", "DTYPE_BF16", "FLAG_BLOCK_ONLY", "FLAG_PORTABLE_KERNELS",
+    "NcOptimHparams", "optim_default", "optim_state_bytes", "optim_scratch_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnc.so")
@@ -26,6 +27,8 @@ TENSOR_IDS = {"E": 0, "Wq": 1, "Wk": 2, "Wv": 3, "Wo": 4, "W1": 5, "W2": 6, "U":
 TRACE_FAMILIES = ["gemm_qkv_rope", "gemm_residual", "gemm_relu2", "gemm_head_lse", "gemm_head_dz", "gemm_dgrad",
                   "gemm_dgrad_relu2", "gemm_wgrad", "attn_fwd", "attn_bwd"]
 SINGLE_KERNEL_FAMILIES = TRACE_FAMILIES[:-1]
+# NC_TRACE_OPTIM_*: launches inside nc_optimizer_step
+OPTIM_TRACE_FAMILIES = ["optim_ns", "optim_adamw"]
 
 
 class NcConfig(ctypes.Structure):
@@ -34,6 +37,17 @@ class NcConfig(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("vocab", ctypes.c_int32),
         ("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("rope_base", ctypes.c_float),
         ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+    ]
+
+
+class NcOptimHparams(ctypes.Structure):
+    """nc_optim_hparams (include/nc.h)."""
+    _fields_ = [
+        ("grad_scale", ctypes.c_float), ("lr_embed", ctypes.c_float), ("lr_unembed", ctypes.c_float),
+        ("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+        ("weight_decay", ctypes.c_float), ("adam_step", ctypes.c_int32), ("lr_matrix", ctypes.c_float),
+        ("momentum", ctypes.c_float), ("nesterov", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
+        ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
     ]
 
 
@@ -54,6 +68,10 @@ _SIGS = {
     "nc_param_offset": (ctypes.c_int, [ctypes.POINTER(NcConfig), _I32, _I32, ctypes.POINTER(_I64),
                                        ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "nc_workspace_bytes": (_I64, [ctypes.POINTER(NcConfig)]),
+    "nc_optim_default": (ctypes.c_int, [ctypes.POINTER(NcConfig), _I64, _I64, _I32, ctypes.POINTER(NcOptimHparams)]),
+    "nc_optim_state_bytes": (_I64, [ctypes.POINTER(NcConfig)]),
+    "nc_optim_scratch_bytes": (_I64, [ctypes.POINTER(NcConfig)]),
+    "nc_optimizer_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(NcOptimHparams)]),
     "nc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nc_init": (ctypes.c_int, [ctypes.POINTER(NcConfig), _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
     "nc_set_stream": (ctypes.c_int, [_P, _P]),
@@ -146,6 +164,26 @@ def workspace_bytes(cfg) -> int:
     return n
 
 
+def optim_default(cfg, it: int, num_iters: int, n_micro: int = 1) -> NcOptimHparams:
+    """nc_optim_default: the step's default hyperparameters (host-only)."""
+    h = NcOptimHparams()
+    _check(lib().nc_optim_default(ctypes.byref(_c(cfg)), int(it), int(num_iters), int(n_micro), ctypes.byref(h)),
+           "nc_optim_default")
+    return h
+
+
+def optim_state_bytes(cfg) -> int:
+    n = lib().nc_optim_state_bytes(ctypes.byref(_c(cfg)))
+    _check(0 if n >= 0 else n, "nc_optim_state_bytes")
+    return n
+
+
+def optim_scratch_bytes(cfg) -> int:
+    n = lib().nc_optim_scratch_bytes(ctypes.byref(_c(cfg)))
+    _check(0 if n >= 0 else n, "nc_optim_scratch_bytes")
+    return n
+
+
 def _ptr(x):
     if x is None:
         return None
@@ -188,7 +226,8 @@ class Context:
     def trace_enable(self, family):
         """Time launches of one kernel family (a name from TRACE_FAMILIES or
         its index; None disables)."""
-        f = -1 if family is None else (TRACE_FAMILIES.index(family) if isinstance(family, str) else int(family))
+        names = TRACE_FAMILIES + OPTIM_TRACE_FAMILIES
+        f = -1 if family is None else (names.index(family) if isinstance(family, str) else int(family))
         _check(lib().nc_trace_enable(self.h, f), "nc_trace_enable", self.h)
 
     def trace_read(self):
@@ -197,6 +236,11 @@ class Context:
         _check(lib().nc_trace_read(self.h, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(by)),
                "nc_trace_read", self.h)
         return n.value, ms.value, fl.value, by.value
+
+    def optimizer_step(self, master, params, grads, state, scratch, hparams: NcOptimHparams):
+        """nc_optimizer_step: AdamW on E and U, Muon on every block matrix."""
+        _check(lib().nc_optimizer_step(self.h, _ptr(master), _ptr(params), _ptr(grads), _ptr(state), _ptr(scratch),
+                                       ctypes.byref(hparams)), "nc_optimizer_step", self.h)
 
     def block_forward(self, params, x, y):
         _check(lib().nc_block_forward(self.h, _ptr(params), _ptr(x), _ptr(y)), "nc_block_forward", self.h)

@@ -228,10 +228,15 @@ __device__ inline void epi_store4(const GemmDesc& g, const GemmTile& c, int64_t 
     x[2] = x2 * c1 - x3 * s1;
     x[3] = x2 * s1 + x3 * c1;
   }
-  if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2) {
+  if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_AXPBY) {
     const float a0 = bf_lo(y.x), a1 = bf_hi(y.x), a2 = bf_lo(y.y), a3 = bf_hi(y.y);
     if constexpr (EPI == EPI_RESID) {
       x[0] += a0; x[1] += a1; x[2] += a2; x[3] += a3;
+    } else if constexpr (EPI == EPI_AXPBY) {
+      x[0] = g.ep_alpha * x[0] + g.ep_gamma * a0;
+      x[1] = g.ep_alpha * x[1] + g.ep_gamma * a1;
+      x[2] = g.ep_alpha * x[2] + g.ep_gamma * a2;
+      x[3] = g.ep_alpha * x[3] + g.ep_gamma * a3;
     } else {
       // aux = relu(h)^2, so 2 relu(h) = 2 sqrt(aux)
       x[0] *= 2.f * __builtin_sqrtf(fmaxf(a0, 0.f));
@@ -253,12 +258,13 @@ __device__ inline void epi_store4(const GemmDesc& g, const GemmTile& c, int64_t 
   // Non-temporal stores keep the streamed-out product from displacing the
   // operand panels in the caches (measured: 1-2 % on most products).  The
   // 2 sqrt(u) gradient, whose aux input streams in beside it, measured
-  // slower that way and keeps the plain store.
+  // slower that way and keeps the plain store, as does the linear
+  // combination, whose small outputs are the next product's operands.
   u32x2 w;
   w.x = pack2(x[0], x[1]);
   w.y = pack2(x[2], x[3]);
   u32x2* dst = reinterpret_cast<u32x2*>((bf16*)g.C + m * g.ldc + n);
-  if constexpr (EPI == EPI_DRELU2) *dst = w;
+  if constexpr (EPI == EPI_DRELU2 || EPI == EPI_AXPBY) *dst = w;
   else __builtin_nontemporal_store(w, dst);
 }
 
@@ -567,7 +573,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
         if constexpr (EPI == EPI_ROPE) tpos = (uint32_t)((c.m0 + h * WTM + r0) % g.rope_T);
         auto fetch = [&](int k) {
           const int64_t m = c.m0 + h * WTM + r0 + k * RPS;
-          if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2)
+          if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_AXPBY)
             pa[k % W] = *reinterpret_cast<const uint2*>((const bf16*)g.aux + m * g.ldaux + n);
           if constexpr (EPI == EPI_ROPE) {
             // a tile with no rotated column (v) reads no rotary factors
@@ -668,7 +674,9 @@ hipError_t launch(const GemmDesc& g, hipStream_t s) {
   X(0, 0, EPI_LSE)            \
   X(0, 0, EPI_DZ)             \
   X(0, 0, EPI_F32)            \
+  X(0, 0, EPI_AXPBY)          \
   X(0, 1, EPI_STORE)          \
+  X(0, 1, EPI_AXPBY)          \
   X(0, 1, EPI_F32)            \
   X(1, 0, EPI_STORE)          \
   X(1, 0, EPI_F32)            \

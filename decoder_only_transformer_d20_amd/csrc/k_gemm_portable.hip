@@ -110,6 +110,12 @@ __global__ void __launch_bounds__(256) k_gemm_portable(GemmDesc g) {
         for (int j = 0; j < 4; ++j) v[j] *= 2.f * sqrtf(fmaxf(to_f32(a[j]), 0.f));
         break;
       }
+      case EPI_AXPBY: {
+        const T* a = (const T*)g.aux + m * g.ldaux + n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = g.ep_alpha * v[j] + g.ep_gamma * to_f32(a[j]);
+        break;
+      }
       case EPI_RELU2:
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = fmaxf(v[j], 0.f) * fmaxf(v[j], 0.f);

@@ -226,7 +226,8 @@ double gemm_bytes(const GemmDesc& g, size_t es) {
     case EPI_LSE: b += M * 4.0 * 2; break;                       // targets in, z[target] out
     case EPI_DZ: b += M * N * es + M * 8.0; break;
     case EPI_RESID:
-    case EPI_DRELU2: b += 2.0 * M * N * es; break;
+    case EPI_DRELU2:
+    case EPI_AXPBY: b += 2.0 * M * N * es; break;
     default: b += M * N * es; break;
   }
   return b;
@@ -256,10 +257,11 @@ hipError_t traced(nc_ctx* ctx, int family, double flops, double bytes, F&& launc
   return hipSuccess;
 }
 
-hipError_t run_gemm(nc_ctx* ctx, const GemmDesc& g) {
+// family < -1: the forward/backward family of the product's layout and epilogue
+hipError_t run_gemm(nc_ctx* ctx, const GemmDesc& g, int family = -2) {
   if (!is_bf16(ctx->cfg)) return gemm_portable<float>(g, ctx->stream);
   if (portable(ctx->cfg) || !gemm_mfma_supported(g)) return gemm_portable<bf16>(g, ctx->stream);
-  hipError_t e = traced(ctx, gemm_family(g), 2.0 * g.M * g.N * g.K, gemm_bytes(g, 2),
+  hipError_t e = traced(ctx, family < -1 ? gemm_family(g) : family, 2.0 * g.M * g.N * g.K, gemm_bytes(g, 2),
                         [&] { return gemm_mfma_bf16_product(g, ctx->stream); });
   if (e == hipSuccess && g.epi == EPI_F32 && g.splits > 1)
     e = splitk_reduce(g.part, g.splits, (int64_t)g.M * g.N, (float*)g.C, g.beta, ctx->stream);
@@ -516,6 +518,146 @@ int block_backward(nc_ctx* ctx, const T* w, const T* dy, T* dx, float* dparams, 
   return layer_backward<T>(ctx, 0, w, dx, dparams, accumulate);
 }
 
+// ---- optimiser step ------------------------------------------------------------
+struct OptimTensor {
+  int tensor, layer;
+  int64_t off, rows, cols;
+};
+
+std::vector<OptimTensor> optim_tensors(const nc_config& c) {
+  std::vector<OptimTensor> v;
+  const int64_t d = c.d_model, F = c.d_ff, V = c.vocab;
+  const int64_t base = is_block(c) ? 0 : V * d;
+  if (!is_block(c)) v.push_back({NC_T_E, -1, 0, V, d});
+  const int64_t sizes[6][2] = {{d, d}, {d, d}, {d, d}, {d, d}, {F, d}, {d, F}};
+  for (int l = 0; l < c.n_layer; ++l) {
+    int64_t off = base + layer_elems(c) * l;
+    for (int t = 0; t < 6; ++t) {
+      v.push_back({NC_T_WQ + t, l, off, sizes[t][0], sizes[t][1]});
+      off += sizes[t][0] * sizes[t][1];
+    }
+  }
+  if (!is_block(c)) v.push_back({NC_T_U, -1, base + layer_elems(c) * c.n_layer, V, d});
+  return v;
+}
+
+int64_t param_count_of(const nc_config& c) {
+  return (is_block(c) ? 0 : 2 * (int64_t)c.vocab * c.d_model) + layer_elems(c) * c.n_layer;
+}
+
+// scratch: Muon partial sums | X (two, ping-pong) | A | B, each 256-aligned
+struct OptimScratch {
+  size_t partials = 0, x0 = 0, x1 = 0, a = 0, b = 0, total = 0;
+};
+
+OptimScratch optim_scratch(const nc_config& c) {
+  int64_t max_rc = 0, max_short = 0;
+  for (const OptimTensor& t : optim_tensors(c)) {
+    if (t.tensor == NC_T_E || t.tensor == NC_T_U) continue;
+    max_rc = std::max(max_rc, t.rows * t.cols);
+    max_short = std::max(max_short, std::min(t.rows, t.cols));
+  }
+  const size_t es = esize(c);
+  OptimScratch o;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t r = off; off += align_up(bytes); return r; };
+  o.partials = take(kMuonMaxPartials * 4);
+  o.x0 = take(max_rc * es);
+  o.x1 = take(max_rc * es);
+  o.a = take(max_short * max_short * es);
+  o.b = take(max_short * max_short * es);
+  o.total = off;
+  return o;
+}
+
+bool hp_ok(const nc_optim_hparams* h) {
+  auto fin = [](float x) { return std::isfinite(x); };
+  if (!fin(h->grad_scale) || !fin(h->lr_embed) || !fin(h->lr_unembed) || !fin(h->lr_matrix) ||
+      !fin(h->weight_decay) || !fin(h->ns_a) || !fin(h->ns_b) || !fin(h->ns_c))
+    return false;
+  if (!(h->beta1 >= 0.f && h->beta1 < 1.f) || !(h->beta2 >= 0.f && h->beta2 < 1.f)) return false;
+  if (!(h->eps >= 0.f) || !fin(h->eps) || h->adam_step < 1) return false;
+  if (!(h->momentum >= 0.f && h->momentum < 1.f)) return false;
+  if (h->nesterov != 0 && h->nesterov != 1) return false;
+  if (h->ns_steps < 0 || h->ns_steps > 100) return false;
+  return true;
+}
+
+// AdamW on E or U: p, m at the tensor's parameter offset; v after the
+// parameter-sized region (E's first, then U's)
+template <typename T>
+hipError_t optim_adamw(nc_ctx* ctx, const OptimTensor& t, float* master, T* params, const float* grads, float* state,
+                       const nc_optim_hparams* h) {
+  const nc_config& c = ctx->cfg;
+  const int64_t n = t.rows * t.cols;
+  const double lr = t.tensor == NC_T_E ? h->lr_embed : h->lr_unembed;
+  AdamwArgs a;
+  a.grad_scale = h->grad_scale;
+  a.beta1 = h->beta1;
+  a.beta2 = h->beta2;
+  a.decay = (float)(1.0 - lr * h->weight_decay);
+  a.lr = (float)lr;
+  a.inv_bc1 = (float)(1.0 / (1.0 - std::pow((double)h->beta1, (double)h->adam_step)));
+  a.inv_bc2 = (float)(1.0 / (1.0 - std::pow((double)h->beta2, (double)h->adam_step)));
+  a.eps = h->eps;
+  float* v = state + param_count_of(c) + (t.tensor == NC_T_E ? 0 : n);
+  return traced(ctx, NC_TRACE_OPTIM_ADAMW, 0.0, 30.0 * (double)n, [&] {
+    return adamw<T>(n, master + t.off, grads + t.off, state + t.off, v, params + t.off, a, ctx->stream);
+  });
+}
+
+// Muon on one matrix
+template <typename T>
+hipError_t optim_muon(nc_ctx* ctx, const OptimTensor& t, float* master, T* params, const float* grads, float* state,
+                      char* scratch, const OptimScratch& sc, const nc_optim_hparams* h) {
+  const int r = (int)t.rows, c = (int)t.cols;
+  const int rw = std::min(r, c), cw = std::max(r, c);   // wide orientation [rw][cw]
+  float* partials = reinterpret_cast<float*>(scratch + sc.partials);
+  T* X = reinterpret_cast<T*>(scratch + sc.x0);
+  T* Xn = reinterpret_cast<T*>(scratch + sc.x1);
+  T* A = reinterpret_cast<T*>(scratch + sc.a);
+  T* B = reinterpret_cast<T*>(scratch + sc.b);
+  const float* g = grads + t.off;
+  float* buf = state + t.off;
+  hipError_t e = muon_momentum((int64_t)r * c, g, buf, h->grad_scale, h->momentum, h->nesterov, partials, ctx->stream);
+  if (e == hipSuccess)
+    e = muon_normalise<T>(r, c, g, buf, h->grad_scale, h->momentum, h->nesterov, partials, 1e-7f, X, ctx->stream);
+  for (int it = 0; it < h->ns_steps && e == hipSuccess; ++it) {
+    // A = X X^T
+    GemmDesc ga = gemm(rw, rw, cw, X, cw, 0, X, cw, 0, EPI_STORE, A, rw);
+    e = run_gemm(ctx, ga, NC_TRACE_OPTIM_NS);
+    // B = ns_c A A^T + ns_b A   (A is symmetric, so A A^T = A A)
+    if (e == hipSuccess) {
+      GemmDesc gb = gemm(rw, rw, rw, A, rw, 0, A, rw, 0, EPI_AXPBY, B, rw);
+      gb.aux = A; gb.ldaux = rw; gb.ep_alpha = h->ns_c; gb.ep_gamma = h->ns_b;
+      e = run_gemm(ctx, gb, NC_TRACE_OPTIM_NS);
+    }
+    // X' = B X + ns_a X
+    if (e == hipSuccess) {
+      GemmDesc gx = gemm(rw, cw, rw, B, rw, 0, X, cw, 1, EPI_AXPBY, Xn, cw);
+      gx.aux = X; gx.ldaux = cw; gx.ep_alpha = 1.f; gx.ep_gamma = h->ns_a;
+      e = run_gemm(ctx, gx, NC_TRACE_OPTIM_NS);
+    }
+    std::swap(X, Xn);
+  }
+  const float lr = (float)((double)h->lr_matrix * std::sqrt(std::max(1.0, (double)r / c)));
+  if (e == hipSuccess) e = muon_apply<T>(r, c, X, lr, master + t.off, params + t.off, ctx->stream);
+  return e;
+}
+
+template <typename T>
+int optimizer_step(nc_ctx* ctx, float* master, T* params, const float* grads, float* state, char* scratch,
+                   const nc_optim_hparams* h) {
+  const OptimScratch sc = optim_scratch(ctx->cfg);
+  for (const OptimTensor& t : optim_tensors(ctx->cfg)) {
+    if (t.tensor == NC_T_E || t.tensor == NC_T_U)
+      NC_TRY(optim_adamw<T>(ctx, t, master, params, grads, state, h), "AdamW");
+    else
+      NC_TRY(optim_muon<T>(ctx, t, master, params, grads, state, scratch, sc, h), "Muon");
+  }
+  return NC_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -680,6 +822,60 @@ int nc_block_backward(nc_ctx* ctx, const void* block_params, const void* dy, voi
              ? block_backward<bf16>(ctx, (const bf16*)block_params, (const bf16*)dy, (bf16*)dx, dparams, accumulate)
              : block_backward<float>(ctx, (const float*)block_params, (const float*)dy, (float*)dx, dparams,
                                      accumulate);
+}
+
+int nc_optim_default(const nc_config* cfg, int64_t it, int64_t num_iters, int32_t n_micro, nc_optim_hparams* out) {
+  int st = validate(cfg);
+  if (st != NC_OK) return st;
+  if (!out || it < 0 || num_iters <= 0 || it > num_iters || n_micro < 1) return NC_ERR_INVALID_ARG;
+  // lrm: 1 until the last 20 % of the iterations, then linear to 0
+  const double warmdown = 0.2, final_frac = 0.0;
+  const double progress = (double)it / (double)num_iters;
+  const double lrm = progress < 1.0 - warmdown ? 1.0 : final_frac + (1.0 - final_frac) * (1.0 - progress) / warmdown;
+  const double width = std::pow((double)cfg->d_model / 768.0, -0.5);
+  const double frac = std::min((double)it / 300.0, 1.0);
+  out->grad_scale = (float)(1.0 / n_micro);
+  out->lr_embed = (float)(0.2 * width * lrm);
+  out->lr_unembed = (float)(0.004 * width * lrm);
+  out->beta1 = 0.8f;
+  out->beta2 = 0.95f;
+  out->eps = 1e-10f;
+  out->weight_decay = 0.f;
+  out->adam_step = (int32_t)std::min<int64_t>(it + 1, INT32_MAX);
+  out->lr_matrix = (float)(0.02 * lrm);
+  out->momentum = (float)((1.0 - frac) * 0.85 + frac * 0.95);
+  out->nesterov = 1;
+  out->ns_steps = 5;
+  out->ns_a = 3.4445f;
+  out->ns_b = -4.7750f;
+  out->ns_c = 2.0315f;
+  return NC_OK;
+}
+
+int64_t nc_optim_state_bytes(const nc_config* cfg) {
+  int st = validate(cfg);
+  if (st != NC_OK) return st;
+  const int64_t extra = is_block(*cfg) ? 0 : 2 * (int64_t)cfg->vocab * cfg->d_model;
+  return (param_count_of(*cfg) + extra) * 4;
+}
+
+int64_t nc_optim_scratch_bytes(const nc_config* cfg) {
+  int st = validate(cfg);
+  if (st != NC_OK) return st;
+  return (int64_t)optim_scratch(*cfg).total;
+}
+
+int nc_optimizer_step(nc_ctx* ctx, float* master, void* params, const float* grads, void* state, void* scratch,
+                      const nc_optim_hparams* hp) {
+  if (!ctx || !master || !params || !grads || !state || !scratch || !hp) return NC_ERR_INVALID_ARG;
+  if (!hp_ok(hp)) return NC_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(scratch) & (kAlign - 1)) || (reinterpret_cast<uintptr_t>(state) & 15) ||
+      (reinterpret_cast<uintptr_t>(master) & 15) || (reinterpret_cast<uintptr_t>(grads) & 15) ||
+      (reinterpret_cast<uintptr_t>(params) & 7))
+    return NC_ERR_INVALID_ARG;
+  return is_bf16(ctx->cfg)
+             ? optimizer_step<bf16>(ctx, master, (bf16*)params, grads, (float*)state, (char*)scratch, hp)
+             : optimizer_step<float>(ctx, master, (float*)params, grads, (float*)state, (char*)scratch, hp);
 }
 
 }  // extern "C"

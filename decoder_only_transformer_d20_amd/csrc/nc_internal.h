@@ -47,6 +47,7 @@ enum Epi {
   EPI_LSE = 5,       // per-row (max, sum exp) of the N-tile -> lse_part; z[tgt] -> ztgt
   EPI_DZ = 6,        // C(T) = (exp(acc - lse[m]) - [n == tgt[m]]) * inv_nvalid
   EPI_RELU2 = 7,     // C(T) = relu(acc)^2
+  EPI_AXPBY = 8,     // C(T) = ep_alpha * acc + ep_gamma * aux(T)   (aux may not alias C)
 };
 
 struct GemmDesc {
@@ -70,6 +71,8 @@ struct GemmDesc {
   float* ztgt;              // [M]
   const float* lse;         // [M]
   const float* inv_nvalid;  // device scalar
+  // EPI_AXPBY
+  float ep_alpha, ep_gamma;
 };
 
 // ---------------------------------------------------------------------------
@@ -125,5 +128,31 @@ hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
 // out [cols][rows] = transpose of in [rows][cols]; rows, cols multiples of 8
 hipError_t transpose_bf16(const bf16* in, int64_t rows, int64_t cols, bf16* out, hipStream_t s);
 hipError_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// optimiser step
+// ---------------------------------------------------------------------------
+struct AdamwArgs {
+  float grad_scale;         // multiplies g first
+  float beta1, beta2;
+  float decay;              // 1 - lr * weight_decay
+  float lr;
+  float inv_bc1, inv_bc2;   // 1 / (1 - beta^step)
+  float eps;
+};
+// p, m, v fp32 [n] updated in place; out = p in the model dtype; n % 4 == 0
+template <typename T> hipError_t adamw(int64_t n, float* p, const float* g, float* m, float* v, T* out,
+                                       const AdamwArgs& a, hipStream_t s);
+constexpr int kMuonMaxPartials = 1024;
+int muon_partials(int64_t n);   // partial sums muon_momentum writes for n elements
+// buf = mu buf + scale g;  partials[i] = sum of u^2 over block i's elements,
+// u = scale g + mu buf (nesterov) or buf;  n % 4 == 0
+hipError_t muon_momentum(int64_t n, const float* g, float* buf, float scale, float mu, int nesterov, float* partials,
+                         hipStream_t s);
+// X = u / (||u||_F + eps) as [r][c], or [c][r] when r > c;  r, c multiples of 64
+template <typename T> hipError_t muon_normalise(int r, int c, const float* g, const float* buf, float scale, float mu,
+                                                int nesterov, const float* partials, float eps, T* X, hipStream_t s);
+// W [r][c] -= lr X (X [r][c], or [c][r] when r > c);  out = W in the model dtype
+template <typename T> hipError_t muon_apply(int r, int c, const T* X, float lr, float* W, T* out, hipStream_t s);
 
 }  // namespace nc

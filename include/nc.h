@@ -173,6 +173,72 @@ int nc_block_forward(nc_ctx* ctx, const void* block_params, const void* x, void*
 int nc_block_backward(nc_ctx* ctx, const void* block_params, const void* dy,
                       void* dx, float* dparams, int32_t accumulate);
 
+/* ---- optimiser step ------------------------------------------------------- */
+/* The step after the backward pass (section Pretraining, optimiser
+ * paragraph: Muon on every matrix, AdamW on the embedding E and the
+ * unembedding U, nothing else trainable; learning-rate paragraph: rates
+ * scale as 1/sqrt(width); the paragraph after the training log: lrm, a
+ * multiplier falling linearly to 0 at the end).  The pages do not define
+ * Muon; it is taken as published (K. Jordan et al., 2024):
+ *   buf = momentum buf + g;  u = g + momentum buf (Nesterov) or buf;
+ *   X = u / (||u||_F + 1e-7), transposed when rows > cols;
+ *   ns_steps times:  A = X X^T;  B = ns_b A + ns_c A A;  X = ns_a X + B X;
+ *   W -= lr_matrix sqrt(max(1, rows/cols)) X (transposed back).
+ * Wq, Wk and Wv are three matrices here.  AdamW is the decoupled-decay
+ * form with bias-corrected moments:
+ *   p = p (1 - lr wd);  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   p -= lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
+ * Every g is first multiplied by grad_scale (1/n averages n micro-batch
+ * gradients accumulated with nc_backward(..., accumulate = 1)).
+ * The learning rates given here are the effective ones. */
+typedef struct {
+  float grad_scale;
+  float lr_embed;        /* AdamW on E */
+  float lr_unembed;      /* AdamW on U */
+  float beta1, beta2, eps, weight_decay;
+  int32_t adam_step;     /* t >= 1: AdamW steps taken, this one included */
+  float lr_matrix;       /* Muon on every block matrix */
+  float momentum;        /* in [0, 1) */
+  int32_t nesterov;      /* 0 or 1 */
+  int32_t ns_steps;      /* 0 .. 100 */
+  float ns_a, ns_b, ns_c;
+} nc_optim_hparams;
+
+/* Default hyperparameters for iteration it (0-based) of num_iters, with
+ * gradients accumulated over n_micro micro-batches.  These are readings, not
+ * values from the pages: AdamW betas (0.8, 0.95), eps 1e-10, no decay,
+ * rates 0.2 (E) and 0.004 (U) times (d/768)^-1/2; Muon rate 0.02, momentum
+ * ramped 0.85 -> 0.95 over the first 300 iterations, Nesterov, 5 steps of
+ * (3.4445, -4.7750, 2.0315); lrm = 1 until the last 20 % of the
+ * iterations, then linear to 0; every rate is multiplied by lrm.
+ * Host-only.  Returns nc_status. */
+int nc_optim_default(const nc_config* cfg, int64_t it, int64_t num_iters, int32_t n_micro, nc_optim_hparams* out);
+
+/* Bytes of optimiser state: fp32 [nc_param_count] holding, at each tensor's
+ * parameter offset, Muon's momentum buffer (matrices) or AdamW's first
+ * moment (E, U); then fp32 AdamW second moments of E [V*d] and U [V*d].
+ * Zero it before the first step.  Negative nc_status on a bad config. */
+int64_t nc_optim_state_bytes(const nc_config* cfg);
+
+/* Bytes of device scratch nc_optimizer_step needs (256-byte aligned). */
+int64_t nc_optim_scratch_bytes(const nc_config* cfg);
+
+/* One optimiser step over every parameter.
+ *   master  device fp32 [nc_param_count]: the parameters, updated in place
+ *   params  device dtype [nc_param_count]: receives the updated parameters
+ *           in the model dtype (the buffer nc_forward reads); may be master
+ *           when the dtype is fp32
+ *   grads   device fp32 [nc_param_count], read only
+ *   state   device, nc_optim_state_bytes(cfg), updated in place
+ *   scratch device, nc_optim_scratch_bytes(cfg)
+ * The Newton-Schulz iteration runs in the model dtype (bf16 operands, fp32
+ * accumulation, as published); everything else in fp32.  Deterministic:
+ * repeated calls on the same inputs give identical bits.  Does not touch the
+ * workspace, so a forward/backward state survives it.  NC_ERR_INVALID_ARG on
+ * a null pointer or an out-of-range hyperparameter. */
+int nc_optimizer_step(nc_ctx* ctx, float* master, void* params, const float* grads, void* state, void* scratch,
+                      const nc_optim_hparams* hp);
+
 /* ---- kernel timing (for roofline reports) --------------------------------- */
 
 /* Kernel families of the step.  Each GEMM family is one matrix-core kernel
@@ -189,6 +255,8 @@ enum {
   NC_TRACE_GEMM_WGRAD,        /* weight gradients dWqkv, dWo, dW1, dW2, dU    */
   NC_TRACE_ATTN_FWD,
   NC_TRACE_ATTN_BWD,
+  NC_TRACE_OPTIM_NS,          /* Muon's Newton-Schulz products (nc_optimizer_step) */
+  NC_TRACE_OPTIM_ADAMW,       /* AdamW on E and U (nc_optimizer_step)         */
   NC_TRACE_COUNT
 };
 

@@ -1,0 +1,245 @@
+"""Parity of the optimiser step (nc_optimizer_step) with the fp64 oracle
+(oracle/optim.py) on the same seeded inputs.
+
+Bars: AdamW (E, U), Muon's momentum buffer and AdamW's moments are fp32
+elementwise, so they must match to 1e-5 relative.  Muon's Newton-Schulz
+iteration runs in the model dtype.  In fp32 the updates must match to 1e-4
+relative.  In bf16 (operands rounded at every product, as published)
+emulating the rounding on the CPU puts the update 0.9-1.2 % (relative
+Frobenius) from fp64 at cosine >= 0.99993 for these shapes.  The bar is
+cosine >= 0.999 per matrix and relative error <= 3 %.  The model-dtype copy
+must equal the fp32 master rounded, bit for bit."""
+import math
+
+import numpy as np
+import pytest
+
+import synthdata
+from oracle import optim as oopt
+from tests._util import cosine, dev, empty, host, zeros
+
+pytestmark = pytest.mark.gpu
+
+
+def _nc():
+    import decoder_only_transformer_d20_amd as nc
+    return nc
+
+
+def _inputs(cfg, seed):
+    """fp32 master parameters (the synthetic init) and two seeded fp32
+    gradients of realistic spread (per-tensor scale 1/sqrt(fan_in))."""
+    master = synthdata.make_params(cfg).astype(np.float32)
+    rng = np.random.default_rng(seed)
+    grads = []
+    for _ in range(2):
+        g = np.empty(master.size, dtype=np.float32)
+        for name, layer, r, c, off in synthdata.param_layout(cfg):
+            g[off:off + r * c] = (rng.standard_normal(r * c) / math.sqrt(c)).astype(np.float32)
+        grads.append(g)
+    return master, grads
+
+
+def _hp_dict(h):
+    return {"grad_scale": h.grad_scale, "lr_embed": h.lr_embed, "lr_unembed": h.lr_unembed,
+            "beta1": h.beta1, "beta2": h.beta2, "eps": h.eps, "weight_decay": h.weight_decay,
+            "adam_step": h.adam_step, "lr_matrix": h.lr_matrix, "momentum": h.momentum,
+            "nesterov": bool(h.nesterov), "ns_steps": h.ns_steps, "ns_coeffs": (h.ns_a, h.ns_b, h.ns_c)}
+
+
+class _Run:
+    """Device buffers of one optimiser run."""
+
+    def __init__(self, cfg, master, portable=False):
+        nc = _nc()
+        self.nc, self.cfg = nc, cfg
+        self.sess = nc.Session(cfg, portable=portable)
+        self.c = nc.make_config(cfg, portable=portable)
+        self.master = dev(master)
+        self.params = empty(master.size, cfg.dtype)
+        self.state = zeros(nc.optim_state_bytes(self.c) // 4)
+        self.scratch = empty(nc.optim_scratch_bytes(self.c) // 4 + 64)
+        base = self.scratch.data_ptr()
+        self.scratch_ptr = (base + 255) // 256 * 256
+
+    def step(self, grads, hp):
+        g = dev(grads)
+        self.sess.optimizer_step(self.master, self.params, g, self.state, self.scratch_ptr, hp)
+        import torch
+        torch.cuda.synchronize()
+
+
+def _check_against_oracle(cfg, run, master0, grads, hps, muon_cos, muon_rel):
+    """Compare the displacement over all steps (master - master0), the
+    state, and the model-dtype copy with the oracle run on the same
+    inputs."""
+    layout = synthdata.param_layout(cfg)
+    want, st = master0.astype(np.float64), oopt.new_state(layout)
+    for g, h in zip(grads, hps):
+        want, st = oopt.optimizer_step(layout, want, g.astype(np.float64), st, _hp_dict(h))
+    got = host(run.master)
+    state = host(run.state)
+    P = synthdata.param_count(cfg)
+    for name, layer, r, c, off in layout:
+        sl = slice(off, off + r * c)
+        dg, dw = got[sl] - master0[sl], want[sl] - master0[sl]
+        if name in ("E", "U"):
+            err = np.abs(dg - dw).max() / np.abs(dw).max()
+            assert err <= 1e-5, (name, err)
+            m_w, v_w = st[(name, layer, "m")].ravel(), st[(name, layer, "v")].ravel()
+            voff = P + (0 if name == "E" else r * c)
+            assert np.abs(state[sl] - m_w).max() <= 1e-5 * np.abs(m_w).max(), name
+            assert np.abs(state[voff:voff + r * c] - v_w).max() <= 1e-5 * np.abs(v_w).max(), name
+        else:
+            cs = cosine(dg, dw)
+            rel = np.linalg.norm(dg - dw) / np.linalg.norm(dw)
+            assert cs >= muon_cos and rel <= muon_rel, (name, layer, cs, rel)
+            b_w = st[(name, layer, "buf")].ravel()
+            assert np.abs(state[sl] - b_w).max() <= 1e-5 * np.abs(b_w).max(), (name, layer)
+    # the model-dtype copy is the master, rounded
+    p = run.params.detach().cpu().numpy()
+    if cfg.dtype == "bf16":
+        assert np.array_equal(p.view(np.uint16), synthdata.f32_to_bf16_bits(got.astype(np.float32)))
+    else:
+        assert np.array_equal(p, got.astype(np.float32))
+
+
+@pytest.mark.parametrize("name,portable", [("small", False), ("small", True), ("tiny", False)])
+def test_two_steps_match_oracle(name, portable):
+    """Two steps from zero state: step 0, then step 900 of 1000 (lrm 0.5,
+    full momentum) with a different gradient, so both AdamW moments and the
+    momentum buffer carry over."""
+    cfg = synthdata.get_config(name)
+    master, grads = _inputs(cfg, seed=31)
+    run = _Run(cfg, master, portable)
+    hps = [run.nc.optim_default(run.c, 0, 1000), run.nc.optim_default(run.c, 900, 1000)]
+    hps[1].adam_step = 2                       # AdamW's own count continues from 1
+    for g, h in zip(grads, hps):
+        run.step(g, h)
+    prec = (0.999, 0.03) if cfg.dtype == "bf16" else (1 - 1e-8, 1e-4)
+    _check_against_oracle(cfg, run, master, grads, hps, *prec)
+
+
+def test_deterministic_and_grad_scale_exact():
+    """Repeated runs give identical bits; grads G with grad_scale 1/2 step
+    exactly as G/2 with grad_scale 1 (halving is exact in fp32)."""
+    cfg = synthdata.get_config("small")
+    master, grads = _inputs(cfg, seed=32)
+    outs = []
+    for g, scale in ((grads[0], 0.5), (grads[0], 0.5), (grads[0] * np.float32(0.5), 1.0)):
+        run = _Run(cfg, master)
+        h = run.nc.optim_default(run.c, 5, 100, n_micro=2)
+        h.grad_scale = scale
+        run.step(g, h)
+        outs.append((host(run.master), host(run.state)))
+    for o in outs[1:]:
+        assert np.array_equal(o[0], outs[0][0]) and np.array_equal(o[1], outs[0][1])
+
+
+def test_zero_rates_and_zero_ns_steps():
+    """lr 0 leaves every parameter as it was (only the state moves);
+    ns_steps 0 applies the normalised direction itself."""
+    cfg = synthdata.get_config("small")
+    master, grads = _inputs(cfg, seed=33)
+    run = _Run(cfg, master)
+    h = run.nc.optim_default(run.c, 0, 10)
+    h.lr_embed = h.lr_unembed = h.lr_matrix = 0.0
+    run.step(grads[0], h)
+    assert np.array_equal(host(run.master), master.astype(np.float64))
+    run = _Run(cfg, master)
+    h = run.nc.optim_default(run.c, 0, 10)
+    h.ns_steps = 0
+    run.step(grads[0], h)
+    got = host(run.master)
+    for name, layer, r, c, off in synthdata.param_layout(cfg):
+        if name in ("E", "U"):
+            continue
+        g = grads[0][off:off + r * c].astype(np.float64)
+        want = -h.lr_matrix * math.sqrt(max(1.0, r / c)) * g / np.linalg.norm(g)
+        d = got[off:off + r * c] - master[off:off + r * c]
+        assert cosine(d, want) >= 0.9999 and np.linalg.norm(d - want) / np.linalg.norm(want) <= 5e-3
+
+
+def test_rejects_bad_hparams():
+    cfg = synthdata.get_config("small")
+    master, grads = _inputs(cfg, seed=34)
+    run = _Run(cfg, master)
+    nc = run.nc
+    for field, value in (("beta1", 1.0), ("momentum", -0.1), ("ns_steps", 101), ("adam_step", 0),
+                         ("nesterov", 2), ("lr_matrix", float("nan")), ("eps", -1.0)):
+        h = nc.optim_default(run.c, 0, 10)
+        setattr(h, field, value)
+        with pytest.raises(nc.NcError) as e:
+            run.step(grads[0], h)
+        assert e.value.status == -1, field
+    assert np.array_equal(host(run.master), master.astype(np.float64))
+
+
+def test_training_loop_lowers_the_loss():
+    """forward, backward (two micro-batches accumulated), optimiser step,
+    five times on the same batch: the loss falls."""
+    import torch
+    cfg = synthdata.get_config("small")
+    nc = _nc()
+    master = synthdata.make_params(cfg).astype(np.float32)
+    idx, tgt = synthdata.make_tokens(cfg)
+    tb = synthdata.make_token_bytes(cfg)
+    run = _Run(cfg, master)
+    I, T, TB = dev(idx.ravel()), dev(tgt.ravel()), dev(tb)
+    half = idx.size // 2
+    G = zeros(master.size)
+    out = zeros(5, "f64")
+    P = dev(master, "bf16")
+    cfg_half = cfg.with_(batch=cfg.batch // 2)
+    sess = nc.Session(cfg_half)
+    losses = []
+    for it in range(5):
+        for mb in range(2):
+            sl = slice(mb * half, (mb + 1) * half)
+            sess.forward(P, I[sl], T[sl])
+            sess.loss_bpb(TB, out)
+            torch.cuda.synchronize()
+            if mb == 0:
+                losses.append(float(out[0].item()))
+            sess.backward(P, G, accumulate=mb == 1)
+        h = nc.optim_default(run.c, it, 5, n_micro=2)
+        run.sess.optimizer_step(run.master, P, G, run.state, run.scratch_ptr, h)
+    torch.cuda.synchronize()
+    assert losses[-1] < losses[0] - 0.2 and all(np.isfinite(losses)), losses
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_d20_step_sampled():
+    """One step on the full d20 parameter set: AdamW checked on 4096
+    sampled elements of E and of U, Muon in full on two matrices (Wq of
+    layer 0, W1 of layer 19), every other matrix finite and moved."""
+    cfg = synthdata.get_config("d20")
+    nc = _nc()
+    master = synthdata.make_params(cfg).astype(np.float32)
+    rng = np.random.default_rng(35)
+    grads = (rng.standard_normal(master.size, dtype=np.float32) * np.float32(0.03))
+    run = _Run(cfg, master)
+    h = nc.optim_default(run.c, 0, 1000)
+    run.step(grads, h)
+    got = host(run.master)
+    hp = _hp_dict(h)
+    for name, layer, r, c, off in synthdata.param_layout(cfg):
+        sl = slice(off, off + r * c)
+        if name in ("E", "U"):
+            pick = off + rng.choice(r * c, 4096, replace=False)
+            lr = hp["lr_embed"] if name == "E" else hp["lr_unembed"]
+            p, _, _ = oopt.adamw_update(master[pick].astype(np.float64), grads[pick].astype(np.float64), 0.0, 0.0, 1,
+                                        lr, hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+            dw = p - master[pick]
+            assert np.abs((got[pick] - master[pick]) - dw).max() <= 1e-5 * np.abs(dw).max(), name
+        elif (name, layer) in (("Wq", 0), ("W1", 19)):
+            W = master[sl].reshape(r, c).astype(np.float64)
+            G = grads[sl].reshape(r, c).astype(np.float64)
+            Wn, _ = oopt.muon_update(W, G, np.zeros_like(W), hp["lr_matrix"], hp["momentum"])
+            dg, dw = got[sl] - master[sl], (Wn - W).ravel()
+            cs, rel = cosine(dg, dw), np.linalg.norm(dg - dw) / np.linalg.norm(dw)
+            assert cs >= 0.999 and rel <= 0.03, (name, layer, cs, rel)
+        else:
+            d = got[sl] - master[sl]
+            assert np.isfinite(d).all() and np.abs(d).max() > 0, (name, layer)

@@ -101,6 +101,8 @@ def test_calls_on_null_context_rejected():
     assert L.nc_backward(None, 1, 1, 0) == -1
     assert L.nc_loss_bpb(None, 1, 1) == -1
     assert L.nc_block_forward(None, 1, 1, 2) == -1
+    h = nc.NcOptimHparams()
+    assert L.nc_optimizer_step(None, 16, 16, 16, 16, 256, ctypes.byref(h)) == -1
     assert L.nc_last_error(None) == b"null context"
 
 
@@ -138,3 +140,38 @@ def test_flop_formula_d20():
     cfg = synthdata.get_config("d20")
     assert flops_per_token(cfg) == pytest.approx(3.492e9, rel=1e-3)
     assert flops_per_step(cfg) == pytest.approx(2.288e14, rel=1e-3)
+
+
+# --------------------------------------------------------------------------
+# optimiser step: host-only queries
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("it,num_iters,n_micro", [(0, 1000, 1), (150, 1000, 8), (850, 1000, 2), (999, 1000, 1),
+                                                  (1000, 1000, 1), (7, 10, 4)])
+def test_optim_default_matches_oracle_schedule(it, num_iters, n_micro):
+    """nc_optim_default (host C) against the oracle's schedule and
+    defaults, at d20 width."""
+    from oracle import optim
+    cfg = synthdata.get_config("d20")
+    h = nc.optim_default(cfg, it, num_iters, n_micro)
+    w = optim.default_hparams(cfg.d_model, it, num_iters, n_micro)
+    for f in ("grad_scale", "lr_embed", "lr_unembed", "beta1", "beta2", "eps", "weight_decay", "lr_matrix",
+              "momentum"):
+        assert getattr(h, f) == pytest.approx(w[f], rel=1e-6, abs=1e-12), f
+    assert h.adam_step == w["adam_step"] and h.nesterov == 1 and h.ns_steps == w["ns_steps"]
+    assert (h.ns_a, h.ns_b, h.ns_c) == pytest.approx(w["ns_coeffs"], rel=1e-6)
+
+
+def test_optim_sizes():
+    cfg = synthdata.get_config("d20")
+    P = synthdata.param_count(cfg)
+    assert nc.optim_state_bytes(cfg) == 4 * (P + 2 * cfg.vocab * cfg.d_model)
+    blk = synthdata.get_config("block")
+    assert nc.optim_state_bytes(blk) == 4 * synthdata.param_count(blk)
+    # two ping-pong copies of the largest matrix (d x 4d), two d x d products
+    # and 4 KB of partial sums, 256-byte aligned
+    es = 2
+    assert nc.optim_scratch_bytes(cfg) == 4096 + 2 * 5120 * 1280 * es + 2 * 1280 * 1280 * es
+    with pytest.raises(nc.NcError):
+        nc.optim_default(cfg, 5, 4, 1)          # it past num_iters
+    with pytest.raises(nc.NcError):
+        nc.optim_default(cfg, 0, 10, 0)         # no micro-batch
