@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--no-roofline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--mfma-calibration", action="store_true")
+    ap.add_argument("--optimizer", action="store_true",
+                    help="time the optimiser step (Muon + AdamW) over the configuration's parameters")
     ap.add_argument("--library-gemm", action="store_true",
                     help="time the vendor BLAS (torch.matmul) next to nc_op_matmul on the d20 product shapes")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
@@ -181,6 +183,54 @@ def library_gemm(reps=10):
     print(json.dumps({"library_gemm": rows, "blas": str(blas), "reps": reps}), flush=True)
 
 
+def optimizer_timing(torch, nc, cfg, steps=5, warmup=1, trace=True):
+    """Time nc_optimizer_step over every parameter of cfg: fp32 master
+    weights, bf16 model copy, seeded fp32 gradients, optimiser state from
+    zero.  Returns ms per step and, per traced family, launches, ms and
+    rate (Newton-Schulz products in TFLOP/s, AdamW in GB/s of its
+    algorithmic 30 bytes per element)."""
+    import numpy as np
+    import synthdata
+    c = nc.make_config(cfg)
+    sess = nc.Session(cfg)
+    stream = sess.stream
+    P = synthdata.param_count(cfg)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    master = (torch.randn(P, device="cuda", generator=g) * 0.02).float()
+    grads = (torch.randn(P, device="cuda", generator=g) * 0.001).float()
+    params = torch.empty(P, dtype=torch.bfloat16 if cfg.dtype == "bf16" else torch.float32, device="cuda")
+    state = torch.zeros(nc.optim_state_bytes(c) // 4, dtype=torch.float32, device="cuda")
+    scratch = torch.empty(nc.optim_scratch_bytes(c) + 256, dtype=torch.uint8, device="cuda")
+    sp = (scratch.data_ptr() + 255) // 256 * 256
+    h = nc.optim_default(c, 0, 1000, n_micro=8)
+
+    def step():
+        sess.optimizer_step(master, params, grads, state, sp, h)
+
+    for _ in range(warmup):
+        step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    out = {"ms_per_step": round(ev[0].elapsed_time(ev[1]) / steps, 3)}
+    if trace:
+        fam = {}
+        for f in nc.OPTIM_TRACE_FAMILIES:
+            sess.trace_enable(f)
+            step()
+            n, ms, fl, by = sess.trace_read()
+            rate = {"tflops": round(fl / (ms * 1e-3) / 1e12, 1)} if fl else {"gbps": round(by / (ms * 1e-3) / 1e9, 1)}
+            fam[f] = {"launches": n, "ms": round(ms, 3), **rate, "flops": fl, "bytes": by}
+        sess.trace_enable(None)
+        out["families"] = fam
+    del master, grads, params, state, scratch
+    return out
+
+
 def measured_peaks(torch, nc, stream):
     """What the chip sustains on this machine, next to the spec peaks: the bf16
     matrix-core rate of a register-only MFMA loop (nc_op_mfma_loop: 8
@@ -228,6 +278,21 @@ def main():
         return
     if args.library_gemm:
         library_gemm()
+        return
+    if args.optimizer:
+        import torch
+        import synthdata
+        import decoder_only_transformer_d20_amd as nc
+        cfg = synthdata.get_config(args.config)
+        r = optimizer_timing(torch, nc, cfg, steps=args.steps, warmup=args.warmup)
+        ns = r["families"]["optim_ns"]
+        print(json.dumps({"metric": "optimiser step time (Muon on every matrix, AdamW on E and U)",
+                          "config": {"workload": f"{cfg.name}: {synthdata.param_count(cfg)} parameters, "
+                                                 f"bf16 Newton-Schulz, fp32 master weights and state"},
+                          "steps": args.steps, "warmup": args.warmup, **r,
+                          "roofline": {"bound": "mfma", "kernel_family": "optim_ns",
+                                       "achieved": ns["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": round(ns["tflops"] / PEAK_BF16_TFLOPS, 4)}}), flush=True)
         return
     if args.mfma_calibration:
         import torch
@@ -360,6 +425,12 @@ def main():
         }
         result["kernel_families"] = families
     del P, G
+    if not args.no_roofline and not cfg.block_only:
+        o = optimizer_timing(torch, nc, cfg, steps=3, warmup=1, trace=False)
+        result["optimizer_step"] = {
+            "ms": o["ms_per_step"],
+            "note": "one Muon + AdamW step over every parameter, timed separately and not part of value; "
+                    "the pages' batch of 2^19 tokens is 8 of these fwd+bwd steps per optimiser step"}
     if not args.no_roofline:
         result["measured_peaks"] = measured_peaks(torch, nc, stream)
         if "roofline" in result:

@@ -139,10 +139,12 @@ __device__ inline uint32_t frag_tr_off(int row0, int l) {
   return (uint32_t)k * (2u * R) + ((uint32_t)((m >> 3) ^ (4 * (j >> 2))) << 4) + 8u * ((m >> 2) & 1);
 }
 
-// One output tile of the persistent grid: split, n-tile, k-tiles, origin.
+// One output tile of the persistent grid: split, n-tile, k-tiles, origin,
+// and the element offsets of its batch item's operands and result.
 struct GemmTile {
   int split, tn, nk;
   int64_t m0, n0, kbeg;
+  int64_t pofs, qofs, cofs, aofs;
 };
 
 // Logical tile -> (split, m-tile, n-tile).  Workgroups are dealt to the 8
@@ -153,17 +155,19 @@ struct GemmTile {
 // m fastest: the ~32 blocks an XCD runs at once cover about 8 m-tiles x 4
 // n-tiles, so each P panel and each Q panel (weights) is reused from that
 // XCD's L2 instead of refetched per tile.  Split i covers the k-tiles
-// [i nkt/splits, (i+1) nkt/splits).
+// [i nkt/splits, (i+1) nkt/splits).  Batch items are outermost of all.
 template <int BM, int BN>
 struct TileMap {
   static constexpr int kGroupM = 8, kNarrow = 8;
   int ntn, ntm, ntiles, total, nkt, G, chunk, splits;
+  int64_t sP, sQ, sC, sAux;
   __device__ inline TileMap(const GemmDesc& g) {
     ntn = g.N / BN;
     ntm = g.M / BM;
     ntiles = ntn * ntm;
     splits = g.splits;
-    total = ntiles * splits;
+    total = ntiles * splits * (g.batch > 1 ? g.batch : 1);
+    sP = g.sP; sQ = g.sQ; sC = g.sC; sAux = g.sAux;
     nkt = g.K / BK;
     G = (int)gridDim.x;
     chunk = (total + 7) >> 3;
@@ -178,8 +182,11 @@ struct TileMap {
   }
   __device__ inline GemmTile coords(int L) const {
     GemmTile c;
-    c.split = L / ntiles;
-    const int t = L - c.split * ntiles;
+    const int outer = L / ntiles;
+    const int b = outer / splits;
+    c.split = outer - b * splits;
+    c.pofs = b * sP; c.qofs = b * sQ; c.cofs = b * sC; c.aofs = b * sAux;
+    const int t = L - outer * ntiles;
     const int first_m = (t / (kGroupM * ntn)) * kGroupM;
     const int gm = min(kGroupM, ntm - first_m);
     const int tg = t - first_m * ntn;
@@ -263,7 +270,7 @@ __device__ inline void epi_store4(const GemmDesc& g, const GemmTile& c, int64_t 
   u32x2 w;
   w.x = pack2(x[0], x[1]);
   w.y = pack2(x[2], x[3]);
-  u32x2* dst = reinterpret_cast<u32x2*>((bf16*)g.C + m * g.ldc + n);
+  u32x2* dst = reinterpret_cast<u32x2*>((bf16*)g.C + c.cofs + m * g.ldc + n);
   if constexpr (EPI == EPI_DRELU2 || EPI == EPI_AXPBY) *dst = w;
   else __builtin_nontemporal_store(w, dst);
 }
@@ -322,8 +329,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   Plan pl;
   const uint32_t my_lds = loadsP ? 0u : (uint32_t)BM * 128u;
   auto plan_init = [&](const Tile& c) {
-    if (loadsP) pl.init<BM, PT>((const bf16*)g.P, g.ldp, c.m0, c.kbeg, tl);
-    else pl.init<BN, QT>((const bf16*)g.Q, g.ldq, c.n0, c.kbeg, tl);
+    if (loadsP) pl.init<BM, PT>((const bf16*)g.P + c.pofs, g.ldp, c.m0, c.kbeg, tl);
+    else pl.init<BN, QT>((const bf16*)g.Q + c.qofs, g.ldq, c.n0, c.kbeg, tl);
   };
   u32x4 reg[8];
   auto stage_load = [&]() {
@@ -574,7 +581,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
         auto fetch = [&](int k) {
           const int64_t m = c.m0 + h * WTM + r0 + k * RPS;
           if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_AXPBY)
-            pa[k % W] = *reinterpret_cast<const uint2*>((const bf16*)g.aux + m * g.ldaux + n);
+            pa[k % W] = *reinterpret_cast<const uint2*>((const bf16*)g.aux + c.aofs + m * g.ldaux + n);
           if constexpr (EPI == EPI_ROPE) {
             // a tile with no rotated column (v) reads no rotary factors
             if (tile_rot) {
@@ -648,7 +655,7 @@ int resident_blocks(Kernel kern, int threads, int (&cached)[16]) {
 template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
 hipError_t launch(const GemmDesc& g, hipStream_t s) {
   static int cached[16] = {0};
-  const int total = (g.M / BM) * (g.N / BN) * g.splits;
+  const int total = (g.M / BM) * (g.N / BN) * g.splits * (g.batch > 1 ? g.batch : 1);
   dim3 grid(std::min(total, resident_blocks(k_gemm_mfma<NW, BM, BN, PT, QT, EPI>, NW * 64, cached)));
   k_gemm_mfma<NW, BM, BN, PT, QT, EPI><<<grid, NW * 64, 0, s>>>(g);
   return hipGetLastError();

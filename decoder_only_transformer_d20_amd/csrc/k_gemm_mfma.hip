@@ -14,6 +14,8 @@ bool gemm_mfma_supported(const GemmDesc& g) {
   if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.M % 128 || g.N % 128 || g.splits < 1) return false;
   if (g.K % mfma::BK || g.splits > g.K / mfma::BK) return false;
   if (g.splits > 1 && g.epi != EPI_F32) return false;
+  if (g.batch > 1 && (g.splits != 1 || (g.epi != EPI_STORE && g.epi != EPI_AXPBY))) return false;
+  if ((int64_t)(g.M / 128) * (g.N / 128) * g.splits * (g.batch > 1 ? g.batch : 1) > (1 << 30)) return false;
   if (g.epi == EPI_ROPE && (g.head_dim % 4 || g.rope_cols % 4)) return false;
   return mfma::combo_supported(g);
 }

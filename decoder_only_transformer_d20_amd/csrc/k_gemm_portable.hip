@@ -153,6 +153,21 @@ __global__ void __launch_bounds__(256) k_gemm_portable(GemmDesc g) {
 
 template <typename T>
 hipError_t gemm_portable(const GemmDesc& g, hipStream_t s) {
+  if (g.batch > 1) {
+    // one launch per item of a batched product
+    if (g.splits != 1 || (g.epi != EPI_STORE && g.epi != EPI_AXPBY)) return hipErrorInvalidValue;
+    for (int b = 0; b < g.batch; ++b) {
+      GemmDesc gi = g;
+      gi.batch = 1;
+      gi.P = (const T*)g.P + b * g.sP;
+      gi.Q = (const T*)g.Q + b * g.sQ;
+      gi.C = (T*)g.C + b * g.sC;
+      gi.aux = g.aux ? (const T*)g.aux + b * g.sAux : nullptr;
+      hipError_t e = gemm_portable<T>(gi, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (g.M % BM || g.N % BN || g.splits < 1 || g.K % 64 || g.splits > g.K / 64) return hipErrorInvalidValue;
   if (g.splits > 1 && g.epi != EPI_F32) return hipErrorInvalidValue;
   dim3 grid(g.N / BN, g.M / BM, g.splits);

@@ -51,14 +51,18 @@ __global__ void __launch_bounds__(kThreads) k_adamw(int64_t n4, float* __restric
   }
 }
 
-// Muon momentum over n elements (n % 4 == 0): buf = mu buf + s g, and the
+// Muon momentum over n elements (n % 4 == 0) of each of gridDim.y matrices
+// (matrix y at element offset y * stride): buf = mu buf + s g, and the
 // direction u = s g + mu buf (Nesterov) or buf.  Each block writes the fp32
-// sum of u^2 over its elements to partials[blockIdx.x] (a fixed tree, so
+// sum of u^2 over its elements to partials[y][blockIdx.x] (a fixed tree, so
 // repeated calls give identical bits).
 __global__ void __launch_bounds__(kThreads) k_muon_momentum(int64_t n4, const float* __restrict__ g,
                                                              float* __restrict__ buf, float s, float mu, int nesterov,
-                                                             float* __restrict__ partials) {
+                                                             float* __restrict__ partials, int64_t stride) {
   __shared__ float red[kThreads / 64];
+  g += blockIdx.y * stride;
+  buf += blockIdx.y * stride;
+  partials += (int64_t)blockIdx.y * kMuonMaxPartials;
   float acc = 0.f;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kThreads) {
     float4 gv = ld4(g + 4 * i), bv = ld4(buf + 4 * i);
@@ -87,14 +91,20 @@ __global__ void __launch_bounds__(kThreads) k_muon_momentum(int64_t n4, const fl
 // u recomputed from g and the updated buf.  X is [r][c] as the matrix, or
 // [c][r] when r > c (the wide orientation).  Every block sums the partials
 // itself, in fp64, in index order.  One block per 64 x 64 tile
-// (r, c multiples of 64); a transposed tile goes through LDS.
+// (r, c multiples of 64) of matrix z (g, buf at z * stride, partials at
+// z * kMuonMaxPartials, X at z * r * c); a transposed tile goes through LDS.
 template <typename T>
 __global__ void __launch_bounds__(kThreads) k_muon_normalise(int r, int c, const float* __restrict__ g,
                                                               const float* __restrict__ buf, float s, float mu,
                                                               int nesterov, const float* __restrict__ partials,
-                                                              int nparts, float eps, T* __restrict__ X) {
+                                                              int nparts, float eps, T* __restrict__ X,
+                                                              int64_t stride) {
   __shared__ float tile[kTile][kTile + 1];
   __shared__ float s_inv;
+  g += blockIdx.z * stride;
+  buf += blockIdx.z * stride;
+  partials += (int64_t)blockIdx.z * kMuonMaxPartials;
+  X += (int64_t)blockIdx.z * r * c;
   if (threadIdx.x == 0) {
     double t = 0.0;
     for (int i = 0; i < nparts; ++i) t += (double)partials[i];
@@ -143,11 +153,15 @@ template <> __device__ inline float4 ld4_t<bf16>(const bf16* p) {
 }
 
 // W -= lr X (X as the matrix [r][c], or [c][r] when r > c); out = W in the
-// model dtype.  One block per 64 x 64 tile of W.
+// model dtype.  One block per 64 x 64 tile of matrix z (W, out at
+// z * stride, X at z * r * c).
 template <typename T>
 __global__ void __launch_bounds__(kThreads) k_muon_apply(int r, int c, const T* __restrict__ X, float lr,
-                                                          float* __restrict__ W, T* __restrict__ out) {
+                                                          float* __restrict__ W, T* __restrict__ out, int64_t stride) {
   __shared__ float tile[kTile][kTile + 1];
+  X += (int64_t)blockIdx.z * r * c;
+  W += blockIdx.z * stride;
+  out += blockIdx.z * stride;
   const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
   const int tc = (threadIdx.x & 15) * 4, tr = threadIdx.x >> 4;
   const bool tall = r > c;
@@ -198,36 +212,37 @@ hipError_t adamw(int64_t n, float* p, const float* g, float* m, float* v, T* out
 
 int muon_partials(int64_t n) { return blocks_for(n / 4); }
 
-hipError_t muon_momentum(int64_t n, const float* g, float* buf, float scale, float mu, int nesterov, float* partials,
-                         hipStream_t s) {
-  if (n <= 0 || n % 4) return hipErrorInvalidValue;
-  k_muon_momentum<<<blocks_for(n / 4), kThreads, 0, s>>>(n / 4, g, buf, scale, mu, nesterov, partials);
+hipError_t muon_momentum(int64_t n, int count, int64_t stride, const float* g, float* buf, float scale, float mu,
+                         int nesterov, float* partials, hipStream_t s) {
+  if (n <= 0 || n % 4 || count < 1 || count > 65535) return hipErrorInvalidValue;
+  k_muon_momentum<<<dim3(blocks_for(n / 4), count), kThreads, 0, s>>>(n / 4, g, buf, scale, mu, nesterov, partials,
+                                                                      stride);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t muon_normalise(int r, int c, const float* g, const float* buf, float scale, float mu, int nesterov,
-                          const float* partials, float eps, T* X, hipStream_t s) {
-  if (r <= 0 || c <= 0 || r % kTile || c % kTile) return hipErrorInvalidValue;
-  k_muon_normalise<T><<<dim3(c / kTile, r / kTile), kThreads, 0, s>>>(
-      r, c, g, buf, scale, mu, nesterov, partials, muon_partials((int64_t)r * c), eps, X);
+hipError_t muon_normalise(int r, int c, int count, int64_t stride, const float* g, const float* buf, float scale,
+                          float mu, int nesterov, const float* partials, float eps, T* X, hipStream_t s) {
+  if (r <= 0 || c <= 0 || r % kTile || c % kTile || count < 1 || count > 65535) return hipErrorInvalidValue;
+  k_muon_normalise<T><<<dim3(c / kTile, r / kTile, count), kThreads, 0, s>>>(
+      r, c, g, buf, scale, mu, nesterov, partials, muon_partials((int64_t)r * c), eps, X, stride);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t muon_apply(int r, int c, const T* X, float lr, float* W, T* out, hipStream_t s) {
-  if (r <= 0 || c <= 0 || r % kTile || c % kTile) return hipErrorInvalidValue;
-  k_muon_apply<T><<<dim3(c / kTile, r / kTile), kThreads, 0, s>>>(r, c, X, lr, W, out);
+hipError_t muon_apply(int r, int c, int count, int64_t stride, const T* X, float lr, float* W, T* out, hipStream_t s) {
+  if (r <= 0 || c <= 0 || r % kTile || c % kTile || count < 1 || count > 65535) return hipErrorInvalidValue;
+  k_muon_apply<T><<<dim3(c / kTile, r / kTile, count), kThreads, 0, s>>>(r, c, X, lr, W, out, stride);
   return hipGetLastError();
 }
 
 template hipError_t adamw<float>(int64_t, float*, const float*, float*, float*, float*, const AdamwArgs&, hipStream_t);
 template hipError_t adamw<bf16>(int64_t, float*, const float*, float*, float*, bf16*, const AdamwArgs&, hipStream_t);
-template hipError_t muon_normalise<float>(int, int, const float*, const float*, float, float, int, const float*, float,
-                                          float*, hipStream_t);
-template hipError_t muon_normalise<bf16>(int, int, const float*, const float*, float, float, int, const float*, float,
-                                         bf16*, hipStream_t);
-template hipError_t muon_apply<float>(int, int, const float*, float, float*, float*, hipStream_t);
-template hipError_t muon_apply<bf16>(int, int, const bf16*, float, float*, bf16*, hipStream_t);
+template hipError_t muon_normalise<float>(int, int, int, int64_t, const float*, const float*, float, float, int,
+                                          const float*, float, float*, hipStream_t);
+template hipError_t muon_normalise<bf16>(int, int, int, int64_t, const float*, const float*, float, float, int,
+                                         const float*, float, bf16*, hipStream_t);
+template hipError_t muon_apply<float>(int, int, int, int64_t, const float*, float, float*, float*, hipStream_t);
+template hipError_t muon_apply<bf16>(int, int, int, int64_t, const bf16*, float, float*, bf16*, hipStream_t);
 
 }  // namespace nc

@@ -261,8 +261,9 @@ hipError_t traced(nc_ctx* ctx, int family, double flops, double bytes, F&& launc
 hipError_t run_gemm(nc_ctx* ctx, const GemmDesc& g, int family = -2) {
   if (!is_bf16(ctx->cfg)) return gemm_portable<float>(g, ctx->stream);
   if (portable(ctx->cfg) || !gemm_mfma_supported(g)) return gemm_portable<bf16>(g, ctx->stream);
-  hipError_t e = traced(ctx, family < -1 ? gemm_family(g) : family, 2.0 * g.M * g.N * g.K, gemm_bytes(g, 2),
-                        [&] { return gemm_mfma_bf16_product(g, ctx->stream); });
+  const double items = g.batch > 1 ? g.batch : 1;
+  hipError_t e = traced(ctx, family < -1 ? gemm_family(g) : family, 2.0 * g.M * g.N * g.K * items,
+                        gemm_bytes(g, 2) * items, [&] { return gemm_mfma_bf16_product(g, ctx->stream); });
   if (e == hipSuccess && g.epi == EPI_F32 && g.splits > 1)
     e = splitk_reduce(g.part, g.splits, (int64_t)g.M * g.N, (float*)g.C, g.beta, ctx->stream);
   return e;
@@ -545,27 +546,59 @@ int64_t param_count_of(const nc_config& c) {
   return (is_block(c) ? 0 : 2 * (int64_t)c.vocab * c.d_model) + layer_elems(c) * c.n_layer;
 }
 
-// scratch: Muon partial sums | X (two, ping-pong) | A | B, each 256-aligned
+// Muon's matrices as sets (one tensor of every layer: same shape, layer l
+// at off0 + l * stride), and the sets grouped by their wide orientation
+// [rw][cw] (rw <= cw): a group's Newton-Schulz products run as one batched
+// launch over its matrices, set by set, layer by layer.
+struct MuonSet {
+  int tensor, r, c, count;
+  int64_t off0, stride;
+};
+struct MuonGroup {
+  int rw, cw, nb;
+  std::vector<MuonSet> sets;
+};
+
+std::vector<MuonGroup> muon_groups(const nc_config& c) {
+  const int64_t d = c.d_model, F = c.d_ff;
+  const int64_t base = is_block(c) ? 0 : (int64_t)c.vocab * d;
+  const int64_t sizes[6][2] = {{d, d}, {d, d}, {d, d}, {d, d}, {F, d}, {d, F}};
+  std::vector<MuonGroup> gs;
+  int64_t off = base;
+  for (int t = 0; t < 6; ++t) {
+    const MuonSet st{NC_T_WQ + t, (int)sizes[t][0], (int)sizes[t][1], c.n_layer, off, layer_elems(c)};
+    off += sizes[t][0] * sizes[t][1];
+    const int rw = std::min(st.r, st.c), cw = std::max(st.r, st.c);
+    auto it = std::find_if(gs.begin(), gs.end(), [&](const MuonGroup& g) { return g.rw == rw && g.cw == cw; });
+    if (it == gs.end()) gs.push_back({rw, cw, st.count, {st}});
+    else { it->sets.push_back(st); it->nb += st.count; }
+  }
+  return gs;
+}
+
+// scratch: per-matrix partial sums | X (two, ping-pong) | A | B, each sized
+// for the largest group and 256-aligned
 struct OptimScratch {
   size_t partials = 0, x0 = 0, x1 = 0, a = 0, b = 0, total = 0;
 };
 
 OptimScratch optim_scratch(const nc_config& c) {
-  int64_t max_rc = 0, max_short = 0;
-  for (const OptimTensor& t : optim_tensors(c)) {
-    if (t.tensor == NC_T_E || t.tensor == NC_T_U) continue;
-    max_rc = std::max(max_rc, t.rows * t.cols);
-    max_short = std::max(max_short, std::min(t.rows, t.cols));
+  int64_t max_x = 0, max_a = 0, max_nb = 0;
+  for (const MuonGroup& g : muon_groups(c)) {
+    const int64_t nb = g.nb;
+    max_x = std::max(max_x, nb * g.rw * g.cw);
+    max_a = std::max(max_a, nb * g.rw * g.rw);
+    max_nb = std::max(max_nb, nb);
   }
   const size_t es = esize(c);
   OptimScratch o;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t r = off; off += align_up(bytes); return r; };
-  o.partials = take(kMuonMaxPartials * 4);
-  o.x0 = take(max_rc * es);
-  o.x1 = take(max_rc * es);
-  o.a = take(max_short * max_short * es);
-  o.b = take(max_short * max_short * es);
+  o.partials = take(max_nb * kMuonMaxPartials * 4);
+  o.x0 = take(max_x * es);
+  o.x1 = take(max_x * es);
+  o.a = take(max_a * es);
+  o.b = take(max_a * es);
   o.total = off;
   return o;
 }
@@ -606,42 +639,60 @@ hipError_t optim_adamw(nc_ctx* ctx, const OptimTensor& t, float* master, T* para
   });
 }
 
-// Muon on one matrix
+// Muon on one group of same-shaped matrices: the elementwise parts one
+// launch per set (all layers), the Newton-Schulz products batched over the
+// whole group
 template <typename T>
-hipError_t optim_muon(nc_ctx* ctx, const OptimTensor& t, float* master, T* params, const float* grads, float* state,
+hipError_t optim_muon(nc_ctx* ctx, const MuonGroup& grp, float* master, T* params, const float* grads, float* state,
                       char* scratch, const OptimScratch& sc, const nc_optim_hparams* h) {
-  const int r = (int)t.rows, c = (int)t.cols;
-  const int rw = std::min(r, c), cw = std::max(r, c);   // wide orientation [rw][cw]
+  const int rw = grp.rw, cw = grp.cw, nb = grp.nb;
+  const int64_t sx = (int64_t)rw * cw, sa = (int64_t)rw * rw;
   float* partials = reinterpret_cast<float*>(scratch + sc.partials);
   T* X = reinterpret_cast<T*>(scratch + sc.x0);
   T* Xn = reinterpret_cast<T*>(scratch + sc.x1);
   T* A = reinterpret_cast<T*>(scratch + sc.a);
   T* B = reinterpret_cast<T*>(scratch + sc.b);
-  const float* g = grads + t.off;
-  float* buf = state + t.off;
-  hipError_t e = muon_momentum((int64_t)r * c, g, buf, h->grad_scale, h->momentum, h->nesterov, partials, ctx->stream);
-  if (e == hipSuccess)
-    e = muon_normalise<T>(r, c, g, buf, h->grad_scale, h->momentum, h->nesterov, partials, 1e-7f, X, ctx->stream);
+  hipError_t e = hipSuccess;
+  int first = 0;                       // the set's first matrix in the group
+  for (const MuonSet& st : grp.sets) {
+    float* part = partials + (size_t)first * kMuonMaxPartials;
+    if (e == hipSuccess)
+      e = muon_momentum((int64_t)st.r * st.c, st.count, st.stride, grads + st.off0, state + st.off0, h->grad_scale,
+                        h->momentum, h->nesterov, part, ctx->stream);
+    if (e == hipSuccess)
+      e = muon_normalise<T>(st.r, st.c, st.count, st.stride, grads + st.off0, state + st.off0, h->grad_scale,
+                            h->momentum, h->nesterov, part, 1e-7f, X + first * sx, ctx->stream);
+    first += st.count;
+  }
   for (int it = 0; it < h->ns_steps && e == hipSuccess; ++it) {
     // A = X X^T
     GemmDesc ga = gemm(rw, rw, cw, X, cw, 0, X, cw, 0, EPI_STORE, A, rw);
+    ga.batch = nb; ga.sP = sx; ga.sQ = sx; ga.sC = sa;
     e = run_gemm(ctx, ga, NC_TRACE_OPTIM_NS);
     // B = ns_c A A^T + ns_b A   (A is symmetric, so A A^T = A A)
     if (e == hipSuccess) {
       GemmDesc gb = gemm(rw, rw, rw, A, rw, 0, A, rw, 0, EPI_AXPBY, B, rw);
       gb.aux = A; gb.ldaux = rw; gb.ep_alpha = h->ns_c; gb.ep_gamma = h->ns_b;
+      gb.batch = nb; gb.sP = sa; gb.sQ = sa; gb.sC = sa; gb.sAux = sa;
       e = run_gemm(ctx, gb, NC_TRACE_OPTIM_NS);
     }
     // X' = B X + ns_a X
     if (e == hipSuccess) {
       GemmDesc gx = gemm(rw, cw, rw, B, rw, 0, X, cw, 1, EPI_AXPBY, Xn, cw);
       gx.aux = X; gx.ldaux = cw; gx.ep_alpha = 1.f; gx.ep_gamma = h->ns_a;
+      gx.batch = nb; gx.sP = sa; gx.sQ = sx; gx.sC = sx; gx.sAux = sx;
       e = run_gemm(ctx, gx, NC_TRACE_OPTIM_NS);
     }
     std::swap(X, Xn);
   }
-  const float lr = (float)((double)h->lr_matrix * std::sqrt(std::max(1.0, (double)r / c)));
-  if (e == hipSuccess) e = muon_apply<T>(r, c, X, lr, master + t.off, params + t.off, ctx->stream);
+  first = 0;
+  for (const MuonSet& st : grp.sets) {
+    const float lr = (float)((double)h->lr_matrix * std::sqrt(std::max(1.0, (double)st.r / st.c)));
+    if (e == hipSuccess)
+      e = muon_apply<T>(st.r, st.c, st.count, st.stride, X + first * sx, lr, master + st.off0, params + st.off0,
+                        ctx->stream);
+    first += st.count;
+  }
   return e;
 }
 
@@ -649,12 +700,11 @@ template <typename T>
 int optimizer_step(nc_ctx* ctx, float* master, T* params, const float* grads, float* state, char* scratch,
                    const nc_optim_hparams* h) {
   const OptimScratch sc = optim_scratch(ctx->cfg);
-  for (const OptimTensor& t : optim_tensors(ctx->cfg)) {
+  for (const OptimTensor& t : optim_tensors(ctx->cfg))
     if (t.tensor == NC_T_E || t.tensor == NC_T_U)
       NC_TRY(optim_adamw<T>(ctx, t, master, params, grads, state, h), "AdamW");
-    else
-      NC_TRY(optim_muon<T>(ctx, t, master, params, grads, state, scratch, sc, h), "Muon");
-  }
+  for (const MuonGroup& grp : muon_groups(ctx->cfg))
+    NC_TRY(optim_muon<T>(ctx, grp, master, params, grads, state, scratch, sc, h), "Muon");
   return NC_OK;
 }
 

@@ -73,6 +73,11 @@ struct GemmDesc {
   const float* inv_nvalid;  // device scalar
   // EPI_AXPBY
   float ep_alpha, ep_gamma;
+  // batched products (EPI_STORE / EPI_AXPBY, splits == 1): item b reads
+  // P + b sP, Q + b sQ, aux + b sAux and writes C + b sC (elements);
+  // batch 0 or 1 is a single product
+  int batch;
+  int64_t sP, sQ, sC, sAux;
 };
 
 // ---------------------------------------------------------------------------
@@ -145,14 +150,19 @@ template <typename T> hipError_t adamw(int64_t n, float* p, const float* g, floa
                                        const AdamwArgs& a, hipStream_t s);
 constexpr int kMuonMaxPartials = 1024;
 int muon_partials(int64_t n);   // partial sums muon_momentum writes for n elements
-// buf = mu buf + scale g;  partials[i] = sum of u^2 over block i's elements,
-// u = scale g + mu buf (nesterov) or buf;  n % 4 == 0
-hipError_t muon_momentum(int64_t n, const float* g, float* buf, float scale, float mu, int nesterov, float* partials,
-                         hipStream_t s);
+// Each call covers `count` matrices of n = r * c elements, matrix j at
+// element offset j * stride of g / buf / W / out, with its partial sums at
+// partials + j * kMuonMaxPartials and its iteration operand at X + j * r * c.
+// buf = mu buf + scale g;  partials[j][i] = sum of u^2 over block i's
+// elements, u = scale g + mu buf (nesterov) or buf;  n % 4 == 0
+hipError_t muon_momentum(int64_t n, int count, int64_t stride, const float* g, float* buf, float scale, float mu,
+                         int nesterov, float* partials, hipStream_t s);
 // X = u / (||u||_F + eps) as [r][c], or [c][r] when r > c;  r, c multiples of 64
-template <typename T> hipError_t muon_normalise(int r, int c, const float* g, const float* buf, float scale, float mu,
-                                                int nesterov, const float* partials, float eps, T* X, hipStream_t s);
+template <typename T> hipError_t muon_normalise(int r, int c, int count, int64_t stride, const float* g,
+                                                const float* buf, float scale, float mu, int nesterov,
+                                                const float* partials, float eps, T* X, hipStream_t s);
 // W [r][c] -= lr X (X [r][c], or [c][r] when r > c);  out = W in the model dtype
-template <typename T> hipError_t muon_apply(int r, int c, const T* X, float lr, float* W, T* out, hipStream_t s);
+template <typename T> hipError_t muon_apply(int r, int c, int count, int64_t stride, const T* X, float lr, float* W,
+                                            T* out, hipStream_t s);
 
 }  // namespace nc

@@ -167,10 +167,11 @@ def test_optim_sizes():
     assert nc.optim_state_bytes(cfg) == 4 * (P + 2 * cfg.vocab * cfg.d_model)
     blk = synthdata.get_config("block")
     assert nc.optim_state_bytes(blk) == 4 * synthdata.param_count(blk)
-    # two ping-pong copies of the largest matrix (d x 4d), two d x d products
-    # and 4 KB of partial sums, 256-byte aligned
+    # Newton-Schulz operands batched per shape group: two ping-pong copies
+    # of the 40 d x 4d matrices (W1 transposed, W2), two d x d products for
+    # each of the 80 square ones, and 4 KB of partial sums per matrix
     es = 2
-    assert nc.optim_scratch_bytes(cfg) == 4096 + 2 * 5120 * 1280 * es + 2 * 1280 * 1280 * es
+    assert nc.optim_scratch_bytes(cfg) == 80 * 4096 + 2 * 40 * 5120 * 1280 * es + 2 * 80 * 1280 * 1280 * es
     with pytest.raises(nc.NcError):
         nc.optim_default(cfg, 5, 4, 1)          # it past num_iters
     with pytest.raises(nc.NcError):
