@@ -10,8 +10,9 @@
 namespace nc {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;      // four waves (the block reductions assume it)
 constexpr int kTile = 64;          // transposing tiles: 64 x 64 elements
+static_assert(kThreads == 256, "block reductions");
 
 __device__ inline float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ inline void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
@@ -100,18 +101,20 @@ __global__ void __launch_bounds__(kThreads) k_muon_normalise(int r, int c, const
                                                               int nparts, float eps, T* __restrict__ X,
                                                               int64_t stride) {
   __shared__ float tile[kTile][kTile + 1];
-  __shared__ float s_inv;
+  __shared__ double red[kThreads / 64];
   g += blockIdx.z * stride;
   buf += blockIdx.z * stride;
   partials += (int64_t)blockIdx.z * kMuonMaxPartials;
   X += (int64_t)blockIdx.z * r * c;
-  if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int i = 0; i < nparts; ++i) t += (double)partials[i];
-    s_inv = (float)(1.0 / (sqrt(t) + (double)eps));
-  }
+  // ||u||^2: thread t sums partials t, t + 256, ... in fp64, then a fixed
+  // tree over the block -- the same order in every block
+  double t = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += kThreads) t += (double)partials[i];
+  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
   __syncthreads();
-  const float inv = s_inv;
+  const double total = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = (float)(1.0 / (sqrt(total) + (double)eps));
   const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
   const int tc = (threadIdx.x & 15) * 4, tr = threadIdx.x >> 4;   // 16 x 4 columns, 16 rows per sweep
   const bool tall = r > c;

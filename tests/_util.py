@@ -64,3 +64,23 @@ def flat_tensors(cfg, flat_or_dict):
         else:
             a = flat_or_dict[off:off + r * c].reshape(r, c)
         yield name, layer, a
+
+
+def newton_schulz_bf16(G, steps, coeffs, eps=1e-7):
+    """Error model of the Newton-Schulz iteration run with bf16 operands and
+    fp32 accumulation: the oracle's iteration (oracle/optim.py) with every
+    product's result rounded to bf16 where the library stores it (X, A,
+    B = c A A + b A, X' = B X + a X).  It serves only to size the
+    tolerance: on rank-deficient inputs (real gradients of a few hundred
+    tokens) bf16 rounding alone moves the result well past a fixed cosine
+    bar, and this says by how much for the input at hand."""
+    a, b, c = coeffs
+    r32 = lambda x: synthdata.bf16_bits_to_f32(synthdata.f32_to_bf16_bits(np.asarray(x, np.float32))).astype(np.float64)
+    tall = G.shape[0] > G.shape[1]
+    X = G.T if tall else G
+    X = r32(X / (np.linalg.norm(X) + eps))
+    for _ in range(steps):
+        A = r32(X @ X.T)
+        B = r32(c * (A @ A.T) + b * A)
+        X = r32(B @ X + a * X)
+    return X.T if tall else X

@@ -16,7 +16,7 @@ import pytest
 
 import synthdata
 from oracle import optim as oopt
-from tests._util import cosine, dev, empty, host, zeros
+from tests._util import cosine, dev, empty, host, newton_schulz_bf16, zeros
 
 pytestmark = pytest.mark.gpu
 
@@ -118,6 +118,43 @@ def test_two_steps_match_oracle(name, portable):
         run.step(g, h)
     prec = (0.999, 0.03) if cfg.dtype == "bf16" else (1 - 1e-8, 1e-4)
     _check_against_oracle(cfg, run, master, grads, hps, *prec)
+
+
+def test_real_gradients_within_bf16_error():
+    """One step on the model's own gradients (the oracle's fp64 gradients of
+    a small batch, rounded to fp32), whose matrices are close to rank
+    deficient.  Each matrix's Muon update must sit as close to the fp64
+    oracle's as bf16 arithmetic allows: cosine no lower than the CPU bf16
+    error model's (tests/_util.py) minus 0.002, and at least 0.99."""
+    import oracle
+    cfg = synthdata.get_config("small").with_(batch=2)
+    params = synthdata.make_params(cfg)
+    idx, tgt = synthdata.make_tokens(cfg, rows=2)
+    want = oracle.train_step(cfg, synthdata.split_params(cfg, params.astype(np.float64)), idx, tgt,
+                             synthdata.make_token_bytes(cfg))
+    layout = synthdata.param_layout(cfg)
+    grads = np.zeros(params.size, dtype=np.float32)
+    for name, layer, r, c, off in layout:
+        w = want["grads"][name] if layer < 0 else want["grads"]["layers"][layer][name]
+        grads[off:off + r * c] = w.ravel()
+    master = params.astype(np.float32)
+    run = _Run(cfg, master)
+    h = run.nc.optim_default(run.c, 0, 100)
+    run.step(grads, h)
+    got = host(run.master)
+    hp = _hp_dict(h)
+    for name, layer, r, c, off in layout:
+        if name in ("E", "U"):
+            continue
+        sl = slice(off, off + r * c)
+        W, G = master[sl].reshape(r, c).astype(np.float64), grads[sl].reshape(r, c).astype(np.float64)
+        Wn, _ = oopt.muon_update(W, G, np.zeros_like(W), hp["lr_matrix"], hp["momentum"])
+        dw = (Wn - W).ravel()
+        u = (1 + hp["momentum"]) * G
+        emu = newton_schulz_bf16(u, hp["ns_steps"], hp["ns_coeffs"])
+        cos_emu = cosine(emu, oopt.newton_schulz(u, hp["ns_steps"], hp["ns_coeffs"]))
+        cs = cosine(got[sl] - master[sl], dw)
+        assert cs >= min(cos_emu - 0.002, 0.999) and cs >= 0.99, (name, layer, cs, cos_emu)
 
 
 def test_deterministic_and_grad_scale_exact():
