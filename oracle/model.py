@@ -158,14 +158,15 @@ def cross_entropy(z, tgt):
 
 
 def cross_entropy_grad(z, tgt, scale):
-    """d(scale * sum ce)/dz = scale * (softmax(z) - onehot(tgt)); rows with
-    an ignored target get 0."""
+    """d(sum_t scale_t ce[t])/dz = scale_t (softmax(z_t) - onehot(tgt_t));
+    scale is one number or one per row; rows with an ignored target get 0."""
     dz = _softmax_rows(z)
     valid = tgt >= 0
     rows = np.nonzero(valid)[0]
     dz[rows, tgt[rows]] -= 1.0
     dz[~valid] = 0.0
-    return dz * scale
+    scale = np.asarray(scale, dtype=np.float64)
+    return dz * (scale[:, None] if scale.ndim == 1 else scale)
 
 
 def loss_bpb(ce, tgt, token_bytes):
@@ -185,6 +186,17 @@ def loss_bpb(ce, tgt, token_bytes):
 # ---------------------------------------------------------------------------
 # one pre-norm block
 # ---------------------------------------------------------------------------
+
+def weighted_loss(ce, tgt, weights):
+    """(sum over valid targets of w_t ce[t], that sum / n_valid); 0 when no
+    target is valid."""
+    ce = np.asarray(ce, dtype=np.float64).ravel()
+    valid = np.asarray(tgt).ravel() >= 0
+    w = np.asarray(weights, dtype=np.float64).ravel()
+    s = float(np.sum(np.where(valid, w * ce, 0.0)))
+    n = int(np.sum(valid))
+    return s, (s / n if n else 0.0)
+
 def block_forward(lp, x, cfg, phi):
     """x [T, d] -> y [T, d]; returns (y, cache)."""
     T, d = x.shape
@@ -278,13 +290,17 @@ def _to64(params):
     return out
 
 
-def train_step(cfg, params, idx, tgt, token_bytes, want_grads=True, rows=None):
+def train_step(cfg, params, idx, tgt, token_bytes, want_grads=True, rows=None, token_weights=None):
     """One fwd(+bwd) step over the batch.
 
     params: {"E", "U", "layers": [{"Wq", "Wk", "Wv", "Wo", "W1", "W2"}]}
     idx, tgt: int [B, T].  Gradients are of the mean cross-entropy over all
-    valid targets of the batch.  ``rows`` limits the work to the given row
-    indices (the loss normalisation still counts the whole batch)."""
+    valid targets of the batch, or, with token_weights w [B, T], of
+    sum_t w_t ce[t] / n_valid (the token-level weighted loss of the
+    simplified GRPO, section Reinforcement learning: per-token advantage
+    weights, normalised over tokens rather than sequences).  ``rows`` limits
+    the work to the given row indices (the loss normalisation still counts
+    the whole batch)."""
     p = _to64(params)
     idx = np.asarray(idx)
     tgt = np.asarray(tgt)
@@ -298,7 +314,8 @@ def train_step(cfg, params, idx, tgt, token_bytes, want_grads=True, rows=None):
         ce_b, cache = model_forward_row(p, idx[b], tgt[b], cfg, phi)
         ce[b] = ce_b
         if want_grads:
-            model_backward_row(p, cache, cfg, scale, grads)
+            row_scale = scale if token_weights is None else scale * np.asarray(token_weights[b], dtype=np.float64)
+            model_backward_row(p, cache, cfg, row_scale, grads)
         del cache
     out = dict(ce=ce, grads=grads)
     if rows is None:

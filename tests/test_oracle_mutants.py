@@ -30,6 +30,9 @@ MUTANTS = [
     ("(s / (LN2 * nbytes) if nbytes else 0.0)", "(s / nbytes if nbytes else 0.0)"),          # bpb without ln 2
     ("xf, rf = rmsnorm(x, cfg.rms_eps)", "xf, rf = x, np.ones(x.shape[0])"),                 # dropped final norm
     ("dq = rope(dqr, phi, inverse=True)", "dq = rope(dqr, phi)"),                            # wrong inverse rotation
+    ("row_scale = scale if token_weights is None else scale * np.asarray(token_weights[b], dtype=np.float64)",
+     "row_scale = scale"),                                                                    # token weights ignored
+    ("np.where(valid, w * ce, 0.0)", "np.where(valid, ce, 0.0)"),                            # weighted loss unweighted
 ]
 
 # (text in oracle/optim.py, the mistake that replaces it)

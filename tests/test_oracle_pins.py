@@ -397,3 +397,65 @@ def test_block_step_gradient_finite_differences():
         fd = (np.sum(oracle.block_step(cfg, lpp, x, dy)["y"] * dy)
               - np.sum(oracle.block_step(cfg, lpm, x, dy)["y"] * dy)) / (2 * h)
         assert fd == pytest.approx(np.sum(out["grads"][k] * w), rel=1e-7), k
+
+
+# --------------------------------------------------------------------------
+# token-weighted cross-entropy (the simplified GRPO's per-token advantages)
+# --------------------------------------------------------------------------
+def _weighted_objective(cfg, flat, idx, tgt, tb, w):
+    out = oracle.train_step(cfg, synthdata.split_params(cfg, flat), idx, tgt, tb, want_grads=False)
+    return oracle.weighted_loss(out["ce"], tgt, w)[1]
+
+
+def test_weighted_gradient_finite_differences():
+    """The weighted gradient is the derivative of sum_t w_t ce[t] / n_valid,
+    by fp64 central differences along a random direction and on single
+    entries, with weights of both signs and an ignored target."""
+    cfg = MICRO
+    flat, p = _micro_params(seed=21)
+    idx, tgt = synthdata.make_tokens(cfg)
+    tgt = tgt.copy()
+    tgt[0, 3] = -1
+    tb = synthdata.make_token_bytes(cfg)
+    w = _rng(22).standard_normal(tgt.shape)
+    g = np.concatenate(_flat(oracle.train_step(cfg, p, idx, tgt, tb, token_weights=w)["grads"], cfg))
+    rng = _rng(23)
+    h = 1e-5
+    v = rng.standard_normal(flat.shape)
+    fd = (_weighted_objective(cfg, flat + h * v, idx, tgt, tb, w)
+          - _weighted_objective(cfg, flat - h * v, idx, tgt, tb, w)) / (2 * h)
+    assert fd == pytest.approx(float(g @ v), rel=1e-7)
+    for j in rng.choice(flat.size, size=6, replace=False):
+        e = np.zeros_like(flat)
+        e[j] = h
+        fd = (_weighted_objective(cfg, flat + e, idx, tgt, tb, w)
+              - _weighted_objective(cfg, flat - e, idx, tgt, tb, w)) / (2 * h)
+        assert fd == pytest.approx(g[j], rel=1e-6, abs=1e-10)
+
+
+def test_weighted_gradient_special_cases():
+    """Unit weights give the unweighted gradient bit for bit; zero weight on
+    a set of tokens equals ignoring those targets, rescaled by the changed
+    count; the gradient is linear in the weights."""
+    cfg = MICRO
+    flat, p = _micro_params(seed=24)
+    idx, tgt = synthdata.make_tokens(cfg)
+    tb = synthdata.make_token_bytes(cfg)
+    plain = np.concatenate(_flat(oracle.train_step(cfg, p, idx, tgt, tb)["grads"], cfg))
+    ones = np.concatenate(_flat(oracle.train_step(cfg, p, idx, tgt, tb, token_weights=np.ones(tgt.shape))["grads"],
+                                cfg))
+    np.testing.assert_array_equal(plain, ones)
+    keep = np.ones(tgt.shape)
+    keep[1, :5] = 0.0
+    keep[0, 7] = 0.0
+    zeroed = np.concatenate(_flat(oracle.train_step(cfg, p, idx, tgt, tb, token_weights=keep)["grads"], cfg))
+    masked_tgt = np.where(keep > 0, tgt, -1)
+    masked = np.concatenate(_flat(oracle.train_step(cfg, p, idx, masked_tgt, tb)["grads"], cfg))
+    n_all, n_kept = tgt.size, int(keep.sum())
+    np.testing.assert_allclose(zeroed, masked * n_kept / n_all, rtol=1e-12, atol=1e-15)
+    w1, w2 = _rng(25).standard_normal(tgt.shape), _rng(26).standard_normal(tgt.shape)
+    g1, g2, g12 = (np.concatenate(_flat(oracle.train_step(cfg, p, idx, tgt, tb, token_weights=w)["grads"], cfg))
+                   for w in (w1, w2, w1 + w2))
+    np.testing.assert_allclose(g12, g1 + g2, rtol=1e-10, atol=1e-14)
+    s, m = oracle.weighted_loss(np.ones(tgt.shape), tgt, w1)
+    assert s == pytest.approx(w1.sum()) and m == pytest.approx(w1.sum() / tgt.size)
