@@ -72,6 +72,8 @@ _SIGS = {
     "nc_optim_state_bytes": (_I64, [ctypes.POINTER(NcConfig)]),
     "nc_optim_scratch_bytes": (_I64, [ctypes.POINTER(NcConfig)]),
     "nc_optimizer_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(NcOptimHparams)]),
+    "nc_backward_weighted": (ctypes.c_int, [_P, _P, _P, _I32, _P]),
+    "nc_loss_weighted": (ctypes.c_int, [_P, _P, _P]),
     "nc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nc_init": (ctypes.c_int, [ctypes.POINTER(NcConfig), _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
     "nc_set_stream": (ctypes.c_int, [_P, _P]),
@@ -222,6 +224,15 @@ class Context:
 
     def backward(self, params, grads, accumulate: bool = False):
         _check(lib().nc_backward(self.h, _ptr(params), _ptr(grads), int(bool(accumulate))), "nc_backward", self.h)
+
+    def backward_weighted(self, params, grads, token_weights, accumulate: bool = False):
+        """nc_backward_weighted: gradient of sum_t w_t ce[t] / n_valid."""
+        _check(lib().nc_backward_weighted(self.h, _ptr(params), _ptr(grads), int(bool(accumulate)),
+                                          _ptr(token_weights)), "nc_backward_weighted", self.h)
+
+    def loss_weighted(self, token_weights, out):
+        """nc_loss_weighted: out[0] = sum_t w_t ce[t], out[1] = that / n_valid."""
+        _check(lib().nc_loss_weighted(self.h, _ptr(token_weights), _ptr(out)), "nc_loss_weighted", self.h)
 
     def trace_enable(self, family):
         """Time launches of one kernel family (a name from TRACE_FAMILIES or

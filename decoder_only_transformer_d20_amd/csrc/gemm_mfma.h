@@ -205,11 +205,12 @@ struct TileMap {
 };
 
 // Finish and store four consecutive outputs (row m, columns n .. n+3) of a
-// row-order epilogue: x holds the fp32 products; y, cs, dz_t, dz_l are the
-// row's prefetched inputs (aux pair, rotary factors, target and lse).
+// row-order epilogue: x holds the fp32 products; y, cs, dz_t, dz_l, dz_s
+// are the row's prefetched inputs (aux pair, rotary factors, target, lse
+// and the dz row factor).
 template <int EPI>
 __device__ inline void epi_store4(const GemmDesc& g, const GemmTile& c, int64_t m, int64_t n, float (&x)[4],
-                                  uint2 y, float4 cs, bool rot, int dz_t, float dz_l, float inv_nv) {
+                                  uint2 y, float4 cs, bool rot, int dz_t, float dz_l, float dz_s) {
   if constexpr (EPI == EPI_F32) {
     if (g.splits > 1) {
       float* dst = g.part + (int64_t)c.split * g.M * g.N + m * g.N + n;
@@ -257,7 +258,6 @@ __device__ inline void epi_store4(const GemmDesc& g, const GemmTile& c, int64_t 
     for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], 0.f) * fmaxf(x[e], 0.f);
   }
   if constexpr (EPI == EPI_DZ) {
-    const float dz_s = dz_t >= 0 ? inv_nv : 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       x[e] = (__builtin_amdgcn_exp2f(x[e] * kLog2e - dz_l) - ((n + e) == dz_t ? 1.f : 0.f)) * dz_s;
@@ -558,7 +558,6 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
       const int cc = etid % CPR, r0 = etid / CPR;
       const int64_t n = c.n0 + 4 * cc;
       constexpr int NR = WTM / RPS;                    // rows per thread and pass
-      const float inv_nv = EPI == EPI_DZ ? *g.inv_nvalid : 0.f;
       int pi = 0;
       if constexpr (EPI == EPI_ROPE) pi = (int)(n % g.head_dim) >> 1;
       const bool rot = EPI == EPI_ROPE && n < g.rope_cols;
@@ -568,11 +567,11 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
         // The pass's global inputs (aux rows, rotary factors, per-row loss
         // terms) are requested W rows ahead of their use, the first W
         // before the LDS round trip, which hides their latency.
-        constexpr int W = EPI == EPI_ROPE ? (NR >= 16 ? NR / 4 : NR) : (NR >= 8 ? NR / 2 : NR);
+        constexpr int W = (EPI == EPI_ROPE || EPI == EPI_DZ) ? (NR >= 16 ? NR / 4 : NR) : (NR >= 8 ? NR / 2 : NR);
         uint2 pa[W];
         float4 pc[W];
         int pt[W];
-        float pl[W];
+        float pl[W], ps[W];
         // rotary: position of the pass's first row in its sequence (rows
         // index tokens; the table is read for every column, in bounds, and
         // used where rot holds)
@@ -594,6 +593,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
           if constexpr (EPI == EPI_DZ) {
             pt[k % W] = g.tgt[m];
             pl[k % W] = g.lse[m];
+            ps[k % W] = g.row_scale[m];
           }
         };
 #pragma unroll
@@ -624,8 +624,9 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
           const float4 cs = pc[k % W];
           const int dz_t = pt[k % W];
           const float dz_l = pl[k % W] * kLog2e;
+          const float dz_s = ps[k % W];
           if (k + W < NR) fetch(k + W);
-          epi_store4<EPI>(g, c, m, n, x, y, cs, rot, dz_t, dz_l, inv_nv);
+          epi_store4<EPI>(g, c, m, n, x, y, cs, rot, dz_t, dz_l, dz_s);
         }
         if (h == 0) __syncthreads();
       }

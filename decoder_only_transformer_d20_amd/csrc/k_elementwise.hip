@@ -474,6 +474,44 @@ __global__ void __launch_bounds__(1024) k_count_valid(const int32_t* __restrict_
   if (threadIdx.x == 0) *inv = red[0] > 0 ? (float)(1.0 / (double)red[0]) : 0.f;
 }
 
+// per-row factor of the head's dz: 1/n_valid (times the token's weight when
+// weights are given) for a valid target, 0 for an ignored one
+__global__ void __launch_bounds__(256) k_row_scale(const int32_t* __restrict__ tgt, const float* __restrict__ w,
+                                                    const float* __restrict__ inv, int64_t n, float* __restrict__ out) {
+  const float iv = *inv;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    out[i] = tgt[i] >= 0 ? (w ? iv * w[i] : iv) : 0.f;
+}
+
+// one block, fixed order: out = {sum w ce, sum w ce / n} over valid targets
+__global__ void __launch_bounds__(1024) k_weighted_loss(const float* __restrict__ ce, const int32_t* __restrict__ tgt,
+                                                        const float* __restrict__ w, int64_t n, double* out) {
+  __shared__ double sce[1024];
+  __shared__ int64_t sn[1024];
+  double a = 0.0;
+  int64_t c = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) {
+    if (tgt[i] >= 0) {
+      a += (double)w[i] * (double)ce[i];
+      c += 1;
+    }
+  }
+  sce[threadIdx.x] = a;
+  sn[threadIdx.x] = c;
+  __syncthreads();
+  for (int k = 512; k > 0; k >>= 1) {
+    if ((int)threadIdx.x < k) {
+      sce[threadIdx.x] += sce[threadIdx.x + k];
+      sn[threadIdx.x] += sn[threadIdx.x + k];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out[0] = sce[0];
+    out[1] = sn[0] > 0 ? sce[0] / (double)sn[0] : 0.0;
+  }
+}
+
 // one block, fixed order: out = {sum ce / n, sum ce / (ln2 * sum bytes), sum ce, sum bytes, n}
 __global__ void __launch_bounds__(1024) k_loss_bpb(const float* __restrict__ ce, const int32_t* __restrict__ tgt,
                                                    const int32_t* __restrict__ bytes, int64_t n, double* out) {
@@ -712,6 +750,15 @@ hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int
 }
 hipError_t count_valid(const int32_t* tgt, int64_t n, float* inv, hipStream_t s) {
   k_count_valid<<<1, 1024, 0, s>>>(tgt, n, inv);
+  return hipGetLastError();
+}
+hipError_t row_scale(const int32_t* tgt, const float* w, const float* inv_nvalid, int64_t n, float* out,
+                     hipStream_t s) {
+  k_row_scale<<<nblocks(n, 256), 256, 0, s>>>(tgt, w, inv_nvalid, n, out);
+  return hipGetLastError();
+}
+hipError_t weighted_loss(const float* ce, const int32_t* tgt, const float* w, int64_t n, double* out, hipStream_t s) {
+  k_weighted_loss<<<1, 1024, 0, s>>>(ce, tgt, w, n, out);
   return hipGetLastError();
 }
 hipError_t loss_bpb(const float* ce, const int32_t* tgt, const int32_t* bytes, int64_t n, double* out,

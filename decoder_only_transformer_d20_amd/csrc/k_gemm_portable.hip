@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(256) k_gemm_portable(GemmDesc g) {
       case EPI_DZ: {
         const int t = g.tgt[m];
         const float l = g.lse[m];
-        const float sc = t >= 0 ? *g.inv_nvalid : 0.f;
+        const float sc = g.row_scale[m];
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = (expf(v[j] - l) - ((n + j) == t ? 1.f : 0.f)) * sc;
         break;

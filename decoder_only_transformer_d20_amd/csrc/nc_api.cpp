@@ -91,7 +91,7 @@ int choose_splits(const nc_config& c, int M, int N, int64_t K) {
 
 struct Plan {
   size_t total = 0;
-  size_t rope = 0, idx = 0, tgt = 0, x = 0, xf = 0, rf = 0, ce = 0, lse_head = 0, ztgt = 0, lse_part = 0;
+  size_t rope = 0, idx = 0, tgt = 0, x = 0, xf = 0, rf = 0, ce = 0, lse_head = 0, ztgt = 0, lse_part = 0, rowscale = 0;
   size_t scalars = 0, dz = 0, g = 0, gtmp = 0, big = 0, part = 0, delta = 0, wt = 0, embs = 0;
   size_t layer0 = 0, layer_stride = 0;
   size_t l_a = 0, l_r1 = 0, l_qkv = 0, l_o = 0, l_lse = 0, l_m = 0, l_r2 = 0, l_u = 0;
@@ -127,6 +127,7 @@ Plan make_plan(const nc_config& c) {
   if (!is_block(c)) {
     p.idx = take(N * 4);
     p.tgt = take(N * 4);
+    p.rowscale = take(N * 4);
     p.x = take(N * d * es);
     p.xf = take(N * d * es);
     p.rf = take(N * 4);
@@ -459,7 +460,7 @@ int model_forward(nc_ctx* ctx, const T* params, const int32_t* idx, const int32_
 }
 
 template <typename T>
-int model_backward(nc_ctx* ctx, const T* params, float* grads, int accumulate) {
+int model_backward(nc_ctx* ctx, const T* params, float* grads, int accumulate, const float* tok_w) {
   const nc_config& c = ctx->cfg;
   const Plan& p = ctx->plan;
   const int N = c.batch * c.seq_len, d = c.d_model, V = c.vocab;
@@ -474,14 +475,17 @@ int model_backward(nc_ctx* ctx, const T* params, float* grads, int accumulate) {
   T* tmp = ctx->at<T>(p.gtmp);
   T* dz = ctx->at<T>(p.dz);
   const int32_t* wtgt = ctx->at<int32_t>(p.tgt);
-  // head, one token chunk at a time: dz = (softmax(z) - onehot) / n_valid,
-  // dxf = dz U, dU (+)= dz^T xf.  (U is transposed once, for every chunk.)
+  // head, one token chunk at a time: dz = (softmax(z) - onehot) w / n_valid
+  // (w = 1 unless token weights are given), dxf = dz U, dU (+)= dz^T xf.
+  // (U is transposed once, for every chunk.)
+  float* rs = ctx->at<float>(p.rowscale);
+  NC_TRY(row_scale(wtgt, tok_w, ctx->at<float>(p.scalars), N, rs, s), "dz row factors");
   GemmDesc gx;
   NC_TRY(dgrad_desc<T>(ctx, 0, dz, V, U, V, d, EPI_STORE, tmp, d, &gx), "transpose U");
   for (int64_t r0 = 0; r0 < N; r0 += p.head_chunk) {
     const int Mc = (int)std::min<int64_t>(p.head_chunk, N - r0);
     GemmDesc g = gemm(Mc, V, d, xf + r0 * d, d, 0, U, d, 0, EPI_DZ, dz, V);
-    g.tgt = wtgt + r0; g.lse = ctx->at<float>(p.lse_head) + r0; g.inv_nvalid = ctx->at<float>(p.scalars);
+    g.tgt = wtgt + r0; g.lse = ctx->at<float>(p.lse_head) + r0; g.row_scale = rs + r0;
     NC_TRY(run_gemm(ctx, g), "recompute logits -> dz");
     gx.M = Mc;
     gx.C = tmp + r0 * d;
@@ -847,8 +851,27 @@ int nc_backward(nc_ctx* ctx, const void* params, float* grads, int32_t accumulat
   if (!ctx || !params || !grads) return NC_ERR_INVALID_ARG;
   if (accumulate != 0 && accumulate != 1) return NC_ERR_INVALID_ARG;
   if (!ctx->have_forward) return NC_ERR_STATE;
-  return is_bf16(ctx->cfg) ? model_backward<bf16>(ctx, (const bf16*)params, grads, accumulate)
-                           : model_backward<float>(ctx, (const float*)params, grads, accumulate);
+  return is_bf16(ctx->cfg) ? model_backward<bf16>(ctx, (const bf16*)params, grads, accumulate, nullptr)
+                           : model_backward<float>(ctx, (const float*)params, grads, accumulate, nullptr);
+}
+
+int nc_backward_weighted(nc_ctx* ctx, const void* params, float* grads, int32_t accumulate,
+                         const float* token_weights) {
+  if (!ctx || !params || !grads || !token_weights) return NC_ERR_INVALID_ARG;
+  if (accumulate != 0 && accumulate != 1) return NC_ERR_INVALID_ARG;
+  if (!ctx->have_forward) return NC_ERR_STATE;
+  return is_bf16(ctx->cfg) ? model_backward<bf16>(ctx, (const bf16*)params, grads, accumulate, token_weights)
+                           : model_backward<float>(ctx, (const float*)params, grads, accumulate, token_weights);
+}
+
+int nc_loss_weighted(nc_ctx* ctx, const float* token_weights, double* out) {
+  if (!ctx || !token_weights || !out) return NC_ERR_INVALID_ARG;
+  if (!ctx->have_forward) return NC_ERR_STATE;
+  const Plan& p = ctx->plan;
+  const int64_t N = (int64_t)ctx->cfg.batch * ctx->cfg.seq_len;
+  NC_TRY(weighted_loss(ctx->at<float>(p.ce), ctx->at<int32_t>(p.tgt), token_weights, N, out, ctx->stream),
+         "weighted loss");
+  return NC_OK;
 }
 
 int nc_block_forward(nc_ctx* ctx, const void* block_params, const void* x, void* y) {

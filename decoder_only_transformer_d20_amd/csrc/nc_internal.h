@@ -70,7 +70,7 @@ struct GemmDesc {
   int lse_stride;           // number of N-tiles
   float* ztgt;              // [M]
   const float* lse;         // [M]
-  const float* inv_nvalid;  // device scalar
+  const float* row_scale;   // [M] factor of row m's dz: w_m / n_valid, 0 for an ignored target
   // EPI_AXPBY
   float ep_alpha, ep_gamma;
   // batched products (EPI_STORE / EPI_AXPBY, splits == 1): item b reads
@@ -128,6 +128,11 @@ hipError_t rope_table(float2* tab, int T, int Q, float base, hipStream_t s);
 hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int32_t* tgt,
                       float* lse, float* ce, int64_t rows, hipStream_t s);
 hipError_t count_valid(const int32_t* tgt, int64_t n, float* inv_nvalid, hipStream_t s);
+// out[i] = tgt[i] >= 0 ? *inv_nvalid * (w ? w[i] : 1) : 0
+hipError_t row_scale(const int32_t* tgt, const float* w, const float* inv_nvalid, int64_t n, float* out,
+                     hipStream_t s);
+// out = {sum over valid targets of w ce, that sum / n_valid}, fp64, fixed order
+hipError_t weighted_loss(const float* ce, const int32_t* tgt, const float* w, int64_t n, double* out, hipStream_t s);
 hipError_t loss_bpb(const float* ce, const int32_t* tgt, const int32_t* bytes, int64_t n, double* out, hipStream_t s);
 hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
 // out [cols][rows] = transpose of in [rows][cols]; rows, cols multiples of 8

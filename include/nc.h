@@ -161,6 +161,21 @@ int nc_loss_bpb(nc_ctx* ctx, const int32_t* token_bytes, double* out);
  * runs in a fixed order, so repeated calls give identical bits. */
 int nc_backward(nc_ctx* ctx, const void* params, float* grads, int32_t accumulate);
 
+/* Token-weighted variant (the simplified GRPO of section Reinforcement
+ * learning: per-token advantage weights, normalised over tokens, no
+ * reference model, no ratio clipping): the gradient of
+ *   sum over valid targets t of w_t ce[t] / n_valid
+ * with token_weights w device fp32 [B*T] (any sign; ignored targets still
+ * contribute nothing).  w = 1 everywhere gives nc_backward's result bit for
+ * bit.  Otherwise as nc_backward. */
+int nc_backward_weighted(nc_ctx* ctx, const void* params, float* grads, int32_t accumulate,
+                         const float* token_weights);
+
+/* The weighted objective of the last nc_forward: out device double [2] =
+ * {sum over valid targets of w_t ce[t], that sum / n_valid} (fp64, fixed
+ * order; 0 / 0 gives 0).  NC_ERR_STATE without a prior nc_forward. */
+int nc_loss_weighted(nc_ctx* ctx, const float* token_weights, double* out);
+
 /* ---- single block (NC_FLAG_BLOCK_ONLY) ------------------------------------ */
 
 /* y = block(x) for x, y device dtype [B*T, d] (may not alias).  Saves what

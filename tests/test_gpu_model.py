@@ -131,6 +131,61 @@ def test_small_bf16_matches_oracle(portable):
         assert cosine(g, w) >= 0.999, (name, layer, cosine(g, w))
 
 
+def _gpu_weighted(cfg, params, idx, tgt, w, portable=False):
+    sess = nc.Session(cfg, portable=portable)
+    P, W = dev(params, cfg.dtype), dev(w)
+    sess.forward(P, dev(idx.ravel()), dev(tgt.ravel()))
+    out, g = empty((2,), "f64"), empty((params.size,), "f32")
+    sess.loss_weighted(W, out)
+    sess.backward_weighted(P, g, W)
+    torch.cuda.synchronize()
+    return host(out), host(g)
+
+
+def _check_weighted(cfg, params, idx, tgt, tb, w, got_out, got_g, bf16):
+    want = _oracle_step(cfg, params, idx, tgt, tb, token_weights=w.astype(np.float64))
+    s, m = oracle.weighted_loss(want["ce"], tgt, w.astype(np.float64))
+    # the weighted sum can cancel: its error is measured against sum |w ce|
+    scale = float(np.sum(np.abs(w.astype(np.float64) * want["ce"])))
+    tol = 1e-2 if bf16 else 1e-4
+    assert abs(got_out[0] - s) <= tol * scale and abs(got_out[1] - m) <= tol * scale / np.sum(tgt >= 0)
+    for (name, layer, g), (_, _, wt) in zip(flat_tensors(cfg, got_g), flat_tensors(cfg, want["grads"])):
+        if bf16:
+            assert cosine(g, wt) >= 0.999, (name, layer, cosine(g, wt))
+        else:
+            assert max_rel_err(g, wt) <= 1e-4, (name, layer, max_rel_err(g, wt))
+
+
+def test_tiny_fp32_weighted_matches_oracle():
+    """Token-weighted loss and gradient (weights of both signs, an ignored
+    target) against the oracle's sum_t w_t ce[t] / n_valid."""
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("tiny"), ignore=[(1, 5)])
+    w = np.random.default_rng(41).standard_normal(tgt.shape).astype(np.float32)
+    out, g = _gpu_weighted(cfg, params, idx, tgt, w)
+    _check_weighted(cfg, params, idx, tgt, tb, w, out, g, bf16=False)
+
+
+@pytest.mark.parametrize("portable", [False, True])
+def test_small_bf16_weighted_matches_oracle(portable):
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("small"), ignore=[(2, 17)])
+    # per-row advantages, as the simplified GRPO gives every token of a
+    # sampled sequence its sequence's mean-shifted reward
+    adv = np.random.default_rng(42).standard_normal(tgt.shape[0])
+    w = np.repeat((adv - adv.mean())[:, None], tgt.shape[1], axis=1).astype(np.float32)
+    out, g = _gpu_weighted(cfg, params, idx, tgt, w, portable)
+    _check_weighted(cfg, params, idx, tgt, tb, w, out, g, bf16=True)
+
+
+def test_unit_weights_equal_plain_backward():
+    """w = 1 gives nc_backward's gradient bit for bit, and the weighted loss
+    equals the mean loss's sum."""
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("small"), ignore=[(0, 3)])
+    plain = _gpu_step(cfg, params, idx, tgt, tb)
+    out, g = _gpu_weighted(cfg, params, idx, tgt, np.ones(tgt.shape, dtype=np.float32))
+    np.testing.assert_array_equal(g, plain["grads"])
+    assert out[0] == pytest.approx(plain["out"][2], rel=1e-12) and out[1] == pytest.approx(plain["out"][0], rel=1e-12)
+
+
 def test_small_bf16_deterministic():
     cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("small"))
     a = _gpu_step(cfg, params, idx, tgt, tb)

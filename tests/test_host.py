@@ -103,6 +103,8 @@ def test_calls_on_null_context_rejected():
     assert L.nc_block_forward(None, 1, 1, 2) == -1
     h = nc.NcOptimHparams()
     assert L.nc_optimizer_step(None, 16, 16, 16, 16, 256, ctypes.byref(h)) == -1
+    assert L.nc_backward_weighted(None, 1, 1, 0, 1) == -1
+    assert L.nc_loss_weighted(None, 1, 1) == -1
     assert L.nc_last_error(None) == b"null context"
 
 
