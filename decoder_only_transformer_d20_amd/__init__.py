@@ -16,6 +16,7 @@ __all__ = [
     "param_offset", "workspace_bytes", "status_string", "ops", "LIB_PATH",
     "DTYPE_F32", "DTYPE_BF16", "FLAG_BLOCK_ONLY", "FLAG_PORTABLE_KERNELS",
     "NcOptimHparams", "optim_default", "optim_state_bytes", "optim_scratch_bytes",
+    "kv_cache_bytes", "decode_scratch_bytes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnc.so")
@@ -73,6 +74,10 @@ _SIGS = {
     "nc_optim_scratch_bytes": (_I64, [ctypes.POINTER(NcConfig)]),
     "nc_optimizer_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(NcOptimHparams)]),
     "nc_backward_weighted": (ctypes.c_int, [_P, _P, _P, _I32, _P]),
+    "nc_kv_cache_bytes": (_I64, [ctypes.POINTER(NcConfig), _I32, _I32]),
+    "nc_decode_scratch_bytes": (_I64, [ctypes.POINTER(NcConfig), _I32, _I32]),
+    "nc_prefill": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, _I32, _P]),
+    "nc_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, _I32, _P, _P]),
     "nc_loss_weighted": (ctypes.c_int, [_P, _P, _P]),
     "nc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nc_init": (ctypes.c_int, [ctypes.POINTER(NcConfig), _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
@@ -186,6 +191,18 @@ def optim_scratch_bytes(cfg) -> int:
     return n
 
 
+def kv_cache_bytes(cfg, max_batch: int, max_len: int) -> int:
+    n = lib().nc_kv_cache_bytes(ctypes.byref(_c(cfg)), int(max_batch), int(max_len))
+    _check(0 if n >= 0 else n, "nc_kv_cache_bytes")
+    return n
+
+
+def decode_scratch_bytes(cfg, max_batch: int, max_len: int) -> int:
+    n = lib().nc_decode_scratch_bytes(ctypes.byref(_c(cfg)), int(max_batch), int(max_len))
+    _check(0 if n >= 0 else n, "nc_decode_scratch_bytes")
+    return n
+
+
 def _ptr(x):
     if x is None:
         return None
@@ -233,6 +250,16 @@ class Context:
     def loss_weighted(self, token_weights, out):
         """nc_loss_weighted: out[0] = sum_t w_t ce[t], out[1] = that / n_valid."""
         _check(lib().nc_loss_weighted(self.h, _ptr(token_weights), _ptr(out)), "nc_loss_weighted", self.h)
+
+    def prefill(self, params, idx, prompt_len: int, nseq: int, kv_cache, max_batch: int, max_len: int, logits):
+        """nc_prefill: the prompt's K, V into the cache, last-position logits."""
+        _check(lib().nc_prefill(self.h, _ptr(params), _ptr(idx), int(prompt_len), int(nseq), _ptr(kv_cache),
+                                int(max_batch), int(max_len), _ptr(logits)), "nc_prefill", self.h)
+
+    def decode(self, params, tokens, nseq: int, pos: int, kv_cache, max_batch: int, max_len: int, scratch, logits):
+        """nc_decode: one token per sequence at position pos, next-token logits."""
+        _check(lib().nc_decode(self.h, _ptr(params), _ptr(tokens), int(nseq), int(pos), _ptr(kv_cache),
+                               int(max_batch), int(max_len), _ptr(scratch), _ptr(logits)), "nc_decode", self.h)
 
     def trace_enable(self, family):
         """Time launches of one kernel family (a name from TRACE_FAMILIES or

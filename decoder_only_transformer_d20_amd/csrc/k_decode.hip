@@ -1,0 +1,265 @@
+// KV-cache inference kernels (nanochat speedrun walkthrough, section
+// Pretraining, the sampling paragraph: a custom Engine with a KV cache and
+// the two phases prefill and decode).  Decode processes one new token for
+// each of a few sequences: every weight is read once per token, so each
+// product is a matrix-vector product bound by HBM, not by the matrix cores.
+// Here it is a VALU kernel that streams weight rows with coalesced 16-byte
+// loads from every CU, with the training step's epilogues (rotary, residual,
+// relu^2) fused.  Attention over the cache splits each sequence's keys into
+// chunks, one workgroup per (chunk, head, sequence), and a second pass
+// combines the chunks' (max, sum, output).
+#include "nc_internal.h"
+
+namespace nc {
+namespace {
+
+constexpr int kWaveD = 64;
+constexpr int kCols = 4;           // output columns per wave of the matrix-vector product
+
+template <typename T> struct V16;   // 16 bytes of T as floats
+template <> struct V16<float> {
+  static constexpr int n = 4;
+  __device__ static inline void load(const float* p, float (&o)[4]) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+};
+template <> struct V16<bf16> {
+  static constexpr int n = 8;
+  __device__ static inline void load(const bf16* p, float (&o)[8]) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = to_f32(bf16{(uint16_t)(w[i] & 0xffff)});
+      o[2 * i + 1] = to_f32(bf16{(uint16_t)(w[i] >> 16)});
+    }
+  }
+};
+
+// y[b][n] = epi(sum_k x[b][k] W[n][k]) for b < nb (<= kMaxDecodeBatch), W
+// [N][K] row-major in T, x [nb][K].  Wave w owns columns 4w .. 4w+3; each
+// lane walks K in 16-byte pieces, 64 pieces (one coalesced row segment) per
+// step, then the 64 lanes' partial sums are combined by a butterfly.
+template <typename T, int EPI>
+__global__ void __launch_bounds__(256) k_gemv(GemvDesc g) {
+  constexpr int VE = V16<T>::n;
+  const int lane = threadIdx.x & 63;
+  const int64_t n0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kCols;
+  if (n0 >= g.N) return;
+  const T* W = (const T*)g.W;
+  const T* x = (const T*)g.x;
+  float acc[kMaxDecodeBatch][kCols];
+#pragma unroll
+  for (int b = 0; b < kMaxDecodeBatch; ++b)
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) acc[b][c] = 0.f;
+  for (int k = lane * VE; k < g.K; k += kWaveD * VE) {
+    float w[kCols][VE];
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) V16<T>::load(W + (n0 + c) * (int64_t)g.K + k, w[c]);
+#pragma unroll
+    for (int b = 0; b < kMaxDecodeBatch; ++b) {
+      if (b < g.nb) {
+        float xv[VE];
+        V16<T>::load(x + (int64_t)b * g.ldx + k, xv);
+#pragma unroll
+        for (int c = 0; c < kCols; ++c)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[b][c] = fmaf(xv[e], w[c][e], acc[b][c]);
+      }
+    }
+  }
+  // butterfly: every lane ends with every (b, c) total
+#pragma unroll
+  for (int b = 0; b < kMaxDecodeBatch; ++b) {
+    if (b < g.nb) {
+#pragma unroll
+      for (int c = 0; c < kCols; ++c)
+        for (int o = 32; o > 0; o >>= 1) acc[b][c] += __shfl_xor(acc[b][c], o, 64);
+    }
+  }
+  // lane b * kCols + c finishes output (b, n0 + c)
+#pragma unroll
+  for (int b = 0; b < kMaxDecodeBatch; ++b) {
+    if (b >= g.nb) continue;
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) {
+      if (lane != b * kCols + c) continue;
+      const int64_t n = n0 + c;
+      float v = acc[b][c];
+      if constexpr (EPI == EPI_ROPE) {
+        // adjacent pairs (2i, 2i+1) of the rotated columns, angle at g.pos
+        if (n < g.rope_cols) {
+          const float other = acc[b][c ^ 1];
+          const float2 cs = g.rope[(n % g.head_dim) >> 1];
+          v = (c & 1) ? other * cs.y + v * cs.x : v * cs.x - other * cs.y;
+        }
+      }
+      if constexpr (EPI == EPI_RESID) v += to_f32(((const T*)g.aux)[(int64_t)b * g.ldy + n]);
+      if constexpr (EPI == EPI_RELU2) v = fmaxf(v, 0.f) * fmaxf(v, 0.f);
+      if constexpr (EPI == EPI_F32)
+        ((float*)g.y)[(int64_t)b * g.ldy + n] = v;
+      else
+        ((T*)g.y)[(int64_t)b * g.ldy + n] = from_f32<T>(v);
+    }
+  }
+}
+
+// copy k and v of the new token (columns d .. 3d of qkv [nb][3d]) into the
+// cache at position pos: K[b][pos][:], V[b][pos][:]
+template <typename T>
+__global__ void __launch_bounds__(256) k_kv_append(const T* __restrict__ qkv, int nb, int d, T* __restrict__ K,
+                                                     T* __restrict__ V, int64_t seq_stride, int pos) {
+  const int b = blockIdx.y;
+  for (int i = threadIdx.x + blockIdx.x * 256; i < d; i += 256 * gridDim.x) {
+    K[(int64_t)b * seq_stride + (int64_t)pos * d + i] = qkv[(int64_t)b * 3 * d + d + i];
+    V[(int64_t)b * seq_stride + (int64_t)pos * d + i] = qkv[(int64_t)b * 3 * d + 2 * d + i];
+  }
+}
+
+// prefill: rows t < len of the forward's qkv [rows][3d] into sequences
+// 0 .. nb-1 of the cache (the same prompt for every sequence)
+template <typename T>
+__global__ void __launch_bounds__(256) k_kv_prefill(const T* __restrict__ qkv, int len, int d, int nb,
+                                                     T* __restrict__ K, T* __restrict__ V, int64_t seq_stride) {
+  const int t = blockIdx.x, b = blockIdx.y;
+  if (t >= len) return;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    K[(int64_t)b * seq_stride + (int64_t)t * d + i] = qkv[(int64_t)t * 3 * d + d + i];
+    V[(int64_t)b * seq_stride + (int64_t)t * d + i] = qkv[(int64_t)t * 3 * d + 2 * d + i];
+  }
+}
+
+// Decode attention, pass 1: workgroup (chunk, h, b) scores keys
+// [chunk * 256, +256) of sequence b against q (head h), L keys in all, and
+// writes the chunk's max m, sum l and unnormalised output o[Q] (fp32) to
+// part[b][h][chunk] = {m, l, o[Q]}.
+template <typename T>
+__global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeDesc a) {
+  constexpr int kChunk = 256;
+  __shared__ float qs[256];
+  __shared__ float ps[kChunk];
+  __shared__ float red[8];
+  __shared__ float os[4][256];
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Q = a.Q, d = a.H * a.Q;
+  const T* q = (const T*)a.qkv + (int64_t)b * 3 * d + h * Q;
+  for (int i = tid; i < Q; i += 256) qs[i] = to_f32(q[i]);
+  __syncthreads();
+  const int64_t base = (int64_t)b * a.seq_stride + h * Q;
+  const int j = chunk * kChunk + tid;      // this thread's key
+  float sc = -INFINITY;
+  if (j < a.L) {
+    const T* kr = (const T*)a.K + base + (int64_t)j * d;
+    float s = 0.f;
+    for (int i = 0; i < Q; i += V16<T>::n) {
+      float kv[V16<T>::n];
+      V16<T>::load(kr + i, kv);
+#pragma unroll
+      for (int e = 0; e < V16<T>::n; ++e) s = fmaf(qs[i + e], kv[e], s);
+    }
+    sc = s * a.scale_log2;
+  }
+  float mx = sc;
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float p = j < a.L ? __builtin_amdgcn_exp2f(sc - M) : 0.f;
+  ps[tid] = p;
+  float l = p;
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+  __syncthreads();
+  if (lane == 0) red[4 + wave] = l;
+  // o: wave w sums keys 64w .. 64w+63 of the chunk; lane handles dims
+  // lane and lane + 64 (Q <= 128)
+  float o0 = 0.f, o1 = 0.f;
+  const int jend = min(kChunk, a.L - chunk * kChunk);
+  for (int jj = wave * 64; jj < min(wave * 64 + 64, jend); ++jj) {
+    const T* vr = (const T*)a.V + base + (int64_t)(chunk * kChunk + jj) * d;
+    const float pj = ps[jj];
+    if (lane < Q) o0 = fmaf(pj, to_f32(vr[lane]), o0);
+    if (lane + 64 < Q) o1 = fmaf(pj, to_f32(vr[lane + 64]), o1);
+  }
+  os[wave][lane] = o0;
+  os[wave][lane + 64] = o1;
+  __syncthreads();
+  float* out = a.part + (((int64_t)b * a.H + h) * a.nchunks + chunk) * (2 + Q);
+  if (tid == 0) {
+    out[0] = M;
+    out[1] = (red[4] + red[5]) + (red[6] + red[7]);
+  }
+  for (int i = tid; i < Q; i += 256) out[2 + i] = (os[0][i] + os[1][i]) + (os[2][i] + os[3][i]);
+}
+
+// pass 2: combine the chunks of (h, b): o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c
+template <typename T>
+__global__ void __launch_bounds__(128) k_attn_decode_combine(AttnDecodeDesc a) {
+  const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+  const int Q = a.Q;
+  const float* part = a.part + ((int64_t)b * a.H + h) * a.nchunks * (2 + Q);
+  float M = -INFINITY;
+  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, part[c * (2 + Q)]);
+  float num = 0.f, den = 0.f;
+  for (int c = 0; c < a.nchunks; ++c) {
+    const float w = __builtin_amdgcn_exp2f(part[c * (2 + Q)] - M);
+    den = fmaf(w, part[c * (2 + Q) + 1], den);
+    if (i < Q) num = fmaf(w, part[c * (2 + Q) + 2 + i], num);
+  }
+  if (i < Q) ((T*)a.o)[(int64_t)b * a.H * Q + h * Q + i] = from_f32<T>(num / den);
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t gemv(const GemvDesc& g, int epi, hipStream_t s) {
+  if (g.nb < 1 || g.nb > kMaxDecodeBatch || g.N % kCols || g.K % V16<T>::n || g.N <= 0 || g.K <= 0)
+    return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)((g.N / kCols + 3) / 4);
+  switch (epi) {
+    case EPI_STORE: k_gemv<T, EPI_STORE><<<blocks, 256, 0, s>>>(g); break;
+    case EPI_ROPE: k_gemv<T, EPI_ROPE><<<blocks, 256, 0, s>>>(g); break;
+    case EPI_RESID: k_gemv<T, EPI_RESID><<<blocks, 256, 0, s>>>(g); break;
+    case EPI_RELU2: k_gemv<T, EPI_RELU2><<<blocks, 256, 0, s>>>(g); break;
+    case EPI_F32: k_gemv<T, EPI_F32><<<blocks, 256, 0, s>>>(g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t kv_append(const T* qkv, int nb, int d, T* K, T* V, int64_t seq_stride, int pos, hipStream_t s) {
+  k_kv_append<T><<<dim3((d + 255) / 256, nb), 256, 0, s>>>(qkv, nb, d, K, V, seq_stride, pos);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t kv_prefill(const T* qkv, int len, int d, int nb, T* K, T* V, int64_t seq_stride, hipStream_t s) {
+  k_kv_prefill<T><<<dim3(len, nb), 256, 0, s>>>(qkv, len, d, nb, K, V, seq_stride);
+  return hipGetLastError();
+}
+
+int attn_decode_chunks(int L) { return (L + 255) / 256; }
+
+template <typename T>
+hipError_t attn_decode(const AttnDecodeDesc& a, int nb, hipStream_t s) {
+  if (a.Q > 128 || a.Q % V16<T>::n || a.L < 1 || a.nchunks != attn_decode_chunks(a.L)) return hipErrorInvalidValue;
+  k_attn_decode<T><<<dim3(a.nchunks, a.H, nb), 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_attn_decode_combine<T><<<dim3(a.H, nb), 128, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template hipError_t gemv<float>(const GemvDesc&, int, hipStream_t);
+template hipError_t gemv<bf16>(const GemvDesc&, int, hipStream_t);
+template hipError_t kv_append<float>(const float*, int, int, float*, float*, int64_t, int, hipStream_t);
+template hipError_t kv_append<bf16>(const bf16*, int, int, bf16*, bf16*, int64_t, int, hipStream_t);
+template hipError_t kv_prefill<float>(const float*, int, int, int, float*, float*, int64_t, hipStream_t);
+template hipError_t kv_prefill<bf16>(const bf16*, int, int, int, bf16*, bf16*, int64_t, hipStream_t);
+template hipError_t attn_decode<float>(const AttnDecodeDesc&, int, hipStream_t);
+template hipError_t attn_decode<bf16>(const AttnDecodeDesc&, int, hipStream_t);
+
+}  // namespace nc

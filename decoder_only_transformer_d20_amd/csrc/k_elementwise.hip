@@ -426,13 +426,13 @@ __global__ void __launch_bounds__(256) k_rmsnorm_bwd(const T* __restrict__ y, co
 // rotary table: tab[t][i] = (cos, sin)(t * base^(-2i/Q)), computed in fp64
 // and rounded once (angles reach T radians, far beyond fp32's safe range)
 // ---------------------------------------------------------------------------
-__global__ void k_rope_table(float2* tab, int T, int Q, double base) {
+__global__ void k_rope_table(float2* tab, int t0, int T, int Q, double base) {
   const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int half = Q / 2;
   if (k >= (int64_t)T * half) return;
   const int t = (int)(k / half), i = (int)(k % half);
   const double theta = pow(base, -2.0 * (double)i / (double)Q);
-  const double phi = (double)t * theta;
+  const double phi = (double)(t0 + t) * theta;
   tab[k] = make_float2((float)cos(phi), (float)sin(phi));
 }
 
@@ -739,8 +739,11 @@ template hipError_t attn_delta<float>(const AttnDesc&, hipStream_t);
 template hipError_t attn_delta<bf16>(const AttnDesc&, hipStream_t);
 
 hipError_t rope_table(float2* tab, int T, int Q, float base, hipStream_t s) {
+  return rope_table_at(tab, 0, T, Q, base, s);
+}
+hipError_t rope_table_at(float2* tab, int t0, int T, int Q, float base, hipStream_t s) {
   const int64_t n = (int64_t)T * (Q / 2);
-  k_rope_table<<<nblocks(n, 256), 256, 0, s>>>(tab, T, Q, (double)base);
+  k_rope_table<<<nblocks(n, 256), 256, 0, s>>>(tab, t0, T, Q, (double)base);
   return hipGetLastError();
 }
 hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int32_t* tgt, float* lse, float* ce,

@@ -712,6 +712,119 @@ int optimizer_step(nc_ctx* ctx, float* master, T* params, const float* grads, fl
   return NC_OK;
 }
 
+// ---- KV-cache inference -------------------------------------------------------
+// decode scratch: x, a, o [mb][d] | qkv [mb][3d] | u [mb][F] (model dtype) |
+// r [mb] | rotary row [Q/2] | attention partials [mb][H][chunks][2+Q] (fp32)
+struct DecodeScratch {
+  size_t x = 0, a = 0, o = 0, qkv = 0, u = 0, r = 0, rope = 0, part = 0, total = 0;
+};
+
+DecodeScratch decode_scratch(const nc_config& c, int mb, int ml) {
+  const size_t es = esize(c);
+  const int64_t d = c.d_model, F = c.d_ff;
+  DecodeScratch o;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t r = off; off += align_up(bytes); return r; };
+  o.x = take(mb * d * es);
+  o.a = take(mb * d * es);
+  o.o = take(mb * d * es);
+  o.qkv = take(mb * 3 * d * es);
+  o.u = take(mb * F * es);
+  o.r = take(mb * 4);
+  o.rope = take(c.head_dim / 2 * 8);
+  o.part = take((size_t)mb * c.n_head * attn_decode_chunks(ml) * (2 + c.head_dim) * 4);
+  o.total = off;
+  return o;
+}
+
+int kv_shape_ok(const nc_config& c, int mb, int ml) {
+  if (is_block(c)) return NC_ERR_STATE;
+  if (mb < 1 || mb > kMaxDecodeBatch || ml < 1 || ml > (1 << 24)) return NC_ERR_SHAPE;
+  if (c.head_dim > 128) return NC_ERR_UNSUPPORTED;
+  return NC_OK;
+}
+
+template <typename T>
+int prefill(nc_ctx* ctx, const T* params, const int32_t* idx, int len, int nseq, T* kv, int mb, int ml,
+            float* logits) {
+  const nc_config& c = ctx->cfg;
+  const Plan& p = ctx->plan;
+  const int d = c.d_model, V = c.vocab;
+  // the whole forward over the (padded) prompt; its targets are the ids
+  // themselves, since only the saved k, v and the final norm are used
+  int st = model_forward<T>(ctx, params, idx, idx, nullptr);
+  if (st != NC_OK) return st;
+  ctx->have_forward = true;
+  const int64_t sstride = (int64_t)ml * d, lstride = 2 * (int64_t)mb * sstride;
+  for (int l = 0; l < c.n_layer; ++l) {
+    const T* qkv = reinterpret_cast<const T*>(ctx->layer(l) + p.l_qkv);
+    T* K = kv + l * lstride;
+    NC_TRY(kv_prefill<T>(qkv, len, d, nseq, K, K + (int64_t)mb * sstride, sstride, ctx->stream), "kv prefill");
+  }
+  const T* U = params + (int64_t)V * d + (int64_t)c.n_layer * layer_elems(c);
+  GemvDesc g{};
+  g.nb = 1; g.N = V; g.K = d; g.W = U;
+  g.x = ctx->at<T>(p.xf) + (int64_t)(len - 1) * d; g.ldx = d;
+  g.y = logits; g.ldy = V;
+  NC_TRY(gemv<T>(g, EPI_F32, ctx->stream), "prefill logits");
+  return NC_OK;
+}
+
+template <typename T>
+int decode(nc_ctx* ctx, const T* params, const int32_t* tokens, int nseq, int pos, T* kv, int mb, int ml,
+           char* scratch, float* logits) {
+  const nc_config& c = ctx->cfg;
+  const int d = c.d_model, F = c.d_ff, V = c.vocab, H = c.n_head, Q = c.head_dim;
+  hipStream_t s = ctx->stream;
+  const DecodeScratch sc = decode_scratch(c, mb, ml);
+  T* x = reinterpret_cast<T*>(scratch + sc.x);
+  T* a = reinterpret_cast<T*>(scratch + sc.a);
+  T* o = reinterpret_cast<T*>(scratch + sc.o);
+  T* qkv = reinterpret_cast<T*>(scratch + sc.qkv);
+  T* u = reinterpret_cast<T*>(scratch + sc.u);
+  float* r = reinterpret_cast<float*>(scratch + sc.r);
+  float2* rope = reinterpret_cast<float2*>(scratch + sc.rope);
+  float* part = reinterpret_cast<float*>(scratch + sc.part);
+  NC_TRY(embed_fwd<T>(params, tokens, x, nseq, d, s), "decode embedding");
+  NC_TRY(rope_table_at(rope, pos, 1, Q, c.rope_base, s), "decode rotary row");
+  const int64_t sstride = (int64_t)ml * d, lstride = 2 * (int64_t)mb * sstride;
+  const T* w = params + (int64_t)V * d;
+  auto gv = [&](const T* W, int N, int K, const T* xin, T* y, int64_t ldy, int epi) {
+    GemvDesc g{};
+    g.nb = nseq; g.N = N; g.K = K; g.W = W; g.x = xin; g.ldx = K; g.y = y; g.ldy = ldy; g.aux = y;
+    g.rope = rope; g.rope_cols = 2 * d; g.head_dim = Q;
+    return gemv<T>(g, epi, s);
+  };
+  for (int l = 0; l < c.n_layer; ++l) {
+    const T* lw = w + (int64_t)l * layer_elems(c);
+    const T* Wqkv = lw;
+    const T* Wo = lw + 3 * (int64_t)d * d;
+    const T* W1 = Wo + (int64_t)d * d;
+    const T* W2 = W1 + (int64_t)F * d;
+    T* K = kv + l * lstride;
+    T* Vc = K + (int64_t)mb * sstride;
+    NC_TRY(rmsnorm_fwd<T>(x, a, r, nseq, d, c.rms_eps, s), "decode rmsnorm (attention)");
+    NC_TRY(gv(Wqkv, 3 * d, d, a, qkv, 3 * d, EPI_ROPE), "decode qkv");
+    NC_TRY(kv_append<T>(qkv, nseq, d, K, Vc, sstride, pos, s), "kv append");
+    AttnDecodeDesc ad{};
+    ad.H = H; ad.Q = Q; ad.L = pos + 1; ad.nchunks = attn_decode_chunks(pos + 1);
+    ad.qkv = qkv; ad.K = K; ad.V = Vc; ad.seq_stride = sstride;
+    ad.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)Q));
+    ad.part = part; ad.o = o;
+    NC_TRY(attn_decode<T>(ad, nseq, s), "decode attention");
+    NC_TRY(gv(Wo, d, d, o, x, d, EPI_RESID), "decode attention output");
+    NC_TRY(rmsnorm_fwd<T>(x, a, r, nseq, d, c.rms_eps, s), "decode rmsnorm (mlp)");
+    NC_TRY(gv(W1, F, d, a, u, F, EPI_RELU2), "decode mlp up");
+    NC_TRY(gv(W2, d, F, u, x, d, EPI_RESID), "decode mlp down");
+  }
+  NC_TRY(rmsnorm_fwd<T>(x, a, r, nseq, d, c.rms_eps, s), "decode final rmsnorm");
+  GemvDesc g{};
+  g.nb = nseq; g.N = V; g.K = d; g.W = w + (int64_t)c.n_layer * layer_elems(c);
+  g.x = a; g.ldx = d; g.y = logits; g.ldy = V;
+  NC_TRY(gemv<T>(g, EPI_F32, s), "decode logits");
+  return NC_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -949,6 +1062,52 @@ int nc_optimizer_step(nc_ctx* ctx, float* master, void* params, const float* gra
   return is_bf16(ctx->cfg)
              ? optimizer_step<bf16>(ctx, master, (bf16*)params, grads, (float*)state, (char*)scratch, hp)
              : optimizer_step<float>(ctx, master, (float*)params, grads, (float*)state, (char*)scratch, hp);
+}
+
+int64_t nc_kv_cache_bytes(const nc_config* cfg, int32_t max_batch, int32_t max_len) {
+  int st = validate(cfg);
+  if (st != NC_OK) return st;
+  st = kv_shape_ok(*cfg, max_batch, max_len);
+  if (st != NC_OK) return st;
+  return 2 * (int64_t)cfg->n_layer * max_batch * max_len * cfg->d_model * (int64_t)esize(*cfg);
+}
+
+int64_t nc_decode_scratch_bytes(const nc_config* cfg, int32_t max_batch, int32_t max_len) {
+  int st = validate(cfg);
+  if (st != NC_OK) return st;
+  st = kv_shape_ok(*cfg, max_batch, max_len);
+  if (st != NC_OK) return st;
+  return (int64_t)decode_scratch(*cfg, max_batch, max_len).total;
+}
+
+int nc_prefill(nc_ctx* ctx, const void* params, const int32_t* idx, int32_t prompt_len, int32_t nseq,
+               void* kv_cache, int32_t max_batch, int32_t max_len, float* logits) {
+  if (!ctx || !params || !idx || !kv_cache || !logits) return NC_ERR_INVALID_ARG;
+  int st = kv_shape_ok(ctx->cfg, max_batch, max_len);
+  if (st != NC_OK) return st;
+  if (ctx->cfg.batch != 1) return NC_ERR_SHAPE;
+  if (prompt_len < 1 || prompt_len > ctx->cfg.seq_len || prompt_len > max_len) return NC_ERR_SHAPE;
+  if (nseq < 1 || nseq > max_batch) return NC_ERR_SHAPE;
+  ctx->have_forward = false;
+  return is_bf16(ctx->cfg)
+             ? prefill<bf16>(ctx, (const bf16*)params, idx, prompt_len, nseq, (bf16*)kv_cache, max_batch, max_len,
+                             logits)
+             : prefill<float>(ctx, (const float*)params, idx, prompt_len, nseq, (float*)kv_cache, max_batch, max_len,
+                              logits);
+}
+
+int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t nseq, int32_t pos, void* kv_cache,
+              int32_t max_batch, int32_t max_len, void* scratch, float* logits) {
+  if (!ctx || !params || !tokens || !kv_cache || !scratch || !logits) return NC_ERR_INVALID_ARG;
+  int st = kv_shape_ok(ctx->cfg, max_batch, max_len);
+  if (st != NC_OK) return st;
+  if (nseq < 1 || nseq > max_batch || pos < 0 || pos >= max_len) return NC_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(scratch) & (kAlign - 1)) return NC_ERR_INVALID_ARG;
+  return is_bf16(ctx->cfg)
+             ? decode<bf16>(ctx, (const bf16*)params, tokens, nseq, pos, (bf16*)kv_cache, max_batch, max_len,
+                            (char*)scratch, logits)
+             : decode<float>(ctx, (const float*)params, tokens, nseq, pos, (float*)kv_cache, max_batch, max_len,
+                             (char*)scratch, logits);
 }
 
 }  // extern "C"

@@ -125,6 +125,8 @@ template <typename T> hipError_t rmsnorm_fwd(const T* x, T* y, float* r, int64_t
 template <typename T> hipError_t rmsnorm_bwd(const T* y, const float* r, const T* dy, T* dx_io, int64_t rows, int d,
                                             int accumulate, hipStream_t s);
 hipError_t rope_table(float2* tab, int T, int Q, float base, hipStream_t s);
+// rows t0 .. t0+T-1 of the same table (same fp64 angles)
+hipError_t rope_table_at(float2* tab, int t0, int T, int Q, float base, hipStream_t s);
 hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int32_t* tgt,
                       float* lse, float* ce, int64_t rows, hipStream_t s);
 hipError_t count_valid(const int32_t* tgt, int64_t n, float* inv_nvalid, hipStream_t s);
@@ -138,6 +140,38 @@ hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
 // out [cols][rows] = transpose of in [rows][cols]; rows, cols multiples of 8
 hipError_t transpose_bf16(const bf16* in, int64_t rows, int64_t cols, bf16* out, hipStream_t s);
 hipError_t copy_bytes(void* dst, const void* src, size_t n, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// KV-cache inference
+// ---------------------------------------------------------------------------
+constexpr int kMaxDecodeBatch = 16;   // sequences per decode step
+// y[b][n] = epi(sum_k x[b][k] W[n][k]), b < nb: EPI_STORE, EPI_ROPE (pairs of
+// columns < rope_cols rotated by the angles in rope[head_dim/2], one
+// position), EPI_RESID (+ aux[b][n], aux may be y), EPI_RELU2, EPI_F32 (fp32 y)
+struct GemvDesc {
+  int nb, N, K;
+  const void* W;            // [N][K]
+  const void* x; int64_t ldx;
+  void* y; int64_t ldy;
+  const void* aux;
+  const float2* rope; int rope_cols, head_dim;
+};
+template <typename T> hipError_t gemv(const GemvDesc& g, int epi, hipStream_t s);
+// K, V [batch][max_len][d] of one layer: seq_stride = max_len * d
+template <typename T> hipError_t kv_append(const T* qkv, int nb, int d, T* K, T* V, int64_t seq_stride, int pos,
+                                           hipStream_t s);
+template <typename T> hipError_t kv_prefill(const T* qkv, int len, int d, int nb, T* K, T* V, int64_t seq_stride,
+                                            hipStream_t s);
+struct AttnDecodeDesc {
+  int H, Q, L, nchunks;     // L keys (positions 0 .. L-1) per sequence
+  const void* qkv;          // [nb][3 H Q], q rotated
+  const void* K; const void* V; int64_t seq_stride;
+  float scale_log2;         // log2(e) / sqrt(Q)
+  float* part;              // [nb][H][nchunks][2 + Q]
+  void* o;                  // [nb][H Q]
+};
+int attn_decode_chunks(int L);
+template <typename T> hipError_t attn_decode(const AttnDecodeDesc& a, int nb, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // optimiser step

@@ -176,6 +176,36 @@ int nc_backward_weighted(nc_ctx* ctx, const void* params, float* grads, int32_t 
  * order; 0 / 0 gives 0).  NC_ERR_STATE without a prior nc_forward. */
 int nc_loss_weighted(nc_ctx* ctx, const float* token_weights, double* out);
 
+/* ---- KV-cache inference: prefill and decode ------------------------------ */
+/* The Engine of the walkthrough (section Pretraining, the paragraph after
+ * the sampled completions): generation with a KV cache in two phases,
+ * prefill over the prompt and decode one token at a time, several samples
+ * of one prompt decoded together.  The cache holds, per layer, K (rotated)
+ * and V as [max_batch][max_len][d] in the model dtype, layer l's K at
+ * element 2 l max_batch max_len d and its V right after.  Decode handles
+ * at most 16 sequences, head_dim <= 128. */
+int64_t nc_kv_cache_bytes(const nc_config* cfg, int32_t max_batch, int32_t max_len);
+
+/* Bytes of the scratch nc_decode needs (256-byte aligned device memory). */
+int64_t nc_decode_scratch_bytes(const nc_config* cfg, int32_t max_batch, int32_t max_len);
+
+/* Prefill: the model over one prompt.  The context must have batch 1;
+ * idx device int32 [seq_len] holds the prompt in its first prompt_len
+ * entries and any valid ids after (causal attention keeps them from
+ * affecting the prompt).  Writes K, V of positions 0 .. prompt_len-1 into
+ * sequences 0 .. nseq-1 of the cache (the same prompt for each) and the
+ * fp32 logits of the last prompt position to logits device [V].  Leaves the
+ * context's forward state as nc_forward would. */
+int nc_prefill(nc_ctx* ctx, const void* params, const int32_t* idx, int32_t prompt_len, int32_t nseq,
+               void* kv_cache, int32_t max_batch, int32_t max_len, float* logits);
+
+/* Decode: one new token per sequence, tokens device int32 [nseq], all at
+ * position pos (the sequences' common length so far; 0 <= pos < max_len).
+ * Appends each token's K, V at pos and writes fp32 logits [nseq][V] of the
+ * next token.  Uses only the scratch (not the context's workspace). */
+int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t nseq, int32_t pos, void* kv_cache,
+              int32_t max_batch, int32_t max_len, void* scratch, float* logits);
+
 /* ---- single block (NC_FLAG_BLOCK_ONLY) ------------------------------------ */
 
 /* y = block(x) for x, y device dtype [B*T, d] (may not alias).  Saves what

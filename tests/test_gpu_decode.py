@@ -1,0 +1,129 @@
+"""KV-cache inference (nc_prefill, nc_decode) against the fp64 oracle.
+
+Decoding is exact in the method: the logits decode produces at position t
+are the logits the forward over the whole sequence gives at t (causal
+attention), so the oracle is the pinned forward (oracle.model_forward_row)
+run on each sequence's prompt + generated tokens.  The generated tokens are
+fixed (teacher-forced), so every step is compared.
+
+Bars: fp32 (tiny) max |dz| / max |z| <= 1e-4 per row.  bf16 (small, d20):
+cosine >= 0.9999 per row and max |dz| <= 0.02 max |z|.  Activations are
+stored in bf16 after every product and norm, so the logits drift with
+depth; at d20 (logits up to ~5, RMS ~1) they sit 1.2 % of the largest
+logit from fp64, at cosine 0.99993."""
+import numpy as np
+import pytest
+
+import oracle
+import synthdata
+from _util import cosine, dev, empty, host, zeros
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import decoder_only_transformer_d20_amd as nc  # noqa: E402
+
+
+def _oracle_logits(cfg, params64, tokens):
+    _, cache = oracle.model_forward_row(params64, np.asarray(tokens), np.zeros(len(tokens), dtype=np.int64), cfg)
+    return cache["z"]
+
+
+def _run(cfg, params, prompt, gen, nseq):
+    """Prefill the prompt for nseq sequences, then decode gen[s][i] at
+    position len(prompt) + i.  Returns (prefill logits [V], decode logits
+    [steps][nseq][V])."""
+    T0 = len(prompt)
+    pad = (T0 + 63) // 64 * 64
+    pcfg = cfg.with_(batch=1, seq_len=pad)
+    steps = gen.shape[1]
+    ml = T0 + steps
+    sess = nc.Session(pcfg)
+    P = dev(params, cfg.dtype)
+    idx = np.concatenate([prompt, np.arange(pad - T0) % cfg.vocab]).astype(np.int32)
+    kv = zeros((nc.kv_cache_bytes(pcfg, nseq, ml) // 4,))
+    scr = empty((nc.decode_scratch_bytes(pcfg, nseq, ml) // 4 + 64,))
+    sp = (scr.data_ptr() + 255) // 256 * 256
+    l0 = empty((cfg.vocab,))
+    sess.prefill(P, dev(idx), T0, nseq, kv, nseq, ml, l0)
+    out = []
+    for i in range(steps):
+        li = empty((nseq, cfg.vocab))
+        sess.decode(P, dev(gen[:, i].astype(np.int32)), nseq, T0 + i, kv, nseq, ml, sp, li)
+        torch.cuda.synchronize()
+        out.append(host(li))
+    torch.cuda.synchronize()
+    return host(l0), out
+
+
+def _check(cfg, params, prompt, gen, nseq, bf16):
+    l0, steps = _run(cfg, params, prompt, gen, nseq)
+    p64 = synthdata.split_params(cfg, params.astype(np.float64))
+    T0 = len(prompt)
+
+    def ok(got, want, what):
+        err = np.abs(got - want).max()
+        if bf16:
+            assert cosine(got, want) >= 0.9999 and err <= 0.02 * np.abs(want).max(), (what, cosine(got, want), err)
+        else:
+            assert err <= 1e-4 * np.abs(want).max(), (what, err)
+
+    for s in range(nseq):
+        z = _oracle_logits(cfg, p64, np.concatenate([prompt, gen[s]]))
+        if s == 0:
+            ok(l0, z[T0 - 1], "prefill")
+        for i, li in enumerate(steps):
+            ok(li[s], z[T0 + i], ("decode", s, i))
+
+
+def _tokens(cfg, T0, nseq, steps, seed):
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, cfg.vocab, T0), rng.integers(0, cfg.vocab, (nseq, steps))
+
+
+def test_tiny_fp32_decode_matches_forward():
+    """A 40-token prompt (padded to 64 for the prefill), three sequences,
+    six steps."""
+    cfg = synthdata.get_config("tiny")
+    params = synthdata.make_params(cfg)
+    prompt, gen = _tokens(cfg, 40, 3, 6, 51)
+    _check(cfg, params, prompt, gen, 3, bf16=False)
+
+
+@pytest.mark.parametrize("T0,nseq,steps", [(100, 4, 5), (255, 2, 3), (1, 1, 4)])
+def test_small_bf16_decode_matches_forward(T0, nseq, steps):
+    """bf16, including a one-token prompt and a cache that crosses the
+    256-key chunk boundary of the decode attention."""
+    cfg = synthdata.get_config("small")
+    params = synthdata.make_params(cfg)
+    prompt, gen = _tokens(cfg, T0, nseq, steps, 52 + T0)
+    _check(cfg, params, prompt, gen, nseq, bf16=True)
+
+
+def test_decode_rejects_bad_shapes():
+    cfg = synthdata.get_config("small").with_(batch=1, seq_len=64)
+    sess = nc.Session(cfg)
+    params = synthdata.make_params(cfg)
+    P = dev(params, "bf16")
+    kv = zeros((nc.kv_cache_bytes(cfg, 2, 64) // 4,))
+    scr = empty((nc.decode_scratch_bytes(cfg, 2, 64) // 4 + 64,))
+    sp = (scr.data_ptr() + 255) // 256 * 256
+    lg = empty((2, cfg.vocab))
+    tok = dev(np.zeros(2, dtype=np.int32))
+    for nseq, pos, mb, ml in ((3, 0, 2, 64), (1, 64, 2, 64), (0, 0, 2, 64), (1, 0, 17, 64)):
+        with pytest.raises(nc.NcError) as e:
+            sess.decode(P, tok, nseq, pos, kv, mb, ml, sp, lg)
+        assert e.value.status == -2
+    with pytest.raises(nc.NcError) as e:
+        sess.prefill(P, dev(np.zeros(64, dtype=np.int32)), 65, 1, kv, 2, 64, lg)
+    assert e.value.status == -2
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_d20_decode_matches_forward():
+    """The full d20 model: a 200-token prompt, two sequences, three steps."""
+    cfg = synthdata.get_config("d20")
+    params = synthdata.make_params(cfg)
+    prompt, gen = _tokens(cfg, 200, 2, 3, 53)
+    _check(cfg, params, prompt, gen, 2, bf16=True)

@@ -178,3 +178,17 @@ def test_optim_sizes():
         nc.optim_default(cfg, 5, 4, 1)          # it past num_iters
     with pytest.raises(nc.NcError):
         nc.optim_default(cfg, 0, 10, 0)         # no micro-batch
+
+
+def test_inference_sizes_and_null_context():
+    cfg = synthdata.get_config("d20")
+    # K and V per layer: [max_batch][max_len][d] bf16
+    assert nc.kv_cache_bytes(cfg, 4, 2048) == 2 * 20 * 4 * 2048 * 1280 * 2
+    assert nc.decode_scratch_bytes(cfg, 4, 2048) > 0
+    with pytest.raises(nc.NcError):
+        nc.kv_cache_bytes(cfg, 17, 2048)          # more sequences than one decode step takes
+    with pytest.raises(nc.NcError):
+        nc.kv_cache_bytes(synthdata.get_config("block"), 1, 64)
+    L = nc.lib()
+    assert L.nc_prefill(None, 1, 1, 1, 1, 1, 1, 64, 1) == -1
+    assert L.nc_decode(None, 1, 1, 1, 0, 1, 1, 64, 256, 1) == -1
