@@ -21,6 +21,6 @@ from .model import (  # noqa: F401
     rmsnorm, rmsnorm_bwd, rope_angles, rope, causal_attention,
     causal_attention_bwd, relu2, cross_entropy, cross_entropy_grad,
     block_forward, block_backward, model_forward_row, model_backward_row,
-    train_step, block_step, loss_bpb, weighted_loss, zero_grads,
+    train_step, block_step, loss_bpb, weighted_loss, sample_next, zero_grads,
 )
 from . import optim  # noqa: F401

@@ -187,6 +187,27 @@ def loss_bpb(ce, tgt, token_bytes):
 # one pre-norm block
 # ---------------------------------------------------------------------------
 
+def sample_next(logits, temperature, top_k, u):
+    """Next token from one row of logits, as the Engine samples (section
+    Pretraining, the Engine paragraph): the largest logit when
+    temperature == 0; otherwise p_i proportional to exp((z_i - max z) /
+    temperature) over the top_k largest logits (all when top_k == 0; values
+    tied with the k-th largest are kept), drawn by inverse CDF in token-id
+    order: the first kept id whose running sum exceeds u * sum p
+    (u in [0, 1); the last kept id if rounding leaves none)."""
+    z = np.asarray(logits, dtype=np.float64)
+    if temperature == 0:
+        return int(np.argmax(z))
+    keep = np.ones(z.shape, dtype=bool)
+    if 0 < top_k < z.size:
+        thr = np.sort(z)[::-1][top_k - 1]
+        keep = z >= thr
+    p = np.where(keep, np.exp((z - z.max()) / temperature), 0.0)
+    c = np.cumsum(p)
+    hit = np.nonzero((c > u * c[-1]) & keep)[0]
+    return int(hit[0]) if hit.size else int(np.nonzero(keep)[0][-1])
+
+
 def weighted_loss(ce, tgt, weights):
     """(sum over valid targets of w_t ce[t], that sum / n_valid); 0 when no
     target is valid."""

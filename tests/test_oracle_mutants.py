@@ -33,6 +33,9 @@ MUTANTS = [
     ("row_scale = scale if token_weights is None else scale * np.asarray(token_weights[b], dtype=np.float64)",
      "row_scale = scale"),                                                                    # token weights ignored
     ("np.where(valid, w * ce, 0.0)", "np.where(valid, ce, 0.0)"),                            # weighted loss unweighted
+    ("np.exp((z - z.max()) / temperature)", "np.exp((z - z.max()) * temperature)"),          # temperature inverted
+    ("thr = np.sort(z)[::-1][top_k - 1]", "thr = np.sort(z)[::-1][top_k]"),                  # top-k off by one
+    ("keep = z >= thr", "keep = z > thr"),                                                    # ties at the k-th dropped
 ]
 
 # (text in oracle/optim.py, the mistake that replaces it)

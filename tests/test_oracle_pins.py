@@ -459,3 +459,37 @@ def test_weighted_gradient_special_cases():
     np.testing.assert_allclose(g12, g1 + g2, rtol=1e-10, atol=1e-14)
     s, m = oracle.weighted_loss(np.ones(tgt.shape), tgt, w1)
     assert s == pytest.approx(w1.sum()) and m == pytest.approx(w1.sum() / tgt.size)
+
+
+# --------------------------------------------------------------------------
+# sampling the next token
+# --------------------------------------------------------------------------
+def test_sample_greedy_and_top1():
+    z = _rng(31).standard_normal(500)
+    z[123] = 9.0
+    assert oracle.sample_next(z, 0.0, 0, 0.7) == 123
+    for u in (0.0, 0.5, 0.999):
+        assert oracle.sample_next(z, 1.3, 1, u) == 123
+
+
+@pytest.mark.parametrize("temperature,top_k", [(1.0, 0), (0.7, 0), (1.5, 10)])
+def test_sample_frequencies_on_a_uniform_grid(temperature, top_k):
+    """Inverse CDF on the grid u_j = (j + 1/2) / N hits each token with
+    frequency equal to its probability to within 1/N; the probabilities are
+    scipy's softmax of z / temperature over the kept tokens."""
+    from scipy.special import softmax
+    z = _rng(32).standard_normal(40) * 2.0
+    N = 20000
+    counts = np.bincount([oracle.sample_next(z, temperature, top_k, (j + 0.5) / N) for j in range(N)],
+                         minlength=z.size)
+    keep = np.ones(z.size, dtype=bool) if top_k == 0 else z >= np.sort(z)[::-1][top_k - 1]
+    p = np.zeros(z.size)
+    p[keep] = softmax(z[keep] / temperature)
+    assert np.abs(counts / N - p).max() <= 1.0 / N + 1e-12
+    assert not np.any(counts[~keep])
+
+
+def test_sample_top_k_keeps_ties():
+    z = np.array([0.0, 3.0, 1.0, 3.0, 2.0, 2.0, -1.0])
+    drawn = {oracle.sample_next(z, 1.0, 3, (j + 0.5) / 1000) for j in range(1000)}
+    assert drawn == {1, 3, 4, 5}           # the two 2.0s tie for third place
