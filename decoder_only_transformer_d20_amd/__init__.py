@@ -16,7 +16,7 @@ __all__ = [
     "param_offset", "workspace_bytes", "status_string", "ops", "LIB_PATH",
     "DTYPE_F32", "DTYPE_BF16", "FLAG_BLOCK_ONLY", "FLAG_PORTABLE_KERNELS",
     "NcOptimHparams", "optim_default", "optim_state_bytes", "optim_scratch_bytes",
-    "kv_cache_bytes", "decode_scratch_bytes",
+    "kv_cache_bytes", "decode_scratch_bytes", "sample",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnc.so")
@@ -75,6 +75,7 @@ _SIGS = {
     "nc_optimizer_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(NcOptimHparams)]),
     "nc_backward_weighted": (ctypes.c_int, [_P, _P, _P, _I32, _P]),
     "nc_kv_cache_bytes": (_I64, [ctypes.POINTER(NcConfig), _I32, _I32]),
+    "nc_sample": (ctypes.c_int, [_P, _I32, _I32, _F32, _I32, _P, _P, _P]),
     "nc_decode_scratch_bytes": (_I64, [ctypes.POINTER(NcConfig), _I32, _I32]),
     "nc_prefill": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, _I32, _P]),
     "nc_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, _I32, _P, _P]),
@@ -189,6 +190,12 @@ def optim_scratch_bytes(cfg) -> int:
     n = lib().nc_optim_scratch_bytes(ctypes.byref(_c(cfg)))
     _check(0 if n >= 0 else n, "nc_optim_scratch_bytes")
     return n
+
+
+def sample(logits, n: int, V: int, temperature: float, top_k: int, u, out, stream=None):
+    """nc_sample: next token per row of fp32 logits [n][V] from uniforms u [n]."""
+    _check(lib().nc_sample(_ptr(logits), int(n), int(V), float(temperature), int(top_k), _ptr(u), _ptr(out),
+                           _ptr(stream)), "nc_sample")
 
 
 def kv_cache_bytes(cfg, max_batch: int, max_len: int) -> int:

@@ -211,7 +211,136 @@ __global__ void __launch_bounds__(128) k_attn_decode_combine(AttnDecodeDesc a) {
   if (i < Q) ((T*)a.o)[(int64_t)b * a.H * Q + h * Q + i] = from_f32<T>(num / den);
 }
 
+// order-preserving map of a float to uint32 (larger float -> larger key)
+__device__ inline uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Next token of row blockIdx.x of logits [n][V] (see nc_sample).  Thread t
+// owns the contiguous ids [t seg, (t+1) seg); every sum runs in a fixed
+// order, in fp64.
+__global__ void __launch_bounds__(1024) k_sample(const float* __restrict__ logits, int V, float temperature,
+                                                  int top_k, const float* __restrict__ u, int32_t* __restrict__ out) {
+  constexpr int NT = 1024;
+  __shared__ float smax[NT];
+  __shared__ int sarg[NT];
+  __shared__ int hist[256];
+  __shared__ double ssum[NT];
+  __shared__ int s_bin, s_k, s_found;
+  const int tid = threadIdx.x;
+  const float* z = logits + (int64_t)blockIdx.x * V;
+  const int seg = (V + NT - 1) / NT;
+  const int i0 = min(V, tid * seg), i1 = min(V, i0 + seg);
+  // 1. largest logit, first id on ties
+  float mx = -INFINITY;
+  int am = V;
+  for (int i = i0; i < i1; ++i)
+    if (z[i] > mx || am == V) { mx = z[i]; am = i; }
+  smax[tid] = mx;
+  sarg[tid] = am;
+  __syncthreads();
+  for (int w = NT / 2; w > 0; w >>= 1) {
+    if (tid < w) {
+      const float a = smax[tid], b = smax[tid + w];
+      const int ia = sarg[tid], ib = sarg[tid + w];
+      if (b > a || (b == a && ib < ia) || ia == V) {
+        if (ib != V) { smax[tid] = b; sarg[tid] = ib; }
+      }
+    }
+    __syncthreads();
+  }
+  const float zmax = smax[0];
+  if (temperature == 0.f) {
+    if (tid == 0) out[blockIdx.x] = sarg[0];
+    return;
+  }
+  // 2. the k-th largest key, 8 bits per pass (ties at it are all kept)
+  uint32_t prefix = 0, mask = 0;
+  const bool select = top_k > 0 && top_k < V;
+  if (select) {
+    if (tid == 0) s_k = top_k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int b = tid; b < 256; b += NT) hist[b] = 0;
+      __syncthreads();
+      for (int i = i0; i < i1; ++i) {
+        const uint32_t key = fkey(z[i]);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int cum = 0, k = s_k, b = 255;
+        for (; b > 0; --b) {
+          if (cum + hist[b] >= k) break;
+          cum += hist[b];
+        }
+        s_bin = b;
+        s_k = k - cum;
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_bin << shift;
+      mask |= 255u << shift;
+      __syncthreads();
+    }
+  }
+  const uint32_t thr = prefix;
+  // 3. weights exp((z - max) / temperature) over the kept ids, fp64
+  double part = 0.0;
+  int last = -1;
+  for (int i = i0; i < i1; ++i) {
+    if (!select || fkey(z[i]) >= thr) {
+      part += exp(((double)z[i] - (double)zmax) / (double)temperature);
+      last = i;
+    }
+  }
+  ssum[tid] = part;
+  sarg[tid] = last;
+  __syncthreads();
+  // inclusive scan of the per-thread sums (Hillis-Steele, fixed order)
+  for (int o = 1; o < NT; o <<= 1) {
+    const double add = tid >= o ? ssum[tid - o] : 0.0;
+    __syncthreads();
+    ssum[tid] += add;
+    __syncthreads();
+  }
+  const double total = ssum[NT - 1];
+  const double target = (double)u[blockIdx.x] * total;
+  const double excl = tid > 0 ? ssum[tid - 1] : 0.0;
+  if (tid == 0) s_found = 0;
+  __syncthreads();
+  // 4. the thread whose range holds the target walks its ids
+  if (excl <= target && target < ssum[tid]) {
+    double run = excl;
+    int pick = last;      // if re-adding in this order rounds past the target: the range's last id
+    for (int i = i0; i < i1; ++i) {
+      if (!select || fkey(z[i]) >= thr) {
+        run += exp(((double)z[i] - (double)zmax) / (double)temperature);
+        if (run > target) {
+          pick = i;
+          break;
+        }
+      }
+    }
+    out[blockIdx.x] = pick;
+    s_found = 1;
+  }
+  __syncthreads();
+  if (!s_found && tid == 0) {
+    // rounding left no id past the target: the last kept id
+    int l = -1;
+    for (int t = 0; t < NT; ++t) l = max(l, sarg[t]);
+    out[blockIdx.x] = l;
+  }
+}
+
 }  // namespace
+
+hipError_t sample(const float* logits, int n, int V, float temperature, int top_k, const float* u, int32_t* out,
+                  hipStream_t s) {
+  if (n < 1 || V < 1 || top_k < 0 || !(temperature >= 0.f)) return hipErrorInvalidValue;
+  k_sample<<<n, 1024, 0, s>>>(logits, V, temperature, top_k, u, out);
+  return hipGetLastError();
+}
 
 template <typename T>
 hipError_t gemv(const GemvDesc& g, int epi, hipStream_t s) {

@@ -1064,6 +1064,15 @@ int nc_optimizer_step(nc_ctx* ctx, float* master, void* params, const float* gra
              : optimizer_step<float>(ctx, master, (float*)params, grads, (float*)state, (char*)scratch, hp);
 }
 
+int nc_sample(const float* logits, int32_t n, int32_t V, float temperature, int32_t top_k, const float* u,
+              int32_t* out, void* hip_stream) {
+  if (!logits || !u || !out) return NC_ERR_INVALID_ARG;
+  if (!(temperature >= 0.f) || !std::isfinite(temperature) || top_k < 0) return NC_ERR_INVALID_ARG;
+  if (n < 1 || V < 1) return NC_ERR_SHAPE;
+  return sample(logits, n, V, temperature, top_k, u, out, (hipStream_t)hip_stream) == hipSuccess ? NC_OK
+                                                                                                   : NC_ERR_HIP;
+}
+
 int64_t nc_kv_cache_bytes(const nc_config* cfg, int32_t max_batch, int32_t max_len) {
   int st = validate(cfg);
   if (st != NC_OK) return st;

@@ -171,6 +171,9 @@ struct AttnDecodeDesc {
   void* o;                  // [nb][H Q]
 };
 int attn_decode_chunks(int L);
+// next token per row of logits [n][V] (nc_sample)
+hipError_t sample(const float* logits, int n, int V, float temperature, int top_k, const float* u, int32_t* out,
+                  hipStream_t s);
 template <typename T> hipError_t attn_decode(const AttnDecodeDesc& a, int nb, hipStream_t s);
 
 // ---------------------------------------------------------------------------

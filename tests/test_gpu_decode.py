@@ -127,3 +127,38 @@ def test_d20_decode_matches_forward():
     params = synthdata.make_params(cfg)
     prompt, gen = _tokens(cfg, 200, 2, 3, 53)
     _check(cfg, params, prompt, gen, 2, bf16=True)
+
+
+@pytest.mark.parametrize("V,temperature,top_k", [(4096, 0.0, 0), (4096, 1.0, 0), (65536, 0.8, 50),
+                                                 (65536, 1.0, 1), (1000, 1.3, 7), (65536, 1.0, 0)])
+def test_sample_matches_oracle(V, temperature, top_k):
+    """nc_sample against oracle.sample_next on 64 rows with the same
+    uniforms, including a row of all-equal logits (top-k keeps every tie)
+    and a row with one dominant logit.  The weights and their running sums
+    are fp64 on both sides, so the draws agree unless u * sum lands within
+    fp64 rounding of a boundary of the inverse CDF, which is checked."""
+    rng = np.random.default_rng(60 + V + top_k)
+    n = 64
+    z = (rng.standard_normal((n, V)) * 3).astype(np.float32)
+    z[5, :] = 0.25
+    z[6, 17] = 40.0
+    u = rng.random(n).astype(np.float32)
+    out = empty((n,), "i32")
+    nc.sample(dev(z), n, V, temperature, top_k, dev(u), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    t32 = float(np.float32(temperature))
+    for r in range(n):
+        want = oracle.sample_next(z[r].astype(np.float64), t32, top_k, float(u[r]))
+        if got[r] == want:
+            continue
+        zz = z[r].astype(np.float64)
+        keep = np.ones(V, bool) if top_k in (0,) or top_k >= V else zz >= np.sort(zz)[::-1][top_k - 1]
+        c = np.cumsum(np.where(keep, np.exp((zz - zz.max()) / t32), 0.0))
+        assert keep[got[r]] and abs(c[min(got[r], want)] - float(u[r]) * c[-1]) <= 1e-12 * c[-1], (r, got[r], want)
+    if temperature == 0.0:
+        np.testing.assert_array_equal(got, np.argmax(z, axis=1))
+    if top_k == 1:
+        # one largest logit: top-1 is greedy; the all-equal row keeps every tie
+        unique = (z == z.max(axis=1, keepdims=True)).sum(axis=1) == 1
+        np.testing.assert_array_equal(got[unique], np.argmax(z, axis=1)[unique])

@@ -192,3 +192,8 @@ def test_inference_sizes_and_null_context():
     L = nc.lib()
     assert L.nc_prefill(None, 1, 1, 1, 1, 1, 1, 64, 1) == -1
     assert L.nc_decode(None, 1, 1, 1, 0, 1, 1, 64, 256, 1) == -1
+    # nc_sample checks its arguments before any launch
+    assert L.nc_sample(None, 1, 8, 1.0, 0, 1, 1, None) == -1
+    assert L.nc_sample(16, 1, 8, -1.0, 0, 16, 16, None) == -1
+    assert L.nc_sample(16, 1, 8, 1.0, -2, 16, 16, None) == -1
+    assert L.nc_sample(16, 0, 8, 1.0, 0, 16, 16, None) == -2
