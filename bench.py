@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--mfma-calibration", action="store_true")
     ap.add_argument("--optimizer", action="store_true",
                     help="time the optimiser step (Muon + AdamW) over the configuration's parameters")
+    ap.add_argument("--decode", action="store_true",
+                    help="time KV-cache inference: prefill of a 512-token prompt, then sampled decode steps")
     ap.add_argument("--library-gemm", action="store_true",
                     help="time the vendor BLAS (torch.matmul) next to nc_op_matmul on the d20 product shapes")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
@@ -231,6 +233,68 @@ def optimizer_timing(torch, nc, cfg, steps=5, warmup=1, trace=True):
     return out
 
 
+def decode_timing(torch, nc, cfg, nseqs=(1, 8, 16), prompt=512, steps=128):
+    """Time nc_prefill + nc_decode + nc_sample on the configuration's model.
+    Per batch of nseq sequences: one prefill of a `prompt`-token prompt,
+    then `steps` decode steps, each followed by sampling (temperature 1,
+    top-k 50, uniforms drawn beforehand on the device).  The decode rate
+    is tokens/s over the timed steps; the HBM rate counts each step's
+    algorithmic bytes: every block matrix and U once, nseq rows of E, the
+    keys and values read so far, the new K/V and the fp32 logits."""
+    import numpy as np
+    import synthdata
+    d, V, L, F = cfg.d_model, cfg.vocab, cfg.n_layer, cfg.d_ff
+    es = 2 if cfg.dtype == "bf16" else 4
+    pcfg = cfg.with_(batch=1, seq_len=prompt)
+    c = nc.make_config(pcfg)
+    sess = nc.Session(pcfg)
+    stream = sess.stream
+    params = synthdata.make_params(cfg)
+    P = torch.from_numpy(synthdata.f32_to_bf16_bits(params).view(np.int16) if es == 2 else params).cuda()
+    g = torch.Generator(device="cuda").manual_seed(11)
+    idx = torch.randint(0, V, (prompt,), device="cuda", generator=g, dtype=torch.int32)
+    res = []
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for nseq in nseqs:
+        ml = prompt + steps + 1
+        kv = torch.zeros(nc.kv_cache_bytes(c, nseq, ml), dtype=torch.uint8, device="cuda")
+        scr = torch.empty(nc.decode_scratch_bytes(c, nseq, ml) + 256, dtype=torch.uint8, device="cuda")
+        sp = (scr.data_ptr() + 255) // 256 * 256
+        logits = torch.empty(nseq, V, dtype=torch.float32, device="cuda")
+        u = torch.rand(steps + 1, nseq, device="cuda", generator=g)
+        tok = torch.empty(steps + 1, nseq, dtype=torch.int32, device="cuda")
+        # warm-up pass (also the first run of every kernel)
+        sess.prefill(P, idx, prompt, nseq, kv, nseq, ml, logits)
+        sess.decode(P, idx[:nseq], nseq, prompt, kv, nseq, ml, sp, logits)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        sess.prefill(P, idx, prompt, nseq, kv, nseq, ml, logits)
+        ev[1].record(stream)
+        nc.sample(logits, 1, V, 1.0, 50, u[0], tok[0], stream.cuda_stream)
+        if nseq > 1:
+            tok[0].copy_(tok[0, :1].expand(nseq))
+        ev[2].record(stream)
+        for i in range(steps):
+            sess.decode(P, tok[i], nseq, prompt + i, kv, nseq, ml, sp, logits)
+            nc.sample(logits, nseq, V, 1.0, 50, u[i + 1], tok[i + 1], stream.cuda_stream)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        t_pre = ev[0].elapsed_time(ev[1])
+        t_dec = ev[2].elapsed_time(ev[3]) / steps
+        kv_read = sum(nseq * (prompt + i + 1) * 2 * d * L * es for i in range(steps)) / steps
+        step_bytes = (12 * L * d * d + V * d) * es + nseq * d * es + kv_read + nseq * 2 * d * L * es + nseq * V * 4
+        res.append({"nseq": nseq, "prompt_tokens": prompt, "decode_steps": steps,
+                    "prefill_ms": round(t_pre, 3), "prefill_tokens_per_s": round(prompt / (t_pre * 1e-3), 1),
+                    "decode_ms_per_step": round(t_dec, 4),
+                    "decode_tokens_per_s": round(nseq / (t_dec * 1e-3), 1),
+                    "decode_hbm_gbps": round(step_bytes / (t_dec * 1e-3) / 1e9, 1),
+                    "decode_hbm_frac_of_8tbps": round(step_bytes / (t_dec * 1e-3) / 8e12, 4),
+                    "decode_bytes_per_step": step_bytes})
+        print(f"[decode] {res[-1]}", file=sys.stderr, flush=True)
+        del kv, scr
+    return res
+
+
 def measured_peaks(torch, nc, stream):
     """What the chip sustains on this machine, next to the spec peaks: the bf16
     matrix-core rate of a register-only MFMA loop (nc_op_mfma_loop: 8
@@ -278,6 +342,17 @@ def main():
         return
     if args.library_gemm:
         library_gemm()
+        return
+    if args.decode:
+        import torch
+        import synthdata
+        import decoder_only_transformer_d20_amd as nc
+        cfg = synthdata.get_config(args.config)
+        r = decode_timing(torch, nc, cfg)
+        print(json.dumps({"metric": "KV-cache decode tokens/s (sampled, temperature 1, top-k 50)",
+                          "config": {"workload": f"{cfg.name}: prefill of a 512-token prompt, then 128 decode "
+                                                 f"steps per batch of sequences, {cfg.dtype}"},
+                          "results": r}), flush=True)
         return
     if args.optimizer:
         import torch

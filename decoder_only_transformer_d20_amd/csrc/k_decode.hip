@@ -38,15 +38,21 @@ template <> struct V16<bf16> {
 };
 
 // y[b][n] = epi(sum_k x[b][k] W[n][k]) for b < nb (<= kMaxDecodeBatch), W
-// [N][K] row-major in T, x [nb][K].  Wave w owns columns 4w .. 4w+3; each
-// lane walks K in 16-byte pieces, 64 pieces (one coalesced row segment) per
-// step, then the 64 lanes' partial sums are combined by a butterfly.
-template <typename T, int EPI>
+// [N][K] row-major in T, x [nb][K].  Workgroup g owns columns 4g .. 4g+3;
+// its 4 waves take interleaved 16-byte pieces of K (wave w, lane l: pieces
+// 64w + l + 256i), so 256 coalesced pieces of each row are in flight per
+// step.  Partial sums are combined by a butterfly within each wave and then
+// across the waves in LDS, in a fixed order.
+template <typename T, int EPI, int S>
 __global__ void __launch_bounds__(256) k_gemv(GemvDesc g) {
+  // S waves share a group of kCols columns, splitting K (S = 4: one group per
+  // workgroup, for narrow products; S = 1: four groups per workgroup, each
+  // wave its own, for the wide logits product)
   constexpr int VE = V16<T>::n;
-  const int lane = threadIdx.x & 63;
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kCols;
-  if (n0 >= g.N) return;
+  __shared__ float red[4][kMaxDecodeBatch * kCols];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave / S, sub = wave % S;
+  const int64_t n0 = ((int64_t)blockIdx.x * (4 / S) + grp) * kCols;   // < N: the launch covers N exactly
   const T* W = (const T*)g.W;
   const T* x = (const T*)g.x;
   float acc[kMaxDecodeBatch][kCols];
@@ -54,7 +60,8 @@ __global__ void __launch_bounds__(256) k_gemv(GemvDesc g) {
   for (int b = 0; b < kMaxDecodeBatch; ++b)
 #pragma unroll
     for (int c = 0; c < kCols; ++c) acc[b][c] = 0.f;
-  for (int k = lane * VE; k < g.K; k += kWaveD * VE) {
+#pragma unroll 2
+  for (int k = (sub * 64 + lane) * VE; k < g.K; k += S * 64 * VE) {
     float w[kCols][VE];
 #pragma unroll
     for (int c = 0; c < kCols; ++c) V16<T>::load(W + (n0 + c) * (int64_t)g.K + k, w[c]);
@@ -70,38 +77,50 @@ __global__ void __launch_bounds__(256) k_gemv(GemvDesc g) {
       }
     }
   }
-  // butterfly: every lane ends with every (b, c) total
 #pragma unroll
   for (int b = 0; b < kMaxDecodeBatch; ++b) {
     if (b < g.nb) {
 #pragma unroll
-      for (int c = 0; c < kCols; ++c)
-        for (int o = 32; o > 0; o >>= 1) acc[b][c] += __shfl_xor(acc[b][c], o, 64);
+      for (int c = 0; c < kCols; ++c) {
+        float v = acc[b][c];
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0) red[wave][b * kCols + c] = v;
+      }
     }
   }
-  // lane b * kCols + c finishes output (b, n0 + c)
-#pragma unroll
-  for (int b = 0; b < kMaxDecodeBatch; ++b) {
-    if (b >= g.nb) continue;
-#pragma unroll
-    for (int c = 0; c < kCols; ++c) {
-      if (lane != b * kCols + c) continue;
-      const int64_t n = n0 + c;
-      float v = acc[b][c];
-      if constexpr (EPI == EPI_ROPE) {
-        // adjacent pairs (2i, 2i+1) of the rotated columns, angle at g.pos
-        if (n < g.rope_cols) {
-          const float other = acc[b][c ^ 1];
-          const float2 cs = g.rope[(n % g.head_dim) >> 1];
-          v = (c & 1) ? other * cs.y + v * cs.x : v * cs.x - other * cs.y;
-        }
+  auto total = [&](int t) {
+    if constexpr (S == 4) return (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+    else return red[wave][t];
+  };
+  __syncthreads();
+  // lane b * kCols + c of the group's first wave finishes output (b, n0 + c)
+  const int t = lane;
+  if (sub != 0 || t >= g.nb * kCols) return;
+  const int b = t / kCols, c = t % kCols;
+  const int64_t n = n0 + c;
+  float v = total(t);
+  if constexpr (EPI == EPI_ROPE) {
+    // adjacent pairs (2i, 2i+1) of the rotated columns, angles of one position
+    if (n < g.rope_cols) {
+      const int tp = t ^ 1;
+      const float other = total(tp);
+      const float2 cs = g.rope[(n % g.head_dim) >> 1];
+      v = (c & 1) ? other * cs.y + v * cs.x : v * cs.x - other * cs.y;
+    }
+  }
+  if constexpr (EPI == EPI_RESID) v += to_f32(((const T*)g.aux)[(int64_t)b * g.ldy + n]);
+  if constexpr (EPI == EPI_RELU2) v = fmaxf(v, 0.f) * fmaxf(v, 0.f);
+  if constexpr (EPI == EPI_F32) {
+    ((float*)g.y)[(int64_t)b * g.ldy + n] = v;
+  } else {
+    const T out = from_f32<T>(v);
+    ((T*)g.y)[(int64_t)b * g.ldy + n] = out;
+    // the qkv product also appends k and v to the cache at position pos
+    if constexpr (EPI == EPI_ROPE) {
+      if (g.kv_K && n >= g.kv_d) {
+        T* dst = n < 2 * g.kv_d ? (T*)g.kv_K + (n - g.kv_d) : (T*)g.kv_V + (n - 2 * g.kv_d);
+        dst[(int64_t)b * g.kv_seq_stride + (int64_t)g.kv_pos * g.kv_d] = out;
       }
-      if constexpr (EPI == EPI_RESID) v += to_f32(((const T*)g.aux)[(int64_t)b * g.ldy + n]);
-      if constexpr (EPI == EPI_RELU2) v = fmaxf(v, 0.f) * fmaxf(v, 0.f);
-      if constexpr (EPI == EPI_F32)
-        ((float*)g.y)[(int64_t)b * g.ldy + n] = v;
-      else
-        ((T*)g.y)[(int64_t)b * g.ldy + n] = from_f32<T>(v);
     }
   }
 }
@@ -132,66 +151,73 @@ __global__ void __launch_bounds__(256) k_kv_prefill(const T* __restrict__ qkv, i
 }
 
 // Decode attention, pass 1: workgroup (chunk, h, b) scores keys
-// [chunk * 256, +256) of sequence b against q (head h), L keys in all, and
+// [64 chunk, +64) of sequence b against q (head h), L keys in all, and
 // writes the chunk's max m, sum l and unnormalised output o[Q] (fp32) to
-// part[b][h][chunk] = {m, l, o[Q]}.
-template <typename T>
+// part[b][h][chunk] = {m, l, o[Q]}.  Four threads share a key's dot product
+// (Q/4 dimensions each); for the values, wave w takes keys 16w .. 16w+15
+// and lane l dimensions 2l, 2l+1, one coalesced row per key.
+template <typename T, int Q>
 __global__ void __launch_bounds__(256) k_attn_decode(AttnDecodeDesc a) {
-  constexpr int kChunk = 256;
-  __shared__ float qs[256];
+  constexpr int kChunk = 64, QP = Q / 4;
+  static_assert(Q % 32 == 0 && Q <= 128, "head dim");
+  __shared__ float qs[Q];
   __shared__ float ps[kChunk];
   __shared__ float red[8];
-  __shared__ float os[4][256];
+  __shared__ float os[4][Q];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Q = a.Q, d = a.H * a.Q;
+  const int d = a.H * Q;
   const T* q = (const T*)a.qkv + (int64_t)b * 3 * d + h * Q;
-  for (int i = tid; i < Q; i += 256) qs[i] = to_f32(q[i]);
+  if (tid < Q) qs[tid] = to_f32(q[tid]);
   __syncthreads();
   const int64_t base = (int64_t)b * a.seq_stride + h * Q;
-  const int j = chunk * kChunk + tid;      // this thread's key
-  float sc = -INFINITY;
+  const int jl = tid >> 2, part = tid & 3;
+  const int j = chunk * kChunk + jl;
+  float s = 0.f;
   if (j < a.L) {
-    const T* kr = (const T*)a.K + base + (int64_t)j * d;
-    float s = 0.f;
-    for (int i = 0; i < Q; i += V16<T>::n) {
+    const T* kr = (const T*)a.K + base + (int64_t)j * d + part * QP;
+#pragma unroll
+    for (int i = 0; i < QP; i += V16<T>::n) {
       float kv[V16<T>::n];
       V16<T>::load(kr + i, kv);
 #pragma unroll
-      for (int e = 0; e < V16<T>::n; ++e) s = fmaf(qs[i + e], kv[e], s);
+      for (int e = 0; e < V16<T>::n; ++e) s = fmaf(qs[part * QP + i + e], kv[e], s);
     }
-    sc = s * a.scale_log2;
   }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  const float sc = j < a.L ? s * a.scale_log2 : -INFINITY;
   float mx = sc;
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   if (lane == 0) red[wave] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float p = j < a.L ? __builtin_amdgcn_exp2f(sc - M) : 0.f;
-  ps[tid] = p;
-  float l = p;
+  if (part == 0) ps[jl] = p;
+  float l = part == 0 ? p : 0.f;
   for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
   __syncthreads();
   if (lane == 0) red[4 + wave] = l;
-  // o: wave w sums keys 64w .. 64w+63 of the chunk; lane handles dims
-  // lane and lane + 64 (Q <= 128)
   float o0 = 0.f, o1 = 0.f;
-  const int jend = min(kChunk, a.L - chunk * kChunk);
-  for (int jj = wave * 64; jj < min(wave * 64 + 64, jend); ++jj) {
-    const T* vr = (const T*)a.V + base + (int64_t)(chunk * kChunk + jj) * d;
-    const float pj = ps[jj];
-    if (lane < Q) o0 = fmaf(pj, to_f32(vr[lane]), o0);
-    if (lane + 64 < Q) o1 = fmaf(pj, to_f32(vr[lane + 64]), o1);
+  const int jn = min(kChunk, a.L - chunk * kChunk);
+  if (2 * lane < Q) {
+#pragma unroll 4
+    for (int jj = wave * 16; jj < min(wave * 16 + 16, jn); ++jj) {
+      const T* vr = (const T*)a.V + base + (int64_t)(chunk * kChunk + jj) * d + 2 * lane;
+      const float pj = ps[jj];
+      o0 = fmaf(pj, to_f32(vr[0]), o0);
+      o1 = fmaf(pj, to_f32(vr[1]), o1);
+    }
+    os[wave][2 * lane] = o0;
+    os[wave][2 * lane + 1] = o1;
   }
-  os[wave][lane] = o0;
-  os[wave][lane + 64] = o1;
   __syncthreads();
   float* out = a.part + (((int64_t)b * a.H + h) * a.nchunks + chunk) * (2 + Q);
   if (tid == 0) {
     out[0] = M;
     out[1] = (red[4] + red[5]) + (red[6] + red[7]);
   }
-  for (int i = tid; i < Q; i += 256) out[2 + i] = (os[0][i] + os[1][i]) + (os[2][i] + os[3][i]);
+  if (tid < Q) out[2 + tid] = (os[0][tid] + os[1][tid]) + (os[2][tid] + os[3][tid]);
 }
 
 // pass 2: combine the chunks of (h, b): o = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c
@@ -346,15 +372,23 @@ template <typename T>
 hipError_t gemv(const GemvDesc& g, int epi, hipStream_t s) {
   if (g.nb < 1 || g.nb > kMaxDecodeBatch || g.N % kCols || g.K % V16<T>::n || g.N <= 0 || g.K <= 0)
     return hipErrorInvalidValue;
-  const unsigned blocks = (unsigned)((g.N / kCols + 3) / 4);
+  // narrow products: 4 waves per column group (K split) for enough waves;
+  // wide ones (the logits): a group per wave, the input read by 4x fewer waves
+  const bool wide = g.N >= 16384 && g.N % (4 * kCols) == 0;
+  const unsigned blocks = wide ? (unsigned)(g.N / (4 * kCols)) : (unsigned)(g.N / kCols);
+#define NC_GEMV(E)                                                   \
+  if (wide) k_gemv<T, E, 1><<<blocks, 256, 0, s>>>(g);               \
+  else k_gemv<T, E, 4><<<blocks, 256, 0, s>>>(g);                    \
+  break;
   switch (epi) {
-    case EPI_STORE: k_gemv<T, EPI_STORE><<<blocks, 256, 0, s>>>(g); break;
-    case EPI_ROPE: k_gemv<T, EPI_ROPE><<<blocks, 256, 0, s>>>(g); break;
-    case EPI_RESID: k_gemv<T, EPI_RESID><<<blocks, 256, 0, s>>>(g); break;
-    case EPI_RELU2: k_gemv<T, EPI_RELU2><<<blocks, 256, 0, s>>>(g); break;
-    case EPI_F32: k_gemv<T, EPI_F32><<<blocks, 256, 0, s>>>(g); break;
+    case EPI_STORE: NC_GEMV(EPI_STORE)
+    case EPI_ROPE: NC_GEMV(EPI_ROPE)
+    case EPI_RESID: NC_GEMV(EPI_RESID)
+    case EPI_RELU2: NC_GEMV(EPI_RELU2)
+    case EPI_F32: NC_GEMV(EPI_F32)
     default: return hipErrorInvalidValue;
   }
+#undef NC_GEMV
   return hipGetLastError();
 }
 
@@ -370,12 +404,16 @@ hipError_t kv_prefill(const T* qkv, int len, int d, int nb, T* K, T* V, int64_t 
   return hipGetLastError();
 }
 
-int attn_decode_chunks(int L) { return (L + 255) / 256; }
+int attn_decode_chunks(int L) { return (L + 63) / 64; }
 
 template <typename T>
 hipError_t attn_decode(const AttnDecodeDesc& a, int nb, hipStream_t s) {
-  if (a.Q > 128 || a.Q % V16<T>::n || a.L < 1 || a.nchunks != attn_decode_chunks(a.L)) return hipErrorInvalidValue;
-  k_attn_decode<T><<<dim3(a.nchunks, a.H, nb), 256, 0, s>>>(a);
+  if (a.L < 1 || a.nchunks != attn_decode_chunks(a.L) || a.nchunks > 65535) return hipErrorInvalidValue;
+  if (a.Q == 128) k_attn_decode<T, 128><<<dim3(a.nchunks, a.H, nb), 256, 0, s>>>(a);
+  else if (a.Q == 64) k_attn_decode<T, 64><<<dim3(a.nchunks, a.H, nb), 256, 0, s>>>(a);
+  else if (a.Q == 96) k_attn_decode<T, 96><<<dim3(a.nchunks, a.H, nb), 256, 0, s>>>(a);
+  else if (a.Q == 32) k_attn_decode<T, 32><<<dim3(a.nchunks, a.H, nb), 256, 0, s>>>(a);
+  else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_attn_decode_combine<T><<<dim3(a.H, nb), 128, 0, s>>>(a);

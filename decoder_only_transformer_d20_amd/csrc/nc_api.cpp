@@ -740,7 +740,7 @@ DecodeScratch decode_scratch(const nc_config& c, int mb, int ml) {
 int kv_shape_ok(const nc_config& c, int mb, int ml) {
   if (is_block(c)) return NC_ERR_STATE;
   if (mb < 1 || mb > kMaxDecodeBatch || ml < 1 || ml > (1 << 24)) return NC_ERR_SHAPE;
-  if (c.head_dim > 128) return NC_ERR_UNSUPPORTED;
+  if (c.head_dim != 32 && c.head_dim != 64 && c.head_dim != 96 && c.head_dim != 128) return NC_ERR_UNSUPPORTED;
   return NC_OK;
 }
 
@@ -804,8 +804,14 @@ int decode(nc_ctx* ctx, const T* params, const int32_t* tokens, int nseq, int po
     T* K = kv + l * lstride;
     T* Vc = K + (int64_t)mb * sstride;
     NC_TRY(rmsnorm_fwd<T>(x, a, r, nseq, d, c.rms_eps, s), "decode rmsnorm (attention)");
-    NC_TRY(gv(Wqkv, 3 * d, d, a, qkv, 3 * d, EPI_ROPE), "decode qkv");
-    NC_TRY(kv_append<T>(qkv, nseq, d, K, Vc, sstride, pos, s), "kv append");
+    {
+      // q, k, v with rotary; k and v also appended to the cache at pos
+      GemvDesc g{};
+      g.nb = nseq; g.N = 3 * d; g.K = d; g.W = Wqkv; g.x = a; g.ldx = d; g.y = qkv; g.ldy = 3 * d;
+      g.rope = rope; g.rope_cols = 2 * d; g.head_dim = Q;
+      g.kv_K = K; g.kv_V = Vc; g.kv_seq_stride = sstride; g.kv_d = d; g.kv_pos = pos;
+      NC_TRY(gemv<T>(g, EPI_ROPE, s), "decode qkv + kv append");
+    }
     AttnDecodeDesc ad{};
     ad.H = H; ad.Q = Q; ad.L = pos + 1; ad.nchunks = attn_decode_chunks(pos + 1);
     ad.qkv = qkv; ad.K = K; ad.V = Vc; ad.seq_stride = sstride;

@@ -155,6 +155,9 @@ struct GemvDesc {
   void* y; int64_t ldy;
   const void* aux;
   const float2* rope; int rope_cols, head_dim;
+  // EPI_ROPE on qkv: when kv_K is set, columns [d, 2d) also go to
+  // kv_K[b][pos][:] and [2d, 3d) to kv_V[b][pos][:] (seq stride in elements)
+  void* kv_K; void* kv_V; int64_t kv_seq_stride; int kv_d, kv_pos;
 };
 template <typename T> hipError_t gemv(const GemvDesc& g, int epi, hipStream_t s);
 // K, V [batch][max_len][d] of one layer: seq_stride = max_len * d

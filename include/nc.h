@@ -183,7 +183,8 @@ int nc_loss_weighted(nc_ctx* ctx, const float* token_weights, double* out);
  * of one prompt decoded together.  The cache holds, per layer, K (rotated)
  * and V as [max_batch][max_len][d] in the model dtype, layer l's K at
  * element 2 l max_batch max_len d and its V right after.  Decode handles
- * at most 16 sequences, head_dim <= 128. */
+ * at most 16 sequences and head_dim 32, 64, 96 or 128 (else
+ * NC_ERR_UNSUPPORTED). */
 int64_t nc_kv_cache_bytes(const nc_config* cfg, int32_t max_batch, int32_t max_len);
 
 /* Bytes of the scratch nc_decode needs (256-byte aligned device memory). */
