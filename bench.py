@@ -62,6 +62,7 @@ def parse():
                     help="time the optimiser step (Muon + AdamW) over the configuration's parameters")
     ap.add_argument("--decode", action="store_true",
                     help="time KV-cache inference: prefill of a 512-token prompt, then sampled decode steps")
+    ap.add_argument("--decode-nseq", default="1,8,16", help="sequences per decode batch, comma-separated")
     ap.add_argument("--library-gemm", action="store_true",
                     help="time the vendor BLAS (torch.matmul) next to nc_op_matmul on the d20 product shapes")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
@@ -348,10 +349,12 @@ def main():
         import synthdata
         import decoder_only_transformer_d20_amd as nc
         cfg = synthdata.get_config(args.config)
-        r = decode_timing(torch, nc, cfg)
+        r = decode_timing(torch, nc, cfg, nseqs=tuple(int(x) for x in args.decode_nseq.split(",")))
         print(json.dumps({"metric": "KV-cache decode tokens/s (sampled, temperature 1, top-k 50)",
                           "config": {"workload": f"{cfg.name}: prefill of a 512-token prompt, then 128 decode "
                                                  f"steps per batch of sequences, {cfg.dtype}"},
+                          "roofline": {"bound": "hbm", "peak": 8000.0, "unit": "GB/s",
+                                       "achieved_by_nseq": {str(x["nseq"]): x["decode_hbm_gbps"] for x in r}},
                           "results": r}), flush=True)
         return
     if args.optimizer:

@@ -227,8 +227,10 @@ __global__ void __launch_bounds__(128) k_attn_decode_combine(AttnDecodeDesc a) {
   const int Q = a.Q;
   const float* part = a.part + ((int64_t)b * a.H + h) * a.nchunks * (2 + Q);
   float M = -INFINITY;
+#pragma unroll 8
   for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, part[c * (2 + Q)]);
   float num = 0.f, den = 0.f;
+#pragma unroll 8
   for (int c = 0; c < a.nchunks; ++c) {
     const float w = __builtin_amdgcn_exp2f(part[c * (2 + Q)] - M);
     den = fmaf(w, part[c * (2 + Q) + 1], den);
@@ -243,118 +245,150 @@ __device__ inline uint32_t fkey(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Next token of row blockIdx.x of logits [n][V] (see nc_sample).  Thread t
-// owns the contiguous ids [t seg, (t+1) seg); every sum runs in a fixed
-// order, in fp64.
+// Next token of row blockIdx.x of logits [n][V] (see nc_sample).  Every
+// pass reads the row coalesced.  The max and the digit counts stride over
+// the row; for the weights, wave w owns the contiguous ids [w S, (w+1) S)
+// and lane l the ids w S + 64 j + l, so the inverse-CDF walk is a
+// wave-wide scan, 64 ids per step.  Every sum runs in a fixed order.
 __global__ void __launch_bounds__(1024) k_sample(const float* __restrict__ logits, int V, float temperature,
                                                   int top_k, const float* __restrict__ u, int32_t* __restrict__ out) {
-  constexpr int NT = 1024;
-  __shared__ float smax[NT];
-  __shared__ int sarg[NT];
-  __shared__ int hist[256];
-  __shared__ double ssum[NT];
+  constexpr int NT = 1024, NW = NT / 64;
+  __shared__ float smax[NW];
+  __shared__ int sarg[NW];
+  __shared__ int hist[NW][16];
+  __shared__ double wsum[NW];
+  __shared__ int wlast[NW];
   __shared__ int s_bin, s_k, s_found;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* z = logits + (int64_t)blockIdx.x * V;
-  const int seg = (V + NT - 1) / NT;
-  const int i0 = min(V, tid * seg), i1 = min(V, i0 + seg);
   // 1. largest logit, first id on ties
   float mx = -INFINITY;
   int am = V;
-  for (int i = i0; i < i1; ++i)
+  for (int i = tid; i < V; i += NT)
     if (z[i] > mx || am == V) { mx = z[i]; am = i; }
-  smax[tid] = mx;
-  sarg[tid] = am;
-  __syncthreads();
-  for (int w = NT / 2; w > 0; w >>= 1) {
-    if (tid < w) {
-      const float a = smax[tid], b = smax[tid + w];
-      const int ia = sarg[tid], ib = sarg[tid + w];
-      if (b > a || (b == a && ib < ia) || ia == V) {
-        if (ib != V) { smax[tid] = b; sarg[tid] = ib; }
-      }
-    }
-    __syncthreads();
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(mx, o, 64);
+    const int a2 = __shfl_xor(am, o, 64);
+    if (a2 != V && (am == V || m2 > mx || (m2 == mx && a2 < am))) { mx = m2; am = a2; }
   }
-  const float zmax = smax[0];
+  if (lane == 0) { smax[wave] = mx; sarg[wave] = am; }
+  __syncthreads();
+  float zmax = smax[0];
+  int amax = sarg[0];
+  for (int w = 1; w < NW; ++w)
+    if (sarg[w] != V && (amax == V || smax[w] > zmax || (smax[w] == zmax && sarg[w] < amax))) {
+      zmax = smax[w];
+      amax = sarg[w];
+    }
   if (temperature == 0.f) {
-    if (tid == 0) out[blockIdx.x] = sarg[0];
+    if (tid == 0) out[blockIdx.x] = amax;
     return;
   }
-  // 2. the k-th largest key, 8 bits per pass (ties at it are all kept)
+  // 2. the k-th largest key, 4 bits per pass (ties at it are all kept);
+  // per-thread counts as 8-bit fields of 4 registers (at most V/1024 <= 255
+  // keys a thread, checked at launch), summed by a butterfly per wave and
+  // over the waves in LDS
   uint32_t prefix = 0, mask = 0;
   const bool select = top_k > 0 && top_k < V;
   if (select) {
     if (tid == 0) s_k = top_k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int b = tid; b < 256; b += NT) hist[b] = 0;
-      __syncthreads();
-      for (int i = i0; i < i1; ++i) {
+    for (int shift = 28; shift >= 0; shift -= 4) {
+      uint32_t pk0 = 0, pk1 = 0, pk2 = 0, pk3 = 0;
+      for (int i = tid; i < V; i += NT) {
         const uint32_t key = fkey(z[i]);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+        if ((key & mask) != prefix) continue;
+        const uint32_t dgt = (key >> shift) & 15u;
+        const uint32_t inc = 1u << (8 * (dgt & 3u));
+        const uint32_t q = dgt >> 2;
+        pk0 += q == 0 ? inc : 0u;
+        pk1 += q == 1 ? inc : 0u;
+        pk2 += q == 2 ? inc : 0u;
+        pk3 += q == 3 ? inc : 0u;
+      }
+#pragma unroll
+      for (int dg = 0; dg < 16; ++dg) {
+        const uint32_t word = dg < 4 ? pk0 : dg < 8 ? pk1 : dg < 12 ? pk2 : pk3;
+        int c = (int)((word >> (8 * (dg & 3))) & 255u);
+        for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+        if (lane == 0) hist[wave][dg] = c;
       }
       __syncthreads();
       if (tid == 0) {
-        int cum = 0, k = s_k, b = 255;
+        int cum = 0, k = s_k, b = 15;
         for (; b > 0; --b) {
-          if (cum + hist[b] >= k) break;
-          cum += hist[b];
+          int hb = 0;
+          for (int w = 0; w < NW; ++w) hb += hist[w][b];
+          if (cum + hb >= k) break;
+          cum += hb;
         }
         s_bin = b;
         s_k = k - cum;
       }
       __syncthreads();
       prefix |= (uint32_t)s_bin << shift;
-      mask |= 255u << shift;
-      __syncthreads();
+      mask |= 15u << shift;
     }
   }
   const uint32_t thr = prefix;
-  // 3. weights exp((z - max) / temperature) over the kept ids, fp64
+  const float wscale = 1.4426950408889634f / temperature;
+  auto weight = [&](int i) -> float {   // 0 outside the row and for ids not kept
+    if (i >= V) return 0.f;
+    const float zi = z[i];
+    if (select && fkey(zi) < thr) return 0.f;
+    return __builtin_amdgcn_exp2f((zi - zmax) * wscale);
+  };
+  // 3. per-wave totals over the wave's contiguous range (fp32 weights,
+  // fp64 sums: per lane across steps, then a butterfly)
+  const int S = ((V + NW - 1) / NW + 63) / 64 * 64;
+  const int w0 = wave * S, w1 = min(V, w0 + S);
   double part = 0.0;
   int last = -1;
-  for (int i = i0; i < i1; ++i) {
-    if (!select || fkey(z[i]) >= thr) {
-      part += exp(((double)z[i] - (double)zmax) / (double)temperature);
-      last = i;
-    }
+  for (int i = w0 + lane; i < w1; i += 64) {
+    part += (double)weight(i);
+    if (!select || fkey(z[i]) >= thr) last = i;
   }
-  ssum[tid] = part;
-  sarg[tid] = last;
-  __syncthreads();
-  // inclusive scan of the per-thread sums (Hillis-Steele, fixed order)
-  for (int o = 1; o < NT; o <<= 1) {
-    const double add = tid >= o ? ssum[tid - o] : 0.0;
-    __syncthreads();
-    ssum[tid] += add;
-    __syncthreads();
+  for (int o = 32; o > 0; o >>= 1) {
+    part += __shfl_xor(part, o, 64);
+    last = max(last, __shfl_xor(last, o, 64));
   }
-  const double total = ssum[NT - 1];
-  const double target = (double)u[blockIdx.x] * total;
-  const double excl = tid > 0 ? ssum[tid - 1] : 0.0;
+  if (lane == 0) { wsum[wave] = part; wlast[wave] = last; }
   if (tid == 0) s_found = 0;
   __syncthreads();
-  // 4. the thread whose range holds the target walks its ids
-  if (excl <= target && target < ssum[tid]) {
+  double total = 0.0, excl = 0.0;
+  for (int w = 0; w < NW; ++w) {
+    if (w == wave) excl = total;
+    total += wsum[w];
+  }
+  const double target = (double)u[blockIdx.x] * total;
+  // 4. the wave whose range holds the target scans it, 64 ids per step
+  if (excl <= target && target < excl + wsum[wave]) {
     double run = excl;
-    int pick = last;      // if re-adding in this order rounds past the target: the range's last id
-    for (int i = i0; i < i1; ++i) {
-      if (!select || fkey(z[i]) >= thr) {
-        run += exp(((double)z[i] - (double)zmax) / (double)temperature);
-        if (run > target) {
-          pick = i;
-          break;
-        }
+    int pick = wlast[wave];    // if rounding carries the scan past the target: the range's last kept id
+    for (int i0 = w0; i0 < w1; i0 += 64) {
+      const double wi = (double)weight(i0 + lane);
+      double incl = wi;
+      for (int o = 1; o < 64; o <<= 1) {
+        const double up = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += up;
       }
+      const bool hit = wi > 0.0 && run + incl > target;
+      const unsigned long long bal = __ballot(hit);
+      if (bal) {
+        pick = i0 + __ffsll((long long)bal) - 1;
+        break;
+      }
+      run += __shfl(incl, 63, 64);
     }
-    out[blockIdx.x] = pick;
-    s_found = 1;
+    if (lane == 0) {
+      out[blockIdx.x] = pick;
+      s_found = 1;
+    }
   }
   __syncthreads();
   if (!s_found && tid == 0) {
-    // rounding left no id past the target: the last kept id
+    // rounding left no id past the target: the row's last kept id
     int l = -1;
-    for (int t = 0; t < NT; ++t) l = max(l, sarg[t]);
+    for (int w = 0; w < NW; ++w) l = max(l, wlast[w]);
     out[blockIdx.x] = l;
   }
 }
@@ -363,7 +397,8 @@ __global__ void __launch_bounds__(1024) k_sample(const float* __restrict__ logit
 
 hipError_t sample(const float* logits, int n, int V, float temperature, int top_k, const float* u, int32_t* out,
                   hipStream_t s) {
-  if (n < 1 || V < 1 || top_k < 0 || !(temperature >= 0.f)) return hipErrorInvalidValue;
+  // a thread's share of a row must fit the 8-bit digit counters
+  if (n < 1 || V < 1 || V > 1024 * 255 || top_k < 0 || !(temperature >= 0.f)) return hipErrorInvalidValue;
   k_sample<<<n, 1024, 0, s>>>(logits, V, temperature, top_k, u, out);
   return hipGetLastError();
 }

@@ -212,10 +212,11 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t ns
  * otherwise p_i proportional to exp((z_i - max z) / temperature) over the
  * top_k largest logits (all when top_k == 0; ties with the k-th largest are
  * kept), drawn by inverse CDF in id order: the first kept id whose running
- * sum exceeds u[row] * sum p (fp64 sums in a fixed order).  u device fp32
- * [n] in [0, 1) are the caller's uniforms; out device int32 [n].  No
- * context: enqueued on hip_stream.  NC_ERR_INVALID_ARG on a negative
- * temperature or top_k, NC_ERR_SHAPE on n < 1 or V < 1. */
+ * sum exceeds u[row] * sum p (fp32 exponentials, fp64 sums in a fixed
+ * order).  u device fp32 [n] in [0, 1) are the caller's uniforms; out
+ * device int32 [n].  No context: enqueued on hip_stream.
+ * NC_ERR_INVALID_ARG on a negative temperature or top_k, NC_ERR_SHAPE on
+ * n < 1, V < 1 or V > 261120. */
 int nc_sample(const float* logits, int32_t n, int32_t V, float temperature, int32_t top_k, const float* u,
               int32_t* out, void* hip_stream);
 

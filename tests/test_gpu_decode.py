@@ -134,9 +134,11 @@ def test_d20_decode_matches_forward():
 def test_sample_matches_oracle(V, temperature, top_k):
     """nc_sample against oracle.sample_next on 64 rows with the same
     uniforms, including a row of all-equal logits (top-k keeps every tie)
-    and a row with one dominant logit.  The weights and their running sums
-    are fp64 on both sides, so the draws agree unless u * sum lands within
-    fp64 rounding of a boundary of the inverse CDF, which is checked."""
+    and a row with one dominant logit.  The GPU's weights are fp32
+    exponentials (relative error ~1e-7) summed in fp64, the oracle's fp64
+    throughout, so a draw may differ only where u * sum lies within 1e-6 of
+    the total from a boundary of the inverse CDF; such a draw must still be
+    a kept id next to the boundary."""
     rng = np.random.default_rng(60 + V + top_k)
     n = 64
     z = (rng.standard_normal((n, V)) * 3).astype(np.float32)
@@ -155,7 +157,7 @@ def test_sample_matches_oracle(V, temperature, top_k):
         zz = z[r].astype(np.float64)
         keep = np.ones(V, bool) if top_k in (0,) or top_k >= V else zz >= np.sort(zz)[::-1][top_k - 1]
         c = np.cumsum(np.where(keep, np.exp((zz - zz.max()) / t32), 0.0))
-        assert keep[got[r]] and abs(c[min(got[r], want)] - float(u[r]) * c[-1]) <= 1e-12 * c[-1], (r, got[r], want)
+        assert keep[got[r]] and abs(c[min(got[r], want)] - float(u[r]) * c[-1]) <= 1e-6 * c[-1], (r, got[r], want)
     if temperature == 0.0:
         np.testing.assert_array_equal(got, np.argmax(z, axis=1))
     if top_k == 1:
