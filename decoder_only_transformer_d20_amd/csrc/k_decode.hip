@@ -26,16 +26,21 @@ template <> struct V16<float> {
 };
 template <> struct V16<bf16> {
   static constexpr int n = 8;
-  __device__ static inline void load(const bf16* p, float (&o)[8]) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+  __device__ static inline void unpack(const uint4 v, float (&o)[8]) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      o[2 * i] = to_f32(bf16{(uint16_t)(w[i] & 0xffff)});
-      o[2 * i + 1] = to_f32(bf16{(uint16_t)(w[i] >> 16)});
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  __device__ static inline void load(const bf16* p, float (&o)[8]) { unpack(*reinterpret_cast<const uint4*>(p), o); }
 };
+template <> struct V16<float>;
+__device__ inline void unpack16(const uint4 v, float (&o)[4]) {
+  o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y); o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+}
+__device__ inline void unpack16(const uint4 v, float (&o)[8]) { V16<bf16>::unpack(v, o); }
 
 // y[b][n] = epi(sum_k x[b][k] W[n][k]) for b < nb (<= kMaxDecodeBatch), W
 // [N][K] row-major in T, x [nb][K].  Workgroup g owns columns 4g .. 4g+3;
@@ -60,16 +65,23 @@ __global__ void __launch_bounds__(256) k_gemv(GemvDesc g) {
   for (int b = 0; b < kMaxDecodeBatch; ++b)
 #pragma unroll
     for (int c = 0; c < kCols; ++c) acc[b][c] = 0.f;
-#pragma unroll 2
   for (int k = (sub * 64 + lane) * VE; k < g.K; k += S * 64 * VE) {
+    // every load of the step is issued before any arithmetic: the weight
+    // rows' pieces and each sequence's input piece, as raw 16-byte words
+    uint4 wr[kCols], xr[kMaxDecodeBatch];
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) wr[c] = *reinterpret_cast<const uint4*>(W + (n0 + c) * (int64_t)g.K + k);
+#pragma unroll
+    for (int b = 0; b < kMaxDecodeBatch; ++b)
+      xr[b] = b < g.nb ? *reinterpret_cast<const uint4*>(x + (int64_t)b * g.ldx + k) : make_uint4(0, 0, 0, 0);
     float w[kCols][VE];
 #pragma unroll
-    for (int c = 0; c < kCols; ++c) V16<T>::load(W + (n0 + c) * (int64_t)g.K + k, w[c]);
+    for (int c = 0; c < kCols; ++c) unpack16(wr[c], w[c]);
 #pragma unroll
     for (int b = 0; b < kMaxDecodeBatch; ++b) {
       if (b < g.nb) {
         float xv[VE];
-        V16<T>::load(x + (int64_t)b * g.ldx + k, xv);
+        unpack16(xr[b], xv);
 #pragma unroll
         for (int c = 0; c < kCols; ++c)
 #pragma unroll
@@ -77,16 +89,42 @@ __global__ void __launch_bounds__(256) k_gemv(GemvDesc g) {
       }
     }
   }
+  // reduce-scatter butterfly over the 64 (sequence, column) sums: at step
+  // s a lane keeps the half of its values selected by lane bit s and adds
+  // the partner's copy of that half, so after 6 steps (63 shuffles, not
+  // 6 per value) lane l holds the wave's total of value l = b * kCols + c
+  static_assert(kMaxDecodeBatch * kCols == 64, "one value per lane");
+  if (g.nb <= 2) {
+    // few values: a full butterfly per value is cheaper (6 shuffles each)
 #pragma unroll
-  for (int b = 0; b < kMaxDecodeBatch; ++b) {
-    if (b < g.nb) {
+    for (int b = 0; b < 2; ++b) {
+      if (b < g.nb) {
 #pragma unroll
-      for (int c = 0; c < kCols; ++c) {
-        float v = acc[b][c];
-        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-        if (lane == 0) red[wave][b * kCols + c] = v;
+        for (int c = 0; c < kCols; ++c) {
+          float t = acc[b][c];
+          for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+          if (lane == 0) red[wave][b * kCols + c] = t;
+        }
       }
     }
+  } else {
+  float vals[64];
+#pragma unroll
+  for (int b = 0; b < kMaxDecodeBatch; ++b)
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) vals[b * kCols + c] = acc[b][c];
+#pragma unroll
+  for (int st = 5; st >= 0; --st) {
+    const int half = 1 << st;
+    const bool upper = (lane >> st) & 1;
+#pragma unroll
+    for (int i = 0; i < half; ++i) {
+      const float send = upper ? vals[i] : vals[i + half];
+      const float keep = upper ? vals[i + half] : vals[i];
+      vals[i] = keep + __shfl_xor(send, half, 64);
+    }
+  }
+  red[wave][lane] = vals[0];
   }
   auto total = [&](int t) {
     if constexpr (S == 4) return (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
