@@ -302,6 +302,7 @@ __global__ void __launch_bounds__(1024) k_sample(const float* __restrict__ logit
   // 1. largest logit, first id on ties
   float mx = -INFINITY;
   int am = V;
+#pragma unroll 8
   for (int i = tid; i < V; i += NT)
     if (z[i] > mx || am == V) { mx = z[i]; am = i; }
   for (int o = 32; o > 0; o >>= 1) {
@@ -323,7 +324,7 @@ __global__ void __launch_bounds__(1024) k_sample(const float* __restrict__ logit
     return;
   }
   // 2. the k-th largest key, 4 bits per pass (ties at it are all kept);
-  // per-thread counts as 8-bit fields of 4 registers (at most V/1024 <= 255
+  // per-thread counts as 8-bit fields of 4 registers (at most V/1024 <= 64
   // keys a thread, checked at launch), summed by a butterfly per wave and
   // over the waves in LDS
   uint32_t prefix = 0, mask = 0;
@@ -332,6 +333,7 @@ __global__ void __launch_bounds__(1024) k_sample(const float* __restrict__ logit
     if (tid == 0) s_k = top_k;
     for (int shift = 28; shift >= 0; shift -= 4) {
       uint32_t pk0 = 0, pk1 = 0, pk2 = 0, pk3 = 0;
+#pragma unroll 8
       for (int i = tid; i < V; i += NT) {
         const uint32_t key = fkey(z[i]);
         if ((key & mask) != prefix) continue;
@@ -375,21 +377,29 @@ __global__ void __launch_bounds__(1024) k_sample(const float* __restrict__ logit
     if (select && fkey(zi) < thr) return 0.f;
     return __builtin_amdgcn_exp2f((zi - zmax) * wscale);
   };
-  // 3. per-wave totals over the wave's contiguous range (fp32 weights,
-  // fp64 sums: per lane across steps, then a butterfly)
+  // 3. wave w owns the ids [w S, (w+1) S), S a multiple of 64, and lane l
+  // the block of 64 ids w S + 64 l .. +63 (S <= 4096 ids, one block per
+  // lane).  Each lane sums its block (fp32 weights, fp64 sum, in id
+  // order); a lane scan gives the blocks' running sums and the wave total.
   const int S = ((V + NW - 1) / NW + 63) / 64 * 64;
   const int w0 = wave * S, w1 = min(V, w0 + S);
-  double part = 0.0;
-  int last = -1;
-  for (int i = w0 + lane; i < w1; i += 64) {
-    part += (double)weight(i);
-    if (!select || fkey(z[i]) >= thr) last = i;
+  const int b0 = w0 + 64 * lane, b1 = min(w1, b0 + 64);
+  double bsum = 0.0;
+  int blast = -1;
+#pragma unroll 8
+  for (int i = b0; i < b1; ++i) {
+    bsum += (double)weight(i);
+    if (!select || fkey(z[i]) >= thr) blast = i;
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    part += __shfl_xor(part, o, 64);
-    last = max(last, __shfl_xor(last, o, 64));
+  double incl = bsum;
+  for (int o = 1; o < 64; o <<= 1) {
+    const double up = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += up;
   }
-  if (lane == 0) { wsum[wave] = part; wlast[wave] = last; }
+  int last = blast;
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (lane == 63) wsum[wave] = incl;
+  if (lane == 0) wlast[wave] = last;
   if (tid == 0) s_found = 0;
   __syncthreads();
   double total = 0.0, excl = 0.0;
@@ -398,24 +408,23 @@ __global__ void __launch_bounds__(1024) k_sample(const float* __restrict__ logit
     total += wsum[w];
   }
   const double target = (double)u[blockIdx.x] * total;
-  // 4. the wave whose range holds the target scans it, 64 ids per step
+  // 4. the wave whose range holds the target picks the block that crosses
+  // it, then scans that block's 64 ids
   if (excl <= target && target < excl + wsum[wave]) {
-    double run = excl;
-    int pick = wlast[wave];    // if rounding carries the scan past the target: the range's last kept id
-    for (int i0 = w0; i0 < w1; i0 += 64) {
-      const double wi = (double)weight(i0 + lane);
-      double incl = wi;
+    const unsigned long long cross = __ballot(bsum > 0.0 && excl + incl > target);
+    int pick = wlast[wave];    // if rounding leaves no crossing: the range's last kept id
+    if (cross) {
+      const int jb = __ffsll((long long)cross) - 1;          // the crossing block
+      const double before = excl + __shfl(incl - bsum, jb, 64);
+      const int i = w0 + 64 * jb + lane;
+      const double wi = i < w1 ? (double)weight(i) : 0.0;
+      double run = wi;
       for (int o = 1; o < 64; o <<= 1) {
-        const double up = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += up;
+        const double up = __shfl_up(run, o, 64);
+        if (lane >= o) run += up;
       }
-      const bool hit = wi > 0.0 && run + incl > target;
-      const unsigned long long bal = __ballot(hit);
-      if (bal) {
-        pick = i0 + __ffsll((long long)bal) - 1;
-        break;
-      }
-      run += __shfl(incl, 63, 64);
+      const unsigned long long hit = __ballot(wi > 0.0 && before + run > target);
+      pick = hit ? w0 + 64 * jb + __ffsll((long long)hit) - 1 : __shfl(blast, jb, 64);
     }
     if (lane == 0) {
       out[blockIdx.x] = pick;
@@ -435,8 +444,8 @@ __global__ void __launch_bounds__(1024) k_sample(const float* __restrict__ logit
 
 hipError_t sample(const float* logits, int n, int V, float temperature, int top_k, const float* u, int32_t* out,
                   hipStream_t s) {
-  // a thread's share of a row must fit the 8-bit digit counters
-  if (n < 1 || V < 1 || V > 1024 * 255 || top_k < 0 || !(temperature >= 0.f)) return hipErrorInvalidValue;
+  // one 64-id block per lane of the 16 waves
+  if (n < 1 || V < 1 || V > 65536 || top_k < 0 || !(temperature >= 0.f)) return hipErrorInvalidValue;
   k_sample<<<n, 1024, 0, s>>>(logits, V, temperature, top_k, u, out);
   return hipGetLastError();
 }

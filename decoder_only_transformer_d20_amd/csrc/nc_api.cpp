@@ -1074,7 +1074,7 @@ int nc_sample(const float* logits, int32_t n, int32_t V, float temperature, int3
               int32_t* out, void* hip_stream) {
   if (!logits || !u || !out) return NC_ERR_INVALID_ARG;
   if (!(temperature >= 0.f) || !std::isfinite(temperature) || top_k < 0) return NC_ERR_INVALID_ARG;
-  if (n < 1 || V < 1 || V > 1024 * 255) return NC_ERR_SHAPE;
+  if (n < 1 || V < 1 || V > 65536) return NC_ERR_SHAPE;
   return sample(logits, n, V, temperature, top_k, u, out, (hipStream_t)hip_stream) == hipSuccess ? NC_OK
                                                                                                    : NC_ERR_HIP;
 }

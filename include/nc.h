@@ -216,7 +216,7 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t ns
  * order).  u device fp32 [n] in [0, 1) are the caller's uniforms; out
  * device int32 [n].  No context: enqueued on hip_stream.
  * NC_ERR_INVALID_ARG on a negative temperature or top_k, NC_ERR_SHAPE on
- * n < 1, V < 1 or V > 261120. */
+ * n < 1, V < 1 or V > 65536. */
 int nc_sample(const float* logits, int32_t n, int32_t V, float temperature, int32_t top_k, const float* u,
               int32_t* out, void* hip_stream);
 
