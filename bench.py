@@ -3,6 +3,8 @@ one MI355X, through the C ABI (include/nc.h).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d20]
                     [--no-cpu-baseline] [--no-roofline] [--copy-calibration]
+                    [--mfma-calibration] [--optimizer] [--decode [--decode-nseq 1,8,16]]
+                    [--library-gemm]
 
 Prints one JSON line.  `value` is training tokens/s of the whole job with
 inputs already resident in HBM (host-to-device copies happen before timing);
@@ -17,11 +19,19 @@ algorithmic FLOPs per launch divided by its average launch time.
 WRITE_SIZE counters (calibrated against a plain device copy), reported only
 while the measured kernel's source is unchanged.
 
-`cpu_baseline`: the fp64 oracle (untuned) on a 512-token prefix of row 0 --
-forward, loss and backward -- on this host's cores.
+`cpu_baseline`: the fp64 oracle (untuned) on the first --cpu-sample-tokens
+(2048) tokens of row 0 -- forward, loss and backward -- on this host's cores.
+`optimizer_step`: one Muon + AdamW step over every parameter, timed
+separately (not part of `value`).
 
-`--copy-calibration` only runs a 1 GiB device-to-device copy (the reference
-kernel for scaling the FETCH_SIZE / WRITE_SIZE counters) and exits.
+Other modes print their own JSON line and exit:
+  --copy-calibration  a 1 GiB device-to-device copy (the reference kernel for
+                      scaling the FETCH_SIZE / WRITE_SIZE counters)
+  --mfma-calibration  the register-only MFMA loop's TFLOP/s
+  --optimizer         the optimiser step alone, with its two kernel families
+  --decode            KV-cache prefill + sampled decode, per batch size
+  --library-gemm      nc_op_matmul next to torch.matmul (the vendor BLAS) on
+                      the d20 product shapes
 """
 from __future__ import annotations
 
@@ -335,7 +345,7 @@ def measured_peaks(torch, nc, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

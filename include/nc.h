@@ -63,7 +63,7 @@ typedef enum {
   NC_ERR_WORKSPACE = -3,     /* workspace too small or misaligned */
   NC_ERR_STATE = -4,         /* call out of order (e.g. backward before forward) */
   NC_ERR_HIP = -5,           /* a HIP call or kernel launch failed; see nc_last_error */
-  NC_ERR_UNSUPPORTED = -6    /* valid but not supported by this build */
+  NC_ERR_UNSUPPORTED = -6    /* valid but not supported by this library */
 } nc_status;
 
 typedef enum { NC_DTYPE_F32 = 0, NC_DTYPE_BF16 = 1 } nc_dtype;
