@@ -37,6 +37,24 @@ int nc_op_matmul(int32_t dtype, int32_t p_trans, int32_t q_trans, int64_t M, int
                  const void* P, const void* Q, void* C, int32_t out_f32, int32_t splits, float* part,
                  int32_t portable, void* hip_stream);
 
+/* Batched matrix products with the linear-combination epilogue, the form
+ * Muon's Newton-Schulz iteration runs in (section Pretraining, optimiser
+ * paragraph): for b < batch,
+ *   C_b[m][n] = alpha * sum_k P_b[m][k] Q_b[n][k] + gamma * aux_b[m][n]
+ * (aux = NULL: C_b = the plain product, alpha and gamma unused), all in the
+ * dtype T, accumulation fp32, one rounding at the store.
+ *   P_b = P + b sP   T [M][K]
+ *   Q_b = Q + b sQ   T [N][K], or [K][N] when q_trans = 1
+ *   C_b = C + b sC, aux_b = aux + b sAux   T [M][N]   (aux may not alias C)
+ * Strides in elements, >= 0 and multiples of 8 (NC_ERR_INVALID_ARG
+ * otherwise).  M, N, K multiples of 64 (NC_ERR_SHAPE); the matrix-core path
+ * (portable = 0, bf16) also needs M, N multiples of 128 and returns
+ * NC_ERR_UNSUPPORTED otherwise.  fp32 always takes the portable kernel. */
+int nc_op_matmul_batched(int32_t dtype, int32_t q_trans, int32_t batch, int64_t M, int64_t N, int64_t K,
+                         const void* P, int64_t sP, const void* Q, int64_t sQ, void* C, int64_t sC,
+                         const void* aux, int64_t sAux, float alpha, float gamma, int32_t portable,
+                         void* hip_stream);
+
 /* Parameter-free RMSNorm (section Pretraining: no RMSNorm parameters):
  * y = x / sqrt(mean(x^2) + eps) per row; r = the per-row factor (fp32).
  *   x, y T [rows][d];  r fp32 [rows]. */

@@ -87,6 +87,53 @@ def test_matmul_split_k_exact(dtype, portable, K, S):
     np.testing.assert_array_equal(host(C), want)
 
 
+@pytest.mark.parametrize("dtype,portable", [("f32", 1), ("bf16", 1), ("bf16", 0)])
+@pytest.mark.parametrize("qt,batch,M,N,K", [(0, 3, 256, 256, 384), (1, 5, 128, 384, 256), (0, 80, 256, 256, 256),
+                                             (1, 2, 512, 1280, 256)])
+def test_matmul_batched_axpby_exact(dtype, portable, qt, batch, M, N, K):
+    """Batched products (items at uneven strides) with and without the
+    alpha acc + gamma aux epilogue, exact on small integers with alpha,
+    gamma powers of two: every product, sum and scaling is exact, so the
+    stored result is the rounding of the exact value."""
+    rng = np.random.default_rng(200 + batch + qt)
+    pad = 64                                          # items not packed back to back
+    P = _ints(rng, (batch, M * K + pad))
+    Q = _ints(rng, (batch, N * K + pad))
+    A = _ints(rng, (batch, M * N + pad))
+    Pd, Qd, Ad = dev(P, dtype), dev(Q, dtype), dev(A, dtype)
+    for alpha, gamma, with_aux in ((1.0, 0.0, False), (2.0, -0.5, True), (-4.0, 0.25, True)):
+        C = empty((batch, M * N + pad), dtype)
+        nc.ops.matmul_batched(DT[dtype], qt, batch, M, N, K, Pd, M * K + pad, Qd, N * K + pad, C, M * N + pad,
+                              Ad if with_aux else None, M * N + pad, alpha, gamma, portable, None)
+        _sync()
+        got = host(C, dtype)
+        for b in range(batch):
+            Pb = P[b, :M * K].reshape(M, K).astype(np.int64)
+            Qb = Q[b, :N * K].astype(np.int64)
+            Qb = Qb.reshape(K, N).T if qt else Qb.reshape(N, K)
+            want = (Pb @ Qb.T).astype(np.float64)
+            if with_aux:
+                want = alpha * want + gamma * A[b, :M * N].reshape(M, N)
+            want = want.astype(np.float32)
+            if dtype == "bf16":
+                want = synthdata.round_to_bf16(want)
+            np.testing.assert_array_equal(got[b, :M * N].reshape(M, N), want, err_msg=f"item {b}")
+
+
+def test_matmul_batched_rejects():
+    P = dev(np.zeros(2 * 192 * 128, np.float32), "bf16")
+    C = empty((2 * 192 * 192,), "bf16")
+    cases = (((1, 0, 2, 192, 192, 128, P, 192 * 128, P, 192 * 128, C, 192 * 192, None, 0, 1.0, 0.0, 0), -6),
+             ((1, 0, 2, 128, 128, 128, P, 128 * 128 + 4, P, 0, C, 0, None, 0, 1.0, 0.0, 1), -1),
+             ((1, 2, 2, 128, 128, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 1), -1),
+             ((1, 0, 0, 128, 128, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 1), -1),
+             ((1, 0, 2, 128, 100, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 1), -2))
+    for args, status in cases:
+        with pytest.raises(nc.NcError) as e:
+            nc.ops.matmul_batched(*args, None)
+        assert e.value.status == status, (args[1:6], e.value.status)
+
+
 def test_matmul_full_size_sampled_rows():
     """The d20 QKV product at its real shape (65,536 x 3,840 x 1,280), checked
     exactly on sampled rows."""
