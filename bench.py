@@ -54,7 +54,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 # Keyed by family; valid only for the recorded hash of the kernel source.
 TRAFFIC = {
     # profiles/d20_step_hbm_traffic.md: 1.592 GB fetched + 0.134 GB written per dispatch
-    "gemm_wgrad": {"bytes_per_launch": 1725662492, "source_hash": "ed4a60b4df1bd9a2"},
+    "gemm_wgrad": {"bytes_per_launch": 1725695338, "source_hash": "da1023a2448e18c3"},
 }
 
 

@@ -86,6 +86,7 @@ _SIGS = {
     "nc_destroy": (None, [_P]),
     "nc_last_error": (ctypes.c_char_p, [_P]),
     "nc_forward": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "nc_forward_eval": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "nc_loss_bpb": (ctypes.c_int, [_P, _P, _P]),
     "nc_backward": (ctypes.c_int, [_P, _P, _P, _I32]),
     "nc_block_forward": (ctypes.c_int, [_P, _P, _P, _P]),
@@ -244,6 +245,11 @@ class Context:
 
     def forward(self, params, idx, targets, ce_out=None):
         _check(lib().nc_forward(self.h, _ptr(params), _ptr(idx), _ptr(targets), _ptr(ce_out)), "nc_forward", self.h)
+
+    def forward_eval(self, params, idx, targets, ce_out=None):
+        """nc_forward_eval: the forward for evaluation (no logits kept)."""
+        _check(lib().nc_forward_eval(self.h, _ptr(params), _ptr(idx), _ptr(targets), _ptr(ce_out)),
+               "nc_forward_eval", self.h)
 
     def loss_bpb(self, token_bytes, out):
         _check(lib().nc_loss_bpb(self.h, _ptr(token_bytes), _ptr(out)), "nc_loss_bpb", self.h)

@@ -262,6 +262,12 @@ __device__ inline void epi_store4(const GemmDesc& g, const GemmTile& c, int64_t 
     for (int e = 0; e < 4; ++e)
       x[e] = (__builtin_amdgcn_exp2f(x[e] * kLog2e - dz_l) - ((n + e) == dz_t ? 1.f : 0.f)) * dz_s;
   }
+  if constexpr (EPI == EPI_LSEZ) {
+    // logits relative to the tile's row maximum (dz_l): entries with a
+    // non-negligible probability sit close to it, where bf16 is finest
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] -= dz_l;
+  }
   // Non-temporal stores keep the streamed-out product from displacing the
   // operand panels in the caches (measured: 1-2 % on most products).  The
   // 2 sqrt(u) gradient, whose aux input streams in beside it, measured
@@ -278,7 +284,8 @@ __device__ inline void epi_store4(const GemmDesc& g, const GemmTile& c, int64_t 
 // Per-row (max, sum exp) of a tile's logits from the WGN column groups
 // (red [WGN][BM], written by the waves), combined by the first BM threads.
 template <int WGN, int BM>
-__device__ inline void lse_combine(const GemmDesc& g, const GemmTile& c, const float2* red, int etid) {
+__device__ inline void lse_combine(const GemmDesc& g, const GemmTile& c, const float2* red, int etid,
+                                   float* row_max) {
   if (etid < BM) {
     float2 p[WGN];
     float M = -INFINITY;
@@ -291,6 +298,7 @@ __device__ inline void lse_combine(const GemmDesc& g, const GemmTile& c, const f
 #pragma unroll
     for (int w = 0; w < WGN; ++w) S += p[w].y * __builtin_amdgcn_exp2f((p[w].x - M) * kLog2e);
     g.lse_part[(c.m0 + etid) * g.lse_stride + c.tn] = make_float2(M, S);
+    if (row_max) row_max[etid] = M;
   }
 }
 
@@ -310,6 +318,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 fragments per wave
   constexpr int STAGE = (BM + BN) * 128;         // bytes per LDS stage
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  __shared__ float zrow_max[EPI == EPI_LSEZ ? BM : 1];      // the tile's row maxima (EPI_LSEZ)
 
   const int tid = threadIdx.x;
   // the wave index as a scalar: wave-role branches are uniform
@@ -511,7 +520,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
     // ---------------------------------------------------------------- epilogue
     // lane holds row m = m0 + wm*WTM + i*32 + (lane&31) and, for register
     // group q (4 regs), columns n = n0 + wn*WTN + j*32 + 8q + 4*(lane>>5) + 0..3
-    if constexpr (EPI == EPI_LSE) {
+    if constexpr (EPI == EPI_LSE || EPI == EPI_LSEZ) {
       const int64_t nw = c.n0 + wn * WTN + 4 * (elane >> 5);
       float2* red = reinterpret_cast<float2*>(smem);      // [4 wn][BM]
 #pragma unroll
@@ -541,9 +550,17 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
             if (t == nw + j * 32 + 8 * (r >> 2) + (r & 3)) g.ztgt[m] = acc[i][j][r];
       }
       __syncthreads();
-      prefetch_next();
-      lse_combine<WGN, BM>(g, c, red, etid);
-    } else {
+      if constexpr (EPI == EPI_LSE) {
+        prefetch_next();
+        lse_combine<WGN, BM>(g, c, red, etid, nullptr);
+      } else {
+        // the logits themselves follow through the row-order store below,
+        // once the maxima are in LDS and the partials read
+        lse_combine<WGN, BM>(g, c, red, etid, zrow_max);
+        __syncthreads();
+      }
+    }
+    if constexpr (EPI != EPI_LSE) {
       // Two passes, one per half of the tile's rows (the waves with wm = h
       // own rows h*WTM ..): those waves write their fp32 accumulators to
       // LDS as [WTM][BN] (16-byte chunk cc of row r at slot cc ^ (r & 15), so
@@ -622,9 +639,14 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
           float x[4] = {f.x, f.y, f.z, f.w};
           const uint2 y = pa[k % W];
           const float4 cs = pc[k % W];
-          const int dz_t = pt[k % W];
-          const float dz_l = pl[k % W] * kLog2e;
-          const float dz_s = ps[k % W];
+          int dz_t = 0;
+          float dz_l = 0.f, dz_s = 0.f;
+          if constexpr (EPI == EPI_DZ) {
+            dz_t = pt[k % W];
+            dz_l = pl[k % W] * kLog2e;
+            dz_s = ps[k % W];
+          }
+          if constexpr (EPI == EPI_LSEZ) dz_l = zrow_max[h * WTM + r];
           if (k + W < NR) fetch(k + W);
           epi_store4<EPI>(g, c, m, n, x, y, cs, rot, dz_t, dz_l, dz_s);
         }
@@ -680,6 +702,7 @@ hipError_t launch(const GemmDesc& g, hipStream_t s) {
   X(0, 0, EPI_RELU2)          \
   X(0, 0, EPI_DRELU2)         \
   X(0, 0, EPI_LSE)            \
+  X(0, 0, EPI_LSEZ)           \
   X(0, 0, EPI_DZ)             \
   X(0, 0, EPI_F32)            \
   X(0, 0, EPI_AXPBY)          \

@@ -460,6 +460,52 @@ __global__ void __launch_bounds__(256) k_ce_combine(const float2* __restrict__ p
   }
 }
 
+// ---------------------------------------------------------------------------
+// dz from the kept logits: z holds each logit minus the maximum of its row in
+// its tile of tile_w columns (part[row][tile].x), so z + max - lse is the log
+// of the softmax probability.  dz = (p - [n == tgt]) * rs; the target column
+// takes p from the fp32 target logit.  A block covers 512
+// 16-byte vectors of one row (bpr blocks per row).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) k_dz_from_logits(const T* __restrict__ z, T* __restrict__ dz, int V,
+                                                         int bpr, int tile_w,
+                                                         const float2* __restrict__ part, int nblk,
+                                                         const float* __restrict__ ztgt,
+                                                         const int32_t* __restrict__ tgt,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ rs) {
+  constexpr int VN = Vec<T>::n;
+  constexpr float kLog2e = 1.4426950408889634f;
+  const int64_t row = blockIdx.x / bpr;
+  const int cpr = V / VN;
+  const int j0 = (int)(blockIdx.x % bpr) * 512 + (int)threadIdx.x;
+  const float l = lse[row], sc = rs[row];
+  const int t = tgt[row];
+  const float pt = __builtin_amdgcn_exp2f((ztgt[row] - l) * kLog2e) - 1.f;   // used only where n = t
+  const T* zr = z + row * V;
+  T* dr = dz + row * V;
+  Vec<T> v[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (j0 + 256 * u < cpr) v[u] = ld16(zr + (int64_t)(j0 + 256 * u) * VN);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = j0 + 256 * u;
+    if (j >= cpr) continue;
+    const int n = j * VN;
+    const float base = (part[row * nblk + n / tile_w].x - l) * kLog2e;
+    Vec<T> o;
+#pragma unroll
+    for (int e = 0; e < VN; ++e) {
+      float p = __builtin_amdgcn_exp2f(fmaf(to_f32(v[u].v[e]), kLog2e, base));
+      if (n + e == t) p = pt;
+      o.v[e] = from_f32<T>(p * sc);
+    }
+    st16(dr + n, o);
+  }
+}
+
 // one block: number of valid targets -> 1/n (0 when none)
 __global__ void __launch_bounds__(1024) k_count_valid(const int32_t* __restrict__ tgt, int64_t n, float* inv) {
   __shared__ int64_t red[1024];
@@ -735,6 +781,10 @@ template hipError_t rmsnorm_fwd<float>(const float*, float*, float*, int64_t, in
 template hipError_t rmsnorm_fwd<bf16>(const bf16*, bf16*, float*, int64_t, int, float, hipStream_t);
 template hipError_t rmsnorm_bwd<float>(const float*, const float*, const float*, float*, int64_t, int, int, hipStream_t);
 template hipError_t rmsnorm_bwd<bf16>(const bf16*, const float*, const bf16*, bf16*, int64_t, int, int, hipStream_t);
+template hipError_t dz_from_logits<float>(const float*, float*, int64_t, int, int, const float2*, int, const float*,
+                                          const int32_t*, const float*, const float*, hipStream_t);
+template hipError_t dz_from_logits<bf16>(const bf16*, bf16*, int64_t, int, int, const float2*, int, const float*,
+                                         const int32_t*, const float*, const float*, hipStream_t);
 template hipError_t attn_delta<float>(const AttnDesc&, hipStream_t);
 template hipError_t attn_delta<bf16>(const AttnDesc&, hipStream_t);
 
@@ -749,6 +799,18 @@ hipError_t rope_table_at(float2* tab, int t0, int T, int Q, float base, hipStrea
 hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int32_t* tgt, float* lse, float* ce,
                       int64_t rows, hipStream_t s) {
   k_ce_combine<<<nblocks(rows, 4), 256, 0, s>>>(part, nblk, ztgt, tgt, lse, ce, rows);
+  return hipGetLastError();
+}
+template <typename T>
+hipError_t dz_from_logits(const T* z, T* dz, int64_t rows, int V, int tile_w, const float2* part, int nblk,
+                          const float* ztgt, const int32_t* tgt, const float* lse, const float* rs, hipStream_t s) {
+  constexpr int VN = Vec<T>::n;
+  if (rows <= 0 || V <= 0 || V % VN || tile_w <= 0 || tile_w % VN || V % tile_w || V / tile_w != nblk)
+    return hipErrorInvalidValue;
+  const int bpr = (V / VN + 511) / 512;
+  if (rows * bpr > INT32_MAX) return hipErrorInvalidValue;
+  k_dz_from_logits<T><<<(unsigned)(rows * bpr), 256, 0, s>>>(z, dz, V, bpr, tile_w, part, nblk, ztgt, tgt, lse,
+                                                              rs);
   return hipGetLastError();
 }
 hipError_t count_valid(const int32_t* tgt, int64_t n, float* inv, hipStream_t s) {

@@ -56,8 +56,10 @@ __global__ void __launch_bounds__(256) k_gemm_portable(GemmDesc g) {
     __syncthreads();
   }
 
-  if (g.epi == EPI_LSE) {
-    // per-row max and sum of exp over this 64-column tile, plus the target logit
+  if (g.epi == EPI_LSE || g.epi == EPI_LSEZ) {
+    // per-row max and sum of exp over this 64-column tile, plus the target
+    // logit; EPI_LSEZ also stores the logits relative to the row max
+    __shared__ float rmax[BM];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -72,6 +74,14 @@ __global__ void __launch_bounds__(256) k_gemm_portable(GemmDesc g) {
       g.lse_part[m * g.lse_stride + blockIdx.x] = make_float2(mx, s);
       const int t = g.tgt[m];
       if (t >= n0 && t < n0 + BN) g.ztgt[m] = Cs[tid][t - n0];
+      rmax[tid] = mx;
+    }
+    if (g.epi == EPI_LSEZ) {
+      __syncthreads();
+      for (int e = tid; e < BM * BN; e += 256) {
+        const int r = e / BN, cl = e % BN;
+        ((T*)g.C)[(m0 + r) * g.ldc + n0 + cl] = from_f32<T>(Cs[r][cl] - rmax[r]);
+      }
     }
     return;
   }

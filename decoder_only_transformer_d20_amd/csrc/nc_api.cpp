@@ -92,7 +92,8 @@ int choose_splits(const nc_config& c, int M, int N, int64_t K) {
 struct Plan {
   size_t total = 0;
   size_t rope = 0, idx = 0, tgt = 0, x = 0, xf = 0, rf = 0, ce = 0, lse_head = 0, ztgt = 0, lse_part = 0, rowscale = 0;
-  size_t scalars = 0, dz = 0, g = 0, gtmp = 0, big = 0, part = 0, delta = 0, wt = 0, embs = 0;
+  bool keep_logits = false;   // zkeep is laid out (the head's backward runs as one chunk)
+  size_t scalars = 0, dz = 0, zkeep = 0, g = 0, gtmp = 0, big = 0, part = 0, delta = 0, wt = 0, embs = 0;
   size_t layer0 = 0, layer_stride = 0;
   size_t l_a = 0, l_r1 = 0, l_qkv = 0, l_o = 0, l_lse = 0, l_m = 0, l_r2 = 0, l_u = 0;
   int head_nblk = 0;
@@ -142,6 +143,9 @@ Plan make_plan(const nc_config& c) {
     const int64_t rows = std::max<int64_t>(1, std::min<int64_t>(c.batch, 65536 / c.seq_len));
     p.head_chunk = rows * c.seq_len;
     p.dz = take((size_t)p.head_chunk * V * es);
+    // the forward's logits, kept for the backward when it is one chunk
+    p.keep_logits = p.head_chunk >= N;
+    if (p.keep_logits) p.zkeep = take((size_t)N * V * es);
     p.embs = take((size_t)embed_bwd_scratch_bytes(N, (int)d));
     need((int)V, (int)d, p.head_chunk);
   }
@@ -174,6 +178,7 @@ struct nc_ctx {
   Plan plan;
   bool have_forward = false;
   bool have_block_forward = false;
+  bool logits_kept = false;        // plan.zkeep holds the last forward's logits
   std::string err;
   // kernel timing (nc_trace_*)
   int trace_family = -1;
@@ -210,7 +215,8 @@ int gemm_family(const GemmDesc& g) {
     case EPI_RESID: return key == 0 ? NC_TRACE_GEMM_RESIDUAL : -1;
     case EPI_RELU2: return key == 0 ? NC_TRACE_GEMM_RELU2 : -1;
     case EPI_STORE: return key <= 1 ? NC_TRACE_GEMM_DGRAD : -1;
-    case EPI_LSE: return key == 0 ? NC_TRACE_GEMM_HEAD_LSE : -1;
+    case EPI_LSE:
+    case EPI_LSEZ: return key == 0 ? NC_TRACE_GEMM_HEAD_LSE : -1;
     case EPI_DZ: return key == 0 ? NC_TRACE_GEMM_HEAD_DZ : -1;
     case EPI_DRELU2: return key <= 1 ? NC_TRACE_GEMM_DGRAD_RELU2 : -1;
     case EPI_F32: return key == 3 ? NC_TRACE_GEMM_WGRAD : -1;
@@ -225,6 +231,7 @@ double gemm_bytes(const GemmDesc& g, size_t es) {
   switch (g.epi) {
     case EPI_F32: b += M * N * 4.0 * (g.beta ? 2 : 1); break;
     case EPI_LSE: b += M * 4.0 * 2; break;                       // targets in, z[target] out
+    case EPI_LSEZ: b += M * 4.0 * 2 + M * N * es; break;         // and the logits out
     case EPI_DZ: b += M * N * es + M * 8.0; break;
     case EPI_RESID:
     case EPI_DRELU2:
@@ -428,7 +435,9 @@ int layer_backward(nc_ctx* ctx, int l, const T* w, T* gr, float* dw, int accumul
 }
 
 template <typename T>
-int model_forward(nc_ctx* ctx, const T* params, const int32_t* idx, const int32_t* tgt, float* ce_out) {
+int model_forward(nc_ctx* ctx, const T* params, const int32_t* idx, const int32_t* tgt, float* ce_out,
+                  bool keep_logits = true) {
+  ctx->logits_kept = false;
   const nc_config& c = ctx->cfg;
   const Plan& p = ctx->plan;
   const int N = c.batch * c.seq_len, d = c.d_model, V = c.vocab;
@@ -449,10 +458,16 @@ int model_forward(nc_ctx* ctx, const T* params, const int32_t* idx, const int32_
   float* rf = ctx->at<float>(p.rf);
   NC_TRY(rmsnorm_fwd<T>(x, xf, rf, N, d, c.rms_eps, s), "final rmsnorm");
   const T* U = w + (int64_t)c.n_layer * layer_elems(c);
-  GemmDesc g = gemm(N, V, d, xf, d, 0, U, d, 0, EPI_LSE, nullptr, 0);
+  // When the head's backward runs as one chunk, the product keeps the
+  // logits (relative to their tile's row maximum) and the backward forms dz
+  // from them instead of recomputing the product.
+  const bool keep_z = keep_logits && p.keep_logits;
+  GemmDesc g = gemm(N, V, d, xf, d, 0, U, d, 0, keep_z ? EPI_LSEZ : EPI_LSE, keep_z ? ctx->at<T>(p.zkeep) : nullptr,
+                    keep_z ? V : 0);
   g.tgt = wtgt; g.lse_part = ctx->at<float2>(p.lse_part); g.lse_stride = p.head_nblk;
   g.ztgt = ctx->at<float>(p.ztgt);
   NC_TRY(run_gemm(ctx, g), "unembedding + log-sum-exp partials");
+  ctx->logits_kept = keep_z;
   float* ce = ctx->at<float>(p.ce);
   NC_TRY(ce_combine(g.lse_part, p.head_nblk, g.ztgt, wtgt, ctx->at<float>(p.lse_head), ce, N, s), "cross-entropy");
   if (ce_out) NC_TRY(copy_bytes(ce_out, ce, (size_t)N * 4, s), "copy ce");
@@ -482,11 +497,24 @@ int model_backward(nc_ctx* ctx, const T* params, float* grads, int accumulate, c
   NC_TRY(row_scale(wtgt, tok_w, ctx->at<float>(p.scalars), N, rs, s), "dz row factors");
   GemmDesc gx;
   NC_TRY(dgrad_desc<T>(ctx, 0, dz, V, U, V, d, EPI_STORE, tmp, d, &gx), "transpose U");
+  const bool kept_z = ctx->logits_kept;          // then the head runs as one chunk
   for (int64_t r0 = 0; r0 < N; r0 += p.head_chunk) {
     const int Mc = (int)std::min<int64_t>(p.head_chunk, N - r0);
-    GemmDesc g = gemm(Mc, V, d, xf + r0 * d, d, 0, U, d, 0, EPI_DZ, dz, V);
-    g.tgt = wtgt + r0; g.lse = ctx->at<float>(p.lse_head) + r0; g.row_scale = rs + r0;
-    NC_TRY(run_gemm(ctx, g), "recompute logits -> dz");
+    GemmDesc g;
+    if (kept_z) {
+      const double nz = (double)N * V;
+      NC_TRY(traced(ctx, NC_TRACE_GEMM_HEAD_DZ, 4.0 * nz, 2.0 * nz * sizeof(T),
+                    [&] {
+                      return dz_from_logits<T>(ctx->at<T>(p.zkeep), dz, N, V, V / p.head_nblk,
+                                               ctx->at<float2>(p.lse_part), p.head_nblk, ctx->at<float>(p.ztgt),
+                                               wtgt, ctx->at<float>(p.lse_head), rs, s);
+                    }),
+             "dz from the kept logits");
+    } else {
+      g = gemm(Mc, V, d, xf + r0 * d, d, 0, U, d, 0, EPI_DZ, dz, V);
+      g.tgt = wtgt + r0; g.lse = ctx->at<float>(p.lse_head) + r0; g.row_scale = rs + r0;
+      NC_TRY(run_gemm(ctx, g), "recompute logits -> dz");
+    }
     gx.M = Mc;
     gx.C = tmp + r0 * d;
     NC_TRY(run_gemm(ctx, gx), "dxf = dz U");
@@ -752,7 +780,7 @@ int prefill(nc_ctx* ctx, const T* params, const int32_t* idx, int len, int nseq,
   const int d = c.d_model, V = c.vocab;
   // the whole forward over the (padded) prompt; its targets are the ids
   // themselves, since only the saved k, v and the final norm are used
-  int st = model_forward<T>(ctx, params, idx, idx, nullptr);
+  int st = model_forward<T>(ctx, params, idx, idx, nullptr, false);
   if (st != NC_OK) return st;
   ctx->have_forward = true;
   const int64_t sstride = (int64_t)ml * d, lstride = 2 * (int64_t)mb * sstride;
@@ -953,6 +981,16 @@ int nc_forward(nc_ctx* ctx, const void* params, const int32_t* idx, const int32_
   ctx->have_forward = false;
   int st = is_bf16(ctx->cfg) ? model_forward<bf16>(ctx, (const bf16*)params, idx, targets, ce_out)
                              : model_forward<float>(ctx, (const float*)params, idx, targets, ce_out);
+  ctx->have_forward = st == NC_OK;
+  return st;
+}
+
+int nc_forward_eval(nc_ctx* ctx, const void* params, const int32_t* idx, const int32_t* targets, float* ce_out) {
+  if (!ctx || !params || !idx || !targets) return NC_ERR_INVALID_ARG;
+  if (is_block(ctx->cfg)) return NC_ERR_STATE;
+  ctx->have_forward = false;
+  int st = is_bf16(ctx->cfg) ? model_forward<bf16>(ctx, (const bf16*)params, idx, targets, ce_out, false)
+                             : model_forward<float>(ctx, (const float*)params, idx, targets, ce_out, false);
   ctx->have_forward = st == NC_OK;
   return st;
 }

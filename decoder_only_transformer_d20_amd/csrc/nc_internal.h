@@ -48,6 +48,8 @@ enum Epi {
   EPI_DZ = 6,        // C(T) = (exp(acc - lse[m]) - [n == tgt[m]]) * inv_nvalid
   EPI_RELU2 = 7,     // C(T) = relu(acc)^2
   EPI_AXPBY = 8,     // C(T) = ep_alpha * acc + ep_gamma * aux(T)   (aux may not alias C)
+  EPI_LSEZ = 9,      // EPI_LSE, and C(T) = acc - (row max of the N-tile): the logits kept
+                     // for the backward, relative to their tile's maximum (lse_part[.].x)
 };
 
 struct GemmDesc {
@@ -129,6 +131,13 @@ hipError_t rope_table(float2* tab, int T, int Q, float base, hipStream_t s);
 hipError_t rope_table_at(float2* tab, int t0, int T, int Q, float base, hipStream_t s);
 hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int32_t* tgt,
                       float* lse, float* ce, int64_t rows, hipStream_t s);
+// dz [rows][V] = (softmax(z) - onehot(tgt)) * rs from z [rows][V] written by
+// an EPI_LSEZ product (z relative to its tile's row max, the tile width
+// tile_w and per-tile maxima from part [rows][nblk]); the target column is
+// formed from the fp32 target logit ztgt
+template <typename T>
+hipError_t dz_from_logits(const T* z, T* dz, int64_t rows, int V, int tile_w, const float2* part, int nblk,
+                          const float* ztgt, const int32_t* tgt, const float* lse, const float* rs, hipStream_t s);
 hipError_t count_valid(const int32_t* tgt, int64_t n, float* inv_nvalid, hipStream_t s);
 // out[i] = tgt[i] >= 0 ? *inv_nvalid * (w ? w[i] : 1) : 0
 hipError_t row_scale(const int32_t* tgt, const float* w, const float* inv_nvalid, int64_t n, float* out,

@@ -144,6 +144,15 @@ const char* nc_last_error(const nc_ctx* ctx);
 int nc_forward(nc_ctx* ctx, const void* params, const int32_t* idx,
                const int32_t* targets, float* ce_out);
 
+/* nc_forward for evaluation (validation loss and bits per byte, section
+ * Pretraining's bpb evaluation): the same results, bit for bit, without the
+ * bf16 copy of the logits that nc_forward keeps in the workspace for the
+ * backward when the batch is at most 65,536 tokens (writing it costs about
+ * 2 % of a d20 training step).  A backward after it is still valid and
+ * recomputes the unembedding product instead. */
+int nc_forward_eval(nc_ctx* ctx, const void* params, const int32_t* idx,
+                    const int32_t* targets, float* ce_out);
+
 /* Loss and bits per byte of the last nc_forward.
  *   token_bytes device int32 [V], UTF-8 bytes of each vocabulary id
  *   out         device double [5]: mean ce in nats, bits per byte,
@@ -307,8 +316,12 @@ enum {
   NC_TRACE_GEMM_QKV_ROPE = 0, /* a Wqkv^T with the rotary epilogue           */
   NC_TRACE_GEMM_RESIDUAL,     /* x + o Wo^T and x + u W2^T                    */
   NC_TRACE_GEMM_RELU2,        /* u = relu(m W1^T)^2                           */
-  NC_TRACE_GEMM_HEAD_LSE,     /* xf U^T with the log-sum-exp epilogue         */
-  NC_TRACE_GEMM_HEAD_DZ,      /* xf U^T recomputed, softmax - onehot          */
+  NC_TRACE_GEMM_HEAD_LSE,     /* xf U^T with the log-sum-exp epilogue (which
+                                 also keeps the logits when the head's
+                                 backward runs as one token chunk)            */
+  NC_TRACE_GEMM_HEAD_DZ,      /* dz = softmax - onehot: from the kept logits
+                                 (an elementwise kernel, flops = 4 per logit),
+                                 else xf U^T recomputed                       */
   NC_TRACE_GEMM_DGRAD,        /* activation gradients g W (dm, do, da, dxf)   */
   NC_TRACE_GEMM_DGRAD_RELU2,  /* dh = (g W2) * 2 relu(h)                      */
   NC_TRACE_GEMM_WGRAD,        /* weight gradients dWqkv, dWo, dW1, dW2, dU    */

@@ -186,6 +186,49 @@ def test_unit_weights_equal_plain_backward():
     assert out[0] == pytest.approx(plain["out"][2], rel=1e-12) and out[1] == pytest.approx(plain["out"][0], rel=1e-12)
 
 
+def test_head_in_two_chunks_matches_one_row():
+    """More than 65,536 tokens: the head's backward runs in two token chunks
+    and recomputes the logits (no kept copy).  33 rows x 2048 with every
+    token weight 0 except row 32's (weight 33, so its dz rows carry the same
+    factor 1/2048 as an unweighted single row): the gradient must equal the
+    single-row step's, which keeps its logits.  Row 32 lies in the second
+    chunk.  The two runs differ in product shapes (tiles, split-K) and in how
+    dz is formed, so the bar is cosine >= 0.9999 per tensor."""
+    base = synthdata.get_config("small")
+    cfg = base.with_(batch=33, seq_len=2048)
+    params = _params(cfg)
+    idx, tgt = synthdata.make_tokens(cfg)
+    w = np.zeros(tgt.shape, dtype=np.float32)
+    w[32] = 33.0
+    out_big, g_big = _gpu_weighted(cfg, params, idx, tgt, w)
+    one = cfg.with_(batch=1)
+    out_one, g_one = _gpu_weighted(one, params, idx[32:33], tgt[32:33], np.ones((1, 2048), dtype=np.float32))
+    assert out_big[0] == pytest.approx(33.0 * out_one[0], rel=1e-3)
+    for (name, layer, a), (_, _, b) in zip(flat_tensors(cfg, g_big), flat_tensors(cfg, g_one)):
+        assert cosine(a, b) >= 0.9999, (name, layer, cosine(a, b))
+
+
+def test_forward_eval_same_results_and_backward_recomputes():
+    """nc_forward_eval gives nc_forward's ce and loss bit for bit; a backward
+    after it recomputes the logits instead of reading a kept copy, and its
+    gradient matches the one after nc_forward to the bf16 bar."""
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("small"), ignore=[(1, 7)])
+    sess = nc.Session(cfg)
+    P, I, Tg, TB = dev(params, cfg.dtype), dev(idx.ravel()), dev(tgt.ravel()), dev(tb)
+    res = []
+    for fwd in (sess.forward, sess.forward_eval):
+        ce, out, g = empty((idx.size,), "f32"), empty((5,), "f64"), empty((params.size,), "f32")
+        fwd(P, I, Tg, ce)
+        sess.loss_bpb(TB, out)
+        sess.backward(P, g)
+        torch.cuda.synchronize()
+        res.append((host(ce), host(out), host(g)))
+    np.testing.assert_array_equal(res[0][0], res[1][0])
+    np.testing.assert_array_equal(res[0][1], res[1][1])
+    for (name, layer, a), (_, _, b) in zip(flat_tensors(cfg, res[0][2]), flat_tensors(cfg, res[1][2])):
+        assert cosine(a, b) >= 0.9999, (name, layer, cosine(a, b))
+
+
 def test_small_bf16_deterministic():
     cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("small"))
     a = _gpu_step(cfg, params, idx, tgt, tb)

@@ -98,6 +98,7 @@ def test_init_checks_before_any_hip_call():
 def test_calls_on_null_context_rejected():
     L = nc.lib()
     assert L.nc_forward(None, 1, 1, 1, None) == -1
+    assert L.nc_forward_eval(None, 1, 1, 1, None) == -1
     assert L.nc_backward(None, 1, 1, 0) == -1
     assert L.nc_loss_bpb(None, 1, 1) == -1
     assert L.nc_block_forward(None, 1, 1, 2) == -1
