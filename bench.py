@@ -274,6 +274,8 @@ def decode_timing(torch, nc, cfg, nseqs=(1, 8, 16), prompt=512, steps=128):
         logits = torch.empty(nseq, V, dtype=torch.float32, device="cuda")
         u = torch.rand(steps + 1, nseq, device="cuda", generator=g)
         tok = torch.empty(steps + 1, nseq, dtype=torch.int32, device="cuda")
+        sscr = torch.empty(nc.sample_scratch_bytes(nseq, V) + 256, dtype=torch.uint8, device="cuda")
+        ssp = (sscr.data_ptr() + 255) // 256 * 256
         # warm-up pass (also the first run of every kernel)
         sess.prefill(P, idx, prompt, nseq, kv, nseq, ml, logits)
         sess.decode(P, idx[:nseq], nseq, prompt, kv, nseq, ml, sp, logits)
@@ -281,13 +283,13 @@ def decode_timing(torch, nc, cfg, nseqs=(1, 8, 16), prompt=512, steps=128):
         ev[0].record(stream)
         sess.prefill(P, idx, prompt, nseq, kv, nseq, ml, logits)
         ev[1].record(stream)
-        nc.sample(logits, 1, V, 1.0, 50, u[0], tok[0], stream.cuda_stream)
+        nc.sample_parallel(logits, 1, V, 1.0, 50, u[0], tok[0], ssp, stream.cuda_stream)
         if nseq > 1:
             tok[0].copy_(tok[0, :1].expand(nseq))
         ev[2].record(stream)
         for i in range(steps):
             sess.decode(P, tok[i], nseq, prompt + i, kv, nseq, ml, sp, logits)
-            nc.sample(logits, nseq, V, 1.0, 50, u[i + 1], tok[i + 1], stream.cuda_stream)
+            nc.sample_parallel(logits, nseq, V, 1.0, 50, u[i + 1], tok[i + 1], ssp, stream.cuda_stream)
         ev[3].record(stream)
         torch.cuda.synchronize()
         t_pre = ev[0].elapsed_time(ev[1])

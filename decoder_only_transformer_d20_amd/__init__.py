@@ -76,6 +76,8 @@ _SIGS = {
     "nc_backward_weighted": (ctypes.c_int, [_P, _P, _P, _I32, _P]),
     "nc_kv_cache_bytes": (_I64, [ctypes.POINTER(NcConfig), _I32, _I32]),
     "nc_sample": (ctypes.c_int, [_P, _I32, _I32, _F32, _I32, _P, _P, _P]),
+    "nc_sample_scratch_bytes": (_I64, [_I32, _I32]),
+    "nc_sample_parallel": (ctypes.c_int, [_P, _I32, _I32, _F32, _I32, _P, _P, _P, _P]),
     "nc_decode_scratch_bytes": (_I64, [ctypes.POINTER(NcConfig), _I32, _I32]),
     "nc_prefill": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, _I32, _P]),
     "nc_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, _I32, _P, _P]),
@@ -199,6 +201,19 @@ def sample(logits, n: int, V: int, temperature: float, top_k: int, u, out, strea
     """nc_sample: next token per row of fp32 logits [n][V] from uniforms u [n]."""
     _check(lib().nc_sample(_ptr(logits), int(n), int(V), float(temperature), int(top_k), _ptr(u), _ptr(out),
                            _ptr(stream)), "nc_sample")
+
+
+def sample_scratch_bytes(n: int, V: int) -> int:
+    r = lib().nc_sample_scratch_bytes(int(n), int(V))
+    _check(0 if r >= 0 else r, "nc_sample_scratch_bytes")
+    return r
+
+
+def sample_parallel(logits, n: int, V: int, temperature: float, top_k: int, u, out, scratch, stream=None):
+    """nc_sample_parallel: nc_sample over ceil(V/1024) workgroups per row;
+    scratch: device buffer of sample_scratch_bytes(n, V) bytes, 256-aligned."""
+    _check(lib().nc_sample_parallel(_ptr(logits), int(n), int(V), float(temperature), int(top_k), _ptr(u), _ptr(out),
+                                    _ptr(scratch), _ptr(stream)), "nc_sample_parallel")
 
 
 def kv_cache_bytes(cfg, max_batch: int, max_len: int) -> int:

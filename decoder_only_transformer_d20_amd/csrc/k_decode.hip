@@ -440,7 +440,311 @@ __global__ void __launch_bounds__(1024) k_sample(const float* __restrict__ logit
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same draw spread over many workgroups: each row is cut into blocks of
+// 1024 ids (one workgroup each) for the heavy passes.
+//   1. per block: max and first argmax; with top-k, the block's k largest
+//      keys (ties cut arbitrarily: the row's k largest are among the union)
+//   2. per row: the k-th largest of the candidates (the threshold), the
+//      row's max and first argmax (temperature 0 ends here)
+//   3. per block: sum of the kept weights (fp32 exponentials, fp64 sum),
+//      the block's last kept id
+//   4. per row: running sums of the blocks in id order pick the block that
+//      crosses u * total, and a scan of its 1024 ids in id order the token
+// ---------------------------------------------------------------------------
+constexpr int kSBlock = 1024;      // ids per workgroup
+constexpr int kSMaxK = 256;        // largest top_k of the parallel path
+
+struct SampleScratch {
+  float* bmax; int* barg; int* bcnt; uint32_t* cand;   // [n][G], [n][G], [n][G], [n][G][kSMaxK]
+  uint32_t* thr; float* zmax;                           // [n], [n]
+  double* bsum; int* blast;                             // [n][G], [n][G]
+};
+inline int64_t sample_scratch_layout(int n, int V, char* base, SampleScratch* ss) {
+  const int64_t G = (V + kSBlock - 1) / kSBlock;
+  int64_t off = 0, o[8];
+  const int64_t bytes[8] = {n * G * 4, n * G * 4, n * G * 4, n * G * kSMaxK * 4, (int64_t)n * 4, (int64_t)n * 4,
+                            n * G * 8, n * G * 4};
+  for (int i = 0; i < 8; ++i) {
+    o[i] = off;
+    off += (bytes[i] + 255) / 256 * 256;
+  }
+  if (ss)
+    *ss = SampleScratch{(float*)(base + o[0]), (int*)(base + o[1]), (int*)(base + o[2]), (uint32_t*)(base + o[3]),
+                        (uint32_t*)(base + o[4]), (float*)(base + o[5]), (double*)(base + o[6]), (int*)(base + o[7])};
+  return off;
+}
+
+// (value, id) of the larger logit, the smaller id on ties; id V = none
+__device__ inline void amax_merge(float& m, int& a, float m2, int a2, int V) {
+  if (a2 != V && (a == V || m2 > m || (m2 == m && a2 < a))) { m = m2; a = a2; }
+}
+
+// The k-th largest (k >= 1) of the keys held by a workgroup (slots j < jn
+// of NK per thread, valid ones flagged; jn uniform), 4 bits per pass.  Each
+// wave counts digits into its own 16 LDS counters (integer adds: the order
+// does not matter); wave 0 adds the waves' counts (lane = digit) and picks
+// the digit by a suffix scan.
+template <int NT, int NK>
+__device__ inline uint32_t block_kth_key(const uint32_t (&key)[NK], const bool (&ok)[NK], int jn, int k,
+                                         int (*hist)[16], int* s_state) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t prefix = 0, mask = 0;
+  for (int shift = 28; shift >= 0; shift -= 4) {
+    if (lane < 16) hist[wave][lane] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NK; ++j)
+      if (j < jn && ok[j] && (key[j] & mask) == prefix) atomicAdd(&hist[wave][(key[j] >> shift) & 15u], 1);
+    __syncthreads();
+    if (wave == 0) {
+      int hb = 0;
+      if (lane < 16)
+        for (int w = 0; w < NW; ++w) hb += hist[w][lane];
+      int suf = hb;                               // keys in digits >= lane
+      for (int o = 1; o < 16; o <<= 1) {
+        const int t = __shfl_down(suf, o, 64);
+        if (lane + o < 16) suf += t;
+      }
+      const unsigned long long ge = __ballot(lane < 16 && suf >= k);
+      const int b = ge ? 63 - __clzll((long long)ge) : 0;   // the largest digit whose suffix reaches k
+      const int above = __shfl(suf - hb, b, 64);            // keys in the digits above it
+      if (lane == 0) {
+        s_state[0] = b;
+        s_state[1] = k - above;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_state[0] << shift;
+    mask |= 15u << shift;
+    k = s_state[1];
+    __syncthreads();                              // before the counts are rewritten
+  }
+  return prefix;
+}
+
+__global__ void __launch_bounds__(256) k_sample_blocks(const float* __restrict__ logits, int V, int G, int top_k,
+                                                       SampleScratch ss) {
+  __shared__ float smax[4];
+  __shared__ int sarg[4];
+  __shared__ int hist[4][16];
+  __shared__ int s_state[2];
+  __shared__ int s_slot;
+  const int g = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* z = logits + (int64_t)row * V;
+  const int base = g * kSBlock;
+  uint32_t key[4];
+  bool ok[4];
+  float mx = -INFINITY;
+  int am = V;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = base + tid + 256 * j;
+    ok[j] = i < V;
+    const float zi = ok[j] ? z[i] : -INFINITY;
+    key[j] = fkey(zi);
+    if (ok[j]) amax_merge(mx, am, zi, i, V);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(mx, o, 64);
+    const int a2 = __shfl_xor(am, o, 64);
+    amax_merge(mx, am, m2, a2, V);
+  }
+  if (lane == 0) { smax[wave] = mx; sarg[wave] = am; }
+  __syncthreads();
+  if (tid == 0) {
+    float m = smax[0];
+    int a = sarg[0];
+    for (int w = 1; w < 4; ++w) amax_merge(m, a, smax[w], sarg[w], V);
+    ss.bmax[(int64_t)row * G + g] = m;
+    ss.barg[(int64_t)row * G + g] = a;
+  }
+  if (top_k <= 0) return;                                   // uniform: no candidates needed
+  const int nvalid = min(kSBlock, V - base);
+  const int kl = min(top_k, nvalid);
+  const uint32_t t = block_kth_key<256, 4>(key, ok, 4, kl, hist, s_state);
+  // candidates: every key above t, then copies of t up to kl
+  if (tid == 0) s_slot = 0;
+  __syncthreads();
+  uint32_t* cand = ss.cand + ((int64_t)row * G + g) * kSMaxK;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (ok[j] && key[j] > t) cand[atomicAdd(&s_slot, 1)] = key[j];
+  __syncthreads();
+  for (int c = s_slot + tid; c < kl; c += 256) cand[c] = t;
+  if (tid == 0) ss.bcnt[(int64_t)row * G + g] = kl;
+}
+
+__global__ void __launch_bounds__(1024) k_sample_threshold(int V, int G, float temperature, int top_k,
+                                                           SampleScratch ss, int32_t* __restrict__ out) {
+  constexpr int NK = (64 * kSMaxK) / 1024;                  // candidates per thread, at most
+  __shared__ int hist[16][16];
+  __shared__ int s_state[2];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  if (tid < 64) {
+    // the row's max and first argmax from the blocks' (G <= 64: one lane each)
+    float m = -INFINITY;
+    int a = V;
+    if (lane < G) {
+      m = ss.bmax[(int64_t)row * G + lane];
+      a = ss.barg[(int64_t)row * G + lane];
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(m, o, 64);
+      const int a2 = __shfl_xor(a, o, 64);
+      amax_merge(m, a, m2, a2, V);
+    }
+    if (lane == 0) {
+      ss.zmax[row] = m;
+      if (temperature == 0.f) out[row] = a;
+    }
+  }
+  if (temperature == 0.f) return;
+  if (top_k <= 0) {
+    if (tid == 0) ss.thr[row] = 0u;                         // every key passes
+    return;
+  }
+  // every block but the last holds top_k candidates (top_k <= 256 < 1024
+  // ids), the last bcnt[G - 1]: candidate e is slot e % top_k of block
+  // e / top_k, e < C
+  const int C = (G - 1) * top_k + ss.bcnt[(int64_t)row * G + G - 1];
+  uint32_t key[NK];
+  bool ok[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int e = tid + 1024 * j;
+    ok[j] = e < C;
+    key[j] = ok[j] ? ss.cand[((int64_t)row * G + e / top_k) * kSMaxK + e % top_k] : 0u;
+  }
+  const uint32_t t = block_kth_key<1024, NK>(key, ok, (C + 1023) / 1024, top_k, hist, s_state);
+  if (tid == 0) ss.thr[row] = t;
+}
+
+__global__ void __launch_bounds__(256) k_sample_sums(const float* __restrict__ logits, int V, int G, float temperature,
+                                                     SampleScratch ss) {
+  __shared__ double ssum[4];
+  __shared__ int slast[4];
+  const int g = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* z = logits + (int64_t)row * V;
+  const uint32_t thr = ss.thr[row];
+  const float zm = ss.zmax[row], wscale = 1.4426950408889634f / temperature;
+  double sum = 0.0;
+  int last = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = g * kSBlock + tid + 256 * j;
+    if (i < V) {
+      const float zi = z[i];
+      if (fkey(zi) >= thr) {
+        sum += (double)__builtin_amdgcn_exp2f((zi - zm) * wscale);
+        last = i;
+      }
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    sum += __shfl_xor(sum, o, 64);
+    last = max(last, __shfl_xor(last, o, 64));
+  }
+  if (lane == 0) { ssum[wave] = sum; slast[wave] = last; }
+  __syncthreads();
+  if (tid == 0) {
+    ss.bsum[(int64_t)row * G + g] = (ssum[0] + ssum[1]) + (ssum[2] + ssum[3]);
+    ss.blast[(int64_t)row * G + g] = max(max(slast[0], slast[1]), max(slast[2], slast[3]));
+  }
+}
+
+__global__ void __launch_bounds__(1024) k_sample_pick(const float* __restrict__ logits, int V, int G,
+                                                      float temperature, const float* __restrict__ u,
+                                                      SampleScratch ss, int32_t* __restrict__ out) {
+  __shared__ double wtot[16];
+  __shared__ int s_block, s_hit;
+  __shared__ double s_before;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const double* bs = ss.bsum + (int64_t)row * G;
+  const int* bl = ss.blast + (int64_t)row * G;
+  if (wave == 0) {
+    // running sums of the blocks in id order (G <= 64: one lane each)
+    const double mine = lane < G ? bs[lane] : 0.0;
+    double incl = mine;
+    for (int o = 1; o < 64; o <<= 1) {
+      const double up = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += up;
+    }
+    const double total = __shfl(incl, 63, 64);
+    const double target = (double)u[row] * total;
+    const unsigned long long cross = __ballot(lane < G && mine > 0.0 && incl > target);
+    int last = lane < G ? bl[lane] : -1;
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+    if (lane == 0) {
+      s_block = cross ? __ffsll((long long)cross) - 1 : -1;
+      s_hit = last;                                         // no crossing (rounding): the row's last kept id
+      s_before = target;
+    }
+    if (cross) {
+      const int jb = __ffsll((long long)cross) - 1;
+      const double before = __shfl(incl - mine, jb, 64);
+      if (lane == 0) s_before = target - before;            // the target within the block
+    }
+  }
+  __syncthreads();
+  const int gb = s_block;
+  if (gb < 0) {
+    if (tid == 0) out[row] = s_hit;
+    return;
+  }
+  // scan the crossing block's ids in id order: thread tid holds id gb * 1024 + tid
+  const float* z = logits + (int64_t)row * V;
+  const uint32_t thr = ss.thr[row];
+  const float zm = ss.zmax[row], wscale = 1.4426950408889634f / temperature;
+  const int i = gb * kSBlock + tid;
+  double w = 0.0;
+  if (i < V) {
+    const float zi = z[i];
+    if (fkey(zi) >= thr) w = (double)__builtin_amdgcn_exp2f((zi - zm) * wscale);
+  }
+  double incl = w;
+  for (int o = 1; o < 64; o <<= 1) {
+    const double up = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += up;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  if (tid == 0) s_hit = bl[gb];                             // rounding fallback: the block's last kept id
+  __syncthreads();
+  double before = 0.0;
+  for (int v = 0; v < wave; ++v) before += wtot[v];
+  const unsigned long long hit = __ballot(w > 0.0 && before + incl > s_before);
+  __syncthreads();
+  if (hit && lane == 0) atomicMin(&s_hit, gb * kSBlock + wave * 64 + __ffsll((long long)hit) - 1);
+  __syncthreads();
+  if (tid == 0) out[row] = s_hit;
+}
+
 }  // namespace
+
+int64_t sample_parallel_scratch_bytes(int n, int V) { return sample_scratch_layout(n, V, nullptr, nullptr); }
+
+hipError_t sample_parallel(const float* logits, int n, int V, float temperature, int top_k, const float* u,
+                           int32_t* out, void* scratch, hipStream_t s) {
+  if (n < 1 || n > 65535 || V < 1 || V > 64 * kSBlock || top_k < 0 || !(temperature >= 0.f))
+    return hipErrorInvalidValue;
+  if (top_k >= V) top_k = 0;                                // keeps every id
+  if (top_k > kSMaxK) return sample(logits, n, V, temperature, top_k, u, out, s);
+  SampleScratch ss;
+  sample_scratch_layout(n, V, (char*)scratch, &ss);
+  const int G = (V + kSBlock - 1) / kSBlock;
+  k_sample_blocks<<<dim3(G, n), 256, 0, s>>>(logits, V, G, temperature == 0.f ? 0 : top_k, ss);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_sample_threshold<<<n, 1024, 0, s>>>(V, G, temperature, top_k, ss, out);
+  e = hipGetLastError();
+  if (e != hipSuccess || temperature == 0.f) return e;
+  k_sample_sums<<<dim3(G, n), 256, 0, s>>>(logits, V, G, temperature, ss);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_sample_pick<<<n, 1024, 0, s>>>(logits, V, G, temperature, u, ss, out);
+  return hipGetLastError();
+}
 
 hipError_t sample(const float* logits, int n, int V, float temperature, int top_k, const float* u, int32_t* out,
                   hipStream_t s) {

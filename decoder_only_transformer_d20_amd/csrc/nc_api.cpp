@@ -1117,6 +1117,22 @@ int nc_sample(const float* logits, int32_t n, int32_t V, float temperature, int3
                                                                                                    : NC_ERR_HIP;
 }
 
+int64_t nc_sample_scratch_bytes(int32_t n, int32_t V) {
+  if (n < 1 || n > 65535 || V < 1 || V > 65536) return NC_ERR_SHAPE;
+  return sample_parallel_scratch_bytes(n, V);
+}
+
+int nc_sample_parallel(const float* logits, int32_t n, int32_t V, float temperature, int32_t top_k, const float* u,
+                       int32_t* out, void* scratch, void* hip_stream) {
+  if (!logits || !u || !out || !scratch) return NC_ERR_INVALID_ARG;
+  if (!(temperature >= 0.f) || !std::isfinite(temperature) || top_k < 0) return NC_ERR_INVALID_ARG;
+  if (n < 1 || n > 65535 || V < 1 || V > 65536) return NC_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(scratch) % 256) return NC_ERR_WORKSPACE;
+  return sample_parallel(logits, n, V, temperature, top_k, u, out, scratch, (hipStream_t)hip_stream) == hipSuccess
+             ? NC_OK
+             : NC_ERR_HIP;
+}
+
 int64_t nc_kv_cache_bytes(const nc_config* cfg, int32_t max_batch, int32_t max_len) {
   int st = validate(cfg);
   if (st != NC_OK) return st;

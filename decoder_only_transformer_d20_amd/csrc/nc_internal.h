@@ -186,6 +186,11 @@ int attn_decode_chunks(int L);
 // next token per row of logits [n][V] (nc_sample)
 hipError_t sample(const float* logits, int n, int V, float temperature, int top_k, const float* u, int32_t* out,
                   hipStream_t s);
+// the same draw over many workgroups (nc_sample_parallel): scratch of
+// sample_parallel_scratch_bytes(n, V) bytes, 256-byte aligned
+int64_t sample_parallel_scratch_bytes(int n, int V);
+hipError_t sample_parallel(const float* logits, int n, int V, float temperature, int top_k, const float* u,
+                           int32_t* out, void* scratch, hipStream_t s);
 template <typename T> hipError_t attn_decode(const AttnDecodeDesc& a, int nb, hipStream_t s);
 
 // ---------------------------------------------------------------------------

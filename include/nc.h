@@ -229,6 +229,20 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t ns
 int nc_sample(const float* logits, int32_t n, int32_t V, float temperature, int32_t top_k, const float* u,
               int32_t* out, void* hip_stream);
 
+/* nc_sample with each row spread over ceil(V / 1024) workgroups instead of
+ * one, for rows that would otherwise leave the chip idle (a decode step's
+ * few sequences).  Same rule and inputs; the fp64 sums run in another fixed
+ * order, so a draw can differ from nc_sample's only where u * sum lies
+ * within rounding of a boundary of the inverse CDF.  top_k above 256 (and
+ * below V) takes nc_sample's single-workgroup kernel.
+ *   scratch  device, nc_sample_scratch_bytes(n, V) bytes, 256-byte aligned
+ *            (NC_ERR_WORKSPACE otherwise), owned by the caller; calls that
+ *            share it must not overlap.
+ * NC_ERR_SHAPE on n < 1, n > 65535, V < 1 or V > 65536. */
+int64_t nc_sample_scratch_bytes(int32_t n, int32_t V);
+int nc_sample_parallel(const float* logits, int32_t n, int32_t V, float temperature, int32_t top_k,
+                       const float* u, int32_t* out, void* scratch, void* hip_stream);
+
 /* ---- single block (NC_FLAG_BLOCK_ONLY) ------------------------------------ */
 
 /* y = block(x) for x, y device dtype [B*T, d] (may not alias).  Saves what

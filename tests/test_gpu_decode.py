@@ -129,24 +129,35 @@ def test_d20_decode_matches_forward():
     _check(cfg, params, prompt, gen, 2, bf16=True)
 
 
+@pytest.mark.parametrize("parallel", [False, True])
 @pytest.mark.parametrize("V,temperature,top_k", [(4096, 0.0, 0), (4096, 1.0, 0), (65536, 0.8, 50),
-                                                 (65536, 1.0, 1), (1000, 1.3, 7), (65536, 1.0, 0)])
-def test_sample_matches_oracle(V, temperature, top_k):
-    """nc_sample against oracle.sample_next on 64 rows with the same
-    uniforms, including a row of all-equal logits (top-k keeps every tie)
-    and a row with one dominant logit.  The GPU's weights are fp32
-    exponentials (relative error ~1e-7) summed in fp64, the oracle's fp64
-    throughout, so a draw may differ only where u * sum lies within 1e-6 of
-    the total from a boundary of the inverse CDF; such a draw must still be
-    a kept id next to the boundary."""
+                                                 (65536, 1.0, 1), (1000, 1.3, 7), (65536, 1.0, 0),
+                                                 (5000, 1.0, 256), (65536, 0.7, 300), (3000, 0.0, 5),
+                                                 (2049, 1.0, 2049)])
+def test_sample_matches_oracle(V, temperature, top_k, parallel):
+    """nc_sample and nc_sample_parallel against oracle.sample_next on 64
+    rows with the same uniforms, including a row of all-equal logits (top-k
+    keeps every tie), a row with one dominant logit and a row whose largest
+    logit repeats in several 1024-id blocks (the first id wins at
+    temperature 0).  The GPU's weights are fp32 exponentials (relative error
+    ~1e-7) summed in fp64, the oracle's fp64 throughout, so a draw may
+    differ only where u * sum lies within 1e-6 of the total from a boundary
+    of the inverse CDF; such a draw must still be a kept id next to the
+    boundary."""
     rng = np.random.default_rng(60 + V + top_k)
     n = 64
     z = (rng.standard_normal((n, V)) * 3).astype(np.float32)
     z[5, :] = 0.25
     z[6, 17] = 40.0
+    z[7, V - 1] = z[7, V // 2] = z[7, 3] = 30.0
     u = rng.random(n).astype(np.float32)
     out = empty((n,), "i32")
-    nc.sample(dev(z), n, V, temperature, top_k, dev(u), out)
+    if parallel:
+        scr = empty((nc.sample_scratch_bytes(n, V) // 4 + 64,))
+        sp = (scr.data_ptr() + 255) // 256 * 256
+        nc.sample_parallel(dev(z), n, V, temperature, top_k, dev(u), out, sp)
+    else:
+        nc.sample(dev(z), n, V, temperature, top_k, dev(u), out)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     t32 = float(np.float32(temperature))

@@ -198,3 +198,10 @@ def test_inference_sizes_and_null_context():
     assert L.nc_sample(16, 1, 8, -1.0, 0, 16, 16, None) == -1
     assert L.nc_sample(16, 1, 8, 1.0, -2, 16, 16, None) == -1
     assert L.nc_sample(16, 0, 8, 1.0, 0, 16, 16, None) == -2
+    assert L.nc_sample_parallel(None, 1, 8, 1.0, 0, 1, 1, 256, None) == -1
+    assert L.nc_sample_parallel(16, 1, 8, 1.0, 0, 16, 16, None, None) == -1
+    assert L.nc_sample_parallel(16, 1, 8, -1.0, 0, 16, 16, 256, None) == -1
+    assert L.nc_sample_parallel(16, 1, 70000, 1.0, 0, 16, 16, 256, None) == -2
+    assert L.nc_sample_parallel(16, 1, 8, 1.0, 0, 16, 16, 257, None) == -3
+    assert L.nc_sample_scratch_bytes(0, 8) == -2 and L.nc_sample_scratch_bytes(1, 65537) == -2
+    assert L.nc_sample_scratch_bytes(16, 65536) >= 16 * 64 * 256 * 4
