@@ -98,7 +98,7 @@ _SIGS = {
                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
     "nc_op_matmul": (ctypes.c_int, [_I32, _I32, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I32, _P, _I32, _P]),
     "nc_op_matmul_batched": (ctypes.c_int, [_I32, _I32, _I32, _I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P,
-                                            _I64, _F32, _F32, _I32, _P]),
+                                            _I64, _F32, _F32, _I32, _I32, _P]),
     "nc_op_rmsnorm_fwd": (ctypes.c_int, [_I32, _I64, _I32, _F32, _P, _P, _P, _P]),
     "nc_op_rmsnorm_bwd": (ctypes.c_int, [_I32, _I64, _I32, _P, _P, _P, _P, _I32, _P]),
     "nc_op_rope_table": (ctypes.c_int, [_I32, _I32, _F32, _P, _P]),

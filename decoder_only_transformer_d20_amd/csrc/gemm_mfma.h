@@ -159,12 +159,13 @@ struct GemmTile {
 template <int BM, int BN>
 struct TileMap {
   static constexpr int kGroupM = 8, kNarrow = 8;
-  int ntn, ntm, ntiles, total, nkt, G, chunk, splits;
+  int ntn, ntm, ntiles, total, nkt, G, chunk, splits, sym;
   int64_t sP, sQ, sC, sAux;
   __device__ inline TileMap(const GemmDesc& g) {
     ntn = g.N / BN;
     ntm = g.M / BM;
-    ntiles = ntn * ntm;
+    sym = g.sym;
+    ntiles = sym ? ntm * (ntm + 1) / 2 : ntn * ntm;   // sym: the tiles with tn >= tm
     splits = g.splits;
     total = ntiles * splits * (g.batch > 1 ? g.batch : 1);
     sP = g.sP; sQ = g.sQ; sC = g.sC; sAux = g.sAux;
@@ -187,6 +188,20 @@ struct TileMap {
     c.split = outer - b * splits;
     c.pofs = b * sP; c.qofs = b * sQ; c.cofs = b * sC; c.aofs = b * sAux;
     const int t = L - outer * ntiles;
+    if (sym) {
+      // row tm of the upper triangle holds ntm - tm tiles
+      int tm = 0, rem = t;
+      while (rem >= ntm - tm) {
+        rem -= ntm - tm;
+        ++tm;
+      }
+      c.tn = tm + rem;
+      c.m0 = (int64_t)tm * BM;
+      c.n0 = (int64_t)c.tn * BN;
+      c.nk = nkt;
+      c.kbeg = 0;
+      return c;
+    }
     const int first_m = (t / (kGroupM * ntn)) * kGroupM;
     const int gm = min(kGroupM, ntm - first_m);
     const int tg = t - first_m * ntn;
@@ -678,7 +693,8 @@ int resident_blocks(Kernel kern, int threads, int (&cached)[16]) {
 template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
 hipError_t launch(const GemmDesc& g, hipStream_t s) {
   static int cached[16] = {0};
-  const int total = (g.M / BM) * (g.N / BN) * g.splits * (g.batch > 1 ? g.batch : 1);
+  const int ntiles = g.sym ? (g.M / BM) * (g.M / BM + 1) / 2 : (g.M / BM) * (g.N / BN);
+  const int total = ntiles * g.splits * (g.batch > 1 ? g.batch : 1);
   dim3 grid(std::min(total, resident_blocks(k_gemm_mfma<NW, BM, BN, PT, QT, EPI>, NW * 64, cached)));
   k_gemm_mfma<NW, BM, BN, PT, QT, EPI><<<grid, NW * 64, 0, s>>>(g);
   return hipGetLastError();

@@ -16,17 +16,45 @@ bool gemm_mfma_supported(const GemmDesc& g) {
   if (g.splits > 1 && g.epi != EPI_F32) return false;
   if (g.batch > 1 && (g.splits != 1 || (g.epi != EPI_STORE && g.epi != EPI_AXPBY))) return false;
   if ((int64_t)(g.M / 128) * (g.N / 128) * g.splits * (g.batch > 1 ? g.batch : 1) > (1 << 30)) return false;
+  if (g.sym && (g.M != g.N || gemm_mfma_tile_m(g.M, g.N) != gemm_mfma_tile_n(g.M, g.N) || g.splits != 1 ||
+                g.batch > 65535 ||
+                (g.epi != EPI_STORE && g.epi != EPI_AXPBY)))
+    return false;
   if (g.epi == EPI_ROPE && (g.head_dim % 4 || g.rope_cols % 4)) return false;
   return mfma::combo_supported(g);
 }
 
+namespace {
+// C[i][j] = C[j][i] wherever the tile row of i lies below the tile row of j
+// (tiles of `tile` rows): the lower tiles of a symmetric product whose upper
+// tiles were computed.  A workgroup moves one 64 x 64 block through LDS.
+__global__ void __launch_bounds__(256) k_mirror_lower(unsigned short* C, int n, int64_t ldc, int64_t sC, int tile) {
+  __shared__ unsigned short blk[64][65];
+  const int bi = blockIdx.x, bj = blockIdx.y;        // destination block (rows bi, columns bj)
+  if ((bi * 64) / tile <= (bj * 64) / tile) return;   // on or above the diagonal tiles: computed
+  unsigned short* c = C + (int64_t)blockIdx.z * sC;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  // source block (rows bj, columns bi), read row by row
+  for (int r = ty; r < 64; r += 4) blk[r][tx] = c[(int64_t)(bj * 64 + r) * ldc + bi * 64 + tx];
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) c[(int64_t)(bi * 64 + r) * ldc + bj * 64 + tx] = blk[tx][r];
+}
+}  // namespace
+
 hipError_t gemm_mfma_bf16_product(const GemmDesc& g, hipStream_t s) {
   if (!gemm_mfma_supported(g)) return hipErrorInvalidValue;
   const int bm = gemm_mfma_tile_m(g.M, g.N), bn = gemm_mfma_tile_n(g.M, g.N);
-  if (bm == 256 && bn == 256) return mfma::gemm_256x256(g, s);
-  if (bm == 256) return mfma::gemm_256x128(g, s);
-  return mfma::gemm_128x128(g, s);
+  hipError_t e;
+  if (bm == 256 && bn == 256) e = mfma::gemm_256x256(g, s);
+  else if (bm == 256) e = mfma::gemm_256x128(g, s);
+  else e = mfma::gemm_128x128(g, s);
+  if (e != hipSuccess || !g.sym) return e;
+  const int nb64 = g.M / 64;
+  k_mirror_lower<<<dim3(nb64, nb64, g.batch > 1 ? g.batch : 1), 256, 0, s>>>((unsigned short*)g.C, g.M, g.ldc,
+                                                                              g.sC, bm);
+  return hipGetLastError();
 }
+
 
 hipError_t gemm_mfma_bf16(const GemmDesc& g, hipStream_t s) {
   hipError_t e = gemm_mfma_bf16_product(g, s);

@@ -269,7 +269,12 @@ hipError_t traced(nc_ctx* ctx, int family, double flops, double bytes, F&& launc
 hipError_t run_gemm(nc_ctx* ctx, const GemmDesc& g, int family = -2) {
   if (!is_bf16(ctx->cfg)) return gemm_portable<float>(g, ctx->stream);
   if (portable(ctx->cfg) || !gemm_mfma_supported(g)) return gemm_portable<bf16>(g, ctx->stream);
-  const double items = g.batch > 1 ? g.batch : 1;
+  double items = g.batch > 1 ? g.batch : 1;
+  if (g.sym) {
+    // the tiles on and above the diagonal are computed, the rest mirrored
+    const double t = g.M / gemm_mfma_tile_m(g.M, g.N);
+    items *= (t + 1) / (2 * t);
+  }
   hipError_t e = traced(ctx, family < -1 ? gemm_family(g) : family, 2.0 * g.M * g.N * g.K * items,
                         gemm_bytes(g, 2) * items, [&] { return gemm_mfma_bf16_product(g, ctx->stream); });
   if (e == hipSuccess && g.epi == EPI_F32 && g.splits > 1)
@@ -698,14 +703,16 @@ hipError_t optim_muon(nc_ctx* ctx, const MuonGroup& grp, float* master, T* param
   }
   for (int it = 0; it < h->ns_steps && e == hipSuccess; ++it) {
     // A = X X^T
+    // (A and B are symmetric: the matrix-core kernel computes their upper
+    // tiles and mirrors the rest)
     GemmDesc ga = gemm(rw, rw, cw, X, cw, 0, X, cw, 0, EPI_STORE, A, rw);
-    ga.batch = nb; ga.sP = sx; ga.sQ = sx; ga.sC = sa;
+    ga.batch = nb; ga.sP = sx; ga.sQ = sx; ga.sC = sa; ga.sym = 1;
     e = run_gemm(ctx, ga, NC_TRACE_OPTIM_NS);
     // B = ns_c A A^T + ns_b A   (A is symmetric, so A A^T = A A)
     if (e == hipSuccess) {
       GemmDesc gb = gemm(rw, rw, rw, A, rw, 0, A, rw, 0, EPI_AXPBY, B, rw);
       gb.aux = A; gb.ldaux = rw; gb.ep_alpha = h->ns_c; gb.ep_gamma = h->ns_b;
-      gb.batch = nb; gb.sP = sa; gb.sQ = sa; gb.sC = sa; gb.sAux = sa;
+      gb.batch = nb; gb.sP = sa; gb.sQ = sa; gb.sC = sa; gb.sAux = sa; gb.sym = 1;
       e = run_gemm(ctx, gb, NC_TRACE_OPTIM_NS);
     }
     // X' = B X + ns_a X

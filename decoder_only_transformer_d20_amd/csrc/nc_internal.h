@@ -80,6 +80,12 @@ struct GemmDesc {
   // batch 0 or 1 is a single product
   int batch;
   int64_t sP, sQ, sC, sAux;
+  // sym = 1 (matrix-core kernel, M == N, square tiles, STORE / AXPBY): the
+  // result is known to be symmetric (P Q^T with Q = P, or a linear
+  // combination of such products); only the tiles on and above the
+  // diagonal are computed and the rest is mirrored from them.  Other
+  // kernels compute every tile.
+  int sym;
 };
 
 // ---------------------------------------------------------------------------

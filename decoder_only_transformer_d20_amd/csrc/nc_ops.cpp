@@ -54,10 +54,12 @@ int nc_op_matmul(int32_t dtype, int32_t p_trans, int32_t q_trans, int64_t M, int
 
 int nc_op_matmul_batched(int32_t dtype, int32_t q_trans, int32_t batch, int64_t M, int64_t N, int64_t K,
                          const void* P, int64_t sP, const void* Q, int64_t sQ, void* C, int64_t sC,
-                         const void* aux, int64_t sAux, float alpha, float gamma, int32_t portable,
+                         const void* aux, int64_t sAux, float alpha, float gamma, int32_t sym, int32_t portable,
                          void* hip_stream) {
   if (!dtype_ok(dtype) || !P || !Q || !C) return NC_ERR_INVALID_ARG;
-  if (batch < 1 || batch > 65536 || (q_trans != 0 && q_trans != 1)) return NC_ERR_INVALID_ARG;
+  if (batch < 1 || batch > 65535 || (q_trans != 0 && q_trans != 1) || (sym != 0 && sym != 1))
+    return NC_ERR_INVALID_ARG;
+  if (sym && M != N) return NC_ERR_SHAPE;
   if (M <= 0 || N <= 0 || K <= 0 || M % 64 || N % 64 || K % 64 || M > (1 << 30) || N > (1 << 30) || K > (1 << 30))
     return NC_ERR_SHAPE;
   if (sP < 0 || sQ < 0 || sC < 0 || sAux < 0 || (sP | sQ | sC | sAux) % 8) return NC_ERR_INVALID_ARG;
@@ -68,7 +70,7 @@ int nc_op_matmul_batched(int32_t dtype, int32_t q_trans, int32_t batch, int64_t 
   g.epi = aux ? EPI_AXPBY : EPI_STORE;
   g.C = C; g.ldc = N; g.splits = 1;
   g.aux = aux; g.ldaux = N; g.ep_alpha = alpha; g.ep_gamma = gamma;
-  g.batch = batch; g.sP = sP; g.sQ = sQ; g.sC = sC; g.sAux = sAux;
+  g.batch = batch; g.sP = sP; g.sQ = sQ; g.sC = sC; g.sAux = sAux; g.sym = sym;
   return status_of(dispatch_gemm(dtype, portable, g, (hipStream_t)hip_stream));
 }
 

@@ -49,10 +49,15 @@ int nc_op_matmul(int32_t dtype, int32_t p_trans, int32_t q_trans, int64_t M, int
  * Strides in elements, >= 0 and multiples of 8 (NC_ERR_INVALID_ARG
  * otherwise).  M, N, K multiples of 64 (NC_ERR_SHAPE); the matrix-core path
  * (portable = 0, bf16) also needs M, N multiples of 128 and returns
- * NC_ERR_UNSUPPORTED otherwise.  fp32 always takes the portable kernel. */
+ * NC_ERR_UNSUPPORTED otherwise.  fp32 always takes the portable kernel.
+ * sym = 1 (M == N; Newton-Schulz's X X^T and c A A + b A): the caller
+ * asserts every C_b is symmetric (Q_b = P_b, and aux_b symmetric); the
+ * matrix-core kernel then computes the tiles on and above the diagonal and
+ * copies the rest across it.  The portable kernel computes every tile.
+ * batch <= 65535. */
 int nc_op_matmul_batched(int32_t dtype, int32_t q_trans, int32_t batch, int64_t M, int64_t N, int64_t K,
                          const void* P, int64_t sP, const void* Q, int64_t sQ, void* C, int64_t sC,
-                         const void* aux, int64_t sAux, float alpha, float gamma, int32_t portable,
+                         const void* aux, int64_t sAux, float alpha, float gamma, int32_t sym, int32_t portable,
                          void* hip_stream);
 
 /* Parameter-free RMSNorm (section Pretraining: no RMSNorm parameters):

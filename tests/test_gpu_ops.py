@@ -104,7 +104,7 @@ def test_matmul_batched_axpby_exact(dtype, portable, qt, batch, M, N, K):
     for alpha, gamma, with_aux in ((1.0, 0.0, False), (2.0, -0.5, True), (-4.0, 0.25, True)):
         C = empty((batch, M * N + pad), dtype)
         nc.ops.matmul_batched(DT[dtype], qt, batch, M, N, K, Pd, M * K + pad, Qd, N * K + pad, C, M * N + pad,
-                              Ad if with_aux else None, M * N + pad, alpha, gamma, portable, None)
+                              Ad if with_aux else None, M * N + pad, alpha, gamma, 0, portable, None)
         _sync()
         got = host(C, dtype)
         for b in range(batch):
@@ -120,14 +120,46 @@ def test_matmul_batched_axpby_exact(dtype, portable, qt, batch, M, N, K):
             np.testing.assert_array_equal(got[b, :M * N].reshape(M, N), want, err_msg=f"item {b}")
 
 
+@pytest.mark.parametrize("portable", [0, 1])
+@pytest.mark.parametrize("batch,n,K", [(3, 1280, 512), (5, 640, 256), (2, 384, 1280), (80, 256, 128)])
+def test_matmul_batched_symmetric_exact(portable, batch, n, K):
+    """sym = 1, the Newton-Schulz products: A_b = X_b X_b^T and then
+    B_b = 2 A_b A_b - 0.5 A_b, bit for bit against numpy; the matrix-core
+    kernel computes the upper tiles (256 x 256 for n = 1280, 128 x 128 for
+    640 and 384) and mirrors the rest.  X is sparse in {-1, 0, 1} (6 %
+    nonzero), so every entry of A is an integer of magnitude < 256 (exact
+    in bf16) and every partial sum of A A stays below 2^24 (exact in
+    fp32): each result is the rounding of the exact value."""
+    rng = np.random.default_rng(300 + n + batch)
+    X = rng.choice(np.array([-1.0, 0.0, 1.0], np.float32), size=(batch, n * K), p=[0.03, 0.94, 0.03])
+    Xd = dev(X, "bf16")
+    A = empty((batch, n * n), "bf16")
+    nc.ops.matmul_batched(1, 0, batch, n, n, K, Xd, n * K, Xd, n * K, A, n * n, None, 0, 1.0, 0.0, 1, portable, None)
+    B = empty((batch, n * n), "bf16")
+    nc.ops.matmul_batched(1, 0, batch, n, n, n, A, n * n, A, n * n, B, n * n, A, n * n, 2.0, -0.5, 1, portable, None)
+    _sync()
+    ga, gb = host(A, "bf16"), host(B, "bf16")
+    for b in range(batch):
+        Xb = X[b].reshape(n, K).astype(np.int64)
+        Ab = Xb @ Xb.T
+        assert np.abs(Ab).max() < 256 and (np.abs(Ab) @ np.abs(Ab)).max() * 2 < 2 ** 24
+        np.testing.assert_array_equal(ga[b].reshape(n, n), synthdata.round_to_bf16(Ab.astype(np.float32)),
+                                      err_msg=f"A item {b}")
+        Ar = ga[b].reshape(n, n).astype(np.float64)         # the rounded A the second product reads
+        want = synthdata.round_to_bf16((2.0 * (Ar @ Ar) - 0.5 * Ar).astype(np.float32))
+        np.testing.assert_array_equal(gb[b].reshape(n, n), want, err_msg=f"B item {b}")
+
+
 def test_matmul_batched_rejects():
     P = dev(np.zeros(2 * 192 * 128, np.float32), "bf16")
     C = empty((2 * 192 * 192,), "bf16")
-    cases = (((1, 0, 2, 192, 192, 128, P, 192 * 128, P, 192 * 128, C, 192 * 192, None, 0, 1.0, 0.0, 0), -6),
-             ((1, 0, 2, 128, 128, 128, P, 128 * 128 + 4, P, 0, C, 0, None, 0, 1.0, 0.0, 1), -1),
-             ((1, 2, 2, 128, 128, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 1), -1),
-             ((1, 0, 0, 128, 128, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 1), -1),
-             ((1, 0, 2, 128, 100, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 1), -2))
+    cases = (((1, 0, 2, 192, 192, 128, P, 192 * 128, P, 192 * 128, C, 192 * 192, None, 0, 1.0, 0.0, 0, 0), -6),
+             ((1, 0, 2, 128, 128, 128, P, 128 * 128 + 4, P, 0, C, 0, None, 0, 1.0, 0.0, 0, 1), -1),
+             ((1, 2, 2, 128, 128, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 0, 1), -1),
+             ((1, 0, 0, 128, 128, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 0, 1), -1),
+             ((1, 0, 2, 128, 100, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 0, 1), -2),
+             ((1, 0, 2, 128, 256, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 1, 0), -2),
+             ((1, 0, 2, 128, 128, 128, P, 0, P, 0, C, 0, None, 0, 1.0, 0.0, 2, 0), -1))
     for args, status in cases:
         with pytest.raises(nc.NcError) as e:
             nc.ops.matmul_batched(*args, None)
