@@ -27,17 +27,40 @@ bool gemm_mfma_supported(const GemmDesc& g) {
 namespace {
 // C[i][j] = C[j][i] wherever the tile row of i lies below the tile row of j
 // (tiles of `tile` rows): the lower tiles of a symmetric product whose upper
-// tiles were computed.  A workgroup moves one 64 x 64 block through LDS.
+// tiles were computed.  A workgroup moves one 64 x 64 block through LDS:
+// 16-byte row pieces in and out (8 per row, two per thread), the transpose
+// done in LDS.  Only the nlow strictly-lower blocks of an item are
+// launched: blockIdx.x enumerates them row by row.
 __global__ void __launch_bounds__(256) k_mirror_lower(unsigned short* C, int n, int64_t ldc, int64_t sC, int tile) {
-  __shared__ unsigned short blk[64][65];
-  const int bi = blockIdx.x, bj = blockIdx.y;        // destination block (rows bi, columns bj)
-  if ((bi * 64) / tile <= (bj * 64) / tile) return;   // on or above the diagonal tiles: computed
-  unsigned short* c = C + (int64_t)blockIdx.z * sC;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  // source block (rows bj, columns bi), read row by row
-  for (int r = ty; r < 64; r += 4) blk[r][tx] = c[(int64_t)(bj * 64 + r) * ldc + bi * 64 + tx];
+  __shared__ unsigned short blk[64][64 + 2];
+  const int per = tile / 64;                          // 64-blocks per tile side
+  int bi = per, rem = blockIdx.x;                     // rows of blocks below the first tile row
+  while (rem >= (bi / per) * per) {                   // block row bi holds (tile row of bi) * per lower blocks
+    rem -= (bi / per) * per;
+    ++bi;
+  }
+  const int bj = rem;
+  unsigned short* c = C + (int64_t)blockIdx.y * sC;
+  const int t = threadIdx.x;
+  // source block (rows bj, columns bi): row r, 16-byte piece q
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = (t >> 3) + 32 * h, q = t & 7;
+    const uint4 v = *reinterpret_cast<const uint4*>(c + (int64_t)(bj * 64 + r) * ldc + bi * 64 + 8 * q);
+    const unsigned short* e = reinterpret_cast<const unsigned short*>(&v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) blk[r][8 * q + k] = e[k];
+  }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) c[(int64_t)(bi * 64 + r) * ldc + bj * 64 + tx] = blk[tx][r];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = (t >> 3) + 32 * h, q = t & 7;      // destination row r = source column
+    uint4 v;
+    unsigned short* e = reinterpret_cast<unsigned short*>(&v);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = blk[8 * q + k][r];
+    *reinterpret_cast<uint4*>(c + (int64_t)(bi * 64 + r) * ldc + bj * 64 + 8 * q) = v;
+  }
 }
 }  // namespace
 
@@ -49,9 +72,13 @@ hipError_t gemm_mfma_bf16_product(const GemmDesc& g, hipStream_t s) {
   else if (bm == 256) e = mfma::gemm_256x128(g, s);
   else e = mfma::gemm_128x128(g, s);
   if (e != hipSuccess || !g.sym) return e;
-  const int nb64 = g.M / 64;
-  k_mirror_lower<<<dim3(nb64, nb64, g.batch > 1 ? g.batch : 1), 256, 0, s>>>((unsigned short*)g.C, g.M, g.ldc,
-                                                                              g.sC, bm);
+  // strictly-lower 64-blocks of one item: tile rows 1 .. T-1, row tr holding
+  // tr * per blocks in each of its per block rows
+  const int per = bm / 64, T = g.M / bm;
+  const int nlow = per * per * T * (T - 1) / 2;
+  if (nlow == 0) return hipSuccess;
+  if (g.ldc % 8 || g.sC % 8) return hipErrorInvalidValue;
+  k_mirror_lower<<<dim3(nlow, g.batch > 1 ? g.batch : 1), 256, 0, s>>>((unsigned short*)g.C, g.M, g.ldc, g.sC, bm);
   return hipGetLastError();
 }
 
