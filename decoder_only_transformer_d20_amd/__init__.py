@@ -87,6 +87,7 @@ _SIGS = {
     "nc_set_stream": (ctypes.c_int, [_P, _P]),
     "nc_destroy": (None, [_P]),
     "nc_last_error": (ctypes.c_char_p, [_P]),
+    "nc_fallback_count": (ctypes.c_int, [_P, ctypes.POINTER(_I64), _I32]),
     "nc_forward": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "nc_forward_eval": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "nc_loss_bpb": (ctypes.c_int, [_P, _P, _P]),
@@ -106,7 +107,7 @@ _SIGS = {
     "nc_op_device_info": (ctypes.c_int, [_I32] + [ctypes.POINTER(_I32)] * 4),
     "nc_op_attention_fwd": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P]),
     "nc_op_attention_bwd": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
-    "nc_op_embed_fwd": (ctypes.c_int, [_I32, _I64, _I32, _P, _P, _P, _P]),
+    "nc_op_embed_fwd": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _P]),
     "nc_op_embed_bwd_scratch_bytes": (_I64, [_I64, _I32]),
     "nc_op_embed_bwd": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _I32, _P, _P]),
     "nc_op_head_scratch_bytes": (_I64, [_I32, _I64, _I32, _I32, _I32]),
@@ -290,6 +291,12 @@ class Context:
         """nc_decode: one token per sequence at position pos, next-token logits."""
         _check(lib().nc_decode(self.h, _ptr(params), _ptr(tokens), int(nseq), int(pos), _ptr(kv_cache),
                                int(max_batch), int(max_len), _ptr(scratch), _ptr(logits)), "nc_decode", self.h)
+
+    def fallback_count(self, reset: bool = False) -> int:
+        """nc_fallback_count: bf16 launches that took a portable kernel."""
+        n = _I64()
+        _check(lib().nc_fallback_count(self.h, ctypes.byref(n), int(bool(reset))), "nc_fallback_count", self.h)
+        return n.value
 
     def trace_enable(self, family):
         """Time launches of one kernel family (a name from TRACE_FAMILIES or

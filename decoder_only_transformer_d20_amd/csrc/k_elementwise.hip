@@ -47,17 +47,24 @@ template <typename T> __device__ inline void st16(T* p, const Vec<T>& r) {
 // ---------------------------------------------------------------------------
 // embedding
 // ---------------------------------------------------------------------------
-// x[n, :] = E[idx[n], :]  (a bitwise copy of the row)
+// x[n, :] = E[idx[n], :]  (a bitwise copy of the row).  An id outside
+// [0, V) reads nothing and gives a row of quiet NaNs, so the error shows in
+// everything computed from that position instead of reading past the table.
 template <typename T>
 __global__ void __launch_bounds__(256) k_embed_fwd(const T* __restrict__ E, const int32_t* __restrict__ idx,
-                                                   T* __restrict__ x, int64_t n, int d) {
+                                                   T* __restrict__ x, int64_t n, int d, int V) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n) return;
-  const int64_t src = (int64_t)idx[row] * d;
+  const int id = idx[row];
   const int chunks = d * (int)sizeof(T) / 16;
-  const uint4* s = reinterpret_cast<const uint4*>(E + src);
   uint4* t = reinterpret_cast<uint4*>(x + row * d);
+  if (id < 0 || id >= V) {
+    const uint32_t q = sizeof(T) == 2 ? 0x7fc07fc0u : 0x7fc00000u;
+    for (int c = lane; c < chunks; c += kWave) t[c] = make_uint4(q, q, q, q);
+    return;
+  }
+  const uint4* s = reinterpret_cast<const uint4*>(E + (int64_t)id * d);
   for (int c = lane; c < chunks; c += kWave) t[c] = s[c];
 }
 
@@ -438,11 +445,13 @@ __global__ void k_rope_table(float2* tab, int t0, int T, int Q, double base) {
 
 // ---------------------------------------------------------------------------
 // cross-entropy: combine per-tile (max, sum exp) partials of one row into
-// lse, then ce = lse - z[target] (0 for an ignored target)
+// lse, then ce = lse - z[target] (0 for an ignored target, NaN for a target
+// >= V, which has no logit)
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_ce_combine(const float2* __restrict__ part, int nblk,
                                                     const float* __restrict__ ztgt, const int32_t* __restrict__ tgt,
-                                                    float* __restrict__ lse, float* __restrict__ ce, int64_t rows) {
+                                                    float* __restrict__ lse, float* __restrict__ ce, int64_t rows,
+                                                    int V) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -456,7 +465,8 @@ __global__ void __launch_bounds__(256) k_ce_combine(const float2* __restrict__ p
   if (lane == 0) {
     const float l = mx + logf(s);
     lse[row] = l;
-    ce[row] = tgt[row] >= 0 ? l - ztgt[row] : 0.f;
+    const int t = tgt[row];
+    ce[row] = t < 0 ? 0.f : t < V ? l - ztgt[row] : __builtin_nanf("");
   }
 }
 
@@ -521,12 +531,16 @@ __global__ void __launch_bounds__(1024) k_count_valid(const int32_t* __restrict_
 }
 
 // per-row factor of the head's dz: 1/n_valid (times the token's weight when
-// weights are given) for a valid target, 0 for an ignored one
+// weights are given) for a valid target, 0 for an ignored one, NaN for a
+// target >= V (the gradient then shows the error)
 __global__ void __launch_bounds__(256) k_row_scale(const int32_t* __restrict__ tgt, const float* __restrict__ w,
-                                                    const float* __restrict__ inv, int64_t n, float* __restrict__ out) {
+                                                    const float* __restrict__ inv, int64_t n, int V,
+                                                    float* __restrict__ out) {
   const float iv = *inv;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    out[i] = tgt[i] >= 0 ? (w ? iv * w[i] : iv) : 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int t = tgt[i];
+    out[i] = t < 0 ? 0.f : t < V ? (w ? iv * w[i] : iv) : __builtin_nanf("");
+  }
 }
 
 // one block, fixed order: out = {sum w ce, sum w ce / n} over valid targets
@@ -559,8 +573,9 @@ __global__ void __launch_bounds__(1024) k_weighted_loss(const float* __restrict_
 }
 
 // one block, fixed order: out = {sum ce / n, sum ce / (ln2 * sum bytes), sum ce, sum bytes, n}
+// (a target >= V has no byte count to read; its ce is NaN, and so are the sums)
 __global__ void __launch_bounds__(1024) k_loss_bpb(const float* __restrict__ ce, const int32_t* __restrict__ tgt,
-                                                   const int32_t* __restrict__ bytes, int64_t n, double* out) {
+                                                   const int32_t* __restrict__ bytes, int64_t n, int V, double* out) {
   __shared__ double sce[1024];
   __shared__ int64_t sb[1024], sn[1024];
   double a = 0.0;
@@ -569,7 +584,7 @@ __global__ void __launch_bounds__(1024) k_loss_bpb(const float* __restrict__ ce,
     const int t = tgt[i];
     if (t >= 0) {
       a += (double)ce[i];
-      b += bytes[t];
+      if (t < V) b += bytes[t];
       c += 1;
     }
   }
@@ -680,8 +695,8 @@ inline unsigned nblocks(int64_t n, int per) { return (unsigned)((n + per - 1) / 
 }  // namespace
 
 template <typename T>
-hipError_t embed_fwd(const T* E, const int32_t* idx, T* x, int64_t n, int d, hipStream_t s) {
-  k_embed_fwd<T><<<nblocks(n, 4), 256, 0, s>>>(E, idx, x, n, d);
+hipError_t embed_fwd(const T* E, const int32_t* idx, T* x, int64_t n, int d, int V, hipStream_t s) {
+  k_embed_fwd<T><<<nblocks(n, 4), 256, 0, s>>>(E, idx, x, n, d, V);
   return hipGetLastError();
 }
 int64_t embed_bwd_scratch_bytes(int64_t n, int d) {
@@ -773,8 +788,8 @@ hipError_t attn_delta(const AttnDesc& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template hipError_t embed_fwd<float>(const float*, const int32_t*, float*, int64_t, int, hipStream_t);
-template hipError_t embed_fwd<bf16>(const bf16*, const int32_t*, bf16*, int64_t, int, hipStream_t);
+template hipError_t embed_fwd<float>(const float*, const int32_t*, float*, int64_t, int, int, hipStream_t);
+template hipError_t embed_fwd<bf16>(const bf16*, const int32_t*, bf16*, int64_t, int, int, hipStream_t);
 template hipError_t embed_bwd<float>(const float*, const int32_t*, float*, int64_t, int, int, int, void*, hipStream_t);
 template hipError_t embed_bwd<bf16>(const bf16*, const int32_t*, float*, int64_t, int, int, int, void*, hipStream_t);
 template hipError_t rmsnorm_fwd<float>(const float*, float*, float*, int64_t, int, float, hipStream_t);
@@ -797,8 +812,8 @@ hipError_t rope_table_at(float2* tab, int t0, int T, int Q, float base, hipStrea
   return hipGetLastError();
 }
 hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int32_t* tgt, float* lse, float* ce,
-                      int64_t rows, hipStream_t s) {
-  k_ce_combine<<<nblocks(rows, 4), 256, 0, s>>>(part, nblk, ztgt, tgt, lse, ce, rows);
+                      int64_t rows, int V, hipStream_t s) {
+  k_ce_combine<<<nblocks(rows, 4), 256, 0, s>>>(part, nblk, ztgt, tgt, lse, ce, rows, V);
   return hipGetLastError();
 }
 template <typename T>
@@ -817,18 +832,18 @@ hipError_t count_valid(const int32_t* tgt, int64_t n, float* inv, hipStream_t s)
   k_count_valid<<<1, 1024, 0, s>>>(tgt, n, inv);
   return hipGetLastError();
 }
-hipError_t row_scale(const int32_t* tgt, const float* w, const float* inv_nvalid, int64_t n, float* out,
+hipError_t row_scale(const int32_t* tgt, const float* w, const float* inv_nvalid, int64_t n, int V, float* out,
                      hipStream_t s) {
-  k_row_scale<<<nblocks(n, 256), 256, 0, s>>>(tgt, w, inv_nvalid, n, out);
+  k_row_scale<<<nblocks(n, 256), 256, 0, s>>>(tgt, w, inv_nvalid, n, V, out);
   return hipGetLastError();
 }
 hipError_t weighted_loss(const float* ce, const int32_t* tgt, const float* w, int64_t n, double* out, hipStream_t s) {
   k_weighted_loss<<<1, 1024, 0, s>>>(ce, tgt, w, n, out);
   return hipGetLastError();
 }
-hipError_t loss_bpb(const float* ce, const int32_t* tgt, const int32_t* bytes, int64_t n, double* out,
+hipError_t loss_bpb(const float* ce, const int32_t* tgt, const int32_t* bytes, int64_t n, int V, double* out,
                     hipStream_t s) {
-  k_loss_bpb<<<1, 1024, 0, s>>>(ce, tgt, bytes, n, out);
+  k_loss_bpb<<<1, 1024, 0, s>>>(ce, tgt, bytes, n, V, out);
   return hipGetLastError();
 }
 hipError_t splitk_reduce(const float* part, int splits, int64_t n, float* out, int beta, hipStream_t s) {

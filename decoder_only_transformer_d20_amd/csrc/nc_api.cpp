@@ -179,6 +179,7 @@ struct nc_ctx {
   bool have_forward = false;
   bool have_block_forward = false;
   bool logits_kept = false;        // plan.zkeep holds the last forward's logits
+  int64_t fallbacks = 0;           // bf16 launches that took a portable kernel (nc_fallback_count)
   std::string err;
   // kernel timing (nc_trace_*)
   int trace_family = -1;
@@ -268,7 +269,11 @@ hipError_t traced(nc_ctx* ctx, int family, double flops, double bytes, F&& launc
 // family < -1: the forward/backward family of the product's layout and epilogue
 hipError_t run_gemm(nc_ctx* ctx, const GemmDesc& g, int family = -2) {
   if (!is_bf16(ctx->cfg)) return gemm_portable<float>(g, ctx->stream);
-  if (portable(ctx->cfg) || !gemm_mfma_supported(g)) return gemm_portable<bf16>(g, ctx->stream);
+  if (portable(ctx->cfg)) return gemm_portable<bf16>(g, ctx->stream);
+  if (!gemm_mfma_supported(g)) {
+    ctx->fallbacks++;
+    return gemm_portable<bf16>(g, ctx->stream);
+  }
   double items = g.batch > 1 ? g.batch : 1;
   if (g.sym) {
     // the tiles on and above the diagonal are computed, the rest mirrored
@@ -331,6 +336,7 @@ template <typename T> hipError_t attn_fwd(nc_ctx* ctx, const AttnDesc& a) {
     return traced(ctx, NC_TRACE_ATTN_FWD, 2 * 2.0 * attn_pairs(a) * a.Q, tok * (3 * d + d) * 2 + tok * a.H * 4,
                   [&] { return attn_fwd_mfma(a, ctx->stream); });
   }
+  if (!portable(ctx->cfg)) ctx->fallbacks++;
   return attn_fwd_portable<T>(a, ctx->stream);
 }
 template <typename T> hipError_t attn_bwd(nc_ctx* ctx, const AttnDesc& a) {
@@ -341,6 +347,7 @@ template <typename T> hipError_t attn_bwd(nc_ctx* ctx, const AttnDesc& a) {
     return traced(ctx, NC_TRACE_ATTN_BWD, 5 * 2.0 * attn_pairs(a) * a.Q, tok * (5 * d + 3 * d) * 2 + tok * a.H * 8,
                   [&] { return attn_bwd_mfma(a, ctx->stream); });
   }
+  if (!portable(ctx->cfg)) ctx->fallbacks++;
   return attn_bwd_portable<T>(a, ctx->stream);
 }
 
@@ -453,7 +460,7 @@ int model_forward(nc_ctx* ctx, const T* params, const int32_t* idx, const int32_
   NC_TRY(copy_bytes(wtgt, tgt, (size_t)N * 4, s), "copy targets");
   NC_TRY(count_valid(wtgt, N, ctx->at<float>(p.scalars), s), "count valid targets");
   T* x = ctx->at<T>(p.x);
-  NC_TRY(embed_fwd<T>(params, widx, x, N, d, s), "embedding gather");
+  NC_TRY(embed_fwd<T>(params, widx, x, N, d, V, s), "embedding gather");
   const T* w = params + (int64_t)V * d;
   for (int l = 0; l < c.n_layer; ++l) {
     int st = layer_forward<T>(ctx, l, w + (int64_t)l * layer_elems(c), x);
@@ -474,7 +481,7 @@ int model_forward(nc_ctx* ctx, const T* params, const int32_t* idx, const int32_
   NC_TRY(run_gemm(ctx, g), "unembedding + log-sum-exp partials");
   ctx->logits_kept = keep_z;
   float* ce = ctx->at<float>(p.ce);
-  NC_TRY(ce_combine(g.lse_part, p.head_nblk, g.ztgt, wtgt, ctx->at<float>(p.lse_head), ce, N, s), "cross-entropy");
+  NC_TRY(ce_combine(g.lse_part, p.head_nblk, g.ztgt, wtgt, ctx->at<float>(p.lse_head), ce, N, V, s), "cross-entropy");
   if (ce_out) NC_TRY(copy_bytes(ce_out, ce, (size_t)N * 4, s), "copy ce");
   return NC_OK;
 }
@@ -499,7 +506,7 @@ int model_backward(nc_ctx* ctx, const T* params, float* grads, int accumulate, c
   // (w = 1 unless token weights are given), dxf = dz U, dU (+)= dz^T xf.
   // (U is transposed once, for every chunk.)
   float* rs = ctx->at<float>(p.rowscale);
-  NC_TRY(row_scale(wtgt, tok_w, ctx->at<float>(p.scalars), N, rs, s), "dz row factors");
+  NC_TRY(row_scale(wtgt, tok_w, ctx->at<float>(p.scalars), N, V, rs, s), "dz row factors");
   GemmDesc gx;
   NC_TRY(dgrad_desc<T>(ctx, 0, dz, V, U, V, d, EPI_STORE, tmp, d, &gx), "transpose U");
   const bool kept_z = ctx->logits_kept;          // then the head runs as one chunk
@@ -805,13 +812,13 @@ int prefill(nc_ctx* ctx, const T* params, const int32_t* idx, int len, int nseq,
   return NC_OK;
 }
 
+// sc: the layout of `scratch` (any layout at least (nseq, pos + 1) large)
 template <typename T>
 int decode(nc_ctx* ctx, const T* params, const int32_t* tokens, int nseq, int pos, T* kv, int mb, int ml,
-           char* scratch, float* logits) {
+           char* scratch, const DecodeScratch& sc, float* logits) {
   const nc_config& c = ctx->cfg;
   const int d = c.d_model, F = c.d_ff, V = c.vocab, H = c.n_head, Q = c.head_dim;
   hipStream_t s = ctx->stream;
-  const DecodeScratch sc = decode_scratch(c, mb, ml);
   T* x = reinterpret_cast<T*>(scratch + sc.x);
   T* a = reinterpret_cast<T*>(scratch + sc.a);
   T* o = reinterpret_cast<T*>(scratch + sc.o);
@@ -820,7 +827,7 @@ int decode(nc_ctx* ctx, const T* params, const int32_t* tokens, int nseq, int po
   float* r = reinterpret_cast<float*>(scratch + sc.r);
   float2* rope = reinterpret_cast<float2*>(scratch + sc.rope);
   float* part = reinterpret_cast<float*>(scratch + sc.part);
-  NC_TRY(embed_fwd<T>(params, tokens, x, nseq, d, s), "decode embedding");
+  NC_TRY(embed_fwd<T>(params, tokens, x, nseq, d, V, s), "decode embedding");
   NC_TRY(rope_table_at(rope, pos, 1, Q, c.rope_base, s), "decode rotary row");
   const int64_t sstride = (int64_t)ml * d, lstride = 2 * (int64_t)mb * sstride;
   const T* w = params + (int64_t)V * d;
@@ -982,6 +989,13 @@ int nc_trace_read(nc_ctx* ctx, int64_t* launches, double* ms, double* flops, dou
 
 const char* nc_last_error(const nc_ctx* ctx) { return ctx ? ctx->err.c_str() : "null context"; }
 
+int nc_fallback_count(nc_ctx* ctx, int64_t* count, int32_t reset) {
+  if (!ctx || !count || (reset != 0 && reset != 1)) return NC_ERR_INVALID_ARG;
+  *count = ctx->fallbacks;
+  if (reset) ctx->fallbacks = 0;
+  return NC_OK;
+}
+
 int nc_forward(nc_ctx* ctx, const void* params, const int32_t* idx, const int32_t* targets, float* ce_out) {
   if (!ctx || !params || !idx || !targets) return NC_ERR_INVALID_ARG;
   if (is_block(ctx->cfg)) return NC_ERR_STATE;
@@ -1007,7 +1021,8 @@ int nc_loss_bpb(nc_ctx* ctx, const int32_t* token_bytes, double* out) {
   if (!ctx->have_forward) return NC_ERR_STATE;
   const Plan& p = ctx->plan;
   const int64_t N = (int64_t)ctx->cfg.batch * ctx->cfg.seq_len;
-  NC_TRY(loss_bpb(ctx->at<float>(p.ce), ctx->at<int32_t>(p.tgt), token_bytes, N, out, ctx->stream), "loss / bpb");
+  NC_TRY(loss_bpb(ctx->at<float>(p.ce), ctx->at<int32_t>(p.tgt), token_bytes, N, ctx->cfg.vocab, out, ctx->stream),
+         "loss / bpb");
   return NC_OK;
 }
 
@@ -1179,11 +1194,12 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t ns
   if (st != NC_OK) return st;
   if (nseq < 1 || nseq > max_batch || pos < 0 || pos >= max_len) return NC_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(scratch) & (kAlign - 1)) return NC_ERR_INVALID_ARG;
+  const DecodeScratch sc = decode_scratch(ctx->cfg, max_batch, max_len);
   return is_bf16(ctx->cfg)
              ? decode<bf16>(ctx, (const bf16*)params, tokens, nseq, pos, (bf16*)kv_cache, max_batch, max_len,
-                            (char*)scratch, logits)
+                            (char*)scratch, sc, logits)
              : decode<float>(ctx, (const float*)params, tokens, nseq, pos, (float*)kv_cache, max_batch, max_len,
-                             (char*)scratch, logits);
+                             (char*)scratch, sc, logits);
 }
 
 }  // extern "C"

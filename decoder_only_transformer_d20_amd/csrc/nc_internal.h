@@ -123,7 +123,9 @@ hipError_t attn_fwd_mfma(const AttnDesc& a, hipStream_t s);
 hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s);
 template <typename T> hipError_t attn_delta(const AttnDesc& a, hipStream_t s);
 
-template <typename T> hipError_t embed_fwd(const T* E, const int32_t* idx, T* x, int64_t n, int d, hipStream_t s);
+// x[n] = E[idx[n]]; an id outside [0, V) gives a NaN row (no read)
+template <typename T> hipError_t embed_fwd(const T* E, const int32_t* idx, T* x, int64_t n, int d, int V,
+                                           hipStream_t s);
 // dE [V][d] (accumulate ? += : =) per-id sums of g rows, deterministic (sort
 // by id, ordered sums); scratch of embed_bwd_scratch_bytes(n, d) bytes
 int64_t embed_bwd_scratch_bytes(int64_t n, int d);
@@ -135,8 +137,9 @@ template <typename T> hipError_t rmsnorm_bwd(const T* y, const float* r, const T
 hipError_t rope_table(float2* tab, int T, int Q, float base, hipStream_t s);
 // rows t0 .. t0+T-1 of the same table (same fp64 angles)
 hipError_t rope_table_at(float2* tab, int t0, int T, int Q, float base, hipStream_t s);
+// ce = 0 for an ignored target, NaN for a target >= V
 hipError_t ce_combine(const float2* part, int nblk, const float* ztgt, const int32_t* tgt,
-                      float* lse, float* ce, int64_t rows, hipStream_t s);
+                      float* lse, float* ce, int64_t rows, int V, hipStream_t s);
 // dz [rows][V] = (softmax(z) - onehot(tgt)) * rs from z [rows][V] written by
 // an EPI_LSEZ product (z relative to its tile's row max, the tile width
 // tile_w and per-tile maxima from part [rows][nblk]); the target column is
@@ -145,12 +148,13 @@ template <typename T>
 hipError_t dz_from_logits(const T* z, T* dz, int64_t rows, int V, int tile_w, const float2* part, int nblk,
                           const float* ztgt, const int32_t* tgt, const float* lse, const float* rs, hipStream_t s);
 hipError_t count_valid(const int32_t* tgt, int64_t n, float* inv_nvalid, hipStream_t s);
-// out[i] = tgt[i] >= 0 ? *inv_nvalid * (w ? w[i] : 1) : 0
-hipError_t row_scale(const int32_t* tgt, const float* w, const float* inv_nvalid, int64_t n, float* out,
+// out[i] = tgt[i] >= 0 ? *inv_nvalid * (w ? w[i] : 1) : 0 (NaN for tgt[i] >= V)
+hipError_t row_scale(const int32_t* tgt, const float* w, const float* inv_nvalid, int64_t n, int V, float* out,
                      hipStream_t s);
 // out = {sum over valid targets of w ce, that sum / n_valid}, fp64, fixed order
 hipError_t weighted_loss(const float* ce, const int32_t* tgt, const float* w, int64_t n, double* out, hipStream_t s);
-hipError_t loss_bpb(const float* ce, const int32_t* tgt, const int32_t* bytes, int64_t n, double* out, hipStream_t s);
+hipError_t loss_bpb(const float* ce, const int32_t* tgt, const int32_t* bytes, int64_t n, int V, double* out,
+                    hipStream_t s);
 hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
 // out [cols][rows] = transpose of in [rows][cols]; rows, cols multiples of 8
 hipError_t transpose_bf16(const bf16* in, int64_t rows, int64_t cols, bf16* out, hipStream_t s);

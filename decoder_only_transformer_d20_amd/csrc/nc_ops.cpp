@@ -144,13 +144,13 @@ int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t 
   return status_of(portable ? attn_bwd_portable<bf16>(a, s) : attn_bwd_mfma(a, s));
 }
 
-int nc_op_embed_fwd(int32_t dtype, int64_t n, int32_t d, const void* E, const int32_t* idx, void* x,
+int nc_op_embed_fwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void* E, const int32_t* idx, void* x,
                     void* hip_stream) {
   if (!dtype_ok(dtype) || !E || !idx || !x) return NC_ERR_INVALID_ARG;
-  if (n <= 0 || d <= 0 || d % 64) return NC_ERR_SHAPE;
+  if (n <= 0 || d <= 0 || d % 64 || V <= 0) return NC_ERR_SHAPE;
   hipStream_t s = (hipStream_t)hip_stream;
-  return status_of(dtype == NC_DTYPE_F32 ? embed_fwd<float>((const float*)E, idx, (float*)x, n, d, s)
-                                         : embed_fwd<bf16>((const bf16*)E, idx, (bf16*)x, n, d, s));
+  return status_of(dtype == NC_DTYPE_F32 ? embed_fwd<float>((const float*)E, idx, (float*)x, n, d, V, s)
+                                         : embed_fwd<bf16>((const bf16*)E, idx, (bf16*)x, n, d, V, s));
 }
 
 int64_t nc_op_embed_bwd_scratch_bytes(int64_t n, int32_t d) {
@@ -191,7 +191,7 @@ int nc_op_head_ce_fwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void
   g.ztgt = (float*)((char*)scratch + n * nblk * 8);
   hipStream_t s = (hipStream_t)hip_stream;
   hipError_t e = dispatch_gemm(dtype, portable, g, s);
-  if (e == hipSuccess) e = ce_combine(g.lse_part, nblk, g.ztgt, tgt, lse, ce, n, s);
+  if (e == hipSuccess) e = ce_combine(g.lse_part, nblk, g.ztgt, tgt, lse, ce, n, V, s);
   return status_of(e);
 }
 

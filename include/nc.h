@@ -130,6 +130,16 @@ void nc_destroy(nc_ctx* ctx);
 /* Text of the last error on this context ("" if none). */
 const char* nc_last_error(const nc_ctx* ctx);
 
+/* In bf16 mode without NC_FLAG_PORTABLE_KERNELS every product and attention
+ * call runs on the matrix-core kernels when its shape allows (products:
+ * sizes the MFMA tiles cover; attention: head dim 128 and T a multiple of
+ * 128); any other shape runs the portable (non-MFMA) kernel instead, with
+ * the same results to rounding but far slower.  *count receives how many
+ * launches on this context took that fallback since it was created or last
+ * reset (reset = 1 zeroes it after reading).  Host-only; fp32 contexts and
+ * NC_FLAG_PORTABLE_KERNELS contexts always count 0. */
+int nc_fallback_count(nc_ctx* ctx, int64_t* count, int32_t reset);
+
 /* ---- full model ------------------------------------------------------------ */
 
 /* Forward pass over B x T tokens.
@@ -139,8 +149,14 @@ const char* nc_last_error(const nc_ctx* ctx);
  *   ce_out  device fp32 [B*T] per-token cross-entropy in nats (0 where the
  *           target is ignored), or NULL
  * idx and targets are copied into the workspace, and every activation the
- * backward pass needs is saved there.  Ids outside [0, V) are undefined
- * behaviour.  Not available in block-only mode (NC_ERR_STATE). */
+ * backward pass needs is saved there.  An id outside [0, V) (or a target
+ * >= V) is an error the library does not check on the host (the ids are in
+ * device memory): nothing is read out of bounds for it, and NaN is written
+ * into what depends on it -- the embedding row of a bad id (and from it the
+ * activations of its row: attention products may carry it to other
+ * positions of the row), the ce of a bad target, so also the loss, bits per
+ * byte and gradients -- which shows after the stream is synchronised.  Not available in block-only mode
+ * (NC_ERR_STATE). */
 int nc_forward(nc_ctx* ctx, const void* params, const int32_t* idx,
                const int32_t* targets, float* ce_out);
 
@@ -212,7 +228,9 @@ int nc_prefill(nc_ctx* ctx, const void* params, const int32_t* idx, int32_t prom
 /* Decode: one new token per sequence, tokens device int32 [nseq], all at
  * position pos (the sequences' common length so far; 0 <= pos < max_len).
  * Appends each token's K, V at pos and writes fp32 logits [nseq][V] of the
- * next token.  Uses only the scratch (not the context's workspace). */
+ * next token.  Uses only the scratch (not the context's workspace).  A
+ * token outside [0, V) reads nothing and makes its sequence's logits (and
+ * the K, V it appends) NaN. */
 int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t nseq, int32_t pos, void* kv_cache,
               int32_t max_batch, int32_t max_len, void* scratch, float* logits);
 

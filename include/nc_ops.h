@@ -107,8 +107,8 @@ int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t 
                         int32_t portable, void* hip_stream);
 
 /* Embedding gather x[n] = E[idx[n]] (T [V][d] -> T [n][d]), a bitwise row
- * copy; idx must lie in [0, V). */
-int nc_op_embed_fwd(int32_t dtype, int64_t n, int32_t d, const void* E, const int32_t* idx, void* x,
+ * copy.  An id outside [0, V) reads nothing: its row of x is all NaN. */
+int nc_op_embed_fwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void* E, const int32_t* idx, void* x,
                     void* hip_stream);
 
 /* Embedding gradient, the transpose of the gather: for every v in [0, V),
@@ -126,7 +126,8 @@ int nc_op_embed_bwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void* 
                     int32_t accumulate, void* scratch, void* hip_stream);
 
 /* Fused unembedding + log-softmax + cross-entropy, forward only:
- * ce[n] = logsumexp_v(xf[n] . U[v]) - xf[n] . U[tgt[n]] (0 where tgt < 0),
+ * ce[n] = logsumexp_v(xf[n] . U[v]) - xf[n] . U[tgt[n]] (0 where tgt < 0,
+ * NaN where tgt >= V),
  * lse[n] the log-sum-exp, without storing the logits.
  *   xf T [n][d], U T [V][d], tgt int32 [n], ce, lse fp32 [n]
  *   scratch: fp32 device scratch of nc_op_head_scratch_bytes(...) bytes */

@@ -119,6 +119,20 @@ def test_decode_rejects_bad_shapes():
     assert e.value.status == -2
 
 
+def test_decode_bad_token_gives_nan_logits_for_its_sequence():
+    """A token outside [0, V) is read nowhere: its sequence's logits are
+    NaN, the other sequences' logits equal a run without it, bit for bit."""
+    cfg = synthdata.get_config("small")
+    params = synthdata.make_params(cfg)
+    prompt, gen = _tokens(cfg, 60, 3, 1, 54)
+    l0, good = _run(cfg, params, prompt, gen, 3)
+    bad = gen.copy()
+    bad[1, 0] = cfg.vocab + 11
+    _, got = _run(cfg, params, prompt, bad, 3)
+    assert np.all(np.isnan(got[0][1]))
+    np.testing.assert_array_equal(got[0][[0, 2]], good[0][[0, 2]])
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_d20_decode_matches_forward():

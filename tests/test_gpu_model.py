@@ -88,6 +88,32 @@ def test_tiny_no_valid_target():
     assert not np.any(got["grads"])
 
 
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_out_of_range_ids_give_nan_not_out_of_bounds_reads(name):
+    """An id outside [0, V) or a target >= V is read nowhere: the bad id's
+    embedding row is NaN, so the ce from its position on in that row is NaN
+    (earlier positions of the same attention tile may be too: a masked
+    score still multiplies the NaN value row, 0 * NaN = NaN, in the
+    matrix-core product), a bad target's ce is NaN, and so are the loss,
+    bpb and the gradient.  Rows without a bad entry are unaffected."""
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config(name))
+    V = cfg.vocab
+    idx, tgt = idx.copy(), tgt.copy()
+    idx[0, 5] = V + 3
+    tgt[1, 7] = V
+    idx[1, 2] = -7 if cfg.batch > 2 else idx[1, 2]
+    got = _gpu_step(cfg, params, idx, tgt, tb)
+    ce = got["ce"]
+    assert np.all(np.isnan(ce[0, 5:]))
+    assert np.isnan(ce[1, 7])
+    assert np.isnan(got["out"][0]) and np.isnan(got["out"][1])
+    assert np.any(np.isnan(got["grads"]))
+    if cfg.batch > 2:
+        good = _gpu_step(cfg.with_(batch=cfg.batch - 2), params, idx[2:], tgt[2:], tb, grads=False)
+        assert np.all(np.isfinite(ce[2:]))
+        np.testing.assert_allclose(ce[2:], good["ce"], rtol=1e-3, atol=1e-3)
+
+
 def test_tiny_fp32_accumulate_doubles():
     cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("tiny"))
     sess = nc.Session(cfg)
@@ -193,7 +219,8 @@ def test_head_in_two_chunks_matches_one_row():
     factor 1/2048 as an unweighted single row): the gradient must equal the
     single-row step's, which keeps its logits.  Row 32 lies in the second
     chunk.  The two runs differ in product shapes (tiles, split-K) and in how
-    dz is formed, so the bar is cosine >= 0.9999 per tensor."""
+    dz is formed, so the bar is cosine >= 0.9999 per tensor; against the
+    oracle's gradient over row 32 the bar is the bf16 one (0.999)."""
     base = synthdata.get_config("small")
     cfg = base.with_(batch=33, seq_len=2048)
     params = _params(cfg)
@@ -206,12 +233,18 @@ def test_head_in_two_chunks_matches_one_row():
     assert out_big[0] == pytest.approx(33.0 * out_one[0], rel=1e-3)
     for (name, layer, a), (_, _, b) in zip(flat_tensors(cfg, g_big), flat_tensors(cfg, g_one)):
         assert cosine(a, b) >= 0.9999, (name, layer, cosine(a, b))
+    # and the recomputed-logit gradient against the oracle on row 32
+    tb = synthdata.make_token_bytes(cfg)
+    want = _oracle_step(cfg, params, idx, tgt, tb, rows=[32], token_weights=w.astype(np.float64))
+    for (name, layer, a), (_, _, b) in zip(flat_tensors(cfg, g_big), flat_tensors(cfg, want["grads"])):
+        assert cosine(a, b) >= 0.999, (name, layer, cosine(a, b))
 
 
 def test_forward_eval_same_results_and_backward_recomputes():
     """nc_forward_eval gives nc_forward's ce and loss bit for bit; a backward
-    after it recomputes the logits instead of reading a kept copy, and its
-    gradient matches the one after nc_forward to the bf16 bar."""
+    after it recomputes the logits instead of reading a kept copy; its
+    gradient matches the one after nc_forward, and the oracle's, to the
+    bf16 bar."""
     cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("small"), ignore=[(1, 7)])
     sess = nc.Session(cfg)
     P, I, Tg, TB = dev(params, cfg.dtype), dev(idx.ravel()), dev(tgt.ravel()), dev(tb)
@@ -227,6 +260,10 @@ def test_forward_eval_same_results_and_backward_recomputes():
     np.testing.assert_array_equal(res[0][1], res[1][1])
     for (name, layer, a), (_, _, b) in zip(flat_tensors(cfg, res[0][2]), flat_tensors(cfg, res[1][2])):
         assert cosine(a, b) >= 0.9999, (name, layer, cosine(a, b))
+    # the recomputing path against the oracle at the bf16 bar
+    want = _oracle_step(cfg, params, idx, tgt, tb)
+    for (name, layer, a), (_, _, b) in zip(flat_tensors(cfg, res[1][2]), flat_tensors(cfg, want["grads"])):
+        assert cosine(a, b) >= 0.999, (name, layer, cosine(a, b))
 
 
 def test_small_bf16_deterministic():
@@ -257,6 +294,7 @@ def test_small_bf16_every_product_on_matrix_cores():
         n, ms, fl, by = sess.trace_read()
         assert n > 0 and ms > 0 and fl > 0, fam
     sess.trace_enable(None)
+    assert sess.fallback_count() == 0
 
 
 def _block_inputs(rows):
@@ -293,17 +331,28 @@ def test_block_real_shape_two_rows():
 
 @pytest.mark.slow
 @pytest.mark.timeout(600)
-def test_block_full_batch_sampled_rows():
-    """The block at the full 32 x 2048 launch; rows 0 and 31 against the
-    oracle (rows are independent in y and dx)."""
+def test_block_full_batch_matches_oracle_on_two_rows():
+    """The block at the full 32 x 2048 launch, with the upstream gradient dy
+    zero except on rows 0 and 31.  Rows never interact, so y and dx of those
+    rows and every weight gradient (a sum over rows, to which only rows 0
+    and 31 contribute) equal the oracle's block step on those two rows; dx
+    of every other row is exactly 0.  The weight gradients run at
+    K = 65,536 tokens with the full launch's split-K."""
     cfg, params, x, dy = _block_inputs(rows=None)
-    y, dx, g = _gpu_block(cfg, params, x, dy)
+    keep = [0, 31]
+    dy0 = np.zeros_like(dy)
+    dy0[keep] = dy[keep]
+    y, dx, g = _gpu_block(cfg, params, x, dy0)
     lp = synthdata.split_params(cfg, params)["layers"][0]
-    want = oracle.block_step(cfg, lp, x[[0, 31]], dy[[0, 31]])
-    for i, b in enumerate((0, 31)):
+    want = oracle.block_step(cfg, lp, x[keep], dy[keep])
+    for i, b in enumerate(keep):
         assert cosine(y[b] - x[b], want["y"][i] - x[b]) >= 0.999
         assert cosine(dx[b], want["dx"][i]) >= 0.999
-    assert np.all(np.isfinite(g))
+    others = np.ones(x.shape[0], bool)
+    others[keep] = False
+    assert not np.any(dx[others])
+    for name, layer, gt in flat_tensors(cfg, g):
+        assert cosine(gt, want["grads"][name]) >= 0.999, (name, cosine(gt, want["grads"][name]))
 
 
 @pytest.mark.slow
@@ -339,6 +388,53 @@ def test_d20_full_batch_consistency():
     assert abs(full["out"][0] - math.log(cfg.vocab)) < 2.0
 
 
+def _full_batch_two_rows(name, keep):
+    """The full launch of a configuration with token weights B/len(keep) on
+    the rows in ``keep`` and 0 elsewhere: sum_t w_t ce[t] / n_valid is then
+    the mean ce over those rows, and its gradient is the oracle's over just
+    those rows (rows never interact).  Every product still runs at the
+    launch's full shape: the kept-logits dz over B*T x V, dU and the weight
+    gradients at K = B*T with their split-K, the embedding gradient over all
+    B*T ids (the Zipf-hot ids included; the other rows add exact zeros)."""
+    cfg, params, idx, tgt, tb = _inputs(synthdata.get_config(name))
+    B = idx.shape[0]
+    w = np.zeros(tgt.shape, dtype=np.float32)
+    w[keep] = B / len(keep)
+    sess = nc.Session(cfg)
+    P = dev(params, cfg.dtype)
+    ce, out, wout = empty((idx.size,), "f32"), empty((5,), "f64"), empty((2,), "f64")
+    g = empty((params.size,), "f32")
+    sess.forward(P, dev(idx.ravel()), dev(tgt.ravel()), ce)
+    sess.loss_bpb(dev(tb), out)
+    W = dev(w)
+    sess.loss_weighted(W, wout)
+    sess.backward_weighted(P, g, W)
+    torch.cuda.synchronize()
+    assert sess.fallback_count() == 0          # every product and attention call on matrix cores
+    got_ce, got_out, got_w, got_g = host(ce).reshape(idx.shape), host(out), host(wout), host(g)
+    del g, P, sess
+    torch.cuda.empty_cache()
+    want = _oracle_step(cfg, params, idx, tgt, tb, rows=keep, token_weights=w.astype(np.float64))
+    # per-token ce of the compared rows, and the weighted loss = their mean
+    assert np.max(np.abs(got_ce[keep] - want["ce"][keep])) <= 0.05
+    mean_ce = float(want["ce"][keep].mean())
+    assert abs(got_w[1] - mean_ce) / mean_ce <= 1e-2
+    # loss and bpb of the whole batch follow from the GPU's own per-token ce
+    s = got_ce.astype(np.float64).sum()
+    assert got_out[0] == pytest.approx(s / idx.size, rel=1e-9)
+    assert got_out[1] == pytest.approx(s / (math.log(2) * tb[tgt].sum()), rel=1e-9)
+    for (tname, layer, a), (_, _, b) in zip(flat_tensors(cfg, got_g), flat_tensors(cfg, want["grads"])):
+        assert cosine(a, b) >= 0.999, (tname, layer, cosine(a, b))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_d20_full_batch_gradients_match_oracle():
+    """The benchmarked launch (d20, 32 x 2048 tokens): every parameter
+    gradient against the oracle, through rows 0 and 31 (weight 16 each)."""
+    _full_batch_two_rows("d20", [0, 31])
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_d30_one_row_matches_oracle():
@@ -352,6 +448,14 @@ def test_d30_one_row_matches_oracle():
     assert abs(got["out"][1] - want["bpb"]) / want["bpb"] <= 1e-2
     for (name, layer, g), (_, _, w) in zip(flat_tensors(cfg, got["grads"]), flat_tensors(cfg, want["grads"])):
         assert cosine(g, w) >= 0.999, (name, layer, cosine(g, w))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_d30_full_batch_gradients_match_oracle():
+    """The d30 launch (16 x 2048 tokens): every parameter gradient against
+    the oracle, through row 15 (weight 16)."""
+    _full_batch_two_rows("d30", [15])
 
 
 @pytest.mark.slow

@@ -235,6 +235,7 @@ ATT_CASES = [
     ("bf16", 1, 2, 192, 2, 128),
     ("bf16", 0, 2, 256, 2, 128),
     ("bf16", 0, 1, 640, 3, 128),
+    ("bf16", 0, 1, 2048, 10, 128),   # one row of the d20 launch: every head, full row length
 ]
 
 
@@ -300,11 +301,13 @@ def test_attention_bwd(dtype, portable, B, T, H, Q, with_rope):
 # embedding
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype,d,V,n", [("f32", 128, 512, 1000), ("bf16", 1280, 512, 1000),
-                                         ("bf16", 192, 65536, 5000), ("f32", 64, 300, 1)])
+                                         ("bf16", 192, 65536, 5000), ("f32", 64, 300, 1),
+                                         ("bf16", 1280, 65536, 65536)])   # the d20 launch: id 0 ~9k times
 def test_embedding_gather_bitwise_and_gradient(dtype, d, V, n):
-    """Gather is a bitwise row copy; the gradient (a per-id sum of rows) is
-    checked against an fp64 np.add.at, with and without accumulation, with
-    ids outside [0, V) dropped, and is bitwise identical across calls."""
+    """Gather is a bitwise row copy (an id outside [0, V) gives a NaN row);
+    the gradient (a per-id sum of rows) is checked against an fp64
+    np.add.at, with and without accumulation, with ids outside [0, V)
+    dropped, and is bitwise identical across calls."""
     rng = np.random.default_rng(30)
     E = rng.standard_normal((V, d)).astype(np.float32)
     if dtype == "bf16":
@@ -312,9 +315,18 @@ def test_embedding_gather_bitwise_and_gradient(dtype, d, V, n):
     cfg = synthdata.get_config("d20")
     idx = (synthdata.make_tokens(cfg.with_(batch=1, seq_len=max(n, 2)), rows=1)[0].ravel()[:n] % V).astype(np.int32)
     x = empty((n, d), dtype)
-    nc.ops.embed_fwd(DT[dtype], n, d, dev(E, dtype), dev(idx), x, None)
+    nc.ops.embed_fwd(DT[dtype], n, d, V, dev(E, dtype), dev(idx), x, None)
     _sync()
     np.testing.assert_array_equal(host(x, dtype), E[idx])
+    if n > 4:
+        oob = idx.copy()
+        oob[2], oob[4] = V, -1
+        nc.ops.embed_fwd(DT[dtype], n, d, V, dev(E, dtype), dev(oob), x, None)
+        _sync()
+        xo = host(x, dtype)
+        assert np.all(np.isnan(xo[[2, 4]]))
+        keep = np.setdiff1d(np.arange(n), [2, 4])
+        np.testing.assert_array_equal(xo[keep], E[oob[keep]])
     g = rng.standard_normal((n, d)).astype(np.float32)
     if dtype == "bf16":
         g = synthdata.round_to_bf16(g)
