@@ -16,7 +16,7 @@ __all__ = [
     "param_offset", "workspace_bytes", "status_string", "ops", "LIB_PATH",
     "DTYPE_F32", "DTYPE_BF16", "FLAG_BLOCK_ONLY", "FLAG_PORTABLE_KERNELS",
     "NcOptimHparams", "optim_default", "optim_state_bytes", "optim_scratch_bytes",
-    "kv_cache_bytes", "decode_scratch_bytes", "sample",
+    "kv_cache_bytes", "decode_scratch_bytes", "decode_static_max_bytes", "sample",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnc.so")
@@ -81,6 +81,8 @@ _SIGS = {
     "nc_decode_scratch_bytes": (_I64, [ctypes.POINTER(NcConfig), _I32, _I32]),
     "nc_prefill": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, _I32, _P]),
     "nc_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, _I32, _P, _P]),
+    "nc_decode_static_max_bytes": (_I64, []),
+    "nc_decode_static": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, _I32, _P]),
     "nc_loss_weighted": (ctypes.c_int, [_P, _P, _P]),
     "nc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "nc_init": (ctypes.c_int, [ctypes.POINTER(NcConfig), _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
@@ -229,6 +231,11 @@ def decode_scratch_bytes(cfg, max_batch: int, max_len: int) -> int:
     return n
 
 
+def decode_static_max_bytes() -> int:
+    """Size of the static scratch nc_decode_static uses (host-only query)."""
+    return lib().nc_decode_static_max_bytes()
+
+
 def _ptr(x):
     if x is None:
         return None
@@ -291,6 +298,12 @@ class Context:
         """nc_decode: one token per sequence at position pos, next-token logits."""
         _check(lib().nc_decode(self.h, _ptr(params), _ptr(tokens), int(nseq), int(pos), _ptr(kv_cache),
                                int(max_batch), int(max_len), _ptr(scratch), _ptr(logits)), "nc_decode", self.h)
+
+    def decode_static(self, params, tokens, nseq: int, pos: int, kv_cache, max_batch: int, max_len: int, logits):
+        """nc_decode_static: nc_decode with the library's static device
+        scratch (no scratch argument, nothing allocated)."""
+        _check(lib().nc_decode_static(self.h, _ptr(params), _ptr(tokens), int(nseq), int(pos), _ptr(kv_cache),
+                                      int(max_batch), int(max_len), _ptr(logits)), "nc_decode_static", self.h)
 
     def fallback_count(self, reset: bool = False) -> int:
         """nc_fallback_count: bf16 launches that took a portable kernel."""

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -180,6 +181,8 @@ struct nc_ctx {
   bool have_block_forward = false;
   bool logits_kept = false;        // plan.zkeep holds the last forward's logits
   int64_t fallbacks = 0;           // bf16 launches that took a portable kernel (nc_fallback_count)
+  void* static_scratch = nullptr;  // this device's nc_decode_static scratch
+  std::string static_scratch_err;
   std::string err;
   // kernel timing (nc_trace_*)
   int trace_family = -1;
@@ -873,6 +876,37 @@ int decode(nc_ctx* ctx, const T* params, const int32_t* tokens, int nseq, int po
   return NC_OK;
 }
 
+// ---- allocation-free decode (nc_decode_static) -------------------------------
+// The scratch lives in a file-scope device array: every GPU the library runs
+// on holds its own copy from the code object's load until the process ends.
+// In host code the array's name is only a host-side stand-in, never a device
+// address: host code uses the address hipGetSymbolAddress returns, looked up
+// once per device (with that device current) and kept per device.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char nc_static_decode_scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices];
+
+// the calling thread's current device's copy of the array
+hipError_t static_scratch_address(void** out) {
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(nc_static_decode_scratch));
+    if (e != hipSuccess) return e;
+    g_static_ptr[dev] = p;
+  }
+  *out = g_static_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -949,6 +983,10 @@ int nc_init(const nc_config* cfg, void* workspace, size_t ws_bytes, void* hip_st
     delete ctx;
     return NC_ERR_HIP;
   }
+  // the device address of this device's static decode scratch; a failure
+  // here only disables nc_decode_static on this context
+  const hipError_t se = static_scratch_address(&ctx->static_scratch);
+  if (se != hipSuccess) ctx->static_scratch_err = hipGetErrorString(se);
   *out = ctx;
   return NC_OK;
 }
@@ -1200,6 +1238,34 @@ int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t ns
                             (char*)scratch, sc, logits)
              : decode<float>(ctx, (const float*)params, tokens, nseq, pos, (float*)kv_cache, max_batch, max_len,
                              (char*)scratch, sc, logits);
+}
+
+int64_t nc_decode_static_max_bytes(void) { return (int64_t)kStaticScratchBytes; }
+
+int nc_decode_static(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t nseq, int32_t pos,
+                     void* kv_cache, int32_t max_batch, int32_t max_len, float* logits) {
+  if (!ctx || !params || !tokens || !kv_cache || !logits) return NC_ERR_INVALID_ARG;
+  int st = kv_shape_ok(ctx->cfg, max_batch, max_len);
+  if (st != NC_OK) return st;
+  if (nseq < 1 || nseq > max_batch || pos < 0 || pos >= max_len) return NC_ERR_SHAPE;
+  // the scratch is laid out for this call's own size (nseq sequences,
+  // pos + 1 cached positions), not for the cache's maximum
+  const DecodeScratch sc = decode_scratch(ctx->cfg, nseq, pos + 1);
+  if (sc.total > kStaticScratchBytes) {
+    ctx->err = "nc_decode_static: this call needs " + std::to_string(sc.total) +
+               " bytes of scratch, more than the static maximum of " + std::to_string(kStaticScratchBytes);
+    return NC_ERR_WORKSPACE;
+  }
+  if (!ctx->static_scratch) {
+    ctx->err = "nc_decode_static: the static scratch's device address is unknown: " + ctx->static_scratch_err;
+    return NC_ERR_HIP;
+  }
+  char* scratch = (char*)ctx->static_scratch;
+  return is_bf16(ctx->cfg)
+             ? decode<bf16>(ctx, (const bf16*)params, tokens, nseq, pos, (bf16*)kv_cache, max_batch, max_len,
+                            scratch, sc, logits)
+             : decode<float>(ctx, (const float*)params, tokens, nseq, pos, (float*)kv_cache, max_batch, max_len,
+                             scratch, sc, logits);
 }
 
 }  // extern "C"

@@ -234,6 +234,23 @@ int nc_prefill(nc_ctx* ctx, const void* params, const int32_t* idx, int32_t prom
 int nc_decode(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t nseq, int32_t pos, void* kv_cache,
               int32_t max_batch, int32_t max_len, void* scratch, float* logits);
 
+/* nc_decode for callers that cannot allocate device memory or pass a
+ * scratch buffer (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results, bit for
+ * bit, with the scratch taken from a static device array of
+ * nc_decode_static_max_bytes() bytes (16 MiB) that every GPU the library
+ * runs on holds until the process ends.  The call allocates nothing.  Its
+ * scratch is laid out for this call's size, (nseq, pos + 1), so it serves,
+ * e.g., d20 with 16 sequences up to ~12k cached positions; a call needing
+ * more returns NC_ERR_WORKSPACE (message in nc_last_error) before any
+ * launch.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (several streams, several contexts) race and must be
+ * serialised by the caller.  No part of the array needs to start at zero:
+ * every call writes what it reads.  Otherwise as nc_decode. */
+int64_t nc_decode_static_max_bytes(void);
+int nc_decode_static(nc_ctx* ctx, const void* params, const int32_t* tokens, int32_t nseq, int32_t pos,
+                     void* kv_cache, int32_t max_batch, int32_t max_len, float* logits);
+
 /* Next token of each row of logits device fp32 [n][V], as the Engine
  * samples: the largest logit (first id on ties) when temperature == 0;
  * otherwise p_i proportional to exp((z_i - max z) / temperature) over the
