@@ -1,7 +1,7 @@
 """Benchmark: one d20 training step (forward + loss/bpb + backward) per step on
 one MI355X, through the C ABI (include/nc.h).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d20]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d20|d30|block]
                     [--no-cpu-baseline] [--no-roofline] [--copy-calibration]
                     [--mfma-calibration] [--optimizer] [--decode [--decode-nseq 1,8,16]]
                     [--library-gemm]
@@ -397,7 +397,8 @@ def main():
 
     cfg = synthdata.get_config(args.config)
     if cfg.block_only:
-        sys.exit("bench.py times the full model; use a model configuration")
+        block_bench(args, cfg)
+        return
     bf16 = cfg.dtype == "bf16"
     N = cfg.batch * cfg.seq_len
     t0 = time.time()
@@ -529,6 +530,72 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, params, idx, tgt, tb, args.cpu_sample_tokens)
     print(json.dumps(result), flush=True)
+
+
+def block_bench(args, cfg):
+    """One d20 layer at its real shape (32 x 2048 tokens, bf16): forward +
+    backward of the block (nc_block_forward + nc_block_backward) per step,
+    seeded N(0,1) input activations and upstream gradients."""
+    import numpy as np
+    import torch
+    import synthdata
+    import decoder_only_transformer_d20_amd as nc
+    from decoder_only_transformer_d20_amd.flops import flops_per_step
+    N = cfg.batch * cfg.seq_len
+    params = synthdata.make_params(cfg)
+    x, dy = synthdata.make_block_io(cfg)
+    sess = nc.Session(cfg)
+    stream = sess.stream
+    P, X, DY = to_dev(params, True), to_dev(x.reshape(N, -1), True), to_dev(dy.reshape(N, -1), True)
+    Y, DX = torch.empty_like(X), torch.empty_like(X)
+    G = torch.empty(params.size, dtype=torch.float32, device="cuda")
+
+    def step():
+        sess.block_forward(P, X, Y)
+        sess.block_backward(P, DY, DX, G)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    families = {}
+    for f in nc.TRACE_FAMILIES:
+        sess.trace_enable(f)
+        step()
+        n, ms, fl, by = sess.trace_read()
+        if n:
+            families[f] = {"launches": n, "ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+    sess.trace_enable(None)
+    single = [f for f in families if f in nc.SINGLE_KERNEL_FAMILIES]
+    dominant = max(single, key=lambda f: families[f]["ms"])
+    sess.trace_enable(dominant)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    n, tms, fl, by = sess.trace_read()
+    sess.trace_enable(None)
+    achieved = fl / n / (tms / n * 1e-3) / 1e12
+    mfu = flops_per_step(cfg) / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
+    print(f"[bench] block: {ms:.3f} ms/step, MFU {mfu:.3f}", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "train tokens/s + MFU (fwd+bwd) of one d20 block on 1 MI355X, 32x2048 tok/step",
+        "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "ms_per_step_min": round(per_step[0], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) activations and upstream gradients, N(0,1/sqrt(fan_in)) weights)",
+        "config": {"workload": f"one d20 block: d{cfg.d_model}, {cfg.n_head}x{cfg.head_dim} heads, MLP {cfg.d_ff}, "
+                               f"forward + backward", "global_batch": cfg.batch, "seq_len": cfg.seq_len,
+                   "tokens_per_step": N, "parallelism": "none (1 GPU)"},
+        "mfu": round(mfu, 4), "model_flops_per_step": flops_per_step(cfg),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel_family": dominant,
+                     "launches_timed": n, "avg_launch_ms": round(tms / n, 4), "flops_per_launch": fl / n},
+        "kernel_families": families}), flush=True)
 
 
 def cpu_baseline(cfg, params, idx, tgt, tb, sample_tokens):

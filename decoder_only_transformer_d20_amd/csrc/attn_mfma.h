@@ -108,6 +108,40 @@ __device__ inline bf16x8 frag_tr(const char* img, uint32_t lo, uint32_t hi) {
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef __attribute__((address_space(1))) void* gbl_vptr;
+
+// Natural image of 64 rows x 128 of one head (row stride ld elements),
+// copied from global memory straight into LDS by the 4 waves of a block
+// (gfx950's global_load_lds_dwordx4: lane L of a wave's load writes the
+// 16 bytes at LDS offset 16 L past the wave-uniform base).  Wave w's four
+// 1 KB pieces hold rows 16w .. 16w+15; lane L of piece i lands in slot
+// L & 15 of row 16w + 4i + L/16, so it reads the chunk that the swizzle puts
+// in that slot.  Completion is waited for with vm_wait() before the barrier
+// that publishes the image.
+__device__ inline void dma_nat64(const bf16* src, int64_t ld, char* img, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * wave + 4 * i + (lane >> 4);
+    const int chunk = (lane & 15) ^ (int)swz(row);
+    __builtin_amdgcn_global_load_lds((gbl_vptr)(src + (int64_t)row * ld + chunk * 8),
+                                     (lds_vptr)(img + (16 * wave + 4 * i) * 256), 16, 0, 0);
+  }
+}
+// The same for a block of NW waves copying `rows` (a multiple of 4 NW) rows:
+// wave w takes rows w * rows / NW .. in 1 KB pieces of 4 rows.
+template <int NW>
+__device__ inline void dma_rows(const bf16* src, int64_t ld, char* img, int rows, int wave, int lane) {
+  const int per = rows / NW, r0 = wave * per;
+  for (int i = 0; i < per; i += 4) {
+    const int row = r0 + i + (lane >> 4);
+    const int chunk = (lane & 15) ^ (int)swz(row);
+    __builtin_amdgcn_global_load_lds((gbl_vptr)(src + (int64_t)row * ld + chunk * 8),
+                                     (lds_vptr)(img + (r0 + i) * 256), 16, 0, 0);
+  }
+}
+__device__ inline void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // 8 consecutive fp32 accumulators -> one bf16x8 operand
 __device__ inline bf16x8 pack8(const floatx16& a, int base) {
   u32x4 v;

@@ -1,14 +1,17 @@
 // Causal flash attention, forward and backward, on gfx950 matrix cores
-// (bf16 operands, fp32 accumulation and softmax statistics), head dim 128.
+// (bf16 operands, fp32 accumulation and softmax statistics), head dim 128,
+// T a multiple of 64.
 //
 // Forward: a workgroup (4 waves) owns 128 query rows of one (row, head), a
 // wave 32 of them; it walks the 64-key tiles up to its diagonal with an
-// online softmax.  Backward: delta = rowsum(dO * O) (attn_delta), then one
-// kernel accumulates dQ over key tiles and one accumulates dK, dV over query
-// tiles, both recomputing P from the saved log-sum-exp -- no atomics, so the
-// result does not depend on scheduling.  dQ and dK leave through the
-// inverse rotary rotation, so the caller receives gradients with respect to
-// the pre-rotation q and k.
+// online softmax, issuing the next tile's score products while it forms
+// the current tile's exponentials.  Backward: one kernel accumulates dQ
+// over key tiles (and forms delta = rowsum(dO * O)), one accumulates dK, dV
+// over query tiles; both recompute P from the saved log-sum-exp -- no
+// atomics, so the result does not depend on scheduling.  dQ and dK leave
+// through the inverse rotary rotation, so the caller receives gradients with
+// respect to the pre-rotation q and k.  Every tile reaches LDS by direct
+// global-to-LDS copies (global_load_lds_dwordx4) into a ring of slots.
 #include <type_traits>
 
 #include "attn_mfma.h"
@@ -34,21 +37,54 @@ __device__ inline void tile_order(int ntile, int H, int B, int& tile, int& h, in
 }
 
 // ===========================================================================
-// forward
+// forward, software-pipelined: while a wave forms the softmax weights of key
+// tile j it already issues the score products of tile j + 1, so its matrix
+// core has independent work during the exponentials; the lazy maximum check
+// of tile j + 1 runs after tile j's value products.  LDS holds K tiles in a
+// ring of two (K[j+1] is read while K[j+2] is staged) and V tiles in a ring
+// of two (V[j] is read while V[j+1] is staged).
 // ===========================================================================
+// kHalf: the one 64-query block that T % 128 == 64 leaves at the end of
+// each row, launched separately (waves 2, 3 have no queries), so the
+// full-block kernel carries none of its guards.
+template <bool kHalf>
 __global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
-  __shared__ __attribute__((aligned(16))) char smem[2][32768];   // per stage: K image | V image
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  // separate arrays, so the compiler can tell the copies into one slot from
+  // the reads of another
+  __shared__ __attribute__((aligned(16))) char sK0[16384], sK1[16384], sV0[16384], sV1[16384];
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, H = a.H, d = H * HD;
   int qt, h, b;
-  tile_order(T / 128, H, a.B, qt, h, b);
-  qt = T / 128 - 1 - qt;                                         // heaviest tiles first
+  if (kHalf) {
+    qt = T / 128;
+    h = blockIdx.y;
+    b = blockIdx.z;
+  } else {
+    tile_order(T / 128, H, a.B, qt, h, b);
+    qt = T / 128 - 1 - qt;                                       // heaviest tiles first
+  }
   const int64_t ld = 3LL * d;
   const bf16* rows = (const bf16*)a.qkv + (int64_t)b * T * ld;
   const bf16* qb = rows + h * HD;
   const bf16* kb = rows + d + h * HD;
   const bf16* vb = rows + 2 * d + h * HD;
-  const int q0 = qt * 128, i0 = q0 + wave * 32, my_i = i0 + (lane & 31);
+  const int q0 = qt * 128, i0 = q0 + wave * 32;
+  // in the half block, waves 2, 3 have no queries: they run on a valid row
+  // and store nothing
+  const bool active = !kHalf || i0 < T;
+  const int my_i = active ? i0 + (lane & 31) : T - 1;
+  const int ntk = T / 64;                                        // key tiles that exist
+  const int ntiles = (q0 + 128) / 64;                            // the block's (even; ntk + 1 for a half block)
+  const int last = (i0 + 31) / 64;                               // this wave's diagonal tile
+
+  auto dmaK = [&](int jt, char* img) { dma_nat64(kb + (int64_t)jt * 64 * ld, ld, img, wave, lane); };
+  auto dmaV = [&](int jt, char* img) { dma_nat64(vb + (int64_t)jt * 64 * ld, ld, img, wave, lane); };
+  // (copies past the last key tile re-copy that tile into a slot nobody
+  // reads: clamped indices keep the loop free of branches)
+  dmaK(0, sK0);
+  dmaV(0, sV0);
+  dmaK(kHalf ? min(1, ntk - 1) : 1, sK1);
 
   bf16x8 qf[8];
 #pragma unroll
@@ -63,121 +99,181 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
   uint32_t offK[2];
 #pragma unroll
   for (int js = 0; js < 2; ++js) offK[js] = offN(js * 32 + (lane & 31), hh);   // chunk 2 ks + hh: ^ 32 ks
-
-  const int ntiles = (q0 + 128) / 64;
-  u32x4 rk[4], rv[4];
-  // next key tile into registers while this one is used; stored after
-  auto gl = [&](int jt) {
-    const int64_t j0 = (int64_t)jt * 64;
-    load_nat64<256>(kb + j0 * ld, ld, tid, rk);
-    load_nat64<256>(vb + j0 * ld, ld, tid, rv);
+  auto kfrag = [&](const char* sK, int js, int ks) {
+    return *reinterpret_cast<const bf16x8*>(sK + (offK[js] ^ (32u * ks)));
   };
-  auto st = [&](int stage) {
-    store_nat64<256>(smem[stage], tid, rk);
-    store_nat64<256>(smem[stage] + 16384, tid, rv);
-  };
-  gl(0);
-  st(0);
-  __syncthreads();
 
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const bool more = jt + 1 < ntiles;
-    if (more) gl(jt + 1);
-    const int j0 = jt * 64;
-    const char* sK = smem[jt & 1];
-    const char* sV = sK + 16384;
-    if (j0 <= i0 + 31) {
-      floatx16 s[2];
-      zero(s[0]);
-      zero(s[1]);
+  // keys after the query on the diagonal tile
+  auto mask = [&](int jt, floatx16 (&s)[2]) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
+    for (int js = 0; js < 2; ++js)
 #pragma unroll
-        for (int js = 0; js < 2; ++js) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (offK[js] ^ (32u * ks)));
-          s[js] = mfma(kf, qf[ks], s[js]);
-        }
-      // running max over raw scores (the positive scale preserves order);
-      // masked keys only on the diagonal tiles
-      if (j0 + 63 > i0) {
+      for (int r = 0; r < 16; ++r)
+        if (jt * 64 + js * 32 + 8 * (r >> 2) + 4 * hh + (r & 3) > my_i) s[js][r] = -INFINITY;
+  };
+  // m is the reference (log2-scaled) the exponentials are taken against.
+  // It follows the running maximum lazily: only when some row's maximum
+  // passes it by more than kLazy is it raised (and the running sums
+  // rescaled), so p <= 2^kLazy -- harmless in fp32 sums and bf16 operands
+  // -- and most tiles skip the rescale.
+  auto raise_max = [&](const floatx16 (&s)[2]) {
+    float mx = -INFINITY;
 #pragma unroll
-        for (int js = 0; js < 2; ++js)
+    for (int js = 0; js < 2; ++js)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (j0 + js * 32 + 8 * (r >> 2) + 4 * hh + (r & 3) > my_i) s[js][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[js][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * kScaleLog2;
+    constexpr float kLazy = 8.f;
+    if (__any(mx > m + kLazy)) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
 #pragma unroll
-      for (int js = 0; js < 2; ++js)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[js][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * kScaleLog2;
-      // m is the reference (log2-scaled) the exponentials are taken
-      // against.  It follows the running maximum lazily: only when some
-      // row's maximum passes it by more than kLazy is it raised (and the
-      // running sums rescaled), so p <= 2^kLazy -- harmless in fp32 sums
-      // and bf16 operands -- and most tiles skip the rescale.
-      constexpr float kLazy = 8.f;
-      if (__any(mx > m + kLazy)) {
-        const float mn = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        l *= alpha;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-        m = mn;
-      }
-      float ls = 0.f;
-#pragma unroll
-      for (int js = 0; js < 2; ++js)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[js][r], kScaleLog2, -m));
-          s[js][r] = p;
-          ls += p;
-        }
-      l += ls;
-#pragma unroll
-      for (int sp = 0; sp < 4; ++sp) {
-        const bf16x8 pf = pack8(s[sp >> 1], 8 * (sp & 1));
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x8 vf = frag_tr(sV, tv.l(t, sp), tv.h(t, sp));
-          o[t] = mfma(vf, pf, o[t]);
-        }
-      }
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      m = mn;
     }
-    if (more) st((jt + 1) & 1);
+  };
+  // weights e = 4 ks .. 4 ks + 3 of the 32 in s (in place), added to ls
+  auto weights4 = [&](floatx16 (&s)[2], int ks, float& ls) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * ks + e;
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r >> 4][r & 15], kScaleLog2, -m));
+      s[r >> 4][r & 15] = p;
+      ls += p;
+    }
+  };
+  auto values = [&](const char* sV, floatx16 (&s)[2]) {
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp) {
+      const bf16x8 pf = pack8(s[sp >> 1], 8 * (sp & 1));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] = mfma(frag_tr(sV, tv.l(t, sp), tv.h(t, sp)), pf, o[t]);
+    }
+  };
+
+  // q rows first: the score products below would otherwise wait on the
+  // memory counter behind the tile copies
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(qf[s]));
+  vm_wait();
+  __syncthreads();
+  floatx16 sa[2], sb[2];
+  zero(sa[0]);
+  zero(sa[1]);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int js = 0; js < 2; ++js) sa[js] = mfma(kfrag(sK0, js, ks), qf[ks], sa[js]);
+  if (last == 0) mask(0, sa);
+  raise_max(sa);
+  __syncthreads();                                               // K slot 0 is rewritten below
+
+  // Key tile jt of parity P: s_cur holds its scores (masked where needed,
+  // m covering their maximum).  Reads K slot 1 - P (tile jt + 1) and V slot
+  // P (tile jt); the copies of K[jt + 2] into K slot P and V[jt + 1] into V
+  // slot 1 - P (both last read before the previous barrier) are issued
+  // before and waited for after.
+  auto slots = [&](auto par, char*& kNext, char*& kFree, char*& vCur, char*& vFree) {
+    constexpr int P = decltype(par)::value;
+    kNext = P ? sK0 : sK1;
+    kFree = P ? sK1 : sK0;
+    vCur = P ? sV1 : sV0;
+    vFree = P ? sV0 : sV1;
+  };
+  // a tile before the wave's diagonal one: tile jt + 1's score products
+  // interleave with tile jt's exponentials
+  auto tile_mid = [&](int jt, const char* kNext, const char* vCur, floatx16 (&s_cur)[2], floatx16 (&s_nxt)[2]) {
+    zero(s_nxt[0]);
+    zero(s_nxt[1]);
+    float ls = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int js = 0; js < 2; ++js) s_nxt[js] = mfma(kfrag(kNext, js, ks), qf[ks], s_nxt[js]);
+      weights4(s_cur, ks, ls);
+    }
+    l += ls;
+    values(vCur, s_cur);
+    if (jt + 1 == last) mask(jt + 1, s_nxt);
+    raise_max(s_nxt);
+  };
+  // the wave's diagonal tile
+  auto tile_last = [&](const char* vCur, floatx16 (&s_cur)[2]) {
+    float ls = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) weights4(s_cur, ks, ls);
+    l += ls;
+    values(vCur, s_cur);
+  };
+  char *kNext, *kFree, *vCur, *vFree;
+  // every wave's diagonal tile is ntiles - 2 (waves 0, 1) or ntiles - 1
+  // (waves 2, 3): the tiles before ntiles - 2 take the same path in every
+  // wave (ntiles - 2 is even, so the loop runs in pairs of slot parities)
+  // (a wave without queries runs the loop on its clamped row and discards
+  // the result)
+  for (int jt = 0; jt < ntiles - 2; jt += 2) {
+    slots(std::false_type{}, kNext, kFree, vCur, vFree);
+    dmaK(jt + 2, kFree);
+    dmaV(jt + 1, vFree);
+    tile_mid(jt, kNext, vCur, sa, sb);
+    vm_wait();
     __syncthreads();
+    slots(std::true_type{}, kNext, kFree, vCur, vFree);
+    dmaK(kHalf ? min(jt + 3, ntk - 1) : jt + 3, kFree);
+    dmaV(jt + 2, vFree);
+    tile_mid(jt + 1, kNext, vCur, sb, sa);
+    vm_wait();
+    __syncthreads();
+  }
+  {
+    const int jt = ntiles - 2;
+    slots(std::false_type{}, kNext, kFree, vCur, vFree);
+    dmaV(kHalf ? min(jt + 1, ntk - 1) : jt + 1, vFree);
+    if (jt < last) tile_mid(jt, kNext, vCur, sa, sb);
+    else tile_last(vCur, sa);
+    vm_wait();
+    __syncthreads();
+    slots(std::true_type{}, kNext, kFree, vCur, vFree);
+    if (jt + 1 == last) tile_last(vCur, sb);
   }
 
   l += __shfl_xor(l, 32, 64);
   const float inv = 1.f / l;
+  // (a wave without queries stores nothing: its lanes are switched off
+  // for the stores rather than returned early, which keeps the register
+  // allocation of the loop above as it is without that wave)
   bf16* out = (bf16*)a.o_out + ((int64_t)b * T + my_i) * d + h * HD + 4 * hh;
+  if (active) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint2 w = make_uint2(pack2(o[t][4 * g] * inv, o[t][4 * g + 1] * inv),
-                                 pack2(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv));
-      *reinterpret_cast<uint2*>(out + t * 32 + 8 * g) = w;
-    }
-  if (hh == 0) a.lse[((int64_t)b * H + h) * T + my_i] = (m + __log2f(l)) * kLn2;
+      for (int g = 0; g < 4; ++g) {
+        const uint2 w = make_uint2(pack2(o[t][4 * g] * inv, o[t][4 * g + 1] * inv),
+                                   pack2(o[t][4 * g + 2] * inv, o[t][4 * g + 3] * inv));
+        *reinterpret_cast<uint2*>(out + t * 32 + 8 * g) = w;
+      }
+    if (hh == 0) a.lse[((int64_t)b * H + h) * T + my_i] = (m + __log2f(l)) * kLn2;
+  }
 }
 
-// inverse rotation of 4 consecutive features (2 adjacent pairs) at pair index pi
-__device__ inline void rope_inv4(float* v, const float2* tab_t, int pi) {
-  const float4 cs = *reinterpret_cast<const float4*>(tab_t + pi);
-  const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
-  v[0] = x0 * cs.x + x1 * cs.y;
-  v[1] = -x0 * cs.y + x1 * cs.x;
-  v[2] = x2 * cs.z + x3 * cs.w;
-  v[3] = -x2 * cs.w + x3 * cs.z;
-}
-
-// store a wave's 32 rows x 128 features accumulator (lane = row, regs = features)
-__device__ inline void store_rows(floatx16 (&acc)[4], float scale, bf16* dst_row, const float2* rope_t, int hh) {
+// store a wave's 32 rows x 128 features accumulator (lane = row, regs =
+// features), rotated back by the row's rotary angles when `rot` (wave-
+// uniform).  Every rotary factor is requested before the first store: the
+// memory counter is in order, so a factor loaded after a store would wait
+// for that store as well.
+__device__ inline void store_rows(floatx16 (&acc)[4], float scale, bf16* dst_row, const float2* rope_t, int hh,
+                                  bool rot) {
+  float4 cs[16];
+  if (rot) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        cs[4 * t + g] = *reinterpret_cast<const float4*>(rope_t + ((t * 32 + 8 * g + 4 * hh) >> 1));
+  }
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -185,40 +281,59 @@ __device__ inline void store_rows(floatx16 (&acc)[4], float scale, bf16* dst_row
       float v[4] = {acc[t][4 * g] * scale, acc[t][4 * g + 1] * scale, acc[t][4 * g + 2] * scale,
                     acc[t][4 * g + 3] * scale};
       const int f = t * 32 + 8 * g + 4 * hh;
-      if (rope_t) rope_inv4(v, rope_t, f >> 1);
+      if (rot) {
+        const float4 c = cs[4 * t + g];
+        const float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+        v[0] = x0 * c.x + x1 * c.y;
+        v[1] = -x0 * c.y + x1 * c.x;
+        v[2] = x2 * c.z + x3 * c.w;
+        v[3] = -x2 * c.w + x3 * c.z;
+      }
       *reinterpret_cast<uint2*>(dst_row + f) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
     }
 }
 
 // ===========================================================================
-// backward: dQ (one wave = 32 query rows, walking key tiles up to the
-// diagonal).  It also forms delta_i = sum_d dO[i,d] O[i,d] from the rows it
-// holds and stores it for the dK kernel.  K and V tiles are double-buffered:
-// the next tile's loads are in flight while this one is used.
+// backward: dQ, restructured so the softmax-gradient arithmetic overlaps
+// matrix-core work.  Per 64-key tile a wave forms S and dP of both 32-key
+// halves, then dS of the first half while the second half's products run,
+// then dS of the second half beside the first half's dQ products.  K and V
+// tiles are copied straight into a 2-slot LDS ring (global_load_lds); the
+// tile on the wave's diagonal is peeled off the loop so the loop body has
+// no masking.  Also forms delta_i = sum_d dO[i,d] O[i,d] for the dK/dV
+// kernel, as k_attn_dq does.
 // ===========================================================================
 __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
-  __shared__ __attribute__((aligned(16))) char smem[2][32768];   // per stage: K image | V image
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+  __shared__ __attribute__((aligned(16))) char sK0[16384], sV0[16384], sK1[16384], sV1[16384];
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, H = a.H, d = H * HD;
   int qt, h, b;
-  tile_order(T / 128, H, a.B, qt, h, b);
-  qt = T / 128 - 1 - qt;
+  const int ntq = (T + 127) / 128;
+  tile_order(ntq, H, a.B, qt, h, b);
+  qt = ntq - 1 - qt;
   const int64_t ld = 3LL * d;
   const bf16* rows = (const bf16*)a.qkv + (int64_t)b * T * ld;
   const bf16* qb = rows + h * HD;
   const bf16* kb = rows + d + h * HD;
   const bf16* vb = rows + 2 * d + h * HD;
-  const int q0 = qt * 128, i0 = q0 + wave * 32, my_i = i0 + (lane & 31);
+  const int q0 = qt * 128, i0 = q0 + wave * 32;
+  // with T % 128 == 64 the last block's waves 2, 3 have no queries: they
+  // load a valid row, compute nothing and store nothing
+  const bool active = i0 < T;
+  const int my_i = active ? i0 + (lane & 31) : T - 1;
   const int64_t tok = (int64_t)b * T + my_i;
   const bf16* dob = (const bf16*)a.dout + tok * d + h * HD;
   const bf16* ob = (const bf16*)a.o + tok * d + h * HD;
+  const int ntk = T / 64;                                        // key tiles that exist
+  const int ntiles = (q0 + 128) / 64;                            // the block's (even; ntk + 1 for a half block)
+  const int last = (i0 + 31) / 64;                               // the wave's diagonal tile
 
-  const int ntiles = (q0 + 128) / 64;
-  // one staging register set, used for the K then the V image of a tile
-  u32x4 rg[4];
-  auto gl = [&](const bf16* src, int jt) { load_nat64<256>(src + (int64_t)jt * 64 * ld, ld, tid, rg); };
-  auto st = [&](char* img) { store_nat64<256>(img, tid, rg); };
-  gl(kb, 0);
+  auto dma = [&](int jt, char* sK, char* sV) {
+    dma_nat64(kb + (int64_t)jt * 64 * ld, ld, sK, wave, lane);
+    dma_nat64(vb + (int64_t)jt * 64 * ld, ld, sV, wave, lane);
+  };
+  dma(0, sK0, sV0);
 
   bf16x8 qf[8], dof[8];
   float Dl = 0.f;
@@ -232,7 +347,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
   }
   Dl += __shfl_xor(Dl, 32, 64);
   const int64_t sidx = ((int64_t)b * H + h) * T + my_i;
-  if (hh == 0) a.delta[sidx] = Dl;
+  if (active && hh == 0) a.delta[sidx] = Dl;
   const float lse2 = a.lse[sidx] * kLog2e;
 
   floatx16 dq[4];
@@ -244,266 +359,288 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
 #pragma unroll
   for (int js = 0; js < 2; ++js) offR[js] = offN(js * 32 + (lane & 31), hh);   // chunk 2 ks + hh: ^ 32 ks
 
-  st(smem[0]);
-  gl(vb, 0);
-  st(smem[0] + 16384);
-  __syncthreads();
-  // The next tile is staged in two halves, each loaded before and written
-  // after half of this tile's work: K(jt+1) around keys 0-31, V(jt+1)
-  // around keys 32-63.
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const bool more = jt + 1 < ntiles;
-    char* nx = smem[(jt + 1) & 1];
-    if (more) gl(kb, jt + 1);
-    const int j0 = jt * 64;
-    const char* sK = smem[jt & 1];
-    const char* sV = sK + 16384;
+  // S = K Q^T and dP = V dO^T of keys js * 32 .. +31 of the tile
+  auto products = [&](const char* sK, const char* sV, int js, floatx16& s, floatx16& dp) {
+    zero(s);
+    zero(dp);
 #pragma unroll
-    for (int js = 0; js < 2; ++js) {
-      if (js == 1 && more) {
-        st(nx);
-        gl(vb, jt + 1);
-      }
-      const int jh = j0 + js * 32;
-      if (jh > i0 + 31) continue;                 // all 32 keys above the diagonal
-      floatx16 s, dp;
-      zero(s);
-      zero(dp);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (offR[js] ^ (32u * ks)));
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + (offR[js] ^ (32u * ks)));
-        s = mfma(kf, qf[ks], s);
-        dp = mfma(vf, dof[ks], dp);
-      }
-      const bool diag = jh + 31 > i0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(s[r] * kScaleLog2 - lse2);
-        if (diag && jh + 8 * (r >> 2) + 4 * hh + (r & 3) > my_i) p = 0.f;
-        s[r] = p * (dp[r] - Dl);                   // dS
-      }
-#pragma unroll
-      for (int gp = 0; gp < 2; ++gp) {
-        const bf16x8 df = pack8(s, 8 * gp);
-        const uint32_t sp = js * 2 + gp;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x8 kf = frag_tr(sK, tk.l(t, sp), tk.h(t, sp));
-          dq[t] = mfma(kf, df, dq[t]);
-        }
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      s = mfma(*reinterpret_cast<const bf16x8*>(sK + (offR[js] ^ (32u * ks))), qf[ks], s);
+      dp = mfma(*reinterpret_cast<const bf16x8*>(sV + (offR[js] ^ (32u * ks))), dof[ks], dp);
     }
-    if (more) st(nx + 16384);
+  };
+  // dS = P (dP - delta), P = exp(S / sqrt(Q) - lse), for elements r0 .. r0+n-1
+  auto grad = [&](floatx16& s, const floatx16& dp, int r0, int n) {
+#pragma unroll
+    for (int r = r0; r < r0 + n; ++r) {
+      const float p = __builtin_amdgcn_exp2f(s[r] * kScaleLog2 - lse2);
+      s[r] = p * (dp[r] - Dl);
+    }
+  };
+  auto mask = [&](int jh, floatx16& s) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (jh + 8 * (r >> 2) + 4 * hh + (r & 3) > my_i) s[r] = -INFINITY;
+  };
+  // dQ += dS K over keys js * 32 .. +31 (K^T read transposed), 2 MFMAs per
+  // key group gp; `during(gp)` runs beside them
+  auto dq_acc = [&](const char* sK, int js, const floatx16& ds, auto during) {
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      const bf16x8 df = pack8(ds, 8 * gp);
+      const uint32_t sp = js * 2 + gp;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dq[t] = mfma(frag_tr(sK, tk.l(t, sp), tk.h(t, sp)), df, dq[t]);
+      during(gp);
+    }
+  };
+
+  // a tile wholly below the wave's diagonal
+  auto tile_full = [&](const char* sK, const char* sV) {
+    floatx16 s0, p0, s1, p1;
+    products(sK, sV, 0, s0, p0);
+    // second half's products beside the first half's dS
+    zero(s1);
+    zero(p1);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s1 = mfma(*reinterpret_cast<const bf16x8*>(sK + (offR[1] ^ (32u * ks))), qf[ks], s1);
+      p1 = mfma(*reinterpret_cast<const bf16x8*>(sV + (offR[1] ^ (32u * ks))), dof[ks], p1);
+      grad(s0, p0, 2 * ks, 2);
+    }
+    dq_acc(sK, 0, s0, [&](int gp) { grad(s1, p1, 8 * gp, 8); });
+    dq_acc(sK, 1, s1, [&](int) {});
+  };
+  // the wave's diagonal tile: keys jd .. jd+31 cross it (jd = i0 or i0 - 32)
+  auto tile_diag = [&](const char* sK, const char* sV, int jt) {
+    const bool odd = (wave & 1) != 0;                            // first half wholly below
+    floatx16 s0, p0;
+    products(sK, sV, 0, s0, p0);
+    if (odd) {
+      floatx16 s1, p1;
+      products(sK, sV, 1, s1, p1);
+      grad(s0, p0, 0, 16);
+      mask(jt * 64 + 32, s1);
+      grad(s1, p1, 0, 16);
+      dq_acc(sK, 0, s0, [&](int) {});
+      dq_acc(sK, 1, s1, [&](int) {});
+    } else {
+      mask(jt * 64, s0);
+      grad(s0, p0, 0, 16);
+      dq_acc(sK, 0, s0, [&](int) {});
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    asm volatile("" : "+v"(qf[s]));
+    asm volatile("" : "+v"(dof[s]));
+  }
+  vm_wait();
+  __syncthreads();
+  // every wave's diagonal tile is ntiles - 2 (waves 0, 1) or ntiles - 1
+  // (waves 2, 3); the tiles before take the same path in every wave
+  // (a wave without queries runs the loop on its clamped row and discards
+  // the result; copies past the last key tile re-copy that tile)
+  for (int jt = 0; jt < ntiles - 2; jt += 2) {
+    dma(jt + 1, sK1, sV1);
+    tile_full(sK0, sV0);
+    vm_wait();
+    __syncthreads();
+    dma(jt + 2, sK0, sV0);
+    tile_full(sK1, sV1);
+    vm_wait();
     __syncthreads();
   }
+  {
+    const int jt = ntiles - 2;
+    dma(min(jt + 1, ntk - 1), sK1, sV1);
+    if (active) {
+      if (jt < last) tile_full(sK0, sV0);
+      else tile_diag(sK0, sV0, jt);
+    }
+    vm_wait();
+    __syncthreads();
+    if (active && jt + 1 == last) tile_diag(sK1, sV1, jt + 1);
+  }
+  if (!active) return;
   bf16* dst = (bf16*)a.dqkv + tok * ld + h * HD;
-  store_rows(dq, 0.08838834764831845f, dst, a.rope ? a.rope + (int64_t)my_i * (HD / 2) : nullptr, hh);
+  store_rows(dq, 0.08838834764831845f, dst, a.rope + (int64_t)my_i * (HD / 2), hh, a.rope != nullptr);
 }
 
 // ===========================================================================
-// backward: dK and dV.  A block owns 128 keys and has 8 waves in 4 pairs;
-// the two waves of pair w (w and w + 4, on the same SIMD) own keys
-// jb + 32w .. +31 and walk the 32-query halves of the query tiles from the
-// diagonal, splitting the work:
-//   wave w     (P role): S = Q K^T, P = exp(S - lse) -> LDS, dV += P^T dO
-//   wave w + 4 (D role): dP = dO V^T; one half later, with that half's P
-//                        from LDS, dS = P (dP - delta), dK += dS^T Q
-// The D role lags one half so that, between two barriers, the two waves'
-// work is independent and interleaves on their SIMD; each issues 32 MFMAs
-// per half and P's exponentials are formed once.  Q and dO tiles (with
-// their log-sum-exp and delta values) are double-buffered: the next tile's
-// loads are in flight during this one, and a stage is rewritten only after
-// the lagging role's last use of it.
+// backward: dK and dV, one wave per 32 keys doing all four products, two
+// blocks per CU.  A block owns 128 keys (4 waves) and walks the 32-query
+// tiles from its first key on.  Each wave keeps its keys' K rows in
+// registers (the B operand of S = Q K^T); the block's V rows sit in LDS
+// (the B operand of dP = dO V^T); Q, dO, lse and delta of the current query
+// tile are copied into a 2-slot LDS ring.  Per tile a wave forms S and dP,
+// P = exp(S - lse) and dS = P (dP - delta), and accumulates dV += P^T dO and
+// dK += dS^T Q (dO^T, Q^T read transposed).  No exchange between waves: the
+// only barrier is the ring swap, and with two blocks per CU the two waves
+// on a SIMD come from different blocks.  No atomics: each wave sums its
+// keys' gradients over the query tiles in order.
 // ===========================================================================
-__global__ void __launch_bounds__(512, 1) k_attn_dkdv(AttnDesc a) {
-  constexpr int SST = 32768 + 512;               // per stage: Q image | dO image | lse2[64] | delta[64]
-  constexpr int PX = 4096;                       // one pair's P for one half: [4][64 lanes][4 floats]
-  __shared__ __attribute__((aligned(16))) char smem[2 * SST + 8 * PX];
+constexpr int kDkdvKeys = 128;
+__global__ void __launch_bounds__(256, 2) k_attn_dkdv(AttnDesc a) {
+  constexpr int SST = 16384 + 256;               // per slot: Q image | dO image | lse[32] | delta[32]
+  __shared__ __attribute__((aligned(16))) char sV[kDkdvKeys * 256];
+  __shared__ __attribute__((aligned(16))) char st0[SST], st1[SST];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pair = wave & 3;
-  const bool roleP = wave < 4;
   const int T = a.T, H = a.H, d = H * HD;
   int kt, h, b;
-  tile_order(T / 128, H, a.B, kt, h, b);                         // low key tiles do the most work
+  tile_order((T + kDkdvKeys - 1) / kDkdvKeys, H, a.B, kt, h, b);
   const int64_t ld = 3LL * d;
   const bf16* rows = (const bf16*)a.qkv + (int64_t)b * T * ld;
   const bf16* qb = rows + h * HD;
   const bf16* kb = rows + d + h * HD;
   const bf16* vb = rows + 2 * d + h * HD;
   const bf16* dob = (const bf16*)a.dout + (int64_t)b * T * d + h * HD;
-  const int jb = kt * 128, jw = jb + pair * 32, my_j = jw + (lane & 31);
   const float* lse_bh = a.lse + ((int64_t)b * H + h) * T;
   const float* del_bh = a.delta + ((int64_t)b * H + h) * T;
+  const int jb = kt * kDkdvKeys, jw = jb + 32 * wave;
+  // with T % 128 == 64 the last block's waves 2, 3 have no keys: they load a
+  // valid K row, skip every tile (all its queries precede T <= jw) and store
+  // nothing
+  const bool keys = jw < T;
+  const int my_j = keys ? jw + (lane & 31) : T - 1;
 
-  u32x4 rq[2], ro[2];
-  float rs = 0.f;                                // lse (threads 0-63) or delta (64-127) of one query
-  // (lse is scaled to base 2 when stored, not when loaded: a use right
-  // after the load would wait for every load in flight)
-  auto gl = [&](int qt) {
-    const int64_t i0 = (int64_t)qt * 64;
-    load_nat64<512>(qb + i0 * ld, ld, tid, rq);
-    load_nat64<512>(dob + i0 * d, d, tid, ro);
-    if (tid < 64) rs = lse_bh[i0 + tid];
-    else if (tid < 128) rs = del_bh[i0 + tid - 64];
-  };
-  auto st = [&](char* base) {
-    store_nat64<512>(base, tid, rq);
-    store_nat64<512>(base + 16384, tid, ro);
-    if (tid < 128) reinterpret_cast<float*>(base + 32768)[tid] = tid < 64 ? rs * kLog2e : rs;
-  };
-  const int qt0 = jb / 64, nq = T / 64;
-  gl(qt0);
-
-  // key-side operand: K rows (P role) or V rows (D role) of the pair's keys
-  bf16x8 kv[8];
-  {
-    const bf16* src = (roleP ? kb : vb) + (int64_t)my_j * ld + 8 * hh;
+  // this wave's V rows into the block's image (rows 32 wave ..)
+  if (keys) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kv[s] = as_bf16x8(gload(src + 16 * s));
-    // Wait for these rows here, once: otherwise the loop's first products
-    // wait on the load counter, which by then also counts the next tile's
-    // loads, and every tile would sit out their latency.
-#pragma unroll
-    for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(kv[s]));
+    for (int i = 0; i < 32; i += 4) {
+      const int row = 32 * wave + i + (lane >> 4);
+      const int chunk = (lane & 15) ^ (int)swz(row);
+      __builtin_amdgcn_global_load_lds((gbl_vptr)(vb + (int64_t)(jb + row) * ld + chunk * 8),
+                                       (lds_vptr)(sV + (32 * wave + i) * 256), 16, 0, 0);
+    }
   }
-  floatx16 acc[4];                               // dV (P role) or dK (D role)
+  // one 32-query tile (Q, dO rows and their lse, delta) into a ring slot
+  auto dma = [&](int qt, char* st) __attribute__((always_inline)) {
+    const int64_t i0 = (int64_t)qt * 32;
+    dma_rows<4>(qb + i0 * ld, ld, st, 32, wave, lane);
+    dma_rows<4>(dob + i0 * d, d, st + 8192, 32, wave, lane);
+    if (lane < 32) {
+      if (wave == 0)
+        __builtin_amdgcn_global_load_lds((gbl_vptr)(lse_bh + i0 + lane), (lds_vptr)(st + 16384), 4, 0, 0);
+      else if (wave == 1)
+        __builtin_amdgcn_global_load_lds((gbl_vptr)(del_bh + i0 + lane), (lds_vptr)(st + 16384 + 128), 4, 0, 0);
+    }
+  };
+  const int qt0 = jb / 32, nq = T / 32;
+  dma(qt0, st0);
+
+  bf16x8 kf[8];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) zero(acc[t]);
+  for (int s = 0; s < 8; ++s) kf[s] = as_bf16x8(gload(kb + (int64_t)my_j * ld + 16 * s + 8 * hh));
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(kf[s]));
+
+  floatx16 accV[4], accK[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    zero(accV[t]);
+    zero(accK[t]);
+  }
   TrOff tt;
   tt.init(lane);
-  uint32_t offR[2];
-#pragma unroll
-  for (int is = 0; is < 2; ++is) offR[is] = offN(is * 32 + (lane & 31), hh);   // chunk 2 ks + hh: ^ 32 ks
-  float* pxb = reinterpret_cast<float*>(smem + 2 * SST) + pair * 2 * (PX / 4);
+  const uint32_t offR = offN(lane & 31, hh);                     // chunk 2 ks + hh: ^ 32 ks
+  const uint32_t offV = offN(32 * wave + (lane & 31), hh);
 
-  // phase 2 of a half: acc += X^T x with X^T read transposed from img (Q^T
-  // for dK, dO^T for dV) at the half's slot pairs
-  auto accumulate = [&](floatx16& x, const char* img, int is) {
+  // acc += X^T x over the tile's 32 queries, X^T read transposed from img
+  auto accumulate = [&](floatx16 (&acc)[4], const floatx16& x, const char* img) __attribute__((always_inline)) {
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp) {
-      const uint32_t sp = is * 2 + gp;
       const bf16x8 bfr = pack8(x, 8 * gp);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t] = mfma(frag_tr(img, tt.l(t, sp), tt.h(t, sp)), bfr, acc[t]);
+      for (int t = 0; t < 4; ++t) acc[t] = mfma(frag_tr(img, tt.l(t, gp), tt.h(t, gp)), bfr, acc[t]);
     }
   };
-  // D role, lagging half: dS = P (dP - delta), dK += dS^T Q
-  floatx16 dpp;                                  // dP of the pending half
-  zero(dpp);
-  bool pend = false;                             // a half waits for its dS / dK
-  const char* pQ = smem;                         // that half's stage
-  int pis = 0, pk = 0;
-  auto finish_d = [&]() {
-    const float* px = pxb + (pk & 1) * (PX / 4);
-    const float* sD = reinterpret_cast<const float*>(pQ + 32768) + 64;
+  // one 32-query tile in slot st (lane = key, register r = query
+  // i0 + 8 (r / 4) + 4 hh + r % 4)
+  auto tile = [&](const char* st, int qt) __attribute__((always_inline)) {
+    const int i0 = qt * 32;
+    if (i0 < jw) return;                         // every query of the tile precedes the keys
+    const char* sQ = st;
+    const char* sO = st + 8192;
+    const float* sL = reinterpret_cast<const float*>(st + 16384);
+    floatx16 x, y;
+    zero(x);
+    zero(y);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      x = mfma(*reinterpret_cast<const bf16x8*>(sQ + (offR ^ (32u * ks))), kf[ks], x);
+      y = mfma(*reinterpret_cast<const bf16x8*>(sO + (offR ^ (32u * ks))),
+               *reinterpret_cast<const bf16x8*>(sV + (offV ^ (32u * ks))), y);
+    }
+    if (i0 == jw) {                              // the tile on the diagonal
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (i0 + 8 * (r >> 2) + 4 * hh + (r & 3) < my_j) x[r] = -INFINITY;
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int il = pis * 32 + 8 * g + 4 * hh;
-      const float4 Dv = *reinterpret_cast<const float4*>(sD + il);
-      const float4 P = *reinterpret_cast<const float4*>(px + (g * 64 + lane) * 4);
-      dpp[4 * g + 0] = P.x * (dpp[4 * g + 0] - Dv.x);
-      dpp[4 * g + 1] = P.y * (dpp[4 * g + 1] - Dv.y);
-      dpp[4 * g + 2] = P.z * (dpp[4 * g + 2] - Dv.z);
-      dpp[4 * g + 3] = P.w * (dpp[4 * g + 3] - Dv.w);
+      const float4 L = *reinterpret_cast<const float4*>(sL + 8 * g + 4 * hh);
+      x[4 * g + 0] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 0], kScaleLog2, -L.x * kLog2e));
+      x[4 * g + 1] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 1], kScaleLog2, -L.y * kLog2e));
+      x[4 * g + 2] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 2], kScaleLog2, -L.z * kLog2e));
+      x[4 * g + 3] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 3], kScaleLog2, -L.w * kLog2e));
     }
-    accumulate(dpp, pQ, pis);
+    accumulate(accV, x, sO);                     // dV += P^T dO
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 D = *reinterpret_cast<const float4*>(sL + 32 + 8 * g + 4 * hh);
+      y[4 * g + 0] = x[4 * g + 0] * (y[4 * g + 0] - D.x);
+      y[4 * g + 1] = x[4 * g + 1] * (y[4 * g + 1] - D.y);
+      y[4 * g + 2] = x[4 * g + 2] * (y[4 * g + 2] - D.z);
+      y[4 * g + 3] = x[4 * g + 3] * (y[4 * g + 3] - D.w);
+    }
+    accumulate(accK, y, sQ);                     // dK += dS^T Q
   };
-
-  st(smem);
+  vm_wait();
   __syncthreads();
-  // One loop per role (the roles branch on a wave-uniform value; both
-  // loops pass the same barriers).
-  auto run = [&](auto role) {
-    constexpr bool kP = decltype(role)::value;
-    int k = 0;                                   // half counter: P of half k goes to buffer k & 1
-    for (int qt = qt0; qt < nq; ++qt) {
-      const bool more = qt + 1 < nq;
-      if (more) gl(qt + 1);
-      const int i0 = qt * 64;
-      const char* sQ = smem + ((qt - qt0) & 1) * SST;
-      const char* sO = sQ + 16384;
-      const float* sL = reinterpret_cast<const float*>(sQ + 32768);
-#pragma unroll
-      for (int is = 0; is < 2; ++is, ++k) {
-        const int ih = i0 + is * 32;
-        const bool live = ih + 31 >= jw;          // some query of the half sees the pair's keys
-        const bool diag = ih < jw + 31;
-        if constexpr (!kP) {
-          if (pend) finish_d();
-        }
-        // lane = key j, register r = query ih + 8(r/4) + 4hh + r%4
-        floatx16 x;
-        zero(x);
-        if (live) {
-          const char* img = kP ? sQ : sO;
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 fa = *reinterpret_cast<const bf16x8*>(img + (offR[is] ^ (32u * ks)));
-            x = mfma(fa, kv[ks], x);
-          }
-        }
-        if constexpr (kP) {
-          if (live) {
-            float* px = pxb + (k & 1) * (PX / 4);
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int il = is * 32 + 8 * g + 4 * hh;
-              const float4 L = *reinterpret_cast<const float4*>(sL + il);
-              const float Ls[4] = {L.x, L.y, L.z, L.w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 4 * g + e;
-                float p = __builtin_amdgcn_exp2f(x[r] * kScaleLog2 - Ls[e]);
-                if (diag && i0 + il + e < my_j) p = 0.f;
-                x[r] = p;
-              }
-              *reinterpret_cast<float4*>(px + (g * 64 + lane) * 4) =
-                  make_float4(x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]);
-            }
-            accumulate(x, sO, is);                // dV += P^T dO
-          }
-        } else {
-          dpp = x;
-          pend = live;
-          pQ = sQ;
-          pis = is;
-          pk = k;
-        }
-        // P of this half visible to the D role from here on; with is = 1,
-        // the staged next tile is written first (its stage last served the
-        // previous tile, whose pending half the D role finished above)
-        if (is == 1 && more) st(smem + ((qt + 1 - qt0) & 1) * SST);
-        __syncthreads();
-      }
-    }
-  };
-  if (roleP) run(std::true_type{});
-  else run(std::false_type{});
-  if (!roleP && pend) finish_d();
+  // two tiles per trip, so each ring slot is a fixed array (nq - qt0 is even)
+  for (int qt = qt0; qt < nq; qt += 2) {
+    dma(qt + 1, st1);
+    tile(st0, qt);
+    vm_wait();
+    __syncthreads();
+    if (qt + 2 < nq) dma(qt + 2, st0);
+    tile(st1, qt + 1);
+    vm_wait();
+    __syncthreads();
+  }
+  if (!keys) return;
   bf16* dst = (bf16*)a.dqkv + ((int64_t)b * T + my_j) * ld + h * HD;
-  if (roleP) store_rows(acc, 1.f, dst + 2 * d, nullptr, hh);
-  else store_rows(acc, 0.08838834764831845f, dst + d, a.rope ? a.rope + (int64_t)my_j * (HD / 2) : nullptr, hh);
+  store_rows(accV, 1.f, dst + 2 * d, nullptr, hh, false);
+  store_rows(accK, 0.08838834764831845f, dst + d, a.rope + (int64_t)my_j * (HD / 2), hh, a.rope != nullptr);
 }
 
 }  // namespace
 
-bool attn_mfma_supported(const AttnDesc& a) { return a.Q == HD && a.T % 128 == 0 && a.T > 0; }
+// T a multiple of 64: the forward and dQ kernels take 128-query blocks and
+// the dK/dV kernel 128-key blocks, so when T % 128 == 64 the last block's
+// waves past T sit idle (no loads, no stores).
+bool attn_mfma_supported(const AttnDesc& a) { return a.Q == HD && a.T % 64 == 0 && a.T > 0; }
 
 hipError_t attn_fwd_mfma(const AttnDesc& a, hipStream_t s) {
   if (!attn_mfma_supported(a)) return hipErrorNotSupported;
-  k_attn_fwd<<<dim3(a.T / 128, a.H, a.B), 256, 0, s>>>(a);
+  if (a.T >= 128) {
+    k_attn_fwd<false><<<dim3(a.T / 128, a.H, a.B), 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.T % 128) k_attn_fwd<true><<<dim3(1, a.H, a.B), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s) {
   if (!attn_mfma_supported(a)) return hipErrorNotSupported;
-  const dim3 grid(a.T / 128, a.H, a.B);
-  k_attn_dq<<<grid, 256, 0, s>>>(a);             // also writes delta
+  k_attn_dq<<<dim3((a.T + 127) / 128, a.H, a.B), 256, 0, s>>>(a);   // also writes delta
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_attn_dkdv<<<grid, 512, 0, s>>>(a);
+  k_attn_dkdv<<<dim3((a.T + kDkdvKeys - 1) / kDkdvKeys, a.H, a.B), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

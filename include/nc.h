@@ -132,8 +132,8 @@ const char* nc_last_error(const nc_ctx* ctx);
 
 /* In bf16 mode without NC_FLAG_PORTABLE_KERNELS every product and attention
  * call runs on the matrix-core kernels when its shape allows (products:
- * sizes the MFMA tiles cover; attention: head dim 128 and T a multiple of
- * 128); any other shape runs the portable (non-MFMA) kernel instead, with
+ * B*T and the widths multiples of 128; attention: head dim 128 with T a
+ * multiple of 64); any other shape runs the portable (non-MFMA) kernel instead, with
  * the same results to rounding but far slower.  *count receives how many
  * launches on this context took that fallback since it was created or last
  * reset (reset = 1 zeroes it after reading).  Host-only; fp32 contexts and

@@ -84,3 +84,31 @@ def newton_schulz_bf16(G, steps, coeffs, eps=1e-7):
         B = r32(c * (A @ A.T) + b * A)
         X = r32(B @ X + a * X)
     return X.T if tall else X
+
+
+def logits_bf16_storage(cfg, p64, tokens):
+    """Error model of the bf16 forward, used only to size the decode
+    tolerance: the oracle's components (oracle/model.py) composed as the
+    library stores activations -- the residual stream, both norm outputs, q
+    and k after rotation, v, the attention output, relu(h)^2 and the final
+    norm rounded to bf16 where the library writes them; weights are the
+    same bf16 values; every product is exact (fp64).  The fp32 logits of
+    every position, [T][V]."""
+    import oracle
+    r = lambda x: synthdata.round_to_bf16(np.asarray(x, np.float32)).astype(np.float64)
+    tokens = np.asarray(tokens)
+    T, H, Q = len(tokens), cfg.n_head, cfg.head_dim
+    phi = oracle.rope_angles(T, Q, cfg.rope_base)
+    x = p64["E"][tokens]
+    for lp in p64["layers"]:
+        a = r(oracle.rmsnorm(x, cfg.rms_eps)[0])
+        q = r(oracle.rope((a @ lp["Wq"].T).reshape(T, H, Q), phi))
+        k = r(oracle.rope((a @ lp["Wk"].T).reshape(T, H, Q), phi))
+        v = r((a @ lp["Wv"].T).reshape(T, H, Q))
+        o = r(oracle.causal_attention(q, k, v).reshape(T, -1))
+        x = r(x + o @ lp["Wo"].T)
+        m = r(oracle.rmsnorm(x, cfg.rms_eps)[0])
+        u = r(oracle.relu2(m @ lp["W1"].T))
+        x = r(x + u @ lp["W2"].T)
+    xf = r(oracle.rmsnorm(x, cfg.rms_eps)[0])
+    return xf @ p64["U"].T

@@ -7,16 +7,23 @@ run on each sequence's prompt + generated tokens.  The generated tokens are
 fixed (teacher-forced), so every step is compared.
 
 Bars: fp32 (tiny) max |dz| / max |z| <= 1e-4 per row.  bf16 (small, d20):
-cosine >= 0.9999 per row and max |dz| <= 0.02 max |z|.  Activations are
-stored in bf16 after every product and norm, so the logits drift with
-depth; at d20 (logits up to ~5, RMS ~1) they sit 1.2 % of the largest
-logit from fp64, at cosine 0.99993."""
+from an error model, not from the GPU's own numbers.  The library stores
+every activation in bf16 (residual stream, norm outputs, q/k/v, attention
+output, relu^2), so its logits differ from fp64 by the propagated storage
+rounding.  tests/_util.logits_bf16_storage recomputes the logits on the CPU
+with exactly that rounding (products exact) for the same sequence; per
+position, the GPU's max |dz| must lie within 2x the model's max |dz| (plus
+1e-3 of the row's largest logit), and its cosine distance 1 - cos within
+2x the model's (plus 1e-5).  The factor 2 covers what the model leaves
+out: fp32 accumulation order and rounding in the kernels' intermediates,
+which differ from the model's exact products by far less than the storage
+rounding itself."""
 import numpy as np
 import pytest
 
 import oracle
 import synthdata
-from _util import cosine, dev, empty, host, zeros
+from _util import cosine, dev, empty, host, zeros, logits_bf16_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -61,19 +68,26 @@ def _check(cfg, params, prompt, gen, nseq, bf16):
     p64 = synthdata.split_params(cfg, params.astype(np.float64))
     T0 = len(prompt)
 
-    def ok(got, want, what):
+    def ok(got, want, model, what):
         err = np.abs(got - want).max()
         if bf16:
-            assert cosine(got, want) >= 0.9999 and err <= 0.02 * np.abs(want).max(), (what, cosine(got, want), err)
+            # bars from the bf16 storage error model of the same position
+            m_err = np.abs(model - want).max()
+            m_dist = 1.0 - cosine(model, want)
+            bar = 2.0 * m_err + 1e-3 * np.abs(want).max()
+            assert err <= bar, (what, err, m_err)
+            assert 1.0 - cosine(got, want) <= 2.0 * m_dist + 1e-5, (what, cosine(got, want), 1.0 - m_dist)
         else:
             assert err <= 1e-4 * np.abs(want).max(), (what, err)
 
     for s in range(nseq):
-        z = _oracle_logits(cfg, p64, np.concatenate([prompt, gen[s]]))
+        seq = np.concatenate([prompt, gen[s]])
+        z = _oracle_logits(cfg, p64, seq)
+        zm = logits_bf16_storage(cfg, p64, seq) if bf16 else z
         if s == 0:
-            ok(l0, z[T0 - 1], "prefill")
+            ok(l0, z[T0 - 1], zm[T0 - 1], "prefill")
         for i, li in enumerate(steps):
-            ok(li[s], z[T0 + i], ("decode", s, i))
+            ok(li[s], z[T0 + i], zm[T0 + i], ("decode", s, i))
 
 
 def _tokens(cfg, T0, nseq, steps, seed):
@@ -98,6 +112,25 @@ def test_small_bf16_decode_matches_forward(T0, nseq, steps):
     params = synthdata.make_params(cfg)
     prompt, gen = _tokens(cfg, T0, nseq, steps, 52 + T0)
     _check(cfg, params, prompt, gen, nseq, bf16=True)
+
+
+@pytest.mark.parametrize("T0", [1, 100, 255, 300])
+def test_prefill_runs_on_matrix_cores(T0):
+    """A prompt padded to a multiple of 128 (the matrix-core products take
+    128-row tiles) runs every product and attention call of the prefill on
+    the matrix-core kernels: no launch falls back to the portable ones.
+    (Attention alone takes any multiple of 64; see the attention op tests
+    at T = 192 and 320.)"""
+    cfg = synthdata.get_config("small")
+    pad = (T0 + 127) // 128 * 128
+    pcfg = cfg.with_(batch=1, seq_len=pad)
+    sess = nc.Session(pcfg)
+    P = dev(synthdata.make_params(cfg), "bf16")
+    kv = zeros((nc.kv_cache_bytes(pcfg, 1, pad) // 4,))
+    lg = empty((cfg.vocab,))
+    sess.prefill(P, dev(np.zeros(pad, dtype=np.int32)), T0, 1, kv, 1, pad, lg)
+    torch.cuda.synchronize()
+    assert sess.fallback_count() == 0
 
 
 def test_decode_rejects_bad_shapes():

@@ -236,6 +236,8 @@ ATT_CASES = [
     ("bf16", 0, 2, 256, 2, 128),
     ("bf16", 0, 1, 640, 3, 128),
     ("bf16", 0, 1, 2048, 10, 128),   # one row of the d20 launch: every head, full row length
+    ("bf16", 0, 2, 192, 2, 128),     # T % 128 == 64: half-empty last query and key blocks
+    ("bf16", 0, 1, 320, 3, 128),
 ]
 
 
