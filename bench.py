@@ -434,7 +434,8 @@ def main():
             step()
             n, ms, fl, by = sess.trace_read()
             if n:
-                families[f] = {"launches": n, "ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+                families[f] = {"launches": n, "ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                               "alg_gb_per_launch": round(by / n / 1e9, 4)}
         sess.trace_enable(None)
         single = [f for f in families if f in nc.SINGLE_KERNEL_FAMILIES]
         dominant = max(single, key=lambda f: families[f]["ms"]) if single else None
@@ -462,7 +463,8 @@ def main():
           file=sys.stderr, flush=True)
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if cfg.name == "d20" else
+                  f"train tokens/s + MFU (fwd+bwd) on 1 MI355X, {cfg.name} at {cfg.batch}x{cfg.seq_len} tok/step",
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -563,7 +565,8 @@ def block_bench(args, cfg):
         step()
         n, ms, fl, by = sess.trace_read()
         if n:
-            families[f] = {"launches": n, "ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1)}
+            families[f] = {"launches": n, "ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                           "alg_gb_per_launch": round(by / n / 1e9, 4)}
     sess.trace_enable(None)
     single = [f for f in families if f in nc.SINGLE_KERNEL_FAMILIES]
     dominant = max(single, key=lambda f: families[f]["ms"])
@@ -582,7 +585,11 @@ def block_bench(args, cfg):
     achieved = fl / n / (tms / n * 1e-3) / 1e12
     mfu = flops_per_step(cfg) / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)
     print(f"[bench] block: {ms:.3f} ms/step, MFU {mfu:.3f}", file=sys.stderr, flush=True)
-    print(json.dumps({
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = block_cpu_baseline(cfg, params, x, dy, args.cpu_sample_tokens)
+        print(f"[bench] cpu baseline: {cpu['value']} tok/s on {cpu['cores']} cores", file=sys.stderr, flush=True)
+    out = {
         "metric": "train tokens/s + MFU (fwd+bwd) of one d20 block on 1 MI355X, 32x2048 tok/step",
         "value": round(N / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "ms_per_step_min": round(per_step[0], 4),
@@ -595,7 +602,30 @@ def block_bench(args, cfg):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel_family": dominant,
                      "launches_timed": n, "avg_launch_ms": round(tms / n, 4), "flops_per_launch": fl / n},
-        "kernel_families": families}), flush=True)
+        "kernel_families": families}
+    if cpu:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+def block_cpu_baseline(cfg, params, x, dy, sample_tokens):
+    """The fp64 oracle's block step (forward + backward of one layer, as
+    written) on the first `sample_tokens` tokens of row 0."""
+    import synthdata
+    import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    T = min(sample_tokens, cfg.seq_len)
+    c = cfg.with_(batch=1, seq_len=T)
+    lp = synthdata.split_params(cfg, params)["layers"][0]
+    t0 = time.time()
+    oracle.block_step(c, lp, x[:1, :T].astype("float64"), dy[:1, :T].astype("float64"))
+    dt = time.time() - t0
+    return {"value": round(T / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy oracle block step (fwd+bwd of one layer) on the first {T} tokens of row 0 "
+                      f"of the {cfg.name} workload ({dt:.1f} s wall)"}
 
 
 def cpu_baseline(cfg, params, idx, tgt, tb, sample_tokens):

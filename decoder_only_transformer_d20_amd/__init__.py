@@ -109,6 +109,8 @@ _SIGS = {
     "nc_op_device_info": (ctypes.c_int, [_I32] + [ctypes.POINTER(_I32)] * 4),
     "nc_op_attention_fwd": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _I32, _P]),
     "nc_op_attention_bwd": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
+    "nc_op_attention_bwd_ds": (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "nc_op_attention_ds_bytes": (_I64, [_I32, _I32, _I32]),
     "nc_op_embed_fwd": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _P]),
     "nc_op_embed_bwd_scratch_bytes": (_I64, [_I64, _I32]),
     "nc_op_embed_bwd": (ctypes.c_int, [_I32, _I64, _I32, _I32, _P, _P, _P, _I32, _P, _P]),

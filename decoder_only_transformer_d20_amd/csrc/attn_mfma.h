@@ -141,6 +141,13 @@ __device__ inline void dma_rows(const bf16* src, int64_t ld, char* img, int rows
   }
 }
 __device__ inline void vm_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// every vector-memory operation but the 2 most recently issued has completed
+__device__ inline void vm_wait_but2() { asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); }
+// A workgroup barrier for LDS traffic only: the wave's LDS operations are
+// complete, then s_barrier.  Unlike __syncthreads() it carries no release
+// fence, which would wait for every global store of the wave as well.  Use
+// it only where no other wave reads this wave's global stores.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // 8 consecutive fp32 accumulators -> one bf16x8 operand
 __device__ inline bf16x8 pack8(const floatx16& a, int base) {

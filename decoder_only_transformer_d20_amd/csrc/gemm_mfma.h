@@ -142,8 +142,8 @@ __device__ inline uint32_t frag_tr_off(int row0, int l) {
 // One output tile of the persistent grid: split, n-tile, k-tiles, origin,
 // and the element offsets of its batch item's operands and result.
 struct GemmTile {
-  int split, tn, nk;
-  int64_t m0, n0, kbeg;
+  int split, tm, tn, nk;     // a shifted last tile (RAG) stores from row tm * BM,
+  int64_t m0, n0, kbeg;      // column tn * BN on (> m0 / n0); tm is set only there
   int64_t pofs, qofs, cofs, aofs;
 };
 
@@ -156,14 +156,19 @@ struct GemmTile {
 // n-tiles, so each P panel and each Q panel (weights) is reused from that
 // XCD's L2 instead of refetched per tile.  Split i covers the k-tiles
 // [i nkt/splits, (i+1) nkt/splits).  Batch items are outermost of all.
+// A dimension that is not a multiple of the tile (a multiple of 128, at
+// least 2 tiles) ends in a tile shifted back to end at the matrix edge: it
+// computes the outputs it shares with its neighbour again and stores only
+// its own (from tm * BM / tn * BN on), so every output is written by one
+// tile.
 template <int BM, int BN>
 struct TileMap {
   static constexpr int kGroupM = 8, kNarrow = 8;
   int ntn, ntm, ntiles, total, nkt, G, chunk, splits, sym;
   int64_t sP, sQ, sC, sAux;
   __device__ inline TileMap(const GemmDesc& g) {
-    ntn = g.N / BN;
-    ntm = g.M / BM;
+    ntn = (g.N + BN - 1) / BN;
+    ntm = (g.M + BM - 1) / BM;
     sym = g.sym;
     ntiles = sym ? ntm * (ntm + 1) / 2 : ntn * ntm;   // sym: the tiles with tn >= tm
     splits = g.splits;
@@ -181,7 +186,8 @@ struct TileMap {
     const int L = x * chunk + j;
     return (j < chunk && L < total) ? L : -1;
   }
-  __device__ inline GemmTile coords(int L) const {
+  template <bool RAG>
+  __device__ inline GemmTile coords(int L, const GemmDesc& g) const {
     GemmTile c;
     const int outer = L / ntiles;
     const int b = outer / splits;
@@ -195,6 +201,7 @@ struct TileMap {
         rem -= ntm - tm;
         ++tm;
       }
+      if constexpr (RAG) c.tm = tm;
       c.tn = tm + rem;
       c.m0 = (int64_t)tm * BM;
       c.n0 = (int64_t)c.tn * BN;
@@ -210,8 +217,15 @@ struct TileMap {
     // wide ones: m fastest, so each Q panel serves gm blocks
     const bool nfast = ntn <= kNarrow;
     c.tn = nfast ? tg % ntn : tg / gm;
-    c.m0 = (int64_t)(first_m + (nfast ? tg / ntn : tg % gm)) * BM;
-    c.n0 = (int64_t)c.tn * BN;
+    const int tmi = first_m + (nfast ? tg / ntn : tg % gm);
+    if constexpr (RAG) {
+      c.tm = tmi;
+      c.m0 = (int64_t)min(tmi * BM, g.M - BM);
+      c.n0 = (int64_t)min(c.tn * BN, g.N - BN);
+    } else {
+      c.m0 = (int64_t)tmi * BM;
+      c.n0 = (int64_t)c.tn * BN;
+    }
     const int kt0 = (int)((int64_t)c.split * nkt / splits);
     c.nk = (int)((int64_t)(c.split + 1) * nkt / splits) - kt0;
     c.kbeg = (int64_t)kt0 * BK;
@@ -326,7 +340,10 @@ __device__ inline void lse_combine(const GemmDesc& g, const GemmTile& c, const f
 // While a tile's epilogue runs, the first k-tile of the block's next tile is
 // already on its way into registers, so tile boundaries cost neither a
 // block launch nor an exposed load latency.
-template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
+//
+// RAG: M or N is not a multiple of the tile; a separate instantiation, so
+// the exact-fit kernels carry none of the shifted tile's bookkeeping.
+template <int NW, int BM, int BN, bool PT, bool QT, int EPI, bool RAG>
 __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   static_assert(BM % 64 == 0 && BN % 128 == 0 && NW == 8, "tile");
   constexpr int WGN = NW / 2;                    // waves along n
@@ -437,7 +454,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
 
   int v = blockIdx.x;
   if (tm.logical(v) < 0) return;                 // no tile for this block (uniform)
-  Tile cur = tm.coords(tm.logical(v));
+  Tile cur = tm.template coords<RAG>(tm.logical(v), g);
   plan_init(cur);
   stage_load();                 // k-tile 0 of the first tile
 
@@ -520,7 +537,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
     const Tile c = cur;
     auto prefetch_next = [&]() {
       if (more) {
-        cur = tm.coords(Ln);
+        cur = tm.template coords<RAG>(Ln, g);
         plan_init(cur);
         stage_load();
       }
@@ -595,8 +612,14 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
       if constexpr (EPI == EPI_ROPE) pi = (int)(n % g.head_dim) >> 1;
       const bool rot = EPI == EPI_ROPE && n < g.rope_cols;
       const bool tile_rot = EPI == EPI_ROPE && c.n0 < g.rope_cols;   // uniform over the block
+      // a shifted last tile stores from row tm BM, column tn BN on: the
+      // shift is 0 or 128 (dimensions are multiples of 128), so whole passes
+      // (WTM = 128 rows) and whole column runs of a thread drop out
+      const int row_skip = RAG ? c.tm * BM - (int)c.m0 : 0;
+      const bool col_keep = !RAG || 4 * cc >= c.tn * BN - (int)c.n0;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        const bool keep = !RAG || (col_keep && h * WTM >= row_skip);
         // The pass's global inputs (aux rows, rotary factors, per-row loss
         // terms) are requested W rows ahead of their use, the first W
         // before the LDS round trip, which hides their latency.
@@ -664,7 +687,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
           }
           if constexpr (EPI == EPI_LSEZ) dz_l = zrow_max[h * WTM + r];
           if (k + W < NR) fetch(k + W);
-          epi_store4<EPI>(g, c, m, n, x, y, cs, rot, dz_t, dz_l, dz_s);
+          if (keep) epi_store4<EPI>(g, c, m, n, x, y, cs, rot, dz_t, dz_l, dz_s);
         }
         if (h == 0) __syncthreads();
       }
@@ -691,16 +714,15 @@ int resident_blocks(Kernel kern, int threads, int (&cached)[16]) {
   return cached[dev];
 }
 
-template <int NW, int BM, int BN, bool PT, bool QT, int EPI>
+template <int NW, int BM, int BN, bool PT, bool QT, int EPI, bool RAG>
 hipError_t launch(const GemmDesc& g, hipStream_t s) {
   static int cached[16] = {0};
-  const int ntiles = g.sym ? (g.M / BM) * (g.M / BM + 1) / 2 : (g.M / BM) * (g.N / BN);
+  const int ntiles = g.sym ? (g.M / BM) * (g.M / BM + 1) / 2 : ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   const int total = ntiles * g.splits * (g.batch > 1 ? g.batch : 1);
-  dim3 grid(std::min(total, resident_blocks(k_gemm_mfma<NW, BM, BN, PT, QT, EPI>, NW * 64, cached)));
-  k_gemm_mfma<NW, BM, BN, PT, QT, EPI><<<grid, NW * 64, 0, s>>>(g);
+  dim3 grid(std::min(total, resident_blocks(k_gemm_mfma<NW, BM, BN, PT, QT, EPI, RAG>, NW * 64, cached)));
+  k_gemm_mfma<NW, BM, BN, PT, QT, EPI, RAG><<<grid, NW * 64, 0, s>>>(g);
   return hipGetLastError();
 }
-
 
 }  // namespace mfma
 }  // namespace nc
@@ -712,6 +734,16 @@ hipError_t launch(const GemmDesc& g, hipStream_t s) {
 //             activation gradients against transposed weight images
 //             (both k-major: STORE, DRELU2)
 //   tests:    every layout with fp32 and bf16 stores
+// Combinations that also run with M or N a multiple of 128 but not of a
+// 256 tile (a shifted last tile): the products of a model whose widths are
+// odd multiples of 128 -- qkv + rotary, the residual products, activation
+// gradients and weight gradients.
+#define NC_MFMA_RAGGED_COMBOS(X) \
+  X(0, 0, EPI_STORE)             \
+  X(0, 0, EPI_ROPE)              \
+  X(0, 0, EPI_RESID)             \
+  X(1, 1, EPI_F32)
+
 #define NC_MFMA_COMBOS(X)     \
   X(0, 0, EPI_STORE)          \
   X(0, 0, EPI_ROPE)           \
@@ -741,10 +773,28 @@ inline bool combo_supported(const GemmDesc& g) {
   return false;
 }
 
+inline bool ragged_combo(const GemmDesc& g) {
+#define NC_X(PT, QT, EPI) \
+  if (g.p_trans == PT && g.q_trans == QT && g.epi == EPI) return true;
+  NC_MFMA_RAGGED_COMBOS(NC_X)
+#undef NC_X
+  return false;
+}
+
 template <int NW, int BM, int BN>
 hipError_t dispatch(const GemmDesc& g, hipStream_t s) {
+  if (g.M % BM || g.N % BN) {
+    if constexpr (BM == 256) {
+      if (g.sym || g.M < BM || g.N < BN) return hipErrorInvalidValue;
 #define NC_X(PT, QT, EPI) \
-  if (g.p_trans == PT && g.q_trans == QT && g.epi == EPI) return launch<NW, BM, BN, PT, QT, EPI>(g, s);
+  if (g.p_trans == PT && g.q_trans == QT && g.epi == EPI) return launch<NW, BM, BN, PT, QT, EPI, true>(g, s);
+      NC_MFMA_RAGGED_COMBOS(NC_X)
+#undef NC_X
+    }
+    return hipErrorInvalidValue;
+  }
+#define NC_X(PT, QT, EPI) \
+  if (g.p_trans == PT && g.q_trans == QT && g.epi == EPI) return launch<NW, BM, BN, PT, QT, EPI, false>(g, s);
   NC_MFMA_COMBOS(NC_X)
 #undef NC_X
   return hipErrorInvalidValue;

@@ -481,7 +481,16 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
 // on a SIMD come from different blocks.  No atomics: each wave sums its
 // keys' gradients over the query tiles in order.
 // ===========================================================================
+// kDS: also store dS^T, the tile's 32 keys x 32 queries, into the dS^T
+// tile buffer the stored-dS dQ kernel reads.  Tile (head, query block qb,
+// 64-key tile kt) holds four 4 KB pieces, one per 32-query tile, each
+// [64 keys][32 queries] bf16 (64-byte rows, so two key rows fill a 128-byte
+// line and a wave's two stores write whole lines).  Lane (key, hh) writes
+// its two packed groups gp (the dK product's B operands) as 16-byte chunks
+// at query columns 16 gp + 8 hh .. +7: the columns hold the queries in the
+// products' slot order (within each 16: 0-3, 8-11, 4-7, 12-15).
 constexpr int kDkdvKeys = 128;
+template <bool kDS>
 __global__ void __launch_bounds__(256, 2) k_attn_dkdv(AttnDesc a) {
   constexpr int SST = 16384 + 256;               // per slot: Q image | dO image | lse[32] | delta[32]
   __shared__ __attribute__((aligned(16))) char sV[kDkdvKeys * 256];
@@ -500,6 +509,12 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkdv(AttnDesc a) {
   const float* lse_bh = a.lse + ((int64_t)b * H + h) * T;
   const float* del_bh = a.delta + ((int64_t)b * H + h) * T;
   const int jb = kt * kDkdvKeys, jw = jb + 32 * wave;
+  const int nqb = (T + 127) / 128;
+  // this lane's row (key) of its 64-key tile in query block 0; query block
+  // qb's tiles start qb (qb + 1) tiles further
+  bf16* ds_w = kDS ? (bf16*)a.ds + (((int64_t)b * H + h) * nqb * (nqb + 1) + (jw >> 6)) * (64 * HD) +
+                         ((jw & 63) + (lane & 31)) * 32 + 8 * hh
+                   : nullptr;
   // with T % 128 == 64 the last block's waves 2, 3 have no keys: they load a
   // valid K row, skip every tile (all its queries precede T <= jw) and store
   // nothing
@@ -561,60 +576,210 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkdv(AttnDesc a) {
   // i0 + 8 (r / 4) + 4 hh + r % 4)
   auto tile = [&](const char* st, int qt) __attribute__((always_inline)) {
     const int i0 = qt * 32;
-    if (i0 < jw) return;                         // every query of the tile precedes the keys
-    const char* sQ = st;
-    const char* sO = st + 8192;
-    const float* sL = reinterpret_cast<const float*>(st + 16384);
-    floatx16 x, y;
-    zero(x);
-    zero(y);
+    bf16* dst_ds = kDS ? ds_w + ((i0 >> 7) * ((i0 >> 7) + 1)) * (64 * HD) + (i0 & 127) * 64 : nullptr;
+    // with kDS the tile's dS is stored even where every query precedes the
+    // keys (zeros), so every tile leaves exactly two stores behind its copy
+    bf16x8 d0 = {}, d1 = {};
+    if (i0 >= jw) {                              // else every query of the tile precedes the keys
+      const char* sQ = st;
+      const char* sO = st + 8192;
+      const float* sL = reinterpret_cast<const float*>(st + 16384);
+      floatx16 x, y;
+      zero(x);
+      zero(y);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      x = mfma(*reinterpret_cast<const bf16x8*>(sQ + (offR ^ (32u * ks))), kf[ks], x);
-      y = mfma(*reinterpret_cast<const bf16x8*>(sO + (offR ^ (32u * ks))),
-               *reinterpret_cast<const bf16x8*>(sV + (offV ^ (32u * ks))), y);
-    }
-    if (i0 == jw) {                              // the tile on the diagonal
+      for (int ks = 0; ks < 8; ++ks) {
+        x = mfma(*reinterpret_cast<const bf16x8*>(sQ + (offR ^ (32u * ks))), kf[ks], x);
+        y = mfma(*reinterpret_cast<const bf16x8*>(sO + (offR ^ (32u * ks))),
+                 *reinterpret_cast<const bf16x8*>(sV + (offV ^ (32u * ks))), y);
+      }
+      if (i0 == jw) {                            // the tile on the diagonal
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (i0 + 8 * (r >> 2) + 4 * hh + (r & 3) < my_j) x[r] = -INFINITY;
-    }
+        for (int r = 0; r < 16; ++r)
+          if (i0 + 8 * (r >> 2) + 4 * hh + (r & 3) < my_j) x[r] = -INFINITY;
+      }
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 L = *reinterpret_cast<const float4*>(sL + 8 * g + 4 * hh);
-      x[4 * g + 0] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 0], kScaleLog2, -L.x * kLog2e));
-      x[4 * g + 1] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 1], kScaleLog2, -L.y * kLog2e));
-      x[4 * g + 2] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 2], kScaleLog2, -L.z * kLog2e));
-      x[4 * g + 3] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 3], kScaleLog2, -L.w * kLog2e));
-    }
-    accumulate(accV, x, sO);                     // dV += P^T dO
+      for (int g = 0; g < 4; ++g) {
+        const float4 L = *reinterpret_cast<const float4*>(sL + 8 * g + 4 * hh);
+        x[4 * g + 0] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 0], kScaleLog2, -L.x * kLog2e));
+        x[4 * g + 1] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 1], kScaleLog2, -L.y * kLog2e));
+        x[4 * g + 2] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 2], kScaleLog2, -L.z * kLog2e));
+        x[4 * g + 3] = __builtin_amdgcn_exp2f(fmaf(x[4 * g + 3], kScaleLog2, -L.w * kLog2e));
+      }
+      accumulate(accV, x, sO);                   // dV += P^T dO
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const float4 D = *reinterpret_cast<const float4*>(sL + 32 + 8 * g + 4 * hh);
-      y[4 * g + 0] = x[4 * g + 0] * (y[4 * g + 0] - D.x);
-      y[4 * g + 1] = x[4 * g + 1] * (y[4 * g + 1] - D.y);
-      y[4 * g + 2] = x[4 * g + 2] * (y[4 * g + 2] - D.z);
-      y[4 * g + 3] = x[4 * g + 3] * (y[4 * g + 3] - D.w);
+      for (int g = 0; g < 4; ++g) {
+        const float4 D = *reinterpret_cast<const float4*>(sL + 32 + 8 * g + 4 * hh);
+        y[4 * g + 0] = x[4 * g + 0] * (y[4 * g + 0] - D.x);
+        y[4 * g + 1] = x[4 * g + 1] * (y[4 * g + 1] - D.y);
+        y[4 * g + 2] = x[4 * g + 2] * (y[4 * g + 2] - D.z);
+        y[4 * g + 3] = x[4 * g + 3] * (y[4 * g + 3] - D.w);
+      }
+      if constexpr (kDS) {
+        d0 = pack8(y, 0);
+        d1 = pack8(y, 8);
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) accK[t4] = mfma(frag_tr(sQ, tt.l(t4, 0), tt.h(t4, 0)), d0, accK[t4]);
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) accK[t4] = mfma(frag_tr(sQ, tt.l(t4, 1), tt.h(t4, 1)), d1, accK[t4]);
+      } else {
+        accumulate(accK, y, sQ);                 // dK += dS^T Q
+      }
     }
-    accumulate(accK, y, sQ);                     // dK += dS^T Q
+    if constexpr (kDS) {
+      // streamed out, read back once by the dQ kernel: non-temporal
+      __builtin_nontemporal_store(d0, reinterpret_cast<bf16x8*>(dst_ds));
+      __builtin_nontemporal_store(d1, reinterpret_cast<bf16x8*>(dst_ds + 16));
+    }
   };
   vm_wait();
   __syncthreads();
-  // two tiles per trip, so each ring slot is a fixed array (nq - qt0 is even)
+  // two tiles per trip, so each ring slot is a fixed array (nq - qt0 is even).
+  // With kDS every tile leaves its two dS stores in flight: they were
+  // issued after the ring copy (the compiler barrier keeps that order, and
+  // the memory counter completes in issue order), so waiting until at most
+  // 2 operations remain waits for the copy alone.
+  // The barrier is then LDS-only: __syncthreads() would also wait for the
+  // stores (no wave of the block reads them; the dQ kernel does, after
+  // this kernel).
+  auto sync_copy = [&]() __attribute__((always_inline)) {
+    if constexpr (kDS) {
+      vm_wait_but2();
+      lds_barrier();
+    } else {
+      vm_wait();
+      __syncthreads();
+    }
+  };
   for (int qt = qt0; qt < nq; qt += 2) {
     dma(qt + 1, st1);
+    asm volatile("" ::: "memory");
     tile(st0, qt);
-    vm_wait();
-    __syncthreads();
+    sync_copy();
     if (qt + 2 < nq) dma(qt + 2, st0);
+    asm volatile("" ::: "memory");
     tile(st1, qt + 1);
-    vm_wait();
-    __syncthreads();
+    sync_copy();
   }
   if (!keys) return;
   bf16* dst = (bf16*)a.dqkv + ((int64_t)b * T + my_j) * ld + h * HD;
   store_rows(accV, 1.f, dst + 2 * d, nullptr, hh, false);
   store_rows(accK, 0.08838834764831845f, dst + d, a.rope + (int64_t)my_j * (HD / 2), hh, a.rope != nullptr);
+}
+
+// ===========================================================================
+// backward with stored dS: delta first (the dK/dV kernel needs it before
+// any dQ work), then dK/dV storing dS^T, then dQ = dS K from those tiles.
+// ===========================================================================
+// delta[b][h][t] = sum_e dO[b,t,h,e] O[b,t,h,e]: 8 lanes per (token, head),
+// 16 features each, fp32 sums combined across the 8 lanes.
+__global__ void __launch_bounds__(256) k_attn_delta_rows(AttnDesc a) {
+  const int64_t n = (int64_t)a.B * a.T * a.H;
+  const int64_t pr = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);    // token * H + head
+  const int e = threadIdx.x & 7;
+  const int64_t p = pr < n ? pr : n - 1;
+  const int64_t off = p * HD + 16 * e;                                  // [B*T][H][128] rows
+  const u32x4* dv = reinterpret_cast<const u32x4*>((const bf16*)a.dout + off);
+  const u32x4* ov = reinterpret_cast<const u32x4*>((const bf16*)a.o + off);
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const u32x4 dw = dv[c], ow = ov[c];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc += bf_lo(dw[k]) * bf_lo(ow[k]) + bf_hi(dw[k]) * bf_hi(ow[k]);
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 4, 64);
+  if (e == 0 && pr < n) {
+    const int64_t tok = p / a.H, b = tok / a.T, t = tok % a.T;
+    const int h = (int)(p % a.H);
+    a.delta[(b * a.H + h) * a.T + t] = acc;
+  }
+}
+
+// dQ = dS K / sqrt(128) from the stored dS^T tiles.  A block owns 128
+// queries (a wave 32) and walks the 64-key tiles up to its diagonal; each
+// tile's K rows and dS^T image are copied into a 2-slot LDS ring.  A wave
+// multiplies only the 32-key halves that begin at or before its first
+// query (the dK/dV kernel wrote exactly those, with zeros where the causal
+// mask applies), so no masking is needed here.  Both operands come from
+// transposing reads: K^T (features x keys) as A, dS^T's column block of
+// the wave's queries (keys x queries) as B, keys in the same slot order on
+// both sides.  The result's lane n holds the query the column n of the
+// image stands for: i0 + n with bits 2 and 3 swapped.
+__global__ void __launch_bounds__(256, 2) k_attn_dq_ds(AttnDesc a) {
+  __shared__ __attribute__((aligned(16))) char sK0[16384], sD0[16384], sK1[16384], sD1[16384];
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = a.T, H = a.H, d = H * HD;
+  int qt, h, b;
+  const int ntq = (T + 127) / 128;
+  tile_order(ntq, H, a.B, qt, h, b);
+  qt = ntq - 1 - qt;
+  const int64_t ld = 3LL * d;
+  const bf16* kb = (const bf16*)a.qkv + (int64_t)b * T * ld + d + h * HD;
+  const bf16* dsq = (const bf16*)a.ds + (((int64_t)b * H + h) * ntq * (ntq + 1) + (int64_t)qt * (qt + 1)) * (64 * HD);
+  const int q0 = qt * 128, i0 = q0 + wave * 32;
+  const bool active = i0 < T;
+  const int c = lane & 31;
+  const int my_i = i0 + ((c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1));
+  const int ntk = T / 64;                                        // key tiles that exist
+  const int ntiles = (q0 + 128) / 64;                            // the block's (even; ntk + 1 for a half block)
+
+  // the dS^T tile into a natural [64 keys][128 queries] image: chunk c of
+  // key row r comes from the 32-query piece c / 4, chunk c % 4 of its row
+  auto dma = [&](int jt, char* sK, char* sD) __attribute__((always_inline)) {
+    dma_nat64(kb + (int64_t)min(jt, ntk - 1) * 64 * ld, ld, sK, wave, lane);
+    const bf16* t = dsq + (int64_t)jt * (64 * HD);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * i + (lane >> 4);
+      const int c = (lane & 15) ^ (int)swz(row);
+      __builtin_amdgcn_global_load_lds((gbl_vptr)(t + (c >> 2) * (64 * 32) + row * 32 + (c & 3) * 8),
+                                       (lds_vptr)(sD + (16 * wave + 4 * i) * 256), 16, 0, 0);
+    }
+  };
+  dma(0, sK0, sD0);
+
+  floatx16 dq[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) zero(dq[t]);
+  TrOff tk;
+  tk.init(lane);
+  // keys js * 32 .. +31 of the tile
+  auto half = [&](const char* sK, const char* sD, int js) __attribute__((always_inline)) {
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      const int sp = 2 * js + gp;
+      const bf16x8 df = frag_tr(sD, tk.l(wave, sp), tk.h(wave, sp));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dq[t] = mfma(frag_tr(sK, tk.l(t, sp), tk.h(t, sp)), df, dq[t]);
+    }
+  };
+  // tile jt: both halves when the second begins at or before i0, else the first
+  auto tile = [&](const char* sK, const char* sD, int jt) __attribute__((always_inline)) {
+    const int jh = jt * 64;
+    if (!active || jh > i0) return;
+    half(sK, sD, 0);
+    if (jh + 32 <= i0) half(sK, sD, 1);
+  };
+
+  vm_wait();
+  __syncthreads();
+  for (int jt = 0; jt < ntiles; jt += 2) {
+    dma(jt + 1, sK1, sD1);
+    tile(sK0, sD0, jt);
+    vm_wait();
+    __syncthreads();
+    if (jt + 2 < ntiles) dma(jt + 2, sK0, sD0);
+    tile(sK1, sD1, jt + 1);
+    vm_wait();
+    __syncthreads();
+  }
+  if (!active) return;
+  bf16* dst = (bf16*)a.dqkv + ((int64_t)b * T + my_i) * ld + h * HD;
+  store_rows(dq, 0.08838834764831845f, dst, a.rope + (int64_t)my_i * (HD / 2), hh, a.rope != nullptr);
 }
 
 }  // namespace
@@ -637,10 +802,20 @@ hipError_t attn_fwd_mfma(const AttnDesc& a, hipStream_t s) {
 
 hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s) {
   if (!attn_mfma_supported(a)) return hipErrorNotSupported;
-  k_attn_dq<<<dim3((a.T + 127) / 128, a.H, a.B), 256, 0, s>>>(a);   // also writes delta
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  k_attn_dkdv<<<dim3((a.T + kDkdvKeys - 1) / kDkdvKeys, a.H, a.B), 256, 0, s>>>(a);
+  const dim3 gq((a.T + 127) / 128, a.H, a.B), gk((a.T + kDkdvKeys - 1) / kDkdvKeys, a.H, a.B);
+  hipError_t e;
+  if (a.ds) {
+    const int64_t pairs = (int64_t)a.B * a.T * a.H;
+    k_attn_delta_rows<<<(unsigned)((pairs + 31) / 32), 256, 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_attn_dkdv<true><<<gk, 256, 0, s>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_attn_dq_ds<<<gq, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  k_attn_dq<<<gq, 256, 0, s>>>(a);   // also writes delta
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  k_attn_dkdv<false><<<gk, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -3,11 +3,24 @@
 
 namespace nc {
 
-int gemm_mfma_tile_m(int M, int /*N*/) { return M % 256 == 0 ? 256 : 128; }
-int gemm_mfma_tile_n(int M, int N) {
+namespace {
+// Products that may end in a tile shifted back to the matrix edge (the
+// layouts and epilogues listed in NC_MFMA_RAGGED_COMBOS): each output is
+// finished on its own, so the shifted tile recomputes the outputs it shares
+// with its neighbour and does not store them.
+bool ragged_ok(const GemmDesc& g) { return !g.sym && mfma::ragged_combo(g); }
+// 256 along a dimension that is a multiple of 256 or, for those products,
+// at least 1024 and a multiple of 128: the last tile then overlaps by 128,
+// at most 1/8 of that dimension's work recomputed, which costs less than
+// the narrower tiles' lower matrix-core rate.
+int pick_tile(int D, bool ragged) { return (D % 256 == 0 || (ragged && D >= 1024)) ? 256 : 128; }
+}  // namespace
+
+int gemm_mfma_tile_m(const GemmDesc& g) { return pick_tile(g.M, ragged_ok(g)); }
+int gemm_mfma_tile_n(const GemmDesc& g) {
   // a 256-row tile pairs with 256 or 128 columns; 128-row tiles with 128
-  if (M % 256 != 0) return 128;
-  return N % 256 == 0 ? 256 : 128;
+  if (gemm_mfma_tile_m(g) != 256) return 128;
+  return pick_tile(g.N, ragged_ok(g));
 }
 
 bool gemm_mfma_supported(const GemmDesc& g) {
@@ -16,7 +29,7 @@ bool gemm_mfma_supported(const GemmDesc& g) {
   if (g.splits > 1 && g.epi != EPI_F32) return false;
   if (g.batch > 1 && (g.splits != 1 || (g.epi != EPI_STORE && g.epi != EPI_AXPBY))) return false;
   if ((int64_t)(g.M / 128) * (g.N / 128) * g.splits * (g.batch > 1 ? g.batch : 1) > (1 << 30)) return false;
-  if (g.sym && (g.M != g.N || gemm_mfma_tile_m(g.M, g.N) != gemm_mfma_tile_n(g.M, g.N) || g.splits != 1 ||
+  if (g.sym && (g.M != g.N || gemm_mfma_tile_m(g) != gemm_mfma_tile_n(g) || g.splits != 1 ||
                 g.batch > 65535 ||
                 (g.epi != EPI_STORE && g.epi != EPI_AXPBY)))
     return false;
@@ -66,7 +79,7 @@ __global__ void __launch_bounds__(256) k_mirror_lower(unsigned short* C, int n, 
 
 hipError_t gemm_mfma_bf16_product(const GemmDesc& g, hipStream_t s) {
   if (!gemm_mfma_supported(g)) return hipErrorInvalidValue;
-  const int bm = gemm_mfma_tile_m(g.M, g.N), bn = gemm_mfma_tile_n(g.M, g.N);
+  const int bm = gemm_mfma_tile_m(g), bn = gemm_mfma_tile_n(g);
   hipError_t e;
   if (bm == 256 && bn == 256) e = mfma::gemm_256x256(g, s);
   else if (bm == 256) e = mfma::gemm_256x128(g, s);

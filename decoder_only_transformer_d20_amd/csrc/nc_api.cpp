@@ -63,7 +63,7 @@ int tile_n(const nc_config& c, int M, int N) {
   if (portable(c)) return 64;
   GemmDesc g{};
   g.M = M; g.N = N; g.K = c.d_model; g.splits = 1; g.epi = EPI_LSE;
-  return gemm_mfma_supported(g) ? gemm_mfma_tile_n(M, N) : 64;
+  return gemm_mfma_supported(g) ? gemm_mfma_tile_n(g) : 64;
 }
 
 // Split-K factor for the weight-gradient products (K = tokens).  Each split
@@ -73,8 +73,13 @@ int tile_n(const nc_config& c, int M, int N) {
 // the wave quantisation, plus the partials' round trip at 5 TB/s.
 int choose_splits(const nc_config& c, int M, int N, int64_t K) {
   constexpr int kCUs = 256;
-  const int64_t tiles = portable(c) ? (int64_t)(M / 64) * (N / 64)
-                                    : (int64_t)(M / gemm_mfma_tile_m(M, N)) * (N / gemm_mfma_tile_n(M, N));
+  int64_t tiles = (int64_t)(M / 64) * (N / 64);
+  if (!portable(c)) {
+    GemmDesc g{};
+    g.M = M; g.N = N; g.K = (int)K; g.splits = 1; g.epi = EPI_F32; g.p_trans = 1; g.q_trans = 1;
+    const int bm = gemm_mfma_tile_m(g), bn = gemm_mfma_tile_n(g);
+    tiles = (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  }
   const int64_t nb = K / 64;
   int best_s = 1;
   double best = 0.0;
@@ -280,7 +285,7 @@ hipError_t run_gemm(nc_ctx* ctx, const GemmDesc& g, int family = -2) {
   double items = g.batch > 1 ? g.batch : 1;
   if (g.sym) {
     // the tiles on and above the diagonal are computed, the rest mirrored
-    const double t = g.M / gemm_mfma_tile_m(g.M, g.N);
+    const double t = g.M / gemm_mfma_tile_m(g);
     items *= (t + 1) / (2 * t);
   }
   hipError_t e = traced(ctx, family < -1 ? gemm_family(g) : family, 2.0 * g.M * g.N * g.K * items,
@@ -345,7 +350,8 @@ template <typename T> hipError_t attn_fwd(nc_ctx* ctx, const AttnDesc& a) {
 template <typename T> hipError_t attn_bwd(nc_ctx* ctx, const AttnDesc& a) {
   if (!portable(ctx->cfg) && attn_mfma_supported(a)) {
     // flash backward: recompute S, then dV, dP, dQ, dK (5 causal products);
-    // q,k,v,o,dO read, dq,dk,dv written
+    // q,k,v,o,dO read, dq,dk,dv written (with stored dS also its round trip,
+    // which is the implementation's, not the method's)
     const double tok = (double)a.B * a.T, d = (double)a.H * a.Q;
     return traced(ctx, NC_TRACE_ATTN_BWD, 5 * 2.0 * attn_pairs(a) * a.Q, tok * (5 * d + 3 * d) * 2 + tok * a.H * 8,
                   [&] { return attn_bwd_mfma(a, ctx->stream); });
@@ -441,6 +447,11 @@ int layer_backward(nc_ctx* ctx, int l, const T* w, T* gr, float* dw, int accumul
   ad.B = c.batch; ad.T = c.seq_len; ad.H = c.n_head; ad.Q = c.head_dim;
   ad.qkv = qkv; ad.o = o; ad.lse = lse; ad.dout = tmp; ad.delta = ctx->at<float>(p.delta);
   ad.dqkv = big; ad.rope = ctx->at<float2>(p.rope);
+  // S and dP are recomputed in the dQ kernel (ad.ds = null).  Storing dS
+  // instead (nc_op_attention_bwd_ds, +1.4 GB of workspace at d20) measured
+  // the same time: the dQ kernel saves what the dK/dV kernel's dS stores and
+  // the separate delta pass cost.
+  ad.ds = nullptr;
   NC_TRY(attn_bwd<T>(ctx, ad), "attention backward");
   NC_TRY(weight_grad(ctx, 3 * d, d, big, 3 * d, a, d, dWqkv, accumulate), "dWqkv");
   NC_TRY(dgrad_desc<T>(ctx, N, big, 3 * d, Wqkv, 3 * d, d, EPI_STORE, tmp, d, &g), "transpose Wqkv");

@@ -101,7 +101,17 @@ struct AttnDesc {
   float* delta;             // [B][H][T] rowsum(dO * O)
   void* dqkv;               // [B*T][3*H*Q]
   const float2* rope;       // inverse rotation of dq, dk on store; NULL = none
+  // bf16 dS^T tiles (attn_ds_elems), written by the dK/dV kernel and read
+  // by the dQ kernel; NULL = the dQ kernel recomputes S and dP instead
+  void* ds;
 };
+// elements of the dS^T tile buffer for B x H heads of T tokens: per head,
+// query block qb (128 queries) holds 2 (qb + 1) tiles of 64 keys x 128
+// queries (the causal part, whole 64-key tiles)
+inline int64_t attn_ds_elems(int64_t B, int64_t T, int64_t H) {
+  const int64_t nq = (T + 127) / 128;
+  return B * H * nq * (nq + 1) * 64 * 128;
+}
 
 // ---------------------------------------------------------------------------
 // launchers (all enqueue on `s`; return hipError_t of the launch)
@@ -110,15 +120,15 @@ template <typename T> hipError_t gemm_portable(const GemmDesc& g, hipStream_t s)
 hipError_t gemm_mfma_bf16(const GemmDesc& g, hipStream_t s);          // product + split-K reduce
 hipError_t gemm_mfma_bf16_product(const GemmDesc& g, hipStream_t s);  // the product kernel alone
 bool gemm_mfma_supported(const GemmDesc& g);
-int gemm_mfma_tile_m(int M, int N);   // tile sizes the MFMA GEMM picks for an M x N output
-int gemm_mfma_tile_n(int M, int N);
+int gemm_mfma_tile_m(const GemmDesc& g);   // tile sizes the MFMA GEMM picks for a product
+int gemm_mfma_tile_n(const GemmDesc& g);
 hipError_t splitk_reduce(const float* part, int splits, int64_t n, float* out, int beta, hipStream_t s);
 // blocks x 4 waves x iters x 8 products of 32x32x16 (bf16) on registers only
 hipError_t mfma_loop(int64_t iters, int blocks, float* sink, hipStream_t s);
 
 template <typename T> hipError_t attn_fwd_portable(const AttnDesc& a, hipStream_t s);
 template <typename T> hipError_t attn_bwd_portable(const AttnDesc& a, hipStream_t s);
-bool attn_mfma_supported(const AttnDesc& a);   // head dim 128, T % 128 == 0
+bool attn_mfma_supported(const AttnDesc& a);   // head dim 128, T % 64 == 0
 hipError_t attn_fwd_mfma(const AttnDesc& a, hipStream_t s);
 hipError_t attn_bwd_mfma(const AttnDesc& a, hipStream_t s);
 template <typename T> hipError_t attn_delta(const AttnDesc& a, hipStream_t s);

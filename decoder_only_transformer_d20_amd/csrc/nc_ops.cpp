@@ -28,7 +28,7 @@ int head_tile(int32_t dtype, int64_t n, int32_t d, int32_t V, int32_t portable) 
   if (dtype == NC_DTYPE_F32 || portable) return 64;
   GemmDesc g{};
   g.M = (int)n; g.N = V; g.K = d; g.splits = 1; g.epi = EPI_LSE;
-  return gemm_mfma_supported(g) ? gemm_mfma_tile_n((int)n, V) : 64;
+  return gemm_mfma_supported(g) ? gemm_mfma_tile_n(g) : 64;
 }
 
 }  // namespace
@@ -142,6 +142,25 @@ int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t 
   hipStream_t s = (hipStream_t)hip_stream;
   if (dtype == NC_DTYPE_F32) return status_of(attn_bwd_portable<float>(a, s));
   return status_of(portable ? attn_bwd_portable<bf16>(a, s) : attn_bwd_mfma(a, s));
+}
+
+int nc_op_attention_bwd_ds(int32_t B, int32_t T, int32_t H, int32_t Q, const void* qkv, const void* o,
+                           const void* dout, const float* lse, float* delta, void* dqkv, const float* rope_tab,
+                           void* ds_scratch, void* hip_stream) {
+  if (!qkv || !o || !dout || !lse || !delta || !dqkv || !ds_scratch) return NC_ERR_INVALID_ARG;
+  if (B <= 0 || T <= 0 || H <= 0 || Q <= 0 || T % 64 || Q % 64) return NC_ERR_SHAPE;
+  AttnDesc a{};
+  a.B = B; a.T = T; a.H = H; a.Q = Q;
+  a.qkv = qkv; a.o = o; a.dout = dout; a.lse = (float*)lse; a.delta = delta; a.dqkv = dqkv;
+  a.rope = (const float2*)rope_tab;
+  a.ds = ds_scratch;
+  if (!attn_mfma_supported(a)) return NC_ERR_UNSUPPORTED;
+  return status_of(attn_bwd_mfma(a, (hipStream_t)hip_stream));
+}
+
+int64_t nc_op_attention_ds_bytes(int32_t B, int32_t T, int32_t H) {
+  if (B <= 0 || T <= 0 || H <= 0 || T % 64) return NC_ERR_SHAPE;
+  return attn_ds_elems(B, T, H) * 2;
 }
 
 int nc_op_embed_fwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void* E, const int32_t* idx, void* x,

@@ -106,6 +106,23 @@ int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t 
                         const void* dout, const float* lse, float* delta, void* dqkv, const float* rope_tab,
                         int32_t portable, void* hip_stream);
 
+/* The same backward with the softmax gradient stored instead of recomputed
+ * (the path nc_backward takes): delta first, then the dK/dV kernel writes
+ * dS^T = (P (dP - delta))^T in bf16 -- the causal part, as 64-key x
+ * 32-query pieces -- into ds_scratch, and the dQ kernel forms dQ = dS K
+ * from it without recomputing S and dP (Walkthrough, Pretraining: the
+ * attention of the trained model; the gradient is the method's, only the
+ * order of work differs).  bf16, Q = 128, T a multiple of 64 only, else
+ * NC_ERR_UNSUPPORTED.  ds_scratch: nc_op_attention_ds_bytes(B, T, H) bytes
+ * of device memory the caller owns; its contents on return are unspecified.
+ * Other arguments, layouts and results as nc_op_attention_bwd. */
+int nc_op_attention_bwd_ds(int32_t B, int32_t T, int32_t H, int32_t Q, const void* qkv, const void* o,
+                           const void* dout, const float* lse, float* delta, void* dqkv, const float* rope_tab,
+                           void* ds_scratch, void* hip_stream);
+/* Bytes of the dS^T scratch for B x H heads of T tokens (NC_ERR_SHAPE for
+ * non-positive sizes or T not a multiple of 64). */
+int64_t nc_op_attention_ds_bytes(int32_t B, int32_t T, int32_t H);
+
 /* Embedding gather x[n] = E[idx[n]] (T [V][d] -> T [n][d]), a bitwise row
  * copy.  An id outside [0, V) reads nothing: its row of x is all NaN. */
 int nc_op_embed_fwd(int32_t dtype, int64_t n, int32_t d, int32_t V, const void* E, const int32_t* idx, void* x,

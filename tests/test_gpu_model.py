@@ -4,7 +4,11 @@ nc_backward, nc_block_*) against the fp64 oracle on the same seeded inputs.
 Tolerances: fp32 configuration -- max relative error <= 1e-4 on loss, bpb
 and every gradient tensor (max_i |g - g*| / max_i |g*|); bf16
 configurations -- loss and bpb within 1e-2 relative, cosine similarity
->= 0.999 for every parameter-gradient tensor (and dx / y in block mode)."""
+>= 0.999 for every parameter-gradient tensor (and dx / y in block mode).
+Per-token ce at the full launches: within twice the error that bf16
+storage of the activations alone gives (tests/_util.logits_bf16_storage,
+the oracle's forward with the library's stored activations rounded to
+bf16), plus 1e-3."""
 import math
 
 import numpy as np
@@ -12,7 +16,9 @@ import pytest
 
 import oracle
 import synthdata
-from _util import dev, host, empty, max_rel_err, cosine, flat_tensors
+from scipy.special import logsumexp
+
+from _util import dev, host, empty, max_rel_err, cosine, flat_tensors, logits_bf16_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -329,6 +335,27 @@ def test_block_real_shape_two_rows():
         assert cosine(gt, want["grads"][name]) >= 0.999, name
 
 
+def test_block_d30_width_two_rows():
+    """One layer at the d30 widths (d 1920, 15 heads, MLP 7680) on 2 rows of
+    2048: the products with a 1920- or 5760-wide side end in a 256-wide tile
+    shifted back by 128 -- the rotary epilogue, both in-place residual adds,
+    the activation gradients and the accumulating weight gradients -- so an
+    output stored twice or not at all would show in y - x, dx or a weight
+    gradient."""
+    cfg = synthdata.get_config("block").with_(name="block_d30w", d_model=1920, n_head=15, d_ff=7680)
+    params = synthdata.make_params(cfg)
+    x, dy = synthdata.make_block_io(cfg, rows=2)
+    cfg = cfg.with_(batch=x.shape[0])
+    y, dx, g = _gpu_block(cfg, params, x, dy)
+    lp = synthdata.split_params(cfg, params)["layers"][0]
+    want = oracle.block_step(cfg, lp, x, dy)
+    assert cosine(y - x, want["y"] - x) >= 0.999
+    assert max_rel_err(y, want["y"]) <= 2e-2
+    assert cosine(dx, want["dx"]) >= 0.999
+    for name, layer, gt in flat_tensors(cfg, g):
+        assert cosine(gt, want["grads"][name]) >= 0.999, name
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(600)
 def test_block_full_batch_matches_oracle_on_two_rows():
@@ -415,8 +442,18 @@ def _full_batch_two_rows(name, keep):
     del g, P, sess
     torch.cuda.empty_cache()
     want = _oracle_step(cfg, params, idx, tgt, tb, rows=keep, token_weights=w.astype(np.float64))
-    # per-token ce of the compared rows, and the weighted loss = their mean
-    assert np.max(np.abs(got_ce[keep] - want["ce"][keep])) <= 0.05
+    # per-token ce of the compared rows against the bar the bf16 storage
+    # error model gives for the same rows, and the weighted loss = their mean
+    p64 = synthdata.split_params(cfg, params.astype(np.float64))
+    model_err = 0.0
+    for r in keep:
+        z = logits_bf16_storage(cfg, p64, idx[r])
+        valid = tgt[r] >= 0
+        ce_m = logsumexp(z, axis=1) - z[np.arange(z.shape[0]), np.maximum(tgt[r], 0)]
+        model_err = max(model_err, float(np.max(np.abs(ce_m - want["ce"][r])[valid])))
+        del z
+    err = float(np.max(np.abs(got_ce[keep] - want["ce"][keep])[tgt[keep] >= 0]))
+    assert err <= 2.0 * model_err + 1e-3, (err, model_err)
     mean_ce = float(want["ce"][keep].mean())
     assert abs(got_w[1] - mean_ce) / mean_ce <= 1e-2
     # loss and bpb of the whole batch follow from the GPU's own per-token ce
@@ -440,7 +477,8 @@ def test_d20_full_batch_gradients_match_oracle():
 def test_d30_one_row_matches_oracle():
     """The scaled d30 model (30 layers, d_model 1920, 15 heads x 128, MLP
     7680, vocab 65,536) on one 2048-token row.  Its widths 1920 and 5760 are
-    not multiples of 256, so the projections run on 256 x 128 tiles."""
+    not multiples of 256, so the products with those sides end in a 256-wide
+    tile shifted back by 128 (stored only past the overlap)."""
     cfg, params, idx, tgt, tb = _inputs(synthdata.get_config("d30"), rows=1)
     got = _gpu_step(cfg, params, idx, tgt, tb)
     want = _oracle_step(cfg, params, idx, tgt, tb)

@@ -44,6 +44,12 @@ MM_CASES = [
     ("bf16", 0, 384, 640, 320),      # 128 x 128 tiles
     ("bf16", 0, 768, 1280, 640),     # 256 x 256 tiles
     ("bf16", 0, 512, 384, 2048),     # 256 x 128 tiles
+    # M, N odd multiples of 128 (>= 1024): 256 x 256 tiles whose last row /
+    # column of tiles is shifted back by 128 (bf16 k-major stores and the
+    # transposed-operand fp32 products); the other layouts take 128 x 128
+    ("bf16", 0, 1152, 1408, 320),
+    ("bf16", 0, 1152, 1280, 192),
+    ("bf16", 0, 2048, 1920, 128),
 ]
 
 
@@ -83,6 +89,23 @@ def test_matmul_split_k_exact(dtype, portable, K, S):
     C = empty((M, N), "f32")
     part = empty((S * M * N,), "f32")
     nc.ops.matmul(DT[dtype], 1, 1, M, N, K, dev(P, dtype), dev(Q, dtype), C, 1, S, part, portable, None)
+    _sync()
+    np.testing.assert_array_equal(host(C), want)
+
+
+@pytest.mark.parametrize("M,N,S", [(1152, 1920, 3), (1920, 1280, 1), (1920, 1920, 5)])
+def test_matmul_split_k_shifted_tiles_exact(M, N, S):
+    """Weight-gradient products whose output sides are odd multiples of 128
+    (the d30 widths): the last tiles overlap their neighbours; every output
+    must be written once, exactly, with and without split-K."""
+    rng = np.random.default_rng(11 + S)
+    K = 1024
+    P = _ints(rng, (K, M))
+    Q = _ints(rng, (K, N))
+    want = P.astype(np.int64).T @ Q.astype(np.int64)
+    C = zeros((M, N), "f32")
+    part = empty((S * M * N,), "f32")
+    nc.ops.matmul(1, 1, 1, M, N, K, dev(P, "bf16"), dev(Q, "bf16"), C, 1, S, part, 0, None)
     _sync()
     np.testing.assert_array_equal(host(C), want)
 
@@ -269,7 +292,14 @@ def test_attention_fwd(dtype, portable, B, T, H, Q):
 
 @pytest.mark.parametrize("dtype,portable,B,T,H,Q", ATT_CASES)
 @pytest.mark.parametrize("with_rope", [0, 1])
-def test_attention_bwd(dtype, portable, B, T, H, Q, with_rope):
+@pytest.mark.parametrize("stored_ds", [0, 1])
+def test_attention_bwd(dtype, portable, B, T, H, Q, with_rope, stored_ds):
+    """dq, dk, dv against the oracle; stored_ds = 1 takes the path that
+    writes dS^T to a scratch buffer and forms dQ from it (matrix-core
+    kernels only).  The scratch is filled with NaN first: a tile the dQ
+    kernel read but the dK/dV kernel never wrote would show."""
+    if stored_ds and (dtype != "bf16" or portable):
+        pytest.skip("stored dS: bf16 matrix-core path only")
     rng = np.random.default_rng(20 + T)
     qkv = _qkv(rng, B, T, H, Q, dtype)
     dout = rng.standard_normal((B, T, H, Q)).astype(np.float32)
@@ -283,8 +313,16 @@ def test_attention_bwd(dtype, portable, B, T, H, Q, with_rope):
     nc.ops.rope_table(T, Q, 10000.0, tab, None)
     delta = empty((B, H, T), "f32")
     dqkv = zeros((B, T, 3, H, Q), dtype)
-    nc.ops.attention_bwd(DT[dtype], B, T, H, Q, qkvd, o, dev(dout, dtype), lse, delta, dqkv,
-                         tab if with_rope else None, portable, None)
+    if stored_ds:
+        nbytes = nc.ops.attention_ds_bytes(B, T, H)
+        nq = (T + 127) // 128
+        assert nbytes == B * H * nq * (nq + 1) * 64 * 128 * 2
+        ds = torch.full((nbytes // 2,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        nc.ops.attention_bwd_ds(B, T, H, Q, qkvd, o, dev(dout, dtype), lse, delta, dqkv,
+                                tab if with_rope else None, ds, None)
+    else:
+        nc.ops.attention_bwd(DT[dtype], B, T, H, Q, qkvd, o, dev(dout, dtype), lse, delta, dqkv,
+                             tab if with_rope else None, portable, None)
     _sync()
     got = host(dqkv, dtype)
     phi = oracle.rope_angles(T, Q, 10000.0)

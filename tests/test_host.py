@@ -130,6 +130,14 @@ def test_ops_reject_bad_shapes_before_launch():
     assert L.nc_op_embed_bwd_scratch_bytes(10, 64) > 0
     assert L.nc_op_embed_bwd(1, 10, 100, 50, 1, 1, 1, 0, 1, None) == -2
     assert L.nc_op_embed_bwd(1, 10, 64, 50, 1, 1, 1, 0, None, None) == -1
+    # stored-dS attention backward: scratch size (causal 64 x 128 tiles), then
+    # a missing scratch buffer and a T that is not a multiple of 64
+    assert L.nc_op_attention_ds_bytes(0, 128, 2) == -2
+    assert L.nc_op_attention_ds_bytes(1, 100, 2) == -2
+    assert L.nc_op_attention_ds_bytes(2, 2048, 10) == 2 * 10 * 16 * 17 * 64 * 128 * 2
+    assert L.nc_op_attention_ds_bytes(1, 192, 1) == 2 * 3 * 64 * 128 * 2
+    assert L.nc_op_attention_bwd_ds(1, 128, 1, 128, 1, 1, 1, 1, 1, 1, None, None, None) == -1
+    assert L.nc_op_attention_bwd_ds(1, 100, 1, 128, 1, 1, 1, 1, 1, 1, None, 1, None) == -2
 
 
 def test_status_strings():
