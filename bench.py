@@ -54,7 +54,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 # Keyed by family; valid only for the recorded hash of the kernel source.
 TRAFFIC = {
     # profiles/d20_step_hbm_traffic.md: 1.592 GB fetched + 0.134 GB written per dispatch
-    "gemm_wgrad": {"bytes_per_launch": 1725496100, "source_hash": "7fda353a75c16081"},
+    "gemm_wgrad": {"bytes_per_launch": 1725471147, "source_hash": "5f7264783a681f2e"},
 }
 
 

@@ -290,16 +290,18 @@ def test_attention_fwd(dtype, portable, B, T, H, Q):
             np.testing.assert_allclose(lg[b, h], logsumexp(S, axis=1), rtol=1e-5, atol=1e-5)
 
 
-@pytest.mark.parametrize("dtype,portable,B,T,H,Q", ATT_CASES)
+# every case with the recompute path; the bf16 matrix-core cases also with
+# the stored-dS path (nc_op_attention_bwd_ds)
+ATT_BWD_CASES = [c + (0,) for c in ATT_CASES] + [c + (1,) for c in ATT_CASES if c[0] == "bf16" and c[1] == 0]
+
+
+@pytest.mark.parametrize("dtype,portable,B,T,H,Q,stored_ds", ATT_BWD_CASES)
 @pytest.mark.parametrize("with_rope", [0, 1])
-@pytest.mark.parametrize("stored_ds", [0, 1])
-def test_attention_bwd(dtype, portable, B, T, H, Q, with_rope, stored_ds):
+def test_attention_bwd(dtype, portable, B, T, H, Q, stored_ds, with_rope):
     """dq, dk, dv against the oracle; stored_ds = 1 takes the path that
-    writes dS^T to a scratch buffer and forms dQ from it (matrix-core
-    kernels only).  The scratch is filled with NaN first: a tile the dQ
-    kernel read but the dK/dV kernel never wrote would show."""
-    if stored_ds and (dtype != "bf16" or portable):
-        pytest.skip("stored dS: bf16 matrix-core path only")
+    writes dS^T to a scratch buffer and forms dQ from it.  The scratch is
+    filled with NaN first: a piece the dQ kernel read but the dK/dV kernel
+    never wrote would show."""
     rng = np.random.default_rng(20 + T)
     qkv = _qkv(rng, B, T, H, Q, dtype)
     dout = rng.standard_normal((B, T, H, Q)).astype(np.float32)
