@@ -48,13 +48,24 @@ __device__ inline void unpack16(const uint4 v, float (&o)[8]) { V16<bf16>::unpac
 // 64w + l + 256i), so 256 coalesced pieces of each row are in flight per
 // step.  Partial sums are combined by a butterfly within each wave and then
 // across the waves in LDS, in a fixed order.
-template <typename T, int EPI, int S>
+//
+// NORM: the input rows are the residual stream x and the product is taken
+// of RMSNorm(x); each wave also sums x^2 over its share of K (the same
+// pieces it multiplies), and the finishing lane scales its output by
+// r = 1 / sqrt(sum / K + eps) -- the norm is linear in x, so
+// sum_k (r x_k) w_k = r sum_k x_k w_k.  Nothing is rounded to bf16 between
+// the norm and the product.
+template <typename T, int EPI, int S, bool NORM>
 __global__ void __launch_bounds__(256) k_gemv(GemvDesc g) {
   // S waves share a group of kCols columns, splitting K (S = 4: one group per
   // workgroup, for narrow products; S = 1: four groups per workgroup, each
   // wave its own, for the wide logits product)
   constexpr int VE = V16<T>::n;
   __shared__ float red[4][kMaxDecodeBatch * kCols];
+  __shared__ float red_sq[4][NORM ? kMaxDecodeBatch : 1];
+  float sq[NORM ? kMaxDecodeBatch : 1];
+#pragma unroll
+  for (int b = 0; b < (NORM ? kMaxDecodeBatch : 1); ++b) sq[b] = 0.f;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = wave / S, sub = wave % S;
   const int64_t n0 = ((int64_t)blockIdx.x * (4 / S) + grp) * kCols;   // < N: the launch covers N exactly
@@ -86,6 +97,10 @@ __global__ void __launch_bounds__(256) k_gemv(GemvDesc g) {
         for (int c = 0; c < kCols; ++c)
 #pragma unroll
           for (int e = 0; e < VE; ++e) acc[b][c] = fmaf(xv[e], w[c][e], acc[b][c]);
+        if constexpr (NORM) {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) sq[b] = fmaf(xv[e], xv[e], sq[b]);
+        }
       }
     }
   }
@@ -126,6 +141,13 @@ __global__ void __launch_bounds__(256) k_gemv(GemvDesc g) {
   }
   red[wave][lane] = vals[0];
   }
+  if constexpr (NORM) {
+    for (int b = 0; b < g.nb; ++b) {
+      float t = sq[b];
+      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+      if (lane == 0) red_sq[wave][b] = t;
+    }
+  }
   auto total = [&](int t) {
     if constexpr (S == 4) return (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
     else return red[wave][t];
@@ -136,12 +158,18 @@ __global__ void __launch_bounds__(256) k_gemv(GemvDesc g) {
   if (sub != 0 || t >= g.nb * kCols) return;
   const int b = t / kCols, c = t % kCols;
   const int64_t n = n0 + c;
-  float v = total(t);
+  float rs = 1.f;                                   // the row's RMSNorm scale
+  if constexpr (NORM) {
+    // S = 4: the group's waves split K; S = 1: the wave saw all of K
+    const float ss = S == 4 ? (red_sq[0][b] + red_sq[1][b]) + (red_sq[2][b] + red_sq[3][b]) : red_sq[wave][b];
+    rs = 1.f / __builtin_sqrtf(ss / (float)g.K + g.norm_eps);
+  }
+  float v = total(t) * rs;
   if constexpr (EPI == EPI_ROPE) {
     // adjacent pairs (2i, 2i+1) of the rotated columns, angles of one position
     if (n < g.rope_cols) {
       const int tp = t ^ 1;
-      const float other = total(tp);
+      const float other = total(tp) * rs;
       const float2 cs = g.rope[(n % g.head_dim) >> 1];
       v = (c & 1) ? other * cs.y + v * cs.x : v * cs.x - other * cs.y;
     }
@@ -762,17 +790,26 @@ hipError_t gemv(const GemvDesc& g, int epi, hipStream_t s) {
   // wide ones (the logits): a group per wave, the input read by 4x fewer waves
   const bool wide = g.N >= 16384 && g.N % (4 * kCols) == 0;
   const unsigned blocks = wide ? (unsigned)(g.N / (4 * kCols)) : (unsigned)(g.N / kCols);
-#define NC_GEMV(E)                                                   \
-  if (wide) k_gemv<T, E, 1><<<blocks, 256, 0, s>>>(g);               \
-  else k_gemv<T, E, 4><<<blocks, 256, 0, s>>>(g);                    \
+  if (g.norm && epi != EPI_ROPE && epi != EPI_RELU2 && epi != EPI_F32) return hipErrorInvalidValue;
+#define NC_GEMV(E, N)                                                \
+  if (wide) k_gemv<T, E, 1, N><<<blocks, 256, 0, s>>>(g);            \
+  else k_gemv<T, E, 4, N><<<blocks, 256, 0, s>>>(g);                 \
   break;
-  switch (epi) {
-    case EPI_STORE: NC_GEMV(EPI_STORE)
-    case EPI_ROPE: NC_GEMV(EPI_ROPE)
-    case EPI_RESID: NC_GEMV(EPI_RESID)
-    case EPI_RELU2: NC_GEMV(EPI_RELU2)
-    case EPI_F32: NC_GEMV(EPI_F32)
-    default: return hipErrorInvalidValue;
+  if (g.norm) {
+    switch (epi) {
+      case EPI_ROPE: NC_GEMV(EPI_ROPE, true)
+      case EPI_RELU2: NC_GEMV(EPI_RELU2, true)
+      default: NC_GEMV(EPI_F32, true)
+    }
+  } else {
+    switch (epi) {
+      case EPI_STORE: NC_GEMV(EPI_STORE, false)
+      case EPI_ROPE: NC_GEMV(EPI_ROPE, false)
+      case EPI_RESID: NC_GEMV(EPI_RESID, false)
+      case EPI_RELU2: NC_GEMV(EPI_RELU2, false)
+      case EPI_F32: NC_GEMV(EPI_F32, false)
+      default: return hipErrorInvalidValue;
+    }
   }
 #undef NC_GEMV
   return hipGetLastError();

@@ -314,11 +314,14 @@ __global__ void __launch_bounds__(256) k_embed_fix(const int32_t* __restrict__ s
     if (k < kWave) break;
   }
   // Pl[tile] + Pf[tile+1] + ... + Pf[ulast], added in that order; the loads
-  // of four partial rows are issued before their additions.
+  // of kAhead partial rows are issued before their additions.  A Zipf-hot
+  // id spans hundreds of tiles (id 0 of the d20 batch: ~280), so this one
+  // wave's chain of round trips sets the kernel's time: 16 rows in flight
+  // where the registers allow it.
   RowAcc<T, NCH> acc;
   acc.zero();
   acc.add_f32(Pl + tile * d, lane, chunks);
-  constexpr int kAhead = 4;
+  constexpr int kAhead = NCH <= 3 ? 16 : 4;
   for (int64_t u = tile + 1; u <= ulast; u += kAhead) {
     float v[kAhead][NCH][RowAcc<T, NCH>::VN];
 #pragma unroll

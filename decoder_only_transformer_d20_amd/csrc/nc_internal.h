@@ -187,6 +187,11 @@ struct GemvDesc {
   // EPI_ROPE on qkv: when kv_K is set, columns [d, 2d) also go to
   // kv_K[b][pos][:] and [2d, 3d) to kv_V[b][pos][:] (seq stride in elements)
   void* kv_K; void* kv_V; int64_t kv_seq_stride; int kv_d, kv_pos;
+  // norm = 1: x is the raw residual stream and the product is taken of
+  // RMSNorm(x) = x / sqrt(mean(x^2) + norm_eps), the row scale formed in the
+  // same pass (EPI_ROPE, EPI_RELU2 and EPI_F32 only)
+  int norm;
+  float norm_eps;
 };
 template <typename T> hipError_t gemv(const GemvDesc& g, int epi, hipStream_t s);
 // K, V [batch][max_len][d] of one layer: seq_stride = max_len * d
