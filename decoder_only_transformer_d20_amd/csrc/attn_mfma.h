@@ -128,6 +128,34 @@ __device__ inline void dma_nat64(const bf16* src, int64_t ld, char* img, int wav
                                      (lds_vptr)(img + (16 * wave + 4 * i) * 256), 16, 0, 0);
   }
 }
+// dma_nat64 through a buffer resource, for a block of NW waves (4 or 8):
+// measured 4-5 % faster than the global-address form in the forward kernel.
+// wave w copies rows (64 / NW) w .. in 1 KB pieces of 4 rows.  The per-lane
+// byte offsets are computed once; a tile is selected by the scalar offset,
+// so a copy is one buffer_load ... lds per piece with no per-tile address
+// arithmetic.  Offsets at or past `bytes` read zeros.
+template <int NW>
+struct TileCopy {
+  static constexpr int kPieces = 16 / NW;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[kPieces];
+  __device__ inline void init(const bf16* base, int64_t bytes, int64_t ld, int wave, int lane) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int row = (64 / NW) * wave + 4 * i + (lane >> 4);
+      const int chunk = (lane & 15) ^ (int)swz(row);
+      off[i] = (uint32_t)(((int64_t)row * ld + chunk * 8) * 2);
+    }
+  }
+  // rows row0 .. row0 + 63 of the base (row stride ld elements) into img
+  __device__ inline void copy(int row0, int64_t ld, char* img, int wave) const {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_vptr)(img + ((64 / NW) * wave + 4 * i) * 256), 16, off[i],
+                                               (int)(row0 * ld * 2), 0, 0);
+  }
+};
 // The same for a block of NW waves copying `rows` (a multiple of 4 NW) rows:
 // wave w takes rows w * rows / NW .. in 1 KB pieces of 4 rows.
 template <int NW>

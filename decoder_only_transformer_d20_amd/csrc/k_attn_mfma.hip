@@ -78,8 +78,13 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
   const int ntiles = (q0 + 128) / 64;                            // the block's (even; ntk + 1 for a half block)
   const int last = (i0 + 31) / 64;                               // this wave's diagonal tile
 
-  auto dmaK = [&](int jt, char* img) { dma_nat64(kb + (int64_t)jt * 64 * ld, ld, img, wave, lane); };
-  auto dmaV = [&](int jt, char* img) { dma_nat64(vb + (int64_t)jt * 64 * ld, ld, img, wave, lane); };
+  // the bytes of one head's K (or V) column block: rows 0 .. T-1, 128 wide
+  const int64_t span = (int64_t)(T - 1) * ld * 2 + HD * 2;
+  TileCopy<4> ck, cv;
+  ck.init(kb, span, ld, wave, lane);
+  cv.init(vb, span, ld, wave, lane);
+  auto dmaK = [&](int jt, char* img) { ck.copy(jt * 64, ld, img, wave); };
+  auto dmaV = [&](int jt, char* img) { cv.copy(jt * 64, ld, img, wave); };
   // (copies past the last key tile re-copy that tile into a slot nobody
   // reads: clamped indices keep the loop free of branches)
   dmaK(0, sK0);
@@ -259,6 +264,11 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd(AttnDesc a) {
   }
 }
 
+// (instantiated explicitly: without it the host stub of one of the
+// launched instantiations was left undefined in the library)
+template __global__ void k_attn_fwd<false>(AttnDesc);
+template __global__ void k_attn_fwd<true>(AttnDesc);
+
 // store a wave's 32 rows x 128 features accumulator (lane = row, regs =
 // features), rotated back by the row's rotary angles when `rot` (wave-
 // uniform).  Every rotary factor is requested before the first store: the
@@ -329,9 +339,13 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq(AttnDesc a) {
   const int ntiles = (q0 + 128) / 64;                            // the block's (even; ntk + 1 for a half block)
   const int last = (i0 + 31) / 64;                               // the wave's diagonal tile
 
+  const int64_t span = (int64_t)(T - 1) * ld * 2 + HD * 2;
+  TileCopy<4> ck, cv;
+  ck.init(kb, span, ld, wave, lane);
+  cv.init(vb, span, ld, wave, lane);
   auto dma = [&](int jt, char* sK, char* sV) {
-    dma_nat64(kb + (int64_t)jt * 64 * ld, ld, sK, wave, lane);
-    dma_nat64(vb + (int64_t)jt * 64 * ld, ld, sV, wave, lane);
+    ck.copy(jt * 64, ld, sK, wave);
+    cv.copy(jt * 64, ld, sV, wave);
   };
   dma(0, sK0, sV0);
 

@@ -261,6 +261,8 @@ ATT_CASES = [
     ("bf16", 0, 1, 2048, 10, 128),   # one row of the d20 launch: every head, full row length
     ("bf16", 0, 2, 192, 2, 128),     # T % 128 == 64: half-empty last query and key blocks
     ("bf16", 0, 1, 320, 3, 128),
+    ("bf16", 0, 1, 448, 2, 128),     # 256-query blocks, a 128-query block and a 64-query block
+    ("bf16", 0, 1, 64, 2, 128),      # the 64-query block alone
 ]
 
 
