@@ -112,3 +112,80 @@ def logits_bf16_storage(cfg, p64, tokens):
         x = r(x + u @ lp["W2"].T)
     xf = r(oracle.rmsnorm(x, cfg.rms_eps)[0])
     return xf @ p64["U"].T
+
+
+# ---------------------------------------------------------------------------
+# Rounding model of the matrix-core attention kernels (one head).  The
+# kernels' arithmetic is written out step by step with every rounding the
+# kernels make: scores accumulated to fp32, the log2-scaled exponent formed
+# by one fused multiply-add in fp32, the lazily raised reference maximum
+# (raised for all 32 rows of a wave when any row's 64-key tile maximum
+# passes it by more than 8), the exponentials' bf16 rounding where they
+# enter a product (P for PV and P^T dO, dS for dS K and dS^T Q), fp32 row
+# sums, and the final bf16 stores.  What it leaves out is the order of the
+# fp32 sums and the hardware exp2 / log2 / reciprocal error -- a few fp32
+# ulps each -- so a kernel that follows these steps reproduces the model's
+# bf16 outputs bit for bit except where such an ulp moves a value across a
+# bf16 rounding boundary (about one rounding in 2^13).
+# ---------------------------------------------------------------------------
+_F32 = np.float32
+_SCALE = _F32(0.08838834764831845)                      # 1 / sqrt(128)
+_SCALE_LOG2 = _F32(_F32(1.4426950408889634) * _SCALE)   # log2(e) / sqrt(128), as the kernels form it
+
+
+def _bf16(x):
+    return synthdata.round_to_bf16(np.asarray(x, _F32)).astype(np.float64)
+
+
+def attention_fwd_rounding_model(q, k, v):
+    """Forward of one head: q, k, v [T][128] (bf16 values, T a multiple of
+    64) -> (bf16 output [T][128] as float64, fp32 log-sum-exp [T])."""
+    T, Q = q.shape
+    S = (q @ k.T).astype(_F32)
+    out = np.zeros((T, Q))
+    lse = np.zeros(T, _F32)
+    for w0 in range(0, T, 32):
+        rows = np.arange(w0, min(w0 + 32, T))
+        last = (w0 + 31) // 64                      # the wave's diagonal tile
+        m = np.full(len(rows), -np.inf, _F32)
+        l = np.zeros(len(rows))
+        o = np.zeros((len(rows), Q))
+        for jt in range(last + 1):
+            j0, j1 = jt * 64, min(jt * 64 + 64, T)
+            s = S[rows[0]:rows[-1] + 1, j0:j1].copy()
+            s[np.arange(j0, j1)[None, :] > rows[:, None]] = -np.inf
+            mx = (s.max(axis=1) * _SCALE_LOG2).astype(_F32)
+            if np.any(mx > m + _F32(8)):
+                mn = np.maximum(m, mx)
+                alpha = np.exp2((m - mn).astype(np.float64))
+                l, o, m = l * alpha, o * alpha[:, None], mn
+            x = (s.astype(np.float64) * np.float64(_SCALE_LOG2) - m[:, None].astype(np.float64)).astype(_F32)
+            p = np.exp2(x.astype(np.float64)).astype(_F32)
+            l = l + p.astype(np.float64).sum(axis=1)
+            o = o + _bf16(p) @ v[j0:j1]
+        lf = l.astype(_F32)
+        inv = (_F32(1) / lf).astype(_F32)
+        out[rows] = _bf16(o.astype(_F32) * inv[:, None])
+        lse[rows] = ((m + np.log2(lf)).astype(_F32) * _F32(0.69314718055994531)).astype(_F32)
+    return out, lse
+
+
+def attention_bwd_rounding_model(q, k, v, o, lse, do):
+    """Backward of one head from the model's own forward (o bf16 values,
+    lse fp32) and dO (bf16 values): (dq, dk, dv) as the kernels store them
+    (bf16, before any rotary rotation) as float64."""
+    T = q.shape[0]
+    delta = (do * o).sum(axis=1).astype(_F32)
+    lse2 = (lse.astype(_F32) * _F32(1.4426950408889634)).astype(_F32)
+    S = (q @ k.T).astype(_F32)
+    x = (S.astype(np.float64) * np.float64(_SCALE_LOG2) - lse2[:, None].astype(np.float64)).astype(_F32)
+    P = np.exp2(x.astype(np.float64)).astype(_F32)
+    P[np.triu(np.ones((T, T), bool), 1)] = 0
+    dP = (do @ v.T).astype(_F32)
+    dS = (P * (dP - delta[:, None]).astype(_F32)).astype(_F32)
+    dSb = _bf16(dS)
+    dv = _bf16((_bf16(P).T @ do).astype(_F32))
+    dk = _bf16((dSb.T @ q).astype(_F32) * _SCALE)
+    dq = _bf16((dSb @ k).astype(_F32) * _SCALE)
+    return dq, dk, dv
+

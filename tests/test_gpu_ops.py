@@ -17,6 +17,7 @@ from scipy.special import logsumexp
 import oracle
 import synthdata
 from _util import dev, host, empty, zeros, max_rel_err, cosine
+from _util import attention_fwd_rounding_model, attention_bwd_rounding_model
 
 pytestmark = pytest.mark.gpu
 
@@ -339,6 +340,50 @@ def test_attention_bwd(dtype, portable, B, T, H, Q, stored_ds, with_rope):
         for i, want in enumerate((dq, dk, dv)):
             assert max_rel_err(got[b, :, i], want) <= tol, ("dq", "dk", "dv")[i]
             assert cosine(got[b, :, i], want) >= 0.9999, ("dq", "dk", "dv")[i]
+
+
+@pytest.mark.parametrize("T,H", [(448, 2), (2048, 2)])
+def test_attention_matches_rounding_model(T, H):
+    """The matrix-core forward and backward against a step-by-step model of
+    their own arithmetic (_util.attention_*_rounding_model: every rounding
+    the kernels make, in fp32 and bf16).  What the model leaves out -- the
+    order of the fp32 sums and the hardware exp2 / log2 / reciprocal, a few
+    fp32 ulps each -- moves a value across a bf16 rounding boundary about
+    once in 2^13 roundings.  A flip moves one rounded value by one bf16
+    ulp of itself: an output by one ulp, a P or dS term by one ulp of the
+    term, which in a sum of terms (dq, dk, dv) is at most an ulp of the
+    sum's scale even where the sum itself cancels to a small value.  So
+    the bar is: at least 99 % of the bf16 outputs bitwise equal to the
+    model's, every difference within one bf16 ulp of the tensor's largest
+    magnitude, and the log-sum-exp within 1e-6.  T = 448 runs the full, the
+    128-row and the 64-row query blocks; T = 2048 the d20 row length."""
+    rng = np.random.default_rng(40 + T)
+    B, Q = 1, 128
+    qkv = _qkv(rng, B, T, H, Q, "bf16")
+    dout = synthdata.round_to_bf16(rng.standard_normal((B, T, H, Q)).astype(np.float32))
+    qkvd = dev(qkv, "bf16")
+    o = empty((B, T, H, Q), "bf16")
+    lse = empty((B, H, T), "f32")
+    nc.ops.attention_fwd(DT["bf16"], B, T, H, Q, qkvd, o, lse, 0, None)
+    delta = empty((B, H, T), "f32")
+    dqkv = zeros((B, T, 3, H, Q), "bf16")
+    nc.ops.attention_bwd(DT["bf16"], B, T, H, Q, qkvd, o, dev(dout, "bf16"), lse, delta, dqkv, None, 0, None)
+    _sync()
+    og, lg, gg = host(o, "bf16"), host(lse), host(dqkv, "bf16")
+    for h in range(H):
+        q, k, v = (qkv[0, :, i, h].astype(np.float64) for i in range(3))
+        mo, ml = attention_fwd_rounding_model(q, k, v)
+        np.testing.assert_allclose(lg[0, h], ml, rtol=1e-6, atol=1e-6)
+        grads = attention_bwd_rounding_model(q, k, v, mo, ml, dout[0, :, h].astype(np.float64))
+        for name, got, want in [("o", og[0, :, h], mo)] + [(n, gg[0, :, i, h], w) for i, (n, w) in
+                                                          enumerate(zip(("dq", "dk", "dv"), grads))]:
+            same = float(np.mean(got == want))
+            top = np.max(np.abs(want))
+            ulps = np.max(np.abs(got - want)) / 2.0 ** (np.floor(np.log2(top)) - 7)
+            print(f"T={T} h={h} {name}: bitwise equal {same:.5f}, largest difference {ulps:.3f} ulp of the "
+                  f"largest magnitude", flush=True)
+            assert same >= 0.99, name
+            assert ulps <= 1.0, name
 
 
 # ---------------------------------------------------------------------------

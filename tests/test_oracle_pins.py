@@ -493,3 +493,4 @@ def test_sample_top_k_keeps_ties():
     z = np.array([0.0, 3.0, 1.0, 3.0, 2.0, 2.0, -1.0])
     drawn = {oracle.sample_next(z, 1.0, 3, (j + 0.5) / 1000) for j in range(1000)}
     assert drawn == {1, 3, 4, 5}           # the two 2.0s tie for third place
+
