@@ -104,10 +104,11 @@ def test_tiny_fp32_decode_matches_forward():
     _check(cfg, params, prompt, gen, 3, bf16=False)
 
 
-@pytest.mark.parametrize("T0,nseq,steps", [(100, 4, 5), (255, 2, 3), (1, 1, 4)])
+@pytest.mark.parametrize("T0,nseq,steps", [(100, 4, 5), (255, 2, 3), (1, 1, 4), (1022, 2, 4)])
 def test_small_bf16_decode_matches_forward(T0, nseq, steps):
-    """bf16, including a one-token prompt and a cache that crosses the
-    256-key chunk boundary of the decode attention."""
+    """bf16, including a one-token prompt, caches that cross 64-key chunk
+    boundaries of the decode attention, and one of 1023 to 1026 keys (17
+    chunks)."""
     cfg = synthdata.get_config("small")
     params = synthdata.make_params(cfg)
     prompt, gen = _tokens(cfg, T0, nseq, steps, 52 + T0)
