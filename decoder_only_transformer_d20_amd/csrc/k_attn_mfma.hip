@@ -11,7 +11,9 @@
 // atomics, so the result does not depend on scheduling.  dQ and dK leave
 // through the inverse rotary rotation, so the caller receives gradients with
 // respect to the pre-rotation q and k.  Every tile reaches LDS by direct
-// global-to-LDS copies (global_load_lds_dwordx4) into a ring of slots.
+// global-to-LDS copies into a ring of slots: the forward's and dQ's K/V
+// tiles as buffer loads (TileCopy: a scalar tile offset on offsets computed
+// once), the others as global_load_lds_dwordx4.
 #include <type_traits>
 
 #include "attn_mfma.h"
@@ -308,7 +310,7 @@ __device__ inline void store_rows(floatx16 (&acc)[4], float scale, bf16* dst_row
 // matrix-core work.  Per 64-key tile a wave forms S and dP of both 32-key
 // halves, then dS of the first half while the second half's products run,
 // then dS of the second half beside the first half's dQ products.  K and V
-// tiles are copied straight into a 2-slot LDS ring (global_load_lds); the
+// tiles are copied straight into a 2-slot LDS ring (TileCopy); the
 // tile on the wave's diagonal is peeled off the loop so the loop body has
 // no masking.  Also forms delta_i = sum_d dO[i,d] O[i,d] for the dK/dV
 // kernel, as k_attn_dq does.
