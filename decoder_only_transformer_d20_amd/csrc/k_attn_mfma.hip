@@ -803,7 +803,12 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_ds(AttnDesc a) {
 // T a multiple of 64: the forward and dQ kernels take 128-query blocks and
 // the dK/dV kernel 128-key blocks, so when T % 128 == 64 the last block's
 // waves past T sit idle (no loads, no stores).
-bool attn_mfma_supported(const AttnDesc& a) { return a.Q == HD && a.T % 64 == 0 && a.T > 0; }
+// The tile copies address one batch row's qkv block through a buffer
+// resource (32-bit size and offsets): T * 3 H Q * 2 bytes must stay below
+// 2^31.
+bool attn_mfma_supported(const AttnDesc& a) {
+  return a.Q == HD && a.T % 64 == 0 && a.T > 0 && (int64_t)a.T * 3 * a.H * HD * 2 < (int64_t(1) << 31);
+}
 
 hipError_t attn_fwd_mfma(const AttnDesc& a, hipStream_t s) {
   if (!attn_mfma_supported(a)) return hipErrorNotSupported;

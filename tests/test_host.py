@@ -138,6 +138,10 @@ def test_ops_reject_bad_shapes_before_launch():
     assert L.nc_op_attention_ds_bytes(1, 192, 1) == 2 * 3 * 64 * 128 * 2
     assert L.nc_op_attention_bwd_ds(1, 128, 1, 128, 1, 1, 1, 1, 1, 1, None, None, None) == -1
     assert L.nc_op_attention_bwd_ds(1, 100, 1, 128, 1, 1, 1, 1, 1, 1, None, 1, None) == -2
+    # a batch row's qkv block of 2^31 bytes or more is beyond the matrix-core
+    # kernels' 32-bit tile addressing: unsupported, reported before any launch
+    assert L.nc_op_attention_fwd(1, 1, 1 << 19, 10, 128, 1, 1, 1, 0, None) == -6
+    assert L.nc_op_attention_bwd_ds(1, 1 << 19, 10, 128, 1, 1, 1, 1, 1, 1, None, 1, None) == -6
 
 
 def test_status_strings():
