@@ -593,7 +593,63 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
         __syncthreads();
       }
     }
-    if constexpr (EPI != EPI_LSE) {
+    // Plain and relu^2 outputs: the op needs no other input, so it is
+    // applied to the accumulators where they are and the half-tile is staged
+    // in LDS as bf16 ([WTM][BN], 512-byte rows of 32 16-byte chunks, chunk
+    // ch of row r at slot ch ^ (r & 31)): half the LDS traffic of fp32
+    // staging, and 16-byte row-contiguous stores.  The result is the same
+    // bits (one rounding of the same fp32 value).
+    constexpr bool kBf16Stage = (EPI == EPI_STORE || EPI == EPI_RELU2) && BN == 256 && WTM == 128;
+    if constexpr (kBf16Stage) {
+      constexpr int CH = BN / 8;                       // 16-byte bf16 chunks per row
+      constexpr int PER = WTM * CH / (NW * 64);        // chunks per thread and pass
+      static_assert(WTM * BN * 2 <= 2 * STAGE && (WTM * CH) % (NW * 64) == 0, "epilogue staging");
+      char* eb = smem;
+      // a shifted last tile stores from row tm BM and column tn BN on (0 or
+      // 128 past the tile's origin): whole passes and whole chunks drop out
+      const int row_skip = RAG ? c.tm * BM - (int)c.m0 : 0;
+      const int col_from = RAG ? c.tn * BN - (int)c.n0 : 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (wm == h) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int r = i * 32 + (elane & 31);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int col = wn * WTN + j * 32 + 8 * q + 4 * (elane >> 5);
+                float x[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                if constexpr (EPI == EPI_RELU2) {
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], 0.f) * fmaxf(x[e], 0.f);
+                }
+                u32x2 w;
+                w.x = pack2(x[0], x[1]);
+                w.y = pack2(x[2], x[3]);
+                *reinterpret_cast<u32x2*>(eb + r * 512 + (((col >> 3) ^ (r & 31)) << 4) + 8 * ((col >> 2) & 1)) = w;
+              }
+          }
+        }
+        __syncthreads();
+        if (h == 1) prefetch_next();
+        if (!RAG || h * WTM >= row_skip) {
+#pragma unroll
+          for (int k = 0; k < PER; ++k) {
+            const int idx = k * (NW * 64) + etid;
+            const int r = idx / CH, ch = idx % CH;
+            if (!RAG || ch * 8 >= col_from) {
+              const u32x4 v = *reinterpret_cast<const u32x4*>(eb + r * 512 + ((ch ^ (r & 31)) << 4));
+              bf16* dst = (bf16*)g.C + c.cofs + (c.m0 + h * WTM + r) * g.ldc + c.n0 + ch * 8;
+              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+            }
+          }
+        }
+        if (h == 0) __syncthreads();
+      }
+    }
+    if constexpr (EPI != EPI_LSE && !kBf16Stage) {
       // Two passes, one per half of the tile's rows (the waves with wm = h
       // own rows h*WTM ..): those waves write their fp32 accumulators to
       // LDS as [WTM][BN] (16-byte chunk cc of row r at slot cc ^ (r & 15), so

@@ -34,6 +34,8 @@ bool gemm_mfma_supported(const GemmDesc& g) {
                 (g.epi != EPI_STORE && g.epi != EPI_AXPBY)))
     return false;
   if (g.epi == EPI_ROPE && (g.head_dim % 4 || g.rope_cols % 4)) return false;
+  // 16-byte output stores (the bf16 stores of the plain and relu^2 outputs)
+  if (g.epi != EPI_F32 && g.epi != EPI_LSE && (g.ldc % 8 || (uintptr_t)g.C % 16)) return false;
   return mfma::combo_supported(g);
 }
 
