@@ -593,13 +593,14 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
         __syncthreads();
       }
     }
-    // Plain and relu^2 outputs: the op needs no other input, so it is
+    // Plain, relu^2 and kept-logit outputs: the op needs no input beyond
+    // the tile (the kept logits its row maxima, already in LDS), so it is
     // applied to the accumulators where they are and the half-tile is staged
     // in LDS as bf16 ([WTM][BN], 512-byte rows of 32 16-byte chunks, chunk
     // ch of row r at slot ch ^ (r & 31)): half the LDS traffic of fp32
     // staging, and 16-byte row-contiguous stores.  The result is the same
     // bits (one rounding of the same fp32 value).
-    constexpr bool kBf16Stage = (EPI == EPI_STORE || EPI == EPI_RELU2) && BN == 256 && WTM == 128;
+    constexpr bool kBf16Stage = (EPI == EPI_STORE || EPI == EPI_RELU2 || EPI == EPI_LSEZ) && BN == 256 && WTM == 128;
     if constexpr (kBf16Stage) {
       constexpr int CH = BN / 8;                       // 16-byte bf16 chunks per row
       constexpr int PER = WTM * CH / (NW * 64);        // chunks per thread and pass
@@ -624,6 +625,12 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
                 if constexpr (EPI == EPI_RELU2) {
 #pragma unroll
                   for (int e = 0; e < 4; ++e) x[e] = fmaxf(x[e], 0.f) * fmaxf(x[e], 0.f);
+                }
+                if constexpr (EPI == EPI_LSEZ) {
+                  // the kept logits, relative to the tile's row maximum
+                  const float zm = zrow_max[h * WTM + r];
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) x[e] -= zm;
                 }
                 u32x2 w;
                 w.x = pack2(x[0], x[1]);
