@@ -32,7 +32,10 @@ extern "C" {
  *        blocks [i*nb/splits, (i+1)*nb/splits), nb = K/64; splits > 1 needs
  *        `part`, fp32 scratch of splits*M*N elements, reduced in a fixed
  *        order.
- * M, N multiples of 64; K a multiple of 64, splits <= K/64. */
+ * M, N multiples of 64; K a multiple of 64, splits <= K/64.  The
+ * matrix-core kernel (portable = 0, bf16) stores a rounded C in 16-byte
+ * pieces: with out_f32 = 0, C must be 16-byte aligned (N is a multiple of
+ * 64, so every row then is), otherwise NC_ERR_UNSUPPORTED. */
 int nc_op_matmul(int32_t dtype, int32_t p_trans, int32_t q_trans, int64_t M, int64_t N, int64_t K,
                  const void* P, const void* Q, void* C, int32_t out_f32, int32_t splits, float* part,
                  int32_t portable, void* hip_stream);
@@ -48,8 +51,8 @@ int nc_op_matmul(int32_t dtype, int32_t p_trans, int32_t q_trans, int64_t M, int
  *   C_b = C + b sC, aux_b = aux + b sAux   T [M][N]   (aux may not alias C)
  * Strides in elements, >= 0 and multiples of 8 (NC_ERR_INVALID_ARG
  * otherwise).  M, N, K multiples of 64 (NC_ERR_SHAPE); the matrix-core path
- * (portable = 0, bf16) also needs M, N multiples of 128 and returns
- * NC_ERR_UNSUPPORTED otherwise.  fp32 always takes the portable kernel.
+ * (portable = 0, bf16) also needs M, N multiples of 128 and a 16-byte
+ * aligned C, and returns NC_ERR_UNSUPPORTED otherwise.  fp32 always takes the portable kernel.
  * sym = 1 (M == N; Newton-Schulz's X X^T and c A A + b A): the caller
  * asserts every C_b is symmetric (Q_b = P_b, and aux_b symmetric); the
  * matrix-core kernel then computes the tiles on and above the diagonal and
