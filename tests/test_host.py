@@ -113,6 +113,8 @@ def test_ops_reject_bad_shapes_before_launch():
     L = nc.lib()
     # M not a multiple of 64
     assert L.nc_op_matmul(1, 0, 0, 100, 64, 64, 1, 1, 1, 1, 1, None, 0, None) == -2
+    # the matrix-core kernel's rounded output must be 16-byte aligned
+    assert L.nc_op_matmul(1, 0, 0, 128, 128, 64, 256, 256, 258, 0, 1, None, 0, None) == -6
     # split-K without partial buffer / with a stored (non-fp32) output
     assert L.nc_op_matmul(1, 0, 0, 64, 64, 128, 1, 1, 1, 1, 2, None, 0, None) == -1
     assert L.nc_op_matmul(1, 0, 0, 64, 64, 128, 1, 1, 1, 0, 2, 1, 0, None) == -1
