@@ -147,6 +147,22 @@ struct GemmTile {
   int64_t pofs, qofs, cofs, aofs;
 };
 
+// The coordinates are the same in every lane, but forming them takes
+// divisions the compiler runs on the vector unit; moved to scalar registers
+// explicitly, they stop occupying 18 VGPRs through the main loop.
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline int64_t uni(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ inline GemmTile uniform(GemmTile c) {
+  c.split = uni(c.split); c.tm = uni(c.tm); c.tn = uni(c.tn); c.nk = uni(c.nk);
+  c.m0 = uni(c.m0); c.n0 = uni(c.n0); c.kbeg = uni(c.kbeg);
+  c.pofs = uni(c.pofs); c.qofs = uni(c.qofs); c.cofs = uni(c.cofs); c.aofs = uni(c.aofs);
+  return c;
+}
+
 // Logical tile -> (split, m-tile, n-tile).  Workgroups are dealt to the 8
 // XCDs round-robin (and a full grid's G is a multiple of 8, so a block stays
 // on one XCD), so block slots are renumbered to give each XCD a contiguous
@@ -454,7 +470,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
 
   int v = blockIdx.x;
   if (tm.logical(v) < 0) return;                 // no tile for this block (uniform)
-  Tile cur = tm.template coords<RAG>(tm.logical(v), g);
+  Tile cur = uniform(tm.template coords<RAG>(tm.logical(v), g));
   plan_init(cur);
   stage_load();                 // k-tile 0 of the first tile
 
@@ -537,7 +553,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
     const Tile c = cur;
     auto prefetch_next = [&]() {
       if (more) {
-        cur = tm.template coords<RAG>(Ln, g);
+        cur = uniform(tm.template coords<RAG>(Ln, g));
         plan_init(cur);
         stage_load();
       }
@@ -556,6 +572,11 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
     if constexpr (EPI == EPI_LSE || EPI == EPI_LSEZ) {
       const int64_t nw = c.n0 + wn * WTN + 4 * (elane >> 5);
       float2* red = reinterpret_cast<float2*>(smem);      // [4 wn][BM]
+      // the rows' targets, all requested before the reductions: their
+      // latency is exposed once per tile and overlaps the exponentials
+      int tg[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) tg[i] = g.tgt[c.m0 + wm * WTM + i * 32 + (elane & 31)];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int ml = wm * WTM + i * 32 + (elane & 31);
@@ -575,7 +596,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
         s += __shfl_xor(s, 32, 64);
         if (elane < 32) red[wn * BM + ml] = make_float2(mx, s);
         // the target's logit, from whichever lane holds it
-        const int t = g.tgt[m];
+        const int t = tg[i];
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
