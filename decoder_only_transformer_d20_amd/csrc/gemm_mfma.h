@@ -473,6 +473,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   Tile cur = uniform(tm.template coords<RAG>(tm.logical(v), g));
   plan_init(cur);
   stage_load();                 // k-tile 0 of the first tile
+  stage_store(smem);
 
   for (;;) {
     const int nk = cur.nk;
@@ -499,7 +500,6 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
     // K-tiles past the last are never fetched: the staged index is clamped
     // to nk-1 (the pointer stops advancing), so the final iterations restage
     // the last k-tile into the idle stage instead of branching around it.
-    stage_store(smem);          // k-tile 0
     stage_advance(nk > 1);
     stage_load();               // k-tile min(1, nk-1)
     __syncthreads();
@@ -616,27 +616,34 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
     }
     // Plain, relu^2 and kept-logit outputs: the op needs no input beyond
     // the tile (the kept logits its row maxima, already in LDS), so it is
-    // applied to the accumulators where they are and the half-tile is staged
-    // in LDS as bf16 ([WTM][BN], 512-byte rows of 32 16-byte chunks, chunk
-    // ch of row r at slot ch ^ (r & 31)): half the LDS traffic of fp32
-    // staging, and 16-byte row-contiguous stores.  The result is the same
-    // bits (one rounding of the same fp32 value).
+    // applied to the accumulators where they are and the tile is staged in
+    // LDS as bf16 ([rows][BN], 512-byte rows of 32 16-byte chunks, chunk ch
+    // of row r at slot ch ^ (r & 31)), then stored in 16-byte row-contiguous
+    // pieces.  The result is the same bits (one rounding of the same fp32
+    // value).  The whole tile goes through LDS at once, written by all
+    // waves; the kept logits go in two halves (waves with wm = h write half
+    // h), which measured faster for that epilogue only.
+    // A rotary product's tiles with no rotated column (v) take this path too.
     constexpr bool kBf16Stage = (EPI == EPI_STORE || EPI == EPI_RELU2 || EPI == EPI_LSEZ) && BN == 256 && WTM == 128;
-    if constexpr (kBf16Stage) {
+    constexpr bool kBf16Able = kBf16Stage || (EPI == EPI_ROPE && BN == 256 && WTM == 128);
+    const bool bf16_tile = kBf16Able && (kBf16Stage || (EPI == EPI_ROPE && c.n0 >= g.rope_cols));   // uniform
+    if constexpr (kBf16Able) if (bf16_tile) {
+      constexpr int NPASS = EPI == EPI_LSEZ ? 2 : 1;
+      constexpr int RP = BM / NPASS;                   // rows per pass
       constexpr int CH = BN / 8;                       // 16-byte bf16 chunks per row
-      constexpr int PER = WTM * CH / (NW * 64);        // chunks per thread and pass
-      static_assert(WTM * BN * 2 <= 2 * STAGE && (WTM * CH) % (NW * 64) == 0, "epilogue staging");
+      constexpr int PER = RP * CH / (NW * 64);         // chunks per thread and pass
+      static_assert(RP * BN * 2 <= 2 * STAGE && (RP * CH) % (NW * 64) == 0 && RP % WTM == 0, "epilogue staging");
       char* eb = smem;
       // a shifted last tile stores from row tm BM and column tn BN on (0 or
-      // 128 past the tile's origin): whole passes and whole chunks drop out
+      // 128 past the tile's origin): whole row blocks and chunks drop out
       const int row_skip = RAG ? c.tm * BM - (int)c.m0 : 0;
       const int col_from = RAG ? c.tn * BN - (int)c.n0 : 0;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (wm == h) {
+      for (int h = 0; h < NPASS; ++h) {
+        if (NPASS == 1 || wm == h) {
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
-            const int r = i * 32 + (elane & 31);
+            const int r = (NPASS == 1 ? wm * WTM : 0) + i * 32 + (elane & 31);   // row within the pass
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -649,7 +656,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
                 }
                 if constexpr (EPI == EPI_LSEZ) {
                   // the kept logits, relative to the tile's row maximum
-                  const float zm = zrow_max[h * WTM + r];
+                  const float zm = zrow_max[h * RP + r];
 #pragma unroll
                   for (int e = 0; e < 4; ++e) x[e] -= zm;
                 }
@@ -661,23 +668,21 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
           }
         }
         __syncthreads();
-        if (h == 1) prefetch_next();
-        if (!RAG || h * WTM >= row_skip) {
+        if (h == NPASS - 1) prefetch_next();
 #pragma unroll
-          for (int k = 0; k < PER; ++k) {
-            const int idx = k * (NW * 64) + etid;
-            const int r = idx / CH, ch = idx % CH;
-            if (!RAG || ch * 8 >= col_from) {
-              const u32x4 v = *reinterpret_cast<const u32x4*>(eb + r * 512 + ((ch ^ (r & 31)) << 4));
-              bf16* dst = (bf16*)g.C + c.cofs + (c.m0 + h * WTM + r) * g.ldc + c.n0 + ch * 8;
-              __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
-            }
+        for (int k = 0; k < PER; ++k) {
+          const int idx = k * (NW * 64) + etid;
+          const int r = idx / CH, ch = idx % CH;
+          if (!RAG || (h * RP + r >= row_skip && ch * 8 >= col_from)) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(eb + r * 512 + ((ch ^ (r & 31)) << 4));
+            bf16* dst = (bf16*)g.C + c.cofs + (c.m0 + h * RP + r) * g.ldc + c.n0 + ch * 8;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
           }
         }
-        if (h == 0) __syncthreads();
+        if (h + 1 < NPASS) __syncthreads();
       }
     }
-    if constexpr (EPI != EPI_LSE && !kBf16Stage) {
+    if constexpr (EPI != EPI_LSE && !kBf16Stage) if (!bf16_tile) {
       // Two passes, one per half of the tile's rows (the waves with wm = h
       // own rows h*WTM ..): those waves write their fp32 accumulators to
       // LDS as [WTM][BN] (16-byte chunk cc of row r at slot cc ^ (r & 15), so
@@ -778,6 +783,12 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
     }
     if (!more) break;
     __syncthreads();            // epilogue LDS traffic done before k-tile 0 is written
+    // The next tile's k-tile 0, staged here rather than at the top of the
+    // loop: its loads were issued before the epilogue's stores, and in
+    // straight-line code the wait for them leaves those stores in flight
+    // (at the loop head, merged with the first tile's path, it would wait
+    // for the stores as well).
+    stage_store(smem);
   }
 }
 
