@@ -614,30 +614,72 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
         __syncthreads();
       }
     }
-    // Plain, relu^2 and kept-logit outputs: the op needs no input beyond
-    // the tile (the kept logits its row maxima, already in LDS), so it is
-    // applied to the accumulators where they are and the tile is staged in
-    // LDS as bf16 ([rows][BN], 512-byte rows of 32 16-byte chunks, chunk ch
-    // of row r at slot ch ^ (r & 31)), then stored in 16-byte row-contiguous
-    // pieces.  The result is the same bits (one rounding of the same fp32
-    // value).  The whole tile goes through LDS at once, written by all
-    // waves; the kept logits go in two halves (waves with wm = h write half
-    // h), which measured faster for that epilogue only.
-    // A rotary product's tiles with no rotated column (v) take this path too.
-    constexpr bool kBf16Stage = (EPI == EPI_STORE || EPI == EPI_RELU2 || EPI == EPI_LSEZ) && BN == 256 && WTM == 128;
-    constexpr bool kBf16Able = kBf16Stage || (EPI == EPI_ROPE && BN == 256 && WTM == 128);
-    const bool bf16_tile = kBf16Able && (kBf16Stage || (EPI == EPI_ROPE && c.n0 >= g.rope_cols));   // uniform
-    if constexpr (kBf16Able) if (bf16_tile) {
+    // Outputs staged in LDS as bf16 ([rows][BN], 512-byte rows of 32
+    // 16-byte chunks, chunk ch of row r at slot ch ^ (r & 31)), then stored
+    // in 16-byte row-contiguous pieces.  The whole tile goes through LDS at
+    // once, written by all waves; the kept logits go in two halves (waves
+    // with wm = h write half h), which measured faster for that epilogue
+    // only.
+    //  * plain, relu^2, kept logits: the op needs no input beyond the tile
+    //    (the kept logits its row maxima, already in LDS), so it is applied
+    //    to the accumulators where they are; one rounding of the same fp32
+    //    value as a row-order pass would give.
+    //  * residual, 2 sqrt(u), rotary: the product is rounded to bf16 as it
+    //    is staged and the op is applied to that in the row-order pass,
+    //    where its inputs (the aux row pieces, the rotary factors of the
+    //    row's position) are contiguous: half the LDS traffic and one pass
+    //    instead of two, for a second rounding of the result.  Their inputs
+    //    are requested before the staging writes, so their latency overlaps
+    //    the LDS round trip.
+    constexpr bool kOpPass = EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_ROPE;
+    constexpr bool kBf16Stage =
+        (EPI == EPI_STORE || EPI == EPI_RELU2 || EPI == EPI_LSEZ || kOpPass) && BN == 256 && WTM == 128;
+    if constexpr (kBf16Stage) {
       constexpr int NPASS = EPI == EPI_LSEZ ? 2 : 1;
       constexpr int RP = BM / NPASS;                   // rows per pass
       constexpr int CH = BN / 8;                       // 16-byte bf16 chunks per row
       constexpr int PER = RP * CH / (NW * 64);         // chunks per thread and pass
+      constexpr int RSTEP = NW * 64 / CH;              // rows between a thread's chunks
       static_assert(RP * BN * 2 <= 2 * STAGE && (RP * CH) % (NW * 64) == 0 && RP % WTM == 0, "epilogue staging");
+      static_assert(!kOpPass || NPASS == 1, "op pass");
       char* eb = smem;
       // a shifted last tile stores from row tm BM and column tn BN on (0 or
       // 128 past the tile's origin): whole row blocks and chunks drop out
       const int row_skip = RAG ? c.tm * BM - (int)c.m0 : 0;
       const int col_from = RAG ? c.tn * BN - (int)c.n0 : 0;
+      // a thread's chunks share one column run (ch_t) and are RSTEP rows apart
+      const int ch_t = etid % CH, r_t = etid / CH;
+      // residual / 2 sqrt(u): the thread's aux pieces, all requested now
+      u32x4 pa[kOpPass && EPI != EPI_ROPE ? PER : 1];
+      if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2) {
+        const bf16* ax = (const bf16*)g.aux + c.aofs + (c.m0 + r_t) * g.ldaux + c.n0 + ch_t * 8;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) pa[k] = *reinterpret_cast<const u32x4*>(ax + (int64_t)k * RSTEP * g.ldaux);
+      }
+      // rotary: the (cos, sin) of the chunk's four pairs at each row's
+      // position, requested WR rows ahead (the first WR now)
+      constexpr int WR = EPI == EPI_ROPE ? 4 : 1;
+      float4 pc[WR][2];
+      const int n_t = (int)c.n0 + 8 * ch_t;
+      const bool rot = EPI == EPI_ROPE && n_t < g.rope_cols;
+      const float2* rp = nullptr;
+      uint32_t t0 = 0;
+      if constexpr (EPI == EPI_ROPE) {
+        rp = g.rope + ((n_t % g.head_dim) >> 1);
+        t0 = (uint32_t)((c.m0 + r_t) % g.rope_T);
+      }
+      auto fetch_rope = [&](int k) {
+        if constexpr (EPI == EPI_ROPE) {
+          if (rot) {
+            const uint32_t t = (t0 + (uint32_t)(k * RSTEP)) % (uint32_t)g.rope_T;
+            const float4* f = reinterpret_cast<const float4*>(rp + t * (uint32_t)(g.head_dim >> 1));
+            pc[k % WR][0] = f[0];
+            pc[k % WR][1] = f[1];
+          }
+        }
+      };
+#pragma unroll
+      for (int k = 0; k < WR; ++k) fetch_rope(k);
 #pragma unroll
       for (int h = 0; h < NPASS; ++h) {
         if (NPASS == 1 || wm == h) {
@@ -671,18 +713,49 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
         if (h == NPASS - 1) prefetch_next();
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-          const int idx = k * (NW * 64) + etid;
-          const int r = idx / CH, ch = idx % CH;
-          if (!RAG || (h * RP + r >= row_skip && ch * 8 >= col_from)) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(eb + r * 512 + ((ch ^ (r & 31)) << 4));
-            bf16* dst = (bf16*)g.C + c.cofs + (c.m0 + h * RP + r) * g.ldc + c.n0 + ch * 8;
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+          const int r = r_t + k * RSTEP;
+          u32x4 v = *reinterpret_cast<const u32x4*>(eb + r * 512 + ((ch_t ^ (r & 31)) << 4));
+          if constexpr (EPI == EPI_RESID || EPI == EPI_DRELU2) {
+            const u32x4 y = pa[k];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float lo = bf_lo(v[e]), hi = bf_hi(v[e]);
+              if constexpr (EPI == EPI_RESID) {
+                lo += bf_lo(y[e]);
+                hi += bf_hi(y[e]);
+              } else {
+                // aux = relu(h)^2, so 2 relu(h) = 2 sqrt(aux)
+                lo *= 2.f * __builtin_sqrtf(fmaxf(bf_lo(y[e]), 0.f));
+                hi *= 2.f * __builtin_sqrtf(fmaxf(bf_hi(y[e]), 0.f));
+              }
+              v[e] = pack2(lo, hi);
+            }
+          }
+          if constexpr (EPI == EPI_ROPE) {
+            if (rot) {
+              const float4 f0 = pc[k % WR][0], f1 = pc[k % WR][1];
+              const float cs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float x0 = bf_lo(v[e]), x1 = bf_hi(v[e]);
+                const float co = cs[2 * e], si = cs[2 * e + 1];
+                v[e] = pack2(x0 * co - x1 * si, x0 * si + x1 * co);
+              }
+            }
+            if (k + WR < PER) fetch_rope(k + WR);
+          }
+          if (!RAG || (h * RP + r >= row_skip && ch_t * 8 >= col_from)) {
+            bf16* dst = (bf16*)g.C + c.cofs + (c.m0 + h * RP + r) * g.ldc + c.n0 + ch_t * 8;
+            // the 2 sqrt(u) gradient keeps plain stores (its aux input
+            // streams in beside the output; measured slower non-temporal)
+            if constexpr (EPI == EPI_DRELU2) *reinterpret_cast<u32x4*>(dst) = v;
+            else __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
           }
         }
         if (h + 1 < NPASS) __syncthreads();
       }
     }
-    if constexpr (EPI != EPI_LSE && !kBf16Stage) if (!bf16_tile) {
+    if constexpr (EPI != EPI_LSE && !kBf16Stage) {
       // Two passes, one per half of the tile's rows (the waves with wm = h
       // own rows h*WTM ..): those waves write their fp32 accumulators to
       // LDS as [WTM][BN] (16-byte chunk cc of row r at slot cc ^ (r & 15), so

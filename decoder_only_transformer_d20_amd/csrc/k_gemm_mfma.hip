@@ -36,6 +36,9 @@ bool gemm_mfma_supported(const GemmDesc& g) {
   if (g.epi == EPI_ROPE && (g.head_dim % 4 || g.rope_cols % 4)) return false;
   // 16-byte output stores (the bf16 stores of the plain and relu^2 outputs)
   if (g.epi != EPI_F32 && g.epi != EPI_LSE && (g.ldc % 8 || (uintptr_t)g.C % 16)) return false;
+  // 16-byte reads of the residual / relu(h)^2 rows and of the rotary factors
+  if ((g.epi == EPI_RESID || g.epi == EPI_DRELU2) && (g.ldaux % 8 || (uintptr_t)g.aux % 16)) return false;
+  if (g.epi == EPI_ROPE && (uintptr_t)g.rope % 16) return false;
   return mfma::combo_supported(g);
 }
 
