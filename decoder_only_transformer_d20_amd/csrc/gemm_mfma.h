@@ -447,6 +447,13 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
   // last step before the barrier the staged k-tile's LDS writes and the next
   // global loads, then the fragment reads of the following step; in the
   // other steps the fragment reads, spread evenly.
+  // In the staging step the next step's fragment reads can go to the LDS
+  // queue ahead of the k-tile's writes (kReadsFirst), so they are not
+  // waited for behind the writes at the barrier: 1-4 % faster per product
+  // family.  The rotary, log-sum-exp and dz epilogues keep the reads after
+  // the writes: with their extra live state the other order spills.
+  constexpr bool kReadsFirst = EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_DRELU2 || EPI == EPI_RELU2 ||
+                               (EPI == EPI_F32 && PT == QT);
   constexpr int kMfma = FM * FN;
   constexpr int kReads = FM * (PT ? 2 : 1) + FN * (QT ? 2 : 1);   // LDS read instructions per step
   constexpr int kStage = BM / 32;                                 // LDS writes / global loads per k-tile
@@ -510,7 +517,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
       char* nx = smem + ((kt + 1) & 1) * STAGE;
 #pragma unroll
       for (int s = 0; s < BK / 16 - 1; ++s) {
-        if (s == BK / 16 - 2) {
+        if (s == BK / 16 - 2 && !kReadsFirst) {
           // before the next fragment reads, so the staging registers are
           // free again by the time those land
           stage_store(nx);      // k-tile min(kt+1, nk-1)
@@ -518,6 +525,11 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
           stage_load();         // k-tile min(kt+2, nk-1)
         }
         read_frags(st, s + 1, (s + 1) & 1);
+        if (s == BK / 16 - 2 && kReadsFirst) {
+          stage_store(nx);
+          stage_advance(kt + 2 < nk);
+          stage_load();
+        }
         mfmas(s & 1);
         // Interleave so every memory instruction issues between MFMAs: in
         // the last step before the barrier the staged k-tile's LDS writes
@@ -527,12 +539,20 @@ __global__ void __launch_bounds__(NW * 64, 1) k_gemm_mfma(GemmDesc g) {
 #pragma unroll
           for (int q = 0; q < kMfma; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // MFMA
+            if constexpr (kReadsFirst) {
+              const int r = reads_early(q);
+              if (r >= 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+              if (r >= 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              if (r >= 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
             if (q < kStage) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // DS write
             if (q < kStage) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
-            const int r = reads_late(q);
-            if (r >= 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
-            if (r >= 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (r >= 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if constexpr (!kReadsFirst) {
+              const int r = reads_late(q);
+              if (r >= 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+              if (r >= 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              if (r >= 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
           }
         } else {
           interleave_reads();
