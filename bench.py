@@ -54,7 +54,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 # Keyed by family; valid only for the recorded hash of the kernel source.
 TRAFFIC = {
     # profiles/d20_step_hbm_traffic.md: 1.592 GB fetched + 0.134 GB written per dispatch
-    "gemm_wgrad": {"bytes_per_launch": 1725470583, "source_hash": "2b71cd2745520d47"},
+    "gemm_wgrad": {"bytes_per_launch": 1725486373, "source_hash": "ae9d0f9c7516286c"},
 }
 
 
