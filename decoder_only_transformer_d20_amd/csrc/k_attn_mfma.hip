@@ -25,17 +25,37 @@ namespace {
 
 constexpr float kScaleLog2 = kLog2e * 0.08838834764831845f;   // log2(e) / sqrt(128)
 
-// Block -> (tile, head, row).  Workgroups are dealt to the 8 XCDs
+// Block -> (tile, head, row); tile 0 is the heaviest of a (row, head) group
+// (the most key or query tiles to walk).  Workgroups are dealt to the 8 XCDs
 // round-robin; renumbering so each XCD takes a contiguous run of the
-// (row, head) groups keeps the 16 tiles that share one head's K/V (or Q/dO)
-// rows in one XCD's L2.
+// (row, head) groups keeps the tiles that share one head's K/V (or Q/dO)
+// rows in one XCD's L2.  Within an XCD's run, windows of kOrderWindow groups
+// are dispatched heaviest tile first across the window (all its groups'
+// tile 0, then their tile 1, ...): a window holds about as many blocks as
+// the XCD runs at once, so the groups in flight are the same as group by
+// group, but the light tiles come last and fill the slots the heavy ones
+// leave, instead of one group's heavy tile starting last and running alone.
+constexpr int kOrderWindow = 4;
 __device__ inline void tile_order(int ntile, int H, int B, int& tile, int& h, int& b) {
   const int total = ntile * H * B;
-  int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  if ((total & 7) == 0) L = (L & 7) * (total >> 3) + (L >> 3);
-  tile = L % ntile;
-  h = (L / ntile) % H;
-  b = L / (ntile * H);
+  const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  int grp;
+  if ((H * B) % 8 == 0) {
+    const int per = H * B / 8;                   // groups per XCD
+    const int x = L & 7, j = L >> 3;
+    const int wi = j / (kOrderWindow * ntile);
+    const int g0 = wi * kOrderWindow;
+    const int gw = min(kOrderWindow, per - g0);  // groups in this window
+    const int r = j - wi * kOrderWindow * ntile;
+    tile = r / gw;
+    grp = x * per + g0 + r % gw;
+  } else {
+    const int Lr = (total & 7) == 0 ? (L & 7) * (total >> 3) + (L >> 3) : L;
+    tile = Lr % ntile;
+    grp = Lr / ntile;
+  }
+  h = grp % H;
+  b = grp / H;
 }
 
 // ===========================================================================
